@@ -1,0 +1,250 @@
+"""Attention references of the oracle (test infrastructure only).
+
+"HyQuant paper" = the arXiv page "HyQuant: Hybrid-Precision Quantization for LLM
+Attention".
+
+* ``decode_ref``      -- exact softmax attention of one step's queries over the cache in
+                         its stored precision (the plain definition of Alg. 3's result).
+* ``flash_os`` / ``merge_states`` -- FlashAttention-style online-softmax state update and
+                         the ReduceSoftmax merge of split partial states (Alg. 3).
+* ``uniform_kv``      -- every position quantized with the same b-bit group scheme
+                         (uniform-precision comparison points of §2.2 Fig. 2).
+* ``prefill_ref``     -- step-by-step emulation of the hybrid prefill operator
+                         (Alg. 2; readings listed in its docstring).
+* ``attention_exact`` -- exact causal softmax attention (fp64) over bf16 inputs.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from . import numerics as nm
+
+
+# ----------------------------------------------------------------------------- decode
+
+
+def decode_ref(q: np.ndarray, Kh: np.ndarray, Vh: np.ndarray) -> np.ndarray:
+    """o_h = sum_j softmax_j(alpha * q_h . k_j) v_j over all positions, alpha = 1/sqrt(D)
+    (HyQuant paper §4.3 Eq. 8-9 and Alg. 3: every segment -- quantized prefix, vertical
+    lines, staging, window -- enters one softmax).  q: [g][D] fp32; Kh, Vh: [L][D] fp32
+    stored-precision values.  Computed in fp64, returned fp32 [g][D]."""
+    q = np.asarray(q, np.float64)
+    K = np.asarray(Kh, np.float64)
+    V = np.asarray(Vh, np.float64)
+    alpha = 1.0 / np.sqrt(K.shape[1])
+    z = alpha * (q @ K.T)
+    z -= z.max(axis=1, keepdims=True)
+    p = np.exp(z)
+    p /= p.sum(axis=1, keepdims=True)
+    return (p @ V).astype(np.float32)
+
+
+def decode_weights(q: np.ndarray, Kh: np.ndarray) -> np.ndarray:
+    """The softmax weights decode_ref applies (fp64), for the convex-combination checks."""
+    q = np.asarray(q, np.float64)
+    K = np.asarray(Kh, np.float64)
+    z = (q @ K.T) / np.sqrt(K.shape[1])
+    z -= z.max(axis=1, keepdims=True)
+    p = np.exp(z)
+    return p / p.sum(axis=1, keepdims=True)
+
+
+def flash_os(scores: np.ndarray, V: np.ndarray, state):
+    """One online-softmax update (FlashOS of Alg. 2/3) in fp64.
+    state = (m, l, acc) with m = running max of the scores (natural-log domain)."""
+    m, l, acc = state
+    scores = np.asarray(scores, np.float64)
+    if scores.size == 0:
+        return state
+    m_new = max(m, float(scores.max()))
+    c = 0.0 if m == -np.inf else np.exp(m - m_new)
+    p = np.exp(scores - m_new)
+    return m_new, l * c + p.sum(), acc * c + p @ np.asarray(V, np.float64)
+
+
+def merge_states(states):
+    """ReduceSoftmax of Alg. 3: m = max m_s, l = sum l_s e^(m_s - m),
+    acc = sum acc_s e^(m_s - m).  Returns the merged (m, l, acc)."""
+    states = [s for s in states if s[0] != -np.inf]
+    m = max(s[0] for s in states)
+    l = sum(s[1] * np.exp(s[0] - m) for s in states)
+    acc = sum(s[2] * np.exp(s[0] - m) for s in states)
+    return m, l, acc
+
+
+def init_state(D: int):
+    return -np.inf, 0.0, np.zeros(D)
+
+
+# ----------------------------------------------------------------------------- uniform precision
+
+
+def uniform_kv(K_bits: np.ndarray, V_bits: np.ndarray, bits: int, group: int = 32):
+    """Every position quantized with (2^bits - 1)-level asymmetric groups of ``group``
+    channels (same operation order as the INT4 quantizer); bits = 16 returns the bf16
+    values unchanged.  The uniform 4-bit / 8-bit comparison points of §2.2 Fig. 2."""
+    K = nm.bf16_to_f32(K_bits)
+    V = nm.bf16_to_f32(V_bits)
+    if bits >= 16:
+        return K, V
+    levels = (1 << bits) - 1
+    out = []
+    for X in (K, V):
+        L, D = X.shape
+        Xg = X.reshape(L, D // group, group)
+        c, s, m = nm.quant_asym(Xg, levels)
+        out.append(nm.dequant_asym(c, s, m).reshape(L, D))
+    return out[0], out[1]
+
+
+# ----------------------------------------------------------------------------- prefill
+
+
+def attention_exact(Q_bits, K_bits, V_bits) -> np.ndarray:
+    """Exact causal softmax attention, fp64, of bf16 inputs.  Q [Hq][N][D], K/V [Hkv][N][D];
+    Q head h reads KV head h // (Hq/Hkv).  Returns fp64 [Hq][N][D]."""
+    Q = nm.bf16_to_f32(Q_bits).astype(np.float64)
+    K = nm.bf16_to_f32(K_bits).astype(np.float64)
+    V = nm.bf16_to_f32(V_bits).astype(np.float64)
+    Hq, N, D = Q.shape
+    g = Hq // K.shape[0]
+    out = np.empty_like(Q)
+    mask = np.tril(np.ones((N, N), bool))
+    for h in range(Hq):
+        z = (Q[h] @ K[h // g].T) / np.sqrt(D)
+        z = np.where(mask, z, -np.inf)
+        z -= z.max(axis=1, keepdims=True)
+        p = np.exp(z)
+        p /= p.sum(axis=1, keepdims=True)
+        out[h] = p @ V[h // g]
+    return out
+
+
+def prefill_quantize(Q_bits, K_bits, V_bits, anchors, BM: int = 64, BN: int = 64):
+    """Operand quantization of the hybrid prefill (HyQuant paper Alg. 2 Stage 2, c_B = 127
+    for INT8 and 448 for FP8).  Readings:
+      * Q: symmetric INT8 per 64-query block per Q head, scale max|Q_blk|/127 (fp32).
+      * K: symmetric INT8 per 64-position block per KV head; anchor rows are left out of
+        the block maximum (their codes are never used).
+      * V: OCP E4M3 with a per-channel fp32 scale s_V[c] = max over the head's non-anchor
+        keys of |V[:, c]| / 448; code = e4m3(fp32(V / s_V)).
+    Returns dict of codes and scales (numpy)."""
+    Q = nm.bf16_to_f32(Q_bits)
+    K = nm.bf16_to_f32(K_bits)
+    V = nm.bf16_to_f32(V_bits)
+    Hq, N, D = Q.shape
+    Hkv = K.shape[0]
+    nqb = (N + BM - 1) // BM
+    nkb = (N + BN - 1) // BN
+    q8 = np.zeros(Q.shape, np.int8)
+    sq = np.zeros((Hq, nqb), np.float32)
+    for h in range(Hq):
+        for b in range(nqb):
+            q8[h, b * BM:(b + 1) * BM], sq[h, b] = nm.quant_int8_sym(Q[h, b * BM:(b + 1) * BM])
+    k8 = np.zeros(K.shape, np.int8)
+    sk = np.zeros((Hkv, nkb), np.float32)
+    v8 = np.zeros(V.shape, np.float64)  # e4m3 code values (as numbers)
+    sv = np.zeros((Hkv, D), np.float32)
+    for h in range(Hkv):
+        isanc = np.zeros(N, bool)
+        isanc[np.asarray(anchors[h], np.int64)] = True
+        Kz = np.where(isanc[:, None], np.float32(0), K[h])
+        for b in range(nkb):
+            k8[h, b * BN:(b + 1) * BN], sk[h, b] = nm.quant_int8_sym(Kz[b * BN:(b + 1) * BN])
+        Vz = np.where(isanc[:, None], np.float32(0), V[h])
+        amax = np.abs(Vz).max(axis=0).astype(np.float32)
+        sv[h] = amax / np.float32(448)
+        with np.errstate(divide="ignore", invalid="ignore"):
+            ratio = np.where(sv[h] > 0, Vz / np.where(sv[h] > 0, sv[h], np.float32(1)), np.float32(0))
+        v8[h] = nm.e4m3_round_fast(ratio.astype(np.float32))
+    return dict(q8=q8, sq=sq, k8=k8, sk=sk, v8=v8, sv=sv)
+
+
+def prefill_ref(Q_bits, K_bits, V_bits, anchors, W: int = 128, BM: int = 64, BN: int = 64,
+                blocks=None, round_p: bool = True):
+    """Emulation of the hybrid prefill operator (HyQuant paper §4.2 Eq. 6-7, Alg. 2).
+
+    For query i (causal), keys split three ways (Eq. 1 applied per query):
+      window  [max(0, i-W+1), i]             -- bf16 Q.K, bf16 V
+      anchors a <= i-W                       -- bf16 Q.K, bf16 V
+      the rest j <= i-W                      -- INT8 Q.K (int32 dot * s_Q * s_K * alpha),
+                                                FP8 P and FP8 V (per-channel scale)
+    One online softmax per row, tiles of BN keys, segment order A (quantized prefix,
+    ascending 64-key tiles) -> B (anchors, ascending 64-anchor tiles) -> C (window,
+    ascending 64-key tiles) as in Alg. 2 Stage 3.  After each tile's max update
+    p = exp(s - m_run); with ``round_p`` p is rounded as the operator stores it:
+    segment A: e4m3(448 p) / 448, segments B and C: bf16(p); l sums the rounded values.
+    Scores and exp in fp64.  ``blocks``: optional list of query-block indices to
+    compute (others are NaN).  Returns fp64 [Hq][N][D].
+    """
+    Qf = nm.bf16_to_f32(Q_bits).astype(np.float64)
+    Kf = nm.bf16_to_f32(K_bits).astype(np.float64)
+    Vf = nm.bf16_to_f32(V_bits).astype(np.float64)
+    Hq, N, D = Qf.shape
+    Hkv = Kf.shape[0]
+    g = Hq // Hkv
+    alpha = 1.0 / np.sqrt(D)
+    qz = prefill_quantize(Q_bits, K_bits, V_bits, anchors, BM, BN)
+    nqb = (N + BM - 1) // BM
+    if blocks is None:
+        blocks = range(nqb)
+    out = np.full((Hq, N, D), np.nan)
+    for h in range(Hq):
+        hk = h // g
+        anc = np.asarray(anchors[hk], np.int64)
+        isanc = np.zeros(N, bool)
+        isanc[anc] = True
+        k8 = qz["k8"][hk].astype(np.int64)
+        vq = qz["v8"][hk] * qz["sv"][hk].astype(np.float64)[None, :]  # dequantized FP8 V
+        for b in blocks:
+            r0, r1 = b * BM, min(N, (b + 1) * BM)
+            rows = np.arange(r0, r1)
+            q8 = qz["q8"][h, r0:r1].astype(np.int64)
+            sq = float(qz["sq"][h, b])
+            m = np.full(len(rows), -np.inf)
+            l = np.zeros(len(rows))
+            acc = np.zeros((len(rows), D))
+
+            def step(s, valid, Vt, seg):
+                nonlocal m, l, acc
+                s = np.where(valid, s, -np.inf)
+                tmax = s.max(axis=1)
+                m_new = np.maximum(m, tmax)
+                live = m_new > -np.inf
+                had = m > -np.inf
+                c = np.where(live & had, np.exp(np.where(had, m, 0.0) - np.where(live, m_new, 0.0)), 0.0)
+                p = np.where(valid, np.exp(s - np.where(live, m_new, 0.0)[:, None]), 0.0)
+                if round_p:
+                    if seg == "A":
+                        p = nm.e4m3_round_fast(448.0 * p) / 448.0
+                    else:
+                        p = nm.bf16_to_f32(nm.f32_to_bf16(p.astype(np.float32))).astype(np.float64)
+                l = l * c + p.sum(axis=1)
+                acc = acc * c[:, None] + p @ Vt
+                m = np.where(live, m_new, m)
+
+            # Segment A: quantized prefix tiles.
+            last_q = r1 - 1 - W
+            if last_q >= 0:
+                for t in range(last_q // BN + 1):
+                    j = np.arange(t * BN, min(N, (t + 1) * BN))
+                    dot = (q8 @ k8[j].T).astype(np.float64)
+                    s = dot * (sq * float(qz["sk"][hk, t])) * alpha
+                    valid = (j[None, :] <= rows[:, None] - W) & ~isanc[j][None, :]
+                    step(s, valid, vq[j], "A")
+            # Segment B: anchors, ascending tiles of BN anchors.
+            for u in range((len(anc) + BN - 1) // BN):
+                j = anc[u * BN:(u + 1) * BN]
+                s = alpha * (Qf[h, r0:r1] @ Kf[hk, j].T)
+                valid = j[None, :] <= rows[:, None] - W
+                step(s, valid, Vf[hk, j], "B")
+            # Segment C: window, ascending aligned tiles.
+            t_lo = max(0, r0 - W + 1) // BN
+            t_hi = (r1 - 1) // BN
+            for t in range(t_lo, t_hi + 1):
+                j = np.arange(t * BN, min(N, (t + 1) * BN))
+                s = alpha * (Qf[h, r0:r1] @ Kf[hk, j].T)
+                valid = (j[None, :] <= rows[:, None]) & (j[None, :] >= rows[:, None] - W + 1)
+                step(s, valid, Vf[hk, j], "C")
+            out[h, r0:r1] = acc / l[:, None]
+    return out

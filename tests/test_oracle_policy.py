@@ -1,0 +1,212 @@
+"""Pins for oracle.policy: anchor-count rule, vertical-line scores, top-k and the hybrid
+cache state machine, against closed forms and brute force on tiny inputs (CPU only)."""
+import math
+
+import numpy as np
+import pytest
+
+from hybrid_precision_kv_amd import synth
+from oracle import numerics as nm
+from oracle import policy as pol
+from oracle import attention as att
+
+
+# ----------------------------------------------------------------------------- k rule
+
+def test_k_rule_closed_forms():
+    # empty candidate set -> no anchors (Alg. 1: P = max(0, L_K - W), return empty when P = 0)
+    assert pol.k_rule(0) == 0 and pol.k_rule(100) == 0 and pol.k_rule(128) == 0
+    # at least one anchor once a candidate exists, never more than P
+    assert pol.k_rule(129) == 1
+    assert pol.k_rule(130, pct_num=100, pct_den=100) == 2
+    # ceil of 5% of the context length
+    assert pol.k_rule(1024) == 52 and pol.k_rule(4096) == 205
+    assert pol.k_rule(16384) == 820 and pol.k_rule(32768) == 1639
+    assert pol.k_rule(32768, pct_num=1) == 328 and pol.k_rule(32768, pct_num=10) == 3277
+    for L in range(129, 3000, 37):
+        k = pol.k_rule(L)
+        assert 1 <= k <= L - 128
+        assert k == L - 128 or (k >= 0.05 * L - 1e-9 and k < 0.05 * L + 1)
+
+
+# ----------------------------------------------------------------------------- scores / top-k
+
+def _brute_scores(proxy, keys, n_cand):
+    R, D = proxy.shape
+    L = keys.shape[0]
+    S = [0.0] * n_cand
+    for r in range(R):
+        z = [sum(float(proxy[r, c]) * float(keys[j, c]) for c in range(D)) / math.sqrt(D) for j in range(L)]
+        mx = max(z)
+        e = [math.exp(v - mx) for v in z]
+        tot = sum(e)
+        for j in range(n_cand):
+            S[j] += e[j] / tot
+    return np.array(S)
+
+
+def test_vertical_scores_brute_force():
+    rng = np.random.default_rng(0)
+    for D, L, R, P in [(32, 17, 5, 9), (64, 40, 8, 31), (32, 12, 1, 12)]:
+        proxy = rng.standard_normal((R, D)).astype(np.float32)
+        keys = rng.standard_normal((L, D)).astype(np.float32) * 1.7
+        ours = pol.vertical_scores(proxy, keys, P)
+        ref = _brute_scores(proxy, keys, P)
+        assert np.allclose(ours, ref, rtol=1e-12, atol=1e-14)
+
+
+def test_vertical_scores_mass_conservation():
+    rng = np.random.default_rng(1)
+    proxy = rng.standard_normal((12, 64))
+    keys = rng.standard_normal((300, 64)) * 2
+    S = pol.vertical_scores(proxy, keys, 300)
+    assert abs(S.sum() - 12) < 1e-10  # every proxy row's softmax sums to one
+    assert np.all(S >= 0)
+
+
+def test_topk_brute_force_and_ties():
+    rng = np.random.default_rng(2)
+    for _ in range(50):
+        n = int(rng.integers(1, 60))
+        s = rng.integers(0, 6, n).astype(float)  # many ties
+        k = int(rng.integers(0, n + 1))
+        ref = sorted(sorted(range(n), key=lambda j: (-s[j], j))[:k])
+        assert list(pol.topk_lower_index(s, k)) == ref
+
+
+# ----------------------------------------------------------------------------- cache state machine
+
+class BruteCache:
+    """Independent set-based model of the cache rules, for tiny inputs."""
+
+    def __init__(self, W):
+        self.W = W
+        self.val = {}  # pos -> (kvals, vvals) fp32 as stored
+        self.kind = {}
+
+    def _q(self, bits):
+        c, s, m = nm.quant_int4_token(nm.bf16_to_f32(bits), 32 if bits.shape[-1] % 32 == 0 else bits.shape[-1])
+        return nm.dequant_int4_token(c, s, m, 32 if bits.shape[-1] % 32 == 0 else bits.shape[-1])
+
+    def freeze(self, K, V, A):
+        L = len(K)
+        self.L = L
+        self.bits = {}
+        for p in range(L):
+            self.bits[p] = (K[p], V[p])
+            if p >= L - self.W:
+                self.kind[p] = "win"
+            elif p in set(A):
+                self.kind[p] = "anc"
+            else:
+                self.kind[p] = "q"
+                self.bits[p] = ("q", self._q(K[p]), self._q(V[p]))
+
+    def append(self, k, v):
+        if self.L >= self.W:
+            self.kind[self.L - self.W] = "stg"
+        self.kind[self.L] = "win"
+        self.bits[self.L] = (k, v)
+        self.L += 1
+
+    def refresh(self, A):
+        A = set(int(a) for a in A)
+        for p in range(self.L - self.W):
+            kd = self.kind[p]
+            if p in A:
+                if kd == "q":
+                    _, kq, vq = self.bits[p]
+                    self.bits[p] = (nm.f32_to_bf16(kq), nm.f32_to_bf16(vq))
+                self.kind[p] = "anc"
+            elif kd in ("anc", "stg"):
+                k, v = self.bits[p]
+                self.bits[p] = ("q", self._q(k), self._q(v))
+                self.kind[p] = "q"
+
+    def values(self):
+        Ks, Vs = [], []
+        for p in range(self.L):
+            b = self.bits[p]
+            if self.kind[p] == "q":
+                Ks.append(b[1]); Vs.append(b[2])
+            else:
+                Ks.append(nm.bf16_to_f32(b[0])); Vs.append(nm.bf16_to_f32(b[1]))
+        return np.array(Ks), np.array(Vs)
+
+
+def _brute_attn(q, K, V):
+    out = []
+    for h in range(q.shape[0]):
+        z = [sum(float(q[h, c]) * float(K[j, c]) for c in range(K.shape[1])) / math.sqrt(K.shape[1]) for j in range(len(K))]
+        mx = max(z)
+        e = [math.exp(t - mx) for t in z]
+        tot = sum(e)
+        out.append([sum(e[j] * float(V[j, c]) for j in range(len(K))) / tot for c in range(K.shape[1])])
+    return np.array(out)
+
+
+@pytest.mark.parametrize("D,W,L0,steps,seed", [(32, 4, 20, 9, 0), (64, 8, 33, 7, 1), (32, 8, 6, 12, 2)])
+def test_cache_state_machine_brute_force(D, W, L0, steps, seed):
+    rng = np.random.default_rng(seed)
+    g = 2
+    bf = lambda a: nm.f32_to_bf16(a.astype(np.float32))
+    K = bf(rng.standard_normal((L0, D)) * 1.3)
+    V = bf(rng.standard_normal((L0, D)))
+    P0 = max(0, L0 - W)
+    A0 = np.sort(rng.choice(P0, size=min(3, P0), replace=False)) if P0 else np.zeros(0, np.int64)
+    ref = pol.HybridCacheRef(D=D, W=W, group=32, g=g, proxy_cap=4)
+    ref.freeze(K, V, A0)
+    bc = BruteCache(W)
+    bc.freeze(K, V, list(A0))
+    for t in range(steps):
+        k = bf(rng.standard_normal(D)); v = bf(rng.standard_normal(D)); q = bf(rng.standard_normal((g, D)))
+        ref.append(k, v, q)
+        bc.append(k, v)
+        if t % 4 == 3:
+            P = ref.L - W
+            A = np.sort(rng.choice(P, size=min(P, 4), replace=False)) if P > 0 else np.zeros(0, np.int64)
+            ref.refresh(A)
+            bc.refresh(A)
+        Kh, Vh = ref.stored_kv()
+        Kb, Vb = bc.values()
+        assert np.array_equal(Kh, Kb.astype(np.float32)) and np.array_equal(Vh, Vb.astype(np.float32))
+        qf = nm.bf16_to_f32(q)
+        o = att.decode_ref(qf, Kh, Vh)
+        ob = _brute_attn(qf, Kb, Vb)
+        assert np.allclose(o, ob, rtol=0, atol=2e-6)
+        c = ref.counts()
+        assert c["win"] == min(ref.L, W)
+        assert c["win"] + c["staged"] + c["anchor"] + c["int4"] == ref.L
+
+
+def test_cache_counts_follow_closed_form():
+    s = synth.HeadStream(5, 600, 4)
+    A, _ = pol.select_dense(s.K, s.queries(64))
+    c = pol.HybridCacheRef(g=4)
+    c.freeze(s.K, s.V, A, s.queries(64))
+    k0 = pol.k_rule(600)
+    assert c.counts() == dict(L=600, win=128, staged=0, anchor=k0, int4=600 - 128 - k0)
+    for t in range(70):
+        k, v, q = s.new_tokens(1)
+        c.append(k[0], v[0], q[:, 0])
+    assert c.counts()["staged"] == 70 and c.proxy.shape[1] == 64
+    A2, _ = c.select()
+    c.refresh(A2)
+    k1 = pol.k_rule(670)
+    assert c.counts() == dict(L=670, win=128, staged=0, anchor=k1, int4=670 - 128 - k1)
+    assert np.array_equal(c.anchors(), A2)
+
+
+def test_promoted_positions_carry_bf16_of_dequant():
+    s = synth.HeadStream(7, 400, 2)
+    c = pol.HybridCacheRef(g=2)
+    c.freeze(s.K, s.V, np.array([3, 10]))
+    Kh0, Vh0 = c.stored_kv()
+    c.refresh(np.array([3, 50]))  # 50 was INT4 -> promoted; 10 demoted
+    Kh1, Vh1 = c.stored_kv()
+    assert np.array_equal(Kh1[50], nm.bf16_to_f32(nm.f32_to_bf16(Kh0[50])))
+    assert np.array_equal(Kh1[3], Kh0[3])
+    # a demoted anchor holding its original bf16 gets the same codes Freeze would give
+    c2 = pol.HybridCacheRef(g=2)
+    c2.freeze(s.K, s.V, np.array([3]))
+    assert np.array_equal(c2.stored_kv()[0][10], Kh1[10])
