@@ -1,0 +1,234 @@
+"""Python binding of the C ABI (include/hyq.h): torch tensors in, the same calls out.
+
+Every step of the method runs in the HIP library; this module checks tensor shapes/dtypes,
+allocates caller-owned buffers with torch, and passes pointers plus the current HIP stream.
+"""
+from __future__ import annotations
+
+import ctypes as C
+from dataclasses import dataclass
+
+import torch
+
+from . import _lib
+from ._lib import HyqCache, HyqShape, check
+
+D = 128
+WINDOW = 128
+PROXY_CAP = 64
+
+
+def _stream() -> C.c_void_p:
+    return C.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ptr(t: torch.Tensor | None) -> C.c_void_p:
+    return C.c_void_p(0 if t is None else t.data_ptr())
+
+
+def _bf16(t: torch.Tensor, shape: tuple, name: str) -> torch.Tensor:
+    if t.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
+        raise TypeError(f"{name}: expected bfloat16 (or its 16-bit pattern), got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name}: must be a contiguous device tensor")
+    return t
+
+
+def anchor_count(L: int, pct_num: int = 5, pct_den: int = 100, window: int = WINDOW) -> int:
+    """k = min(P, max(1, ceil(L * pct))) with P = max(0, L - window); 0 when P = 0."""
+    P = max(0, L - window)
+    if P == 0:
+        return 0
+    return min(P, max(1, -(-L * pct_num // pct_den)))
+
+
+@dataclass
+class Shape:
+    batch: int
+    n_q_heads: int
+    n_kv_heads: int
+    int4_cap: int
+    anchor_cap: int
+    staging_cap: int = 64
+
+    def c(self) -> HyqShape:
+        return HyqShape(self.batch, self.n_q_heads, self.n_kv_heads, D, 32, WINDOW, PROXY_CAP,
+                        self.staging_cap, self.int4_cap, self.anchor_cap)
+
+    @property
+    def g(self) -> int:
+        return self.n_q_heads // self.n_kv_heads
+
+    @staticmethod
+    def for_context(batch: int, n_q_heads: int, n_kv_heads: int, max_len: int, pct_num: int = 5,
+                    staging_cap: int = 64) -> "Shape":
+        """Capacities for contexts up to ``max_len`` with anchors at ``pct_num``%."""
+        r32 = lambda x: max(32, -(-x // 32) * 32)
+        k = anchor_count(max_len, pct_num)
+        return Shape(batch, n_q_heads, n_kv_heads, r32(max(0, max_len - WINDOW)), r32(k), r32(staging_cap))
+
+
+def buffer_bytes(shape: Shape) -> dict:
+    lib = _lib.load()
+    out = (C.c_size_t * _lib.HYQ_NBUF)()
+    s = shape.c()
+    check("hyq_cache_buffer_bytes", lib.hyq_cache_buffer_bytes(C.byref(s), C.byref(out)))
+    return {name: int(out[i]) for i, name in enumerate(_lib.BUFFERS)}
+
+
+def workspace_bytes(shape: Shape, op: int, length: int = 0, n_splits: int = 0) -> int:
+    lib = _lib.load()
+    s = shape.c()
+    return int(lib.hyq_workspace_bytes(C.byref(s), op, length, n_splits))
+
+
+class HybridKVCache:
+    """Caller-owned device buffers of the hybrid cache plus the host counters."""
+
+    def __init__(self, shape: Shape, device: str | torch.device = "cuda"):
+        self.shape = shape
+        self.device = torch.device(device)
+        sizes = buffer_bytes(shape)
+        self.buffers = {n: torch.empty(max(16, b), dtype=torch.uint8, device=self.device) for n, b in sizes.items()}
+        self.c = HyqCache()
+        self.c.shape = shape.c()
+        for n, t in self.buffers.items():
+            setattr(self.c, n, t.data_ptr())
+
+    # counters
+    @property
+    def len(self) -> int: return self.c.len
+    @property
+    def n_int4(self) -> int: return self.c.n_int4
+    @property
+    def n_anchor(self) -> int: return self.c.n_anchor
+    @property
+    def n_staged(self) -> int: return self.c.n_staged
+    @property
+    def n_proxy(self) -> int: return self.c.n_proxy
+
+    def counters(self) -> dict:
+        return {k: getattr(self.c, k) for k in ("len", "n_int4", "n_anchor", "n_staged", "n_proxy", "proxy_head")}
+
+    def snapshot(self) -> tuple[dict, dict]:
+        """Copy of the device buffers and the host counters (checkpoint)."""
+        return {n: t.clone() for n, t in self.buffers.items()}, self.counters()
+
+    def restore(self, snap: tuple[dict, dict]) -> None:
+        bufs, ctr = snap
+        for n, t in bufs.items():
+            self.buffers[n].copy_(t)
+        for k, v in ctr.items():
+            setattr(self.c, k, v)
+
+    def view(self, name: str, dtype: torch.dtype) -> torch.Tensor:
+        return self.buffers[name].view(dtype)
+
+
+def quantize_kv(cache: HybridKVCache, k: torch.Tensor, v: torch.Tensor, anchors: torch.Tensor | None = None,
+                q_tail: torch.Tensor | None = None) -> None:
+    """Freeze a dense prefill cache into the hybrid layout (hyq_quantize_kv)."""
+    s = cache.shape
+    L = k.shape[2]
+    _bf16(k, (s.batch, s.n_kv_heads, L, D), "k")
+    _bf16(v, (s.batch, s.n_kv_heads, L, D), "v")
+    n_anchor = 0
+    if anchors is not None:
+        if anchors.dtype != torch.int32 or not anchors.is_cuda or not anchors.is_contiguous():
+            raise TypeError("anchors: contiguous int32 device tensor expected")
+        if anchors.dim() != 3 or anchors.shape[:2] != (s.batch, s.n_kv_heads):
+            raise ValueError("anchors: shape [B][Hkv][k] expected")
+        n_anchor = anchors.shape[2]
+    n_tail = 0
+    if q_tail is not None:
+        n_tail = q_tail.shape[2]
+        _bf16(q_tail, (s.batch, s.n_q_heads, n_tail, D), "q_tail")
+    lib = _lib.load()
+    check("hyq_quantize_kv", lib.hyq_quantize_kv(C.byref(cache.c), _ptr(k), _ptr(v), L,
+                                                 _ptr(anchors if n_anchor else None), n_anchor,
+                                                 _ptr(q_tail), n_tail, _stream()))
+
+
+def append_token(cache: HybridKVCache, k_t: torch.Tensor, v_t: torch.Tensor, q_t: torch.Tensor | None = None) -> None:
+    s = cache.shape
+    _bf16(k_t, (s.batch, s.n_kv_heads, D), "k_t")
+    _bf16(v_t, (s.batch, s.n_kv_heads, D), "v_t")
+    if q_t is not None:
+        _bf16(q_t, (s.batch, s.n_q_heads, D), "q_t")
+    lib = _lib.load()
+    check("hyq_append_token", lib.hyq_append_token(C.byref(cache.c), _ptr(k_t), _ptr(v_t), _ptr(q_t), _stream()))
+
+
+class _Workspace:
+    def __init__(self):
+        self.t = None
+
+    def get(self, nbytes: int, device) -> torch.Tensor:
+        if self.t is None or self.t.numel() < nbytes or self.t.device != device:
+            self.t = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+        return self.t
+
+
+_ws = _Workspace()
+
+
+def decode_attn(cache: HybridKVCache, q: torch.Tensor, n_splits: int = 0, out: torch.Tensor | None = None,
+                ws: torch.Tensor | None = None) -> torch.Tensor:
+    """o = softmax(q K^T / sqrt(128)) V over the hybrid cache (hyq_decode_attn); fp32 out."""
+    s = cache.shape
+    _bf16(q, (s.batch, s.n_q_heads, D), "q")
+    if out is None:
+        out = torch.empty((s.batch, s.n_q_heads, D), dtype=torch.float32, device=q.device)
+    need = workspace_bytes(s, _lib.HYQ_OP_DECODE, 0, n_splits)
+    if ws is None:
+        ws = _ws.get(need, q.device)
+    lib = _lib.load()
+    check("hyq_decode_attn", lib.hyq_decode_attn(C.byref(cache.c), _ptr(q), _ptr(out), n_splits, _ptr(ws),
+                                                 ws.numel(), _stream()))
+    return out
+
+
+def select_vlines(shape: Shape, k: int, cache: HybridKVCache | None = None, dense_k: torch.Tensor | None = None,
+                  proxy: torch.Tensor | None = None, apply: bool = False, scores: bool = False):
+    """Vertical-line selector (hyq_select_vlines); returns idx [B][Hkv][k] (and scores)."""
+    lib = _lib.load()
+    dev = dense_k.device if dense_k is not None else cache.device
+    if dense_k is not None:
+        L = dense_k.shape[2]
+        _bf16(dense_k, (shape.batch, shape.n_kv_heads, L, D), "dense_k")
+        n_proxy = proxy.shape[2]
+        _bf16(proxy, (shape.batch, shape.n_q_heads, n_proxy, D), "proxy")
+    else:
+        L, n_proxy = cache.len, cache.n_proxy
+    P = max(0, L - WINDOW)
+    idx = torch.empty((shape.batch, shape.n_kv_heads, max(k, 1)), dtype=torch.int32, device=dev)
+    sc = torch.empty((shape.batch, shape.n_kv_heads, max(P, 1)), dtype=torch.float32, device=dev) if scores else None
+    s = shape.c()
+    need = int(lib.hyq_workspace_bytes(C.byref(s), _lib.HYQ_OP_SELECT, L, 0))
+    ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    check("hyq_select_vlines", lib.hyq_select_vlines(
+        C.byref(s), C.byref(cache.c) if cache is not None else None, _ptr(dense_k), L,
+        _ptr(proxy), n_proxy, k, int(apply), _ptr(idx), _ptr(sc), _ptr(ws), ws.numel(), _stream()))
+    idx = idx[..., :k]
+    return (idx, sc) if scores else idx
+
+
+def prefill_attn(shape: Shape, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                 anchors: torch.Tensor | None = None) -> torch.Tensor:
+    """Hybrid prefill attention for one sequence (hyq_prefill_attn); fp32 out [Hq][N][128]."""
+    lib = _lib.load()
+    N = q.shape[1]
+    _bf16(q, (shape.n_q_heads, N, D), "q")
+    _bf16(k, (shape.n_kv_heads, N, D), "k")
+    _bf16(v, (shape.n_kv_heads, N, D), "v")
+    n_anchor = 0 if anchors is None else anchors.shape[-1]
+    o = torch.empty((shape.n_q_heads, N, D), dtype=torch.float32, device=q.device)
+    s = shape.c()
+    need = int(lib.hyq_workspace_bytes(C.byref(s), _lib.HYQ_OP_PREFILL, N, 0))
+    ws = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    check("hyq_prefill_attn", lib.hyq_prefill_attn(C.byref(s), _ptr(q), _ptr(k), _ptr(v), N,
+                                                   _ptr(anchors if n_anchor else None), n_anchor, _ptr(o),
+                                                   _ptr(ws), ws.numel(), _stream()))
+    return o

@@ -1,0 +1,234 @@
+// C ABI of the hybrid-precision KV attention library: argument validation, host-side cache
+// counters, workspace sizing and kernel launches.  Declarations and contracts: include/hyq.h.
+#include <hip/hip_runtime.h>
+#include <string.h>
+
+#include "../../include/hyq.h"
+#include "hyq_launch.h"
+
+namespace {
+
+constexpr int D = HYQ_HEAD_DIM;
+constexpr int W = HYQ_WINDOW;
+
+int check_shape(const hyq_shape_t* s) {
+  if (!s) return HYQ_ERR_INVALID;
+  if (s->batch <= 0 || s->n_q_heads <= 0 || s->n_kv_heads <= 0) return HYQ_ERR_INVALID;
+  if (s->head_dim != D || s->group != HYQ_GROUP || s->window != W || s->proxy_cap != HYQ_PROXY_CAP)
+    return HYQ_ERR_UNSUPPORTED;
+  if (s->n_q_heads % s->n_kv_heads) return HYQ_ERR_INVALID;
+  const int g = s->n_q_heads / s->n_kv_heads;
+  if (g != 1 && g != 2 && g != 4 && g != 8 && g != 16) return HYQ_ERR_UNSUPPORTED;
+  if (s->staging_cap <= 0 || s->staging_cap % 32 || s->int4_cap < 0 || s->int4_cap % 32 || s->anchor_cap < 0 ||
+      s->anchor_cap % 32)
+    return HYQ_ERR_INVALID;
+  return HYQ_OK;
+}
+
+size_t nheads(const hyq_shape_t* s) { return (size_t)s->batch * s->n_kv_heads; }
+
+int check_cache_ptrs(const hyq_cache_t* c) {
+  if (!c->k_codes || !c->v_codes || !c->k_sm || !c->v_sm || !c->slot_pos || !c->a_k || !c->a_v || !c->a_pos ||
+      !c->s_k || !c->s_v || !c->w_k || !c->w_v || !c->proxy_q)
+    return HYQ_ERR_INVALID;
+  return HYQ_OK;
+}
+
+hyq::CacheView view(const hyq_cache_t* c) {
+  hyq::CacheView v;
+  v.k_codes = (uint8_t*)c->k_codes;
+  v.v_codes = (uint32_t*)c->v_codes;
+  v.k_sm = (uint32_t*)c->k_sm;
+  v.v_sm = (uint32_t*)c->v_sm;
+  v.slot_pos = c->slot_pos;
+  v.a_k = (uint16_t*)c->a_k;
+  v.a_v = (uint16_t*)c->a_v;
+  v.a_pos = c->a_pos;
+  v.s_k = (uint16_t*)c->s_k;
+  v.s_v = (uint16_t*)c->s_v;
+  v.w_k = (uint16_t*)c->w_k;
+  v.w_v = (uint16_t*)c->w_v;
+  v.proxy_q = (uint16_t*)c->proxy_q;
+  v.B = c->shape.batch;
+  v.Hkv = c->shape.n_kv_heads;
+  v.G = c->shape.n_q_heads / c->shape.n_kv_heads;
+  v.int4_cap = c->shape.int4_cap;
+  v.anchor_cap = c->shape.anchor_cap;
+  v.staging_cap = c->shape.staging_cap;
+  v.proxy_cap = c->shape.proxy_cap;
+  return v;
+}
+
+// consistency of the host counters with the method's invariants
+int check_counters(const hyq_cache_t* c) {
+  const hyq_shape_t& s = c->shape;
+  if (c->len < 0 || c->n_int4 < 0 || c->n_anchor < 0 || c->n_staged < 0) return HYQ_ERR_INVALID;
+  const int P = c->len > W ? c->len - W : 0;
+  if (c->n_int4 + c->n_anchor + c->n_staged != P) return HYQ_ERR_INVALID;
+  if (c->n_int4 > s.int4_cap || c->n_anchor > s.anchor_cap || c->n_staged > s.staging_cap) return HYQ_ERR_CAPACITY;
+  if (c->n_proxy < 0 || c->n_proxy > s.proxy_cap || c->proxy_head < 0 || c->proxy_head >= s.proxy_cap)
+    return HYQ_ERR_INVALID;
+  return HYQ_OK;
+}
+
+int auto_splits(const hyq_cache_t* c) {
+  const int G = c->shape.n_q_heads / c->shape.n_kv_heads;
+  const long units = (long)nheads(&c->shape) * ((G + 3) / 4);
+  const long tiles = (c->n_int4 + 31) / 32 + 3 * ((c->n_anchor + 31) / 32 + (c->n_staged + 31) / 32 + 4);
+  long s = (2048 + units - 1) / units;          // aim for ~2048 workgroups
+  const long by_work = (tiles + 15) / 16;        // >= ~4 tiles per wave
+  if (s > by_work) s = by_work;
+  if (s < 1) s = 1;
+  if (s > 256) s = 256;
+  return (int)s;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* hyq_status_string(int status) {
+  switch (status) {
+    case HYQ_OK: return "ok";
+    case HYQ_ERR_INVALID: return "invalid argument";
+    case HYQ_ERR_UNSUPPORTED: return "unsupported shape";
+    case HYQ_ERR_CAPACITY: return "capacity exceeded";
+    case HYQ_ERR_WORKSPACE: return "workspace missing or too small";
+    case HYQ_ERR_HIP: return "HIP launch failure";
+    default: return "unknown status";
+  }
+}
+
+int hyq_cache_buffer_bytes(const hyq_shape_t* s, size_t bytes[HYQ_NBUF]) {
+  int st = check_shape(s);
+  if (st) return st;
+  if (!bytes) return HYQ_ERR_INVALID;
+  const size_t H = nheads(s);
+  bytes[HYQ_BUF_K_CODES] = H * s->int4_cap * 64;
+  bytes[HYQ_BUF_V_CODES] = H * s->int4_cap * 64;
+  bytes[HYQ_BUF_K_SM] = H * s->int4_cap * 16;
+  bytes[HYQ_BUF_V_SM] = H * s->int4_cap * 16;
+  bytes[HYQ_BUF_SLOT_POS] = H * s->int4_cap * 4;
+  bytes[HYQ_BUF_A_K] = H * s->anchor_cap * D * 2;
+  bytes[HYQ_BUF_A_V] = H * s->anchor_cap * D * 2;
+  bytes[HYQ_BUF_A_POS] = H * s->anchor_cap * 4;
+  bytes[HYQ_BUF_S_K] = H * s->staging_cap * D * 2;
+  bytes[HYQ_BUF_S_V] = H * s->staging_cap * D * 2;
+  bytes[HYQ_BUF_W_K] = H * W * D * 2;
+  bytes[HYQ_BUF_W_V] = H * W * D * 2;
+  bytes[HYQ_BUF_PROXY_Q] = (size_t)s->batch * s->n_q_heads * s->proxy_cap * D * 2;
+  return HYQ_OK;
+}
+
+size_t hyq_workspace_bytes(const hyq_shape_t* s, int op, int32_t len, int32_t n_splits) {
+  if (check_shape(s)) return 0;
+  switch (op) {
+    case HYQ_OP_DECODE: {
+      const int S = n_splits > 0 ? n_splits : 256;
+      return (size_t)s->batch * s->n_q_heads * S * (D + 2) * sizeof(float);
+    }
+    default: return 0;
+  }
+}
+
+int hyq_quantize_kv(hyq_cache_t* c, const void* k, const void* v, int32_t len, const int32_t* anchors,
+                    int32_t n_anchor, const void* q_tail, int32_t n_tail, hipStream_t stream) {
+  if (!c) return HYQ_ERR_INVALID;
+  int st = check_shape(&c->shape);
+  if (st) return st;
+  if ((st = check_cache_ptrs(c))) return st;
+  if (!k || !v || len <= 0 || n_anchor < 0 || n_tail < 0) return HYQ_ERR_INVALID;
+  if (n_anchor > 0 && !anchors) return HYQ_ERR_INVALID;
+  if (n_tail > 0 && !q_tail) return HYQ_ERR_INVALID;
+  const int P = len > W ? len - W : 0;
+  if (n_anchor > P) return HYQ_ERR_CAPACITY;
+  if (n_anchor > c->shape.anchor_cap || P - n_anchor > c->shape.int4_cap) return HYQ_ERR_CAPACITY;
+  hipError_t e = hyq::launch_freeze(view(c), (const uint16_t*)k, (const uint16_t*)v, len, anchors, n_anchor,
+                                    (const uint16_t*)q_tail, n_tail, stream);
+  if (e != hipSuccess) return HYQ_ERR_HIP;
+  c->len = len;
+  c->n_anchor = n_anchor;
+  c->n_int4 = P - n_anchor;
+  c->n_staged = 0;
+  const int np = n_tail < c->shape.proxy_cap ? n_tail : c->shape.proxy_cap;
+  c->n_proxy = np;
+  c->proxy_head = np % c->shape.proxy_cap;
+  return HYQ_OK;
+}
+
+int hyq_append_token(hyq_cache_t* c, const void* k_t, const void* v_t, const void* q_t, hipStream_t stream) {
+  if (!c) return HYQ_ERR_INVALID;
+  int st = check_shape(&c->shape);
+  if (st) return st;
+  if ((st = check_cache_ptrs(c))) return st;
+  if ((st = check_counters(c))) return st;
+  if (!k_t || !v_t || c->len <= 0) return HYQ_ERR_INVALID;
+  const bool leaves = c->len >= W;
+  if (leaves && c->n_staged >= c->shape.staging_cap) return HYQ_ERR_CAPACITY;
+  hipError_t e = hyq::launch_append(view(c), (const uint16_t*)k_t, (const uint16_t*)v_t, (const uint16_t*)q_t,
+                                    c->len, c->n_staged, c->proxy_head, stream);
+  if (e != hipSuccess) return HYQ_ERR_HIP;
+  c->len += 1;
+  if (leaves) c->n_staged += 1;
+  if (q_t) {
+    c->proxy_head = (c->proxy_head + 1) % c->shape.proxy_cap;
+    if (c->n_proxy < c->shape.proxy_cap) c->n_proxy += 1;
+  }
+  return HYQ_OK;
+}
+
+int hyq_decode_attn(const hyq_cache_t* c, const void* q, float* o, int32_t n_splits, void* ws, size_t ws_bytes,
+                    hipStream_t stream) {
+  if (!c) return HYQ_ERR_INVALID;
+  int st = check_shape(&c->shape);
+  if (st) return st;
+  if ((st = check_cache_ptrs(c))) return st;
+  if ((st = check_counters(c))) return st;
+  if (!q || !o || c->len <= 0 || n_splits < 0 || n_splits > 4096) return HYQ_ERR_INVALID;
+  const int S = n_splits > 0 ? n_splits : auto_splits(c);
+  const size_t need = (size_t)c->shape.batch * c->shape.n_q_heads * S * (D + 2) * sizeof(float);
+  if (!ws || ws_bytes < need) return HYQ_ERR_WORKSPACE;
+  hyq::DecodeParams p;
+  p.k_codes = (const uint8_t*)c->k_codes;
+  p.v_codes = (const uint32_t*)c->v_codes;
+  p.k_sm = (const uint32_t*)c->k_sm;
+  p.v_sm = (const uint32_t*)c->v_sm;
+  p.a_k = (const uint16_t*)c->a_k;
+  p.a_v = (const uint16_t*)c->a_v;
+  p.s_k = (const uint16_t*)c->s_k;
+  p.s_v = (const uint16_t*)c->s_v;
+  p.w_k = (const uint16_t*)c->w_k;
+  p.w_v = (const uint16_t*)c->w_v;
+  p.q = (const uint16_t*)q;
+  p.part = (float*)ws;
+  p.Hkv = c->shape.n_kv_heads;
+  p.G = c->shape.n_q_heads / c->shape.n_kv_heads;
+  p.int4_cap = c->shape.int4_cap;
+  p.anchor_cap = c->shape.anchor_cap;
+  p.staging_cap = c->shape.staging_cap;
+  p.n_int4 = c->n_int4;
+  p.n_anchor = c->n_anchor;
+  p.n_staged = c->n_staged;
+  p.n_win = c->len < W ? c->len : W;
+  p.n_splits = S;
+  hipError_t e = hyq::launch_decode(p, o, c->shape.batch, stream);
+  return e == hipSuccess ? HYQ_OK : HYQ_ERR_HIP;
+}
+
+int hyq_select_vlines(const hyq_shape_t* shape, hyq_cache_t* cache, const void* dense_k, int32_t len,
+                      const void* proxy, int32_t n_proxy, int32_t k, int32_t apply, int32_t* idx_out,
+                      float* scores_out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  (void)shape; (void)cache; (void)dense_k; (void)len; (void)proxy; (void)n_proxy; (void)k; (void)apply;
+  (void)idx_out; (void)scores_out; (void)ws; (void)ws_bytes; (void)stream;
+  return HYQ_ERR_UNSUPPORTED;
+}
+
+int hyq_prefill_attn(const hyq_shape_t* shape, const void* q, const void* k, const void* v, int32_t len,
+                     const int32_t* anchors, int32_t n_anchor, float* o, void* ws, size_t ws_bytes,
+                     hipStream_t stream) {
+  (void)shape; (void)q; (void)k; (void)v; (void)len; (void)anchors; (void)n_anchor; (void)o; (void)ws;
+  (void)ws_bytes; (void)stream;
+  return HYQ_ERR_UNSUPPORTED;
+}
+
+}  // extern "C"

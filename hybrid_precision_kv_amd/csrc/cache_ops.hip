@@ -1,0 +1,253 @@
+// Cache maintenance kernels: Freeze (prefill -> decode organisation) and token append.
+//
+// HyQuant paper ("HyQuant: Hybrid-Precision Quantization for LLM Attention"), Alg. 4: the last
+// W keys become the local window, the vertical-line positions keep bf16, every other position
+// of the non-window prefix is quantized with group size G (here per token, 32 channels, INT4
+// asymmetric with fp16 scale and min); new decode tokens pass through the window and a bf16
+// staging buffer (Alg. 3 segment 3).
+//
+// This file is compiled with -ffp-contract=off: the quantizer's operation order is part of
+// its contract (codes are reproducible bit for bit).
+#include "hyq_common.h"
+#include "hyq_launch.h"
+
+namespace hyq {
+
+namespace {
+
+// Number of anchors a_i (ascending, i = rank) with a_i - i <= s: the INT4 slot s of a Freeze
+// holds position s + that count (slots enumerate the non-anchor prefix in order).
+__device__ inline int slot_to_pos(const int32_t* anc, int n_anchor, int s) {
+  int lo = 0, hi = n_anchor;  // first index with a_i - i > s
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (anc[mid] - mid <= s) lo = mid + 1; else hi = mid;
+  }
+  return s + lo;
+}
+
+// nibble j of a V-code dword -> k-slot e (inverse of kslot_nibble)
+__device__ inline int nibble_kslot(int j) { return ((j & 3) << 1) | (j >> 2); }
+
+// ---------------------------------------------------------------- Freeze: INT4 slots
+__global__ __launch_bounds__(256) void freeze_int4_kernel(CacheView c, const uint16_t* __restrict__ k,
+                                                          const uint16_t* __restrict__ v, int len,
+                                                          const int32_t* __restrict__ anchors, int n_anchor,
+                                                          int n_int4) {
+  __shared__ uint8_t vlds[D][32];
+  const int tile = blockIdx.x, b = blockIdx.z, hkv = blockIdx.y;
+  const size_t hb = (size_t)b * c.Hkv + hkv;
+  const int t = threadIdx.x;
+  const int sl = t >> 3, kv = (t >> 2) & 1, g = t & 3;
+  const int slot = tile * 32 + sl;
+  bool valid = slot < n_int4;
+  const int32_t* anc = anchors ? anchors + hb * (size_t)n_anchor : nullptr;
+  int pos = valid ? slot_to_pos(anc, n_anchor, slot) : 0;
+  if (pos >= len) { valid = false; pos = 0; }  // anchors outside [0, len - W): contract violation
+
+  uint8_t code[32];
+  __half s16 = __float2half(0.f), m16 = __float2half(0.f);
+  if (valid) {
+    const uint16_t* src = (kv ? v : k) + (hb * (size_t)len + pos) * D + 32 * g;
+    float x[32];
+#pragma unroll
+    for (int j = 0; j < 32; j += 8) {
+      const u32x4 w = *(const u32x4*)(src + j);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        x[j + 2 * e] = bf16_bits_to_f32((uint16_t)(w[e] & 0xffff));
+        x[j + 2 * e + 1] = bf16_bits_to_f32((uint16_t)(w[e] >> 16));
+      }
+    }
+    quant_group32(x, code, s16, m16);
+  } else {
+#pragma unroll
+    for (int j = 0; j < 32; ++j) code[j] = 0;
+  }
+  const uint32_t smw = (uint32_t)__half_as_ushort(s16) | ((uint32_t)__half_as_ushort(m16) << 16);
+  if (kv == 0) {
+    u32x4 packed;
+#pragma unroll
+    for (int d4 = 0; d4 < 4; ++d4) {
+      uint32_t w = 0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) w |= (uint32_t)code[8 * d4 + j] << (4 * j);
+      packed[d4] = w;
+    }
+    *(u32x4*)(c.k_codes + (hb * (size_t)c.int4_cap + slot) * 64 + 16 * g) = packed;
+    c.k_sm[hb * (size_t)(c.int4_cap / 16) * 64 + sm_index(slot, g)] = smw;
+    if (g == 0) c.slot_pos[hb * (size_t)c.int4_cap + slot] = valid ? pos : -1;
+  } else {
+    c.v_sm[hb * (size_t)(c.int4_cap / 16) * 64 + sm_index(slot, g)] = smw;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) vlds[32 * g + j][sl] = code[j];
+  }
+  __syncthreads();
+  uint32_t* vtile = c.v_codes + hb * (size_t)(c.int4_cap / 32) * 512 + (size_t)tile * 512;
+  for (int d = t; d < 512; d += 256) {
+    const int i = d >> 5, q = (d >> 3) & 3, r = d & 7;
+    const int ch = 16 * r + i;
+    uint32_t w = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int e = nibble_kslot(j);
+      const int p = 4 * q + (e & 3) + 16 * (e >> 2);
+      w |= (uint32_t)vlds[ch][p] << (4 * j);
+    }
+    vtile[d] = w;
+  }
+}
+
+// ---------------------------------------------------------------- Freeze: bf16 stores
+// mode 0: anchor store (tile u holds anchors 32u..32u+31); mode 1: window ring (tile u holds
+// ring slots 32u..32u+31).  Positions past the count are written as zeros.
+__global__ __launch_bounds__(256) void freeze_bf16_kernel(CacheView c, const uint16_t* __restrict__ k,
+                                                          const uint16_t* __restrict__ v, int len,
+                                                          const int32_t* __restrict__ anchors, int n_anchor,
+                                                          int mode) {
+  __shared__ uint16_t vl[32][D + 8];
+  const int tile = blockIdx.x, b = blockIdx.z, hkv = blockIdx.y;
+  const size_t hb = (size_t)b * c.Hkv + hkv;
+  const int t = threadIdx.x;
+  uint16_t *dk, *dv;
+  size_t slab;
+  if (mode == 0) { slab = (size_t)c.anchor_cap * D; dk = c.a_k + hb * slab; dv = c.a_v + hb * slab; }
+  else { slab = (size_t)WIN * D; dk = c.w_k + hb * slab; dv = c.w_v + hb * slab; }
+  // each thread: one position (t >> 3), 16 channels (t & 7)
+  const int pl = t >> 3, cc = (t & 7) * 16;
+  const int s = tile * 32 + pl;
+  int pos = -1;
+  if (mode == 0) {
+    if (s < n_anchor) pos = anchors[hb * (size_t)n_anchor + s];
+    if (pos >= len) pos = -1;  // contract violation: never read past the prefill buffer
+  } else {
+    if (len >= WIN) pos = (len - WIN) + ((s - len) % WIN + WIN) % WIN;
+    else if (s < len) pos = s;
+  }
+  u32x4 kw0 = {0, 0, 0, 0}, kw1 = {0, 0, 0, 0}, vw0 = {0, 0, 0, 0}, vw1 = {0, 0, 0, 0};
+  if (pos >= 0) {
+    const size_t off = (hb * (size_t)len + pos) * D + cc;
+    kw0 = *(const u32x4*)(k + off);
+    kw1 = *(const u32x4*)(k + off + 8);
+    vw0 = *(const u32x4*)(v + off);
+    vw1 = *(const u32x4*)(v + off + 8);
+  }
+  *(u32x4*)(dk + (size_t)s * D + cc) = kw0;
+  *(u32x4*)(dk + (size_t)s * D + cc + 8) = kw1;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    vl[pl][cc + 2 * e] = (uint16_t)(vw0[e] & 0xffff);
+    vl[pl][cc + 2 * e + 1] = (uint16_t)(vw0[e] >> 16);
+    vl[pl][cc + 8 + 2 * e] = (uint16_t)(vw1[e] & 0xffff);
+    vl[pl][cc + 8 + 2 * e + 1] = (uint16_t)(vw1[e] >> 16);
+  }
+  if (mode == 0 && (t & 7) == 0 && s < c.anchor_cap) c.a_pos[hb * (size_t)c.anchor_cap + s] = pos;
+  __syncthreads();
+  // tile-transposed V: chunk (i, q, r) = 8 bf16 of channel 16r + i at the quad's 8 positions
+  uint16_t* vt = dv + (size_t)tile * 4096;
+  for (int ch = t; ch < 512; ch += 256) {
+    const int i = ch >> 5, q = (ch >> 3) & 3, r = ch & 7;
+    const int chn = 16 * r + i;
+    u32x4 w;
+#pragma unroll
+    for (int e2 = 0; e2 < 4; ++e2) {
+      const int ea = 2 * e2, eb = 2 * e2 + 1;
+      const int pa = 4 * q + (ea & 3) + 16 * (ea >> 2), pb = 4 * q + (eb & 3) + 16 * (eb >> 2);
+      w[e2] = (uint32_t)vl[pa][chn] | ((uint32_t)vl[pb][chn] << 16);
+    }
+    *(u32x4*)(vt + (size_t)ch * 8) = w;
+  }
+}
+
+__global__ void fill_zero_kernel(uint32_t* __restrict__ p, size_t n) {
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) p[i] = 0u;
+}
+
+// proxy ring <- the last n queries of q_tail (slots 0..n-1)
+__global__ void proxy_init_kernel(CacheView c, const uint16_t* __restrict__ q_tail, int n_tail, int n) {
+  const int hq = blockIdx.y, b = blockIdx.z, j = blockIdx.x, ch = threadIdx.x;
+  const int Hq = c.Hkv * c.G;
+  const size_t src = (((size_t)b * Hq + hq) * n_tail + (n_tail - n + j)) * D + ch;
+  const size_t dst = (((size_t)b * Hq + hq) * c.proxy_cap + j) * D + ch;
+  c.proxy_q[dst] = q_tail[src];
+}
+
+// ---------------------------------------------------------------- append
+__global__ __launch_bounds__(128) void append_kernel(CacheView c, const uint16_t* __restrict__ k_t,
+                                                     const uint16_t* __restrict__ v_t,
+                                                     const uint16_t* __restrict__ q_t, int len, int n_staged,
+                                                     int proxy_head) {
+  const int hkv = blockIdx.x, b = blockIdx.y, ch = threadIdx.x;
+  const size_t hb = (size_t)b * c.Hkv + hkv;
+  const int r = len % WIN;
+  uint16_t* wk = c.w_k + hb * (size_t)WIN * D;
+  uint16_t* wv = c.w_v + hb * (size_t)WIN * D;
+  if (len >= WIN) {  // position len - W leaves the window for staging slot n_staged
+    uint16_t* sk = c.s_k + hb * (size_t)c.staging_cap * D;
+    uint16_t* sv = c.s_v + hb * (size_t)c.staging_cap * D;
+    sk[(size_t)n_staged * D + ch] = wk[(size_t)r * D + ch];
+    sv[vbf_index(n_staged, ch)] = wv[vbf_index(r, ch)];
+  }
+  wk[(size_t)r * D + ch] = k_t[hb * D + ch];
+  wv[vbf_index(r, ch)] = v_t[hb * D + ch];
+  if (q_t) {
+    const int Hq = c.Hkv * c.G;
+    for (int j = 0; j < c.G; ++j) {
+      const int hq = hkv * c.G + j;
+      c.proxy_q[(((size_t)b * Hq + hq) * c.proxy_cap + proxy_head) * D + ch] = q_t[((size_t)b * Hq + hq) * D + ch];
+    }
+  }
+}
+
+hipError_t zero_fill(void* p, size_t bytes, hipStream_t stream) {
+  const size_t n = bytes / 4;
+  if (n == 0) return hipSuccess;
+  int blocks = (int)((n + 255) / 256);
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(fill_zero_kernel, dim3(blocks), dim3(256), 0, stream, (uint32_t*)p, n);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_freeze(const CacheView& c, const uint16_t* k, const uint16_t* v, int len,
+                         const int32_t* anchors, int n_anchor, const uint16_t* q_tail, int n_tail,
+                         hipStream_t stream) {
+  hipError_t e;
+  const int P = len > WIN ? len - WIN : 0;
+  const int n_int4 = P - n_anchor;
+  if (n_int4 > 0) {
+    dim3 grid((n_int4 + 31) / 32, c.Hkv, c.B);
+    hipLaunchKernelGGL(freeze_int4_kernel, grid, dim3(256), 0, stream, c, k, v, len, anchors, n_anchor, n_int4);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  if (n_anchor > 0) {
+    dim3 grid((n_anchor + 31) / 32, c.Hkv, c.B);
+    hipLaunchKernelGGL(freeze_bf16_kernel, grid, dim3(256), 0, stream, c, k, v, len, anchors, n_anchor, 0);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  {
+    dim3 grid(WIN / 32, c.Hkv, c.B);
+    hipLaunchKernelGGL(freeze_bf16_kernel, grid, dim3(256), 0, stream, c, k, v, len, anchors, n_anchor, 1);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  const size_t stage_bytes = (size_t)c.B * c.Hkv * c.staging_cap * D * 2;
+  if ((e = zero_fill(c.s_k, stage_bytes, stream)) != hipSuccess) return e;
+  if ((e = zero_fill(c.s_v, stage_bytes, stream)) != hipSuccess) return e;
+  if (q_tail && n_tail > 0) {
+    const int n = n_tail < c.proxy_cap ? n_tail : c.proxy_cap;
+    dim3 grid(n, c.Hkv * c.G, c.B);
+    hipLaunchKernelGGL(proxy_init_kernel, grid, dim3(D), 0, stream, c, q_tail, n_tail, n);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+hipError_t launch_append(const CacheView& c, const uint16_t* k_t, const uint16_t* v_t, const uint16_t* q_t,
+                         int len, int n_staged, int proxy_head, hipStream_t stream) {
+  hipLaunchKernelGGL(append_kernel, dim3(c.Hkv, c.B), dim3(D), 0, stream, c, k_t, v_t, q_t, len, n_staged,
+                     proxy_head);
+  return hipGetLastError();
+}
+
+}  // namespace hyq

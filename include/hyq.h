@@ -1,0 +1,209 @@
+/*
+ * hyq.h -- C ABI of the hybrid-precision KV attention library for AMD MI355X (gfx950).
+ *
+ * The method is HyQuant (arXiv page "HyQuant: Hybrid-Precision Quantization for LLM
+ * Attention", called "the HyQuant paper" below): in decode, most cached positions are held
+ * as asymmetric INT4 (K4V4, one fp16 scale and one fp16 minimum per 32-channel group of a
+ * token), while a small set of "vertical-line" anchor positions and a sliding window of the
+ * most recent 128 positions stay in bf16 (§4.1 Eq. 1-5, §4.3 Eq. 8).  Decode attention
+ * dequantizes INT4 inside one online-softmax pass (§4.3 Eq. 9, Alg. 3).  The prefill
+ * operator runs the bulk of Q.K^T in INT8 and P.V in FP8 with anchors and the window in
+ * bf16, merged in one online softmax (§4.2 Eq. 6-7, Alg. 2).
+ *
+ * General rules for every entry point
+ * -----------------------------------
+ *  - Pointers marked "device" are HIP device pointers owned by the caller; the library
+ *    never allocates, frees or synchronises, and keeps no mutable global state.
+ *  - Work is enqueued asynchronously on the caller's stream; inputs must stay alive until
+ *    the stream has passed the call.  Host structs are read/updated before returning.
+ *  - All checks run on the host before anything is enqueued.  On any error nothing is
+ *    enqueued and the hyq_cache_t is left unchanged.  Device faults surface at the
+ *    caller's next synchronisation.  NaN/Inf inputs are not checked and propagate.
+ *  - bf16 tensors are passed as raw 16-bit patterns.  Head dimension is fixed at 128,
+ *    the channel group at 32 and the window at 128.
+ *  - Q head h belongs to KV head h / (n_q_heads / n_kv_heads) (grouped-query layout).
+ *
+ * Cache memory layout (per (sequence b, KV head h); "head slab" index hb = b*Hkv + h;
+ * every buffer is the concatenation of its head slabs, slab sizes given by
+ * hyq_cache_buffer_bytes).  Tiles hold 32 positions.
+ *
+ *  k_codes  u8  [hb][int4_cap][64]      INT4 K codes, one 64-byte row per slot; byte j holds
+ *                                       channel 2j in the low nibble, 2j+1 in the high nibble.
+ *  v_codes  u32 [hb][int4_cap/32][16][4][8]  INT4 V codes, tile-transposed: the dword
+ *                                       (i, q, r) of a tile holds channel c = 16r + i for the
+ *                                       8 slots s of quad q listed by HYQ_V_NIBBLE below.
+ *  k_sm,v_sm f16 [hb][int4_cap/16][4][16][2]  (scale, min) per (16-slot block, group g,
+ *                                       slot in block): dequant x = scale*code + min.
+ *  slot_pos i32 [hb][int4_cap]          position held by each INT4 slot (-1 for unused).
+ *  a_k, s_k, w_k  bf16 [hb][cap][128]   anchor / staging / window K rows.
+ *  a_v, s_v, w_v  bf16 [hb][cap/32][16][4][8][8]  V, tile-transposed: element
+ *                                       (i, q, r, e) of a tile is channel 16r + i of the
+ *                                       position 4q + (e & 3) + 16*(e >> 2) of the tile.
+ *  a_pos    i32 [hb][anchor_cap]        anchor positions, ascending.
+ *  proxy_q  bf16 [b][n_q_heads][proxy_cap][128]  ring of the last proxy queries.
+ *  The window is a ring: position p sits in window slot p % 128.  Staging slot i holds
+ *  position len - 128 - n_staged + i.
+ *  Inside an INT4 tile, slot s = 4q + (e & 3) + 16*(e >> 2) (q = quad, e = 0..7) is stored in
+ *  nibble HYQ_V_NIBBLE[e] of its (i, q, r) dwords.
+ */
+#ifndef HYQ_H
+#define HYQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define HYQ_HEAD_DIM 128
+#define HYQ_GROUP 32
+#define HYQ_WINDOW 128
+#define HYQ_TILE 32
+#define HYQ_PROXY_CAP 64
+/* nibble index (0..7, 4 bits each, low first) of k-slot e inside a V-code dword */
+#define HYQ_V_NIBBLE_INIT {0, 4, 1, 5, 2, 6, 3, 7}
+
+/* status codes */
+#define HYQ_OK 0
+#define HYQ_ERR_INVALID 1      /* null pointer, bad dimension, inconsistent counters */
+#define HYQ_ERR_UNSUPPORTED 2  /* head_dim != 128, group != 32, window != 128, GQA not in {1,2,4,8,16} */
+#define HYQ_ERR_CAPACITY 3     /* len > capacity, k > anchor_cap or > candidates, staging full */
+#define HYQ_ERR_WORKSPACE 4    /* workspace missing or smaller than hyq_workspace_bytes */
+#define HYQ_ERR_HIP 5          /* a kernel launch failed (hipGetLastError) */
+
+/* operations for hyq_workspace_bytes */
+#define HYQ_OP_DECODE 1
+#define HYQ_OP_SELECT 2
+#define HYQ_OP_PREFILL 3
+
+typedef struct {
+  int32_t batch;        /* sequences */
+  int32_t n_q_heads;    /* Q heads */
+  int32_t n_kv_heads;   /* KV heads; n_q_heads / n_kv_heads in {1, 2, 4, 8, 16} */
+  int32_t head_dim;     /* must be 128 */
+  int32_t group;        /* must be 32 (channels per INT4 scale/min group) */
+  int32_t window;       /* must be 128 */
+  int32_t proxy_cap;    /* must be 64 (proxy-query buffer, HyQuant paper §5.5) */
+  int32_t staging_cap;  /* staging capacity per head, multiple of 32, >= the refresh interval */
+  int32_t int4_cap;     /* INT4 slots per head, multiple of 32 */
+  int32_t anchor_cap;   /* anchor slots per head, multiple of 32 */
+} hyq_shape_t;
+
+typedef struct {
+  hyq_shape_t shape;
+  /* caller-owned device buffers, layouts above */
+  void *k_codes, *v_codes, *k_sm, *v_sm;
+  int32_t *slot_pos;
+  void *a_k, *a_v;
+  int32_t *a_pos;
+  void *s_k, *s_v;
+  void *w_k, *w_v;
+  void *proxy_q;
+  /* host-side counters, identical for every sequence of the batch; updated in place by
+     hyq_quantize_kv, hyq_append_token and hyq_select_vlines(apply=1) */
+  int32_t len;        /* positions cached */
+  int32_t n_int4;     /* INT4 slots in use */
+  int32_t n_anchor;   /* anchors held in bf16 */
+  int32_t n_staged;   /* staged positions (left the window since the last refresh) */
+  int32_t n_proxy;    /* valid proxy queries per Q head (<= proxy_cap) */
+  int32_t proxy_head; /* next proxy ring slot to write */
+} hyq_cache_t;
+
+/* Buffer indices for hyq_cache_buffer_bytes */
+enum {
+  HYQ_BUF_K_CODES = 0, HYQ_BUF_V_CODES, HYQ_BUF_K_SM, HYQ_BUF_V_SM, HYQ_BUF_SLOT_POS,
+  HYQ_BUF_A_K, HYQ_BUF_A_V, HYQ_BUF_A_POS, HYQ_BUF_S_K, HYQ_BUF_S_V, HYQ_BUF_W_K,
+  HYQ_BUF_W_V, HYQ_BUF_PROXY_Q, HYQ_NBUF
+};
+
+/* Human-readable status text (static storage). */
+const char* hyq_status_string(int status);
+
+/* Validates a shape; fills bytes[HYQ_NBUF] with the total size in bytes of each cache
+   buffer (all head slabs).  Host only, no GPU work. */
+int hyq_cache_buffer_bytes(const hyq_shape_t* shape, size_t bytes[HYQ_NBUF]);
+
+/* Workspace bytes an operation needs: op = HYQ_OP_DECODE (len unused; n_splits = the value
+   that will be passed, 0 = automatic), HYQ_OP_SELECT (len = context length), HYQ_OP_PREFILL
+   (len = sequence length).  Returns 0 for an invalid shape. */
+size_t hyq_workspace_bytes(const hyq_shape_t* shape, int op, int32_t len, int32_t n_splits);
+
+/* Freeze: prefill -> decode cache organisation (HyQuant paper Alg. 4).
+   k, v: device bf16 [B][Hkv][len][128] dense prefill keys/values.
+   anchors: device int32 [B][Hkv][n_anchor], ascending per head, inside [0, len - 128);
+            n_anchor may be 0 (pass NULL).  Typically the output of hyq_select_vlines.
+   q_tail:  device bf16 [B][Hq][n_tail][128], the last prefill queries; the last
+            min(n_tail, 64) seed the proxy ring (nullable, then n_tail must be 0).
+   Effect: window ring <- positions [max(0,len-128), len); anchor store <- the anchors (bf16);
+   INT4 slots <- every other position of [0, len-128) in ascending order, quantized per
+   token and 32-channel group (min/max asymmetric, fp16 scale = fp16((max-min)/15), fp16
+   min, codes rint((x-min)/scale) clamped to [0,15]); staging emptied; unused tails zeroed.
+   Counters: len, n_int4 = max(0,len-128) - n_anchor, n_anchor, n_staged = 0, proxy.
+   Errors: INVALID, UNSUPPORTED, CAPACITY (len-128-n_anchor > int4_cap, n_anchor >
+   anchor_cap), HIP. */
+int hyq_quantize_kv(hyq_cache_t* cache, const void* k, const void* v, int32_t len,
+                    const int32_t* anchors, int32_t n_anchor, const void* q_tail, int32_t n_tail,
+                    hipStream_t stream);
+
+/* Append one decode token to every sequence (HyQuant paper Alg. 3 staging segment, Alg. 4
+   staging buffer): position len enters window slot len % 128; when len >= 128 the position
+   it replaces (len - 128) moves to staging slot n_staged.  q_t (nullable) is pushed into the
+   proxy ring.  k_t, v_t: device bf16 [B][Hkv][128]; q_t: device bf16 [B][Hq][128].
+   Counters: len += 1, n_staged += (old len >= 128), proxy ring advanced.
+   Errors: INVALID, CAPACITY (staging full: call hyq_select_vlines with apply = 1), HIP. */
+int hyq_append_token(hyq_cache_t* cache, const void* k_t, const void* v_t, const void* q_t,
+                     hipStream_t stream);
+
+/* Vertical-line selector (HyQuant paper §4.1 Eq. 4-5, Alg. 1; cadence: every 64 decode
+   tokens per the techwalker.com article on HyQuant).
+   For each (b, KV head): rows r = every proxy query of every Q head of the group;
+   p_r = softmax(q_r . k_j / sqrt(128)) over all len keys; S(j) = sum_r p_r(j) for candidate
+   j in [0, len - 128); idx = the k largest S (ties to the lower position), ascending.
+   Dense mode (dense_k != NULL): keys = dense_k, device bf16 [B][Hkv][len][128]; proxy =
+     device bf16 [B][Hq][n_proxy][128]; cache may be NULL; apply must be 0.
+   Cache mode (dense_k == NULL): keys = the cache in its stored precision, proxy = the cache's
+     proxy ring (proxy must be NULL, len and n_proxy are taken from the cache).  With
+     apply = 1 the new set is applied: anchors in the set keep bf16; staged positions in the
+     set become anchors with their bf16 values; INT4 positions in the set become anchors
+     holding bf16(dequantized value); anchors and staged positions not in the set are
+     quantized into INT4 slots; staging is emptied.  Counters: n_anchor = k, n_staged = 0,
+     n_int4 = len - 128 - k.
+   idx_out: device int32 [B][Hkv][k]; scores_out: device f32 [B][Hkv][len - 128] (nullable).
+   k must satisfy 0 <= k <= len - 128 (and <= anchor_cap when apply = 1).
+   ws: device workspace of at least hyq_workspace_bytes(shape, HYQ_OP_SELECT, len, 0) bytes.
+   Errors: INVALID, UNSUPPORTED, CAPACITY, WORKSPACE, HIP. */
+int hyq_select_vlines(const hyq_shape_t* shape, hyq_cache_t* cache, const void* dense_k,
+                      int32_t len, const void* proxy, int32_t n_proxy, int32_t k, int32_t apply,
+                      int32_t* idx_out, float* scores_out, void* ws, size_t ws_bytes,
+                      hipStream_t stream);
+
+/* Decode attention over the hybrid cache (HyQuant paper §4.3 Eq. 8-9, Alg. 3): for every
+   (b, Q head), o = sum_j softmax_j(q . k_j / sqrt(128)) v_j over all len cached positions,
+   INT4 positions dequantized in registers, bf16 anchors, staging and window in the same
+   online softmax; split-K partial states merged by ReduceSoftmax.
+   q: device bf16 [B][Hq][128]; o: device f32 [B][Hq][128].  n_splits: splits per (b, KV
+   head), 0 = automatic.  ws: >= hyq_workspace_bytes(shape, HYQ_OP_DECODE, 0, n_splits).
+   Reads the cache only.  Errors: INVALID, UNSUPPORTED, WORKSPACE, HIP. */
+int hyq_decode_attn(const hyq_cache_t* cache, const void* q, float* o, int32_t n_splits,
+                    void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Hybrid prefill attention (HyQuant paper §4.2 Eq. 6-7, Alg. 2), causal, batch of one
+   sequence per call (shape->batch must be 1).  For query i: keys [i-127, i] and anchors
+   a <= i-128 use bf16 Q.K and bf16 P.V; every other key j <= i-128 uses INT8 Q.K (Q per
+   64-query block, K per 64-key block, symmetric, scale max|x|/127) and FP8 E4M3 P.V (P
+   scaled by 448, V with a per-channel scale max|V[:,c]|/448 over non-anchor keys).  One
+   online softmax, 64-key tiles, order: quantized tiles, anchor tiles, window tiles.
+   q: device bf16 [Hq][len][128]; k, v: device bf16 [Hkv][len][128]; anchors: device int32
+   [Hkv][n_anchor] ascending inside [0, len-128) (nullable when n_anchor = 0);
+   o: device f32 [Hq][len][128].  ws: >= hyq_workspace_bytes(shape, HYQ_OP_PREFILL, len, 0).
+   Errors: INVALID, UNSUPPORTED, WORKSPACE, HIP. */
+int hyq_prefill_attn(const hyq_shape_t* shape, const void* q, const void* k, const void* v,
+                     int32_t len, const int32_t* anchors, int32_t n_anchor, float* o, void* ws,
+                     size_t ws_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* HYQ_H */

@@ -1,0 +1,82 @@
+"""Test-side reader of the documented cache layout (include/hyq.h): turns the device buffers
+of a HybridKVCache into per-position arrays that can be compared with the oracle.
+
+This is a host-side decoder of the byte layout only (no method arithmetic beyond unpacking
+nibbles and reading fp16 pairs)."""
+from __future__ import annotations
+
+import numpy as np
+
+D, W = 128, 128
+KSLOT_NIBBLE = np.array([0, 4, 1, 5, 2, 6, 3, 7])
+
+
+def _tile_pos(p):
+    p = np.asarray(p)
+    q = (p & 15) >> 2
+    e = (p & 3) + 4 * (p >> 4)
+    return q, e
+
+
+def read_cache(cache) -> list:
+    """Per (b, h_kv): dict with int4 {pos: (kcodes[128], ksm[4,2], vcodes[128], vsm[4,2])},
+    anchors {pos: (k bf16[128], v bf16[128])}, staged, window (same), in numpy."""
+    s = cache.shape
+    H = s.batch * s.n_kv_heads
+    ctr = cache.counters()
+    host = {n: t.cpu().numpy() for n, t in cache.buffers.items()}
+    kc = host["k_codes"][: H * s.int4_cap * 64].reshape(H, s.int4_cap, 64)
+    vc = host["v_codes"][: H * s.int4_cap * 64].view(np.uint32).reshape(H, s.int4_cap // 32, 16, 4, 8)
+    ksm = host["k_sm"][: H * s.int4_cap * 16].view(np.float16).reshape(H, s.int4_cap // 16, 4, 16, 2)
+    vsm = host["v_sm"][: H * s.int4_cap * 16].view(np.float16).reshape(H, s.int4_cap // 16, 4, 16, 2)
+    slot_pos = host["slot_pos"][: H * s.int4_cap * 4].view(np.int32).reshape(H, s.int4_cap)
+
+    def bf_rows(name, cap):
+        return host[name][: H * cap * D * 2].view(np.uint16).reshape(H, cap, D)
+
+    def bf_vt(name, cap):
+        t = host[name][: H * cap * D * 2].view(np.uint16).reshape(H, cap // 32, 16, 4, 8, 8)
+        out = np.empty((H, cap, D), np.uint16)
+        p = np.arange(32)
+        q, e = _tile_pos(p)
+        for c in range(D):
+            i, r = c & 15, c >> 4
+            out[:, :, c] = t[:, :, i, q, r, e].reshape(H, cap)
+        return out
+
+    a_k, a_v = bf_rows("a_k", s.anchor_cap), bf_vt("a_v", s.anchor_cap)
+    s_k, s_v = bf_rows("s_k", s.staging_cap), bf_vt("s_v", s.staging_cap)
+    w_k, w_v = bf_rows("w_k", W), bf_vt("w_v", W)
+    a_pos = host["a_pos"][: H * s.anchor_cap * 4].view(np.int32).reshape(H, s.anchor_cap)
+
+    # V codes back to [slot][channel]
+    nsl = s.int4_cap
+    sl = np.arange(nsl)
+    q, e = _tile_pos(sl & 31)
+    shift = 4 * KSLOT_NIBBLE[e]
+    vcodes = np.empty((H, nsl, D), np.uint8)
+    for c in range(D):
+        i, r = c & 15, c >> 4
+        words = vc[:, sl >> 5, i, q, r]
+        vcodes[:, :, c] = (words >> shift) & 0xF
+    kcodes = np.empty((H, nsl, D), np.uint8)
+    kcodes[:, :, 0::2] = kc & 0xF
+    kcodes[:, :, 1::2] = kc >> 4
+    ksm_s = ksm.transpose(0, 1, 3, 2, 4)[:, sl >> 4, sl & 15]  # [H][slot][g][2]
+    vsm_s = vsm.transpose(0, 1, 3, 2, 4)[:, sl >> 4, sl & 15]
+
+    L, n4, na, ns = ctr["len"], ctr["n_int4"], ctr["n_anchor"], ctr["n_staged"]
+    res = []
+    for h in range(H):
+        d = dict(int4={}, anchors={}, staged={}, window={})
+        for t in range(n4):
+            d["int4"][int(slot_pos[h, t])] = (kcodes[h, t], ksm_s[h, t], vcodes[h, t], vsm_s[h, t])
+        for t in range(na):
+            d["anchors"][int(a_pos[h, t])] = (a_k[h, t], a_v[h, t])
+        for t in range(ns):
+            d["staged"][L - W - ns + t] = (s_k[h, t], s_v[h, t])
+        for p in range(max(0, L - W), L):
+            d["window"][p] = (w_k[h, p % W], w_v[h, p % W])
+        d["a_pos"] = a_pos[h, :na].copy()
+        res.append(d)
+    return res

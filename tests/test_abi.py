@@ -1,0 +1,99 @@
+"""Host-only checks of the C ABI: the library loads, exports every symbol include/hyq.h
+declares, sizes its buffers by the documented closed form, and rejects bad arguments before
+enqueuing anything (no GPU needed: every call here fails validation on the host)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+from hybrid_precision_kv_amd import _lib
+from hybrid_precision_kv_amd._lib import HyqCache, HyqShape
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        from hybrid_precision_kv_amd import build
+        build.build_library()
+    return _lib.load()
+
+
+def _shape(**kw):
+    d = dict(batch=2, n_q_heads=8, n_kv_heads=2, head_dim=128, group=32, window=128, proxy_cap=64,
+             staging_cap=64, int4_cap=1024, anchor_cap=64)
+    d.update(kw)
+    return HyqShape(**d)
+
+
+def test_exports_every_declared_symbol(lib):
+    hdr = open(os.path.join(ROOT, "include", "hyq.h")).read()
+    declared = sorted(set(re.findall(r"\b(hyq_[a-z_]+)\s*\(", hdr)))
+    assert declared == sorted(_lib.EXPORTS)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_buffer_sizes_closed_form(lib):
+    s = _shape()
+    out = (C.c_size_t * _lib.HYQ_NBUF)()
+    assert lib.hyq_cache_buffer_bytes(C.byref(s), C.byref(out)) == 0
+    H = 4
+    b = dict(zip(_lib.BUFFERS, list(out)))
+    # 160 bytes per INT4 position: 64 + 64 code bytes, 16 + 16 bytes of fp16 (scale, min) x 4 groups
+    assert b["k_codes"] + b["v_codes"] + b["k_sm"] + b["v_sm"] == H * 1024 * 160
+    assert b["a_k"] + b["a_v"] == H * 64 * 512 and b["w_k"] + b["w_v"] == H * 128 * 512
+    assert b["s_k"] == H * 64 * 256 and b["slot_pos"] == H * 1024 * 4
+    assert b["proxy_q"] == 2 * 8 * 64 * 256  # 64 x H_Q x d x 2 bytes per sequence
+
+
+@pytest.mark.parametrize("kw,status", [(dict(head_dim=64), 2), (dict(group=16), 2), (dict(window=64), 2),
+                                       (dict(n_q_heads=24, n_kv_heads=2), 2), (dict(n_q_heads=7), 1),
+                                       (dict(int4_cap=1000), 1), (dict(staging_cap=0), 1), (dict(batch=0), 1)])
+def test_shape_validation(lib, kw, status):
+    s = _shape(**kw)
+    out = (C.c_size_t * _lib.HYQ_NBUF)()
+    assert lib.hyq_cache_buffer_bytes(C.byref(s), C.byref(out)) == status
+
+
+def _fake_cache(**counters):
+    c = HyqCache()
+    c.shape = _shape()
+    for i, n in enumerate(_lib.BUFFERS):  # never dereferenced: validation fails first
+        setattr(c, n, 0x1000 * (i + 1))
+    c.len, c.n_int4, c.n_anchor, c.n_staged, c.n_proxy, c.proxy_head = 1000, 872 - 43, 43, 0, 0, 0
+    for k, v in counters.items():
+        setattr(c, k, v)
+    return c
+
+
+def test_error_paths_enqueue_nothing(lib):
+    c = _fake_cache()
+    before = bytes(c)
+    # null cache / null tensors
+    assert lib.hyq_decode_attn(None, 1, 1, 0, 1, 1 << 20, None) == 1
+    assert lib.hyq_decode_attn(C.byref(c), None, 1, 0, 1, 1 << 20, None) == 1
+    # workspace too small
+    assert lib.hyq_decode_attn(C.byref(c), 0x10, 0x20, 4, 0x30, 16, None) == 4
+    assert lib.hyq_decode_attn(C.byref(c), 0x10, 0x20, 4, None, 1 << 30, None) == 4
+    # inconsistent counters
+    bad = _fake_cache(n_int4=5)
+    assert lib.hyq_decode_attn(C.byref(bad), 0x10, 0x20, 4, 0x30, 1 << 30, None) == 1
+    # staging full
+    full = _fake_cache(len=1000 + 64, n_staged=64)
+    assert lib.hyq_append_token(C.byref(full), 0x10, 0x20, None, None) == 3
+    # too many anchors for the candidates / capacity
+    assert lib.hyq_quantize_kv(C.byref(c), 0x10, 0x20, 200, 0x30, 73, None, 0, None) == 3
+    assert lib.hyq_quantize_kv(C.byref(c), 0x10, 0x20, 2000, 0x30, 65, None, 0, None) == 3
+    assert lib.hyq_quantize_kv(C.byref(c), 0x10, 0x20, 2000, None, 5, None, 0, None) == 1
+    assert bytes(c) == before  # host struct unchanged on error
+    assert lib.hyq_status_string(4) == b"workspace missing or too small"
+
+
+def test_workspace_sizes(lib):
+    s = _shape()
+    assert lib.hyq_workspace_bytes(C.byref(s), _lib.HYQ_OP_DECODE, 0, 8) == 2 * 8 * 8 * 130 * 4
+    bad = _shape(head_dim=64)
+    assert lib.hyq_workspace_bytes(C.byref(bad), _lib.HYQ_OP_DECODE, 0, 8) == 0

@@ -1,0 +1,165 @@
+"""GPU parity of Freeze, append and decode attention against the oracle (through the C ABI).
+
+Bar: INT4 codes, fp16 scale/min and anchor sets bit-exact; fp32 outputs within 2e-3 max-abs
+and 1e-3 relative L2 of the oracle's fp64 decode over the same stored cache."""
+import numpy as np
+import pytest
+import torch
+
+from hybrid_precision_kv_amd import api as hq
+from hybrid_precision_kv_amd import synth
+from oracle import attention as att
+from oracle import numerics as nm
+from oracle import policy as pol
+from tests.gpu_layout import read_cache
+
+pytestmark = pytest.mark.gpu
+
+MAX_ABS, REL_L2 = 2e-3, 1e-3
+
+
+def dev(a: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to("cuda").view(torch.bfloat16)
+
+
+class Pair:
+    """The same seeded workload on the GPU cache and in per-head oracle caches."""
+
+    def __init__(self, seed, B, Hkv, G, L, n_steps=0, pct=5, staging_cap=64, max_len=None):
+        self.B, self.Hkv, self.G, self.L = B, Hkv, G, L
+        print(f"[case] seed={seed} B={B} Hkv={Hkv} G={G} L={L} steps={n_steps}", flush=True)
+        self.d = synth.gen_batch(seed, B, Hkv, G, L, n_proxy=64, n_steps=n_steps)
+        k = pol.k_rule(L, pct_num=pct)
+        self.refs = []
+        anchors = np.zeros((B, Hkv, max(k, 1)), np.int32)
+        for b in range(B):
+            for h in range(Hkv):
+                prox = self.d["proxy"][b, h * G:(h + 1) * G]
+                A, _ = pol.select_dense(self.d["K"][b, h], prox, pct_num=pct)
+                anchors[b, h, :k] = A
+                r = pol.HybridCacheRef(g=G)
+                r.freeze(self.d["K"][b, h], self.d["V"][b, h], A, prox)
+                self.refs.append(r)
+        shape = hq.Shape.for_context(B, Hkv * G, Hkv, max_len or (L + n_steps), pct, staging_cap)
+        self.cache = hq.HybridKVCache(shape)
+        hq.quantize_kv(self.cache, dev(self.d["K"]), dev(self.d["V"]),
+                       torch.from_numpy(anchors[..., :k].copy()).cuda() if k else None, dev(self.d["proxy"]))
+        self.step = 0
+
+    def append(self):
+        t = self.step
+        k = self.d["new_k"][:, :, t]
+        v = self.d["new_v"][:, :, t]
+        q = self.d["new_q"][:, :, t]
+        hq.append_token(self.cache, dev(k), dev(v), dev(q))
+        for b in range(self.B):
+            for h in range(self.Hkv):
+                self.refs[b * self.Hkv + h].append(k[b, h], v[b, h], q[b, h * self.G:(h + 1) * self.G])
+        self.step += 1
+        return q
+
+    def decode_check(self, q_bits, n_splits=0):
+        o = hq.decode_attn(self.cache, dev(q_bits), n_splits).cpu().numpy()
+        ref = np.empty_like(o)
+        for b in range(self.B):
+            for h in range(self.Hkv):
+                Kh, Vh = self.refs[b * self.Hkv + h].stored_kv()
+                qf = nm.bf16_to_f32(q_bits[b, h * self.G:(h + 1) * self.G])
+                ref[b, h * self.G:(h + 1) * self.G] = att.decode_ref(qf, Kh, Vh)
+        err = np.abs(o - ref).max()
+        rel = np.linalg.norm(o - ref) / np.linalg.norm(ref)
+        assert np.all(np.isfinite(o)), "non-finite output"
+        assert err <= MAX_ABS and rel <= REL_L2, f"max-abs {err:.3g} rel-L2 {rel:.3g} (splits={n_splits})"
+        return err, rel
+
+    def codes_check(self):
+        got = read_cache(self.cache)
+        for hb, r in enumerate(self.refs):
+            g = got[hb]
+            cnt = r.counts()
+            assert len(g["int4"]) == cnt["int4"] and len(g["anchors"]) == cnt["anchor"]
+            assert len(g["staged"]) == cnt["staged"] and len(g["window"]) == cnt["win"]
+            assert np.array_equal(np.sort(g["a_pos"]), r.anchors())
+            for pos, (kc, ksm, vc, vsm) in g["int4"].items():
+                assert r.kind[pos] == pol.INT4
+                assert np.array_equal(kc, r.kc[pos]) and np.array_equal(vc, r.vc[pos]), f"codes @ {pos}"
+                assert np.array_equal(ksm[:, 0].view(np.uint16), r.ks[pos].view(np.uint16))
+                assert np.array_equal(ksm[:, 1].view(np.uint16), r.km[pos].view(np.uint16))
+                assert np.array_equal(vsm[:, 0].view(np.uint16), r.vs[pos].view(np.uint16))
+                assert np.array_equal(vsm[:, 1].view(np.uint16), r.vm[pos].view(np.uint16))
+            for kind in ("anchors", "staged", "window"):
+                for pos, (kb, vb) in g[kind].items():
+                    assert np.array_equal(kb, r.kb[pos]) and np.array_equal(vb, r.vb[pos]), f"{kind} @ {pos}"
+
+
+def test_tiny_freeze_codes_and_one_decode_step():
+    """1 sequence, 1 KV head, GQA 4, L = 1024: Freeze with the top 52 anchors, one step."""
+    p = Pair(1001, 1, 1, 4, 1024, n_steps=1)
+    p.codes_check()
+    q = p.append()
+    p.codes_check()
+    p.decode_check(q)
+    for s in (1, 2, 5):
+        p.decode_check(q, n_splits=s)
+
+
+def test_ragged_multi_tile_and_split_invariance():
+    p = Pair(77, 2, 2, 4, 3001, n_steps=3)
+    p.codes_check()
+    for _ in range(3):
+        q = p.append()
+    outs = []
+    for s in (1, 3, 7, 0):
+        outs.append(p.decode_check(q, n_splits=s))
+    p.codes_check()
+
+
+@pytest.mark.parametrize("G", [1, 2, 8, 16])
+def test_gqa_factors(G):
+    p = Pair(300 + G, 1, 2, G, 700, n_steps=1)
+    q = p.append()
+    p.decode_check(q)
+
+
+@pytest.mark.parametrize("L", [1, 50, 127, 128, 129, 160, 161])
+def test_edge_lengths(L):
+    p = Pair(500 + L, 1, 2, 4, L, n_steps=2)
+    p.codes_check()
+    q = p.append()
+    p.decode_check(q)
+    q = p.append()
+    p.codes_check()
+    p.decode_check(q, n_splits=3)
+
+
+def test_staging_fills_then_capacity_error():
+    p = Pair(900, 1, 2, 4, 600, n_steps=65)
+    for t in range(64):
+        q = p.append()
+        if t % 16 == 15:
+            p.decode_check(q)
+    p.codes_check()
+    assert p.cache.n_staged == 64
+    before = p.cache.counters()
+    with pytest.raises(hq._lib.HyqError) as ei:
+        hq.append_token(p.cache, dev(p.d["new_k"][:, :, 64]), dev(p.d["new_v"][:, :, 64]))
+    assert ei.value.status == 3 and p.cache.counters() == before
+
+
+def test_snapshot_restore_reproduces_outputs():
+    p = Pair(901, 1, 2, 4, 800, n_steps=4)
+    q = p.append()
+    snap = p.cache.snapshot()
+    o1 = hq.decode_attn(p.cache, dev(q)).clone()
+    q2 = p.append()
+    p.cache.restore(snap)
+    o2 = hq.decode_attn(p.cache, dev(q)).clone()
+    assert torch.equal(o1, o2)
+
+
+def test_decode_deterministic():
+    p = Pair(902, 2, 2, 4, 2000, n_steps=1)
+    q = p.append()
+    a = hq.decode_attn(p.cache, dev(q)).clone()
+    b = hq.decode_attn(p.cache, dev(q)).clone()
+    assert torch.equal(a, b)
