@@ -11,9 +11,8 @@ HYQ_OK = 0
 STATUS = {0: "HYQ_OK", 1: "HYQ_ERR_INVALID", 2: "HYQ_ERR_UNSUPPORTED", 3: "HYQ_ERR_CAPACITY",
           4: "HYQ_ERR_WORKSPACE", 5: "HYQ_ERR_HIP"}
 HYQ_OP_DECODE, HYQ_OP_SELECT, HYQ_OP_PREFILL = 1, 2, 3
-HYQ_NBUF = 13
-BUFFERS = ["k_codes", "v_codes", "k_sm", "v_sm", "slot_pos", "a_k", "a_v", "a_pos", "s_k", "s_v",
-           "w_k", "w_v", "proxy_q"]
+HYQ_NBUF = 10
+BUFFERS = ["int4", "slot_pos", "a_k", "a_v", "a_pos", "s_k", "s_v", "w_k", "w_v", "proxy_q"]
 
 # every symbol include/hyq.h declares
 EXPORTS = ["hyq_status_string", "hyq_cache_buffer_bytes", "hyq_workspace_bytes", "hyq_quantize_kv",

@@ -174,9 +174,16 @@ class _Workspace:
 _ws = _Workspace()
 
 
+def decode_workspace(shape: Shape, n_splits: int = 0, device="cuda") -> torch.Tensor:
+    """A decode workspace for ``n_splits`` splits (0 = automatic)."""
+    return torch.empty(max(workspace_bytes(shape, _lib.HYQ_OP_DECODE, 0, n_splits), 256), dtype=torch.uint8,
+                       device=device)
+
+
 def decode_attn(cache: HybridKVCache, q: torch.Tensor, n_splits: int = 0, out: torch.Tensor | None = None,
                 ws: torch.Tensor | None = None) -> torch.Tensor:
-    """o = softmax(q K^T / sqrt(128)) V over the hybrid cache (hyq_decode_attn); fp32 out."""
+    """o = softmax(q K^T / sqrt(128)) V over the hybrid cache (hyq_decode_attn); fp32 out.
+    ``ws`` (optional) must come from ``decode_workspace``."""
     s = cache.shape
     _bf16(q, (s.batch, s.n_q_heads, D), "q")
     if out is None:

@@ -28,7 +28,7 @@ int check_shape(const hyq_shape_t* s) {
 size_t nheads(const hyq_shape_t* s) { return (size_t)s->batch * s->n_kv_heads; }
 
 int check_cache_ptrs(const hyq_cache_t* c) {
-  if (!c->k_codes || !c->v_codes || !c->k_sm || !c->v_sm || !c->slot_pos || !c->a_k || !c->a_v || !c->a_pos ||
+  if (!c->int4 || !c->slot_pos || !c->a_k || !c->a_v || !c->a_pos ||
       !c->s_k || !c->s_v || !c->w_k || !c->w_v || !c->proxy_q)
     return HYQ_ERR_INVALID;
   return HYQ_OK;
@@ -36,10 +36,7 @@ int check_cache_ptrs(const hyq_cache_t* c) {
 
 hyq::CacheView view(const hyq_cache_t* c) {
   hyq::CacheView v;
-  v.k_codes = (uint8_t*)c->k_codes;
-  v.v_codes = (uint32_t*)c->v_codes;
-  v.k_sm = (uint32_t*)c->k_sm;
-  v.v_sm = (uint32_t*)c->v_sm;
+  v.int4 = (uint8_t*)c->int4;
   v.slot_pos = c->slot_pos;
   v.a_k = (uint16_t*)c->a_k;
   v.a_v = (uint16_t*)c->a_v;
@@ -75,7 +72,7 @@ int auto_splits(const hyq_cache_t* c) {
   const int G = c->shape.n_q_heads / c->shape.n_kv_heads;
   const long units = (long)nheads(&c->shape) * ((G + 3) / 4);
   const long tiles = (c->n_int4 + 31) / 32 + 3 * ((c->n_anchor + 31) / 32 + (c->n_staged + 31) / 32 + 4);
-  long s = (2048 + units - 1) / units;          // aim for ~2048 workgroups
+  long s = (1024 + units - 1) / units;          // aim for ~1024 workgroups (4 per CU)
   const long by_work = (tiles + 15) / 16;        // >= ~4 tiles per wave
   if (s > by_work) s = by_work;
   if (s < 1) s = 1;
@@ -104,10 +101,7 @@ int hyq_cache_buffer_bytes(const hyq_shape_t* s, size_t bytes[HYQ_NBUF]) {
   if (st) return st;
   if (!bytes) return HYQ_ERR_INVALID;
   const size_t H = nheads(s);
-  bytes[HYQ_BUF_K_CODES] = H * s->int4_cap * 64;
-  bytes[HYQ_BUF_V_CODES] = H * s->int4_cap * 64;
-  bytes[HYQ_BUF_K_SM] = H * s->int4_cap * 16;
-  bytes[HYQ_BUF_V_SM] = H * s->int4_cap * 16;
+  bytes[HYQ_BUF_INT4] = H * s->int4_cap * 160;  // 5120-byte record per 32-slot tile
   bytes[HYQ_BUF_SLOT_POS] = H * s->int4_cap * 4;
   bytes[HYQ_BUF_A_K] = H * s->anchor_cap * D * 2;
   bytes[HYQ_BUF_A_V] = H * s->anchor_cap * D * 2;
@@ -189,10 +183,7 @@ int hyq_decode_attn(const hyq_cache_t* c, const void* q, float* o, int32_t n_spl
   const size_t need = (size_t)c->shape.batch * c->shape.n_q_heads * S * (D + 2) * sizeof(float);
   if (!ws || ws_bytes < need) return HYQ_ERR_WORKSPACE;
   hyq::DecodeParams p;
-  p.k_codes = (const uint8_t*)c->k_codes;
-  p.v_codes = (const uint32_t*)c->v_codes;
-  p.k_sm = (const uint32_t*)c->k_sm;
-  p.v_sm = (const uint32_t*)c->v_sm;
+  p.int4 = (const uint8_t*)c->int4;
   p.a_k = (const uint16_t*)c->a_k;
   p.a_v = (const uint16_t*)c->a_v;
   p.s_k = (const uint16_t*)c->s_k;
@@ -201,6 +192,8 @@ int hyq_decode_attn(const hyq_cache_t* c, const void* q, float* o, int32_t n_spl
   p.w_v = (const uint16_t*)c->w_v;
   p.q = (const uint16_t*)q;
   p.part = (float*)ws;
+  p.o = o;
+  p.B = c->shape.batch;
   p.Hkv = c->shape.n_kv_heads;
   p.G = c->shape.n_q_heads / c->shape.n_kv_heads;
   p.int4_cap = c->shape.int4_cap;
@@ -211,7 +204,7 @@ int hyq_decode_attn(const hyq_cache_t* c, const void* q, float* o, int32_t n_spl
   p.n_staged = c->n_staged;
   p.n_win = c->len < W ? c->len : W;
   p.n_splits = S;
-  hipError_t e = hyq::launch_decode(p, o, c->shape.batch, stream);
+  hipError_t e = hyq::launch_decode(p, stream);
   return e == hipSuccess ? HYQ_OK : HYQ_ERR_HIP;
 }
 

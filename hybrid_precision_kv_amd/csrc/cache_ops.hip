@@ -42,6 +42,7 @@ __global__ __launch_bounds__(256) void freeze_int4_kernel(CacheView c, const uin
   const int slot = tile * 32 + sl;
   bool valid = slot < n_int4;
   const int32_t* anc = anchors ? anchors + hb * (size_t)n_anchor : nullptr;
+  uint8_t* slab = c.int4 + hb * (size_t)c.int4_cap * 160;
   int pos = valid ? slot_to_pos(anc, n_anchor, slot) : 0;
   if (pos >= len) { valid = false; pos = 0; }  // anchors outside [0, len - W): contract violation
 
@@ -74,18 +75,18 @@ __global__ __launch_bounds__(256) void freeze_int4_kernel(CacheView c, const uin
       for (int j = 0; j < 8; ++j) w |= (uint32_t)code[8 * d4 + j] << (4 * j);
       packed[d4] = w;
     }
-    *(u32x4*)(c.k_codes + (hb * (size_t)c.int4_cap + slot) * 64 + 16 * g) = packed;
-    c.k_sm[hb * (size_t)(c.int4_cap / 16) * 64 + sm_index(slot, g)] = smw;
+    *(u32x4*)(slab + kcode_chunk(slot, g)) = packed;
+    *(uint32_t*)(slab + ksm_byte(slot, g)) = smw;
     if (g == 0) c.slot_pos[hb * (size_t)c.int4_cap + slot] = valid ? pos : -1;
   } else {
-    c.v_sm[hb * (size_t)(c.int4_cap / 16) * 64 + sm_index(slot, g)] = smw;
+    *(uint32_t*)(slab + vsm_byte(slot, g)) = smw;
 #pragma unroll
     for (int j = 0; j < 32; ++j) vlds[32 * g + j][sl] = code[j];
   }
   __syncthreads();
-  uint32_t* vtile = c.v_codes + hb * (size_t)(c.int4_cap / 32) * 512 + (size_t)tile * 512;
-  for (int d = t; d < 512; d += 256) {
-    const int i = d >> 5, q = (d >> 3) & 3, r = d & 7;
+  uint32_t* vtile = (uint32_t*)(slab + (size_t)tile * T4_BYTES + T4_VC);
+  for (int d = t; d < 512; d += 256) {  // d = vcode_dword_in_tile(p, ch) for the quad's slots
+    const int l = (d & 255) >> 2, q = l >> 4, i = l & 15, r = 4 * (d >> 8) + (d & 3);
     const int ch = 16 * r + i;
     uint32_t w = 0;
 #pragma unroll
@@ -132,8 +133,8 @@ __global__ __launch_bounds__(256) void freeze_bf16_kernel(CacheView c, const uin
     vw0 = *(const u32x4*)(v + off);
     vw1 = *(const u32x4*)(v + off + 8);
   }
-  *(u32x4*)(dk + (size_t)s * D + cc) = kw0;
-  *(u32x4*)(dk + (size_t)s * D + cc + 8) = kw1;
+  *(u32x4*)(dk + kbf_index(s, cc)) = kw0;
+  *(u32x4*)(dk + kbf_index(s, cc + 8)) = kw1;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     vl[pl][cc + 2 * e] = (uint16_t)(vw0[e] & 0xffff);
@@ -143,10 +144,10 @@ __global__ __launch_bounds__(256) void freeze_bf16_kernel(CacheView c, const uin
   }
   if (mode == 0 && (t & 7) == 0 && s < c.anchor_cap) c.a_pos[hb * (size_t)c.anchor_cap + s] = pos;
   __syncthreads();
-  // tile-transposed V: chunk (i, q, r) = 8 bf16 of channel 16r + i at the quad's 8 positions
+  // tile-transposed V: chunk (r, q, i) = 8 bf16 of channel 16r + i at the quad's 8 positions
   uint16_t* vt = dv + (size_t)tile * 4096;
   for (int ch = t; ch < 512; ch += 256) {
-    const int i = ch >> 5, q = (ch >> 3) & 3, r = ch & 7;
+    const int r = ch >> 6, q = (ch >> 4) & 3, i = ch & 15;
     const int chn = 16 * r + i;
     u32x4 w;
 #pragma unroll
@@ -185,10 +186,10 @@ __global__ __launch_bounds__(128) void append_kernel(CacheView c, const uint16_t
   if (len >= WIN) {  // position len - W leaves the window for staging slot n_staged
     uint16_t* sk = c.s_k + hb * (size_t)c.staging_cap * D;
     uint16_t* sv = c.s_v + hb * (size_t)c.staging_cap * D;
-    sk[(size_t)n_staged * D + ch] = wk[(size_t)r * D + ch];
+    sk[kbf_index(n_staged, ch)] = wk[kbf_index(r, ch)];
     sv[vbf_index(n_staged, ch)] = wv[vbf_index(r, ch)];
   }
-  wk[(size_t)r * D + ch] = k_t[hb * D + ch];
+  wk[kbf_index(r, ch)] = k_t[hb * D + ch];
   wv[vbf_index(r, ch)] = v_t[hb * D + ch];
   if (q_t) {
     const int Hq = c.Hkv * c.G;

@@ -10,15 +10,20 @@
 //    the KV group spread over the 16 MFMA columns as (head, channel group) pairs: column
 //    4*h + g carries q[h] restricted to group g, so the MFMA returns per-group partial dots and
 //    every lane owns a distinct (head, group).  INT4 codes enter as f16 *subnormals*
-//    (bits 0x000c == c * 2^-24, exact), one AND per code pair.  The per-group scale and min are
-//    applied in fp32 afterwards: q.k = sum_g s_g * (q_g . code_g) + m_g * sum(q_g).
+//    (bits 0x000c == c * 2^-24, exact): 8 codes become 8 MFMA operands with one shift and four
+//    masks (two of the four pairs come out multiplied by 16; the other operand carries 1/16 on
+//    those k-slots).  The per-group scale and min are applied in fp32 afterwards:
+//    q.k = sum_g s_g * (q_g . code_g) + m_g * sum(q_g).
 //  * Sum over the 4 groups with two DPP quad permutes; max across the tile with two lane swaps.
-//  * P.V on the same MFMA: A = V codes of 16 channels x 8 positions per lane, read from a
-//    tile-transposed layout so one dword is one MFMA operand pair set; B = P' = p * s_V (the
-//    MFMA output layout of the K product is exactly the B layout needed here), split into
+//  * P.V on the same MFMA: A = V codes of 16 channels x 8 positions per lane, B = P' = p * s_V
+//    (the MFMA output layout of the K product is exactly the B layout needed here), split into
 //    f16 hi + lo parts so the weights keep ~22 bits.  The V min enters as sum p * m_V.
-//  * bf16 tiles use the bf16 MFMA with the same softmax state.
-//  * 4 waves per workgroup merge their states in LDS; a second tiny kernel merges splits.
+//  * bf16 tiles (anchors, staging, window) use the bf16 MFMA with the same softmax state.
+//  * Every load is a coalesced 1 KB read of one 5 KB tile record (layouts in hyq_common.h); the
+//    next INT4 tile is loaded while the current one is computed (two register sets).  Worker w
+//    of a head takes tiles w, w + NW, ... so the head's workers sweep its records together.
+//  * 4 waves per workgroup merge their states in LDS and write one record per split; a second
+//    small launch merges the records.
 #include "hyq_common.h"
 #include "hyq_launch.h"
 
@@ -28,59 +33,122 @@ namespace {
 
 constexpr int WAVES = 4;
 constexpr float LOG2E = 1.4426950408889634f;
-constexpr float PSCALE = 256.0f;         // P' = p * s_V * PSCALE keeps f16 weights normal
-constexpr float ACC_SCALE = 65536.0f;    // 2^24 / PSCALE: INT4 accumulators -> true scale
+constexpr float PSCALE = 256.0f;              // P' = p * s_V * PSCALE keeps f16 weights normal
+constexpr float ACC_SCALE = 65536.0f;         // 2^24 / PSCALE: INT4 accumulators -> true scale
 constexpr float BF_PSCALE = 1.0f / 65536.0f;  // bf16 tiles feed p * PSCALE * 2^-24
-constexpr uint32_t NIB = 0x000F000Fu;
 
+// 8 INT4 codes (one dword) -> 8 f16 MFMA operands (subnormal bit patterns).  Element order:
+// nibbles 0,4 | 1,5 (x16) | 2,6 | 3,7 (x16).
 __device__ inline f16x8 codes_to_f16(uint32_t x) {
+  const uint32_t y = x >> 8;
   u32x4 a;
-  a[0] = x & NIB;
-  a[1] = (x >> 4) & NIB;
-  a[2] = (x >> 8) & NIB;
-  a[3] = (x >> 12) & NIB;
+  a[0] = x & 0x000F000Fu;
+  a[1] = x & 0x00F000F0u;
+  a[2] = y & 0x000F000Fu;
+  a[3] = y & 0x00F000F0u;
   return __builtin_bit_cast(f16x8, a);
 }
 __device__ inline float half_lo(uint32_t v) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(v & 0xffff)); }
 __device__ inline float half_hi(uint32_t v) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(v >> 16)); }
-
-// maps a cut point of the weighted work sequence (INT4 tiles weigh 5, bf16 tiles 16 --
-// their byte ratio) to (INT4 tile index, bf16 tile index)
-__device__ inline void work_cut(long x, int T4, int TB, int& i, int& u) {
-  const long w4 = 5L * T4;
-  if (x <= w4) { i = (int)((x + 2) / 5); u = 0; }
-  else { i = T4; u = (int)((x - w4 + 8) / 16); if (u > TB) u = TB; }
-  if (i > T4) i = T4;
-}
 
 struct WaveState {
   float m, l, mt;
   f32x4 acc[8];
 };
 
+struct Int4Tile {
+  u32x4 kc0, kc1, vc0, vc1, ks0, ks1, vs0, vs1;
+};
+
+// all loads of one 32-slot INT4 tile record for this lane; every one is a coalesced read of the
+// same 5 KB record
+__device__ inline void load_int4_tile(Int4Tile& x, const uint8_t* slab, int t, uint32_t lane16, uint32_t smoff) {
+  const uint8_t* rec = slab + (size_t)t * T4_BYTES;
+  x.kc0 = *(const u32x4*)(rec + lane16);
+  x.kc1 = *(const u32x4*)(rec + 1024 + lane16);
+  x.vc0 = *(const u32x4*)(rec + T4_VC + lane16);
+  x.vc1 = *(const u32x4*)(rec + T4_VC + 1024 + lane16);
+  x.ks0 = *(const u32x4*)(rec + T4_KSM + smoff);
+  x.ks1 = *(const u32x4*)(rec + T4_KSM + 256 + smoff);
+  x.vs0 = *(const u32x4*)(rec + T4_VSM + smoff);
+  x.vs1 = *(const u32x4*)(rec + T4_VSM + 256 + smoff);
+}
+
 // online-softmax update for one tile; sc[8] are log2-domain scores (-inf = masked)
 __device__ inline void tile_softmax(WaveState& st, const float (&sc)[8], float (&pv)[8]) {
-  float tmax = sc[0];
-#pragma unroll
-  for (int j = 1; j < 8; ++j) tmax = fmaxf(tmax, sc[j]);
+  float tmax = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])), fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
   tmax = fmaxf(tmax, shfl_xor_f(tmax, 16));
   tmax = fmaxf(tmax, shfl_xor_f(tmax, 32));
-  const float m_new = fmaxf(st.m, tmax);
-  if (m_new > st.m) {
-    const float c = __builtin_amdgcn_exp2f(st.m - m_new);
+  if (tmax > st.m) {  // rescale only when the running max grows
+    const float c = __builtin_amdgcn_exp2f(st.m - tmax);
     st.l *= c;
     st.mt *= c;
 #pragma unroll
     for (int r = 0; r < 8; ++r) st.acc[r] *= c;
-    st.m = m_new;
+    st.m = tmax;
   }
-  const bool live = st.m != -INFINITY;
+  const float mref = st.m == -INFINITY ? 0.f : st.m;  // all masked so far: every p is 0
 #pragma unroll
-  for (int j = 0; j < 8; ++j) pv[j] = live ? __builtin_amdgcn_exp2f(sc[j] - st.m) : 0.0f;
-  float ls = 0.f;
+  for (int j = 0; j < 8; ++j) pv[j] = __builtin_amdgcn_exp2f(sc[j] - mref);
+  st.l += ((pv[0] + pv[1]) + (pv[2] + pv[3])) + ((pv[4] + pv[5]) + (pv[6] + pv[7]));
+}
+
+template <bool MASK>
+__device__ inline void int4_tile(WaveState& st, const Int4Tile& x, const f16x8 (&bq)[4], float qsum24, float c_int4,
+                                 int base, int n_int4, int q4) {
+  f32x4 S0 = {0.f, 0.f, 0.f, 0.f}, S1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int j = 0; j < 8; ++j) ls += pv[j];
-  st.l += ls;
+  for (int tt = 0; tt < 4; ++tt) {
+    S0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(codes_to_f16(x.kc0[tt]), bq[tt], S0, 0, 0, 0);
+    S1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(codes_to_f16(x.kc1[tt]), bq[tt], S1, 0, 0, 0);
+  }
+  float sc[8];
+  bool valid[8];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    float v0 = fmaf(half_lo(x.ks0[r]), S0[r], half_hi(x.ks0[r]) * qsum24);
+    float v1 = fmaf(half_lo(x.ks1[r]), S1[r], half_hi(x.ks1[r]) * qsum24);
+    v0 += dpp_quad_xor1(v0);
+    v1 += dpp_quad_xor1(v1);
+    v0 += dpp_quad_xor2(v0);
+    v1 += dpp_quad_xor2(v1);
+    sc[r] = v0 * c_int4;
+    sc[4 + r] = v1 * c_int4;
+    if (MASK) {
+      valid[r] = base + 4 * q4 + r < n_int4;
+      valid[4 + r] = base + 16 + 4 * q4 + r < n_int4;
+      sc[r] = valid[r] ? sc[r] : -INFINITY;
+      sc[4 + r] = valid[4 + r] ? sc[4 + r] : -INFINITY;
+    }
+  }
+  float pv[8];
+  tile_softmax(st, sc, pv);
+  f16x8 bhi, blo;
+  float mt = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const uint32_t smv = j < 4 ? x.vs0[j] : x.vs1[j - 4];
+    const float pj = pv[j];
+    // k-slots 2,3,6,7 meet codes multiplied by 16 (see codes_to_f16)
+    float pp = pj * half_lo(smv) * ((j & 2) ? PSCALE * 0.0625f : PSCALE);
+    float mm = pj * half_hi(smv);
+    if (MASK) {  // unused slots may hold any scale/min bits: keep them out entirely
+      pp = valid[j] ? pp : 0.f;
+      mm = valid[j] ? mm : 0.f;
+    }
+    mt += mm;
+    const _Float16 h = (_Float16)pp;
+    bhi[j] = h;
+    blo[j] = (_Float16)(pp - (float)h);
+  }
+  st.mt += mt;
+  f16x8 a[8];
+#pragma unroll
+  for (int rr = 0; rr < 8; ++rr) a[rr] = codes_to_f16(rr < 4 ? x.vc0[rr] : x.vc1[rr - 4]);
+#pragma unroll
+  for (int rr = 0; rr < 8; ++rr) st.acc[rr] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[rr], bhi, st.acc[rr], 0, 0, 0);
+#pragma unroll
+  for (int rr = 0; rr < 8; ++rr) st.acc[rr] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[rr], blo, st.acc[rr], 0, 0, 0);
 }
 
 __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
@@ -95,27 +163,45 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
   const size_t hb = (size_t)b * p.Hkv + hkv;
   const int Hq = p.Hkv * p.G;
 
-  // ---- B operands: q restricted to this lane's column group (zero elsewhere)
-  f16x8 bq4[4];
-  bf16x8 bqb[4];
-  float qsum = 0.f;
+  // ---- q of the (up to 4) Q heads of this head block, staged once through LDS
+  __shared__ uint32_t q_lds[4][D / 2];
   {
-    const uint16_t* qv = p.q + ((size_t)b * Hq + (size_t)hkv * p.G + (head_ok ? head : 0)) * D;
-    const bool use = head_ok && (g == q4);
+    const int h2 = threadIdx.x >> 6, cp = threadIdx.x & 63;  // 256 threads x 2 channels
+    const int hd = sub * 4 + h2;
+    uint32_t v = 0;
+    if (hd < p.G) v = *(const uint32_t*)(p.q + ((size_t)b * Hq + (size_t)hkv * p.G + hd) * D + 2 * cp);
+    q_lds[h2][cp] = v;
+  }
+  __syncthreads();
+  // B operand of the INT4 path: q[head] restricted to this lane's column group, channels in
+  // the order the nibble extraction produces them (k-slots 2,3,6,7 divided by 16); zero
+  // outside the group
+  f16x8 bq4[4];
+  float qsum = 0.f;
+  const bool use = head_ok && (g == q4);
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const u32x4 w = *(const u32x4*)&q_lds[hh][16 * q4 + 4 * t];  // channels 32q4+8t .. +7
+    float f[8];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      f[2 * e] = bf16_bits_to_f32((uint16_t)(w[e] & 0xffff));
+      f[2 * e + 1] = bf16_bits_to_f32((uint16_t)(w[e] >> 16));
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float v = f[kslot_nibble(e)] * ((e & 2) ? 0.0625f : 1.0f);
+      bq4[t][e] = use ? (_Float16)v : (_Float16)0.f;
+    }
+  }
+  if (head_ok) {
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
+      const u32x4 w = *(const u32x4*)&q_lds[hh][16 * g + 4 * t];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int cp = 32 * q4 + 8 * t + kslot_nibble(e);
-        const int cn = 32 * q4 + 8 * t + e;
-        const uint16_t bp = use ? qv[cp] : (uint16_t)0;
-        const uint16_t bn = use ? qv[cn] : (uint16_t)0;
-        bq4[t][e] = (_Float16)bf16_bits_to_f32(bp);
-        bqb[t][e] = __builtin_bit_cast(__bf16, bn);
-      }
-    }
-    if (head_ok) {
-      for (int c = 0; c < 32; ++c) qsum += (float)(_Float16)bf16_bits_to_f32(qv[32 * g + c]);
+      for (int e = 0; e < 4; ++e)
+        qsum += (float)(_Float16)bf16_bits_to_f32((uint16_t)(w[e] & 0xffff)) +
+                (float)(_Float16)bf16_bits_to_f32((uint16_t)(w[e] >> 16));
     }
   }
   const float qsum24 = qsum * (1.0f / 16777216.0f);
@@ -123,94 +209,66 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
   const float c_int4 = alpha_log2 * 16777216.0f;
 
   WaveState st;
-  st.m = -INFINITY; st.l = 0.f; st.mt = 0.f;
+  st.m = -INFINITY;
+  st.l = 0.f;
+  st.mt = 0.f;
 #pragma unroll
   for (int r = 0; r < 8; ++r) st.acc[r] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-  // ---- work range of this worker
+  // ---- work of this worker: INT4 tiles w, w + NW, w + 2 NW, ... (the workers of a head sweep
+  // the head's records side by side); bf16 tiles go to the workers with the fewest INT4 tiles
   const int NW = p.n_splits * WAVES, w = split * WAVES + wave;
   const int T4 = (p.n_int4 + 31) >> 5;
   const int TA = (p.n_anchor + 31) >> 5, TS = (p.n_staged + 31) >> 5, TWn = (p.n_win + 31) >> 5;
   const int TB = TA + TS + TWn;
-  const long Wt = 5L * T4 + 16L * TB;
-  int i0, u0, i1, u1;
-  work_cut(Wt * w / NW, T4, TB, i0, u0);
-  work_cut(Wt * (w + 1) / NW, T4, TB, i1, u1);
-
-  // ---- INT4 tiles
-  const uint8_t* kc_head = p.k_codes + hb * (size_t)p.int4_cap * 64;
-  const uint32_t* vc_head = p.v_codes + hb * (size_t)(p.int4_cap / 32) * 512;
-  const uint32_t* ksm_head = p.k_sm + hb * (size_t)(p.int4_cap / 16) * 64;
-  const uint32_t* vsm_head = p.v_sm + hb * (size_t)(p.int4_cap / 16) * 64;
-  for (int t = i0; t < i1; ++t) {
-    const int base = t * 32;
-    const u32x4 kc0 = *(const u32x4*)(kc_head + (size_t)(base + n) * 64 + q4 * 16);
-    const u32x4 kc1 = *(const u32x4*)(kc_head + (size_t)(base + 16 + n) * 64 + q4 * 16);
-    const u32x4 ks0 = *(const u32x4*)(ksm_head + (size_t)(2 * t) * 64 + g * 16 + q4 * 4);
-    const u32x4 ks1 = *(const u32x4*)(ksm_head + (size_t)(2 * t + 1) * 64 + g * 16 + q4 * 4);
-    const u32x4 vs0 = *(const u32x4*)(vsm_head + (size_t)(2 * t) * 64 + g * 16 + q4 * 4);
-    const u32x4 vs1 = *(const u32x4*)(vsm_head + (size_t)(2 * t + 1) * 64 + g * 16 + q4 * 4);
-    const u32x4 vc0 = *(const u32x4*)(vc_head + (size_t)t * 512 + (n * 4 + q4) * 8);
-    const u32x4 vc1 = *(const u32x4*)(vc_head + (size_t)t * 512 + (n * 4 + q4) * 8 + 4);
-
-    f32x4 S0 = {0.f, 0.f, 0.f, 0.f}, S1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
-      S0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(codes_to_f16(kc0[tt]), bq4[tt], S0, 0, 0, 0);
-      S1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(codes_to_f16(kc1[tt]), bq4[tt], S1, 0, 0, 0);
-    }
-    float sc[8];
-    bool valid[8];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      float v0 = fmaf(half_lo(ks0[r]), S0[r], half_hi(ks0[r]) * qsum24);
-      float v1 = fmaf(half_lo(ks1[r]), S1[r], half_hi(ks1[r]) * qsum24);
-      v0 += dpp_quad_xor1(v0);
-      v1 += dpp_quad_xor1(v1);
-      v0 += dpp_quad_xor2(v0);
-      v1 += dpp_quad_xor2(v1);
-      valid[r] = base + 4 * q4 + r < p.n_int4;
-      valid[4 + r] = base + 16 + 4 * q4 + r < p.n_int4;
-      sc[r] = valid[r] ? v0 * c_int4 : -INFINITY;
-      sc[4 + r] = valid[4 + r] ? v1 * c_int4 : -INFINITY;
-    }
-    float pv[8];
-    tile_softmax(st, sc, pv);
-    f16x8 bhi, blo;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const uint32_t smv = j < 4 ? vs0[j] : vs1[j - 4];
-      const float pj = valid[j] ? pv[j] : 0.f;
-      st.mt = valid[j] ? fmaf(pj, half_hi(smv), st.mt) : st.mt;
-      const float pp = valid[j] ? pj * half_lo(smv) * PSCALE : 0.f;
-      const _Float16 h = (_Float16)pp;
-      bhi[j] = h;
-      blo[j] = (_Float16)(pp - (float)h);
-    }
-#pragma unroll
-    for (int rr = 0; rr < 8; ++rr) {
-      const f16x8 a = codes_to_f16(rr < 4 ? vc0[rr] : vc1[rr - 4]);
-      st.acc[rr] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bhi, st.acc[rr], 0, 0, 0);
-      st.acc[rr] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, blo, st.acc[rr], 0, 0, 0);
+  const int wr = NW - 1 - w;  // bf16 tiles u with u % NW == wr
+  const uint8_t* slab = p.int4 + hb * (size_t)p.int4_cap * 160;
+  const uint32_t lane16 = (uint32_t)lane * 16;
+  const uint32_t smoff = (uint32_t)(g * 64 + q4 * 16);
+  const int full = p.n_int4 >> 5;  // tiles below this index hold 32 valid slots
+  if (w < T4) {
+    Int4Tile ta, tb;
+    int t = w;
+    load_int4_tile(ta, slab, t, lane16, smoff);
+    for (;;) {
+      load_int4_tile(tb, slab, t + NW < T4 ? t + NW : t, lane16, smoff);
+      if (t < full) int4_tile<false>(st, ta, bq4, qsum24, c_int4, t * 32, p.n_int4, q4);
+      else int4_tile<true>(st, ta, bq4, qsum24, c_int4, t * 32, p.n_int4, q4);
+      t += NW;
+      if (t >= T4) break;
+      load_int4_tile(ta, slab, t + NW < T4 ? t + NW : t, lane16, smoff);
+      if (t < full) int4_tile<false>(st, tb, bq4, qsum24, c_int4, t * 32, p.n_int4, q4);
+      else int4_tile<true>(st, tb, bq4, qsum24, c_int4, t * 32, p.n_int4, q4);
+      t += NW;
+      if (t >= T4) break;
     }
   }
 
   // ---- bf16 tiles (anchors, staging, window)
   const size_t slab_a = (size_t)p.anchor_cap * D, slab_s = (size_t)p.staging_cap * D, slab_w = (size_t)WIN * D;
-  for (int u = u0; u < u1; ++u) {
+  for (int u = wr; u < TB; u += NW) {
     const uint16_t *kb, *vb;
     int cnt, tl;
     if (u < TA) { kb = p.a_k + hb * slab_a; vb = p.a_v + hb * slab_a; cnt = p.n_anchor; tl = u; }
     else if (u < TA + TS) { kb = p.s_k + hb * slab_s; vb = p.s_v + hb * slab_s; cnt = p.n_staged; tl = u - TA; }
     else { kb = p.w_k + hb * slab_w; vb = p.w_v + hb * slab_w; cnt = p.n_win; tl = u - TA - TS; }
     const int base = tl * 32;
+    const uint16_t* kt = kb + (size_t)tl * 4096 + lane * 8;
+    const uint16_t* vt = vb + (size_t)tl * 4096 + lane * 8;
+    bf16x8 ka[8], va[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) ka[j] = *(const bf16x8*)(kt + j * 512);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) va[j] = *(const bf16x8*)(vt + j * 512);
     f32x4 S0 = {0.f, 0.f, 0.f, 0.f}, S1 = {0.f, 0.f, 0.f, 0.f};
-    const uint16_t* r0 = kb + (size_t)(base + n) * D + 32 * q4;
-    const uint16_t* r1 = kb + (size_t)(base + 16 + n) * D + 32 * q4;
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) {
-      S0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)(r0 + 8 * tt), bqb[tt], S0, 0, 0, 0);
-      S1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)(r1 + 8 * tt), bqb[tt], S1, 0, 0, 0);
+      // B operand: q[head] channels 32q4+8tt .. +7 in natural order, zero outside the group
+      u32x4 qw = *(const u32x4*)&q_lds[hh][16 * q4 + 4 * tt];
+      if (!use) qw = (u32x4){0u, 0u, 0u, 0u};
+      const bf16x8 bqb = __builtin_bit_cast(bf16x8, qw);
+      S0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[tt], bqb, S0, 0, 0, 0);
+      S1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[4 + tt], bqb, S1, 0, 0, 0);
     }
     float sc[8];
     bool valid[8];
@@ -236,13 +294,10 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
       bhi[j] = h;
       blo[j] = (__bf16)(pp - (float)h);
     }
-    const uint16_t* vt = vb + (size_t)tl * 4096 + (size_t)(n * 4 + q4) * 64;
 #pragma unroll
-    for (int rr = 0; rr < 8; ++rr) {
-      const bf16x8 a = *(const bf16x8*)(vt + rr * 8);
-      st.acc[rr] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bhi, st.acc[rr], 0, 0, 0);
-      st.acc[rr] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, blo, st.acc[rr], 0, 0, 0);
-    }
+    for (int rr = 0; rr < 8; ++rr) st.acc[rr] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[rr], bhi, st.acc[rr], 0, 0, 0);
+#pragma unroll
+    for (int rr = 0; rr < 8; ++rr) st.acc[rr] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[rr], blo, st.acc[rr], 0, 0, 0);
   }
 
   // ---- per-wave totals, then merge the 4 waves through LDS
@@ -284,36 +339,70 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
     if (c == 0) { rec[0] = M; rec[1] = L; }
     rec[2 + c] = O;
   }
+
 }
 
-// ReduceSoftmax over splits (HyQuant paper Alg. 3): one workgroup per (b, Q head).
-__global__ __launch_bounds__(128) void decode_reduce_kernel(const float* __restrict__ part, float* __restrict__ o,
-                                                            int n_splits) {
-  const int bh = blockIdx.x, c = threadIdx.x;
+// ReduceSoftmax over the split records (HyQuant paper Alg. 3): one workgroup per (b, Q head).
+// A separate launch: the kernel boundary makes the records of all XCDs visible without the
+// L2 write-back an in-kernel agent-scope release would cost every workgroup.
+__global__ __launch_bounds__(64) void decode_reduce_kernel(const float* __restrict__ part, float* __restrict__ o,
+                                                           int n_splits) {
+  // one wave per (b, Q head); lane j holds split j's (m, l) (64 splits per pass), every load of
+  // a pass is independent so the whole merge costs about one memory latency per pass
+  const int bh = blockIdx.x, lane = threadIdx.x;
   const float* rec = part + (size_t)bh * n_splits * (D + 2);
   float M = -INFINITY;
-  for (int s = 0; s < n_splits; ++s) M = fmaxf(M, rec[(size_t)s * (D + 2)]);
-  float O = 0.f, L = 0.f;
+  for (int s0 = 0; s0 < n_splits; s0 += 64) {
+    const int s = s0 + lane;
+    float m = s < n_splits ? rec[(size_t)s * (D + 2)] : -INFINITY;
+#pragma unroll
+    for (int k = 32; k >= 1; k >>= 1) m = fmaxf(m, shfl_xor_f(m, k));
+    M = fmaxf(M, m);
+  }
+  float L = 0.f, O0 = 0.f, O1 = 0.f;
   if (M != -INFINITY) {
-    for (int s = 0; s < n_splits; ++s) {
-      const float* r = rec + (size_t)s * (D + 2);
-      const float f = __builtin_amdgcn_exp2f(r[0] - M);
-      L += r[1] * f;
-      O += r[2 + c] * f;
+    for (int s0 = 0; s0 < n_splits; s0 += 64) {
+      const int s = s0 + lane;
+      float w = 0.f, lw = 0.f;
+      if (s < n_splits) {
+        w = __builtin_amdgcn_exp2f(rec[(size_t)s * (D + 2)] - M);
+        lw = rec[(size_t)s * (D + 2) + 1] * w;
+      }
+#pragma unroll
+      for (int k = 32; k >= 1; k >>= 1) lw += shfl_xor_f(lw, k);
+      L += lw;
+      const int ns = min(64, n_splits - s0);
+      for (int j0 = 0; j0 < ns; j0 += 8) {  // 16 independent loads in flight per batch
+        float a[8], c[8], wj[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int j = min(j0 + u, ns - 1);
+          const float* r = rec + (size_t)(s0 + j) * (D + 2) + 2;
+          a[u] = r[lane];
+          c[u] = r[lane + 64];
+          wj[u] = j0 + u < ns ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), j)) : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          O0 = fmaf(a[u], wj[u], O0);
+          O1 = fmaf(c[u], wj[u], O1);
+        }
+      }
     }
   }
-  o[(size_t)bh * D + c] = O / L;
+  o[(size_t)bh * D + lane] = O0 / L;
+  o[(size_t)bh * D + lane + 64] = O1 / L;
 }
 
 }  // namespace
 
-hipError_t launch_decode(const DecodeParams& p, float* o, int B, hipStream_t stream) {
+hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
   const int nsub = (p.G + 3) >> 2;
-  dim3 grid(p.n_splits, p.Hkv * nsub, B);
+  dim3 grid(p.n_splits, p.Hkv * nsub, p.B);
   hipLaunchKernelGGL(decode_split_kernel, grid, dim3(256), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_reduce_kernel, dim3(B * p.Hkv * p.G), dim3(D), 0, stream, p.part, o, p.n_splits);
+  hipLaunchKernelGGL(decode_reduce_kernel, dim3(p.B * p.Hkv * p.G), dim3(64), 0, stream, p.part, p.o, p.n_splits);
   return hipGetLastError();
 }
 

@@ -34,30 +34,56 @@ __device__ inline uint16_t f32_to_bf16_bits(float f) {
 }
 
 // ---------------------------------------------------------------- layout helpers
+// All per-head stores use 32-position tiles laid out so that each 16-byte piece one lane feeds
+// to an MFMA sits at offset 16 * lane of a contiguous 1 KB block (lane = 16 * quad + row), i.e.
+// every load instruction of the decode kernel is one fully coalesced 1 KB read.
+//
 // Position p (0..31) inside a tile -> (quad q, k-slot e):  p = 4q + (e & 3) + 16 (e >> 2)
 __device__ __host__ inline int tile_quad(int p) { return (p & 15) >> 2; }
 __device__ __host__ inline int tile_kslot(int p) { return (p & 3) + ((p >> 4) << 2); }
-// nibble index of k-slot e inside a V-code dword (pairs (n0,n4),(n1,n5),(n2,n6),(n3,n7) are
-// extracted with one shift+mask each and feed k-slots (0,1),(2,3),(4,5),(6,7))
+// nibble index of k-slot e inside a code dword (pairs (n0,n4),(n1,n5),(n2,n6),(n3,n7) are
+// extracted with one mask (and one shared shift) each and feed k-slots (0,1),(2,3),(4,5),(6,7))
 __device__ __host__ inline int kslot_nibble(int e) { return ((e & 1) << 2) | (e >> 1); }
 
-// INT4 V codes: dword index inside a head slab for (slot, channel)
-__device__ __host__ inline size_t vcode_dword(int slot, int c) {
-  int t = slot >> 5, p = slot & 31;
-  int i = c & 15, r = c >> 4, q = tile_quad(p);
-  return (size_t)t * 512 + (size_t)((i * 4 + q) * 8 + r);
+// INT4 store: one contiguous 5120-byte record per 32-slot tile (each wave streams one record
+// per step): [0, 2048) K codes, [2048, 4096) V codes, [4096, 4608) K (scale, min),
+// [4608, 5120) V (scale, min).  Offsets below are bytes inside a head slab.
+constexpr int T4_BYTES = 5120, T4_VC = 2048, T4_KSM = 4096, T4_VSM = 4608;
+// K codes: 16-byte chunk holding channels 32*q4 .. 32*q4+31 of a slot (even channel in the low
+// nibble); code region = [16-slot block][q4][slot in block][16 B].
+__device__ __host__ inline size_t kcode_chunk(int slot, int q4) {
+  return (size_t)(slot >> 5) * T4_BYTES + (size_t)(((slot >> 4) & 1) * 1024 + q4 * 256 + (slot & 15) * 16);
+}
+// V codes: dword (inside the V code region of a tile) for (slot, channel): region =
+// [half][quad][channel & 15][4]; dword (half, q, i, r4) holds channel 16*(4*half + r4) + i for
+// the 8 slots of quad q; the slot with k-slot e sits in nibble kslot_nibble(e).
+__device__ __host__ inline int vcode_dword_in_tile(int p, int c) {
+  const int i = c & 15, r = c >> 4, q = tile_quad(p);
+  return (r >> 2) * 256 + (q * 16 + i) * 4 + (r & 3);
+}
+__device__ __host__ inline size_t vcode_byte(int slot, int c) {
+  return (size_t)(slot >> 5) * T4_BYTES + T4_VC + 4 * (size_t)vcode_dword_in_tile(slot & 31, c);
 }
 __device__ __host__ inline int vcode_shift(int slot) { return 4 * kslot_nibble(tile_kslot(slot & 31)); }
-
-// bf16 V (anchors / staging / window): element index inside a head slab for (pos, channel)
-__device__ __host__ inline size_t vbf_index(int pos, int c) {
-  int t = pos >> 5, p = pos & 31;
-  int i = c & 15, r = c >> 4, q = tile_quad(p), e = tile_kslot(p);
-  return (size_t)t * 4096 + (size_t)((((i * 4 + q) * 8 + r) * 8) + e);
+// (scale, min) half2 for (slot, group): region = [16-slot block][g][slot in block]
+__device__ __host__ inline size_t ksm_byte(int slot, int g) {
+  return (size_t)(slot >> 5) * T4_BYTES + T4_KSM + 4 * (size_t)(((slot >> 4) & 1) * 64 + g * 16 + (slot & 15));
 }
-// (scale, min) half2 index inside a head slab for (slot, group)
-__device__ __host__ inline size_t sm_index(int slot, int g) {
-  return (size_t)(slot >> 4) * 64 + (size_t)g * 16 + (slot & 15);
+__device__ __host__ inline size_t vsm_byte(int slot, int g) {
+  return (size_t)(slot >> 5) * T4_BYTES + T4_VSM + 4 * (size_t)(((slot >> 4) & 1) * 64 + g * 16 + (slot & 15));
+}
+
+// bf16 K (anchors / staging / window): element index for (pos, channel).  Tile = 4096
+// elements: [16-pos block][8-channel chunk tt][quad q4 = channel / 32][pos in block][8].
+__device__ __host__ inline size_t kbf_index(int pos, int c) {
+  const int t = pos >> 5, p = pos & 31;
+  return (size_t)t * 4096 + (size_t)(((((p >> 4) * 4 + ((c & 31) >> 3)) * 4 + (c >> 5)) * 16 + (p & 15)) * 8 + (c & 7));
+}
+// bf16 V: element index for (pos, channel).  Tile = 4096 elements: [channel / 16][quad]
+// [channel & 15][k-slot e]: one 16-byte piece = one channel at the 8 positions of a quad.
+__device__ __host__ inline size_t vbf_index(int pos, int c) {
+  const int t = pos >> 5, p = pos & 31;
+  return (size_t)t * 4096 + (size_t)((((c >> 4) * 4 + tile_quad(p)) * 16 + (c & 15)) * 8 + tile_kslot(p));
 }
 
 // ---------------------------------------------------------------- INT4 group quantizer

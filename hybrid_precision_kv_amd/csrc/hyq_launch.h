@@ -6,25 +6,20 @@
 namespace hyq {
 
 struct DecodeParams {
-  const uint8_t* k_codes;
-  const uint32_t* v_codes;
-  const uint32_t* k_sm;
-  const uint32_t* v_sm;
+  const uint8_t* int4;  // [hb][int4_cap/32] 5120-byte tile records
   const uint16_t *a_k, *a_v, *s_k, *s_v, *w_k, *w_v;
   const uint16_t* q;  // [B][Hq][128]
   float* part;        // [B][Hq][n_splits][130] partial (m, l, acc) records
-  int Hkv, G;         // KV heads, Q heads per KV head
+  float* o;           // [B][Hq][128]
+  int B, Hkv, G;      // sequences, KV heads, Q heads per KV head
   int int4_cap, anchor_cap, staging_cap;
   int n_int4, n_anchor, n_staged, n_win;
   int n_splits;
 };
-hipError_t launch_decode(const DecodeParams& p, float* o, int B, hipStream_t stream);
+hipError_t launch_decode(const DecodeParams& p, hipStream_t stream);
 
 struct CacheView {
-  uint8_t* k_codes;
-  uint32_t* v_codes;
-  uint32_t* k_sm;
-  uint32_t* v_sm;
+  uint8_t* int4;
   int32_t* slot_pos;
   uint16_t *a_k, *a_v;
   int32_t* a_pos;

@@ -27,24 +27,27 @@
  * every buffer is the concatenation of its head slabs, slab sizes given by
  * hyq_cache_buffer_bytes).  Tiles hold 32 positions.
  *
- *  k_codes  u8  [hb][int4_cap][64]      INT4 K codes, one 64-byte row per slot; byte j holds
- *                                       channel 2j in the low nibble, 2j+1 in the high nibble.
- *  v_codes  u32 [hb][int4_cap/32][16][4][8]  INT4 V codes, tile-transposed: the dword
- *                                       (i, q, r) of a tile holds channel c = 16r + i for the
- *                                       8 slots s of quad q listed by HYQ_V_NIBBLE below.
- *  k_sm,v_sm f16 [hb][int4_cap/16][4][16][2]  (scale, min) per (16-slot block, group g,
- *                                       slot in block): dequant x = scale*code + min.
+ *  Inside a tile, position/slot p = 4q + (e & 3) + 16*(e >> 2) with quad q = 0..3 and
+ *  k-slot e = 0..7; "lane" below means 16*q + (row within a 16-position block).
+ *
+ *  int4     u8 [hb][int4_cap/32][5120]  one record per 32-slot INT4 tile:
+ *     [0, 2048)    K codes  [16-slot block][q4][slot in block][16 B]: the 16 bytes hold
+ *                  channels 32*q4 .. 32*q4+31 of the slot, channel 2j in the low nibble of
+ *                  byte j, 2j+1 in its high nibble;
+ *     [2048, 4096) V codes  u32 [half][q][i][r4]: channel 16*(4*half + r4) + i of the 8 slots
+ *                  of quad q, k-slot e in nibble HYQ_V_NIBBLE[e] (4 bits each, low first);
+ *     [4096, 4608) K (scale, min) fp16 pairs [16-slot block][group g][slot in block];
+ *     [4608, 5120) V (scale, min), same order.  Dequantized x = scale * code + min.
  *  slot_pos i32 [hb][int4_cap]          position held by each INT4 slot (-1 for unused).
- *  a_k, s_k, w_k  bf16 [hb][cap][128]   anchor / staging / window K rows.
- *  a_v, s_v, w_v  bf16 [hb][cap/32][16][4][8][8]  V, tile-transposed: element
- *                                       (i, q, r, e) of a tile is channel 16r + i of the
- *                                       position 4q + (e & 3) + 16*(e >> 2) of the tile.
+ *  a_k, s_k, w_k  bf16 [hb][cap/32][4096]  anchor / staging / window K, per tile
+ *                  [16-position block][tt][q4][position in block][8]: channels
+ *                  32*q4 + 8*tt .. +7 of the position.
+ *  a_v, s_v, w_v  bf16 [hb][cap/32][4096]  V per tile [c / 16][q][c & 15][e]: channel c at
+ *                  the 8 positions of quad q in k-slot order.
  *  a_pos    i32 [hb][anchor_cap]        anchor positions, ascending.
  *  proxy_q  bf16 [b][n_q_heads][proxy_cap][128]  ring of the last proxy queries.
  *  The window is a ring: position p sits in window slot p % 128.  Staging slot i holds
  *  position len - 128 - n_staged + i.
- *  Inside an INT4 tile, slot s = 4q + (e & 3) + 16*(e >> 2) (q = quad, e = 0..7) is stored in
- *  nibble HYQ_V_NIBBLE[e] of its (i, q, r) dwords.
  */
 #ifndef HYQ_H
 #define HYQ_H
@@ -94,7 +97,7 @@ typedef struct {
 typedef struct {
   hyq_shape_t shape;
   /* caller-owned device buffers, layouts above */
-  void *k_codes, *v_codes, *k_sm, *v_sm;
+  void *int4;
   int32_t *slot_pos;
   void *a_k, *a_v;
   int32_t *a_pos;
@@ -113,7 +116,7 @@ typedef struct {
 
 /* Buffer indices for hyq_cache_buffer_bytes */
 enum {
-  HYQ_BUF_K_CODES = 0, HYQ_BUF_V_CODES, HYQ_BUF_K_SM, HYQ_BUF_V_SM, HYQ_BUF_SLOT_POS,
+  HYQ_BUF_INT4 = 0, HYQ_BUF_SLOT_POS,
   HYQ_BUF_A_K, HYQ_BUF_A_V, HYQ_BUF_A_POS, HYQ_BUF_S_K, HYQ_BUF_S_V, HYQ_BUF_W_K,
   HYQ_BUF_W_V, HYQ_BUF_PROXY_Q, HYQ_NBUF
 };
@@ -184,8 +187,10 @@ int hyq_select_vlines(const hyq_shape_t* shape, hyq_cache_t* cache, const void* 
    INT4 positions dequantized in registers, bf16 anchors, staging and window in the same
    online softmax; split-K partial states merged by ReduceSoftmax.
    q: device bf16 [B][Hq][128]; o: device f32 [B][Hq][128].  n_splits: splits per (b, KV
-   head), 0 = automatic.  ws: >= hyq_workspace_bytes(shape, HYQ_OP_DECODE, 0, n_splits).
-   Reads the cache only.  Errors: INVALID, UNSUPPORTED, WORKSPACE, HIP. */
+   head), 0 = automatic.  ws: >= hyq_workspace_bytes(shape, HYQ_OP_DECODE, 0, n_splits) bytes
+   of scratch for the split partial states (no initialisation needed); calls sharing one
+   workspace must not overlap in time (same stream is fine).  Two kernel launches (splits,
+   then their merge).  Reads the cache only.  Errors: INVALID, UNSUPPORTED, WORKSPACE, HIP. */
 int hyq_decode_attn(const hyq_cache_t* cache, const void* q, float* o, int32_t n_splits,
                     void* ws, size_t ws_bytes, hipStream_t stream);
 

@@ -25,31 +25,39 @@ def read_cache(cache) -> list:
     H = s.batch * s.n_kv_heads
     ctr = cache.counters()
     host = {n: t.cpu().numpy() for n, t in cache.buffers.items()}
-    kc = host["k_codes"][: H * s.int4_cap * 64].reshape(H, s.int4_cap, 64)
-    vc = host["v_codes"][: H * s.int4_cap * 64].view(np.uint32).reshape(H, s.int4_cap // 32, 16, 4, 8)
-    ksm = host["k_sm"][: H * s.int4_cap * 16].view(np.float16).reshape(H, s.int4_cap // 16, 4, 16, 2)
-    vsm = host["v_sm"][: H * s.int4_cap * 16].view(np.float16).reshape(H, s.int4_cap // 16, 4, 16, 2)
+    nt = s.int4_cap // 32
+    rec = host["int4"][: H * nt * 5120].reshape(H, nt, 5120)
+    # K codes: [16-slot block][q4][slot in block][16 bytes]
+    kc = rec[:, :, :2048].reshape(H, nt, 2, 4, 16, 16)
+    kc = kc.transpose(0, 1, 2, 4, 3, 5).reshape(H, s.int4_cap, 64)  # -> [slot][64 bytes]
+    # V codes: [half][quad][channel & 15][4 dwords r4], channel = 16*(4*half + r4) + i
+    vc = np.ascontiguousarray(rec[:, :, 2048:4096]).view(np.uint32).reshape(H, nt, 2, 4, 16, 4)
+    # (scale, min): [16-slot block][g][slot in block][2]
+    ksm = np.ascontiguousarray(rec[:, :, 4096:4608]).view(np.float16).reshape(H, nt * 2, 4, 16, 2)
+    vsm = np.ascontiguousarray(rec[:, :, 4608:5120]).view(np.float16).reshape(H, nt * 2, 4, 16, 2)
     slot_pos = host["slot_pos"][: H * s.int4_cap * 4].view(np.int32).reshape(H, s.int4_cap)
 
-    def bf_rows(name, cap):
-        return host[name][: H * cap * D * 2].view(np.uint16).reshape(H, cap, D)
+    p32 = np.arange(32)
+    q32, e32 = _tile_pos(p32)
 
-    def bf_vt(name, cap):
-        t = host[name][: H * cap * D * 2].view(np.uint16).reshape(H, cap // 32, 16, 4, 8, 8)
-        out = np.empty((H, cap, D), np.uint16)
-        p = np.arange(32)
-        q, e = _tile_pos(p)
+    def bf_k(name, cap):
+        # tile [16-pos block][chunk tt][quad q4][pos in block][8]
+        t = host[name][: H * cap * D * 2].view(np.uint16).reshape(H, cap // 32, 2, 4, 4, 16, 8)
+        return t.transpose(0, 1, 2, 5, 4, 3, 6).reshape(H, cap, D)
+
+    def bf_v(name, cap):
+        # tile [channel / 16][quad][channel & 15][k-slot]
+        t = host[name][: H * cap * D * 2].view(np.uint16).reshape(H, cap // 32, 8, 4, 16, 8)
+        out = np.empty((H, cap // 32, 32, D), np.uint16)
         for c in range(D):
-            i, r = c & 15, c >> 4
-            out[:, :, c] = t[:, :, i, q, r, e].reshape(H, cap)
-        return out
+            out[:, :, :, c] = t[:, :, c >> 4, q32, c & 15, e32]
+        return out.reshape(H, cap, D)
 
-    a_k, a_v = bf_rows("a_k", s.anchor_cap), bf_vt("a_v", s.anchor_cap)
-    s_k, s_v = bf_rows("s_k", s.staging_cap), bf_vt("s_v", s.staging_cap)
-    w_k, w_v = bf_rows("w_k", W), bf_vt("w_v", W)
+    a_k, a_v = bf_k("a_k", s.anchor_cap), bf_v("a_v", s.anchor_cap)
+    s_k, s_v = bf_k("s_k", s.staging_cap), bf_v("s_v", s.staging_cap)
+    w_k, w_v = bf_k("w_k", W), bf_v("w_v", W)
     a_pos = host["a_pos"][: H * s.anchor_cap * 4].view(np.int32).reshape(H, s.anchor_cap)
 
-    # V codes back to [slot][channel]
     nsl = s.int4_cap
     sl = np.arange(nsl)
     q, e = _tile_pos(sl & 31)
@@ -57,7 +65,7 @@ def read_cache(cache) -> list:
     vcodes = np.empty((H, nsl, D), np.uint8)
     for c in range(D):
         i, r = c & 15, c >> 4
-        words = vc[:, sl >> 5, i, q, r]
+        words = vc[:, sl >> 5, r >> 2, q, i, r & 3]
         vcodes[:, :, c] = (words >> shift) & 0xF
     kcodes = np.empty((H, nsl, D), np.uint8)
     kcodes[:, :, 0::2] = kc & 0xF

@@ -43,7 +43,7 @@ def test_buffer_sizes_closed_form(lib):
     H = 4
     b = dict(zip(_lib.BUFFERS, list(out)))
     # 160 bytes per INT4 position: 64 + 64 code bytes, 16 + 16 bytes of fp16 (scale, min) x 4 groups
-    assert b["k_codes"] + b["v_codes"] + b["k_sm"] + b["v_sm"] == H * 1024 * 160
+    assert b["int4"] == H * 1024 * 160
     assert b["a_k"] + b["a_v"] == H * 64 * 512 and b["w_k"] + b["w_v"] == H * 128 * 512
     assert b["s_k"] == H * 64 * 256 and b["slot_pos"] == H * 1024 * 4
     assert b["proxy_q"] == 2 * 8 * 64 * 256  # 64 x H_Q x d x 2 bytes per sequence
