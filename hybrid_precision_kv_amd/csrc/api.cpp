@@ -68,6 +68,36 @@ int check_counters(const hyq_cache_t* c) {
   return HYQ_OK;
 }
 
+// select workspace layout (all sizes rounded to 256 bytes)
+struct SelectWs {
+  size_t qsum, rowpart, rowstat, scores, refresh, status, total;
+  size_t per_head;
+  int inset_words, del_words, max_moves, n_tasks;
+};
+size_t r256(size_t x) { return (x + 255) / 256 * 256; }
+SelectWs select_ws(const hyq_shape_t* s, int32_t len) {
+  SelectWs w;
+  const size_t H = nheads(s);
+  const int G = s->n_q_heads / s->n_kv_heads;
+  const size_t R = (size_t)s->proxy_cap * G;
+  const int P = len > W ? len - W : 0;
+  const int n_tiles_max = (len + 31) / 32 + 4;
+  w.n_tasks = hyq::select_task_count(n_tiles_max);
+  w.inset_words = (P + 31) / 32 + 1;
+  w.del_words = (s->int4_cap + 31) / 32 + 1;
+  w.max_moves = 2 * s->anchor_cap + s->staging_cap + 32;
+  w.per_head = r256((size_t)(w.inset_words + w.del_words) * 4 + (size_t)2 * s->anchor_cap * D * 2 +
+                    (size_t)2 * s->anchor_cap * 4 + (size_t)3 * w.max_moves * 4);
+  w.qsum = 0;
+  w.rowpart = w.qsum + r256(H * R * 4 * 4);
+  w.rowstat = w.rowpart + r256(H * w.n_tasks * R * 2 * 4);
+  w.scores = w.rowstat + r256(H * R * 2 * 4);
+  w.refresh = w.scores + r256(H * (size_t)(P > 0 ? P : 1) * 4);
+  w.status = w.refresh + H * w.per_head;
+  w.total = w.status + r256(H * 4);
+  return w;
+}
+
 int auto_splits(const hyq_cache_t* c) {
   const int G = c->shape.n_q_heads / c->shape.n_kv_heads;
   const long units = (long)nheads(&c->shape) * ((G + 3) / 4);
@@ -121,6 +151,7 @@ size_t hyq_workspace_bytes(const hyq_shape_t* s, int op, int32_t len, int32_t n_
       const int S = n_splits > 0 ? n_splits : 256;
       return (size_t)s->batch * s->n_q_heads * S * (D + 2) * sizeof(float);
     }
+    case HYQ_OP_SELECT: return len > 0 ? select_ws(s, len).total : 0;
     default: return 0;
   }
 }
@@ -211,9 +242,100 @@ int hyq_decode_attn(const hyq_cache_t* c, const void* q, float* o, int32_t n_spl
 int hyq_select_vlines(const hyq_shape_t* shape, hyq_cache_t* cache, const void* dense_k, int32_t len,
                       const void* proxy, int32_t n_proxy, int32_t k, int32_t apply, int32_t* idx_out,
                       float* scores_out, void* ws, size_t ws_bytes, hipStream_t stream) {
-  (void)shape; (void)cache; (void)dense_k; (void)len; (void)proxy; (void)n_proxy; (void)k; (void)apply;
-  (void)idx_out; (void)scores_out; (void)ws; (void)ws_bytes; (void)stream;
-  return HYQ_ERR_UNSUPPORTED;
+  int st = check_shape(shape);
+  if (st) return st;
+  const bool dense = dense_k != nullptr;
+  if (dense) {
+    if (!proxy || n_proxy <= 0 || n_proxy > shape->proxy_cap || len <= 0 || apply) return HYQ_ERR_INVALID;
+  } else {
+    if (!cache || proxy) return HYQ_ERR_INVALID;
+    if ((st = check_shape(&cache->shape))) return st;
+    if (memcmp(&cache->shape, shape, sizeof(hyq_shape_t))) return HYQ_ERR_INVALID;
+    if ((st = check_cache_ptrs(cache))) return st;
+    if ((st = check_counters(cache))) return st;
+    len = cache->len;
+    n_proxy = cache->n_proxy;
+    if (len <= 0 || n_proxy <= 0) return HYQ_ERR_INVALID;
+  }
+  const int P = len > W ? len - W : 0;
+  if (k < 0 || k > P) return HYQ_ERR_CAPACITY;
+  if (k > 0 && !idx_out) return HYQ_ERR_INVALID;
+  if (apply && (k > shape->anchor_cap || P - k > shape->int4_cap)) return HYQ_ERR_CAPACITY;
+  const SelectWs w = select_ws(shape, len);
+  if (!ws || ws_bytes < w.total) return HYQ_ERR_WORKSPACE;
+  char* wb = (char*)ws;
+  const int G = shape->n_q_heads / shape->n_kv_heads;
+  if (P > 0) {
+    hyq::SelectParams p;
+    memset(&p, 0, sizeof(p));
+    p.dense_k = (const uint16_t*)dense_k;
+    p.proxy = dense ? (const uint16_t*)proxy : (const uint16_t*)cache->proxy_q;
+    p.proxy_stride = dense ? n_proxy : shape->proxy_cap;
+    p.n_proxy = n_proxy;
+    p.B = shape->batch;
+    p.Hkv = shape->n_kv_heads;
+    p.G = G;
+    p.len = len;
+    p.int4_cap = shape->int4_cap;
+    p.anchor_cap = shape->anchor_cap;
+    p.staging_cap = shape->staging_cap;
+    if (dense) {
+      p.n_tiles = (len + 31) / 32;
+    } else {
+      p.int4 = (const uint8_t*)cache->int4;
+      p.slot_pos = cache->slot_pos;
+      p.a_k = (const uint16_t*)cache->a_k;
+      p.s_k = (const uint16_t*)cache->s_k;
+      p.w_k = (const uint16_t*)cache->w_k;
+      p.a_pos = cache->a_pos;
+      p.n_int4 = cache->n_int4;
+      p.n_anchor = cache->n_anchor;
+      p.n_staged = cache->n_staged;
+      p.n_win = len < W ? len : W;
+      p.n_tiles = (p.n_int4 + 31) / 32 + (p.n_anchor + 31) / 32 + (p.n_staged + 31) / 32 + (p.n_win + 31) / 32;
+    }
+    p.n_tasks = hyq::select_task_count(p.n_tiles);
+    p.k = k;
+    p.qsum = (float*)(wb + w.qsum);
+    p.rowpart = (float*)(wb + w.rowpart);
+    p.rowstat = (float*)(wb + w.rowstat);
+    p.scores = scores_out ? scores_out : (float*)(wb + w.scores);
+    p.idx_out = idx_out;
+    if (hyq::launch_select(p, stream) != hipSuccess) return HYQ_ERR_HIP;
+  }
+  if (apply) {
+    hyq::RefreshParams r;
+    memset(&r, 0, sizeof(r));
+    r.int4 = (uint8_t*)cache->int4;
+    r.slot_pos = cache->slot_pos;
+    r.a_k = (uint16_t*)cache->a_k;
+    r.a_v = (uint16_t*)cache->a_v;
+    r.a_pos = cache->a_pos;
+    r.s_k = (const uint16_t*)cache->s_k;
+    r.s_v = (const uint16_t*)cache->s_v;
+    r.idx = idx_out;
+    r.B = shape->batch;
+    r.Hkv = shape->n_kv_heads;
+    r.len = len;
+    r.k = k;
+    r.int4_cap = shape->int4_cap;
+    r.anchor_cap = shape->anchor_cap;
+    r.staging_cap = shape->staging_cap;
+    r.n_int4_old = cache->n_int4;
+    r.n_anchor_old = cache->n_anchor;
+    r.n_staged = cache->n_staged;
+    r.ws = (uint8_t*)(wb + w.refresh);
+    r.ws_per_head = w.per_head;
+    r.inset_words = w.inset_words;
+    r.del_words = w.del_words;
+    r.max_moves = w.max_moves;
+    r.status = (int*)(wb + w.status);
+    if (P > 0 && hyq::launch_refresh(r, stream) != hipSuccess) return HYQ_ERR_HIP;
+    cache->n_anchor = k;
+    cache->n_int4 = P - k;
+    cache->n_staged = 0;
+  }
+  return HYQ_OK;
 }
 
 int hyq_prefill_attn(const hyq_shape_t* shape, const void* q, const void* k, const void* v, int32_t len,

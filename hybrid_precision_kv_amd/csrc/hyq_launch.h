@@ -29,6 +29,44 @@ struct CacheView {
   int int4_cap, anchor_cap, staging_cap, proxy_cap;
 };
 
+struct SelectParams {
+  const uint16_t* dense_k;  // dense mode: [B][Hkv][len][128]; null in cache mode
+  const uint8_t* int4;
+  const int32_t* slot_pos;
+  const uint16_t *a_k, *s_k, *w_k;
+  const int32_t* a_pos;
+  const uint16_t* proxy;  // [B][Hq][proxy_stride][128], rows 0..n_proxy-1 valid
+  int proxy_stride, n_proxy;
+  int B, Hkv, G, len;
+  int int4_cap, anchor_cap, staging_cap;
+  int n_int4, n_anchor, n_staged, n_win;
+  int n_tiles, n_tasks, k;
+  float* qsum;     // [H][R][4]
+  float* rowpart;  // [H][n_tasks][R][2]
+  float* rowstat;  // [H][R][2]
+  float* scores;   // [H][len - 128] by position
+  int32_t* idx_out;  // [H][k]
+};
+hipError_t launch_select(SelectParams p, hipStream_t stream);
+int select_task_count(int n_tiles);
+
+struct RefreshParams {
+  uint8_t* int4;
+  int32_t* slot_pos;
+  uint16_t *a_k, *a_v;
+  int32_t* a_pos;
+  const uint16_t *s_k, *s_v;
+  const int32_t* idx;  // [H][k] new set, ascending
+  int B, Hkv, len, k;
+  int int4_cap, anchor_cap, staging_cap;
+  int n_int4_old, n_anchor_old, n_staged;
+  uint8_t* ws;  // per-head scratch
+  size_t ws_per_head;
+  int inset_words, del_words, max_moves;
+  int* status;  // [H] 0 = counts consistent
+};
+hipError_t launch_refresh(const RefreshParams& p, hipStream_t stream);
+
 // Freeze (prefill -> decode)
 hipError_t launch_freeze(const CacheView& c, const uint16_t* k, const uint16_t* v, int len,
                          const int32_t* anchors, int n_anchor, const uint16_t* q_tail, int n_tail,
