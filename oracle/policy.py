@@ -10,8 +10,9 @@ Readings of the pages taken here (each is also listed in the design notes):
   * Anchors ("vertical lines") are chosen from the non-window prefix [0, L-W)
     (§4.1 Eq. 1, Eq. 3, Eq. 5).
   * Their count is k = min(P, max(1, ceil(rho * L))) with P = L - W candidates,
-    and k = 0 when P = 0 (the clamp and the empty case of Alg. 1; the basis L of the
-    ratio follows the workload definition of 52 anchors at L = 1024, rho = 5%).
+    and k = 0 when P = 0 (the clamp and the empty case of Alg. 1).  Reading: the ratio
+    is applied to the context length L (5% of a 1024-position context = 52 anchors),
+    not to P as Alg. 1 writes it.
   * The score of a key is its summed attention probability over the proxy queries
     of all Q heads of its KV group, softmax taken over every cached key (Eq. 4; GQA
     handled per KV head as in Alg. 1's GQA-native form and Alg. 4's per-KV-head
@@ -234,7 +235,7 @@ class HybridCacheRef:
 
 def select_dense(K_bits: np.ndarray, proxy_bits: np.ndarray, W: int = 128, pct_num: int = 5,
                  pct_den: int = 100):
-    """Selector at Freeze on the dense bf16 prefix (Alg. 4 line VTI(Q_tail, K, ...)):
+    """Selector at Freeze on the dense bf16 prefix (Alg. 4: the set comes from the prefill tail queries):
     K_bits [L][D]; proxy_bits [g][n][D] (the last prefill queries of the group)."""
     K = nm.bf16_to_f32(K_bits)
     L, D = K.shape
