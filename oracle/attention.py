@@ -161,7 +161,7 @@ def prefill_quantize(Q_bits, K_bits, V_bits, anchors, BM: int = 64, BN: int = 64
 
 
 def prefill_ref(Q_bits, K_bits, V_bits, anchors, W: int = 128, BM: int = 64, BN: int = 64,
-                blocks=None, round_p: bool = True):
+                blocks=None, round_p: bool = True, heads=None, qz=None):
     """Emulation of the hybrid prefill operator (HyQuant paper §4.2 Eq. 6-7, Alg. 2).
 
     For query i (causal), keys split three ways (Eq. 1 applied per query):
@@ -174,8 +174,16 @@ def prefill_ref(Q_bits, K_bits, V_bits, anchors, W: int = 128, BM: int = 64, BN:
     ascending 64-key tiles) as in Alg. 2 Stage 3.  After each tile's max update
     p = exp(s - m_run); with ``round_p`` p is rounded as the operator stores it:
     segment A: e4m3(448 p) / 448, segments B and C: bf16(p); l sums the rounded values.
-    Scores and exp in fp64.  ``blocks``: optional list of query-block indices to
-    compute (others are NaN).  Returns fp64 [Hq][N][D].
+
+    Precision.  With ``round_p`` the values that decide a rounded code -- the score s,
+    the running max m and p -- are taken in IEEE fp32 (the pages fix no precision for
+    them; fp32 is the operator's): s = ((dot * s_Q) * s_K) * alpha for quantized keys
+    (dot an exact integer), s = fp32(fp32(q.k) * alpha) for bf16 keys, p = fp32(exp(s - m)),
+    then 448 p in fp32 before the E4M3 rounding.  The rescale factors, l and the
+    accumulator stay fp64.  Without ``round_p`` everything is fp64 (the exact mixed
+    softmax of Eq. 7).  ``blocks`` / ``heads``: optional lists of 64-query blocks and Q heads
+    to compute (others are NaN); ``qz``: the ``prefill_quantize`` result, if already at hand.
+    Returns fp64 [Hq][N][D].
     """
     Qf = nm.bf16_to_f32(Q_bits).astype(np.float64)
     Kf = nm.bf16_to_f32(K_bits).astype(np.float64)
@@ -184,12 +192,19 @@ def prefill_ref(Q_bits, K_bits, V_bits, anchors, W: int = 128, BM: int = 64, BN:
     Hkv = Kf.shape[0]
     g = Hq // Hkv
     alpha = 1.0 / np.sqrt(D)
-    qz = prefill_quantize(Q_bits, K_bits, V_bits, anchors, BM, BN)
+
+    def bscore(dot64):
+        if round_p:
+            return dot64.astype(np.float32) * np.float32(alpha)
+        return alpha * dot64
+
+    if qz is None:
+        qz = prefill_quantize(Q_bits, K_bits, V_bits, anchors, BM, BN)
     nqb = (N + BM - 1) // BM
     if blocks is None:
         blocks = range(nqb)
     out = np.full((Hq, N, D), np.nan)
-    for h in range(Hq):
+    for h in (range(Hq) if heads is None else heads):
         hk = h // g
         anc = np.asarray(anchors[hk], np.int64)
         isanc = np.zeros(N, bool)
@@ -200,27 +215,31 @@ def prefill_ref(Q_bits, K_bits, V_bits, anchors, W: int = 128, BM: int = 64, BN:
             r0, r1 = b * BM, min(N, (b + 1) * BM)
             rows = np.arange(r0, r1)
             q8 = qz["q8"][h, r0:r1].astype(np.int64)
-            sq = float(qz["sq"][h, b])
-            m = np.full(len(rows), -np.inf)
+            sq = qz["sq"][h, b] if round_p else float(qz["sq"][h, b])
+            m = np.full(len(rows), -np.inf, dtype=np.float32 if round_p else np.float64)
             l = np.zeros(len(rows))
             acc = np.zeros((len(rows), D))
 
+            ft = np.float32 if round_p else np.float64
+
             def step(s, valid, Vt, seg):
                 nonlocal m, l, acc
-                s = np.where(valid, s, -np.inf)
+                s = np.where(valid, s, -np.inf).astype(ft)
                 tmax = s.max(axis=1)
                 m_new = np.maximum(m, tmax)
                 live = m_new > -np.inf
                 had = m > -np.inf
-                c = np.where(live & had, np.exp(np.where(had, m, 0.0) - np.where(live, m_new, 0.0)), 0.0)
-                p = np.where(valid, np.exp(s - np.where(live, m_new, 0.0)[:, None]), 0.0)
+                c = np.where(live & had, np.exp(np.where(had, m, 0.0).astype(np.float64)
+                                                 - np.where(live, m_new, 0.0)), 0.0)
+                with np.errstate(invalid="ignore"):
+                    p = np.where(valid, np.exp(s - np.where(live, m_new, ft(0))[:, None]), ft(0))
                 if round_p:
                     if seg == "A":
-                        p = nm.e4m3_round_fast(448.0 * p) / 448.0
+                        p = nm.e4m3_round_fast(np.float32(448) * p) / 448.0
                     else:
-                        p = nm.bf16_to_f32(nm.f32_to_bf16(p.astype(np.float32))).astype(np.float64)
-                l = l * c + p.sum(axis=1)
-                acc = acc * c[:, None] + p @ Vt
+                        p = nm.bf16_to_f32(nm.f32_to_bf16(p)).astype(np.float64)
+                l = l * c + p.sum(axis=1, dtype=np.float64)
+                acc = acc * c[:, None] + p.astype(np.float64) @ Vt
                 m = np.where(live, m_new, m)
 
             # Segment A: quantized prefix tiles.
@@ -228,14 +247,17 @@ def prefill_ref(Q_bits, K_bits, V_bits, anchors, W: int = 128, BM: int = 64, BN:
             if last_q >= 0:
                 for t in range(last_q // BN + 1):
                     j = np.arange(t * BN, min(N, (t + 1) * BN))
-                    dot = (q8 @ k8[j].T).astype(np.float64)
-                    s = dot * (sq * float(qz["sk"][hk, t])) * alpha
+                    dot = q8 @ k8[j].T
+                    if round_p:
+                        s = ((dot.astype(np.float32) * np.float32(sq)) * qz["sk"][hk, t]) * np.float32(alpha)
+                    else:
+                        s = dot.astype(np.float64) * (sq * float(qz["sk"][hk, t])) * alpha
                     valid = (j[None, :] <= rows[:, None] - W) & ~isanc[j][None, :]
                     step(s, valid, vq[j], "A")
             # Segment B: anchors, ascending tiles of BN anchors.
             for u in range((len(anc) + BN - 1) // BN):
                 j = anc[u * BN:(u + 1) * BN]
-                s = alpha * (Qf[h, r0:r1] @ Kf[hk, j].T)
+                s = bscore(Qf[h, r0:r1] @ Kf[hk, j].T)
                 valid = j[None, :] <= rows[:, None] - W
                 step(s, valid, Vf[hk, j], "B")
             # Segment C: window, ascending aligned tiles.
@@ -243,7 +265,7 @@ def prefill_ref(Q_bits, K_bits, V_bits, anchors, W: int = 128, BM: int = 64, BN:
             t_hi = (r1 - 1) // BN
             for t in range(t_lo, t_hi + 1):
                 j = np.arange(t * BN, min(N, (t + 1) * BN))
-                s = alpha * (Qf[h, r0:r1] @ Kf[hk, j].T)
+                s = bscore(Qf[h, r0:r1] @ Kf[hk, j].T)
                 valid = (j[None, :] <= rows[:, None]) & (j[None, :] >= rows[:, None] - W + 1)
                 step(s, valid, Vf[hk, j], "C")
             out[h, r0:r1] = acc / l[:, None]
