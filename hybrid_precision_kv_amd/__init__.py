@@ -5,7 +5,7 @@ only marshals torch tensors (device memory and the current stream) into its call
 library is loaded on first use and its absence raises -- there is no CPU fallback.
 """
 from .api import (HybridKVCache, Shape, anchor_count, append_token, decode_attn, prefill_attn,
-                  quantize_kv, select_vlines, workspace_bytes)
+                  prefill_workspace, quantize_kv, select_vlines, workspace_bytes)
 
 __all__ = ["HybridKVCache", "Shape", "anchor_count", "append_token", "decode_attn", "prefill_attn",
-           "quantize_kv", "select_vlines", "workspace_bytes"]
+           "prefill_workspace", "quantize_kv", "select_vlines", "workspace_bytes"]

@@ -222,20 +222,40 @@ def select_vlines(shape: Shape, k: int, cache: HybridKVCache | None = None, dens
     return (idx, sc) if scores else idx
 
 
+def prefill_workspace(shape: Shape, N: int, device=None) -> torch.Tensor:
+    """A workspace for hyq_prefill_attn at sequence length N (uint8, on ``device``)."""
+    lib = _lib.load()
+    s = shape.c()
+    need = int(lib.hyq_workspace_bytes(C.byref(s), _lib.HYQ_OP_PREFILL, N, 0))
+    if need == 0:
+        raise ValueError(f"prefill: unsupported shape or length N={N}")
+    return torch.empty(need, dtype=torch.uint8, device=device or "cuda")
+
+
 def prefill_attn(shape: Shape, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
-                 anchors: torch.Tensor | None = None) -> torch.Tensor:
-    """Hybrid prefill attention for one sequence (hyq_prefill_attn); fp32 out [Hq][N][128]."""
+                 anchors: torch.Tensor | None = None, out: torch.Tensor | None = None,
+                 ws: torch.Tensor | None = None) -> torch.Tensor:
+    """Hybrid prefill attention for one sequence (hyq_prefill_attn); fp32 out [Hq][N][128].
+    ``ws`` (from ``prefill_workspace``) receives the quantized operands."""
     lib = _lib.load()
     N = q.shape[1]
     _bf16(q, (shape.n_q_heads, N, D), "q")
     _bf16(k, (shape.n_kv_heads, N, D), "k")
     _bf16(v, (shape.n_kv_heads, N, D), "v")
-    n_anchor = 0 if anchors is None else anchors.shape[-1]
-    o = torch.empty((shape.n_q_heads, N, D), dtype=torch.float32, device=q.device)
+    n_anchor = 0
+    if anchors is not None:
+        if anchors.dtype != torch.int32 or not anchors.is_contiguous() or anchors.dim() != 2 \
+                or anchors.shape[0] != shape.n_kv_heads or anchors.device != q.device:
+            raise ValueError("anchors: contiguous int32 [Hkv][n_anchor] on the queries' device")
+        n_anchor = anchors.shape[1]
+    if out is None:
+        out = torch.empty((shape.n_q_heads, N, D), dtype=torch.float32, device=q.device)
+    elif out.dtype != torch.float32 or tuple(out.shape) != (shape.n_q_heads, N, D) or not out.is_contiguous():
+        raise ValueError("out: contiguous float32 [Hq][N][128]")
+    if ws is None:
+        ws = prefill_workspace(shape, N, q.device)
     s = shape.c()
-    need = int(lib.hyq_workspace_bytes(C.byref(s), _lib.HYQ_OP_PREFILL, N, 0))
-    ws = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
     check("hyq_prefill_attn", lib.hyq_prefill_attn(C.byref(s), _ptr(q), _ptr(k), _ptr(v), N,
-                                                   _ptr(anchors if n_anchor else None), n_anchor, _ptr(o),
+                                                   _ptr(anchors if n_anchor else None), n_anchor, _ptr(out),
                                                    _ptr(ws), ws.numel(), _stream()))
-    return o
+    return out

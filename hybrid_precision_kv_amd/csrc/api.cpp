@@ -98,6 +98,28 @@ SelectWs select_ws(const hyq_shape_t* s, int32_t len) {
   return w;
 }
 
+// prefill workspace layout (sections in this order, each rounded up to 256 bytes)
+struct PrefillWs {
+  size_t q8, sq, k8, sk, v8, sv, vmax, abits, total;
+  int Npad;
+};
+PrefillWs prefill_ws(const hyq_shape_t* s, int32_t len) {
+  PrefillWs w;
+  const size_t Hq = s->n_q_heads, Hkv = s->n_kv_heads;
+  const size_t Np = (size_t)(len + 127) / 128 * 128;
+  w.Npad = (int)Np;
+  w.q8 = 0;
+  w.sq = w.q8 + r256(Hq * Np * D);
+  w.k8 = w.sq + r256(Hq * (Np / 64) * 4);
+  w.sk = w.k8 + r256(Hkv * Np * D);
+  w.v8 = w.sk + r256(Hkv * (Np / 64) * 4);
+  w.sv = w.v8 + r256(Hkv * Np * D);
+  w.vmax = w.sv + r256(Hkv * D * 4);
+  w.abits = w.vmax + r256(Hkv * (Np / 64) * D * 4);
+  w.total = w.abits + r256(Hkv * (Np / 32) * 4);
+  return w;
+}
+
 int auto_splits(const hyq_cache_t* c) {
   const int G = c->shape.n_q_heads / c->shape.n_kv_heads;
   const long units = (long)nheads(&c->shape) * ((G + 3) / 4);
@@ -152,6 +174,7 @@ size_t hyq_workspace_bytes(const hyq_shape_t* s, int op, int32_t len, int32_t n_
       return (size_t)s->batch * s->n_q_heads * S * (D + 2) * sizeof(float);
     }
     case HYQ_OP_SELECT: return len > 0 ? select_ws(s, len).total : 0;
+    case HYQ_OP_PREFILL: return len > 0 && len <= HYQ_PREFILL_MAX_LEN ? prefill_ws(s, len).total : 0;
     default: return 0;
   }
 }
@@ -341,9 +364,38 @@ int hyq_select_vlines(const hyq_shape_t* shape, hyq_cache_t* cache, const void* 
 int hyq_prefill_attn(const hyq_shape_t* shape, const void* q, const void* k, const void* v, int32_t len,
                      const int32_t* anchors, int32_t n_anchor, float* o, void* ws, size_t ws_bytes,
                      hipStream_t stream) {
-  (void)shape; (void)q; (void)k; (void)v; (void)len; (void)anchors; (void)n_anchor; (void)o; (void)ws;
-  (void)ws_bytes; (void)stream;
-  return HYQ_ERR_UNSUPPORTED;
+  int st = check_shape(shape);
+  if (st) return st;
+  if (shape->batch != 1) return HYQ_ERR_UNSUPPORTED;
+  if (!q || !k || !v || !o || len <= 0 || n_anchor < 0) return HYQ_ERR_INVALID;
+  if (len > HYQ_PREFILL_MAX_LEN) return HYQ_ERR_UNSUPPORTED;
+  const int P = len > W ? len - W : 0;
+  if (n_anchor > P || (n_anchor > 0 && !anchors)) return HYQ_ERR_INVALID;
+  const PrefillWs w = prefill_ws(shape, len);
+  if (!ws || ws_bytes < w.total) return HYQ_ERR_WORKSPACE;
+  char* wb = (char*)ws;
+  hyq::PrefillParams p;
+  p.q = (const uint16_t*)q;
+  p.k = (const uint16_t*)k;
+  p.v = (const uint16_t*)v;
+  p.anchors = anchors;
+  p.n_anchor = n_anchor;
+  p.o = o;
+  p.N = len;
+  p.Npad = w.Npad;
+  p.Hq = shape->n_q_heads;
+  p.Hkv = shape->n_kv_heads;
+  p.G = shape->n_q_heads / shape->n_kv_heads;
+  p.q8 = (int8_t*)(wb + w.q8);
+  p.sq = (float*)(wb + w.sq);
+  p.k8 = (int8_t*)(wb + w.k8);
+  p.sk = (float*)(wb + w.sk);
+  p.v8 = (uint8_t*)(wb + w.v8);
+  p.sv = (float*)(wb + w.sv);
+  p.vmax = (float*)(wb + w.vmax);
+  p.abits = (uint32_t*)(wb + w.abits);
+  if (hyq::launch_prefill(p, stream) != hipSuccess) return HYQ_ERR_HIP;
+  return HYQ_OK;
 }
 
 }  // extern "C"

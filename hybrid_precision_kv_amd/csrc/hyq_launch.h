@@ -75,4 +75,21 @@ hipError_t launch_freeze(const CacheView& c, const uint16_t* k, const uint16_t* 
 hipError_t launch_append(const CacheView& c, const uint16_t* k_t, const uint16_t* v_t, const uint16_t* q_t,
                          int len, int n_staged, int proxy_head, hipStream_t stream);
 
+// Hybrid prefill (one sequence).  Workspace sections are described with hyq_prefill_attn.
+struct PrefillParams {
+  const uint16_t* q;        // [Hq][N][128] bf16
+  const uint16_t* k;        // [Hkv][N][128] bf16
+  const uint16_t* v;        // [Hkv][N][128] bf16
+  const int32_t* anchors;   // [Hkv][n_anchor]
+  int n_anchor;
+  float* o;                 // [Hq][N][128]
+  int N, Npad, Hq, Hkv, G;
+  int8_t* q8; float* sq;    // Q codes (operand order) and per-64-query scales
+  int8_t* k8; float* sk;    // K codes (operand order) and per-64-key scales
+  uint8_t* v8; float* sv;   // V E4M3 codes (operand order) and per-channel scales
+  float* vmax;              // per-64-key-block channel maxima of |V| (non-anchor)
+  uint32_t* abits;          // anchor bitmap
+};
+hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream);
+
 }  // namespace hyq

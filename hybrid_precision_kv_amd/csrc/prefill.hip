@@ -1,0 +1,576 @@
+// Hybrid prefill attention for gfx950 (HyQuant paper §4.2 Eq. 6-7, Alg. 2).
+//
+// Query i attends, causally, to three key sets: the window [i-127, i] and the anchors
+// a <= i-128 in bf16, and every other key j <= i-128 through INT8 Q.K and FP8 P.V.  The pass
+// is split into operand quantization (Alg. 2 Stage 2: four small kernels writing codes and
+// scales into the caller's workspace) and one attention kernel (Alg. 2 Stage 3) that runs a
+// single online softmax per query row over 64-key tiles in the order: quantized tiles,
+// anchor tiles, window tiles.
+//
+// Attention kernel design (one workgroup = 128 queries of one Q head, 4 waves x 32 queries):
+//  * Scores are computed transposed, S^T = K . Q^T, with 16x16 MFMA tiles: a lane then holds
+//    16 keys of ONE query per 16-query block, so row maxima are mostly in-lane and the score
+//    registers are directly the B operand of O^T = V^T . P^T (keys permuted identically in
+//    the V tile layout).  The accumulator O^T keeps 4 channels x 1 query per lane and block.
+//  * Quantized tiles: i32 MFMA 16x16x64 on INT8 codes; the mask (anchors, causal edge) enters
+//    as the MFMA's C input (-2^28), so interior tiles pay nothing for it; P = E4M3(448 p)
+//    feeds FP8 MFMA 16x16x32 against E4M3 V codes; the row sum of the rounded P comes out of
+//    one more MFMA against a row of ones.  After the last quantized tile the accumulator is
+//    scaled by the per-channel V scale / 448.
+//  * Anchor and window tiles: bf16 MFMA 16x16x32 with a -inf mask in the C input; P = bf16(p).
+//  * The running max is exact per 64-key tile (no lazy threshold): the P codes depend on it.
+//    A row's accumulator is rescaled only when its max moved (wave-uniform branch).
+//  * Q is quantized in registers from the bf16 operand fragments (block maximum exchanged
+//    through LDS); the codes are also written to the workspace.
+#include "hyq_common.h"
+#include "hyq_launch.h"
+
+namespace hyq {
+namespace {
+
+constexpr int KBLK = 64;          // quantization block (queries and keys) = softmax key tile
+constexpr int WG_ROWS = 128;      // queries per attention workgroup
+constexpr int NEG_DOT = -(1 << 28);  // masked INT8 dot (|valid dot| < 2^21)
+constexpr float AL2 = 0.08838834764831845f * 1.4426950408889634f;  // alpha * log2(e), alpha = 1/sqrt(128)
+constexpr float LOG2_448 = 8.807354922057604f;
+constexpr float C2_FAST_MIN = 1e-6f;  // below: masked INT8 scores are zeroed explicitly
+constexpr int K8_LD = 144;        // LDS row stride (bytes) of the INT8 K tile
+constexpr int KB_LD = 272;        // LDS row stride (bytes) of the bf16 K tile
+constexpr int LDS_V = 64 * KB_LD; // V tile offset
+constexpr int LDS_TILE = LDS_V + 16384;
+
+typedef long i64;
+
+__device__ inline float bf_lo(uint32_t x) { return __uint_as_float(x << 16); }
+__device__ inline float bf_hi(uint32_t x) { return __uint_as_float(x & 0xffff0000u); }
+
+// symmetric INT8 code of x with scale s (s == 0 -> 0); IEEE divide, half-even rounding
+__device__ inline int int8_code(float x, float s) {
+  if (s == 0.0f) return 0;
+  float c = rintf(__fdiv_rn(x, s));
+  c = fminf(fmaxf(c, -127.0f), 127.0f);
+  return (int)c;
+}
+
+__device__ inline int wave_max_i(int v) {
+  v = max(v, __shfl_xor(v, 16));
+  return max(v, __shfl_xor(v, 32));
+}
+__device__ inline float wave_max_f16(float v) {  // over the 4 lane groups holding one column
+  v = fmaxf(v, shfl_xor_f(v, 16));
+  return fmaxf(v, shfl_xor_f(v, 32));
+}
+
+// ------------------------------------------------------------------ operand quantization
+
+// Anchor bitmap: bit (j & 31) of word j >> 5 is set for every listed anchor j.
+__global__ void __launch_bounds__(256) pf_bitmap_kernel(PrefillParams p) {
+  const int h = blockIdx.x;
+  const int nw = p.Npad >> 5;
+  const int32_t* anc = p.anchors + (size_t)h * p.n_anchor;
+  for (int w = threadIdx.x; w < nw; w += blockDim.x) {
+    const int lo_key = 32 * w;
+    int lo = 0, hi = p.n_anchor;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (anc[mid] < lo_key) lo = mid + 1; else hi = mid;
+    }
+    uint32_t bits = 0;
+    for (int i = lo; i < p.n_anchor; ++i) {
+      const int a = anc[i];
+      if (a < lo_key || a >= lo_key + 32) break;
+      bits |= 1u << (a - lo_key);
+    }
+    p.abits[(size_t)h * nw + w] = bits;
+  }
+}
+
+// K: per (KV head, 64-key block) symmetric INT8 with the anchors left out of the maximum;
+// V: per-channel maximum of |V| over the block's non-anchor keys.
+__global__ void __launch_bounds__(256) pf_kquant_kernel(PrefillParams p) {
+  __shared__ float red[4];
+  __shared__ float vt[64][129];
+  const int blk = blockIdx.x, h = blockIdx.y;
+  const int t = threadIdx.x, row = t >> 2, qd = t & 3;
+  const int key = blk * KBLK + row;
+  const int nw = p.Npad >> 5, nb = p.Npad >> 6;
+  const uint32_t word = p.abits[(size_t)h * nw + (key >> 5)];
+  const bool live = key < p.N && !((word >> (key & 31)) & 1u);
+  float kx[32], vx[32];
+#pragma unroll
+  for (int e = 0; e < 32; ++e) { kx[e] = 0.0f; vx[e] = 0.0f; }
+  if (live) {
+    const u32x4* ks = (const u32x4*)(p.k + ((size_t)h * p.N + key) * D + 32 * qd);
+    const u32x4* vs = (const u32x4*)(p.v + ((size_t)h * p.N + key) * D + 32 * qd);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const u32x4 a = ks[c], b = vs[c];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        kx[8 * c + 2 * e] = bf_lo(a[e]); kx[8 * c + 2 * e + 1] = bf_hi(a[e]);
+        vx[8 * c + 2 * e] = bf_lo(b[e]); vx[8 * c + 2 * e + 1] = bf_hi(b[e]);
+      }
+    }
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int e = 0; e < 32; ++e) amax = fmaxf(amax, fabsf(kx[e]));
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) amax = fmaxf(amax, shfl_xor_f(amax, o));
+  if ((t & 63) == 0) red[t >> 6] = amax;
+#pragma unroll
+  for (int e = 0; e < 32; ++e) vt[row][32 * qd + e] = fabsf(vx[e]);
+  __syncthreads();
+  amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float s = __fdiv_rn(amax, 127.0f);
+  // operand order: dim 32 qd + 8 jj + e  ->  byte 64 (qd >> 1) + 16 jj + 8 (qd & 1) + e
+  int8_t* dst = p.k8 + ((size_t)h * p.Npad + key) * D + 64 * (qd >> 1) + 8 * (qd & 1);
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj) {
+    uint32_t w0 = 0, w1 = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      w0 |= (uint32_t)(int8_code(kx[8 * jj + e], s) & 0xff) << (8 * e);
+      w1 |= (uint32_t)(int8_code(kx[8 * jj + 4 + e], s) & 0xff) << (8 * e);
+    }
+    *(uint2*)(dst + 16 * jj) = make_uint2(w0, w1);
+  }
+  if (t == 0) p.sk[(size_t)h * nb + blk] = s;
+  if (t < D) {
+    float m = 0.0f;
+    for (int r = 0; r < 64; ++r) m = fmaxf(m, vt[r][t]);
+    p.vmax[((size_t)h * nb + blk) * D + t] = m;
+  }
+}
+
+// s_V[c] = max over blocks / 448 (IEEE divide).  Block = 8 x 128 threads.
+__global__ void __launch_bounds__(1024) pf_vscale_kernel(PrefillParams p) {
+  __shared__ float part[8][D];
+  const int h = blockIdx.x, c = threadIdx.x & (D - 1), g = threadIdx.x >> 7;
+  const int nb = p.Npad >> 6;
+  float m = 0.0f;
+  for (int b = g; b < nb; b += 8) m = fmaxf(m, p.vmax[((size_t)h * nb + b) * D + c]);
+  part[g][c] = m;
+  __syncthreads();
+  if (g == 0) {
+#pragma unroll
+    for (int i = 1; i < 8; ++i) m = fmaxf(m, part[i][c]);
+    p.sv[h * D + c] = __fdiv_rn(m, 448.0f);
+  }
+}
+
+// V -> E4M3(V / s_V[c]) (hardware conversion: round to nearest even).  Operand order: byte
+// 8 jj + e of (32-key block, channel) holds key 16 (e >> 2) + 4 jj + (e & 3) of the block.
+__global__ void __launch_bounds__(128) pf_vquant_kernel(PrefillParams p) {
+  const int b = blockIdx.x, h = blockIdx.y, c = threadIdx.x;
+  const uint32_t word = p.abits[(size_t)h * (p.Npad >> 5) + b];
+  const float s = p.sv[h * D + c];
+  uint32_t w[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) w[i] = 0;
+#pragma unroll
+  for (int kk = 0; kk < 32; ++kk) {
+    const int key = 32 * b + kk;
+    float x = 0.0f;
+    if (key < p.N && !((word >> kk) & 1u)) x = bf16_bits_to_f32(p.v[((size_t)h * p.N + key) * D + c]);
+    uint32_t code = 0;
+    if (s != 0.0f) code = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(__fdiv_rn(x, s), 0.0f, 0, false) & 0xffu;
+    const int byte = 8 * ((kk & 15) >> 2) + 4 * (kk >> 4) + (kk & 3);
+    w[byte >> 2] |= code << (8 * (byte & 3));
+  }
+  u32x4* dst = (u32x4*)(p.v8 + (((size_t)h * (p.Npad >> 5) + b) * D + c) * 32);
+  dst[0] = (u32x4){w[0], w[1], w[2], w[3]};
+  dst[1] = (u32x4){w[4], w[5], w[6], w[7]};
+}
+
+// ------------------------------------------------------------------ attention
+
+struct RowState {
+  float m[2];        // running max, log2 units, per 16-query block
+  f32x4 acc[2][8];   // O^T: channels 16 cb + 4 j + r, query l16
+  f32x4 lacc[2];     // row sums (all 4 entries equal)
+};
+
+// Online-softmax bookkeeping for one 16-query block and one tile: returns the value to
+// subtract inside exp2 (+inf for a row without a valid key in the tile) and rescales the
+// row state when its max moved.  tmax2 = tile max in log2 units (used only if `valid`).
+__device__ inline float os_update(RowState& st, int qb, bool valid, float tmax2, float shift) {
+  const float mold = st.m[qb];
+  const float mnew = valid ? fmaxf(mold, tmax2) : mold;
+  const float resc = (mnew == mold) ? 1.0f : __builtin_amdgcn_exp2f(mold - mnew);
+  st.m[qb] = mnew;
+  if (__builtin_amdgcn_ballot_w64(resc != 1.0f)) {
+#pragma unroll
+    for (int cb = 0; cb < 8; ++cb) st.acc[qb][cb] *= resc;
+    st.lacc[qb] *= resc;
+  }
+  return valid ? mnew - shift : INFINITY;
+}
+
+__device__ inline uint32_t pack_bf16x2(float a, float b) {
+  return (uint32_t)f32_to_bf16_bits(a) | ((uint32_t)f32_to_bf16_bits(b) << 16);
+}
+
+struct Ctx {
+  int h, hk, r0w, N, Npad, nb64, tid, l16, j;
+};
+
+// Quantized tile t: INT8 K rows [64 t, 64 t + 64) (row stride K8_LD) and the two 32-key
+// blocks of E4M3 V codes, copied as stored.
+__device__ inline void load_tile_q(const PrefillParams& p, const Ctx& c, uint8_t* lds, int t) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int ch = c.tid + 256 * i, row = ch >> 3, part = ch & 7;
+    *(u32x4*)(lds + row * K8_LD + 16 * part) =
+        *(const u32x4*)(p.k8 + ((size_t)c.hk * c.Npad + 64 * t + row) * D + 16 * part);
+  }
+  const uint8_t* vsrc = p.v8 + ((size_t)c.hk * (c.Npad >> 5) + 2 * t) * D * 32;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int ch = c.tid + 256 * i;
+    *(u32x4*)(lds + LDS_V + 16 * ch) = *(const u32x4*)(vsrc + 16 * ch);
+  }
+}
+
+// bf16 tile: K rows (row stride KB_LD) and V^T, for 64 keys given by key_of(row) (< 0 or
+// >= N: zeros).  V^T element (key row, channel ch) sits at ((row/32 * 128 + ch) * 4 + jj) * 8
+// + ee (bf16 units) with kk = row % 32, jj = (kk % 16) / 4, ee = 4 (kk / 16) + kk % 4.
+template <typename KeyOf>
+__device__ inline void load_tile_bf(const PrefillParams& p, const Ctx& c, uint8_t* lds, KeyOf key_of) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int ch = c.tid + 256 * i, row = ch >> 4, part = ch & 15;
+    const int key = key_of(row);
+    u32x4 kx = {0u, 0u, 0u, 0u}, vx = {0u, 0u, 0u, 0u};
+    if (key >= 0 && key < c.N) {
+      kx = *(const u32x4*)(p.k + ((size_t)c.hk * c.N + key) * D + 8 * part);
+      vx = *(const u32x4*)(p.v + ((size_t)c.hk * c.N + key) * D + 8 * part);
+    }
+    *(u32x4*)(lds + row * KB_LD + 16 * part) = kx;
+    const int kb32 = row >> 5, kk = row & 31, jj = (kk & 15) >> 2, ee = 4 * (kk >> 4) + (kk & 3);
+    uint16_t* vd = (uint16_t*)(lds + LDS_V) + ((kb32 * D + 8 * part) * 4 + jj) * 8 + ee;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      vd[(2 * e) * 32] = (uint16_t)(vx[e] & 0xffffu);
+      vd[(2 * e + 1) * 32] = (uint16_t)(vx[e] >> 16);
+    }
+  }
+}
+
+// One quantized tile for the wave's 32 queries.
+__device__ inline void compute_tile_q(const PrefillParams& p, const Ctx& c, const uint8_t* lds, int t,
+                                      const i32x4 (&qi)[2][2], float sq, const uint32_t* abits, RowState& st) {
+  const int kt0 = 64 * t;
+  if (kt0 > c.r0w + 31 - WIN) return;  // no key of the tile is in range for this wave
+  const bool interior = kt0 + 63 <= c.r0w - WIN;
+  const uint32_t w0 = abits[kt0 >> 5], w1 = abits[(kt0 >> 5) + 1];
+  float c2 = sq * p.sk[(size_t)c.hk * c.nb64 + t] * AL2;
+  c2 = c2 > 0.0f ? c2 : 1.0f;  // a zero scale means every valid dot is 0
+  i32x4 S2[2][4];
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    const uint32_t nib = ((kb < 2 ? w0 : w1) >> (16 * (kb & 1) + 4 * c.j)) & 0xfu;
+    i32x4 bias;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) bias[r] = ((nib >> r) & 1u) ? NEG_DOT : 0;
+    const i32x4 kf0 = *(const i32x4*)(lds + (16 * kb + c.l16) * K8_LD + 16 * c.j);
+    const i32x4 kf1 = *(const i32x4*)(lds + (16 * kb + c.l16) * K8_LD + 64 + 16 * c.j);
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      i32x4 acc = bias;
+      if (!interior) {
+        const int row = c.r0w + 16 * qb + c.l16;
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (kt0 + 16 * kb + 4 * c.j + r > row - WIN) acc[r] = NEG_DOT;
+      }
+      acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(kf0, qi[qb][0], acc, 0, 0, 0);
+      S2[qb][kb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(kf1, qi[qb][1], acc, 0, 0, 0);
+    }
+  }
+  i64 pk[2][2];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    int mi = NEG_DOT;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+      mi = max(mi, max(max(S2[qb][kb][0], S2[qb][kb][1]), max(S2[qb][kb][2], S2[qb][kb][3])));
+    mi = wave_max_i(mi);
+    const bool valid = mi > NEG_DOT / 2;
+    const float muse = os_update(st, qb, valid, (float)mi * c2, LOG2_448);
+    uint32_t pw[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      float pv[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        pv[r] = __builtin_amdgcn_exp2f(__builtin_fmaf((float)S2[qb][kb][r], c2, -muse));
+        if (c2 < C2_FAST_MIN && S2[qb][kb][r] <= NEG_DOT / 2) pv[r] = 0.0f;
+      }
+      const uint32_t w = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(pv[0], pv[1], 0, false);
+      pw[kb] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(pv[2], pv[3], (int)w, true);
+    }
+    pk[qb][0] = (i64)pw[0] | ((i64)pw[1] << 32);
+    pk[qb][1] = (i64)pw[2] | ((i64)pw[3] << 32);
+  }
+#pragma unroll
+  for (int cb = 0; cb < 8; ++cb) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const i64 vf = *(const i64*)(lds + LDS_V + ((ks * D + 16 * cb + c.l16) * 32 + 8 * c.j));
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+        st.acc[qb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(vf, pk[qb][ks], st.acc[qb][cb], 0, 0, 0);
+    }
+  }
+  const i64 ONES8 = 0x3838383838383838L;  // E4M3 1.0
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+      st.lacc[qb] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(ONES8, pk[qb][ks], st.lacc[qb], 0, 0, 0);
+}
+
+// One bf16 tile (anchors: ANCHOR = true, keys from the LDS list; window: 64 aligned keys
+// from kt0) for the wave's 32 queries.
+template <bool ANCHOR>
+__device__ inline void compute_tile_bf(const PrefillParams& p, const Ctx& c, const uint8_t* lds,
+                                       const int* anc_s, int kt0, RowState& st) {
+  int keyv[4][4];
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      keyv[kb][r] = ANCHOR ? anc_s[16 * kb + 4 * c.j + r] : kt0 + 16 * kb + 4 * c.j + r;
+  bf16x8 pb[2][2];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const int row = c.r0w + 16 * qb + c.l16;
+    const int rowc = row < c.N ? row : c.N - 1;  // padded rows: any finite query, never stored
+    const uint16_t* qrow = p.q + ((size_t)c.h * c.N + rowc) * D + 8 * c.j;
+    f32x4 S[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int key = keyv[kb][r];
+        const bool ok = ANCHOR ? (key >= 0 && key <= row - WIN) : (key <= row && key >= row - WIN + 1);
+        S[kb][r] = ok ? 0.0f : -INFINITY;
+      }
+    }
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const bf16x8 qfr = __builtin_bit_cast(bf16x8, *(const u32x4*)(qrow + 32 * ks));
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const bf16x8 kfr = *(const bf16x8*)(lds + (16 * kb + c.l16) * KB_LD + 2 * (32 * ks + 8 * c.j));
+        S[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kfr, qfr, S[kb], 0, 0, 0);
+      }
+    }
+    float mt = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) mt = fmaxf(mt, fmaxf(fmaxf(S[kb][0], S[kb][1]), fmaxf(S[kb][2], S[kb][3])));
+    mt = wave_max_f16(mt);
+    const bool valid = mt > -INFINITY;
+    const float muse = os_update(st, qb, valid, mt * AL2, 0.0f);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      uint32_t w[4];
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const f32x4 sv = S[2 * ks + hh];
+        float pv[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) pv[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[r], AL2, -muse));
+        w[2 * hh] = pack_bf16x2(pv[0], pv[1]);
+        w[2 * hh + 1] = pack_bf16x2(pv[2], pv[3]);
+      }
+      const u32x4 wv = {w[0], w[1], w[2], w[3]};
+      pb[qb][ks] = __builtin_bit_cast(bf16x8, wv);
+    }
+  }
+#pragma unroll
+  for (int cb = 0; cb < 8; ++cb) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const bf16x8 vf = *(const bf16x8*)(lds + LDS_V + ((ks * D + 16 * cb + c.l16) * 4 + c.j) * 16);
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+        st.acc[qb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb[qb][ks], st.acc[qb][cb], 0, 0, 0);
+    }
+  }
+  const bf16x8 ONESB = {(__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f,
+                        (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+      st.lacc[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ONESB, pb[qb][ks], st.lacc[qb], 0, 0, 0);
+}
+
+__global__ void __launch_bounds__(256, 2) pf_attn_kernel(PrefillParams p) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[LDS_TILE];
+  __shared__ int anc_s[64];
+  __shared__ float qmax[4];
+  __shared__ int nb_anchor_s;
+
+  const int nQB = p.Npad / WG_ROWS;
+  const int qblk = nQB - 1 - (int)blockIdx.x / p.Hq;  // longest rows first
+  Ctx c;
+  c.h = (int)blockIdx.x % p.Hq;
+  c.hk = c.h / p.G;
+  const int r0 = qblk * WG_ROWS;
+  c.tid = threadIdx.x;
+  const int wave = c.tid >> 6, lane = c.tid & 63;
+  c.l16 = lane & 15;
+  c.j = lane >> 4;
+  c.r0w = r0 + 32 * wave;
+  c.N = p.N;
+  c.Npad = p.Npad;
+  c.nb64 = p.Npad >> 6;
+
+  // ---- Q: bf16 operand fragments, block maximum, INT8 codes (also stored)
+  i32x4 qi[2][2];
+  float sq;
+  {
+    u32x4 qf[2][4];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const int row = c.r0w + 16 * qb + c.l16;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        qf[qb][ks] = row < c.N ? *(const u32x4*)(p.q + ((size_t)c.h * c.N + row) * D + 32 * ks + 8 * c.j)
+                               : (u32x4){0u, 0u, 0u, 0u};
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          amax = fmaxf(amax, fmaxf(fabsf(bf_lo(qf[qb][ks][e])), fabsf(bf_hi(qf[qb][ks][e]))));
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) amax = fmaxf(amax, shfl_xor_f(amax, o));
+    if (lane == 0) qmax[wave] = amax;
+    if (c.tid == 0) {
+      // anchors some row of the workgroup may use: a <= r0 + 127 - 128
+      const int32_t* anc = p.anchors + (size_t)c.hk * p.n_anchor;
+      const int lim = r0 + WG_ROWS - 1 - WIN;
+      int lo = 0, hi = p.n_anchor;
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (anc[mid] <= lim) lo = mid + 1; else hi = mid;
+      }
+      nb_anchor_s = lo;
+    }
+    __syncthreads();
+    sq = __fdiv_rn(fmaxf(qmax[wave], qmax[wave ^ 1]), 127.0f);
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+#pragma unroll
+      for (int s8 = 0; s8 < 2; ++s8) {
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const u32x4 x = qf[qb][2 * s8 + hh];
+          uint32_t w0 = 0, w1 = 0;
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            w0 |= (uint32_t)(int8_code(bf_lo(x[e]), sq) & 0xff) << (16 * e);
+            w0 |= (uint32_t)(int8_code(bf_hi(x[e]), sq) & 0xff) << (16 * e + 8);
+            w1 |= (uint32_t)(int8_code(bf_lo(x[2 + e]), sq) & 0xff) << (16 * e);
+            w1 |= (uint32_t)(int8_code(bf_hi(x[2 + e]), sq) & 0xff) << (16 * e + 8);
+          }
+          qi[qb][s8][2 * hh] = (int)w0;
+          qi[qb][s8][2 * hh + 1] = (int)w1;
+        }
+        const int row = c.r0w + 16 * qb + c.l16;
+        *(i32x4*)(p.q8 + ((size_t)c.h * c.Npad + row) * D + 64 * s8 + 16 * c.j) = qi[qb][s8];
+      }
+    }
+    if (lane == 0 && (wave & 1) == 0) p.sq[(size_t)c.h * c.nb64 + (c.r0w >> 6)] = sq;
+  }
+
+  RowState st;
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    st.m[qb] = -INFINITY;
+    st.lacc[qb] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int cb = 0; cb < 8; ++cb) st.acc[qb][cb] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  }
+
+  // ---- segment A: quantized tiles
+  const int lastA = r0 + WG_ROWS - 1 - WIN;
+  const int nA = lastA >= 0 ? (lastA >> 6) + 1 : 0;
+  const uint32_t* abits = p.abits + (size_t)c.hk * (c.Npad >> 5);
+  for (int t = 0; t < nA; ++t) {
+    __syncthreads();
+    load_tile_q(p, c, lds, t);
+    __syncthreads();
+    compute_tile_q(p, c, lds, t, qi, sq, abits, st);
+  }
+  // acc holds sum E4M3(448 p) * code(V): scale to values
+#pragma unroll
+  for (int cb = 0; cb < 8; ++cb) {
+    const f32x4 svc = *(const f32x4*)(p.sv + c.hk * D + 16 * cb + 4 * c.j) * (1.0f / 448.0f);
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) st.acc[qb][cb] *= svc;
+  }
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) st.lacc[qb] *= (1.0f / 448.0f);
+
+  // ---- segment B: anchor tiles (64 consecutive list entries each)
+  const int32_t* anc_g = p.anchors + (size_t)c.hk * p.n_anchor;
+  const int nB = (nb_anchor_s + 63) >> 6;
+  const int n_anchor = p.n_anchor;
+  for (int u = 0; u < nB; ++u) {
+    __syncthreads();
+    if (c.tid < 64) {
+      const int idx = 64 * u + c.tid;
+      anc_s[c.tid] = idx < n_anchor ? anc_g[idx] : -1;
+    }
+    load_tile_bf(p, c, lds, [&](int row) {
+      const int idx = 64 * u + row;
+      return idx < n_anchor ? anc_g[idx] : -1;
+    });
+    __syncthreads();
+    const int a0 = anc_s[0];
+    if (a0 >= 0 && a0 <= c.r0w + 31 - WIN) compute_tile_bf<true>(p, c, lds, anc_s, 0, st);
+  }
+
+  // ---- segment C: window tiles (aligned)
+  const int tC0 = max(0, r0 - WIN + 1) >> 6, tC1 = (r0 + WG_ROWS - 1) >> 6;
+  for (int t = tC0; t <= tC1; ++t) {
+    const int kt0 = 64 * t;
+    __syncthreads();
+    load_tile_bf(p, c, lds, [&](int row) { return kt0 + row; });
+    __syncthreads();
+    if (!(kt0 > c.r0w + 31 || kt0 + 63 < c.r0w - WIN + 1)) compute_tile_bf<false>(p, c, lds, anc_s, kt0, st);
+  }
+
+  // ---- epilogue: o = acc / l  (every real row has its own key in the window)
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const int row = c.r0w + 16 * qb + c.l16;
+    if (row >= c.N) continue;
+    const float inv = 1.0f / st.lacc[qb][0];
+    float* dst = p.o + ((size_t)c.h * c.N + row) * D + 4 * c.j;
+#pragma unroll
+    for (int cb = 0; cb < 8; ++cb) *(f32x4*)(dst + 16 * cb) = st.acc[qb][cb] * inv;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream) {
+  const int Hkv = p.Hkv;
+  hipLaunchKernelGGL(pf_bitmap_kernel, dim3(Hkv), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL(pf_kquant_kernel, dim3(p.Npad / KBLK, Hkv), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL(pf_vscale_kernel, dim3(Hkv), dim3(1024), 0, stream, p);
+  hipLaunchKernelGGL(pf_vquant_kernel, dim3(p.Npad / 32, Hkv), dim3(128), 0, stream, p);
+  hipLaunchKernelGGL(pf_attn_kernel, dim3((p.Npad / WG_ROWS) * p.Hq), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace hyq

@@ -194,16 +194,42 @@ int hyq_select_vlines(const hyq_shape_t* shape, hyq_cache_t* cache, const void* 
 int hyq_decode_attn(const hyq_cache_t* cache, const void* q, float* o, int32_t n_splits,
                     void* ws, size_t ws_bytes, hipStream_t stream);
 
-/* Hybrid prefill attention (HyQuant paper §4.2 Eq. 6-7, Alg. 2), causal, batch of one
-   sequence per call (shape->batch must be 1).  For query i: keys [i-127, i] and anchors
-   a <= i-128 use bf16 Q.K and bf16 P.V; every other key j <= i-128 uses INT8 Q.K (Q per
-   64-query block, K per 64-key block, symmetric, scale max|x|/127) and FP8 E4M3 P.V (P
-   scaled by 448, V with a per-channel scale max|V[:,c]|/448 over non-anchor keys).  One
-   online softmax, 64-key tiles, order: quantized tiles, anchor tiles, window tiles.
+/* Hybrid prefill attention (HyQuant paper §4.2 Eq. 6-7, Alg. 2), causal, one sequence per
+   call (shape->batch must be 1; Q head h reads KV head h / (Hq / Hkv)).
+   For query i: keys [i-127, i] and anchors a <= i-128 use bf16 Q.K and bf16 P.V; every
+   other key j <= i-128 uses INT8 Q.K and FP8 E4M3 P.V (Alg. 2 Stage 2):
+     Q: per 64-query block and Q head, scale s_Q = max|Q_blk| / 127 (fp32, IEEE divide),
+        code = clamp(rint(q / s_Q), -127, 127), 0 when s_Q = 0;
+     K: per 64-key block and KV head, same rule with the anchor rows left out of the
+        maximum (their codes are 0 and never used);
+     V: per channel and KV head, s_V[c] = max over non-anchor keys of |V[:,c]| / 448,
+        code = E4M3(v / s_V[c]) rounded to nearest even (0 when s_V[c] = 0);
+     score = dot_int32 * s_Q * s_K / sqrt(128); P = E4M3(448 p) / 448 on these keys and
+     bf16(p) on the bf16 keys, p = exp(score - running max) after the tile's max update.
+   One online softmax per row over 64-key tiles in the order: quantized tiles (ascending),
+   anchor tiles (64 consecutive entries of the anchor list), window tiles (aligned).
    q: device bf16 [Hq][len][128]; k, v: device bf16 [Hkv][len][128]; anchors: device int32
-   [Hkv][n_anchor] ascending inside [0, len-128) (nullable when n_anchor = 0);
-   o: device f32 [Hq][len][128].  ws: >= hyq_workspace_bytes(shape, HYQ_OP_PREFILL, len, 0).
-   Errors: INVALID, UNSUPPORTED, WORKSPACE, HIP. */
+   [Hkv][n_anchor], ascending and distinct inside [0, len-128) (nullable when n_anchor = 0;
+   other contents give unspecified results but no out-of-bounds access);
+   o: device f32 [Hq][len][128].
+   ws: device workspace of at least hyq_workspace_bytes(shape, HYQ_OP_PREFILL, len, 0)
+   bytes, no initialisation needed.  After the call it holds the operands, in this order,
+   each section starting at a multiple of 256 bytes (Np = len rounded up to 128):
+     q8   int8 [Hq][Np][128]        Q codes, operand order (below), rows >= len zero
+     sq   f32  [Hq][Np/64]          s_Q per 64-query block
+     k8   int8 [Hkv][Np][128]       K codes, operand order
+     sk   f32  [Hkv][Np/64]         s_K per 64-key block
+     v8   u8   [Hkv][Np/32][128][32] V codes: byte 8 j + e of (32-key block b, channel c)
+                                    is key 32 b + 16 (e >> 2) + 4 j + (e & 3)
+     sv   f32  [Hkv][128]           s_V
+     vmax f32  [Hkv][Np/64][128]    per-block max |V| over non-anchor keys
+     abits u32 [Hkv][Np/32]         anchor bitmap (bit j & 31 of word j >> 5)
+   Operand order of an INT8 row: byte 64 s + 16 j + 8 t + e holds channel
+   32 (2 s + t) + 8 j + e (s, t in {0,1}, j < 4, e < 8).
+   Calls sharing one workspace must not overlap in time (same stream is fine).
+   Five kernel launches.  Errors: INVALID (null pointers, len <= 0, n_anchor outside
+   [0, max(0, len-128)]), UNSUPPORTED (batch != 1, len > HYQ_PREFILL_MAX_LEN), WORKSPACE, HIP. */
+#define HYQ_PREFILL_MAX_LEN (1 << 20)
 int hyq_prefill_attn(const hyq_shape_t* shape, const void* q, const void* k, const void* v,
                      int32_t len, const int32_t* anchors, int32_t n_anchor, float* o, void* ws,
                      size_t ws_bytes, hipStream_t stream);

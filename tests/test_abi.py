@@ -97,3 +97,24 @@ def test_workspace_sizes(lib):
     assert lib.hyq_workspace_bytes(C.byref(s), _lib.HYQ_OP_DECODE, 0, 8) == 2 * 8 * 8 * 130 * 4
     bad = _shape(head_dim=64)
     assert lib.hyq_workspace_bytes(C.byref(bad), _lib.HYQ_OP_DECODE, 0, 8) == 0
+
+
+def test_prefill_workspace_layout_and_errors(lib):
+    from tests.gpu_layout import prefill_ws_offsets
+    one = _shape(batch=1, n_q_heads=32, n_kv_heads=8)
+    for N in (1, 127, 128, 129, 1000, 8192, 32768):
+        assert lib.hyq_workspace_bytes(C.byref(one), _lib.HYQ_OP_PREFILL, N, 0) == prefill_ws_offsets(32, 8, N)["total"]
+    assert lib.hyq_workspace_bytes(C.byref(one), _lib.HYQ_OP_PREFILL, 0, 0) == 0
+    assert lib.hyq_workspace_bytes(C.byref(one), _lib.HYQ_OP_PREFILL, (1 << 20) + 1, 0) == 0
+    need = prefill_ws_offsets(32, 8, 1000)["total"]
+    f = lib.hyq_prefill_attn
+    # batch != 1 -> UNSUPPORTED; null tensors / bad anchor counts -> INVALID; small ws -> WORKSPACE
+    assert f(C.byref(_shape(batch=2)), 0x10, 0x20, 0x30, 1000, None, 0, 0x40, 0x50, need, None) == 2
+    assert f(C.byref(one), None, 0x20, 0x30, 1000, None, 0, 0x40, 0x50, need, None) == 1
+    assert f(C.byref(one), 0x10, 0x20, 0x30, 0, None, 0, 0x40, 0x50, need, None) == 1
+    assert f(C.byref(one), 0x10, 0x20, 0x30, 1000, 0x60, 873, 0x40, 0x50, need, None) == 1
+    assert f(C.byref(one), 0x10, 0x20, 0x30, 1000, None, 5, 0x40, 0x50, need, None) == 1
+    assert f(C.byref(one), 0x10, 0x20, 0x30, 100, 0x60, 1, 0x40, 0x50, need, None) == 1
+    assert f(C.byref(one), 0x10, 0x20, 0x30, 1000, None, 0, 0x40, 0x50, need - 1, None) == 4
+    assert f(C.byref(one), 0x10, 0x20, 0x30, 1000, None, 0, 0x40, None, need, None) == 4
+    assert f(C.byref(one), 0x10, 0x20, 0x30, (1 << 20) + 1, None, 0, 0x40, 0x50, need, None) == 2

@@ -1,0 +1,156 @@
+"""GPU parity of the hybrid prefill (hyq_prefill_attn, HyQuant paper §4.2 Eq. 6-7, Alg. 2)
+against the oracle's step-by-step emulation.
+
+Bar:
+  * operand quantization -- INT8 Q and K codes, E4M3 V codes, their fp32 scales and the anchor
+    bitmap -- bit-exact (read back from the documented workspace layout);
+  * outputs within 2e-3 max-abs and 1e-3 relative L2 of ``oracle.attention.prefill_ref``,
+    which takes the P rounding decisions in fp32 like the kernel.  The P codes themselves are
+    not compared: the kernel's exp2 and the oracle's exp may land on opposite sides of an
+    E4M3 rounding boundary for a rare element, and that effect lies inside the output bound.
+"""
+import numpy as np
+import pytest
+import torch
+
+from hybrid_precision_kv_amd import api as hq
+from hybrid_precision_kv_amd import synth
+from oracle import attention as att
+from oracle import numerics as nm
+from oracle import policy as pol
+from tests.gpu_layout import read_prefill_ws
+from tests.test_gpu_decode import dev
+
+pytestmark = pytest.mark.gpu
+
+MAX_ABS, REL_L2 = 2e-3, 1e-3
+
+
+def anchors_dense(d, Hq, Hkv, N, pct=5):
+    """Prefill anchors: the oracle selector over the last 64 queries of each group (dense keys)."""
+    g = Hq // Hkv
+    k = pol.k_rule(N, pct_num=pct)
+    A = np.zeros((Hkv, k), np.int32)
+    for h in range(Hkv):
+        if k:
+            A[h], _ = pol.select_dense(d["K"][h], d["Q"][h * g:(h + 1) * g, max(0, N - 64):], pct_num=pct)
+    return A
+
+
+def run_gpu(d, A, Hq, Hkv, N):
+    shape = hq.Shape.for_context(1, Hq, Hkv, N)
+    ws = hq.prefill_workspace(shape, N)
+    anc = torch.from_numpy(np.ascontiguousarray(A)).cuda() if A.shape[1] else None
+    o = hq.prefill_attn(shape, dev(d["Q"]), dev(d["K"]), dev(d["V"]), anchors=anc, ws=ws)
+    torch.cuda.synchronize()
+    return o.cpu().numpy(), read_prefill_ws(ws.cpu().numpy(), Hq, Hkv, N)
+
+
+def check_operands(w, qz, A, N):
+    nb = (N + 63) // 64
+    assert np.array_equal(w["q8"][:, :N], qz["q8"]), "Q codes"
+    assert not w["q8"][:, N:].any(), "padded Q rows"
+    assert np.array_equal(w["sq"][:, :nb].view(np.uint32), qz["sq"].view(np.uint32)), "s_Q"
+    assert np.array_equal(w["k8"][:, :N], qz["k8"]), "K codes"
+    assert np.array_equal(w["sk"][:, :nb].view(np.uint32), qz["sk"].view(np.uint32)), "s_K"
+    assert np.array_equal(w["sv"].view(np.uint32), qz["sv"].view(np.uint32)), "s_V"
+    assert np.array_equal(nm.e4m3_value(w["v8"][:, :N]), qz["v8"]), "V codes"
+    bits = np.zeros(w["abits"].shape, np.uint32)
+    for h in range(A.shape[0]):
+        for a in A[h]:
+            bits[h, a >> 5] |= np.uint32(1 << (int(a) & 31))
+    assert np.array_equal(w["abits"], bits), "anchor bitmap"
+
+
+def check_out(o, ref, label, vscale=1.0):
+    """vscale: how much larger than the unit-variance inputs' (|V| up to about 4.5) the values
+    are; an output error (a rare P rounding flip times a value) scales with them."""
+    m = ~np.isnan(ref)
+    assert m.any()
+    diff = np.abs(o[m] - ref[m])
+    rel = np.linalg.norm(o[m] - ref[m]) / np.linalg.norm(ref[m])
+    print(f"[{label}] max-abs {diff.max():.3g} rel-L2 {rel:.3g}")
+    assert diff.max() <= MAX_ABS * vscale and rel <= REL_L2, label
+
+
+def parity(d, A, Hq, Hkv, N, label, blocks=None, heads=None, vscale=1.0):
+    print(f"[case] {label} Hq={Hq} Hkv={Hkv} N={N} k={A.shape[1]}", flush=True)
+    o, w = run_gpu(d, A, Hq, Hkv, N)
+    qz = att.prefill_quantize(d["Q"], d["K"], d["V"], A)
+    check_operands(w, qz, A, N)
+    ref = att.prefill_ref(d["Q"], d["K"], d["V"], A, blocks=blocks, heads=heads, qz=qz)
+    check_out(o, ref, label, vscale)
+    return o
+
+
+@pytest.mark.parametrize("Hq,Hkv,N,pct", [(4, 1, 1000, 5), (8, 2, 1500, 5), (2, 1, 700, 10),
+                                          (16, 1, 600, 5), (8, 8, 900, 5)])
+def test_prefill_parity(Hq, Hkv, N, pct):
+    d = synth.gen_prefill(5000 + N, Hq, Hkv, N)
+    parity(d, anchors_dense(d, Hq, Hkv, N, pct), Hq, Hkv, N, f"prefill pct={pct}")
+
+
+@pytest.mark.parametrize("N", [1, 5, 64, 127, 128, 129, 191, 192, 255, 256, 257, 320])
+def test_prefill_edge_lengths(N):
+    d = synth.gen_prefill(5100 + N, 2, 1, N)
+    parity(d, anchors_dense(d, 2, 1, N), 2, 1, N, f"edge N={N}")
+
+
+def test_prefill_no_anchors_and_all_anchors():
+    d = synth.gen_prefill(5200, 4, 2, 700)
+    parity(d, np.zeros((2, 0), np.int32), 4, 2, 700, "no anchors")
+    d = synth.gen_prefill(5201, 4, 2, 400)
+    A = np.tile(np.arange(400 - 128, dtype=np.int32), (2, 1))  # every candidate is an anchor
+    parity(d, A, 4, 2, 400, "all anchors")
+
+
+def test_prefill_degenerate_scales():
+    """A zero query block (s_Q = 0), a zero key block outside the anchors (s_K = 0), a zero V
+    channel (s_V = 0), then tiny-magnitude Q and K (the masked-score path for tiny scales)."""
+    N = 600
+    d = synth.gen_prefill(5300, 4, 1, N)
+    A = anchors_dense(d, 4, 1, N)
+    zero = nm.f32_to_bf16(np.zeros(128, np.float32))[0]
+    d["Q"][1, 128:192] = zero
+    blk = 3
+    rows = [r for r in range(64 * blk, 64 * blk + 64) if r not in set(A[0])]
+    d["K"][0, rows] = zero
+    d["V"][0, :, 17] = zero
+    parity(d, A, 4, 1, N, "zero blocks")
+    tiny = synth.gen_prefill(5301, 4, 1, N)
+    for name in ("Q", "K"):
+        x = nm.bf16_to_f32(tiny[name]) * np.float32(1e-3)
+        tiny[name] = nm.f32_to_bf16(x)
+    parity(tiny, anchors_dense(tiny, 4, 1, N), 4, 1, N, "tiny Q/K")
+
+
+def test_prefill_e4m3_ties():
+    """V values on E4M3 rounding midpoints (s_V = 1 exactly): ties must go to the even code."""
+    N = 300
+    d = synth.gen_prefill(5400, 2, 1, N)
+    V = nm.bf16_to_f32(d["V"])[0]
+    rng = np.random.default_rng(7)
+    vals = nm.e4m3_decode_table()[:126]
+    mids = ((vals[:-1] + vals[1:]) / 2).astype(np.float32)
+    mids = mids[nm.bf16_to_f32(nm.f32_to_bf16(mids)) == mids]  # midpoints bf16 can hold
+    V[:, :] = rng.choice(mids, size=V.shape) * rng.choice([-1, 1], size=V.shape)
+    V[0, :] = 448.0  # channel maxima 448 -> s_V = 1
+    d["V"][0] = nm.f32_to_bf16(V.astype(np.float32))
+    parity(d, np.zeros((1, 0), np.int32), 2, 1, N, "e4m3 ties", vscale=448 / 4.5)
+
+
+def test_prefill_deterministic():
+    d = synth.gen_prefill(5500, 4, 1, 800)
+    A = anchors_dense(d, 4, 1, 800)
+    a, _ = run_gpu(d, A, 4, 1, 800)
+    b, _ = run_gpu(d, A, 4, 1, 800)
+    assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("N,blocks,heads", [(8192, [0, 2, 64, 127], [0, 5, 31]),
+                                            (32768, [0, 255, 511], [0, 31])])
+def test_prefill_full_size_sampled(N, blocks, heads):
+    """Hybrid-prefill workload shape: 32 Q / 8 KV heads, head_dim 128, 5% anchors from the last
+    64 queries.  Operands compared in full, outputs on sampled (64-query block, head) pairs."""
+    d = synth.gen_prefill(5600 + N, 32, 8, N)
+    parity(d, anchors_dense(d, 32, 8, N), 32, 8, N, f"full N={N}", blocks=blocks, heads=heads)
