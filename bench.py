@@ -48,6 +48,9 @@ def parse():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 1 GiB device copy (PMC byte-counter calibration)")
     ap.add_argument("--seed", type=int, default=3000)
+    ap.add_argument("--no-rows", action="store_true",
+                    help="skip the other hot-path rows (append, selector/refresh, prefill)")
+    ap.add_argument("--prefill-lens", default="8192,32768")
     return ap.parse_args()
 
 
@@ -127,6 +130,129 @@ def algorithmic_bytes(cache, B, Hkv, Hq):
     n_win = min(c["len"], W)
     per_head = 160 * c["n_int4"] + 512 * (c["n_anchor"] + c["n_staged"] + n_win)
     return B * Hkv * per_head + B * Hq * D * (2 + 4)
+
+
+def timed(torch, fn, reps, warm=2):
+    """Mean and min microseconds of fn() over reps launches (events on the current stream)."""
+    for _ in range(warm):
+        fn()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in evs:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    t = [a.elapsed_time(b) * 1e3 for a, b in evs]
+    return sum(t) / len(t), min(t)
+
+
+def bench_maintenance(torch, hq, cache, B, Hkv, G, L, gen, dev, ws, out, splits):
+    """Decode steps with cache maintenance on one layer: per token hyq_append_token +
+    hyq_decode_attn, and every 64 tokens hyq_select_vlines(apply=1) at the 5% rule (the
+    refresh cadence of the techwalker.com article on HyQuant)."""
+    Hq = Hkv * G
+    toks = [((torch.randn(B, Hkv, D, generator=gen, device=dev)).to(torch.bfloat16),
+             (torch.randn(B, Hkv, D, generator=gen, device=dev)).to(torch.bfloat16),
+             (torch.randn(B, Hq, D, generator=gen, device=dev)).to(torch.bfloat16)) for _ in range(64)]
+    q = toks[0][2]
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    t_app, t_dec = 0.0, 0.0
+    for i in range(64):
+        k_t, v_t, q_t = toks[i]
+        ev[0].record()
+        hq.append_token(cache, k_t, v_t, q_t)
+        ev[1].record()
+        hq.decode_attn(cache, q_t, splits, out, ws)
+        ev[2].record()
+        torch.cuda.synchronize()
+        t_app += ev[0].elapsed_time(ev[1]) * 1e3
+        t_dec += ev[1].elapsed_time(ev[2]) * 1e3
+    k = hq.anchor_count(cache.len)
+    ev[0].record()
+    hq.select_vlines(cache.shape, k, cache=cache, apply=True)
+    ev[1].record()
+    torch.cuda.synchronize()
+    t_ref = ev[0].elapsed_time(ev[1]) * 1e3
+    return {"append_us": round(t_app / 64, 2), "decode_us_with_staging": round(t_dec / 64, 2),
+            "select_refresh_us": round(t_ref, 1), "anchors_after_refresh": k,
+            "us_per_token_amortized": round((t_app + t_dec + t_ref) / 64, 2),
+            "note": f"one layer, bs{B} ctx {L}+64, refresh every 64 tokens"}
+
+
+def bench_selector(torch, hq, gen, dev, B=4, Hq=64, Hkv=8, L=32768):
+    """Selector and cache maintenance at Qwen3-32B shape (64 Q / 8 KV heads, batch 4, 32K):
+    hyq_select_vlines scores + top-k at 1% / 5% / 10%, then apply (refresh), then 64 appends."""
+    G = Hq // Hkv
+    shape = hq.Shape.for_context(B, Hq, Hkv, L + 64, 10)
+    cache, _ = make_layer(torch, hq, shape, B, Hkv, G, L, gen, dev)
+    res = {"workload": f"qwen3-32b-shape select bs{B} ctx{L} hq{Hq} hkv{Hkv}"}
+    for pct in (1, 5, 10):
+        k = hq.anchor_count(L, pct)
+        us, _ = timed(torch, lambda: hq.select_vlines(shape, k, cache=cache), 5)
+        res[f"select_{pct}pct_us"] = round(us, 1)
+    k_t = torch.randn(B, Hkv, D, generator=gen, device=dev).to(torch.bfloat16)
+    q_t = torch.randn(B, Hq, D, generator=gen, device=dev).to(torch.bfloat16)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    ev[0].record()
+    for _ in range(64):
+        hq.append_token(cache, k_t, k_t, q_t)
+    ev[1].record()
+    hq.select_vlines(shape, hq.anchor_count(cache.len, 5), cache=cache, apply=True)
+    ev[2].record()
+    torch.cuda.synchronize()
+    res["append_64_us"] = round(ev[0].elapsed_time(ev[1]) * 1e3, 1)
+    res["refresh_apply_us"] = round(ev[1].elapsed_time(ev[2]) * 1e3, 1)
+    del cache
+    return res
+
+
+def prefill_ops(anchors_row, N, Hq):
+    """Algorithmic MFMA work of the hybrid prefill (per Q head: every (query, key) pair the
+    method visits, QK^T and PV at 2 x 128 multiply-adds each): quantized pairs j <= i-128 not
+    anchors; bf16 pairs = anchors a <= i-128 plus the window min(i+1, 128)."""
+    import numpy as np
+    a = np.sort(np.asarray(anchors_row))
+    i = np.arange(N)
+    n_before = np.maximum(0, i - W + 1)
+    n_anc = np.searchsorted(a, i - W, side="right")
+    n_win = np.minimum(i + 1, W)
+    per_pair = 2 * 2 * D
+    ops8 = float((n_before - n_anc).sum()) * Hq * per_pair
+    opsb = float((n_anc + n_win).sum()) * Hq * per_pair
+    return ops8, opsb
+
+
+def bench_prefill(torch, hq, gen, dev, N, Hq=32, Hkv=8):
+    """Hybrid prefill, one sequence of N tokens, 32 Q / 8 KV heads; anchors = the library's
+    selector over the last 64 queries (dense keys), 5% rule."""
+    G = Hq // Hkv
+    u = torch.randn(Hkv, D, generator=gen, device=dev)
+    u = u / u.norm(dim=-1, keepdim=True)
+    K = torch.randn(Hkv, N, D, generator=gen, device=dev)
+    pos = torch.cat([torch.zeros(Hkv, 1, dtype=torch.long, device=dev),
+                     1 + torch.rand(Hkv, N - W - 1, generator=gen, device=dev).argsort(dim=1)[:, :15]], dim=1)
+    K[torch.arange(Hkv, device=dev)[:, None], pos] += 4.0 * u[:, None, :]
+    K = K.to(torch.bfloat16)
+    V = torch.randn(Hkv, N, D, generator=gen, device=dev).to(torch.bfloat16)
+    Q = (2.0 * u.repeat_interleave(G, dim=0)[:, None, :] + torch.randn(Hq, N, D, generator=gen, device=dev)).to(torch.bfloat16)
+    shape = hq.Shape.for_context(1, Hq, Hkv, N)
+    k = hq.anchor_count(N)
+    anchors = hq.select_vlines(shape, k, dense_k=K[None], proxy=Q[None, :, N - 64:].contiguous())[0].contiguous()
+    ws = hq.prefill_workspace(shape, N, dev)
+    o = torch.empty(Hq, N, D, dtype=torch.float32, device=dev)
+    reps = 10 if N <= 8192 else 3
+    us, us_min = timed(torch, lambda: hq.prefill_attn(shape, Q, K, V, anchors=anchors, out=o, ws=ws), reps)
+    ops8, opsb = prefill_ops(anchors[0].cpu().numpy(), N, Hq)
+    t_roof = ops8 / 5.0e15 + opsb / 2.5e15
+    del K, V, Q, o, ws
+    return {"workload": f"hybrid prefill N{N} hq{Hq} hkv{Hkv} anchors{k}", "us_per_call": round(us, 1),
+            "us_min": round(us_min, 1), "tokens_per_s": round(N / (us * 1e-6), 1),
+            "roofline": {"bound": "mfma", "achieved": round((ops8 + opsb) / (us * 1e-6) / 1e12, 1),
+                         "peak": round((ops8 + opsb) / t_roof / 1e12, 1), "unit": "TFLOP/s",
+                         "frac": round(t_roof / (us * 1e-6), 4), "traffic": None,
+                         "ops_int8_fp8": ops8, "ops_bf16": opsb,
+                         "peak_basis": "int8/fp8 5.0 POP/s and bf16 2.5 PFLOP/s dense, blended by op mix"}}
 
 
 def cpu_baseline(args, G, bytes_per_head):
@@ -239,13 +365,26 @@ def main():
                    "splits": args.splits or "auto", "bytes_per_step": nbytes},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "kernel": "decode_split_kernel", "kernel_us_mean": round(mean_us, 2),
+                     "kernel": "hyq_decode_attn (split-K kernel + merge kernel, timed together)",
+                     "kernel_us_mean": round(mean_us, 2),
                      "kernel_us_p50": round(per[len(per) // 2], 2), "kernel_us_p90": round(per[int(0.9 * len(per))], 2)},
         "wall_s_timed": round(wall, 3),
     }
+    c0 = layers[0][0]
+    cpu_bytes_per_head = 160 * c0.n_int4 + 512 * (c0.n_anchor + min(L, W)) + G * D * 6
+    if not args.no_rows:
+        rows = {}
+        rows["decode_with_maintenance"] = bench_maintenance(torch, hq, layers[0][0], B, Hkv, G, L, gen, dev, ws,
+                                                            out, args.splits)
+        del layers, c0
+        torch.cuda.empty_cache()
+        for n in [int(x) for x in args.prefill_lens.split(",") if x]:
+            rows[f"prefill_{n}"] = bench_prefill(torch, hq, gen, dev, n)
+            print(f"[bench] prefill N={n}: {rows[f'prefill_{n}']['us_per_call']} us", file=sys.stderr, flush=True)
+        rows["selector"] = bench_selector(torch, hq, gen, dev)
+        line["rows"] = rows
     if not args.no_cpu_baseline:
-        per_head = 160 * layers[0][0].n_int4 + 512 * (layers[0][0].n_anchor + min(L, W)) + G * D * 6
-        line["cpu_baseline"] = cpu_baseline(args, G, per_head)
+        line["cpu_baseline"] = cpu_baseline(args, G, cpu_bytes_per_head)
     print(json.dumps(line), flush=True)
 
 

@@ -100,7 +100,7 @@ SelectWs select_ws(const hyq_shape_t* s, int32_t len) {
 
 // prefill workspace layout (sections in this order, each rounded up to 256 bytes)
 struct PrefillWs {
-  size_t q8, sq, k8, sk, v8, sv, vmax, abits, total;
+  size_t q8, sq, k8, sk, v8, sv, vmax, abits, vt16, ka16, va16, total;
   int Npad;
 };
 PrefillWs prefill_ws(const hyq_shape_t* s, int32_t len) {
@@ -116,7 +116,11 @@ PrefillWs prefill_ws(const hyq_shape_t* s, int32_t len) {
   w.sv = w.v8 + r256(Hkv * Np * D);
   w.vmax = w.sv + r256(Hkv * D * 4);
   w.abits = w.vmax + r256(Hkv * (Np / 64) * D * 4);
-  w.total = w.abits + r256(Hkv * (Np / 32) * 4);
+  w.vt16 = w.abits + r256(Hkv * (Np / 32) * 4);
+  const size_t Ac = (size_t)(s->anchor_cap + 63) / 64 * 64;
+  w.ka16 = w.vt16 + r256(Hkv * Np * D * 2);
+  w.va16 = w.ka16 + r256(Hkv * Ac * D * 2);
+  w.total = w.va16 + r256(Hkv * Ac * D * 2);
   return w;
 }
 
@@ -371,6 +375,7 @@ int hyq_prefill_attn(const hyq_shape_t* shape, const void* q, const void* k, con
   if (len > HYQ_PREFILL_MAX_LEN) return HYQ_ERR_UNSUPPORTED;
   const int P = len > W ? len - W : 0;
   if (n_anchor > P || (n_anchor > 0 && !anchors)) return HYQ_ERR_INVALID;
+  if (n_anchor > shape->anchor_cap) return HYQ_ERR_CAPACITY;
   const PrefillWs w = prefill_ws(shape, len);
   if (!ws || ws_bytes < w.total) return HYQ_ERR_WORKSPACE;
   char* wb = (char*)ws;
@@ -394,6 +399,10 @@ int hyq_prefill_attn(const hyq_shape_t* shape, const void* q, const void* k, con
   p.sv = (float*)(wb + w.sv);
   p.vmax = (float*)(wb + w.vmax);
   p.abits = (uint32_t*)(wb + w.abits);
+  p.vt16 = (uint16_t*)(wb + w.vt16);
+  p.ka16 = (uint16_t*)(wb + w.ka16);
+  p.va16 = (uint16_t*)(wb + w.va16);
+  p.n_anchor_pad = (n_anchor + 63) / 64 * 64;
   if (hyq::launch_prefill(p, stream) != hipSuccess) return HYQ_ERR_HIP;
   return HYQ_OK;
 }

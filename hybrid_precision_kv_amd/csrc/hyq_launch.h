@@ -89,6 +89,10 @@ struct PrefillParams {
   uint8_t* v8; float* sv;   // V E4M3 codes (operand order) and per-channel scales
   float* vmax;              // per-64-key-block channel maxima of |V| (non-anchor)
   uint32_t* abits;          // anchor bitmap
+  uint16_t* vt16;           // V^T bf16 in the bf16 MFMA operand order, all keys
+  uint16_t* ka16;           // anchor K rows (list order), bf16
+  uint16_t* va16;           // anchor V^T (list order), bf16, operand order
+  int n_anchor_pad;         // n_anchor rounded up to 64 (rows of ka16 / va16 written)
 };
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream);
 

@@ -36,8 +36,15 @@ constexpr float LOG2_448 = 8.807354922057604f;
 constexpr float C2_FAST_MIN = 1e-6f;  // below: masked INT8 scores are zeroed explicitly
 constexpr int K8_LD = 144;        // LDS row stride (bytes) of the INT8 K tile
 constexpr int KB_LD = 272;        // LDS row stride (bytes) of the bf16 K tile
-constexpr int LDS_V = 64 * KB_LD; // V tile offset
-constexpr int LDS_TILE = LDS_V + 16384;
+constexpr int LDS_V = 64 * KB_LD; // V tile offset (bf16 tiles)
+constexpr int LDS_BF = LDS_V + 16384;
+// quantized tiles are double-buffered: buffer b at b * LDS_QBUF, V codes at + LDS_QV
+constexpr int LDS_QV = 64 * K8_LD;
+constexpr int LDS_QBUF = LDS_QV + 8192;
+constexpr int LDS_TILE = 2 * LDS_QBUF > LDS_BF ? 2 * LDS_QBUF : LDS_BF;
+// INT8 Q codes of the workgroup's 128 queries (operand order), after the tile buffers
+constexpr int LDS_Q8 = LDS_TILE;
+constexpr int LDS_TOTAL = LDS_Q8 + 128 * K8_LD;
 
 typedef long i64;
 
@@ -52,13 +59,25 @@ __device__ inline int int8_code(float x, float s) {
   return (int)c;
 }
 
-__device__ inline int wave_max_i(int v) {
-  v = max(v, __shfl_xor(v, 16));
-  return max(v, __shfl_xor(v, 32));
+// value of lane 0 (bit-exact; tells the compiler the value is wave-uniform)
+__device__ inline float uniform_f(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, x)));
 }
-__device__ inline float wave_max_f16(float v) {  // over the 4 lane groups holding one column
-  v = fmaxf(v, shfl_xor_f(v, 16));
-  return fmaxf(v, shfl_xor_f(v, 32));
+
+// Maximum over the 4 lanes l, l^16, l^32, l^48 (one MFMA column).  v_permlane32_swap(v, v)
+// returns (v[l], v[l+32]) on lanes < 32 and (v[l-32], v[l]) above; v_permlane16_swap does the
+// same between the two halves of each 32-lane half -- VALU ops, no LDS round trip.
+__device__ inline int wave_max_i(int v) {
+  const auto a = __builtin_amdgcn_permlane32_swap((unsigned)v, (unsigned)v, false, false);
+  v = max((int)a[0], (int)a[1]);
+  const auto b = __builtin_amdgcn_permlane16_swap((unsigned)v, (unsigned)v, false, false);
+  return max((int)b[0], (int)b[1]);
+}
+__device__ inline float wave_max_f16(float v) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
 // ------------------------------------------------------------------ operand quantization
@@ -159,28 +178,67 @@ __global__ void __launch_bounds__(1024) pf_vscale_kernel(PrefillParams p) {
   }
 }
 
-// V -> E4M3(V / s_V[c]) (hardware conversion: round to nearest even).  Operand order: byte
-// 8 jj + e of (32-key block, channel) holds key 16 (e >> 2) + 4 jj + (e & 3) of the block.
+// V -> E4M3(V / s_V[c]) (hardware conversion: round to nearest even).  Operand order: per
+// 32-key block, [jj][channel][8 bytes]; byte e of (jj, channel) holds key 16 (e >> 2) + 4 jj +
+// (e & 3) of the block.  One lane group's 8-byte fragments of 16 channels are then 128
+// contiguous bytes (no LDS bank conflicts).
 __global__ void __launch_bounds__(128) pf_vquant_kernel(PrefillParams p) {
   const int b = blockIdx.x, h = blockIdx.y, c = threadIdx.x;
   const uint32_t word = p.abits[(size_t)h * (p.Npad >> 5) + b];
   const float s = p.sv[h * D + c];
-  uint32_t w[8];
+  uint32_t w[8], raw[16];
 #pragma unroll
   for (int i = 0; i < 8; ++i) w[i] = 0;
 #pragma unroll
+  for (int i = 0; i < 16; ++i) raw[i] = 0;
+#pragma unroll
   for (int kk = 0; kk < 32; ++kk) {
     const int key = 32 * b + kk;
+    const uint16_t vb = key < p.N ? p.v[((size_t)h * p.N + key) * D + c] : (uint16_t)0;
+    const int slot = 8 * ((kk & 15) >> 2) + 4 * (kk >> 4) + (kk & 3);  // 8 jj + e
+    raw[slot >> 1] |= (uint32_t)vb << (16 * (slot & 1));
     float x = 0.0f;
-    if (key < p.N && !((word >> kk) & 1u)) x = bf16_bits_to_f32(p.v[((size_t)h * p.N + key) * D + c]);
+    if (key < p.N && !((word >> kk) & 1u)) x = bf16_bits_to_f32(vb);
     uint32_t code = 0;
     if (s != 0.0f) code = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(__fdiv_rn(x, s), 0.0f, 0, false) & 0xffu;
-    const int byte = 8 * ((kk & 15) >> 2) + 4 * (kk >> 4) + (kk & 3);
+    const int byte = 8 * ((kk & 15) >> 2) + 4 * (kk >> 4) + (kk & 3);  // 8 jj + e
     w[byte >> 2] |= code << (8 * (byte & 3));
   }
-  u32x4* dst = (u32x4*)(p.v8 + (((size_t)h * (p.Npad >> 5) + b) * D + c) * 32);
-  dst[0] = (u32x4){w[0], w[1], w[2], w[3]};
-  dst[1] = (u32x4){w[4], w[5], w[6], w[7]};
+  uint8_t* blk = p.v8 + ((size_t)h * (p.Npad >> 5) + b) * D * 32;
+  uint16_t* tblk = p.vt16 + ((size_t)h * (p.Npad >> 5) + b) * D * 32;
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj) {
+    *(uint2*)(blk + (jj * D + c) * 8) = make_uint2(w[2 * jj], w[2 * jj + 1]);
+    *(u32x4*)(tblk + (jj * D + c) * 8) = (u32x4){raw[4 * jj], raw[4 * jj + 1], raw[4 * jj + 2], raw[4 * jj + 3]};
+  }
+}
+
+// Anchor gather: K rows (list order) and V^T in the bf16 operand order, for list entries
+// [0, n_anchor_pad); entries past n_anchor (or outside [0, N)) are zero.
+__global__ void __launch_bounds__(128) pf_agather_kernel(PrefillParams p) {
+  const int b = blockIdx.x, h = blockIdx.y, c = threadIdx.x;
+  const int32_t* anc = p.anchors + (size_t)h * p.n_anchor;
+  const int Ac = p.n_anchor_pad;
+  uint32_t raw[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) raw[i] = 0;
+#pragma unroll
+  for (int kk = 0; kk < 32; ++kk) {
+    const int idx = 32 * b + kk;
+    const int a = idx < p.n_anchor ? anc[idx] : -1;
+    uint16_t kb = 0, vb = 0;
+    if (a >= 0 && a < p.N) {
+      kb = p.k[((size_t)h * p.N + a) * D + c];
+      vb = p.v[((size_t)h * p.N + a) * D + c];
+    }
+    p.ka16[((size_t)h * Ac + idx) * D + c] = kb;
+    const int slot = 8 * ((kk & 15) >> 2) + 4 * (kk >> 4) + (kk & 3);
+    raw[slot >> 1] |= (uint32_t)vb << (16 * (slot & 1));
+  }
+  uint16_t* tblk = p.va16 + ((size_t)h * (Ac >> 5) + b) * D * 32;
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj)
+    *(u32x4*)(tblk + (jj * D + c) * 8) = (u32x4){raw[4 * jj], raw[4 * jj + 1], raw[4 * jj + 2], raw[4 * jj + 3]};
 }
 
 // ------------------------------------------------------------------ attention
@@ -212,69 +270,73 @@ __device__ inline uint32_t pack_bf16x2(float a, float b) {
 }
 
 struct Ctx {
-  int h, hk, r0w, N, Npad, nb64, tid, l16, j;
+  int h, hk, r0w, N, Npad, nb64, tid, wave, l16, j;
 };
 
-// Quantized tile t: INT8 K rows [64 t, 64 t + 64) (row stride K8_LD) and the two 32-key
-// blocks of E4M3 V codes, copied as stored.
-__device__ inline void load_tile_q(const PrefillParams& p, const Ctx& c, uint8_t* lds, int t) {
+// Quantized tile t: INT8 K rows [64 t, 64 t + 64) (row stride K8_LD in LDS) and the two
+// 32-key blocks of E4M3 V codes, copied as stored.  fetch: global -> registers (issued one
+// tile ahead), store: registers -> LDS.
+struct TileQRegs {
+  u32x4 k[2], v[2];
+  uint32_t w0, w1;  // anchor bitmap words of the tile
+  float sk;         // K scale of the tile
+};
+__device__ inline void fetch_tile_q(const PrefillParams& p, const Ctx& c, int t, TileQRegs& r) {
+  const uint32_t* ab = p.abits + (size_t)c.hk * (c.Npad >> 5) + 2 * t;
+  r.w0 = ab[0];
+  r.w1 = ab[1];
+  r.sk = p.sk[(size_t)c.hk * c.nb64 + t];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int ch = c.tid + 256 * i, row = ch >> 3, part = ch & 7;
-    *(u32x4*)(lds + row * K8_LD + 16 * part) =
-        *(const u32x4*)(p.k8 + ((size_t)c.hk * c.Npad + 64 * t + row) * D + 16 * part);
+    r.k[i] = *(const u32x4*)(p.k8 + ((size_t)c.hk * c.Npad + 64 * t + row) * D + 16 * part);
   }
   const uint8_t* vsrc = p.v8 + ((size_t)c.hk * (c.Npad >> 5) + 2 * t) * D * 32;
 #pragma unroll
+  for (int i = 0; i < 2; ++i) r.v[i] = *(const u32x4*)(vsrc + 16 * (c.tid + 256 * i));
+}
+__device__ inline void store_tile_q(const Ctx& c, uint8_t* lds, const TileQRegs& r) {
+#pragma unroll
   for (int i = 0; i < 2; ++i) {
-    const int ch = c.tid + 256 * i;
-    *(u32x4*)(lds + LDS_V + 16 * ch) = *(const u32x4*)(vsrc + 16 * ch);
+    const int ch = c.tid + 256 * i, row = ch >> 3, part = ch & 7;
+    *(u32x4*)(lds + row * K8_LD + 16 * part) = r.k[i];
+    *(u32x4*)(lds + LDS_QV + 16 * ch) = r.v[i];
   }
 }
 
-// bf16 tile: K rows (row stride KB_LD) and V^T, for 64 keys given by key_of(row) (< 0 or
-// >= N: zeros).  V^T element (key row, channel ch) sits at ((row/32 * 128 + ch) * 4 + jj) * 8
-// + ee (bf16 units) with kk = row % 32, jj = (kk % 16) / 4, ee = 4 (kk / 16) + kk % 4.
+// bf16 tile: 64 K rows (row stride KB_LD in LDS; rows whose key_of(row) is outside [0, N)
+// are zero) and the tile's V^T (16 KB, copied as stored: [32-key block][jj][channel][8]).
 template <typename KeyOf>
-__device__ inline void load_tile_bf(const PrefillParams& p, const Ctx& c, uint8_t* lds, KeyOf key_of) {
+__device__ inline void load_tile_bf(const Ctx& c, uint8_t* lds, const uint16_t* krows, int kstride_ok_n,
+                                    const uint16_t* vt, KeyOf key_of) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int ch = c.tid + 256 * i, row = ch >> 4, part = ch & 15;
     const int key = key_of(row);
-    u32x4 kx = {0u, 0u, 0u, 0u}, vx = {0u, 0u, 0u, 0u};
-    if (key >= 0 && key < c.N) {
-      kx = *(const u32x4*)(p.k + ((size_t)c.hk * c.N + key) * D + 8 * part);
-      vx = *(const u32x4*)(p.v + ((size_t)c.hk * c.N + key) * D + 8 * part);
-    }
+    u32x4 kx = {0u, 0u, 0u, 0u};
+    if (key >= 0 && key < kstride_ok_n) kx = *(const u32x4*)(krows + (size_t)key * D + 8 * part);
     *(u32x4*)(lds + row * KB_LD + 16 * part) = kx;
-    const int kb32 = row >> 5, kk = row & 31, jj = (kk & 15) >> 2, ee = 4 * (kk >> 4) + (kk & 3);
-    uint16_t* vd = (uint16_t*)(lds + LDS_V) + ((kb32 * D + 8 * part) * 4 + jj) * 8 + ee;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      vd[(2 * e) * 32] = (uint16_t)(vx[e] & 0xffffu);
-      vd[(2 * e + 1) * 32] = (uint16_t)(vx[e] >> 16);
-    }
+    *(u32x4*)(lds + LDS_V + 16 * ch) = *(const u32x4*)(vt + 8 * ch);
   }
 }
 
-// One quantized tile for the wave's 32 queries.
-__device__ inline void compute_tile_q(const PrefillParams& p, const Ctx& c, const uint8_t* lds, int t,
-                                      const i32x4 (&qi)[2][2], float sq, const uint32_t* abits, RowState& st) {
+// Scores of one quantized tile for the wave's 32 queries: S^T = K . Q^T on INT8 codes, with
+// the masked keys (anchors; j > i - 128 on an edge tile) pushed to NEG_DOT through the MFMA's
+// C input.  Two passes over the 64 channels of each k-step so the 8 independent (qb, kb)
+// chains interleave in the MFMA pipe.
+__device__ inline void qk_tile_q(const Ctx& c, const uint8_t* buf, const uint8_t* q8s, int t,
+                                 uint32_t w0, uint32_t w1, i32x4 (&S2)[2][4]) {
   const int kt0 = 64 * t;
-  if (kt0 > c.r0w + 31 - WIN) return;  // no key of the tile is in range for this wave
+  // Q codes of this lane's query (row l16 of block qb): 16 bytes per k-step
+  const uint8_t* qrow = q8s + (32 * c.wave + c.l16) * K8_LD + 16 * c.j;
   const bool interior = kt0 + 63 <= c.r0w - WIN;
-  const uint32_t w0 = abits[kt0 >> 5], w1 = abits[(kt0 >> 5) + 1];
-  float c2 = sq * p.sk[(size_t)c.hk * c.nb64 + t] * AL2;
-  c2 = c2 > 0.0f ? c2 : 1.0f;  // a zero scale means every valid dot is 0
-  i32x4 S2[2][4];
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb) {
     const uint32_t nib = ((kb < 2 ? w0 : w1) >> (16 * (kb & 1) + 4 * c.j)) & 0xfu;
     i32x4 bias;
 #pragma unroll
     for (int r = 0; r < 4; ++r) bias[r] = ((nib >> r) & 1u) ? NEG_DOT : 0;
-    const i32x4 kf0 = *(const i32x4*)(lds + (16 * kb + c.l16) * K8_LD + 16 * c.j);
-    const i32x4 kf1 = *(const i32x4*)(lds + (16 * kb + c.l16) * K8_LD + 64 + 16 * c.j);
+    const i32x4 kf0 = *(const i32x4*)(buf + (16 * kb + c.l16) * K8_LD + 16 * c.j);
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       i32x4 acc = bias;
@@ -284,10 +346,28 @@ __device__ inline void compute_tile_q(const PrefillParams& p, const Ctx& c, cons
         for (int r = 0; r < 4; ++r)
           if (kt0 + 16 * kb + 4 * c.j + r > row - WIN) acc[r] = NEG_DOT;
       }
-      acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(kf0, qi[qb][0], acc, 0, 0, 0);
-      S2[qb][kb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(kf1, qi[qb][1], acc, 0, 0, 0);
+      const i32x4 q0 = *(const i32x4*)(qrow + 16 * K8_LD * qb);
+      S2[qb][kb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(kf0, q0, acc, 0, 0, 0);
     }
   }
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    const i32x4 kf1 = *(const i32x4*)(buf + (16 * kb + c.l16) * K8_LD + 64 + 16 * c.j);
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const i32x4 q1 = *(const i32x4*)(qrow + 16 * K8_LD * qb + 64);
+      S2[qb][kb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(kf1, q1, S2[qb][kb], 0, 0, 0);
+    }
+  }
+}
+
+// Online softmax of one quantized tile's scores and its P.V: P = E4M3(448 p) against the
+// E4M3 V codes, the row sum of the rounded P from an MFMA against a row of ones.
+// c2 = s_Q s_K alpha log2(e) (wave-uniform).  Below C2_FAST_MIN a masked score is not
+// guaranteed to underflow exp2, so the masked entries are zeroed explicitly.
+template <bool TINY>
+__device__ inline void sm_pv_tile_q(const Ctx& c, const uint8_t* buf, const i32x4 (&S2)[2][4], float c2,
+                                    RowState& st) {
   i64 pk[2][2];
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
@@ -305,7 +385,7 @@ __device__ inline void compute_tile_q(const PrefillParams& p, const Ctx& c, cons
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         pv[r] = __builtin_amdgcn_exp2f(__builtin_fmaf((float)S2[qb][kb][r], c2, -muse));
-        if (c2 < C2_FAST_MIN && S2[qb][kb][r] <= NEG_DOT / 2) pv[r] = 0.0f;
+        if (TINY && S2[qb][kb][r] <= NEG_DOT / 2) pv[r] = 0.0f;
       }
       const uint32_t w = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(pv[0], pv[1], 0, false);
       pw[kb] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(pv[2], pv[3], (int)w, true);
@@ -317,7 +397,7 @@ __device__ inline void compute_tile_q(const PrefillParams& p, const Ctx& c, cons
   for (int cb = 0; cb < 8; ++cb) {
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      const i64 vf = *(const i64*)(lds + LDS_V + ((ks * D + 16 * cb + c.l16) * 32 + 8 * c.j));
+      const i64 vf = *(const i64*)(buf + LDS_QV + ((ks * 4 + c.j) * D + 16 * cb + c.l16) * 8);
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb)
         st.acc[qb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(vf, pk[qb][ks], st.acc[qb][cb], 0, 0, 0);
@@ -393,7 +473,7 @@ __device__ inline void compute_tile_bf(const PrefillParams& p, const Ctx& c, con
   for (int cb = 0; cb < 8; ++cb) {
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      const bf16x8 vf = *(const bf16x8*)(lds + LDS_V + ((ks * D + 16 * cb + c.l16) * 4 + c.j) * 16);
+      const bf16x8 vf = *(const bf16x8*)(lds + LDS_V + ((ks * 4 + c.j) * D + 16 * cb + c.l16) * 16);
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb)
         st.acc[qb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb[qb][ks], st.acc[qb][cb], 0, 0, 0);
@@ -408,10 +488,61 @@ __device__ inline void compute_tile_bf(const PrefillParams& p, const Ctx& c, con
       st.lacc[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ONESB, pb[qb][ks], st.lacc[qb], 0, 0, 0);
 }
 
+// Segment A (quantized tiles 0 .. nA-1) for one workgroup.
+template <bool TINY>
+__device__ inline void segment_a(const PrefillParams& p, const Ctx& c, uint8_t* lds, int nA, float sq_u,
+                                 RowState& st) {
+  // Software pipeline: iteration t stores tile t+1 into the other LDS buffer, issues the
+  // QK^T MFMAs of tile t+1, then runs the softmax (VALU) and P.V of tile t -- the MFMA pipe
+  // works on tile t+1 while the VALU works on tile t.  Tiles past the wave's last row
+  // (64 t > r0w + 31 - 128) are loaded for the other waves but not computed.
+  const int nAw = c.r0w + 31 - WIN >= 0 ? ((c.r0w + 31 - WIN) >> 6) + 1 : 0;
+  if (nA > 0) {
+    TileQRegs pre;
+    fetch_tile_q(p, c, 0, pre);
+    __syncthreads();
+    store_tile_q(c, lds, pre);
+    float sk_cur = pre.sk;
+    const uint32_t w0 = pre.w0, w1 = pre.w1;
+    if (nA > 1) fetch_tile_q(p, c, 1, pre);
+    __syncthreads();
+    i32x4 S2[2][4];
+    if (nAw > 0) qk_tile_q(c, lds, lds + LDS_Q8, 0, w0, w1, S2);
+    for (int t = 0; t < nA; ++t) {
+      const uint8_t* cur = lds + (t & 1) * LDS_QBUF;
+      uint8_t* nxt = lds + ((t + 1) & 1) * LDS_QBUF;
+      float sk_nxt = 0.0f;
+      uint32_t nw0 = 0, nw1 = 0;
+      __syncthreads();  // everyone is done with tile t-1 (it lived in nxt)
+      if (t + 1 < nA) {
+        store_tile_q(c, nxt, pre);
+        sk_nxt = pre.sk;
+        nw0 = pre.w0;
+        nw1 = pre.w1;
+      }
+      __syncthreads();
+      if (t + 2 < nA) fetch_tile_q(p, c, t + 2, pre);  // in flight during this tile's compute
+      i32x4 S2n[2][4];
+      if (t + 1 < nAw) qk_tile_q(c, nxt, lds + LDS_Q8, t + 1, nw0, nw1, S2n);
+      if (t < nAw) {
+        float c2 = uniform_f(sq_u * sk_cur * AL2);
+        if (TINY) c2 = c2 > 0.0f ? c2 : 1.0f;  // a zero scale means every valid dot is 0
+        sm_pv_tile_q<TINY>(c, cur, S2, c2, st);
+      }
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) S2[qb][kb] = S2n[qb][kb];
+      sk_cur = sk_nxt;
+    }
+  }
+}
+
 __global__ void __launch_bounds__(256, 2) pf_attn_kernel(PrefillParams p) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[LDS_TILE];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[LDS_TOTAL];
   __shared__ int anc_s[64];
   __shared__ float qmax[4];
+  __shared__ float skmin[4];
   __shared__ int nb_anchor_s;
 
   const int nQB = p.Npad / WG_ROWS;
@@ -422,9 +553,10 @@ __global__ void __launch_bounds__(256, 2) pf_attn_kernel(PrefillParams p) {
   const int r0 = qblk * WG_ROWS;
   c.tid = threadIdx.x;
   const int wave = c.tid >> 6, lane = c.tid & 63;
+  c.wave = wave;
   c.l16 = lane & 15;
   c.j = lane >> 4;
-  c.r0w = r0 + 32 * wave;
+  c.r0w = __builtin_amdgcn_readfirstlane(r0 + 32 * wave);  // wave-uniform: scalar branches
   c.N = p.N;
   c.Npad = p.Npad;
   c.nb64 = p.Npad >> 6;
@@ -486,6 +618,7 @@ __global__ void __launch_bounds__(256, 2) pf_attn_kernel(PrefillParams p) {
         }
         const int row = c.r0w + 16 * qb + c.l16;
         *(i32x4*)(p.q8 + ((size_t)c.h * c.Npad + row) * D + 64 * s8 + 16 * c.j) = qi[qb][s8];
+        *(i32x4*)(lds + LDS_Q8 + (32 * wave + 16 * qb + c.l16) * K8_LD + 64 * s8 + 16 * c.j) = qi[qb][s8];
       }
     }
     if (lane == 0 && (wave & 1) == 0) p.sq[(size_t)c.h * c.nb64 + (c.r0w >> 6)] = sq;
@@ -503,12 +636,21 @@ __global__ void __launch_bounds__(256, 2) pf_attn_kernel(PrefillParams p) {
   // ---- segment A: quantized tiles
   const int lastA = r0 + WG_ROWS - 1 - WIN;
   const int nA = lastA >= 0 ? (lastA >> 6) + 1 : 0;
-  const uint32_t* abits = p.abits + (size_t)c.hk * (c.Npad >> 5);
-  for (int t = 0; t < nA; ++t) {
+  // Masked INT8 scores underflow exp2 only when s_Q s_K is not tiny; the rare wave with a
+  // tiny product over its tiles runs the variant that zeroes them explicitly.
+  {
+    float m = INFINITY;
+    for (int t = c.tid; t < nA; t += 256) m = fminf(m, p.sk[(size_t)c.hk * c.nb64 + t]);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) m = fminf(m, shfl_xor_f(m, o));
+    if (lane == 0) skmin[wave] = m;
     __syncthreads();
-    load_tile_q(p, c, lds, t);
-    __syncthreads();
-    compute_tile_q(p, c, lds, t, qi, sq, abits, st);
+    m = fminf(fminf(skmin[0], skmin[1]), fminf(skmin[2], skmin[3]));
+    const float sq_u = uniform_f(sq);
+    if (sq_u * m * AL2 >= C2_FAST_MIN)
+      segment_a<false>(p, c, lds, nA, sq_u, st);
+    else
+      segment_a<true>(p, c, lds, nA, sq_u, st);
   }
   // acc holds sum E4M3(448 p) * code(V): scale to values
 #pragma unroll
@@ -530,10 +672,8 @@ __global__ void __launch_bounds__(256, 2) pf_attn_kernel(PrefillParams p) {
       const int idx = 64 * u + c.tid;
       anc_s[c.tid] = idx < n_anchor ? anc_g[idx] : -1;
     }
-    load_tile_bf(p, c, lds, [&](int row) {
-      const int idx = 64 * u + row;
-      return idx < n_anchor ? anc_g[idx] : -1;
-    });
+    load_tile_bf(c, lds, p.ka16 + ((size_t)c.hk * p.n_anchor_pad + 64 * u) * D, 64,
+                 p.va16 + ((size_t)c.hk * (p.n_anchor_pad >> 5) + 2 * u) * D * 32, [&](int row) { return row; });
     __syncthreads();
     const int a0 = anc_s[0];
     if (a0 >= 0 && a0 <= c.r0w + 31 - WIN) compute_tile_bf<true>(p, c, lds, anc_s, 0, st);
@@ -544,7 +684,8 @@ __global__ void __launch_bounds__(256, 2) pf_attn_kernel(PrefillParams p) {
   for (int t = tC0; t <= tC1; ++t) {
     const int kt0 = 64 * t;
     __syncthreads();
-    load_tile_bf(p, c, lds, [&](int row) { return kt0 + row; });
+    load_tile_bf(c, lds, p.k + (size_t)c.hk * c.N * D, c.N,
+                 p.vt16 + ((size_t)c.hk * (c.Npad >> 5) + 2 * t) * D * 32, [&](int row) { return kt0 + row; });
     __syncthreads();
     if (!(kt0 > c.r0w + 31 || kt0 + 63 < c.r0w - WIN + 1)) compute_tile_bf<false>(p, c, lds, anc_s, kt0, st);
   }
@@ -569,6 +710,8 @@ hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream) {
   hipLaunchKernelGGL(pf_kquant_kernel, dim3(p.Npad / KBLK, Hkv), dim3(256), 0, stream, p);
   hipLaunchKernelGGL(pf_vscale_kernel, dim3(Hkv), dim3(1024), 0, stream, p);
   hipLaunchKernelGGL(pf_vquant_kernel, dim3(p.Npad / 32, Hkv), dim3(128), 0, stream, p);
+  if (p.n_anchor_pad > 0)
+    hipLaunchKernelGGL(pf_agather_kernel, dim3(p.n_anchor_pad / 32, Hkv), dim3(128), 0, stream, p);
   hipLaunchKernelGGL(pf_attn_kernel, dim3((p.Npad / WG_ROWS) * p.Hq), dim3(256), 0, stream, p);
   return hipGetLastError();
 }

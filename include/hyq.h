@@ -219,16 +219,21 @@ int hyq_decode_attn(const hyq_cache_t* cache, const void* q, float* o, int32_t n
      sq   f32  [Hq][Np/64]          s_Q per 64-query block
      k8   int8 [Hkv][Np][128]       K codes, operand order
      sk   f32  [Hkv][Np/64]         s_K per 64-key block
-     v8   u8   [Hkv][Np/32][128][32] V codes: byte 8 j + e of (32-key block b, channel c)
+     v8   u8   [Hkv][Np/32][4][128][8] V codes: byte e of (32-key block b, j, channel c)
                                     is key 32 b + 16 (e >> 2) + 4 j + (e & 3)
      sv   f32  [Hkv][128]           s_V
      vmax f32  [Hkv][Np/64][128]    per-block max |V| over non-anchor keys
      abits u32 [Hkv][Np/32]         anchor bitmap (bit j & 31 of word j >> 5)
+     vt16 bf16 [Hkv][Np/32][4][128][8] V (all keys, rows >= len zero) in the layout of v8
+     ka16 bf16 [Hkv][Ap][128]       K rows of the anchors in list order (Ap = n_anchor
+                                    rounded up to 64; the section is sized for anchor_cap)
+     va16 bf16 [Hkv][Ap/32][4][128][8] V of the anchors in list order, layout of v8
    Operand order of an INT8 row: byte 64 s + 16 j + 8 t + e holds channel
    32 (2 s + t) + 8 j + e (s, t in {0,1}, j < 4, e < 8).
    Calls sharing one workspace must not overlap in time (same stream is fine).
-   Five kernel launches.  Errors: INVALID (null pointers, len <= 0, n_anchor outside
-   [0, max(0, len-128)]), UNSUPPORTED (batch != 1, len > HYQ_PREFILL_MAX_LEN), WORKSPACE, HIP. */
+   Six kernel launches.  Errors: INVALID (null pointers, len <= 0, n_anchor outside
+   [0, max(0, len-128)]), CAPACITY (n_anchor > shape->anchor_cap), UNSUPPORTED (batch != 1,
+   len > HYQ_PREFILL_MAX_LEN), WORKSPACE, HIP. */
 #define HYQ_PREFILL_MAX_LEN (1 << 20)
 int hyq_prefill_attn(const hyq_shape_t* shape, const void* q, const void* k, const void* v,
                      int32_t len, const int32_t* anchors, int32_t n_anchor, float* o, void* ws,

@@ -96,12 +96,14 @@ def _r256(x: int) -> int:
     return (x + 255) // 256 * 256
 
 
-def prefill_ws_offsets(Hq: int, Hkv: int, N: int) -> dict:
+def prefill_ws_offsets(Hq: int, Hkv: int, N: int, anchor_cap: int) -> dict:
     """Section offsets of the prefill workspace, in the order the header lists them."""
     Np = (N + 127) // 128 * 128
+    Ac = (anchor_cap + 63) // 64 * 64
     sizes = [("q8", Hq * Np * D), ("sq", Hq * (Np // 64) * 4), ("k8", Hkv * Np * D),
              ("sk", Hkv * (Np // 64) * 4), ("v8", Hkv * Np * D), ("sv", Hkv * D * 4),
-             ("vmax", Hkv * (Np // 64) * D * 4), ("abits", Hkv * (Np // 32) * 4)]
+             ("vmax", Hkv * (Np // 64) * D * 4), ("abits", Hkv * (Np // 32) * 4),
+             ("vt16", Hkv * Np * D * 2), ("ka16", Hkv * Ac * D * 2), ("va16", Hkv * Ac * D * 2)]
     off, out = 0, {"Np": Np}
     for name, n in sizes:
         out[name] = off
@@ -122,11 +124,11 @@ def _int8_natural_index() -> np.ndarray:
     return perm
 
 
-def read_prefill_ws(ws: np.ndarray, Hq: int, Hkv: int, N: int) -> dict:
+def read_prefill_ws(ws: np.ndarray, Hq: int, Hkv: int, N: int, anchor_cap: int) -> dict:
     """Decode the prefill workspace (uint8 numpy) into natural-order arrays:
     q8 int8 [Hq][Np][128], sq f32 [Hq][Np/64], k8 int8 [Hkv][Np][128], sk, v8 uint8 codes
     [Hkv][Np][128], sv f32 [Hkv][128], abits uint32 [Hkv][Np/32]."""
-    o = prefill_ws_offsets(Hq, Hkv, N)
+    o = prefill_ws_offsets(Hq, Hkv, N, anchor_cap)
     Np = o["Np"]
 
     def sec(name, dtype, count):
@@ -136,12 +138,12 @@ def read_prefill_ws(ws: np.ndarray, Hq: int, Hkv: int, N: int) -> dict:
     perm = _int8_natural_index()
     q8 = sec("q8", np.int8, Hq * Np * D).reshape(Hq, Np, D)[:, :, perm]
     k8 = sec("k8", np.int8, Hkv * Np * D).reshape(Hkv, Np, D)[:, :, perm]
-    raw = sec("v8", np.uint8, Hkv * Np * D).reshape(Hkv, Np // 32, D, 32)
+    raw = sec("v8", np.uint8, Hkv * Np * D).reshape(Hkv, Np // 32, 4, D, 8)
     v8 = np.empty((Hkv, Np, D), np.uint8)
     for j in range(4):
         for e in range(8):
             kk = 16 * (e >> 2) + 4 * j + (e & 3)
-            v8[:, kk::32, :] = raw[:, :, :, 8 * j + e]
+            v8[:, kk::32, :] = raw[:, :, j, :, e]
     return dict(Np=Np, q8=q8, k8=k8, v8=v8,
                 sq=sec("sq", np.float32, Hq * (Np // 64)).reshape(Hq, Np // 64),
                 sk=sec("sk", np.float32, Hkv * (Np // 64)).reshape(Hkv, Np // 64),

@@ -103,10 +103,11 @@ def test_prefill_workspace_layout_and_errors(lib):
     from tests.gpu_layout import prefill_ws_offsets
     one = _shape(batch=1, n_q_heads=32, n_kv_heads=8)
     for N in (1, 127, 128, 129, 1000, 8192, 32768):
-        assert lib.hyq_workspace_bytes(C.byref(one), _lib.HYQ_OP_PREFILL, N, 0) == prefill_ws_offsets(32, 8, N)["total"]
+        assert lib.hyq_workspace_bytes(C.byref(one), _lib.HYQ_OP_PREFILL, N, 0) == \
+            prefill_ws_offsets(32, 8, N, one.anchor_cap)["total"]
     assert lib.hyq_workspace_bytes(C.byref(one), _lib.HYQ_OP_PREFILL, 0, 0) == 0
     assert lib.hyq_workspace_bytes(C.byref(one), _lib.HYQ_OP_PREFILL, (1 << 20) + 1, 0) == 0
-    need = prefill_ws_offsets(32, 8, 1000)["total"]
+    need = prefill_ws_offsets(32, 8, 1000, one.anchor_cap)["total"]
     f = lib.hyq_prefill_attn
     # batch != 1 -> UNSUPPORTED; null tensors / bad anchor counts -> INVALID; small ws -> WORKSPACE
     assert f(C.byref(_shape(batch=2)), 0x10, 0x20, 0x30, 1000, None, 0, 0x40, 0x50, need, None) == 2
@@ -118,3 +119,4 @@ def test_prefill_workspace_layout_and_errors(lib):
     assert f(C.byref(one), 0x10, 0x20, 0x30, 1000, None, 0, 0x40, 0x50, need - 1, None) == 4
     assert f(C.byref(one), 0x10, 0x20, 0x30, 1000, None, 0, 0x40, None, need, None) == 4
     assert f(C.byref(one), 0x10, 0x20, 0x30, (1 << 20) + 1, None, 0, 0x40, 0x50, need, None) == 2
+    assert f(C.byref(one), 0x10, 0x20, 0x30, 1000, 0x60, one.anchor_cap + 1, 0x40, 0x50, need, None) == 3

@@ -38,12 +38,12 @@ def anchors_dense(d, Hq, Hkv, N, pct=5):
 
 
 def run_gpu(d, A, Hq, Hkv, N):
-    shape = hq.Shape.for_context(1, Hq, Hkv, N)
+    shape = hq.Shape(1, Hq, Hkv, int4_cap=32, anchor_cap=max(32, -(-A.shape[1] // 32) * 32))
     ws = hq.prefill_workspace(shape, N)
     anc = torch.from_numpy(np.ascontiguousarray(A)).cuda() if A.shape[1] else None
     o = hq.prefill_attn(shape, dev(d["Q"]), dev(d["K"]), dev(d["V"]), anchors=anc, ws=ws)
     torch.cuda.synchronize()
-    return o.cpu().numpy(), read_prefill_ws(ws.cpu().numpy(), Hq, Hkv, N)
+    return o.cpu().numpy(), read_prefill_ws(ws.cpu().numpy(), Hq, Hkv, N, shape.anchor_cap)
 
 
 def check_operands(w, qz, A, N):
