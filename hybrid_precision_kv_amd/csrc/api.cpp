@@ -1,5 +1,6 @@
 // C ABI of the hybrid-precision KV attention library: argument validation, host-side cache
 // counters, workspace sizing and kernel launches.  Declarations and contracts: include/hyq.h.
+#include <atomic>
 #include <hip/hip_runtime.h>
 #include <string.h>
 
@@ -124,12 +125,27 @@ PrefillWs prefill_ws(const hyq_shape_t* s, int32_t len) {
   return w;
 }
 
+// compute units of the current device (cached per device; 256 if the query fails)
+int cu_count() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n > 0) return n;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+  cache[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+// Splits per (b, KV head): one full round of workgroups -- two decode workgroups fit on a CU
+// (register budget) -- and at least ~4 tiles per wave.
 int auto_splits(const hyq_cache_t* c) {
   const int G = c->shape.n_q_heads / c->shape.n_kv_heads;
   const long units = (long)nheads(&c->shape) * ((G + 3) / 4);
   const long tiles = (c->n_int4 + 31) / 32 + 3 * ((c->n_anchor + 31) / 32 + (c->n_staged + 31) / 32 + 4);
-  long s = (1024 + units - 1) / units;          // aim for ~1024 workgroups (4 per CU)
-  const long by_work = (tiles + 15) / 16;        // >= ~4 tiles per wave
+  const long target = 2L * cu_count();
+  long s = (target + units - 1) / units;
+  const long by_work = (tiles + 15) / 16;
   if (s > by_work) s = by_work;
   if (s < 1) s = 1;
   if (s > 256) s = 256;
