@@ -87,8 +87,7 @@ SelectWs select_ws(const hyq_shape_t* s, int32_t len) {
   w.inset_words = (P + 31) / 32 + 1;
   w.del_words = (s->int4_cap + 31) / 32 + 1;
   w.max_moves = 2 * s->anchor_cap + s->staging_cap + 32;
-  w.per_head = r256((size_t)(w.inset_words + w.del_words) * 4 + (size_t)2 * s->anchor_cap * D * 2 +
-                    (size_t)2 * s->anchor_cap * 4 + (size_t)3 * w.max_moves * 4);
+  w.per_head = r256(hyq::refresh_scratch_bytes(w.inset_words, w.del_words, s->anchor_cap, w.max_moves));
   w.qsum = 0;
   w.rowpart = w.qsum + r256(H * R * 4 * 4);
   w.rowstat = w.rowpart + r256(H * w.n_tasks * R * 2 * 4);

@@ -66,6 +66,8 @@ struct RefreshParams {
   int* status;  // [H] 0 = counts consistent
 };
 hipError_t launch_refresh(const RefreshParams& p, hipStream_t stream);
+// bytes of per-head refresh scratch
+size_t refresh_scratch_bytes(int inset_words, int del_words, int anchor_cap, int max_moves);
 
 // Freeze (prefill -> decode)
 hipError_t launch_freeze(const CacheView& c, const uint16_t* k, const uint16_t* v, int len,
