@@ -71,7 +71,8 @@ int check_counters(const hyq_cache_t* c) {
 
 // select workspace layout (all sizes rounded to 256 bytes)
 struct SelectWs {
-  size_t qsum, rowpart, rowstat, scores, refresh, status, total;
+  size_t qsum, pq16, pqbf, rowpart, rowstat, scores, refresh, status, total;
+  int rb_max;
   size_t per_head;
   int inset_words, del_words, max_moves, n_tasks;
 };
@@ -88,8 +89,11 @@ SelectWs select_ws(const hyq_shape_t* s, int32_t len) {
   w.del_words = (s->int4_cap + 31) / 32 + 1;
   w.max_moves = 2 * s->anchor_cap + s->staging_cap + 32;
   w.per_head = r256(hyq::refresh_scratch_bytes(w.inset_words, w.del_words, s->anchor_cap, w.max_moves));
+  w.rb_max = (int)((R + 15) / 16);
   w.qsum = 0;
-  w.rowpart = w.qsum + r256(H * R * 4 * 4);
+  w.pq16 = w.qsum + r256(H * R * 4 * 4);
+  w.pqbf = w.pq16 + r256(H * (size_t)w.rb_max * 256 * 16);
+  w.rowpart = w.pqbf + r256(H * (size_t)w.rb_max * 256 * 16);
   w.rowstat = w.rowpart + r256(H * w.n_tasks * R * 2 * 4);
   w.scores = w.rowstat + r256(H * R * 2 * 4);
   w.refresh = w.scores + r256(H * (size_t)(P > 0 ? P : 1) * 4);
@@ -339,6 +343,9 @@ int hyq_select_vlines(const hyq_shape_t* shape, hyq_cache_t* cache, const void* 
     p.n_tasks = hyq::select_task_count(p.n_tiles);
     p.k = k;
     p.qsum = (float*)(wb + w.qsum);
+    p.pq16 = wb + w.pq16;
+    p.pqbf = wb + w.pqbf;
+    p.rb_stride = w.rb_max;
     p.rowpart = (float*)(wb + w.rowpart);
     p.rowstat = (float*)(wb + w.rowstat);
     p.scores = scores_out ? scores_out : (float*)(wb + w.scores);

@@ -42,7 +42,10 @@ struct SelectParams {
   int n_int4, n_anchor, n_staged, n_win;
   int n_tiles, n_tasks, k;
   float* qsum;     // [H][R][4]
-  float* rowpart;  // [H][n_tasks][R][2]
+  void* pq16;      // [H][RBmax][256] f16x8: proxy rows, INT4-key operand order
+  void* pqbf;      // [H][RBmax][256] bf16x8: proxy rows, bf16-key operand order
+  int rb_stride;   // RBmax (16-row blocks per head slot)
+  float* rowpart;  // [H][R][n_tasks][2]
   float* rowstat;  // [H][R][2]
   float* scores;   // [H][len - 128] by position
   int32_t* idx_out;  // [H][k]

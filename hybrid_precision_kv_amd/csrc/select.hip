@@ -27,7 +27,7 @@ namespace hyq {
 namespace {
 
 constexpr float LOG2E = 1.4426950408889634f;
-constexpr int SW = 8;             // waves per workgroup
+constexpr int SW = 4;             // waves per workgroup
 constexpr int KEYS_WG = SW * 32;  // keys per task (one 32-key tile per wave)
 
 __device__ inline f16x8 codes_to_f16(uint32_t x) {
@@ -72,14 +72,20 @@ __device__ inline const uint16_t* proxy_row(const SelectParams& p, int b, int hk
   return p.proxy + (((size_t)b * Hq + (size_t)hkv * p.G + h) * p.proxy_stride + i) * D;
 }
 
-// Stage proxy rows [r0, r0+16) into LDS in the two operand orders: f16 with the nibble-pair
-// channel order and 1/16 on k-slots 2,3,6,7 (INT4 keys), and bf16 natural order (bf16 keys).
-// Layout: [group g][lane = 16*q4 + n][8]: lane (n, q4) of group g holds row r0+n, channels
-// 32g + 8q4 .. +7.  Rows >= R are zero.
-__device__ inline void stage_rows(const SelectParams& p, int b, int hkv, int r0, int R, f16x8* s16, bf16x8* sbf) {
-  for (int idx = threadIdx.x; idx < 4 * 64; idx += blockDim.x) {
+// Operand prep, once per call: proxy rows in the two B-operand orders of the score MFMAs,
+// per 16-row block rb and entry idx = 64 g + 16 q4 + n (row 16 rb + n, channels 32 g + 8 q4 ..
+// + 7): pq16 = f16 with the nibble-pair channel order and 1/16 on k-slots 2,3,6,7 (INT4 keys),
+// pqbf = bf16 in natural order (bf16 keys).  Rows >= R are zero.  Also the per-row group sums
+// qsum[r][g] = sum_{c in g} q[r][c] (fp32 of the f16-rounded q, as the MFMA uses it).
+__global__ __launch_bounds__(256) void select_prep_kernel(SelectParams p) {
+  const int hb = blockIdx.y, b = hb / p.Hkv, hkv = hb % p.Hkv;
+  const int R = p.n_proxy * p.G, RB = (R + 15) >> 4;
+  f16x8* pq16 = (f16x8*)p.pq16 + (size_t)hb * p.rb_stride * 256;
+  bf16x8* pqbf = (bf16x8*)p.pqbf + (size_t)hb * p.rb_stride * 256;
+  for (int t = blockIdx.x * blockDim.x + threadIdx.x; t < RB * 256; t += gridDim.x * blockDim.x) {
+    const int rb = t >> 8, idx = t & 255;
     const int g = idx >> 6, ln = idx & 63, n = ln & 15, q4 = ln >> 4;
-    const int r = r0 + n;
+    const int r = 16 * rb + n;
     u32x4 w = {0u, 0u, 0u, 0u};
     if (r < R) w = *(const u32x4*)(proxy_row(p, b, hkv, r) + 32 * g + 8 * q4);
     float f[8];
@@ -91,16 +97,9 @@ __device__ inline void stage_rows(const SelectParams& p, int b, int hkv, int r0,
     f16x8 h;
 #pragma unroll
     for (int e = 0; e < 8; ++e) h[e] = (_Float16)(f[kslot_nibble(e)] * ((e & 2) ? 0.0625f : 1.0f));
-    s16[idx] = h;
-    sbf[idx] = __builtin_bit_cast(bf16x8, w);
+    pq16[t] = h;
+    pqbf[t] = __builtin_bit_cast(bf16x8, w);
   }
-}
-
-// Per-row group sums sum_{c in g} q[r][c] (fp32 of the f16-rounded q, as the MFMA uses it),
-// computed once per call into qsum[hb][R][4].
-__global__ __launch_bounds__(256) void select_qsum_kernel(SelectParams p) {
-  const int hb = blockIdx.y, b = hb / p.Hkv, hkv = hb % p.Hkv;
-  const int R = p.n_proxy * p.G;
   for (int idx = blockIdx.x * blockDim.x + threadIdx.x; idx < R * 4; idx += gridDim.x * blockDim.x) {
     const int r = idx >> 2, g = idx & 3;
     const uint16_t* row = proxy_row(p, b, hkv, r) + 32 * g;
@@ -110,29 +109,42 @@ __global__ __launch_bounds__(256) void select_qsum_kernel(SelectParams p) {
   }
 }
 
-// A operands and (scale, min) of this wave's 32 keys.  Lane (n, q4): key rows n and 16 + n of
-// the tile; for INT4 keys instruction g covers group g (channels 32g + 8q4 + nibble order).
-struct KeyOps {
-  f16x8 a4[2][4];   // INT4: [block][group]
-  bf16x8 ab[2][4];  // bf16: [block][8-channel chunk]
-  u32x4 sm0[4], sm1[4];  // INT4: (scale, min) of output rows 4q4..4q4+3, [group], blocks 0 / 1
+// A operands of this wave's 32 keys.  Lane (n, q4): key rows n and 16 + n of the tile; for
+// INT4 keys instruction g covers group g (channels 32g + 8q4 + nibble order), the group scales
+// of the lane's output keys 4q4 + j are kept in fp32, and the group minima enter one fp32 MFMA
+// (A = min of key l%16, group l/16; B = the rows' group sums).
+struct KeyOps4 {
+  f16x8 a[2][4];     // [block][group]
+  float sc[2][4][4]; // scale [block][group][j] of keys 4q4 + j
+  float ma[2];       // min of (key lane%16, group lane/16), per block
+};
+struct KeyOpsB {
+  bf16x8 a[2][4];    // [block][8-channel chunk]
 };
 
-__device__ inline void load_keys(const SelectParams& p, const KeySrc& ks, size_t hb, int lane, KeyOps& o) {
+__device__ inline void load_keys4(const SelectParams& p, const KeySrc& ks, size_t hb, int lane, KeyOps4& o) {
   const int n = lane & 15, q4 = lane >> 4;
-  if (ks.kind == 0) {
-    const uint8_t* rec = p.int4 + hb * (size_t)p.int4_cap * 160 + (size_t)ks.tile * T4_BYTES;
+  const uint8_t* rec = p.int4 + hb * (size_t)p.int4_cap * 160 + (size_t)ks.tile * T4_BYTES;
 #pragma unroll
-    for (int blk = 0; blk < 2; ++blk)
+  for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-      for (int g = 0; g < 4; ++g)
-        o.a4[blk][g] = codes_to_f16(*(const uint32_t*)(rec + blk * 1024 + g * 256 + n * 16 + q4 * 4));
+    for (int g = 0; g < 4; ++g)
+      o.a[blk][g] = codes_to_f16(*(const uint32_t*)(rec + blk * 1024 + g * 256 + n * 16 + q4 * 4));
+#pragma unroll
+  for (int blk = 0; blk < 2; ++blk) {
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      o.sm0[g] = *(const u32x4*)(rec + T4_KSM + g * 64 + q4 * 16);
-      o.sm1[g] = *(const u32x4*)(rec + T4_KSM + 256 + g * 64 + q4 * 16);
+      const u32x4 w = *(const u32x4*)(rec + T4_KSM + blk * 256 + g * 64 + q4 * 16);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) o.sc[blk][g][j] = half_lo(w[j]);
     }
-  } else if (ks.kind == 1) {
+    o.ma[blk] = half_hi(*(const uint32_t*)(rec + T4_KSM + blk * 256 + 4 * lane));
+  }
+}
+
+__device__ inline void load_keysB(const SelectParams& p, const KeySrc& ks, size_t hb, int lane, KeyOpsB& o) {
+  const int n = lane & 15, q4 = lane >> 4;
+  if (ks.kind == 1) {
     const uint16_t* base;
     size_t slab;
     if (ks.seg == 1) { slab = (size_t)p.anchor_cap * D; base = p.a_k; }
@@ -142,7 +154,7 @@ __device__ inline void load_keys(const SelectParams& p, const KeySrc& ks, size_t
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-      for (int tt = 0; tt < 4; ++tt) o.ab[blk][tt] = *(const bf16x8*)(t + (blk * 4 + tt) * 512);
+      for (int tt = 0; tt < 4; ++tt) o.a[blk][tt] = *(const bf16x8*)(t + (blk * 4 + tt) * 512);
   } else {
     // dense rows: key row (tile*32 + 16 blk + n), channels 32 q4 + 8 tt .. +7
 #pragma unroll
@@ -151,72 +163,142 @@ __device__ inline void load_keys(const SelectParams& p, const KeySrc& ks, size_t
       if (key >= ks.count) key = ks.count - 1;  // masked later; stay inside the buffer
       const uint16_t* row = p.dense_k + (hb * (size_t)p.len + key) * D + 32 * q4;
 #pragma unroll
-      for (int tt = 0; tt < 4; ++tt) o.ab[blk][tt] = *(const bf16x8*)(row + 8 * tt);
+      for (int tt = 0; tt < 4; ++tt) o.a[blk][tt] = *(const bf16x8*)(row + 8 * tt);
     }
   }
 }
 
 // Scores (log2 domain, alpha included) of this lane's 8 (key, row) pairs for one row block:
 // keys 4q4 + j (block 0) and 16 + 4q4 + j (block 1), row r0 + n.
-__device__ inline void block_scores(const KeySrc& ks, const KeyOps& o, const f16x8* s16, const bf16x8* sbf,
-                                    const float* qs, int lane, float (&sc)[8]) {
-  const float alpha_log2 = LOG2E * 0.08838834764831845f;
-  if (ks.kind == 0) {
-    f32x4 acc0[4], acc1[4];
+// INT4: q.k = sum_g s_g (q_g . code_g) + sum_g m_g qsum_g; codes carry 2^-24 and qsb carries
+// the rows' group sums times 2^-24 (B operand: group lane/16, row lane%16).
+__device__ inline void scores4(const KeyOps4& o, const f16x8 (&bq)[4], float qsb, float (&sc)[8]) {
+  const float c = LOG2E * 0.08838834764831845f * 16777216.0f;
+  f32x4 v0 = __builtin_amdgcn_mfma_f32_16x16x4f32(o.ma[0], qsb, (f32x4){0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+  f32x4 v1 = __builtin_amdgcn_mfma_f32_16x16x4f32(o.ma[1], qsb, (f32x4){0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+  f32x4 acc0[4], acc1[4];
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    acc0[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(o.a[0][g], bq[g], (f32x4){0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+    acc1[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(o.a[1][g], bq[g], (f32x4){0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      const f16x8 bq = s16[g * 64 + lane];
-      acc0[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(o.a4[0][g], bq, (f32x4){0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-      acc1[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(o.a4[1][g], bq, (f32x4){0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+      v0[j] = fmaf(o.sc[0][g][j], acc0[g][j], v0[j]);
+      v1[j] = fmaf(o.sc[1][g][j], acc1[g][j], v1[j]);
     }
-    const float c = alpha_log2 * 16777216.0f;  // codes carry 2^-24
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      float v0 = 0.f, v1 = 0.f;
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        v0 += half_lo(o.sm0[g][j]) * acc0[g][j] + half_hi(o.sm0[g][j]) * qs[g] * (1.0f / 16777216.0f);
-        v1 += half_lo(o.sm1[g][j]) * acc1[g][j] + half_hi(o.sm1[g][j]) * qs[g] * (1.0f / 16777216.0f);
-      }
-      sc[j] = v0 * c;
-      sc[4 + j] = v1 * c;
-    }
-  } else {
-    f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
-      // B: rows' channels 32q4 + 8tt .. +7 (natural order) = staged chunk (g = q4? no: lane's quad
-      // q4 needs channels of group q4 at chunk tt) -> staged entry [q4][16 tt + n]
-      const bf16x8 bq = sbf[(lane >> 4) * 64 + 16 * tt + (lane & 15)];
-      a0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(o.ab[0][tt], bq, a0, 0, 0, 0);
-      a1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(o.ab[1][tt], bq, a1, 0, 0, 0);
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      sc[j] = a0[j] * alpha_log2;
-      sc[4 + j] = a1[j] * alpha_log2;
-    }
+    sc[j] = v0[j] * c;
+    sc[4 + j] = v1[j] * c;
   }
 }
 
-template <int PASS>
-__global__ __launch_bounds__(512) void select_pass_kernel(SelectParams p) {
-  __shared__ f16x8 s16[2][4 * 64];
-  __shared__ bf16x8 sbf[2][4 * 64];
-  __shared__ float red[SW][16][2];
-  const int task = blockIdx.x, hb = blockIdx.y, b = hb / p.Hkv, hkv = hb % p.Hkv;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+__device__ inline void scoresB(const KeyOpsB& o, const bf16x8 (&bq)[4], float (&sc)[8]) {
+  const float alpha_log2 = LOG2E * 0.08838834764831845f;
+  f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int tt = 0; tt < 4; ++tt) {
+    a0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(o.a[0][tt], bq[tt], a0, 0, 0, 0);
+    a1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(o.a[1][tt], bq[tt], a1, 0, 0, 0);
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    sc[j] = a0[j] * alpha_log2;
+    sc[4 + j] = a1[j] * alpha_log2;
+  }
+}
+
+// B operands (and per-row values) of row block rb, loaded one block ahead of their use.
+// INT4: entry [group g][lane]; bf16: the lane's rows at channels 32 q4 + 8 tt .. +7 =
+// prepared entry [group q4][16 tt + n].
+template <int PASS, int KIND>
+struct RowBlock {
+  f16x8 b4[KIND == 0 ? 4 : 1];
+  bf16x8 bb[KIND == 0 ? 1 : 4];
+  float qsb, M, iz;
+};
+template <int PASS, int KIND>
+__device__ inline void load_rows(const SelectParams& p, size_t hb, int R, int rb, int lane, RowBlock<PASS, KIND>& x) {
+  const int n = lane & 15, q4 = lane >> 4;
+  if constexpr (KIND == 0) {
+    const f16x8* pq16 = (const f16x8*)p.pq16 + (hb * p.rb_stride + rb) * 256;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) x.b4[g] = pq16[g * 64 + lane];
+    const int rq = rb * 16 + n;  // minima MFMA B operand: row lane%16, group lane/16
+    x.qsb = rq < R ? p.qsum[(hb * R + rq) * 4 + q4] * (1.0f / 16777216.0f) : 0.0f;
+  } else {
+    const bf16x8* pqbf = (const bf16x8*)p.pqbf + (hb * p.rb_stride + rb) * 256;
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) x.bb[tt] = pqbf[q4 * 64 + 16 * tt + n];
+  }
+  if (PASS == 2) {
+    const int r = rb * 16 + n;
+    x.M = r < R ? p.rowstat[(hb * R + r) * 2] : 0.0f;
+    x.iz = r < R ? p.rowstat[(hb * R + r) * 2 + 1] : 0.0f;
+  }
+}
+
+// Sweep of the proxy rows for one wave's keys (KIND 0: INT4 tile, 1: bf16 keys).  PASS 1
+// writes the wave's per-row (max, sum exp2) partial to red[wave][r]; PASS 2 accumulates the
+// column sums of the lane's 8 keys into colsum.
+template <int PASS, int KIND>
+__device__ inline void sweep(const SelectParams& p, const KeySrc& ks, size_t hb, int lane, int wave,
+                             const bool (&valid)[8], float* red, float (&colsum)[8]) {
   const int n = lane & 15, q4 = lane >> 4;
   const int R = p.n_proxy * p.G;
   const int RB = (R + 15) >> 4;
+  KeyOps4 k4;
+  KeyOpsB kb;
+  if (KIND == 0) load_keys4(p, ks, hb, lane, k4);
+  else load_keysB(p, ks, hb, lane, kb);
+  RowBlock<PASS, KIND> cur, nxt;
+  load_rows(p, hb, R, 0, lane, cur);
+  for (int rb = 0; rb < RB; ++rb) {
+    if (rb + 1 < RB) load_rows(p, hb, R, rb + 1, lane, nxt);
+    const int r = rb * 16 + n;
+    const bool rvalid = r < R;
+    float sc[8];
+    if constexpr (KIND == 0) scores4(k4, cur.b4, cur.qsb, sc);
+    else scoresB(kb, cur.bb, sc);
+    if (PASS == 1) {
+      float m = -INFINITY;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) m = valid[j] ? fmaxf(m, sc[j]) : m;
+      m = col4_max(m);
+      float s = 0.f;
+      if (m != -INFINITY) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) s += valid[j] ? __builtin_amdgcn_exp2f(sc[j] - m) : 0.f;
+      }
+      s = col4_sum(s);
+      if (q4 == 0 && rvalid) {
+        red[((size_t)wave * R + r) * 2] = m;
+        red[((size_t)wave * R + r) * 2 + 1] = s;
+      }
+    } else if (rvalid) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) colsum[j] += valid[j] ? __builtin_amdgcn_exp2f(sc[j] - cur.M) * cur.iz : 0.f;
+    }
+    cur = nxt;
+  }
+}
+
+// One pass over the keys.  A wave owns one 32-key tile and sweeps the proxy rows in 16-row
+// blocks, reading the prepared B operands straight from L2 (no LDS staging, no barrier inside
+// the sweep).  PASS 1: per-row (max, sum exp2) over the workgroup's keys -- each wave keeps its
+// partial of every row in LDS, merged once at the end; PASS 2: column sums by position.
+template <int PASS>
+__global__ __launch_bounds__(SW * 64) __attribute__((amdgpu_waves_per_eu(3))) void select_pass_kernel(SelectParams p) {
+  extern __shared__ float red[];  // PASS 1: [SW][R][2]
+  const int task = blockIdx.x, hb = blockIdx.y;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n = lane & 15, q4 = lane >> 4;
+  const int R = p.n_proxy * p.G;
   const int gt = task * SW + wave;  // this wave's global tile
   const bool has = gt < p.n_tiles;
   KeySrc ks;
-  KeyOps ko;
-  if (has) {
-    ks = key_src(p, gt);
-    load_keys(p, ks, hb, lane, ko);
-  }
+  if (has) ks = key_src(p, gt);
   // validity of this lane's 8 keys
   bool valid[8];
 #pragma unroll
@@ -224,61 +306,31 @@ __global__ __launch_bounds__(512) void select_pass_kernel(SelectParams p) {
     const int key = (has ? ks.tile * 32 : 0) + ((j >> 2) << 4) + 4 * q4 + (j & 3);
     valid[j] = has && key < ks.count;
   }
-  const float* qsum = p.qsum + (size_t)hb * R * 4;
   float colsum[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-
-  stage_rows(p, b, hkv, 0, R, s16[0], sbf[0]);
-  __syncthreads();
-  for (int rb = 0; rb < RB; ++rb) {
-    const int cur = rb & 1;
-    if (rb + 1 < RB) stage_rows(p, b, hkv, (rb + 1) * 16, R, s16[cur ^ 1], sbf[cur ^ 1]);
-    const int r = rb * 16 + n;
-    const bool rvalid = r < R;
-    float sc[8];
-    if (has) {
-      float qs[4] = {0.f, 0.f, 0.f, 0.f};
-      if (ks.kind == 0 && rvalid) {
-#pragma unroll
-        for (int g = 0; g < 4; ++g) qs[g] = qsum[(size_t)r * 4 + g];
-      }
-      block_scores(ks, ko, s16[cur], sbf[cur], qs, lane, sc);
+  if (has) {
+    if (ks.kind == 0) sweep<PASS, 0>(p, ks, hb, lane, wave, valid, red, colsum);
+    else sweep<PASS, 1>(p, ks, hb, lane, wave, valid, red, colsum);
+  } else if (PASS == 1 && q4 == 0) {
+    for (int r = n; r < R; r += 16) {  // no keys: empty partials
+      red[((size_t)wave * R + r) * 2] = -INFINITY;
+      red[((size_t)wave * R + r) * 2 + 1] = 0.f;
     }
-    if (PASS == 1) {
-      // partial (max, sum exp2) of row r over this wave's keys
-      float m = -INFINITY;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) m = (has && valid[j]) ? fmaxf(m, sc[j]) : m;
-      m = fmaxf(m, shfl_xor_f(m, 16));
-      m = fmaxf(m, shfl_xor_f(m, 32));
-      float s = 0.f;
-      if (m != -INFINITY) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) s += (has && valid[j]) ? __builtin_amdgcn_exp2f(sc[j] - m) : 0.f;
-      }
-      s += shfl_xor_f(s, 16);
-      s += shfl_xor_f(s, 32);
-      if (q4 == 0) { red[wave][n][0] = m; red[wave][n][1] = s; }
-      __syncthreads();
-      if (threadIdx.x < 16 && rb * 16 + threadIdx.x < R) {
-        const int rr = threadIdx.x;
-        float M = -INFINITY;
-        for (int w2 = 0; w2 < SW; ++w2) M = fmaxf(M, red[w2][rr][0]);
-        float S = 0.f;
-        if (M != -INFINITY)
-          for (int w2 = 0; w2 < SW; ++w2) S += red[w2][rr][1] * __builtin_amdgcn_exp2f(red[w2][rr][0] - M);
-        float* dst = p.rowpart + (((size_t)hb * p.n_tasks + task) * R + rb * 16 + rr) * 2;
-        dst[0] = M;
-        dst[1] = S;
-      }
-    } else {
-      if (has && rvalid) {
-        const float M = p.rowstat[((size_t)hb * R + r) * 2];
-        const float iz = p.rowstat[((size_t)hb * R + r) * 2 + 1];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) colsum[j] += valid[j] ? __builtin_amdgcn_exp2f(sc[j] - M) * iz : 0.f;
-      }
-    }
+  }
+  if (PASS == 1) {
     __syncthreads();
+    for (int rr = threadIdx.x; rr < R; rr += blockDim.x) {
+      float M = -INFINITY;
+      for (int w2 = 0; w2 < SW; ++w2) M = fmaxf(M, red[((size_t)w2 * R + rr) * 2]);
+      float S = 0.f;
+      if (M != -INFINITY)
+        for (int w2 = 0; w2 < SW; ++w2) {
+          const float m2 = red[((size_t)w2 * R + rr) * 2];
+          if (m2 != -INFINITY) S += red[((size_t)w2 * R + rr) * 2 + 1] * __builtin_amdgcn_exp2f(m2 - M);
+        }
+      float* dst = p.rowpart + (((size_t)hb * R + rr) * p.n_tasks + task) * 2;  // [H][R][task]
+      dst[0] = M;
+      dst[1] = S;
+    }
   }
   if (PASS == 2 && has) {
     // sum over the 16 rows of each row block held by lanes n = 0..15 (same keys)
@@ -308,19 +360,27 @@ __global__ __launch_bounds__(512) void select_pass_kernel(SelectParams p) {
   }
 }
 
-// row partials -> (max, 1 / normaliser) per row
+// row partials -> (max, 1 / normaliser) per row: one wave per row, lanes over the tasks
 __global__ __launch_bounds__(256) void select_rowmerge_kernel(SelectParams p) {
-  const int hb = blockIdx.y;
+  const int hb = blockIdx.y, lane = threadIdx.x & 63;
   const int R = p.n_proxy * p.G;
-  for (int r = blockIdx.x * blockDim.x + threadIdx.x; r < R; r += gridDim.x * blockDim.x) {
-    const float* part = p.rowpart + (size_t)hb * p.n_tasks * R * 2;
-    float M = -INFINITY;
-    for (int t = 0; t < p.n_tasks; ++t) M = fmaxf(M, part[((size_t)t * R + r) * 2]);
-    float S = 0.f;
-    for (int t = 0; t < p.n_tasks; ++t) {
-      const float m = part[((size_t)t * R + r) * 2];
-      if (m != -INFINITY) S += part[((size_t)t * R + r) * 2 + 1] * __builtin_amdgcn_exp2f(m - M);
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= R) return;
+  const float* part = p.rowpart + ((size_t)hb * R + r) * p.n_tasks * 2;  // this row's task partials
+  float M = -INFINITY;
+  for (int t = lane; t < p.n_tasks; t += 64) M = fmaxf(M, part[(size_t)t * 2]);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, shfl_xor_f(M, o));
+  float S = 0.f;
+  if (M != -INFINITY) {
+    for (int t = lane; t < p.n_tasks; t += 64) {
+      const float m = part[(size_t)t * 2];
+      if (m != -INFINITY) S += part[(size_t)t * 2 + 1] * __builtin_amdgcn_exp2f(m - M);
     }
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) S += shfl_xor_f(S, o);
+  if (lane == 0) {
     p.rowstat[((size_t)hb * R + r) * 2] = M;
     p.rowstat[((size_t)hb * R + r) * 2 + 1] = 1.0f / S;
   }
@@ -332,81 +392,123 @@ __global__ __launch_bounds__(256) void select_rowmerge_kernel(SelectParams p) {
 // written in ascending position order.
 constexpr int TK_THREADS = 1024;
 
+constexpr int TK_REG = 32;  // scores per thread kept in registers (P <= 32768)
+
+__device__ inline int wave_incl_scan(int x, int lane) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off);
+    if (lane >= off) x += y;
+  }
+  return x;
+}
+
+// exclusive prefix over the 1024 threads (wave scans + the 16 wave totals); *tot = sum
+__device__ inline int tk_block_scan(int v, int* wtot, int* tot) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int incl = wave_incl_scan(v, lane);
+  if (lane == 63) wtot[wv] = incl;
+  __syncthreads();
+  int before = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < TK_THREADS / 64; ++w) {
+    const int t = wtot[w];
+    before += w < wv ? t : 0;
+    all += t;
+  }
+  __syncthreads();
+  *tot = all;
+  return before + incl - v;
+}
+
+// REG: every thread loads its contiguous range of scores once into registers (P <= TK_REG *
+// TK_THREADS); otherwise each pass re-reads them.
+template <bool REG>
 __global__ __launch_bounds__(TK_THREADS) void topk_kernel(SelectParams p) {
   __shared__ int hist[256];
-  __shared__ int scan_a[TK_THREADS], scan_b[TK_THREADS];
+  __shared__ int whist[TK_THREADS / 64][256];  // per-wave histograms (few distinct high digits)
+  __shared__ int wtot[TK_THREADS / 64];
   __shared__ uint32_t s_prefix, s_mask;
   __shared__ int s_need;
   const int hb = blockIdx.x, tid = threadIdx.x;
   const int P = p.len - WIN > 0 ? p.len - WIN : 0;
   const uint32_t* sc = (const uint32_t*)(p.scores + hb * (size_t)P);
   int32_t* out = p.idx_out + hb * (size_t)p.k;
+  // each thread owns the contiguous positions [lo, hi)
+  const int per = (P + TK_THREADS - 1) / TK_THREADS;
+  const int lo = min(P, tid * per), hi = min(P, lo + per);
+  uint32_t v[REG ? TK_REG : 1];
+  if constexpr (REG) {
+#pragma unroll
+    for (int i = 0; i < TK_REG; ++i) v[i] = lo + i < hi ? sc[lo + i] : 0u;
+  }
+  auto val = [&](int i) -> uint32_t {  // score at position lo + i
+    if constexpr (REG) return v[i]; else return sc[lo + i];
+  };
+  const int cnt = REG ? TK_REG : per;
   if (tid == 0) { s_prefix = 0u; s_mask = 0u; s_need = p.k; }
   __syncthreads();
   // four 8-bit digits, most significant first: find T and how many of it to keep
+  const int wv = tid >> 6;
   for (int shift = 24; shift >= 0; shift -= 8) {
-    for (int i = tid; i < 256; i += TK_THREADS) hist[i] = 0;
+    for (int i = tid; i < (TK_THREADS / 64) * 256; i += TK_THREADS) (&whist[0][0])[i] = 0;
     __syncthreads();
     const uint32_t prefix = s_prefix, mask = s_mask;
-    for (int i = tid; i < P; i += TK_THREADS) {
-      const uint32_t v = sc[i];
-      if ((v & mask) == prefix) atomicAdd(&hist[(v >> shift) & 255], 1);
+#pragma unroll
+    for (int i = 0; i < cnt; ++i) {
+      if (lo + i >= hi) continue;
+      const uint32_t x = val(i);
+      if ((x & mask) == prefix) atomicAdd(&whist[wv][(x >> shift) & 255], 1);
     }
     __syncthreads();
-    if (tid == 0) {
-      int need = s_need, d = 255;
-      for (; d > 0; --d) {
-        if (hist[d] >= need) break;
-        need -= hist[d];
+    // digit d = 255 - tid: count with digit >= d (a suffix sum, as a prefix over tid); the
+    // chosen digit is the largest d whose count reaches `need`
+    const int need = s_need;
+    int h = 0, incl = 0;
+    if (tid < 256) {
+#pragma unroll
+      for (int w = 0; w < TK_THREADS / 64; ++w) h += whist[w][255 - tid];
+      incl = wave_incl_scan(h, tid & 63);
+      if ((tid & 63) == 63) hist[tid >> 6] = incl;
+    }
+    __syncthreads();
+    if (tid < 256) {
+      for (int w = 0; w < (tid >> 6); ++w) incl += hist[w];
+      const int excl = incl - h;
+      const int d = 255 - tid;
+      if (excl < need && (incl >= need || d == 0)) {
+        s_prefix = prefix | ((uint32_t)d << shift);
+        s_mask = mask | (255u << shift);
+        s_need = need - excl;  // how many elements equal to the final prefix must be kept
       }
-      s_prefix = prefix | ((uint32_t)d << shift);
-      s_mask = mask | (255u << shift);
-      s_need = need;  // how many elements equal to the final prefix must be kept
     }
     __syncthreads();
   }
   const uint32_t T = s_prefix;
   const int need_eq = s_need;
-  // ordered compaction: each thread owns a contiguous range of positions
-  const int per = (P + TK_THREADS - 1) / TK_THREADS;
-  const int lo = tid * per, hi = min(P, lo + per);
+  // ordered compaction
   int n_gt = 0, n_eq = 0;
-  for (int i = lo; i < hi; ++i) {
-    const uint32_t v = sc[i];
-    n_gt += v > T;
-    n_eq += v == T;
+#pragma unroll
+  for (int i = 0; i < cnt; ++i) {
+    if (lo + i >= hi) continue;
+    const uint32_t x = val(i);
+    n_gt += x > T;
+    n_eq += x == T;
   }
-  scan_a[tid] = n_eq;
-  __syncthreads();
-  // exclusive scan of the equal counts (Hillis-Steele, ping-pong)
-  int* src = scan_a;
-  int* dst = scan_b;
-  for (int off = 1; off < TK_THREADS; off <<= 1) {
-    dst[tid] = src[tid] + (tid >= off ? src[tid - off] : 0);
-    __syncthreads();
-    int* t = src; src = dst; dst = t;
-  }
-  const int eq_before = src[tid] - n_eq;
+  int tot;
+  const int eq_before = tk_block_scan(n_eq, wtot, &tot);
   int take_eq = need_eq - eq_before;
   take_eq = take_eq < 0 ? 0 : (take_eq > n_eq ? n_eq : take_eq);
   const int mine = n_gt + take_eq;
-  __syncthreads();
-  scan_a[tid] = mine;
-  __syncthreads();
-  src = scan_a;
-  dst = scan_b;
-  for (int off = 1; off < TK_THREADS; off <<= 1) {
-    dst[tid] = src[tid] + (tid >= off ? src[tid - off] : 0);
-    __syncthreads();
-    int* t = src; src = dst; dst = t;
-  }
-  int o = src[tid] - mine;
+  int o = tk_block_scan(mine, wtot, &tot);
   int eq_left = take_eq;
-  for (int i = lo; i < hi; ++i) {
-    const uint32_t v = sc[i];
-    if (v > T || (v == T && eq_left > 0)) {
-      if (v == T) --eq_left;
-      if (o < p.k) out[o] = i;  // exactly k are kept for finite scores; never write past k
+#pragma unroll
+  for (int i = 0; i < cnt; ++i) {
+    if (lo + i >= hi) continue;
+    const uint32_t x = val(i);
+    if (x > T || (x == T && eq_left > 0)) {
+      if (x == T) --eq_left;
+      if (o < p.k) out[o] = lo + i;  // exactly k are kept for finite scores; never write past k
       ++o;
     }
   }
@@ -418,17 +520,20 @@ hipError_t launch_select(SelectParams p, hipStream_t stream) {
   const int R = p.n_proxy * p.G;
   const int H = p.B * p.Hkv;
   hipError_t e;
-  hipLaunchKernelGGL(select_qsum_kernel, dim3((R * 4 + 255) / 256, H), dim3(256), 0, stream, p);
+  const int RB = (R + 15) / 16;
+  hipLaunchKernelGGL(select_prep_kernel, dim3((RB * 256 + 255) / 256, H), dim3(256), 0, stream, p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   dim3 grid(p.n_tasks, H);
-  hipLaunchKernelGGL(select_pass_kernel<1>, grid, dim3(SW * 64), 0, stream, p);
+  hipLaunchKernelGGL(select_pass_kernel<1>, grid, dim3(SW * 64), (size_t)SW * R * 2 * sizeof(float), stream, p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(select_rowmerge_kernel, dim3((R + 255) / 256, H), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL(select_rowmerge_kernel, dim3((R + 3) / 4, H), dim3(256), 0, stream, p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(select_pass_kernel<2>, grid, dim3(SW * 64), 0, stream, p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (p.k > 0) {
-    hipLaunchKernelGGL(topk_kernel, dim3(H), dim3(TK_THREADS), 0, stream, p);
+    const int P = p.len > WIN ? p.len - WIN : 0;
+    if (P <= TK_REG * TK_THREADS) hipLaunchKernelGGL(topk_kernel<true>, dim3(H), dim3(TK_THREADS), 0, stream, p);
+    else hipLaunchKernelGGL(topk_kernel<false>, dim3(H), dim3(TK_THREADS), 0, stream, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   return hipSuccess;
