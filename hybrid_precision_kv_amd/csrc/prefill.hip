@@ -38,10 +38,11 @@ constexpr int K8_LD = 144;        // LDS row stride (bytes) of the INT8 K tile
 constexpr int KB_LD = 272;        // LDS row stride (bytes) of the bf16 K tile
 constexpr int LDS_V = 64 * KB_LD; // V tile offset (bf16 tiles)
 constexpr int LDS_BF = LDS_V + 16384;
-// quantized tiles are double-buffered: buffer b at b * LDS_QBUF, V codes at + LDS_QV
+// quantized tiles rotate through a ring of 3 buffers: buffer b at b * LDS_QBUF, V codes at
+// + LDS_QV
 constexpr int LDS_QV = 64 * K8_LD;
 constexpr int LDS_QBUF = LDS_QV + 8192;
-constexpr int LDS_TILE = 2 * LDS_QBUF > LDS_BF ? 2 * LDS_QBUF : LDS_BF;
+constexpr int LDS_TILE = 3 * LDS_QBUF > LDS_BF ? 3 * LDS_QBUF : LDS_BF;
 // INT8 Q codes of the workgroup's 128 queries (operand order), after the tile buffers
 constexpr int LDS_Q8 = LDS_TILE;
 constexpr int LDS_TOTAL = LDS_Q8 + 128 * K8_LD;
@@ -361,14 +362,15 @@ __device__ inline void qk_tile_q(const Ctx& c, const uint8_t* buf, const uint8_t
   }
 }
 
-// Online softmax of one quantized tile's scores and its P.V: P = E4M3(448 p) against the
-// E4M3 V codes, the row sum of the rounded P from an MFMA against a row of ones.
-// c2 = s_Q s_K alpha log2(e) (wave-uniform).  Below C2_FAST_MIN a masked score is not
-// guaranteed to underflow exp2, so the masked entries are zeroed explicitly.
+// Online softmax of one quantized tile's scores: P = E4M3(448 p) codes of the lane's keys as
+// the B operand of the P.V MFMA (pk), after the row state's max update (and rescale of acc
+// when the max moved).  c2 = s_Q s_K alpha log2(e) (wave-uniform).  Below C2_FAST_MIN a masked
+// score is not guaranteed to underflow exp2, so the masked entries are zeroed explicitly.
 template <bool TINY>
-__device__ inline void sm_pv_tile_q(const Ctx& c, const uint8_t* buf, const i32x4 (&S2)[2][4], float c2,
-                                    RowState& st) {
-  i64 pk[2][2];
+__device__ inline void softmax_tile_q(const i32x4 (&S2)[2][4], float c2, RowState& st, i64 (&pk)[2][2]) {
+  // 1. tile maxima and the row-state update of both 16-query blocks
+  float muse[2], resc[2];
+  bool moved = false;
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     int mi = NEG_DOT;
@@ -377,14 +379,23 @@ __device__ inline void sm_pv_tile_q(const Ctx& c, const uint8_t* buf, const i32x
       mi = max(mi, max(max(S2[qb][kb][0], S2[qb][kb][1]), max(S2[qb][kb][2], S2[qb][kb][3])));
     mi = wave_max_i(mi);
     const bool valid = mi > NEG_DOT / 2;
-    const float muse = os_update(st, qb, valid, (float)mi * c2, LOG2_448);
+    const float mold = st.m[qb];
+    const float mnew = valid ? fmaxf(mold, (float)mi * c2) : mold;
+    resc[qb] = (mnew == mold) ? 1.0f : __builtin_amdgcn_exp2f(mold - mnew);
+    moved |= resc[qb] != 1.0f;
+    st.m[qb] = mnew;
+    muse[qb] = valid ? mnew - LOG2_448 : INFINITY;
+  }
+  // 2. P codes of both blocks in one straight-line block (the exp2 chains interleave)
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
     uint32_t pw[4];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
       float pv[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        pv[r] = __builtin_amdgcn_exp2f(__builtin_fmaf((float)S2[qb][kb][r], c2, -muse));
+        pv[r] = __builtin_amdgcn_exp2f(__builtin_fmaf((float)S2[qb][kb][r], c2, -muse[qb]));
         if (TINY && S2[qb][kb][r] <= NEG_DOT / 2) pv[r] = 0.0f;
       }
       const uint32_t w = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(pv[0], pv[1], 0, false);
@@ -393,6 +404,20 @@ __device__ inline void sm_pv_tile_q(const Ctx& c, const uint8_t* buf, const i32x
     pk[qb][0] = (i64)pw[0] | ((i64)pw[1] << 32);
     pk[qb][1] = (i64)pw[2] | ((i64)pw[3] << 32);
   }
+  // 3. rescale the accumulators when some row's max moved (rare after the first tiles)
+  if (__builtin_amdgcn_ballot_w64(moved)) {
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+#pragma unroll
+      for (int cb = 0; cb < 8; ++cb) st.acc[qb][cb] *= resc[qb];
+      st.lacc[qb] *= resc[qb];
+    }
+  }
+}
+
+// P.V of one quantized tile against its E4M3 V codes (buffer buf), plus the row sum of the
+// rounded P from an MFMA against a row of ones.
+__device__ inline void pv_tile_q(const Ctx& c, const uint8_t* buf, const i64 (&pk)[2][2], RowState& st) {
 #pragma unroll
   for (int cb = 0; cb < 8; ++cb) {
 #pragma unroll
@@ -489,52 +514,77 @@ __device__ inline void compute_tile_bf(const PrefillParams& p, const Ctx& c, con
 }
 
 // Segment A (quantized tiles 0 .. nA-1) for one workgroup.
+//
+// Software pipeline over a ring of 3 LDS tile buffers, one barrier per tile.  Iteration t:
+//   store tile t+2 (fetched into registers during iteration t-1) into buffer (t+2) % 3 --
+//   free since the previous barrier, its last reader being P.V(t-1);
+//   fetch tile t+3 into registers;
+//   P.V(t) (MFMA, codes from the previous iteration) and, underneath it, softmax(t+1) (VALU);
+//   barrier (tile t+2 visible to everyone);
+//   QK^T(t+2) (MFMA).
+// The exact per-tile max update of softmax(t+1) may rescale the accumulator: that multiply
+// waits for P.V(t), as the order of Alg. 2 requires.  Tiles past the wave's last row
+// (64 t > r0w + 31 - 128) are loaded for the other waves but not computed.
+struct TileMeta {
+  uint32_t w0, w1;
+  float sk;
+};
+
+template <bool TINY>
+__device__ inline float tile_c2(float sq_u, float sk) {
+  float c2 = uniform_f(sq_u * sk * AL2);
+  if (TINY) c2 = c2 > 0.0f ? c2 : 1.0f;  // a zero scale means every valid dot is 0
+  return c2;
+}
+
+template <bool TINY>
+__device__ inline void segment_a_step(const PrefillParams& p, const Ctx& c, uint8_t* lds, int nA, int nAw,
+                                      float sq_u, int t, TileQRegs& pre, TileMeta& m1, TileMeta& m2,
+                                      i32x4 (&S2)[2][4], const i64 (&pk)[2][2], i64 (&pkn)[2][2],
+                                      RowState& st) {
+  if (t + 2 < nA) {  // tile t+2 -> buffer (t+2) % 3
+    store_tile_q(c, lds + ((t + 2) % 3) * LDS_QBUF, pre);
+    m2 = TileMeta{pre.w0, pre.w1, pre.sk};
+  }
+  if (t + 3 < nA) fetch_tile_q(p, c, t + 3, pre);  // in flight during this tile's compute
+  if (t < nAw) pv_tile_q(c, lds + (t % 3) * LDS_QBUF, pk, st);
+  if (t + 1 < nAw) softmax_tile_q<TINY>(S2, tile_c2<TINY>(sq_u, m1.sk), st, pkn);
+  __syncthreads();
+  if (t + 2 < nAw) qk_tile_q(c, lds + ((t + 2) % 3) * LDS_QBUF, lds + LDS_Q8, t + 2, m2.w0, m2.w1, S2);
+  m1 = m2;
+}
+
 template <bool TINY>
 __device__ inline void segment_a(const PrefillParams& p, const Ctx& c, uint8_t* lds, int nA, float sq_u,
                                  RowState& st) {
-  // Software pipeline: iteration t stores tile t+1 into the other LDS buffer, issues the
-  // QK^T MFMAs of tile t+1, then runs the softmax (VALU) and P.V of tile t -- the MFMA pipe
-  // works on tile t+1 while the VALU works on tile t.  Tiles past the wave's last row
-  // (64 t > r0w + 31 - 128) are loaded for the other waves but not computed.
   const int nAw = c.r0w + 31 - WIN >= 0 ? ((c.r0w + 31 - WIN) >> 6) + 1 : 0;
-  if (nA > 0) {
-    TileQRegs pre;
-    fetch_tile_q(p, c, 0, pre);
-    __syncthreads();
-    store_tile_q(c, lds, pre);
-    float sk_cur = pre.sk;
-    const uint32_t w0 = pre.w0, w1 = pre.w1;
-    if (nA > 1) fetch_tile_q(p, c, 1, pre);
-    __syncthreads();
-    i32x4 S2[2][4];
-    if (nAw > 0) qk_tile_q(c, lds, lds + LDS_Q8, 0, w0, w1, S2);
-    for (int t = 0; t < nA; ++t) {
-      const uint8_t* cur = lds + (t & 1) * LDS_QBUF;
-      uint8_t* nxt = lds + ((t + 1) & 1) * LDS_QBUF;
-      float sk_nxt = 0.0f;
-      uint32_t nw0 = 0, nw1 = 0;
-      __syncthreads();  // everyone is done with tile t-1 (it lived in nxt)
-      if (t + 1 < nA) {
-        store_tile_q(c, nxt, pre);
-        sk_nxt = pre.sk;
-        nw0 = pre.w0;
-        nw1 = pre.w1;
-      }
-      __syncthreads();
-      if (t + 2 < nA) fetch_tile_q(p, c, t + 2, pre);  // in flight during this tile's compute
-      i32x4 S2n[2][4];
-      if (t + 1 < nAw) qk_tile_q(c, nxt, lds + LDS_Q8, t + 1, nw0, nw1, S2n);
-      if (t < nAw) {
-        float c2 = uniform_f(sq_u * sk_cur * AL2);
-        if (TINY) c2 = c2 > 0.0f ? c2 : 1.0f;  // a zero scale means every valid dot is 0
-        sm_pv_tile_q<TINY>(c, cur, S2, c2, st);
-      }
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) S2[qb][kb] = S2n[qb][kb];
-      sk_cur = sk_nxt;
-    }
+  if (nA <= 0) return;
+  TileQRegs pre;
+  TileMeta m0{0u, 0u, 0.0f}, m1{0u, 0u, 0.0f}, m2{0u, 0u, 0.0f};
+  fetch_tile_q(p, c, 0, pre);
+  __syncthreads();  // nothing else uses the tile buffers now
+  store_tile_q(c, lds, pre);
+  m0 = TileMeta{pre.w0, pre.w1, pre.sk};
+  if (nA > 1) {
+    fetch_tile_q(p, c, 1, pre);
+    store_tile_q(c, lds + LDS_QBUF, pre);
+    m1 = TileMeta{pre.w0, pre.w1, pre.sk};
+  }
+  if (nA > 2) fetch_tile_q(p, c, 2, pre);
+  __syncthreads();
+  // prologue: scores and P codes of tile 0, scores of tile 1
+  i32x4 S2[2][4];
+  i64 pa[2][2], pb[2][2];
+  if (nAw > 0) {
+    qk_tile_q(c, lds, lds + LDS_Q8, 0, m0.w0, m0.w1, S2);
+    softmax_tile_q<TINY>(S2, tile_c2<TINY>(sq_u, m0.sk), st, pa);
+  }
+  if (1 < nAw) qk_tile_q(c, lds + LDS_QBUF, lds + LDS_Q8, 1, m1.w0, m1.w1, S2);
+  // unrolled by two so the P-code registers alternate instead of being copied
+  for (int t = 0; t < nA; t += 2) {
+    segment_a_step<TINY>(p, c, lds, nA, nAw, sq_u, t, pre, m1, m2, S2, pa, pb, st);
+    if (t + 1 >= nA) break;
+    segment_a_step<TINY>(p, c, lds, nA, nAw, sq_u, t + 1, pre, m1, m2, S2, pb, pa, st);
   }
 }
 
@@ -545,10 +595,22 @@ __global__ void __launch_bounds__(256, 2) pf_attn_kernel(PrefillParams p) {
   __shared__ float skmin[4];
   __shared__ int nb_anchor_s;
 
+  // Workgroup -> (query block, Q head), longest rows first.  Workgroups are dispatched to the
+  // 8 XCDs round-robin (id % 8); the G Q heads of one KV group read the same K/V tiles in the
+  // same order, so they are given consecutive ids on one XCD and share its L2.
   const int nQB = p.Npad / WG_ROWS;
-  const int qblk = nQB - 1 - (int)blockIdx.x / p.Hq;  // longest rows first
+  const int groups = nQB * p.Hkv, bid = (int)blockIdx.x;
+  int qblk, hq;
+  if (groups % 8 == 0) {
+    const int i = bid >> 3, gi = (i / p.G) * 8 + (bid & 7);
+    qblk = nQB - 1 - gi / p.Hkv;
+    hq = (gi % p.Hkv) * p.G + i % p.G;
+  } else {
+    qblk = nQB - 1 - bid / p.Hq;
+    hq = bid % p.Hq;
+  }
   Ctx c;
-  c.h = (int)blockIdx.x % p.Hq;
+  c.h = hq;
   c.hk = c.h / p.G;
   const int r0 = qblk * WG_ROWS;
   c.tid = threadIdx.x;
