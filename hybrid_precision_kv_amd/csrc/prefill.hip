@@ -41,7 +41,8 @@ constexpr int LDS_BF = LDS_V + 16384;
 // quantized tiles rotate through a ring of 3 buffers: buffer b at b * LDS_QBUF, V codes at
 // + LDS_QV
 constexpr int LDS_QV = 64 * K8_LD;
-constexpr int LDS_QBUF = LDS_QV + 8192;
+constexpr int LDS_QBIAS = LDS_QV + 8192;  // per-key MFMA C input: 0, or NEG_DOT for an anchor
+constexpr int LDS_QBUF = LDS_QBIAS + 256;
 constexpr int LDS_TILE = 3 * LDS_QBUF > LDS_BF ? 3 * LDS_QBUF : LDS_BF;
 // INT8 Q codes of the workgroup's 128 queries (operand order), after the tile buffers
 constexpr int LDS_Q8 = LDS_TILE;
@@ -303,6 +304,10 @@ __device__ inline void store_tile_q(const Ctx& c, uint8_t* lds, const TileQRegs&
     *(u32x4*)(lds + row * K8_LD + 16 * part) = r.k[i];
     *(u32x4*)(lds + LDS_QV + 16 * ch) = r.v[i];
   }
+  if (c.tid < 64) {  // anchor mask of key tid, built once per tile for every wave
+    const uint32_t word = c.tid < 32 ? r.w0 : r.w1;
+    *(int*)(lds + LDS_QBIAS + 4 * c.tid) = ((word >> (c.tid & 31)) & 1u) ? NEG_DOT : 0;
+  }
 }
 
 // bf16 tile: 64 K rows (row stride KB_LD in LDS; rows whose key_of(row) is outside [0, N)
@@ -326,17 +331,14 @@ __device__ inline void load_tile_bf(const Ctx& c, uint8_t* lds, const uint16_t* 
 // C input.  Two passes over the 64 channels of each k-step so the 8 independent (qb, kb)
 // chains interleave in the MFMA pipe.
 __device__ inline void qk_tile_q(const Ctx& c, const uint8_t* buf, const uint8_t* q8s, int t,
-                                 uint32_t w0, uint32_t w1, i32x4 (&S2)[2][4]) {
+                                 i32x4 (&S2)[2][4]) {
   const int kt0 = 64 * t;
   // Q codes of this lane's query (row l16 of block qb): 16 bytes per k-step
   const uint8_t* qrow = q8s + (32 * c.wave + c.l16) * K8_LD + 16 * c.j;
   const bool interior = kt0 + 63 <= c.r0w - WIN;
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb) {
-    const uint32_t nib = ((kb < 2 ? w0 : w1) >> (16 * (kb & 1) + 4 * c.j)) & 0xfu;
-    i32x4 bias;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) bias[r] = ((nib >> r) & 1u) ? NEG_DOT : 0;
+    const i32x4 bias = *(const i32x4*)(buf + LDS_QBIAS + 4 * (16 * kb + 4 * c.j));  // keys 16kb+4j+r
     const i32x4 kf0 = *(const i32x4*)(buf + (16 * kb + c.l16) * K8_LD + 16 * c.j);
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
@@ -550,7 +552,7 @@ __device__ inline void segment_a_step(const PrefillParams& p, const Ctx& c, uint
   if (t < nAw) pv_tile_q(c, lds + (t % 3) * LDS_QBUF, pk, st);
   if (t + 1 < nAw) softmax_tile_q<TINY>(S2, tile_c2<TINY>(sq_u, m1.sk), st, pkn);
   __syncthreads();
-  if (t + 2 < nAw) qk_tile_q(c, lds + ((t + 2) % 3) * LDS_QBUF, lds + LDS_Q8, t + 2, m2.w0, m2.w1, S2);
+  if (t + 2 < nAw) qk_tile_q(c, lds + ((t + 2) % 3) * LDS_QBUF, lds + LDS_Q8, t + 2, S2);
   m1 = m2;
 }
 
@@ -576,10 +578,10 @@ __device__ inline void segment_a(const PrefillParams& p, const Ctx& c, uint8_t* 
   i32x4 S2[2][4];
   i64 pa[2][2], pb[2][2];
   if (nAw > 0) {
-    qk_tile_q(c, lds, lds + LDS_Q8, 0, m0.w0, m0.w1, S2);
+    qk_tile_q(c, lds, lds + LDS_Q8, 0, S2);
     softmax_tile_q<TINY>(S2, tile_c2<TINY>(sq_u, m0.sk), st, pa);
   }
-  if (1 < nAw) qk_tile_q(c, lds + LDS_QBUF, lds + LDS_Q8, 1, m1.w0, m1.w1, S2);
+  if (1 < nAw) qk_tile_q(c, lds + LDS_QBUF, lds + LDS_Q8, 1, S2);
   // unrolled by two so the P-code registers alternate instead of being copied
   for (int t = 0; t < nA; t += 2) {
     segment_a_step<TINY>(p, c, lds, nA, nAw, sq_u, t, pre, m1, m2, S2, pa, pb, st);
