@@ -9,19 +9,22 @@
 //
 // Attention kernel design (one workgroup = 128 queries of one Q head, 4 waves x 32 queries):
 //  * Scores are computed transposed, S^T = K . Q^T, with 16x16 MFMA tiles: a lane then holds
-//    16 keys of ONE query per 16-query block, so row maxima are mostly in-lane and the score
-//    registers are directly the B operand of O^T = V^T . P^T (keys permuted identically in
-//    the V tile layout).  The accumulator O^T keeps 4 channels x 1 query per lane and block.
+//    16 keys of ONE query per 16-query block, so row maxima are mostly in-lane.  One
+//    v_permlane16_swap per packed word regroups the P codes of both 16-query blocks into the
+//    B operand of a 32x32 MFMA (lane l: query l % 32, 32 of the tile's keys), and
+//    O^T = V^T . P^T runs on 32x32 tiles: the fp8 32x32x64 MFMA runs at twice the rate of
+//    the 16x16x32 one.  The V tile layouts permute the keys the same way.
 //  * Quantized tiles: i32 MFMA 16x16x64 on INT8 codes; the mask (anchors, causal edge) enters
 //    as the MFMA's C input (-2^28), so interior tiles pay nothing for it; P = E4M3(448 p)
-//    feeds FP8 MFMA 16x16x32 against E4M3 V codes; the row sum of the rounded P comes out of
-//    one more MFMA against a row of ones.  After the last quantized tile the accumulator is
+//    feeds the fp8 32x32x64 MFMA against E4M3 V codes; the row sum of the rounded P comes out
+//    of 16x16 MFMAs against a row of ones.  After the last quantized tile the accumulator is
 //    scaled by the per-channel V scale / 448.
-//  * Anchor and window tiles: bf16 MFMA 16x16x32 with a -inf mask in the C input; P = bf16(p).
+//  * Anchor and window tiles: bf16 MFMA 16x16x32 for the scores with a -inf mask in the C
+//    input, P = bf16(p), bf16 32x32x16 MFMA for P.V.
 //  * The running max is exact per 64-key tile (no lazy threshold): the P codes depend on it.
-//    A row's accumulator is rescaled only when its max moved (wave-uniform branch).
-//  * Q is quantized in registers from the bf16 operand fragments (block maximum exchanged
-//    through LDS); the codes are also written to the workspace.
+//    The accumulator is rescaled only when some row's max moved (wave-uniform branch).
+//  * Q is quantized in registers from the bf16 rows (block maximum exchanged through LDS);
+//    the codes stay in registers as the QK B operand and are also written to the workspace.
 #include "hyq_common.h"
 #include "hyq_launch.h"
 
@@ -34,19 +37,16 @@ constexpr int NEG_DOT = -(1 << 28);  // masked INT8 dot (|valid dot| < 2^21)
 constexpr float AL2 = 0.08838834764831845f * 1.4426950408889634f;  // alpha * log2(e), alpha = 1/sqrt(128)
 constexpr float LOG2_448 = 8.807354922057604f;
 constexpr float C2_FAST_MIN = 1e-6f;  // below: masked INT8 scores are zeroed explicitly
-constexpr int K8_LD = 144;        // LDS row stride (bytes) of the INT8 K tile
 constexpr int KB_LD = 272;        // LDS row stride (bytes) of the bf16 K tile
 constexpr int LDS_V = 64 * KB_LD; // V tile offset (bf16 tiles)
 constexpr int LDS_BF = LDS_V + 16384;
-// quantized tiles rotate through a ring of 3 buffers: buffer b at b * LDS_QBUF, V codes at
-// + LDS_QV
-constexpr int LDS_QV = 64 * K8_LD;
+// Quantized tiles rotate through a ring of 3 buffers: buffer b at b * LDS_QBUF holds the K
+// codes as [16-byte chunk 8][key 64][16], the V codes at + LDS_QV as stored in the workspace,
+// and the per-key mask at + LDS_QBIAS.
+constexpr int LDS_QV = 8192;
 constexpr int LDS_QBIAS = LDS_QV + 8192;  // per-key MFMA C input: 0, or NEG_DOT for an anchor
 constexpr int LDS_QBUF = LDS_QBIAS + 256;
-constexpr int LDS_TILE = 3 * LDS_QBUF > LDS_BF ? 3 * LDS_QBUF : LDS_BF;
-// INT8 Q codes of the workgroup's 128 queries (operand order), after the tile buffers
-constexpr int LDS_Q8 = LDS_TILE;
-constexpr int LDS_TOTAL = LDS_Q8 + 128 * K8_LD;
+constexpr int LDS_TOTAL = 3 * LDS_QBUF > LDS_BF ? 3 * LDS_QBUF : LDS_BF;
 
 typedef long i64;
 
@@ -144,8 +144,9 @@ __global__ void __launch_bounds__(256) pf_kquant_kernel(PrefillParams p) {
   __syncthreads();
   amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   const float s = __fdiv_rn(amax, 127.0f);
-  // operand order: dim 32 qd + 8 jj + e  ->  byte 64 (qd >> 1) + 16 jj + 8 (qd & 1) + e
-  int8_t* dst = p.k8 + ((size_t)h * p.Npad + key) * D + 64 * (qd >> 1) + 8 * (qd & 1);
+  // operand order: dim 32 qd + 8 jj + e  ->  byte 64 (qd >> 1) + 16 jj + 8 (qd & 1) + e, and
+  // 16-byte chunk k = 4 (qd >> 1) + jj of the row at [tile][chunk][key in tile][16]
+  int8_t* dst = p.k8 + ((size_t)h * nb + blk) * 8192 + (4 * (qd >> 1)) * 1024 + row * 16 + 8 * (qd & 1);
 #pragma unroll
   for (int jj = 0; jj < 4; ++jj) {
     uint32_t w0 = 0, w1 = 0;
@@ -154,7 +155,7 @@ __global__ void __launch_bounds__(256) pf_kquant_kernel(PrefillParams p) {
       w0 |= (uint32_t)(int8_code(kx[8 * jj + e], s) & 0xff) << (8 * e);
       w1 |= (uint32_t)(int8_code(kx[8 * jj + 4 + e], s) & 0xff) << (8 * e);
     }
-    *(uint2*)(dst + 16 * jj) = make_uint2(w0, w1);
+    *(uint2*)(dst + 1024 * jj) = make_uint2(w0, w1);
   }
   if (t == 0) p.sk[(size_t)h * nb + blk] = s;
   if (t < D) {
@@ -180,10 +181,11 @@ __global__ void __launch_bounds__(1024) pf_vscale_kernel(PrefillParams p) {
   }
 }
 
-// V -> E4M3(V / s_V[c]) (hardware conversion: round to nearest even).  Operand order: per
-// 32-key block, [jj][channel][8 bytes]; byte e of (jj, channel) holds key 16 (e >> 2) + 4 jj +
-// (e & 3) of the block.  One lane group's 8-byte fragments of 16 channels are then 128
-// contiguous bytes (no LDS bank conflicts).
+// V -> E4M3(V / s_V[c]) (hardware conversion: round to nearest even).  Per 32-key block:
+// [half h][channel][16 bytes], byte e of (h, channel) holding key 16 (e >> 3) + 8 h + (e & 7)
+// of the block: two blocks' 16-byte rows of one channel and half are the A operand of the
+// 32x32x64 P.V MFMA for the key order the P-code regrouping produces.  The bf16 copy of V
+// (window tiles) is [8-key group][channel][8 keys].
 __global__ void __launch_bounds__(128) pf_vquant_kernel(PrefillParams p) {
   const int b = blockIdx.x, h = blockIdx.y, c = threadIdx.x;
   const uint32_t word = p.abits[(size_t)h * (p.Npad >> 5) + b];
@@ -197,22 +199,22 @@ __global__ void __launch_bounds__(128) pf_vquant_kernel(PrefillParams p) {
   for (int kk = 0; kk < 32; ++kk) {
     const int key = 32 * b + kk;
     const uint16_t vb = key < p.N ? p.v[((size_t)h * p.N + key) * D + c] : (uint16_t)0;
-    const int slot = 8 * ((kk & 15) >> 2) + 4 * (kk >> 4) + (kk & 3);  // 8 jj + e
-    raw[slot >> 1] |= (uint32_t)vb << (16 * (slot & 1));
+    raw[kk >> 1] |= (uint32_t)vb << (16 * (kk & 1));
     float x = 0.0f;
     if (key < p.N && !((word >> kk) & 1u)) x = bf16_bits_to_f32(vb);
     uint32_t code = 0;
     if (s != 0.0f) code = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(__fdiv_rn(x, s), 0.0f, 0, false) & 0xffu;
-    const int byte = 8 * ((kk & 15) >> 2) + 4 * (kk >> 4) + (kk & 3);  // 8 jj + e
+    const int byte = 16 * ((kk >> 3) & 1) + 8 * (kk >> 4) + (kk & 7);  // 16 h + e
     w[byte >> 2] |= code << (8 * (byte & 3));
   }
   uint8_t* blk = p.v8 + ((size_t)h * (p.Npad >> 5) + b) * D * 32;
   uint16_t* tblk = p.vt16 + ((size_t)h * (p.Npad >> 5) + b) * D * 32;
 #pragma unroll
-  for (int jj = 0; jj < 4; ++jj) {
-    *(uint2*)(blk + (jj * D + c) * 8) = make_uint2(w[2 * jj], w[2 * jj + 1]);
-    *(u32x4*)(tblk + (jj * D + c) * 8) = (u32x4){raw[4 * jj], raw[4 * jj + 1], raw[4 * jj + 2], raw[4 * jj + 3]};
-  }
+  for (int hh = 0; hh < 2; ++hh)
+    *(u32x4*)(blk + (hh * D + c) * 16) = (u32x4){w[4 * hh], w[4 * hh + 1], w[4 * hh + 2], w[4 * hh + 3]};
+#pragma unroll
+  for (int g = 0; g < 4; ++g)
+    *(u32x4*)(tblk + (g * D + c) * 8) = (u32x4){raw[4 * g], raw[4 * g + 1], raw[4 * g + 2], raw[4 * g + 3]};
 }
 
 // Anchor gather: K rows (list order) and V^T in the bf16 operand order, for list entries
@@ -234,50 +236,71 @@ __global__ void __launch_bounds__(128) pf_agather_kernel(PrefillParams p) {
       vb = p.v[((size_t)h * p.N + a) * D + c];
     }
     p.ka16[((size_t)h * Ac + idx) * D + c] = kb;
-    const int slot = 8 * ((kk & 15) >> 2) + 4 * (kk >> 4) + (kk & 3);
-    raw[slot >> 1] |= (uint32_t)vb << (16 * (slot & 1));
+    raw[kk >> 1] |= (uint32_t)vb << (16 * (kk & 1));
   }
   uint16_t* tblk = p.va16 + ((size_t)h * (Ac >> 5) + b) * D * 32;
 #pragma unroll
-  for (int jj = 0; jj < 4; ++jj)
-    *(u32x4*)(tblk + (jj * D + c) * 8) = (u32x4){raw[4 * jj], raw[4 * jj + 1], raw[4 * jj + 2], raw[4 * jj + 3]};
+  for (int g = 0; g < 4; ++g)
+    *(u32x4*)(tblk + (g * D + c) * 8) = (u32x4){raw[4 * g], raw[4 * g + 1], raw[4 * g + 2], raw[4 * g + 3]};
 }
 
 // ------------------------------------------------------------------ attention
 
-struct RowState {
-  float m[2];        // running max, log2 units, per 16-query block
-  f32x4 acc[2][8];   // O^T: channels 16 cb + 4 j + r, query l16
-  f32x4 lacc[2];     // row sums (all 4 entries equal)
-};
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
 
-// Online-softmax bookkeeping for one 16-query block and one tile: returns the value to
-// subtract inside exp2 (+inf for a row without a valid key in the tile) and rescales the
-// row state when its max moved.  tmax2 = tile max in log2 units (used only if `valid`).
-__device__ inline float os_update(RowState& st, int qb, bool valid, float tmax2, float shift) {
-  const float mold = st.m[qb];
-  const float mnew = valid ? fmaxf(mold, tmax2) : mold;
-  const float resc = (mnew == mold) ? 1.0f : __builtin_amdgcn_exp2f(mold - mnew);
-  st.m[qb] = mnew;
-  if (__builtin_amdgcn_ballot_w64(resc != 1.0f)) {
-#pragma unroll
-    for (int cb = 0; cb < 8; ++cb) st.acc[qb][cb] *= resc;
-    st.lacc[qb] *= resc;
-  }
-  return valid ? mnew - shift : INFINITY;
-}
+struct RowState {
+  float m[2];        // running max, log2 units, of query l16 in each 16-query block
+  f32x16 acc[4];     // O^T, 32x32 MFMA layout: element 4 i + r is channel 32 cb + 8 i + 4 hh + r
+                     // of query l32
+  f32x4 lacc[2];     // row sums of query l16 in each 16-query block (all 4 entries equal)
+};
 
 __device__ inline uint32_t pack_bf16x2(float a, float b) {
   return (uint32_t)f32_to_bf16_bits(a) | ((uint32_t)f32_to_bf16_bits(b) << 16);
 }
 
 struct Ctx {
-  int h, hk, r0w, N, Npad, nb64, tid, wave, l16, j;
+  int h, hk, r0w, N, Npad, nb64, tid, wave, l16, j, l32, hh, qsel;
 };
 
-// Quantized tile t: INT8 K rows [64 t, 64 t + 64) (row stride K8_LD in LDS) and the two
-// 32-key blocks of E4M3 V codes, copied as stored.  fetch: global -> registers (issued one
-// tile ahead), store: registers -> LDS.
+// Max update of both 16-query blocks of the wave from their tile maxima (log2 units, valid =
+// the block row has an unmasked key in the tile); rescales the accumulators when some row's
+// max moved.  Returns the values to subtract inside exp2 (+inf for rows without a valid key).
+__device__ inline void row_update(const Ctx& c, RowState& st, const bool (&valid)[2], const float (&tmax)[2],
+                                  float shift, float (&muse)[2]) {
+  float resc[2];
+  bool moved = false;
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const float mold = st.m[qb];
+    const float mnew = valid[qb] ? fmaxf(mold, tmax[qb]) : mold;
+    resc[qb] = (mnew == mold) ? 1.0f : __builtin_amdgcn_exp2f(mold - mnew);
+    moved |= resc[qb] != 1.0f;
+    st.m[qb] = mnew;
+    muse[qb] = valid[qb] ? mnew - shift : INFINITY;
+  }
+  if (__builtin_amdgcn_ballot_w64(moved)) {  // rare after the first tiles
+    const float rs = c.qsel ? resc[1] : resc[0];  // the accumulator row of this lane
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) st.acc[cb] *= rs;
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) st.lacc[qb] *= resc[qb];
+  }
+}
+
+// P codes (or bf16 pairs) of the two 16-query blocks, x from block 0 and y from block 1, for
+// the same keys of one lane: after the swap a lane of the 32x32 layout (query l32, half hh)
+// holds x = keys 16 kb + 8 hh + r and y = keys 16 kb + 8 hh + 4 + r of its own query.
+__device__ inline void regroup(uint32_t x, uint32_t y, uint32_t& lo, uint32_t& hi) {
+  const auto s = __builtin_amdgcn_permlane16_swap(x, y, false, false);
+  lo = s[0];
+  hi = s[1];
+}
+
+// Quantized tile t: INT8 K codes of keys [64 t, 64 t + 64) ([chunk][key][16] as stored), the
+// tile's E4M3 V codes (as stored) and its anchor words.  fetch: global -> registers (issued
+// ahead of use), store: registers -> LDS.
 struct TileQRegs {
   u32x4 k[2], v[2];
   uint32_t w0, w1;  // anchor bitmap words of the tile
@@ -288,20 +311,18 @@ __device__ inline void fetch_tile_q(const PrefillParams& p, const Ctx& c, int t,
   r.w0 = ab[0];
   r.w1 = ab[1];
   r.sk = p.sk[(size_t)c.hk * c.nb64 + t];
+  const size_t tile = ((size_t)c.hk * c.nb64 + t) * 8192;
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    const int ch = c.tid + 256 * i, row = ch >> 3, part = ch & 7;
-    r.k[i] = *(const u32x4*)(p.k8 + ((size_t)c.hk * c.Npad + 64 * t + row) * D + 16 * part);
+    r.k[i] = *(const u32x4*)(p.k8 + tile + 16 * (c.tid + 256 * i));
+    r.v[i] = *(const u32x4*)(p.v8 + tile + 16 * (c.tid + 256 * i));
   }
-  const uint8_t* vsrc = p.v8 + ((size_t)c.hk * (c.Npad >> 5) + 2 * t) * D * 32;
-#pragma unroll
-  for (int i = 0; i < 2; ++i) r.v[i] = *(const u32x4*)(vsrc + 16 * (c.tid + 256 * i));
 }
 __device__ inline void store_tile_q(const Ctx& c, uint8_t* lds, const TileQRegs& r) {
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    const int ch = c.tid + 256 * i, row = ch >> 3, part = ch & 7;
-    *(u32x4*)(lds + row * K8_LD + 16 * part) = r.k[i];
+    const int ch = c.tid + 256 * i;
+    *(u32x4*)(lds + 16 * ch) = r.k[i];
     *(u32x4*)(lds + LDS_QV + 16 * ch) = r.v[i];
   }
   if (c.tid < 64) {  // anchor mask of key tid, built once per tile for every wave
@@ -311,7 +332,7 @@ __device__ inline void store_tile_q(const Ctx& c, uint8_t* lds, const TileQRegs&
 }
 
 // bf16 tile: 64 K rows (row stride KB_LD in LDS; rows whose key_of(row) is outside [0, N)
-// are zero) and the tile's V^T (16 KB, copied as stored: [32-key block][jj][channel][8]).
+// are zero) and the tile's V (16 KB, copied as stored: [8-key group][channel][8]).
 template <typename KeyOf>
 __device__ inline void load_tile_bf(const Ctx& c, uint8_t* lds, const uint16_t* krows, int kstride_ok_n,
                                     const uint16_t* vt, KeyOf key_of) {
@@ -326,20 +347,19 @@ __device__ inline void load_tile_bf(const Ctx& c, uint8_t* lds, const uint16_t* 
   }
 }
 
-// Scores of one quantized tile for the wave's 32 queries: S^T = K . Q^T on INT8 codes, with
-// the masked keys (anchors; j > i - 128 on an edge tile) pushed to NEG_DOT through the MFMA's
-// C input.  Two passes over the 64 channels of each k-step so the 8 independent (qb, kb)
-// chains interleave in the MFMA pipe.
-__device__ inline void qk_tile_q(const Ctx& c, const uint8_t* buf, const uint8_t* q8s, int t,
+// Scores of one quantized tile for the wave's 32 queries: S^T = K . Q^T on INT8 codes (Q codes
+// in registers: qi[qb][s] = bytes 64 s + 16 j of query row 16 qb + l16), with the masked keys
+// (anchors; j > i - 128 on an edge tile) pushed to NEG_DOT through the MFMA's C input.  Two
+// passes over the 64 channels of each k-step so the 8 independent (qb, kb) chains interleave
+// in the MFMA pipe.
+__device__ inline void qk_tile_q(const Ctx& c, const uint8_t* buf, const i32x4 (&qi)[2][2], int t,
                                  i32x4 (&S2)[2][4]) {
   const int kt0 = 64 * t;
-  // Q codes of this lane's query (row l16 of block qb): 16 bytes per k-step
-  const uint8_t* qrow = q8s + (32 * c.wave + c.l16) * K8_LD + 16 * c.j;
   const bool interior = kt0 + 63 <= c.r0w - WIN;
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb) {
     const i32x4 bias = *(const i32x4*)(buf + LDS_QBIAS + 4 * (16 * kb + 4 * c.j));  // keys 16kb+4j+r
-    const i32x4 kf0 = *(const i32x4*)(buf + (16 * kb + c.l16) * K8_LD + 16 * c.j);
+    const i32x4 kf0 = *(const i32x4*)(buf + (c.j * 64 + 16 * kb + c.l16) * 16);
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       i32x4 acc = bias;
@@ -349,30 +369,27 @@ __device__ inline void qk_tile_q(const Ctx& c, const uint8_t* buf, const uint8_t
         for (int r = 0; r < 4; ++r)
           if (kt0 + 16 * kb + 4 * c.j + r > row - WIN) acc[r] = NEG_DOT;
       }
-      const i32x4 q0 = *(const i32x4*)(qrow + 16 * K8_LD * qb);
-      S2[qb][kb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(kf0, q0, acc, 0, 0, 0);
+      S2[qb][kb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(kf0, qi[qb][0], acc, 0, 0, 0);
     }
   }
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb) {
-    const i32x4 kf1 = *(const i32x4*)(buf + (16 * kb + c.l16) * K8_LD + 64 + 16 * c.j);
+    const i32x4 kf1 = *(const i32x4*)(buf + ((4 + c.j) * 64 + 16 * kb + c.l16) * 16);
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      const i32x4 q1 = *(const i32x4*)(qrow + 16 * K8_LD * qb + 64);
-      S2[qb][kb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(kf1, q1, S2[qb][kb], 0, 0, 0);
-    }
+    for (int qb = 0; qb < 2; ++qb)
+      S2[qb][kb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(kf1, qi[qb][1], S2[qb][kb], 0, 0, 0);
   }
 }
 
-// Online softmax of one quantized tile's scores: P = E4M3(448 p) codes of the lane's keys as
-// the B operand of the P.V MFMA (pk), after the row state's max update (and rescale of acc
-// when the max moved).  c2 = s_Q s_K alpha log2(e) (wave-uniform).  Below C2_FAST_MIN a masked
-// score is not guaranteed to underflow exp2, so the masked entries are zeroed explicitly.
+// Online softmax of one quantized tile's scores: the row-state max update (rescaling the
+// accumulators when a max moved), P = E4M3(448 p) codes, their row sums (MFMA against a row
+// of ones) and the codes regrouped into the B operand of the 32x32x64 P.V MFMA (pk).
+// c2 = s_Q s_K alpha log2(e) (wave-uniform).  Below C2_FAST_MIN a masked score is not
+// guaranteed to underflow exp2, so the masked entries are zeroed explicitly.
 template <bool TINY>
-__device__ inline void softmax_tile_q(const i32x4 (&S2)[2][4], float c2, RowState& st, i64 (&pk)[2][2]) {
-  // 1. tile maxima and the row-state update of both 16-query blocks
-  float muse[2], resc[2];
-  bool moved = false;
+__device__ inline void softmax_tile_q(const Ctx& c, const i32x4 (&S2)[2][4], float c2, RowState& st, i32x8& pk) {
+  bool valid[2];
+  float tmax[2], muse[2];
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     int mi = NEG_DOT;
@@ -380,18 +397,13 @@ __device__ inline void softmax_tile_q(const i32x4 (&S2)[2][4], float c2, RowStat
     for (int kb = 0; kb < 4; ++kb)
       mi = max(mi, max(max(S2[qb][kb][0], S2[qb][kb][1]), max(S2[qb][kb][2], S2[qb][kb][3])));
     mi = wave_max_i(mi);
-    const bool valid = mi > NEG_DOT / 2;
-    const float mold = st.m[qb];
-    const float mnew = valid ? fmaxf(mold, (float)mi * c2) : mold;
-    resc[qb] = (mnew == mold) ? 1.0f : __builtin_amdgcn_exp2f(mold - mnew);
-    moved |= resc[qb] != 1.0f;
-    st.m[qb] = mnew;
-    muse[qb] = valid ? mnew - LOG2_448 : INFINITY;
+    valid[qb] = mi > NEG_DOT / 2;
+    tmax[qb] = (float)mi * c2;
   }
-  // 2. P codes of both blocks in one straight-line block (the exp2 chains interleave)
+  row_update(c, st, valid, tmax, LOG2_448, muse);
+  uint32_t pw[2][4];
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
-    uint32_t pw[4];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
       float pv[4];
@@ -401,33 +413,7 @@ __device__ inline void softmax_tile_q(const i32x4 (&S2)[2][4], float c2, RowStat
         if (TINY && S2[qb][kb][r] <= NEG_DOT / 2) pv[r] = 0.0f;
       }
       const uint32_t w = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(pv[0], pv[1], 0, false);
-      pw[kb] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(pv[2], pv[3], (int)w, true);
-    }
-    pk[qb][0] = (i64)pw[0] | ((i64)pw[1] << 32);
-    pk[qb][1] = (i64)pw[2] | ((i64)pw[3] << 32);
-  }
-  // 3. rescale the accumulators when some row's max moved (rare after the first tiles)
-  if (__builtin_amdgcn_ballot_w64(moved)) {
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-#pragma unroll
-      for (int cb = 0; cb < 8; ++cb) st.acc[qb][cb] *= resc[qb];
-      st.lacc[qb] *= resc[qb];
-    }
-  }
-}
-
-// P.V of one quantized tile against its E4M3 V codes (buffer buf), plus the row sum of the
-// rounded P from an MFMA against a row of ones.
-__device__ inline void pv_tile_q(const Ctx& c, const uint8_t* buf, const i64 (&pk)[2][2], RowState& st) {
-#pragma unroll
-  for (int cb = 0; cb < 8; ++cb) {
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const i64 vf = *(const i64*)(buf + LDS_QV + ((ks * 4 + c.j) * D + 16 * cb + c.l16) * 8);
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
-        st.acc[qb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(vf, pk[qb][ks], st.acc[qb][cb], 0, 0, 0);
+      pw[qb][kb] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(pv[2], pv[3], (int)w, true);
     }
   }
   const i64 ONES8 = 0x3838383838383838L;  // E4M3 1.0
@@ -435,7 +421,28 @@ __device__ inline void pv_tile_q(const Ctx& c, const uint8_t* buf, const i64 (&p
   for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
-      st.lacc[qb] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(ONES8, pk[qb][ks], st.lacc[qb], 0, 0, 0);
+      st.lacc[qb] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(
+          ONES8, (i64)pw[qb][2 * ks] | ((i64)pw[qb][2 * ks + 1] << 32), st.lacc[qb], 0, 0, 0);
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    uint32_t lo, hi;
+    regroup(pw[0][kb], pw[1][kb], lo, hi);
+    pk[2 * kb] = (int)lo;
+    pk[2 * kb + 1] = (int)hi;
+  }
+}
+
+// P.V of one quantized tile: 32x32x64 E4M3 MFMA per 32-channel block.  The A operand of lane
+// (channel 32 cb + l32, half hh) is the 32 bytes of that channel and half in the tile's two
+// 32-key blocks, in the byte order of pk.
+__device__ inline void pv_tile_q(const Ctx& c, const uint8_t* buf, const i32x8& pk, RowState& st) {
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb) {
+    const u32x4 a0 = *(const u32x4*)(buf + LDS_QV + ((0 + c.hh) * D + 32 * cb + c.l32) * 16);
+    const u32x4 a1 = *(const u32x4*)(buf + LDS_QV + ((2 + c.hh) * D + 32 * cb + c.l32) * 16);
+    const i32x8 a = {(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3], (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+    st.acc[cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pk, st.acc[cb], 0, 0, 0, 127, 0, 127);
+  }
 }
 
 // One bf16 tile (anchors: ANCHOR = true, keys from the LDS list; window: 64 aligned keys
@@ -449,20 +456,19 @@ __device__ inline void compute_tile_bf(const PrefillParams& p, const Ctx& c, con
 #pragma unroll
     for (int r = 0; r < 4; ++r)
       keyv[kb][r] = ANCHOR ? anc_s[16 * kb + 4 * c.j + r] : kt0 + 16 * kb + 4 * c.j + r;
-  bf16x8 pb[2][2];
+  f32x4 S[2][4];
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     const int row = c.r0w + 16 * qb + c.l16;
     const int rowc = row < c.N ? row : c.N - 1;  // padded rows: any finite query, never stored
     const uint16_t* qrow = p.q + ((size_t)c.h * c.N + rowc) * D + 8 * c.j;
-    f32x4 S[4];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int key = keyv[kb][r];
         const bool ok = ANCHOR ? (key >= 0 && key <= row - WIN) : (key <= row && key >= row - WIN + 1);
-        S[kb][r] = ok ? 0.0f : -INFINITY;
+        S[qb][kb][r] = ok ? 0.0f : -INFINITY;
       }
     }
 #pragma unroll
@@ -471,39 +477,33 @@ __device__ inline void compute_tile_bf(const PrefillParams& p, const Ctx& c, con
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
         const bf16x8 kfr = *(const bf16x8*)(lds + (16 * kb + c.l16) * KB_LD + 2 * (32 * ks + 8 * c.j));
-        S[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kfr, qfr, S[kb], 0, 0, 0);
+        S[qb][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kfr, qfr, S[qb][kb], 0, 0, 0);
       }
-    }
-    float mt = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) mt = fmaxf(mt, fmaxf(fmaxf(S[kb][0], S[kb][1]), fmaxf(S[kb][2], S[kb][3])));
-    mt = wave_max_f16(mt);
-    const bool valid = mt > -INFINITY;
-    const float muse = os_update(st, qb, valid, mt * AL2, 0.0f);
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      uint32_t w[4];
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const f32x4 sv = S[2 * ks + hh];
-        float pv[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) pv[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[r], AL2, -muse));
-        w[2 * hh] = pack_bf16x2(pv[0], pv[1]);
-        w[2 * hh + 1] = pack_bf16x2(pv[2], pv[3]);
-      }
-      const u32x4 wv = {w[0], w[1], w[2], w[3]};
-      pb[qb][ks] = __builtin_bit_cast(bf16x8, wv);
     }
   }
+  bool valid[2];
+  float tmax[2], muse[2];
 #pragma unroll
-  for (int cb = 0; cb < 8; ++cb) {
+  for (int qb = 0; qb < 2; ++qb) {
+    float mt = -INFINITY;
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const bf16x8 vf = *(const bf16x8*)(lds + LDS_V + ((ks * 4 + c.j) * D + 16 * cb + c.l16) * 16);
+    for (int kb = 0; kb < 4; ++kb)
+      mt = fmaxf(mt, fmaxf(fmaxf(S[qb][kb][0], S[qb][kb][1]), fmaxf(S[qb][kb][2], S[qb][kb][3])));
+    mt = wave_max_f16(mt);
+    valid[qb] = mt > -INFINITY;
+    tmax[qb] = mt * AL2;
+  }
+  row_update(c, st, valid, tmax, 0.0f, muse);
+  uint32_t w[2][4][2];  // bf16 pairs (r 0-1, r 2-3) of keys 16 kb + 4 j + r
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
-        st.acc[qb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb[qb][ks], st.acc[qb][cb], 0, 0, 0);
+  for (int qb = 0; qb < 2; ++qb) {
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      float pv[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) pv[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[qb][kb][r], AL2, -muse[qb]));
+      w[qb][kb][0] = pack_bf16x2(pv[0], pv[1]);
+      w[qb][kb][1] = pack_bf16x2(pv[2], pv[3]);
     }
   }
   const bf16x8 ONESB = {(__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f,
@@ -511,8 +511,22 @@ __device__ inline void compute_tile_bf(const PrefillParams& p, const Ctx& c, con
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-      st.lacc[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ONESB, pb[qb][ks], st.lacc[qb], 0, 0, 0);
+    for (int ks = 0; ks < 2; ++ks) {
+      const u32x4 b = {w[qb][2 * ks][0], w[qb][2 * ks][1], w[qb][2 * ks + 1][0], w[qb][2 * ks + 1][1]};
+      st.lacc[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ONESB, __builtin_bit_cast(bf16x8, b), st.lacc[qb], 0, 0, 0);
+    }
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    uint32_t x0, y0, x1, y1;
+    regroup(w[0][kb][0], w[1][kb][0], x0, y0);
+    regroup(w[0][kb][1], w[1][kb][1], x1, y1);
+    const bf16x8 pb = __builtin_bit_cast(bf16x8, (u32x4){x0, x1, y0, y1});  // keys 16 kb + 8 hh + (0..7)
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) {
+      const bf16x8 vf = *(const bf16x8*)(lds + LDS_V + ((2 * kb + c.hh) * D + 32 * cb + c.l32) * 16);
+      st.acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb, st.acc[cb], 0, 0, 0);
+    }
+  }
 }
 
 // Segment A (quantized tiles 0 .. nA-1) for one workgroup.
@@ -528,7 +542,6 @@ __device__ inline void compute_tile_bf(const PrefillParams& p, const Ctx& c, con
 // waits for P.V(t), as the order of Alg. 2 requires.  Tiles past the wave's last row
 // (64 t > r0w + 31 - 128) are loaded for the other waves but not computed.
 struct TileMeta {
-  uint32_t w0, w1;
   float sk;
 };
 
@@ -540,53 +553,53 @@ __device__ inline float tile_c2(float sq_u, float sk) {
 }
 
 template <bool TINY>
-__device__ inline void segment_a_step(const PrefillParams& p, const Ctx& c, uint8_t* lds, int nA, int nAw,
-                                      float sq_u, int t, TileQRegs& pre, TileMeta& m1, TileMeta& m2,
-                                      i32x4 (&S2)[2][4], const i64 (&pk)[2][2], i64 (&pkn)[2][2],
+__device__ inline void segment_a_step(const PrefillParams& p, const Ctx& c, uint8_t* lds, const i32x4 (&qi)[2][2],
+                                      int nA, int nAw, float sq_u, int t, TileQRegs& pre, TileMeta& m1,
+                                      TileMeta& m2, i32x4 (&S2)[2][4], const i32x8& pk, i32x8& pkn,
                                       RowState& st) {
   if (t + 2 < nA) {  // tile t+2 -> buffer (t+2) % 3
     store_tile_q(c, lds + ((t + 2) % 3) * LDS_QBUF, pre);
-    m2 = TileMeta{pre.w0, pre.w1, pre.sk};
+    m2 = TileMeta{pre.sk};
   }
   if (t + 3 < nA) fetch_tile_q(p, c, t + 3, pre);  // in flight during this tile's compute
   if (t < nAw) pv_tile_q(c, lds + (t % 3) * LDS_QBUF, pk, st);
-  if (t + 1 < nAw) softmax_tile_q<TINY>(S2, tile_c2<TINY>(sq_u, m1.sk), st, pkn);
+  if (t + 1 < nAw) softmax_tile_q<TINY>(c, S2, tile_c2<TINY>(sq_u, m1.sk), st, pkn);
   __syncthreads();
-  if (t + 2 < nAw) qk_tile_q(c, lds + ((t + 2) % 3) * LDS_QBUF, lds + LDS_Q8, t + 2, S2);
+  if (t + 2 < nAw) qk_tile_q(c, lds + ((t + 2) % 3) * LDS_QBUF, qi, t + 2, S2);
   m1 = m2;
 }
 
 template <bool TINY>
-__device__ inline void segment_a(const PrefillParams& p, const Ctx& c, uint8_t* lds, int nA, float sq_u,
-                                 RowState& st) {
+__device__ inline void segment_a(const PrefillParams& p, const Ctx& c, uint8_t* lds, const i32x4 (&qi)[2][2],
+                                 int nA, float sq_u, RowState& st) {
   const int nAw = c.r0w + 31 - WIN >= 0 ? ((c.r0w + 31 - WIN) >> 6) + 1 : 0;
   if (nA <= 0) return;
   TileQRegs pre;
-  TileMeta m0{0u, 0u, 0.0f}, m1{0u, 0u, 0.0f}, m2{0u, 0u, 0.0f};
+  TileMeta m0{0.0f}, m1{0.0f}, m2{0.0f};
   fetch_tile_q(p, c, 0, pre);
   __syncthreads();  // nothing else uses the tile buffers now
   store_tile_q(c, lds, pre);
-  m0 = TileMeta{pre.w0, pre.w1, pre.sk};
+  m0 = TileMeta{pre.sk};
   if (nA > 1) {
     fetch_tile_q(p, c, 1, pre);
     store_tile_q(c, lds + LDS_QBUF, pre);
-    m1 = TileMeta{pre.w0, pre.w1, pre.sk};
+    m1 = TileMeta{pre.sk};
   }
   if (nA > 2) fetch_tile_q(p, c, 2, pre);
   __syncthreads();
   // prologue: scores and P codes of tile 0, scores of tile 1
   i32x4 S2[2][4];
-  i64 pa[2][2], pb[2][2];
+  i32x8 pa, pb;
   if (nAw > 0) {
-    qk_tile_q(c, lds, lds + LDS_Q8, 0, S2);
-    softmax_tile_q<TINY>(S2, tile_c2<TINY>(sq_u, m0.sk), st, pa);
+    qk_tile_q(c, lds, qi, 0, S2);
+    softmax_tile_q<TINY>(c, S2, tile_c2<TINY>(sq_u, m0.sk), st, pa);
   }
-  if (1 < nAw) qk_tile_q(c, lds + LDS_QBUF, lds + LDS_Q8, 1, S2);
+  if (1 < nAw) qk_tile_q(c, lds + LDS_QBUF, qi, 1, S2);
   // unrolled by two so the P-code registers alternate instead of being copied
   for (int t = 0; t < nA; t += 2) {
-    segment_a_step<TINY>(p, c, lds, nA, nAw, sq_u, t, pre, m1, m2, S2, pa, pb, st);
+    segment_a_step<TINY>(p, c, lds, qi, nA, nAw, sq_u, t, pre, m1, m2, S2, pa, pb, st);
     if (t + 1 >= nA) break;
-    segment_a_step<TINY>(p, c, lds, nA, nAw, sq_u, t + 1, pre, m1, m2, S2, pb, pa, st);
+    segment_a_step<TINY>(p, c, lds, qi, nA, nAw, sq_u, t + 1, pre, m1, m2, S2, pb, pa, st);
   }
 }
 
@@ -620,6 +633,9 @@ __global__ void __launch_bounds__(256, 2) pf_attn_kernel(PrefillParams p) {
   c.wave = wave;
   c.l16 = lane & 15;
   c.j = lane >> 4;
+  c.l32 = lane & 31;
+  c.hh = lane >> 5;
+  c.qsel = (lane >> 4) & 1;
   c.r0w = __builtin_amdgcn_readfirstlane(r0 + 32 * wave);  // wave-uniform: scalar branches
   c.N = p.N;
   c.Npad = p.Npad;
@@ -682,7 +698,6 @@ __global__ void __launch_bounds__(256, 2) pf_attn_kernel(PrefillParams p) {
         }
         const int row = c.r0w + 16 * qb + c.l16;
         *(i32x4*)(p.q8 + ((size_t)c.h * c.Npad + row) * D + 64 * s8 + 16 * c.j) = qi[qb][s8];
-        *(i32x4*)(lds + LDS_Q8 + (32 * wave + 16 * qb + c.l16) * K8_LD + 64 * s8 + 16 * c.j) = qi[qb][s8];
       }
     }
     if (lane == 0 && (wave & 1) == 0) p.sq[(size_t)c.h * c.nb64 + (c.r0w >> 6)] = sq;
@@ -693,9 +708,9 @@ __global__ void __launch_bounds__(256, 2) pf_attn_kernel(PrefillParams p) {
   for (int qb = 0; qb < 2; ++qb) {
     st.m[qb] = -INFINITY;
     st.lacc[qb] = (f32x4){0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int cb = 0; cb < 8; ++cb) st.acc[qb][cb] = (f32x4){0.f, 0.f, 0.f, 0.f};
   }
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb) st.acc[cb] = (f32x16){};
 
   // ---- segment A: quantized tiles
   const int lastA = r0 + WG_ROWS - 1 - WIN;
@@ -712,16 +727,19 @@ __global__ void __launch_bounds__(256, 2) pf_attn_kernel(PrefillParams p) {
     m = fminf(fminf(skmin[0], skmin[1]), fminf(skmin[2], skmin[3]));
     const float sq_u = uniform_f(sq);
     if (sq_u * m * AL2 >= C2_FAST_MIN)
-      segment_a<false>(p, c, lds, nA, sq_u, st);
+      segment_a<false>(p, c, lds, qi, nA, sq_u, st);
     else
-      segment_a<true>(p, c, lds, nA, sq_u, st);
+      segment_a<true>(p, c, lds, qi, nA, sq_u, st);
   }
   // acc holds sum E4M3(448 p) * code(V): scale to values
 #pragma unroll
-  for (int cb = 0; cb < 8; ++cb) {
-    const f32x4 svc = *(const f32x4*)(p.sv + c.hk * D + 16 * cb + 4 * c.j) * (1.0f / 448.0f);
+  for (int cb = 0; cb < 4; ++cb) {
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) st.acc[qb][cb] *= svc;
+    for (int i = 0; i < 4; ++i) {
+      const f32x4 svc = *(const f32x4*)(p.sv + c.hk * D + 32 * cb + 8 * i + 4 * c.hh) * (1.0f / 448.0f);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) st.acc[cb][4 * i + r] *= svc[r];
+    }
   }
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) st.lacc[qb] *= (1.0f / 448.0f);
@@ -755,14 +773,16 @@ __global__ void __launch_bounds__(256, 2) pf_attn_kernel(PrefillParams p) {
   }
 
   // ---- epilogue: o = acc / l  (every real row has its own key in the window)
+  const int orow = c.r0w + c.l32;
+  if (orow < c.N) {
+    const float inv = 1.0f / (c.qsel ? st.lacc[1][0] : st.lacc[0][0]);
+    float* dst = p.o + ((size_t)c.h * c.N + orow) * D + 4 * c.hh;
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const int row = c.r0w + 16 * qb + c.l16;
-    if (row >= c.N) continue;
-    const float inv = 1.0f / st.lacc[qb][0];
-    float* dst = p.o + ((size_t)c.h * c.N + row) * D + 4 * c.j;
+    for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
-    for (int cb = 0; cb < 8; ++cb) *(f32x4*)(dst + 16 * cb) = st.acc[qb][cb] * inv;
+      for (int i = 0; i < 4; ++i)
+        *(f32x4*)(dst + 32 * cb + 8 * i) = (f32x4){st.acc[cb][4 * i], st.acc[cb][4 * i + 1], st.acc[cb][4 * i + 2],
+                                                   st.acc[cb][4 * i + 3]} * inv;
   }
 }
 

@@ -217,17 +217,19 @@ int hyq_decode_attn(const hyq_cache_t* cache, const void* q, float* o, int32_t n
    each section starting at a multiple of 256 bytes (Np = len rounded up to 128):
      q8   int8 [Hq][Np][128]        Q codes, operand order (below), rows >= len zero
      sq   f32  [Hq][Np/64]          s_Q per 64-query block
-     k8   int8 [Hkv][Np][128]       K codes, operand order
+     k8   int8 [Hkv][Np/64][8][64][16] K codes: 16-byte chunk k of the operand-order row
+                                    of key 64 T + r at (tile T, k, r)
      sk   f32  [Hkv][Np/64]         s_K per 64-key block
-     v8   u8   [Hkv][Np/32][4][128][8] V codes: byte e of (32-key block b, j, channel c)
-                                    is key 32 b + 16 (e >> 2) + 4 j + (e & 3)
+     v8   u8   [Hkv][Np/32][2][128][16] V codes: byte e of (32-key block b, half h,
+                                    channel c) is key 32 b + 16 (e >> 3) + 8 h + (e & 7)
      sv   f32  [Hkv][128]           s_V
      vmax f32  [Hkv][Np/64][128]    per-block max |V| over non-anchor keys
      abits u32 [Hkv][Np/32]         anchor bitmap (bit j & 31 of word j >> 5)
-     vt16 bf16 [Hkv][Np/32][4][128][8] V (all keys, rows >= len zero) in the layout of v8
+     vt16 bf16 [Hkv][Np/8][128][8]  V (all keys, rows >= len zero): element e of (group g,
+                                    channel c) is key 8 g + e
      ka16 bf16 [Hkv][Ap][128]       K rows of the anchors in list order (Ap = n_anchor
                                     rounded up to 64; the section is sized for anchor_cap)
-     va16 bf16 [Hkv][Ap/32][4][128][8] V of the anchors in list order, layout of v8
+     va16 bf16 [Hkv][Ap/8][128][8]  V of the anchors in list order, layout of vt16
    Operand order of an INT8 row: byte 64 s + 16 j + 8 t + e holds channel
    32 (2 s + t) + 8 j + e (s, t in {0,1}, j < 4, e < 8).
    Calls sharing one workspace must not overlap in time (same stream is fine).

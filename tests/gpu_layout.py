@@ -137,13 +137,16 @@ def read_prefill_ws(ws: np.ndarray, Hq: int, Hkv: int, N: int, anchor_cap: int) 
 
     perm = _int8_natural_index()
     q8 = sec("q8", np.int8, Hq * Np * D).reshape(Hq, Np, D)[:, :, perm]
-    k8 = sec("k8", np.int8, Hkv * Np * D).reshape(Hkv, Np, D)[:, :, perm]
-    raw = sec("v8", np.uint8, Hkv * Np * D).reshape(Hkv, Np // 32, 4, D, 8)
+    # K codes: per 64-key tile, [16-byte chunk 8][key 64][16] of the operand-order rows
+    kraw = sec("k8", np.int8, Hkv * Np * D).reshape(Hkv, Np // 64, 8, 64, 16)
+    k8 = kraw.transpose(0, 1, 3, 2, 4).reshape(Hkv, Np, D)[:, :, perm]
+    # V codes: per 32-key block, [half h][channel][16]; byte b is key 16 (b >> 3) + 8 h + (b & 7)
+    raw = sec("v8", np.uint8, Hkv * Np * D).reshape(Hkv, Np // 32, 2, D, 16)
     v8 = np.empty((Hkv, Np, D), np.uint8)
-    for j in range(4):
-        for e in range(8):
-            kk = 16 * (e >> 2) + 4 * j + (e & 3)
-            v8[:, kk::32, :] = raw[:, :, j, :, e]
+    for h in range(2):
+        for b in range(16):
+            kk = 16 * (b >> 3) + 8 * h + (b & 7)
+            v8[:, kk::32, :] = raw[:, :, h, :, b]
     return dict(Np=Np, q8=q8, k8=k8, v8=v8,
                 sq=sec("sq", np.float32, Hq * (Np // 64)).reshape(Hq, Np // 64),
                 sk=sec("sk", np.float32, Hkv * (Np // 64)).reshape(Hkv, Np // 64),
