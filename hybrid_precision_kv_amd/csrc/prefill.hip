@@ -44,8 +44,10 @@ constexpr int LDS_BF = LDS_V + 16384;
 // codes as [16-byte chunk 8][key 64][16], the V codes at + LDS_QV as stored in the workspace,
 // and the per-key mask at + LDS_QBIAS.
 constexpr int LDS_QV = 8192;
-constexpr int LDS_QBIAS = LDS_QV + 8192;  // per-key MFMA C input: 0, or NEG_DOT for an anchor
-constexpr int LDS_QBUF = LDS_QBIAS + 256;
+// per-key MFMA C input (0, or NEG_DOT for an anchor), one copy per 16-query block so that
+// each accumulator is loaded directly
+constexpr int LDS_QBIAS = LDS_QV + 8192;
+constexpr int LDS_QBUF = LDS_QBIAS + 512;
 constexpr int LDS_TOTAL = 3 * LDS_QBUF > LDS_BF ? 3 * LDS_QBUF : LDS_BF;
 
 typedef long i64;
@@ -253,7 +255,7 @@ struct RowState {
   float m[2];        // running max, log2 units, of query l16 in each 16-query block
   f32x16 acc[4];     // O^T, 32x32 MFMA layout: element 4 i + r is channel 32 cb + 8 i + 4 hh + r
                      // of query l32
-  f32x4 lacc[2];     // row sums of query l16 in each 16-query block (all 4 entries equal)
+  f32x4 lacc;        // row sum of query l16 of 16-query block hh (all 4 entries equal)
 };
 
 __device__ inline uint32_t pack_bf16x2(float a, float b) {
@@ -262,6 +264,8 @@ __device__ inline uint32_t pack_bf16x2(float a, float b) {
 
 struct Ctx {
   int h, hk, r0w, N, Npad, nb64, tid, wave, l16, j, l32, hh, qsel;
+  i64 sel8;       // E4M3 row-sum selector: ones on the block-0 bytes for rows 0-7, block-1 bytes for 8-15
+  bf16x8 selb;    // the same for bf16 pairs
 };
 
 // Max update of both 16-query blocks of the wave from their tile maxima (log2 units, valid =
@@ -284,18 +288,8 @@ __device__ inline void row_update(const Ctx& c, RowState& st, const bool (&valid
     const float rs = c.qsel ? resc[1] : resc[0];  // the accumulator row of this lane
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) st.acc[cb] *= rs;
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) st.lacc[qb] *= resc[qb];
+    st.lacc *= c.hh ? resc[1] : resc[0];
   }
-}
-
-// P codes (or bf16 pairs) of the two 16-query blocks, x from block 0 and y from block 1, for
-// the same keys of one lane: after the swap a lane of the 32x32 layout (query l32, half hh)
-// holds x = keys 16 kb + 8 hh + r and y = keys 16 kb + 8 hh + 4 + r of its own query.
-__device__ inline void regroup(uint32_t x, uint32_t y, uint32_t& lo, uint32_t& hi) {
-  const auto s = __builtin_amdgcn_permlane16_swap(x, y, false, false);
-  lo = s[0];
-  hi = s[1];
 }
 
 // Quantized tile t: INT8 K codes of keys [64 t, 64 t + 64) ([chunk][key][16] as stored), the
@@ -312,10 +306,12 @@ __device__ inline void fetch_tile_q(const PrefillParams& p, const Ctx& c, int t,
   r.w1 = ab[1];
   r.sk = p.sk[(size_t)c.hk * c.nb64 + t];
   const size_t tile = ((size_t)c.hk * c.nb64 + t) * 8192;
+  const int8_t* kt = p.k8 + tile;
+  const uint8_t* vt = p.v8 + tile;
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    r.k[i] = *(const u32x4*)(p.k8 + tile + 16 * (c.tid + 256 * i));
-    r.v[i] = *(const u32x4*)(p.v8 + tile + 16 * (c.tid + 256 * i));
+    r.k[i] = *(const u32x4*)(kt + 16 * (c.tid + 256 * i));
+    r.v[i] = *(const u32x4*)(vt + 16 * (c.tid + 256 * i));
   }
 }
 __device__ inline void store_tile_q(const Ctx& c, uint8_t* lds, const TileQRegs& r) {
@@ -325,9 +321,10 @@ __device__ inline void store_tile_q(const Ctx& c, uint8_t* lds, const TileQRegs&
     *(u32x4*)(lds + 16 * ch) = r.k[i];
     *(u32x4*)(lds + LDS_QV + 16 * ch) = r.v[i];
   }
-  if (c.tid < 64) {  // anchor mask of key tid, built once per tile for every wave
-    const uint32_t word = c.tid < 32 ? r.w0 : r.w1;
-    *(int*)(lds + LDS_QBIAS + 4 * c.tid) = ((word >> (c.tid & 31)) & 1u) ? NEG_DOT : 0;
+  if (c.tid < 128) {  // anchor mask of key tid % 64, built once per tile for every wave
+    const int key = c.tid & 63;
+    const uint32_t word = key < 32 ? r.w0 : r.w1;
+    *(int*)(lds + LDS_QBIAS + 4 * c.tid) = ((word >> (key & 31)) & 1u) ? NEG_DOT : 0;
   }
 }
 
@@ -349,21 +346,20 @@ __device__ inline void load_tile_bf(const Ctx& c, uint8_t* lds, const uint16_t* 
 
 // Scores of one quantized tile for the wave's 32 queries: S^T = K . Q^T on INT8 codes (Q codes
 // in registers: qi[qb][s] = bytes 64 s + 16 j of query row 16 qb + l16), with the masked keys
-// (anchors; j > i - 128 on an edge tile) pushed to NEG_DOT through the MFMA's C input.  Two
-// passes over the 64 channels of each k-step so the 8 independent (qb, kb) chains interleave
-// in the MFMA pipe.
+// (anchors; on an EDGE tile also j > i - 128) pushed to NEG_DOT through the MFMA's C input.
+// Two passes over the 64 channels of each k-step so the 8 independent (qb, kb) chains
+// interleave in the MFMA pipe.
+template <bool EDGE>
 __device__ inline void qk_tile_q(const Ctx& c, const uint8_t* buf, const i32x4 (&qi)[2][2], int t,
                                  i32x4 (&S2)[2][4]) {
   const int kt0 = 64 * t;
-  const bool interior = kt0 + 63 <= c.r0w - WIN;
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb) {
-    const i32x4 bias = *(const i32x4*)(buf + LDS_QBIAS + 4 * (16 * kb + 4 * c.j));  // keys 16kb+4j+r
     const i32x4 kf0 = *(const i32x4*)(buf + (c.j * 64 + 16 * kb + c.l16) * 16);
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-      i32x4 acc = bias;
-      if (!interior) {
+      i32x4 acc = *(const i32x4*)(buf + LDS_QBIAS + 256 * qb + 4 * (16 * kb + 4 * c.j));  // keys 16kb+4j+r
+      if (EDGE) {
         const int row = c.r0w + 16 * qb + c.l16;
 #pragma unroll
         for (int r = 0; r < 4; ++r)
@@ -379,6 +375,13 @@ __device__ inline void qk_tile_q(const Ctx& c, const uint8_t* buf, const i32x4 (
     for (int qb = 0; qb < 2; ++qb)
       S2[qb][kb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(kf1, qi[qb][1], S2[qb][kb], 0, 0, 0);
   }
+}
+__device__ inline void qk_tile(const Ctx& c, const uint8_t* buf, const i32x4 (&qi)[2][2], int t,
+                               i32x4 (&S2)[2][4]) {
+  if (64 * t + 63 <= c.r0w - WIN)  // every key of the tile is at least 128 before every row
+    qk_tile_q<false>(c, buf, qi, t, S2);
+  else
+    qk_tile_q<true>(c, buf, qi, t, S2);
 }
 
 // Online softmax of one quantized tile's scores: the row-state max update (rescaling the
@@ -401,35 +404,34 @@ __device__ inline void softmax_tile_q(const Ctx& c, const i32x4 (&S2)[2][4], flo
     tmax[qb] = (float)mi * c2;
   }
   row_update(c, st, valid, tmax, LOG2_448, muse);
-  uint32_t pw[2][4];
+  // w[2 kb + qb]: codes of block qb, keys 16 kb + 4 j + r -- the row-sum B operand as is, and
+  // after the in-place swaps of each pair the P.V B operand
+  i32x8 w;
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
+  for (int kb = 0; kb < 4; ++kb) {
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
+    for (int qb = 0; qb < 2; ++qb) {
       float pv[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         pv[r] = __builtin_amdgcn_exp2f(__builtin_fmaf((float)S2[qb][kb][r], c2, -muse[qb]));
         if (TINY && S2[qb][kb][r] <= NEG_DOT / 2) pv[r] = 0.0f;
       }
-      const uint32_t w = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(pv[0], pv[1], 0, false);
-      pw[qb][kb] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(pv[2], pv[3], (int)w, true);
+      const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(pv[0], pv[1], 0, false);
+      w[2 * kb + qb] = __builtin_amdgcn_cvt_pk_fp8_f32(pv[2], pv[3], lo, true);
     }
   }
-  const i64 ONES8 = 0x3838383838383838L;  // E4M3 1.0
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-      st.lacc[qb] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(
-          ONES8, (i64)pw[qb][2 * ks] | ((i64)pw[qb][2 * ks + 1] << 32), st.lacc[qb], 0, 0, 0);
+  for (int kb = 0; kb < 4; ++kb)
+    st.lacc = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(
+        c.sel8, (i64)(uint32_t)w[2 * kb] | ((i64)(uint32_t)w[2 * kb + 1] << 32), st.lacc, 0, 0, 0);
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb) {
-    uint32_t lo, hi;
-    regroup(pw[0][kb], pw[1][kb], lo, hi);
-    pk[2 * kb] = (int)lo;
-    pk[2 * kb + 1] = (int)hi;
+    const auto sw = __builtin_amdgcn_permlane16_swap((uint32_t)w[2 * kb], (uint32_t)w[2 * kb + 1], false, false);
+    w[2 * kb] = (int)sw[0];
+    w[2 * kb + 1] = (int)sw[1];
   }
+  pk = w;
 }
 
 // P.V of one quantized tile: 32x32x64 E4M3 MFMA per 32-channel block.  The A operand of lane
@@ -494,33 +496,23 @@ __device__ inline void compute_tile_bf(const PrefillParams& p, const Ctx& c, con
     tmax[qb] = mt * AL2;
   }
   row_update(c, st, valid, tmax, 0.0f, muse);
-  uint32_t w[2][4][2];  // bf16 pairs (r 0-1, r 2-3) of keys 16 kb + 4 j + r
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
+  for (int kb = 0; kb < 4; ++kb) {
+    // bf16 pairs (r 0-1, r 2-3) of keys 16 kb + 4 j + r, block 0 then block 1: the row-sum B
+    // operand; the two in-place swaps turn it into the P.V B operand (keys 16 kb + 8 hh + e)
+    u32x4 b;
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
+    for (int qb = 0; qb < 2; ++qb) {
       float pv[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) pv[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[qb][kb][r], AL2, -muse[qb]));
-      w[qb][kb][0] = pack_bf16x2(pv[0], pv[1]);
-      w[qb][kb][1] = pack_bf16x2(pv[2], pv[3]);
+      b[2 * qb] = pack_bf16x2(pv[0], pv[1]);
+      b[2 * qb + 1] = pack_bf16x2(pv[2], pv[3]);
     }
-  }
-  const bf16x8 ONESB = {(__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f,
-                        (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f};
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const u32x4 b = {w[qb][2 * ks][0], w[qb][2 * ks][1], w[qb][2 * ks + 1][0], w[qb][2 * ks + 1][1]};
-      st.lacc[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ONESB, __builtin_bit_cast(bf16x8, b), st.lacc[qb], 0, 0, 0);
-    }
-#pragma unroll
-  for (int kb = 0; kb < 4; ++kb) {
-    uint32_t x0, y0, x1, y1;
-    regroup(w[0][kb][0], w[1][kb][0], x0, y0);
-    regroup(w[0][kb][1], w[1][kb][1], x1, y1);
-    const bf16x8 pb = __builtin_bit_cast(bf16x8, (u32x4){x0, x1, y0, y1});  // keys 16 kb + 8 hh + (0..7)
+    st.lacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(c.selb, __builtin_bit_cast(bf16x8, b), st.lacc, 0, 0, 0);
+    const auto s0 = __builtin_amdgcn_permlane16_swap(b[0], b[2], false, false);
+    const auto s1 = __builtin_amdgcn_permlane16_swap(b[1], b[3], false, false);
+    const bf16x8 pb = __builtin_bit_cast(bf16x8, (u32x4){s0[0], s1[0], s0[1], s1[1]});
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) {
       const bf16x8 vf = *(const bf16x8*)(lds + LDS_V + ((2 * kb + c.hh) * D + 32 * cb + c.l32) * 16);
@@ -540,11 +532,9 @@ __device__ inline void compute_tile_bf(const PrefillParams& p, const Ctx& c, con
 //   QK^T(t+2) (MFMA).
 // The exact per-tile max update of softmax(t+1) may rescale the accumulator: that multiply
 // waits for P.V(t), as the order of Alg. 2 requires.  Tiles past the wave's last row
-// (64 t > r0w + 31 - 128) are loaded for the other waves but not computed.
-struct TileMeta {
-  float sk;
-};
-
+// (64 t > r0w + 31 - 128) are loaded for the other waves but not computed.  While all three
+// compute steps are due (t + 2 < the wave's tile count) the loop runs unrolled by three, so
+// the buffer offsets are constants and no step is conditional.
 template <bool TINY>
 __device__ inline float tile_c2(float sq_u, float sk) {
   float c2 = uniform_f(sq_u * sk * AL2);
@@ -552,21 +542,41 @@ __device__ inline float tile_c2(float sq_u, float sk) {
   return c2;
 }
 
-template <bool TINY>
-__device__ inline void segment_a_step(const PrefillParams& p, const Ctx& c, uint8_t* lds, const i32x4 (&qi)[2][2],
-                                      int nA, int nAw, float sq_u, int t, TileQRegs& pre, TileMeta& m1,
-                                      TileMeta& m2, i32x4 (&S2)[2][4], const i32x8& pk, i32x8& pkn,
-                                      RowState& st) {
-  if (t + 2 < nA) {  // tile t+2 -> buffer (t+2) % 3
-    store_tile_q(c, lds + ((t + 2) % 3) * LDS_QBUF, pre);
-    m2 = TileMeta{pre.sk};
-  }
-  if (t + 3 < nA) fetch_tile_q(p, c, t + 3, pre);  // in flight during this tile's compute
-  if (t < nAw) pv_tile_q(c, lds + (t % 3) * LDS_QBUF, pk, st);
-  if (t + 1 < nAw) softmax_tile_q<TINY>(c, S2, tile_c2<TINY>(sq_u, m1.sk), st, pkn);
+struct PipeA {
+  TileQRegs pre;     // tile in flight from global memory
+  float sk1, sk2;    // K scales of the tiles whose scores are held (t+1) and just stored (t+2)
+  i32x4 S2[2][4];    // scores of tile t+1
+  i32x8 pk;          // P codes of tile t
+};
+
+template <bool TINY, int PH>
+__device__ inline void segment_a_main(const PrefillParams& p, const Ctx& c, uint8_t* lds, const i32x4 (&qi)[2][2],
+                                      int nA, float sq_u, int t, PipeA& a, RowState& st) {
+  uint8_t* next = lds + ((PH + 2) % 3) * LDS_QBUF;
+  store_tile_q(c, next, a.pre);
+  a.sk2 = a.pre.sk;
+  fetch_tile_q(p, c, min(t + 3, nA - 1), a.pre);  // past the end: loaded, never stored
+  pv_tile_q(c, lds + PH * LDS_QBUF, a.pk, st);
+  softmax_tile_q<TINY>(c, a.S2, tile_c2<TINY>(sq_u, a.sk1), st, a.pk);
   __syncthreads();
-  if (t + 2 < nAw) qk_tile_q(c, lds + ((t + 2) % 3) * LDS_QBUF, qi, t + 2, S2);
-  m1 = m2;
+  qk_tile(c, next, qi, t + 2, a.S2);
+  a.sk1 = a.sk2;
+}
+
+template <bool TINY>
+__device__ inline void segment_a_tail(const PrefillParams& p, const Ctx& c, uint8_t* lds, const i32x4 (&qi)[2][2],
+                                      int nA, int nAw, float sq_u, int t, PipeA& a, RowState& st) {
+  uint8_t* next = lds + ((t + 2) % 3) * LDS_QBUF;
+  if (t + 2 < nA) {
+    store_tile_q(c, next, a.pre);
+    a.sk2 = a.pre.sk;
+  }
+  if (t + 3 < nA) fetch_tile_q(p, c, t + 3, a.pre);
+  if (t < nAw) pv_tile_q(c, lds + (t % 3) * LDS_QBUF, a.pk, st);
+  if (t + 1 < nAw) softmax_tile_q<TINY>(c, a.S2, tile_c2<TINY>(sq_u, a.sk1), st, a.pk);
+  __syncthreads();
+  if (t + 2 < nAw) qk_tile(c, next, qi, t + 2, a.S2);
+  a.sk1 = a.sk2;
 }
 
 template <bool TINY>
@@ -574,33 +584,33 @@ __device__ inline void segment_a(const PrefillParams& p, const Ctx& c, uint8_t* 
                                  int nA, float sq_u, RowState& st) {
   const int nAw = c.r0w + 31 - WIN >= 0 ? ((c.r0w + 31 - WIN) >> 6) + 1 : 0;
   if (nA <= 0) return;
-  TileQRegs pre;
-  TileMeta m0{0.0f}, m1{0.0f}, m2{0.0f};
-  fetch_tile_q(p, c, 0, pre);
+  PipeA a;
+  float sk0 = 0.0f;
+  a.sk1 = a.sk2 = 0.0f;
+  fetch_tile_q(p, c, 0, a.pre);
   __syncthreads();  // nothing else uses the tile buffers now
-  store_tile_q(c, lds, pre);
-  m0 = TileMeta{pre.sk};
+  store_tile_q(c, lds, a.pre);
+  sk0 = a.pre.sk;
   if (nA > 1) {
-    fetch_tile_q(p, c, 1, pre);
-    store_tile_q(c, lds + LDS_QBUF, pre);
-    m1 = TileMeta{pre.sk};
+    fetch_tile_q(p, c, 1, a.pre);
+    store_tile_q(c, lds + LDS_QBUF, a.pre);
+    a.sk1 = a.pre.sk;
   }
-  if (nA > 2) fetch_tile_q(p, c, 2, pre);
+  if (nA > 2) fetch_tile_q(p, c, 2, a.pre);
   __syncthreads();
   // prologue: scores and P codes of tile 0, scores of tile 1
-  i32x4 S2[2][4];
-  i32x8 pa, pb;
   if (nAw > 0) {
-    qk_tile_q(c, lds, qi, 0, S2);
-    softmax_tile_q<TINY>(c, S2, tile_c2<TINY>(sq_u, m0.sk), st, pa);
+    qk_tile(c, lds, qi, 0, a.S2);
+    softmax_tile_q<TINY>(c, a.S2, tile_c2<TINY>(sq_u, sk0), st, a.pk);
   }
-  if (1 < nAw) qk_tile_q(c, lds + LDS_QBUF, qi, 1, S2);
-  // unrolled by two so the P-code registers alternate instead of being copied
-  for (int t = 0; t < nA; t += 2) {
-    segment_a_step<TINY>(p, c, lds, qi, nA, nAw, sq_u, t, pre, m1, m2, S2, pa, pb, st);
-    if (t + 1 >= nA) break;
-    segment_a_step<TINY>(p, c, lds, qi, nA, nAw, sq_u, t + 1, pre, m1, m2, S2, pb, pa, st);
+  if (1 < nAw) qk_tile(c, lds + LDS_QBUF, qi, 1, a.S2);
+  int t = 0;
+  for (; t + 5 <= nAw; t += 3) {  // iterations t .. t+2 all have t + 2 < nAw
+    segment_a_main<TINY, 0>(p, c, lds, qi, nA, sq_u, t, a, st);
+    segment_a_main<TINY, 1>(p, c, lds, qi, nA, sq_u, t + 1, a, st);
+    segment_a_main<TINY, 2>(p, c, lds, qi, nA, sq_u, t + 2, a, st);
   }
+  for (; t < nA; ++t) segment_a_tail<TINY>(p, c, lds, qi, nA, nAw, sq_u, t, a, st);
 }
 
 __global__ void __launch_bounds__(256, 2) pf_attn_kernel(PrefillParams p) {
@@ -636,6 +646,13 @@ __global__ void __launch_bounds__(256, 2) pf_attn_kernel(PrefillParams p) {
   c.l32 = lane & 31;
   c.hh = lane >> 5;
   c.qsel = (lane >> 4) & 1;
+  {
+    const bool lo_rows = (lane & 15) < 8;  // row-sum selector A operand rows 0-7 vs 8-15
+    c.sel8 = lo_rows ? (i64)0x38383838L : (i64)0x3838383800000000L;
+    const __bf16 one = (__bf16)1.0f, zero = (__bf16)0.0f;
+    const __bf16 a = lo_rows ? one : zero, b = lo_rows ? zero : one;
+    c.selb = (bf16x8){a, a, a, a, b, b, b, b};
+  }
   c.r0w = __builtin_amdgcn_readfirstlane(r0 + 32 * wave);  // wave-uniform: scalar branches
   c.N = p.N;
   c.Npad = p.Npad;
@@ -705,10 +722,8 @@ __global__ void __launch_bounds__(256, 2) pf_attn_kernel(PrefillParams p) {
 
   RowState st;
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    st.m[qb] = -INFINITY;
-    st.lacc[qb] = (f32x4){0.f, 0.f, 0.f, 0.f};
-  }
+  for (int qb = 0; qb < 2; ++qb) st.m[qb] = -INFINITY;
+  st.lacc = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int cb = 0; cb < 4; ++cb) st.acc[cb] = (f32x16){};
 
@@ -741,8 +756,7 @@ __global__ void __launch_bounds__(256, 2) pf_attn_kernel(PrefillParams p) {
       for (int r = 0; r < 4; ++r) st.acc[cb][4 * i + r] *= svc[r];
     }
   }
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb) st.lacc[qb] *= (1.0f / 448.0f);
+  st.lacc *= (1.0f / 448.0f);
 
   // ---- segment B: anchor tiles (64 consecutive list entries each)
   const int32_t* anc_g = p.anchors + (size_t)c.hk * p.n_anchor;
@@ -775,7 +789,10 @@ __global__ void __launch_bounds__(256, 2) pf_attn_kernel(PrefillParams p) {
   // ---- epilogue: o = acc / l  (every real row has its own key in the window)
   const int orow = c.r0w + c.l32;
   if (orow < c.N) {
-    const float inv = 1.0f / (c.qsel ? st.lacc[1][0] : st.lacc[0][0]);
+    // row sum of query l32 = block qsel: this lane's when qsel == hh, else lane l ^ 32's
+    const auto ls = __builtin_amdgcn_permlane32_swap(__float_as_uint(st.lacc[0]), __float_as_uint(st.lacc[0]), false, false);
+    const float other = __uint_as_float(c.hh ? ls[0] : ls[1]);
+    const float inv = 1.0f / (c.qsel == c.hh ? st.lacc[0] : other);
     float* dst = p.o + ((size_t)c.h * c.N + orow) * D + 4 * c.hh;
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb)
