@@ -40,15 +40,14 @@ constexpr float C2_FAST_MIN = 1e-6f;  // below: masked INT8 scores are zeroed ex
 constexpr int KB_LD = 272;        // LDS row stride (bytes) of the bf16 K tile
 constexpr int LDS_V = 64 * KB_LD; // V tile offset (bf16 tiles)
 constexpr int LDS_BF = LDS_V + 16384;
-// Quantized tiles rotate through a ring of 3 buffers: buffer b at b * LDS_QBUF holds the K
+// Quantized tiles rotate through a ring of 4 buffers: buffer b at b * LDS_QBUF holds the K
 // codes as [16-byte chunk 8][key 64][16], the V codes at + LDS_QV as stored in the workspace,
 // and the per-key mask at + LDS_QBIAS.
 constexpr int LDS_QV = 8192;
-// per-key MFMA C input (0, or NEG_DOT for an anchor), one copy per 16-query block so that
-// each accumulator is loaded directly
-constexpr int LDS_QBIAS = LDS_QV + 8192;
-constexpr int LDS_QBUF = LDS_QBIAS + 512;
-constexpr int LDS_TOTAL = 3 * LDS_QBUF > LDS_BF ? 3 * LDS_QBUF : LDS_BF;
+constexpr int LDS_QBIAS = LDS_QV + 8192;  // per-key MFMA C input: 0, or NEG_DOT for an anchor
+constexpr int LDS_QBUF = LDS_QBIAS + 256;
+constexpr int RING = 4;
+constexpr int LDS_TOTAL = RING * LDS_QBUF > LDS_BF ? RING * LDS_QBUF : LDS_BF;
 
 typedef long i64;
 
@@ -68,20 +67,28 @@ __device__ inline float uniform_f(float x) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, x)));
 }
 
-// Maximum over the 4 lanes l, l^16, l^32, l^48 (one MFMA column).  v_permlane32_swap(v, v)
-// returns (v[l], v[l+32]) on lanes < 32 and (v[l-32], v[l]) above; v_permlane16_swap does the
-// same between the two halves of each 32-lane half -- VALU ops, no LDS round trip.
-__device__ inline int wave_max_i(int v) {
-  const auto a = __builtin_amdgcn_permlane32_swap((unsigned)v, (unsigned)v, false, false);
-  v = max((int)a[0], (int)a[1]);
-  const auto b = __builtin_amdgcn_permlane16_swap((unsigned)v, (unsigned)v, false, false);
-  return max((int)b[0], (int)b[1]);
+// Maxima over the 4 lanes l, l^16, l^32, l^48 (one 16x16 MFMA column) of two values at once
+// (a: 16-query block 0, b: block 1).  v_permlane32_swap(a, b) leaves block 0's pair
+// (l, l+32) on the lower 32 lanes and block 1's pair on the upper ones, v_permlane16_swap
+// then folds l^16 in, and a last v_permlane32_swap(y, y) returns block 0's result in its
+// first and block 1's in its second output on every lane -- VALU ops, no LDS round trip.
+__device__ inline void col4_max2_i(int& a, int& b) {
+  const auto x = __builtin_amdgcn_permlane32_swap((unsigned)a, (unsigned)b, false, false);
+  int y = max((int)x[0], (int)x[1]);
+  const auto z = __builtin_amdgcn_permlane16_swap((unsigned)y, (unsigned)y, false, false);
+  y = max((int)z[0], (int)z[1]);
+  const auto u = __builtin_amdgcn_permlane32_swap((unsigned)y, (unsigned)y, false, false);
+  a = (int)u[0];
+  b = (int)u[1];
 }
-__device__ inline float wave_max_f16(float v) {
-  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+__device__ inline void col4_max2_f(float& a, float& b) {
+  const auto x = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  float y = fmaxf(__uint_as_float(x[0]), __uint_as_float(x[1]));
+  const auto z = __builtin_amdgcn_permlane16_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+  y = fmaxf(__uint_as_float(z[0]), __uint_as_float(z[1]));
+  const auto u = __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+  a = __uint_as_float(u[0]);
+  b = __uint_as_float(u[1]);
 }
 
 // ------------------------------------------------------------------ operand quantization
@@ -321,10 +328,9 @@ __device__ inline void store_tile_q(const Ctx& c, uint8_t* lds, const TileQRegs&
     *(u32x4*)(lds + 16 * ch) = r.k[i];
     *(u32x4*)(lds + LDS_QV + 16 * ch) = r.v[i];
   }
-  if (c.tid < 128) {  // anchor mask of key tid % 64, built once per tile for every wave
-    const int key = c.tid & 63;
-    const uint32_t word = key < 32 ? r.w0 : r.w1;
-    *(int*)(lds + LDS_QBIAS + 4 * c.tid) = ((word >> (key & 31)) & 1u) ? NEG_DOT : 0;
+  if (c.tid < 64) {  // anchor mask of key tid, built once per tile for every wave
+    const uint32_t word = c.tid < 32 ? r.w0 : r.w1;
+    *(int*)(lds + LDS_QBIAS + 4 * c.tid) = ((word >> (c.tid & 31)) & 1u) ? NEG_DOT : 0;
   }
 }
 
@@ -344,37 +350,36 @@ __device__ inline void load_tile_bf(const Ctx& c, uint8_t* lds, const uint16_t* 
   }
 }
 
-// Scores of one quantized tile for the wave's 32 queries: S^T = K . Q^T on INT8 codes (Q codes
-// in registers: qi[qb][s] = bytes 64 s + 16 j of query row 16 qb + l16), with the masked keys
-// (anchors; on an EDGE tile also j > i - 128) pushed to NEG_DOT through the MFMA's C input.
-// Two passes over the 64 channels of each k-step so the 8 independent (qb, kb) chains
-// interleave in the MFMA pipe.
+// Scores of one quantized tile (or of its 16-key block kb) for the wave's 32 queries:
+// S^T = K . Q^T on INT8 codes (Q codes in registers: qi[qb][s] = bytes 64 s + 16 j of query
+// row 16 qb + l16), with the masked keys (anchors; on an EDGE tile also j > i - 128) pushed
+// to NEG_DOT through the MFMA's C input.
+template <bool EDGE>
+__device__ inline void qk_block_q(const Ctx& c, const uint8_t* buf, const i32x4 (*qi)[2], int t, int kb,
+                                  i32x4 (&S2)[2][4]) {
+  const i32x4 kf0 = *(const i32x4*)(buf + (c.j * 64 + 16 * kb + c.l16) * 16);
+  const i32x4 kf1 = *(const i32x4*)(buf + ((4 + c.j) * 64 + 16 * kb + c.l16) * 16);
+  const i32x4 bias = *(const i32x4*)(buf + LDS_QBIAS + 4 * (16 * kb + 4 * c.j));  // keys 16kb+4j+r
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    i32x4 acc = bias;
+    if (EDGE) {
+      const int row = c.r0w + 16 * qb + c.l16;
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (64 * t + 16 * kb + 4 * c.j + r > row - WIN) acc[r] = NEG_DOT;
+    }
+    S2[qb][kb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(kf0, qi[qb][0], acc, 0, 0, 0);
+  }
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb)
+    S2[qb][kb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(kf1, qi[qb][1], S2[qb][kb], 0, 0, 0);
+}
 template <bool EDGE>
 __device__ inline void qk_tile_q(const Ctx& c, const uint8_t* buf, const i32x4 (&qi)[2][2], int t,
                                  i32x4 (&S2)[2][4]) {
-  const int kt0 = 64 * t;
 #pragma unroll
-  for (int kb = 0; kb < 4; ++kb) {
-    const i32x4 kf0 = *(const i32x4*)(buf + (c.j * 64 + 16 * kb + c.l16) * 16);
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      i32x4 acc = *(const i32x4*)(buf + LDS_QBIAS + 256 * qb + 4 * (16 * kb + 4 * c.j));  // keys 16kb+4j+r
-      if (EDGE) {
-        const int row = c.r0w + 16 * qb + c.l16;
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (kt0 + 16 * kb + 4 * c.j + r > row - WIN) acc[r] = NEG_DOT;
-      }
-      S2[qb][kb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(kf0, qi[qb][0], acc, 0, 0, 0);
-    }
-  }
-#pragma unroll
-  for (int kb = 0; kb < 4; ++kb) {
-    const i32x4 kf1 = *(const i32x4*)(buf + ((4 + c.j) * 64 + 16 * kb + c.l16) * 16);
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
-      S2[qb][kb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(kf1, qi[qb][1], S2[qb][kb], 0, 0, 0);
-  }
+  for (int kb = 0; kb < 4; ++kb) qk_block_q<EDGE>(c, buf, qi, t, kb, S2);
 }
 __device__ inline void qk_tile(const Ctx& c, const uint8_t* buf, const i32x4 (&qi)[2][2], int t,
                                i32x4 (&S2)[2][4]) {
@@ -386,22 +391,29 @@ __device__ inline void qk_tile(const Ctx& c, const uint8_t* buf, const i32x4 (&q
 
 // Online softmax of one quantized tile's scores: the row-state max update (rescaling the
 // accumulators when a max moved), P = E4M3(448 p) codes, their row sums (MFMA against a row
-// of ones) and the codes regrouped into the B operand of the 32x32x64 P.V MFMA (pk).
+// of ones) and the codes regrouped into the B operand of the 32x32x64 P.V MFMA (pk).  With
+// FUSE_QK the scores of the next, interior tile tq (buffer qkbuf) replace S2 block by block
+// as the exponentials free them, so its MFMAs run under this softmax's VALU work.
 // c2 = s_Q s_K alpha log2(e) (wave-uniform).  Below C2_FAST_MIN a masked score is not
 // guaranteed to underflow exp2, so the masked entries are zeroed explicitly.
-template <bool TINY>
-__device__ inline void softmax_tile_q(const Ctx& c, const i32x4 (&S2)[2][4], float c2, RowState& st, i32x8& pk) {
+template <bool TINY, bool FUSE_QK = false>
+__device__ inline void softmax_tile_q(const Ctx& c, i32x4 (&S2)[2][4], float c2, RowState& st, i32x8& pk,
+                                      const uint8_t* qkbuf = nullptr, const i32x4 (*qi)[2] = nullptr, int tq = 0) {
   bool valid[2];
   float tmax[2], muse[2];
+  int mi[2];
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
-    int mi = NEG_DOT;
+    mi[qb] = NEG_DOT;
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
-      mi = max(mi, max(max(S2[qb][kb][0], S2[qb][kb][1]), max(S2[qb][kb][2], S2[qb][kb][3])));
-    mi = wave_max_i(mi);
-    valid[qb] = mi > NEG_DOT / 2;
-    tmax[qb] = (float)mi * c2;
+      mi[qb] = max(mi[qb], max(max(S2[qb][kb][0], S2[qb][kb][1]), max(S2[qb][kb][2], S2[qb][kb][3])));
+  }
+  col4_max2_i(mi[0], mi[1]);
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    valid[qb] = mi[qb] > NEG_DOT / 2;
+    tmax[qb] = (float)mi[qb] * c2;
   }
   row_update(c, st, valid, tmax, LOG2_448, muse);
   // w[2 kb + qb]: codes of block qb, keys 16 kb + 4 j + r -- the row-sum B operand as is, and
@@ -417,9 +429,12 @@ __device__ inline void softmax_tile_q(const Ctx& c, const i32x4 (&S2)[2][4], flo
         pv[r] = __builtin_amdgcn_exp2f(__builtin_fmaf((float)S2[qb][kb][r], c2, -muse[qb]));
         if (TINY && S2[qb][kb][r] <= NEG_DOT / 2) pv[r] = 0.0f;
       }
-      const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(pv[0], pv[1], 0, false);
+      // the first conversion's high half is overwritten by the second: any old value will do
+      const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(pv[0], pv[1], __float_as_int(pv[1]), false);
       w[2 * kb + qb] = __builtin_amdgcn_cvt_pk_fp8_f32(pv[2], pv[3], lo, true);
     }
+    // block kb's score registers are free: the next tile's (interior) block kb goes there
+    if (FUSE_QK) qk_block_q<false>(c, qkbuf, qi, tq, kb, S2);
   }
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb)
@@ -484,16 +499,19 @@ __device__ inline void compute_tile_bf(const PrefillParams& p, const Ctx& c, con
     }
   }
   bool valid[2];
-  float tmax[2], muse[2];
+  float tmax[2], muse[2], mt[2];
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
-    float mt = -INFINITY;
+    mt[qb] = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
-      mt = fmaxf(mt, fmaxf(fmaxf(S[qb][kb][0], S[qb][kb][1]), fmaxf(S[qb][kb][2], S[qb][kb][3])));
-    mt = wave_max_f16(mt);
-    valid[qb] = mt > -INFINITY;
-    tmax[qb] = mt * AL2;
+      mt[qb] = fmaxf(mt[qb], fmaxf(fmaxf(S[qb][kb][0], S[qb][kb][1]), fmaxf(S[qb][kb][2], S[qb][kb][3])));
+  }
+  col4_max2_f(mt[0], mt[1]);
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    valid[qb] = mt[qb] > -INFINITY;
+    tmax[qb] = mt[qb] * AL2;
   }
   row_update(c, st, valid, tmax, 0.0f, muse);
 #pragma unroll
@@ -523,18 +541,19 @@ __device__ inline void compute_tile_bf(const PrefillParams& p, const Ctx& c, con
 
 // Segment A (quantized tiles 0 .. nA-1) for one workgroup.
 //
-// Software pipeline over a ring of 3 LDS tile buffers, one barrier per tile.  Iteration t:
-//   store tile t+2 (fetched into registers during iteration t-1) into buffer (t+2) % 3 --
+// Software pipeline over a ring of 4 LDS tile buffers, one barrier per tile.  Iteration t:
+//   store tile t+3 (fetched into registers during iteration t-1) into buffer (t+3) % 4 --
 //   free since the previous barrier, its last reader being P.V(t-1);
-//   fetch tile t+3 into registers;
-//   P.V(t) (MFMA, codes from the previous iteration) and, underneath it, softmax(t+1) (VALU);
-//   barrier (tile t+2 visible to everyone);
-//   QK^T(t+2) (MFMA).
+//   fetch tile t+4 into registers;
+//   P.V(t) (MFMA, codes from the previous iteration), softmax(t+1) (VALU) and, under it,
+//   QK^T(t+2) (MFMA; tile t+2 was stored one iteration earlier);
+//   barrier (tile t+3 visible to everyone).
 // The exact per-tile max update of softmax(t+1) may rescale the accumulator: that multiply
 // waits for P.V(t), as the order of Alg. 2 requires.  Tiles past the wave's last row
-// (64 t > r0w + 31 - 128) are loaded for the other waves but not computed.  While all three
-// compute steps are due (t + 2 < the wave's tile count) the loop runs unrolled by three, so
-// the buffer offsets are constants and no step is conditional.
+// (64 t > r0w + 31 - 128) are loaded for the other waves but not computed.  While every step
+// is due and QK^T(t+2) is an interior tile the loop runs unrolled by four, so the buffer
+// offsets are constants and no step is conditional; the rest runs one conditional step at a
+// time.
 template <bool TINY>
 __device__ inline float tile_c2(float sq_u, float sk) {
   float c2 = uniform_f(sq_u * sk * AL2);
@@ -543,52 +562,54 @@ __device__ inline float tile_c2(float sq_u, float sk) {
 }
 
 struct PipeA {
-  TileQRegs pre;     // tile in flight from global memory
-  float sk1, sk2;    // K scales of the tiles whose scores are held (t+1) and just stored (t+2)
-  i32x4 S2[2][4];    // scores of tile t+1
-  i32x8 pk;          // P codes of tile t
+  TileQRegs pre;      // tile in flight from global memory
+  float sk1, sk2, sk3;  // K scales of tiles t+1, t+2, t+3
+  i32x4 S2[2][4];     // scores of tile t+1
+  i32x8 pk;           // P codes of tile t
 };
 
 template <bool TINY, int PH>
 __device__ inline void segment_a_main(const PrefillParams& p, const Ctx& c, uint8_t* lds, const i32x4 (&qi)[2][2],
                                       int nA, float sq_u, int t, PipeA& a, RowState& st) {
-  uint8_t* next = lds + ((PH + 2) % 3) * LDS_QBUF;
-  store_tile_q(c, next, a.pre);
-  a.sk2 = a.pre.sk;
-  fetch_tile_q(p, c, min(t + 3, nA - 1), a.pre);  // past the end: loaded, never stored
+  store_tile_q(c, lds + ((PH + 3) % RING) * LDS_QBUF, a.pre);
+  a.sk3 = a.pre.sk;
+  fetch_tile_q(p, c, min(t + 4, nA - 1), a.pre);  // past the end: loaded, never stored
   pv_tile_q(c, lds + PH * LDS_QBUF, a.pk, st);
-  softmax_tile_q<TINY>(c, a.S2, tile_c2<TINY>(sq_u, a.sk1), st, a.pk);
+  softmax_tile_q<TINY, true>(c, a.S2, tile_c2<TINY>(sq_u, a.sk1), st, a.pk, lds + ((PH + 2) % RING) * LDS_QBUF,
+                             qi, t + 2);
   __syncthreads();
-  qk_tile(c, next, qi, t + 2, a.S2);
   a.sk1 = a.sk2;
+  a.sk2 = a.sk3;
 }
 
 template <bool TINY>
 __device__ inline void segment_a_tail(const PrefillParams& p, const Ctx& c, uint8_t* lds, const i32x4 (&qi)[2][2],
                                       int nA, int nAw, float sq_u, int t, PipeA& a, RowState& st) {
-  uint8_t* next = lds + ((t + 2) % 3) * LDS_QBUF;
-  if (t + 2 < nA) {
-    store_tile_q(c, next, a.pre);
-    a.sk2 = a.pre.sk;
+  if (t + 3 < nA) {
+    store_tile_q(c, lds + ((t + 3) % RING) * LDS_QBUF, a.pre);
+    a.sk3 = a.pre.sk;
   }
-  if (t + 3 < nA) fetch_tile_q(p, c, t + 3, a.pre);
-  if (t < nAw) pv_tile_q(c, lds + (t % 3) * LDS_QBUF, a.pk, st);
+  if (t + 4 < nA) fetch_tile_q(p, c, t + 4, a.pre);
+  if (t < nAw) pv_tile_q(c, lds + (t % RING) * LDS_QBUF, a.pk, st);
   if (t + 1 < nAw) softmax_tile_q<TINY>(c, a.S2, tile_c2<TINY>(sq_u, a.sk1), st, a.pk);
+  if (t + 2 < nAw) qk_tile(c, lds + ((t + 2) % RING) * LDS_QBUF, qi, t + 2, a.S2);
   __syncthreads();
-  if (t + 2 < nAw) qk_tile(c, next, qi, t + 2, a.S2);
   a.sk1 = a.sk2;
+  a.sk2 = a.sk3;
 }
 
 template <bool TINY>
 __device__ inline void segment_a(const PrefillParams& p, const Ctx& c, uint8_t* lds, const i32x4 (&qi)[2][2],
                                  int nA, float sq_u, RowState& st) {
   const int nAw = c.r0w + 31 - WIN >= 0 ? ((c.r0w + 31 - WIN) >> 6) + 1 : 0;
+  // interior tiles (every key at least 128 before every row of the wave): 64 t + 63 <= r0w - 128
+  const int nInt = c.r0w - WIN - 63 >= 0 ? ((c.r0w - WIN - 63) >> 6) + 1 : 0;
   if (nA <= 0) return;
   PipeA a;
   float sk0 = 0.0f;
-  a.sk1 = a.sk2 = 0.0f;
-  fetch_tile_q(p, c, 0, a.pre);
+  a.sk1 = a.sk2 = a.sk3 = 0.0f;
   __syncthreads();  // nothing else uses the tile buffers now
+  fetch_tile_q(p, c, 0, a.pre);
   store_tile_q(c, lds, a.pre);
   sk0 = a.pre.sk;
   if (nA > 1) {
@@ -596,7 +617,12 @@ __device__ inline void segment_a(const PrefillParams& p, const Ctx& c, uint8_t* 
     store_tile_q(c, lds + LDS_QBUF, a.pre);
     a.sk1 = a.pre.sk;
   }
-  if (nA > 2) fetch_tile_q(p, c, 2, a.pre);
+  if (nA > 2) {
+    fetch_tile_q(p, c, 2, a.pre);
+    store_tile_q(c, lds + 2 * LDS_QBUF, a.pre);
+    a.sk2 = a.pre.sk;
+  }
+  if (nA > 3) fetch_tile_q(p, c, 3, a.pre);
   __syncthreads();
   // prologue: scores and P codes of tile 0, scores of tile 1
   if (nAw > 0) {
@@ -605,10 +631,12 @@ __device__ inline void segment_a(const PrefillParams& p, const Ctx& c, uint8_t* 
   }
   if (1 < nAw) qk_tile(c, lds + LDS_QBUF, qi, 1, a.S2);
   int t = 0;
-  for (; t + 5 <= nAw; t += 3) {  // iterations t .. t+2 all have t + 2 < nAw
+  // group t .. t+3: stores up to tile t+6 < nA, QK^T up to tile t+5 interior (< nInt <= nAw)
+  for (; t + 6 < nA && t + 5 < nInt; t += RING) {
     segment_a_main<TINY, 0>(p, c, lds, qi, nA, sq_u, t, a, st);
     segment_a_main<TINY, 1>(p, c, lds, qi, nA, sq_u, t + 1, a, st);
     segment_a_main<TINY, 2>(p, c, lds, qi, nA, sq_u, t + 2, a, st);
+    segment_a_main<TINY, 3>(p, c, lds, qi, nA, sq_u, t + 3, a, st);
   }
   for (; t < nA; ++t) segment_a_tail<TINY>(p, c, lds, qi, nA, nAw, sq_u, t, a, st);
 }
