@@ -51,6 +51,8 @@ def parse():
     ap.add_argument("--no-rows", action="store_true",
                     help="skip the other hot-path rows (append, selector/refresh, prefill)")
     ap.add_argument("--prefill-lens", default="8192,32768")
+    ap.add_argument("--only-prefill", action="store_true",
+                    help="run only the hybrid-prefill rows (for profiling the prefill kernels)")
     return ap.parse_args()
 
 
@@ -333,6 +335,13 @@ def main():
         print(json.dumps({"error": "no GPU visible"}))
         sys.exit(3)
     dev = torch.device("cuda:0")
+    if args.only_prefill:
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(args.seed)
+        rows = {f"prefill_{n}": bench_prefill(torch, hq, gen, dev, n)
+                for n in [int(x) for x in args.prefill_lens.split(",") if x]}
+        print(json.dumps({"rows": rows}), flush=True)
+        return
     B, Hq, Hkv, L = args.batch, args.hq, args.hkv, args.ctx
     G = Hq // Hkv
     shape = hq.Shape.for_context(B, Hq, Hkv, L + 64)
