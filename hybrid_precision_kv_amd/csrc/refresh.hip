@@ -24,6 +24,8 @@
 // Writes of single V codes go through dword atomics (8 slots share each V-code dword).
 //
 // Built with -ffp-contract=off (the quantizer's operation order is part of its contract).
+#include <algorithm>
+
 #include "hyq_common.h"
 #include "hyq_launch.h"
 
@@ -88,34 +90,6 @@ __device__ inline Scratch scratch(const RefreshParams& p, int hb) {
 __device__ inline bool bit_at(const uint32_t* bm, int pos) { return (bm[pos >> 5] >> (pos & 31)) & 1u; }
 __device__ inline int rank_at(const uint32_t* bm, const int32_t* pre, int pos) {
   return pre[pos >> 5] + __popc(bm[pos >> 5] & ((1u << (pos & 31)) - 1u));
-}
-
-// quantize 32 channels (group g) of a bf16 row and store them into INT4 slot `slot`
-__device__ inline void store_int4_group(uint8_t* slab, int slot, int g, bool is_v, const float* x) {
-  uint8_t code[32];
-  __half s16, m16;
-  quant_group32(x, code, s16, m16);
-  const uint32_t smw = (uint32_t)__half_as_ushort(s16) | ((uint32_t)__half_as_ushort(m16) << 16);
-  if (!is_v) {
-    u32x4 packed;
-#pragma unroll
-    for (int d4 = 0; d4 < 4; ++d4) {
-      uint32_t w = 0;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) w |= (uint32_t)code[8 * d4 + j] << (4 * j);
-      packed[d4] = w;
-    }
-    *(u32x4*)(slab + kcode_chunk(slot, g)) = packed;
-    *(uint32_t*)(slab + ksm_byte(slot, g)) = smw;
-  } else {
-    const int sh = vcode_shift(slot);
-    for (int j = 0; j < 32; ++j) {
-      unsigned* dw = (unsigned*)(slab + vcode_byte(slot, 32 * g + j));
-      atomicAnd(dw, ~(0xFu << sh));
-      atomicOr(dw, (uint32_t)code[j] << sh);
-    }
-    *(uint32_t*)(slab + vsm_byte(slot, g)) = smw;
-  }
 }
 
 // ------------------------------------------------------------------ plan
@@ -308,51 +282,108 @@ __global__ __launch_bounds__(256) void refresh_gather_kernel(RefreshParams p) {
 }
 
 // ------------------------------------------------------------------ move: one wave per move
+// The plan's move count is known only on the device, so a fixed grid of MOVE_BLOCKS workgroups
+// per head walks the list (wave w takes moves w, w + waves, ...).
+//
+// Demoting a bf16 row uses the whole wave: lane = 32 kv + 8 g + sub holds channels
+// 32 g + 4 sub + e (e < 4) of K (kv = 0) or V (kv = 1); the group's min and max come from a
+// reduction over its 8 lanes, and every code follows the group quantizer's formula.  A V code
+// is one nibble of a dword shared by 8 slots: each slot is written by exactly one move, so the
+// nibble is replaced with one atomic XOR of (old ^ new), which commutes with the other slots'.
+constexpr int MOVE_BLOCKS = 16;
+
+__device__ inline void put_vcode(uint8_t* slab, int slot, int c, uint32_t code) {
+  unsigned* dw = (unsigned*)(slab + vcode_byte(slot, c));
+  const int sh = vcode_shift(slot);
+  const uint32_t delta = (((*dw >> sh) & 15u) ^ code) << sh;
+  if (delta) atomicXor(dw, delta);
+}
+
+__device__ inline float group8_min(float v) {
+#pragma unroll
+  for (int o = 1; o < 8; o <<= 1) v = fminf(v, shfl_xor_f(v, o));
+  return v;
+}
+__device__ inline float group8_max(float v) {
+#pragma unroll
+  for (int o = 1; o < 8; o <<= 1) v = fmaxf(v, shfl_xor_f(v, o));
+  return v;
+}
+
 __global__ __launch_bounds__(256) void refresh_move_kernel(RefreshParams p) {
   const int hb = blockIdx.y, lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   const Scratch s = scratch(p, hb);
-  if (t >= s.cnt[0]) return;
+  const int n = min(s.cnt[0], p.max_moves), waves = gridDim.x * 4;
   const int P = p.len - WIN;
   const int ps0 = P - p.n_staged;
   uint8_t* slab = p.int4 + hb * (size_t)p.int4_cap * 160;
   int32_t* slot_pos = p.slot_pos + hb * (size_t)p.int4_cap;
   const size_t aslab = (size_t)p.anchor_cap * D, sslab = (size_t)p.staging_cap * D;
-  const int dst = s.mv_dst[t], kind = s.mv_kind[t], src = s.mv_src[t];
-  if (dst < 0 || dst >= p.int4_cap) return;
-  if (kind <= 1) {
-    // quantize a bf16 row (old anchor or staged token): lanes 0..7 = (K/V, group)
-    const uint16_t* sk = kind == 0 ? p.a_k + hb * aslab : p.s_k + hb * sslab;
-    const uint16_t* sv = kind == 0 ? p.a_v + hb * aslab : p.s_v + hb * sslab;
-    if (lane < 8) {
-      const bool is_v = lane >= 4;
-      const int g = lane & 3;
-      float x[32];
-      for (int j = 0; j < 32; ++j) {
-        const int c = 32 * g + j;
-        x[j] = bf16_bits_to_f32(is_v ? sv[vbf_index(src, c)] : sk[kbf_index(src, c)]);
+  const int kv = lane >> 5, g = (lane >> 3) & 3, sub = lane & 7;
+  for (int t = blockIdx.x * 4 + (threadIdx.x >> 6); t < n; t += waves) {
+    const int dst = s.mv_dst[t], kind = s.mv_kind[t], src = s.mv_src[t];
+    const int src_cap = kind == 0 ? p.anchor_cap : kind == 1 ? p.staging_cap : p.int4_cap;
+    if (dst < 0 || dst >= p.int4_cap || src < 0 || src >= src_cap) continue;
+    if (kind <= 1) {
+      // quantize a bf16 row (old anchor or staged token) into slot dst
+      const uint16_t* sk = kind == 0 ? p.a_k + hb * aslab : p.s_k + hb * sslab;
+      const uint16_t* sv = kind == 0 ? p.a_v + hb * aslab : p.s_v + hb * sslab;
+      const int c0 = 32 * g + 4 * sub;
+      float x[4];
+      if (kv == 0) {
+        const uint2 raw = *(const uint2*)(sk + kbf_index(src, c0));  // channels c0 .. c0+3
+        x[0] = bf16_bits_to_f32((uint16_t)raw.x);
+        x[1] = bf16_bits_to_f32((uint16_t)(raw.x >> 16));
+        x[2] = bf16_bits_to_f32((uint16_t)raw.y);
+        x[3] = bf16_bits_to_f32((uint16_t)(raw.y >> 16));
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = bf16_bits_to_f32(sv[vbf_index(src, c0 + e)]);
       }
-      store_int4_group(slab, dst, g, is_v, x);
+      const float mn = group8_min(fminf(fminf(x[0], x[1]), fminf(x[2], x[3])));
+      const float mx = group8_max(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
+      // the group quantizer's scale, minimum and codes (same operations, same order)
+      const __half s16 = __float2half_rn(__fdiv_rn(__fsub_rn(mx, mn), 15.0f));
+      const __half m16 = __float2half_rn(mn);
+      const float sf = __half2float(s16), mf = __half2float(m16);
+      uint32_t code[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float cq = 0.0f;
+        if (sf != 0.0f) {
+          cq = rintf(__fdiv_rn(__fsub_rn(x[e], mf), sf));
+          cq = fminf(fmaxf(cq, 0.0f), 15.0f);
+        }
+        code[e] = (uint32_t)cq;
+      }
+      const uint32_t smw = (uint32_t)__half_as_ushort(s16) | ((uint32_t)__half_as_ushort(m16) << 16);
+      if (kv == 0) {
+        // nibbles 4 sub + e of the group's 32; dword sub / 2 holds lanes sub & ~1 (low) and | 1
+        const uint32_t half16 = code[0] | (code[1] << 4) | (code[2] << 8) | (code[3] << 12);
+        const uint32_t other = (uint32_t)__float_as_int(shfl_xor_f(__int_as_float((int)half16), 1));
+        if ((sub & 1) == 0) *(uint32_t*)(slab + kcode_chunk(dst, g) + 4 * (sub >> 1)) = half16 | (other << 16);
+        if (sub == 0) *(uint32_t*)(slab + ksm_byte(dst, g)) = smw;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) put_vcode(slab, dst, c0 + e, code[e]);
+        if (sub == 0) *(uint32_t*)(slab + vsm_byte(dst, g)) = smw;
+      }
+      if (lane == 0) slot_pos[dst] = kind == 0 ? p.a_pos[hb * (size_t)p.anchor_cap + src] : ps0 + src;
+    } else {
+      // move an INT4 slot: codes, (scale, min), position
+      if (lane < 16) {  // K code chunks (4 x 16 B) as 16 dwords
+        const int q4 = lane >> 2, d = lane & 3;
+        *(uint32_t*)(slab + kcode_chunk(dst, q4) + 4 * d) = *(const uint32_t*)(slab + kcode_chunk(src, q4) + 4 * d);
+      } else if (lane < 20) {
+        const int q4 = lane - 16;
+        *(uint32_t*)(slab + ksm_byte(dst, q4)) = *(const uint32_t*)(slab + ksm_byte(src, q4));
+        *(uint32_t*)(slab + vsm_byte(dst, q4)) = *(const uint32_t*)(slab + vsm_byte(src, q4));
+      }
+      const int shs = vcode_shift(src);
+      for (int c = lane; c < D; c += 64)
+        put_vcode(slab, dst, c, (*(const uint32_t*)(slab + vcode_byte(src, c)) >> shs) & 15u);
+      if (lane == 0) slot_pos[dst] = slot_pos[src];
     }
-    if (lane == 0) slot_pos[dst] = kind == 0 ? p.a_pos[hb * (size_t)p.anchor_cap + src] : ps0 + src;
-  } else {
-    // move an INT4 slot: codes, (scale, min), position
-    if (lane < 16) {  // K code chunks (4 x 16 B) as 16 dwords
-      const int g = lane >> 2, d = lane & 3;
-      *(uint32_t*)(slab + kcode_chunk(dst, g) + 4 * d) = *(const uint32_t*)(slab + kcode_chunk(src, g) + 4 * d);
-    } else if (lane < 20) {
-      const int g = lane - 16;
-      *(uint32_t*)(slab + ksm_byte(dst, g)) = *(const uint32_t*)(slab + ksm_byte(src, g));
-      *(uint32_t*)(slab + vsm_byte(dst, g)) = *(const uint32_t*)(slab + vsm_byte(src, g));
-    }
-    const int shs = vcode_shift(src), shd = vcode_shift(dst);
-    for (int c = lane; c < D; c += 64) {
-      const uint32_t code = (*(const uint32_t*)(slab + vcode_byte(src, c)) >> shs) & 15u;
-      unsigned* dw = (unsigned*)(slab + vcode_byte(dst, c));
-      atomicAnd(dw, ~(0xFu << shd));
-      atomicOr(dw, code << shd);
-    }
-    if (lane == 0) slot_pos[dst] = slot_pos[src];
   }
 }
 
@@ -387,7 +418,8 @@ hipError_t launch_refresh(const RefreshParams& p, hipStream_t stream) {
   hipLaunchKernelGGL(refresh_plan_kernel, dim3(H), dim3(PT), 0, stream, p);
   const int ka = min(p.k, p.anchor_cap);
   if (ka > 0) hipLaunchKernelGGL(refresh_gather_kernel, dim3((ka + 3) / 4, H), dim3(256), 0, stream, p);
-  hipLaunchKernelGGL(refresh_move_kernel, dim3((p.max_moves + 3) / 4, H), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL(refresh_move_kernel, dim3(std::max(1, std::min((p.max_moves + 3) / 4, MOVE_BLOCKS)), H),
+                     dim3(256), 0, stream, p);
   const int a_end = min((p.k + 31) & ~31, p.anchor_cap);
   if (a_end > 0) hipLaunchKernelGGL(refresh_store_kernel, dim3((a_end + 3) / 4, H), dim3(256), 0, stream, p);
   return hipGetLastError();
