@@ -77,8 +77,9 @@ def stored_traffic(workload: str):
     return t.get("bytes_per_launch")
 
 
-def make_layer(torch, hq, shape, B, Hkv, G, L, gen, device):
-    """One layer: planted-anchor K/V/proxies on the GPU, anchors, Freeze into a hybrid cache."""
+def make_layer(torch, hq, shape, B, Hkv, G, L, gen, device, all_bf16=False):
+    """One layer: planted-anchor K/V/proxies on the GPU, anchors, Freeze into a hybrid cache.
+    all_bf16: every candidate position is an anchor (k = P), so nothing is quantized."""
     Hq = Hkv * G
     H = B * Hkv
     u = torch.randn(H, D, generator=gen, device=device)
@@ -97,9 +98,11 @@ def make_layer(torch, hq, shape, B, Hkv, G, L, gen, device):
     uq = u.view(B, Hkv, D).repeat_interleave(G, dim=1)  # [B][Hq][D]
     proxy = (2.0 * uq[:, :, None, :] + torch.randn(B, Hq, 64, D, generator=gen, device=device)).to(torch.bfloat16)
     q = (2.0 * uq + torch.randn(B, Hq, D, generator=gen, device=device)).to(torch.bfloat16)
-    k = hq.anchor_count(L)
+    k = hq.anchor_count(L, 100 if all_bf16 else 5)
     anchors = None
-    if k:
+    if k and all_bf16:
+        anchors = torch.arange(k, dtype=torch.int32, device=device).expand(B, Hkv, k).contiguous()
+    elif k:
         try:
             anchors = hq.select_vlines(shape, k, dense_k=K, proxy=proxy)
         except hq._lib.HyqError:
@@ -182,17 +185,20 @@ def bench_maintenance(torch, hq, cache, B, Hkv, G, L, gen, dev, ws, out, splits)
             "note": f"one layer, bs{B} ctx {L}+64, refresh every 64 tokens"}
 
 
-def bench_decode_bs1(torch, hq, gen, dev, ctxs=(1024, 4096, 16384, 32768), Hq=32, Hkv=8, layers=36, steps=100):
+def bench_decode_bs1(torch, hq, gen, dev, ctxs=(1024, 4096, 16384, 32768), Hq=32, Hkv=8, layers=36, steps=100,
+                     B=1, all_bf16=False):
     """Llama-3.1-8B-shaped decode at batch 1 (32 Q / 8 KV heads): hyq_decode_attn per step over
-    a context sweep, rotating over ``layers`` caches like the batched workload."""
+    a context sweep, rotating over ``layers`` caches like the batched workload.  With all_bf16
+    every position is kept in bf16 (k = P): the full-precision comparison point of the HyQuant
+    paper's Table 7, run by the same kernel."""
     G = Hq // Hkv
     out = {}
     for L in ctxs:
-        shape = hq.Shape.for_context(1, Hq, Hkv, L + 64)
-        lay = [make_layer(torch, hq, shape, 1, Hkv, G, L, gen, dev) for _ in range(layers)]
-        nbytes = algorithmic_bytes(lay[0][0], 1, Hkv, Hq)
+        shape = hq.Shape.for_context(B, Hq, Hkv, L + 64, 100 if all_bf16 else 5)
+        lay = [make_layer(torch, hq, shape, B, Hkv, G, L, gen, dev, all_bf16) for _ in range(layers)]
+        nbytes = algorithmic_bytes(lay[0][0], B, Hkv, Hq)
         ws = hq.decode_workspace(shape, 0, dev)
-        o = torch.empty(1, Hq, D, dtype=torch.float32, device=dev)
+        o = torch.empty(B, Hq, D, dtype=torch.float32, device=dev)
         for i in range(10):
             hq.decode_attn(lay[i % layers][0], lay[i % layers][1], 0, o, ws)
         torch.cuda.synchronize()
@@ -431,6 +437,17 @@ def main():
         torch.cuda.empty_cache()
         rows["decode_bs1"] = bench_decode_bs1(torch, hq, gen, dev)
         print(f"[bench] bs1 sweep done", file=sys.stderr, flush=True)
+        # the same kernel with every position in bf16 (k = P): what the hybrid layout saves
+        allbf = bench_decode_bs1(torch, hq, gen, dev, all_bf16=True)
+        allbf[f"bs{B}_{L}"] = bench_decode_bs1(torch, hq, gen, dev, ctxs=(L,), Hq=Hq, Hkv=Hkv, layers=8,
+                                               B=B, all_bf16=True)[str(L)]
+        for key, r in allbf.items():
+            hyb = rows["decode_bs1"].get(key, {}).get("us_per_step") if not key.startswith("bs") else ms_per_step * 1e3
+            if hyb:
+                r["hybrid_us_per_step"] = round(hyb, 2)
+                r["hybrid_speedup"] = round(r["us_per_step"] / hyb, 2)
+        rows["decode_all_bf16"] = allbf
+        print(f"[bench] all-bf16 sweep done", file=sys.stderr, flush=True)
         for n in [int(x) for x in args.prefill_lens.split(",") if x]:
             rows[f"prefill_{n}"] = bench_prefill(torch, hq, gen, dev, n)
             print(f"[bench] prefill N={n}: {rows[f'prefill_{n}']['us_per_call']} us", file=sys.stderr, flush=True)

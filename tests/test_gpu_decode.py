@@ -163,3 +163,27 @@ def test_decode_deterministic():
     a = hq.decode_attn(p.cache, dev(q)).clone()
     b = hq.decode_attn(p.cache, dev(q)).clone()
     assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("L", [300, 2100])
+def test_all_bf16_mode_is_exact_attention(L):
+    """Every candidate position an anchor (k = P): no INT4 slot, and the decode is plain softmax
+    attention over the bf16 K/V (the comparison axis of the HyQuant paper, Table 7)."""
+    p = Pair(950 + L, 2, 2, 4, L, n_steps=1, pct=100)
+    assert p.cache.counters()["n_int4"] == 0 and p.cache.counters()["n_anchor"] == L - 128
+    p.codes_check()
+    q = p.append()
+    for s in (0, 5):
+        p.decode_check(q, n_splits=s)
+    # against torch's attention on the original bf16 rows (the cache adds no rounding here)
+    o = hq.decode_attn(p.cache, dev(q)).cpu().double()
+    K = torch.from_numpy(nm.bf16_to_f32(np.concatenate([p.d["K"], p.d["new_k"][:, :, :1, :]], axis=2))).double()
+    V = torch.from_numpy(nm.bf16_to_f32(np.concatenate([p.d["V"], p.d["new_v"][:, :, :1, :]], axis=2))).double()
+    Q = torch.from_numpy(nm.bf16_to_f32(q)).double()
+    for h in range(2):
+        qh = Q[:, h * 4:(h + 1) * 4, None, :]
+        Kh = K[:, h:h + 1].expand(-1, 4, -1, -1)
+        Vh = V[:, h:h + 1].expand(-1, 4, -1, -1)
+        ref = torch.nn.functional.scaled_dot_product_attention(qh, Kh, Vh)[:, :, 0]
+        assert torch.allclose(o[:, h * 4:(h + 1) * 4], ref, atol=MAX_ABS, rtol=0), f"head {h}"
+
