@@ -10,7 +10,8 @@ Attention".
 * ``uniform_kv``      -- every position quantized with the same b-bit group scheme
                          (uniform-precision comparison points of §2.2 Fig. 2).
 * ``prefill_ref``     -- step-by-step emulation of the hybrid prefill operator
-                         (Alg. 2; readings listed in its docstring).
+                         (Alg. 2; readings listed in its docstring), with an INT8 or an
+                         MXFP4 (``prefill_quantize_mx``) bulk Q.K^T.
 * ``attention_exact`` -- exact causal softmax attention (fp64) over bf16 inputs.
 """
 from __future__ import annotations
@@ -143,25 +144,65 @@ def prefill_quantize(Q_bits, K_bits, V_bits, anchors, BM: int = 64, BN: int = 64
             q8[h, b * BM:(b + 1) * BM], sq[h, b] = nm.quant_int8_sym(Q[h, b * BM:(b + 1) * BM])
     k8 = np.zeros(K.shape, np.int8)
     sk = np.zeros((Hkv, nkb), np.float32)
-    v8 = np.zeros(V.shape, np.float64)  # e4m3 code values (as numbers)
-    sv = np.zeros((Hkv, D), np.float32)
     for h in range(Hkv):
         isanc = np.zeros(N, bool)
         isanc[np.asarray(anchors[h], np.int64)] = True
         Kz = np.where(isanc[:, None], np.float32(0), K[h])
         for b in range(nkb):
             k8[h, b * BN:(b + 1) * BN], sk[h, b] = nm.quant_int8_sym(Kz[b * BN:(b + 1) * BN])
+    v8, sv = _v_fp8(V, anchors)
+    return dict(q8=q8, sq=sq, k8=k8, sk=sk, v8=v8, sv=sv)
+
+
+def _v_fp8(V, anchors):
+    """V of the bulk segment: OCP E4M3 with a per-channel fp32 scale s_V[c] = max over the
+    head's non-anchor keys of |V[:, c]| / 448; code = e4m3(fp32(V / s_V)).  V: fp32
+    [Hkv][N][D].  Returns (e4m3 code values as numbers, s_V)."""
+    Hkv, N, D = V.shape
+    v8 = np.zeros(V.shape, np.float64)
+    sv = np.zeros((Hkv, D), np.float32)
+    for h in range(Hkv):
+        isanc = np.zeros(N, bool)
+        isanc[np.asarray(anchors[h], np.int64)] = True
         Vz = np.where(isanc[:, None], np.float32(0), V[h])
         amax = np.abs(Vz).max(axis=0).astype(np.float32)
         sv[h] = amax / np.float32(448)
         with np.errstate(divide="ignore", invalid="ignore"):
             ratio = np.where(sv[h] > 0, Vz / np.where(sv[h] > 0, sv[h], np.float32(1)), np.float32(0))
         v8[h] = nm.e4m3_round_fast(ratio.astype(np.float32))
-    return dict(q8=q8, sq=sq, k8=k8, sk=sk, v8=v8, sv=sv)
+    return v8, sv
+
+
+def prefill_quantize_mx(Q_bits, K_bits, V_bits, anchors):
+    """Operand quantization of the hybrid prefill with an MXFP4 bulk (the HyQuant paper's
+    §4.2 names INT4/FP4 as the lower-precision bulk format on backends that have it).
+    Readings:
+      * Q and K: OCP MXFP4 per row and per 32-channel block (``mxfp4_quant_rows``): an E8M0
+        shared scale and E2M1 codes.  Every key row is quantized (an anchor's codes are
+        never used: anchors are masked in the bulk segment).
+      * V: as in ``prefill_quantize`` (E4M3, per-channel scale over non-anchor keys): P.V
+        stays FP8, only Q.K^T moves to FP4.
+    Returns dict(q4, qe, k4, ke, v8, sv): codes uint8, scale exponents int16 [.., 4]."""
+    q4, qe = nm.mxfp4_quant_rows(nm.bf16_to_f32(Q_bits))
+    k4, ke = nm.mxfp4_quant_rows(nm.bf16_to_f32(K_bits))
+    v8, sv = _v_fp8(nm.bf16_to_f32(V_bits), anchors)
+    return dict(q4=q4, qe=qe, k4=k4, ke=ke, v8=v8, sv=sv)
+
+
+def mx_dot(q4, qe, k4, ke) -> np.ndarray:
+    """MXFP4 dot products in fp64: sum over blocks of 2^(e_q + e_k) times the sum of the
+    E2M1 products.  Every product is a multiple of 2^(e_q + e_k - 2) below 2^6 and a block's
+    sum stays below 2^13 of those units, so every partial sum is exact in fp64 -- the result
+    is the exact dot -- as long as the block exponents (e_q + e_k) of one (query, key) pair
+    span fewer than 40 binades (real activations span a few).
+    q4 [M][D], qe [M][D/32], k4 [N][D], ke [N][D/32] -> [M][N]."""
+    qv = nm.e2m1_value(q4) * np.exp2(np.repeat(qe.astype(np.float64), 32, axis=-1))
+    kv = nm.e2m1_value(k4) * np.exp2(np.repeat(ke.astype(np.float64), 32, axis=-1))
+    return qv @ kv.T
 
 
 def prefill_ref(Q_bits, K_bits, V_bits, anchors, W: int = 128, BM: int = 64, BN: int = 64,
-                blocks=None, round_p: bool = True, heads=None, qz=None):
+                blocks=None, round_p: bool = True, heads=None, qz=None, bulk: str = "int8"):
     """Emulation of the hybrid prefill operator (HyQuant paper §4.2 Eq. 6-7, Alg. 2).
 
     For query i (causal), keys split three ways (Eq. 1 applied per query):
@@ -183,6 +224,9 @@ def prefill_ref(Q_bits, K_bits, V_bits, anchors, W: int = 128, BM: int = 64, BN:
     accumulator stay fp64.  Without ``round_p`` everything is fp64 (the exact mixed
     softmax of Eq. 7).  ``blocks`` / ``heads``: optional lists of 64-query blocks and Q heads
     to compute (others are NaN); ``qz``: the ``prefill_quantize`` result, if already at hand.
+    ``bulk="mxfp4"``: the quantized segment's Q.K^T uses ``prefill_quantize_mx`` operands,
+    s = fp32(exact MX dot) * alpha (the products and their block sums are exact in fp64; the
+    operator accumulates them in fp32), everything else unchanged.
     Returns fp64 [Hq][N][D].
     """
     Qf = nm.bf16_to_f32(Q_bits).astype(np.float64)
@@ -198,8 +242,10 @@ def prefill_ref(Q_bits, K_bits, V_bits, anchors, W: int = 128, BM: int = 64, BN:
             return dot64.astype(np.float32) * np.float32(alpha)
         return alpha * dot64
 
+    mx = bulk == "mxfp4"
     if qz is None:
-        qz = prefill_quantize(Q_bits, K_bits, V_bits, anchors, BM, BN)
+        qz = prefill_quantize_mx(Q_bits, K_bits, V_bits, anchors) if mx else \
+            prefill_quantize(Q_bits, K_bits, V_bits, anchors, BM, BN)
     nqb = (N + BM - 1) // BM
     if blocks is None:
         blocks = range(nqb)
@@ -209,13 +255,15 @@ def prefill_ref(Q_bits, K_bits, V_bits, anchors, W: int = 128, BM: int = 64, BN:
         anc = np.asarray(anchors[hk], np.int64)
         isanc = np.zeros(N, bool)
         isanc[anc] = True
-        k8 = qz["k8"][hk].astype(np.int64)
+        if not mx:
+            k8 = qz["k8"][hk].astype(np.int64)
         vq = qz["v8"][hk] * qz["sv"][hk].astype(np.float64)[None, :]  # dequantized FP8 V
         for b in blocks:
             r0, r1 = b * BM, min(N, (b + 1) * BM)
             rows = np.arange(r0, r1)
-            q8 = qz["q8"][h, r0:r1].astype(np.int64)
-            sq = qz["sq"][h, b] if round_p else float(qz["sq"][h, b])
+            if not mx:
+                q8 = qz["q8"][h, r0:r1].astype(np.int64)
+                sq = qz["sq"][h, b] if round_p else float(qz["sq"][h, b])
             m = np.full(len(rows), -np.inf, dtype=np.float32 if round_p else np.float64)
             l = np.zeros(len(rows))
             acc = np.zeros((len(rows), D))
@@ -247,11 +295,15 @@ def prefill_ref(Q_bits, K_bits, V_bits, anchors, W: int = 128, BM: int = 64, BN:
             if last_q >= 0:
                 for t in range(last_q // BN + 1):
                     j = np.arange(t * BN, min(N, (t + 1) * BN))
-                    dot = q8 @ k8[j].T
-                    if round_p:
-                        s = ((dot.astype(np.float32) * np.float32(sq)) * qz["sk"][hk, t]) * np.float32(alpha)
+                    if mx:
+                        dot = mx_dot(qz["q4"][h, r0:r1], qz["qe"][h, r0:r1], qz["k4"][hk, j], qz["ke"][hk, j])
+                        s = dot.astype(np.float32) * np.float32(alpha) if round_p else dot * alpha
                     else:
-                        s = dot.astype(np.float64) * (sq * float(qz["sk"][hk, t])) * alpha
+                        dot = q8 @ k8[j].T
+                        if round_p:
+                            s = ((dot.astype(np.float32) * np.float32(sq)) * qz["sk"][hk, t]) * np.float32(alpha)
+                        else:
+                            s = dot.astype(np.float64) * (sq * float(qz["sk"][hk, t])) * alpha
                     valid = (j[None, :] <= rows[:, None] - W) & ~isanc[j][None, :]
                     step(s, valid, vq[j], "A")
             # Segment B: anchors, ascending tiles of BN anchors.

@@ -191,3 +191,86 @@ def e4m3_round_fast(x) -> np.ndarray:
     mag = np.where(pick_hi, vhi, vlo)
     mag = np.where(a <= 0, 0.0, mag)
     return np.copysign(mag, x)
+
+
+# ----------------------------------------------------------------------------- OCP FP4 E2M1, MX
+
+
+def e2m1_decode_table() -> np.ndarray:
+    """Values of the 16 FP4 E2M1 codes, from the format definition: 1 sign bit, 2 exponent
+    bits (bias 1), 1 mantissa bit; exponent 0 is subnormal (m * 0.5); no infinity or NaN."""
+    vals = np.empty(16, np.float64)
+    for c in range(16):
+        e = (c >> 1) & 3
+        m = c & 1
+        v = m * 0.5 if e == 0 else (1.0 + 0.5 * m) * 2.0 ** (e - 1)
+        vals[c] = -v if c & 8 else v
+    return vals
+
+
+_E2M1 = e2m1_decode_table()
+_E2M1_POS = _E2M1[:8]  # codes 0..7: non-negative values, increasing
+
+
+def e2m1_encode(x) -> np.ndarray:
+    """fp32/fp64 -> FP4 E2M1 code (uint8 0..15): nearest value, ties to the even code
+    (mantissa bit 0), saturating at +-6.  Brute force over the 8 magnitudes."""
+    x = np.asarray(x, dtype=np.float64)
+    flat = x.reshape(-1)
+    out = np.empty(flat.shape, np.uint8)
+    for i, v in enumerate(flat):
+        a = min(abs(v), 6.0)
+        d = np.abs(_E2M1_POS - a)
+        best = np.flatnonzero(d == d.min())
+        c = int(best[0]) if len(best) == 1 else int(best[(best & 1) == 0][0])
+        if v < 0 or (v == 0 and np.signbit(v)):
+            c |= 8
+        out[i] = c
+    return out.reshape(x.shape)
+
+
+def e2m1_value(codes) -> np.ndarray:
+    return _E2M1[np.asarray(codes, dtype=np.uint8)]
+
+
+def mxfp4_quant_block(x):
+    """One OCP MX block (32 values) in MXFP4: shared scale X = 2^e with
+    e = floor(log2(max|x|)) - 2 (2 = the largest E2M1 exponent), clamped to the E8M0 range
+    [-127, 127] (e = -127 for an all-zero block); codes = e2m1(x / X) (the division by a
+    power of two is exact in fp32).  Returns (codes uint8 [32], e int)."""
+    x = np.asarray(x, dtype=F32)
+    amax = float(np.abs(x).max())
+    if amax == 0.0:
+        e = -127
+    else:
+        _, ex = np.frexp(amax)  # amax = f * 2^ex with f in [0.5, 1): floor(log2 amax) = ex - 1
+        e = int(min(127, max(-127, (int(ex) - 1) - 2)))
+    ratio = (x.astype(np.float64) * 2.0 ** (-e)).astype(F32)  # exact (power of two)
+    return e2m1_encode(ratio), e
+
+
+def mxfp4_quant_rows(X, block: int = 32):
+    """MXFP4 of every row of X [..., D] in blocks of ``block`` contiguous channels.
+    Returns (codes uint8 [..., D], e int16 [..., D / block])."""
+    X = np.asarray(X, dtype=F32)
+    lead = X.shape[:-1]
+    Dm = X.shape[-1]
+    flat = X.reshape(-1, Dm // block, block)
+    codes = np.empty(flat.shape, np.uint8)
+    ex = np.empty(flat.shape[:2], np.int16)
+    amax = np.abs(flat).max(axis=2).astype(np.float64)
+    with np.errstate(divide="ignore"):
+        _, fe = np.frexp(amax)
+    e = np.where(amax == 0.0, -127, np.clip(fe.astype(np.int64) - 3, -127, 127))
+    ratio = (flat.astype(np.float64) * np.exp2(-e.astype(np.float64))[:, :, None]).astype(F32)
+    # vectorised nearest-even E2M1 on the exact ratios (the same rule as e2m1_encode)
+    a = np.minimum(np.abs(ratio).astype(np.float64), 6.0)
+    hi = np.clip(np.searchsorted(_E2M1_POS, a, side="left"), 0, 7)
+    lo = np.clip(hi - 1, 0, 7)
+    dlo, dhi = a - _E2M1_POS[lo], _E2M1_POS[hi] - a
+    pick_hi = (dhi < dlo) | ((dhi == dlo) & ((hi & 1) == 0) & (hi != lo))
+    c = np.where(pick_hi, hi, lo).astype(np.uint8)
+    c = np.where(np.signbit(ratio), c | 8, c)
+    codes[...] = c
+    ex[...] = e
+    return codes.reshape(lead + (Dm,)), ex.reshape(lead + (Dm // block,))

@@ -261,3 +261,73 @@ def test_prefill_operand_quantizers():
     isanc = np.zeros(N, bool); isanc[anchors[0]] = True
     col = np.abs(np.where(isanc[:, None], 0, V)).argmax(0)
     assert np.all(np.abs(qz0["v8"][0][col, np.arange(128)]) == 448.0)
+
+
+def test_mx_dot_is_exact_blockwise_sum():
+    """The MXFP4 dot, by brute force with Python fractions of the decoded values."""
+    from fractions import Fraction
+    rng = np.random.default_rng(8)
+    q4 = rng.integers(0, 16, (3, 128)).astype(np.uint8)
+    k4 = rng.integers(0, 16, (4, 128)).astype(np.uint8)
+    qe = rng.integers(-9, 10, (3, 4)).astype(np.int16)  # block exponents span < 40 binades
+    ke = rng.integers(-9, 10, (4, 4)).astype(np.int16)
+    got = att.mx_dot(q4, qe, k4, ke)
+    tab = nm.e2m1_decode_table()
+    for i in range(3):
+        for j in range(4):
+            tot = Fraction(0)
+            for c in range(128):
+                b = c // 32
+                tot += Fraction(tab[q4[i, c]]) * Fraction(tab[k4[j, c]]) * Fraction(2) ** int(qe[i, b] + ke[j, b])
+            assert got[i, j] == float(tot)
+
+
+def test_prefill_mx_unrounded_equals_plain_mixed_softmax():
+    """MXFP4 bulk without P rounding: the segmented online softmax equals one plain softmax
+    per row over the per-key logits (MX dot for quantized keys, bf16 dot otherwise)."""
+    N, W = 330, 128
+    d, anchors = _prefill_inputs(36, 4, 2, N)
+    o = att.prefill_ref(d["Q"], d["K"], d["V"], anchors, round_p=False, bulk="mxfp4")
+    qz = att.prefill_quantize_mx(d["Q"], d["K"], d["V"], anchors)
+    Qf = nm.bf16_to_f32(d["Q"]).astype(np.float64)
+    Kf = nm.bf16_to_f32(d["K"]).astype(np.float64)
+    Vf = nm.bf16_to_f32(d["V"]).astype(np.float64)
+    tab = nm.e2m1_decode_table()
+    for h in range(4):
+        hk = h // 2
+        anc = set(int(a) for a in anchors[hk])
+        for i in range(0, N, 29):
+            z, vals = [], []
+            qv = tab[qz["q4"][h, i]] * np.repeat(2.0 ** qz["qe"][h, i].astype(np.float64), 32)
+            for j in range(i + 1):
+                if j >= i - W + 1 or j in anc:
+                    z.append(float(Qf[h, i] @ Kf[hk, j]) / math.sqrt(128))
+                    vals.append(Vf[hk, j])
+                else:
+                    kv = tab[qz["k4"][hk, j]] * np.repeat(2.0 ** qz["ke"][hk, j].astype(np.float64), 32)
+                    z.append(float(qv @ kv) / math.sqrt(128))
+                    vals.append(qz["v8"][hk, j] * qz["sv"][hk].astype(np.float64))
+            mx = max(z)
+            e = np.array([math.exp(t - mx) for t in z])
+            ref = (e[:, None] * np.array(vals)).sum(0) / e.sum()
+            assert np.allclose(o[h, i], ref, atol=1e-10)
+
+
+def test_prefill_mx_rounded_is_convex_and_coarser_than_int8():
+    N = 400
+    d, anchors = _prefill_inputs(37, 4, 2, N)
+    o4 = att.prefill_ref(d["Q"], d["K"], d["V"], anchors, bulk="mxfp4")
+    o8 = att.prefill_ref(d["Q"], d["K"], d["V"], anchors)
+    ex = att.attention_exact(d["Q"], d["K"], d["V"])
+    qz = att.prefill_quantize_mx(d["Q"], d["K"], d["V"], anchors)
+    Vf = nm.bf16_to_f32(d["V"]).astype(np.float64)
+    for h in range(4):
+        hk = h // 2
+        vq = qz["v8"][hk] * qz["sv"][hk].astype(np.float64)
+        lo = np.minimum(Vf[hk].min(0), vq.min(0))
+        hi = np.maximum(Vf[hk].max(0), vq.max(0))
+        assert np.all(o4[h] >= lo - 1e-9) and np.all(o4[h] <= hi + 1e-9)
+    r4 = np.linalg.norm(o4 - ex) / np.linalg.norm(ex)
+    r8 = np.linalg.norm(o8 - ex) / np.linalg.norm(ex)
+    print(f"rel-L2 vs exact: mxfp4 bulk {r4:.4f}, int8 bulk {r8:.4f}")
+    assert r8 < r4 < 0.2

@@ -155,3 +155,58 @@ def test_e4m3_ties_and_saturation():
     rng = np.random.default_rng(6)
     r = rng.uniform(-460, 460, 20000)
     assert np.array_equal(nm.e4m3_round_fast(r), nm.e4m3_round(r))
+
+
+# ----------------------------------------------------------------------------- FP4 E2M1 and MX
+
+def test_e2m1_table_is_the_format():
+    """E2M1: 1 sign, 2 exponent bits (bias 1), 1 mantissa bit, exponent 0 subnormal."""
+    t = nm.e2m1_decode_table()
+    assert list(t[:8]) == [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    assert list(t[8:]) == [-v for v in t[:8]]
+
+
+def test_e2m1_encode_nearest_ties_even_saturating():
+    vals = nm.e2m1_decode_table()
+    # every code round-trips (the negative zero code included)
+    assert np.array_equal(nm.e2m1_encode(vals), np.arange(16, dtype=np.uint8))
+    x = np.concatenate([np.arange(-8.0, 8.0, 1.0 / 64), _rand_f32(3000, 11, 2.0)]).astype(np.float32)
+    c = nm.e2m1_encode(x)
+    v = nm.e2m1_value(c)
+    mags = vals[:8]
+    for xi, vi, ci in zip(x.astype(np.float64), v, c):
+        a = min(abs(xi), 6.0)
+        gap = np.abs(mags - a)
+        assert abs(abs(vi) - a) == gap.min()          # a nearest magnitude
+        if np.count_nonzero(gap == gap.min()) == 2:   # exact midpoint: even mantissa bit
+            assert (ci & 1) == 0
+        assert (ci >= 8) == bool(np.signbit(xi))      # sign kept
+    # monotone in the value
+    order = np.argsort(x, kind="stable")
+    assert np.all(np.diff(v[order]) >= 0)
+
+
+def test_mxfp4_block_scale_rule():
+    rng = np.random.default_rng(5)
+    for trial in range(300):
+        x = (rng.standard_normal(32) * 10.0 ** rng.uniform(-6, 6)).astype(np.float32)
+        if trial % 50 == 0:
+            x[:] = 0.0
+        codes, e = nm.mxfp4_quant_block(x)
+        amax = float(np.abs(x).max())
+        if amax == 0.0:
+            assert e == -127 and np.all(codes % 8 == 0)
+            continue
+        # the block maximum lands in [4, 8) after the division by the shared scale
+        assert 4.0 <= amax / 2.0 ** e < 8.0
+        # every element is the nearest E2M1 value to x / 2^e (saturating at 6)
+        ratio = x.astype(np.float64) / 2.0 ** e
+        err = np.abs(nm.e2m1_value(codes) - np.clip(ratio, -6, 6))
+        assert np.all(err <= 1.0 + 1e-12)  # half the widest gap (4 -> 6)
+    # the vectorised row quantizer is the same rule (a different code path)
+    X = (rng.standard_normal((7, 128)) * np.array([1e-5, 1e-2, 1, 3, 100, 1e4, 0])[:, None]).astype(np.float32)
+    c, e = nm.mxfp4_quant_rows(X)
+    for r in range(7):
+        for b in range(4):
+            cb, eb = nm.mxfp4_quant_block(X[r, 32 * b:32 * b + 32])
+            assert eb == e[r, b] and np.array_equal(cb, c[r, 32 * b:32 * b + 32])
