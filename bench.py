@@ -262,9 +262,10 @@ def prefill_ops(anchors_row, N, Hq):
     return ops8, opsb
 
 
-def bench_prefill(torch, hq, gen, dev, N, Hq=32, Hkv=8):
+def bench_prefill(torch, hq, gen, dev, N, Hq=32, Hkv=8, bulk="int8"):
     """Hybrid prefill, one sequence of N tokens, 32 Q / 8 KV heads; anchors = the library's
-    selector over the last 64 queries (dense keys), 5% rule."""
+    selector over the last 64 queries (dense keys), 5% rule.  ``bulk``: the bulk Q.K^T format,
+    "int8" or "mxfp4" (P.V stays FP8 in both)."""
     G = Hq // Hkv
     u = torch.randn(Hkv, D, generator=gen, device=dev)
     u = u / u.norm(dim=-1, keepdim=True)
@@ -281,17 +282,23 @@ def bench_prefill(torch, hq, gen, dev, N, Hq=32, Hkv=8):
     ws = hq.prefill_workspace(shape, N, dev)
     o = torch.empty(Hq, N, D, dtype=torch.float32, device=dev)
     reps = 10 if N <= 8192 else 3
-    us, us_min = timed(torch, lambda: hq.prefill_attn(shape, Q, K, V, anchors=anchors, out=o, ws=ws), reps)
+    us, us_min = timed(torch, lambda: hq.prefill_attn(shape, Q, K, V, anchors=anchors, out=o, ws=ws, bulk=bulk),
+                       reps)
     ops8, opsb = prefill_ops(anchors[0].cpu().numpy(), N, Hq)
-    t_roof = ops8 / 5.0e15 + opsb / 2.5e15
+    if bulk == "mxfp4":  # Q.K^T half of the bulk work at the fp4 peak, P.V half at fp8
+        t_roof = 0.5 * ops8 / 10.1e15 + 0.5 * ops8 / 5.0e15 + opsb / 2.5e15
+        basis = "fp4 10.1 (bulk Q.K), fp8 5.0 (bulk P.V) and bf16 2.5 PFLOP/s dense, blended by op mix"
+    else:
+        t_roof = ops8 / 5.0e15 + opsb / 2.5e15
+        basis = "int8/fp8 5.0 POP/s and bf16 2.5 PFLOP/s dense, blended by op mix"
     del K, V, Q, o, ws
-    return {"workload": f"hybrid prefill N{N} hq{Hq} hkv{Hkv} anchors{k}", "us_per_call": round(us, 1),
+    return {"workload": f"hybrid prefill N{N} hq{Hq} hkv{Hkv} anchors{k} bulk {bulk}", "us_per_call": round(us, 1),
             "us_min": round(us_min, 1), "tokens_per_s": round(N / (us * 1e-6), 1),
             "roofline": {"bound": "mfma", "achieved": round((ops8 + opsb) / (us * 1e-6) / 1e12, 1),
                          "peak": round((ops8 + opsb) / t_roof / 1e12, 1), "unit": "TFLOP/s",
                          "frac": round(t_roof / (us * 1e-6), 4), "traffic": None,
                          "ops_int8_fp8": ops8, "ops_bf16": opsb,
-                         "peak_basis": "int8/fp8 5.0 POP/s and bf16 2.5 PFLOP/s dense, blended by op mix"}}
+                         "peak_basis": basis}}
 
 
 def cpu_baseline(args, G, bytes_per_head):
@@ -345,8 +352,10 @@ def main():
     if args.only_prefill:
         gen = torch.Generator(device=dev)
         gen.manual_seed(args.seed)
-        rows = {f"prefill_{n}": bench_prefill(torch, hq, gen, dev, n)
-                for n in [int(x) for x in args.prefill_lens.split(",") if x]}
+        rows = {}
+        for n in [int(x) for x in args.prefill_lens.split(",") if x]:
+            rows[f"prefill_{n}"] = bench_prefill(torch, hq, gen, dev, n)
+            rows[f"prefill_mx_{n}"] = bench_prefill(torch, hq, gen, dev, n, bulk="mxfp4")
         print(json.dumps({"rows": rows}), flush=True)
         return
     B, Hq, Hkv, L = args.batch, args.hq, args.hkv, args.ctx
@@ -451,6 +460,9 @@ def main():
         for n in [int(x) for x in args.prefill_lens.split(",") if x]:
             rows[f"prefill_{n}"] = bench_prefill(torch, hq, gen, dev, n)
             print(f"[bench] prefill N={n}: {rows[f'prefill_{n}']['us_per_call']} us", file=sys.stderr, flush=True)
+            rows[f"prefill_mx_{n}"] = bench_prefill(torch, hq, gen, dev, n, bulk="mxfp4")
+            print(f"[bench] prefill mxfp4 N={n}: {rows[f'prefill_mx_{n}']['us_per_call']} us", file=sys.stderr,
+                  flush=True)
         rows["selector"] = bench_selector(torch, hq, gen, dev)
         line["rows"] = rows
     if not args.no_cpu_baseline:

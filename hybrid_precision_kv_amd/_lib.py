@@ -16,7 +16,8 @@ BUFFERS = ["int4", "slot_pos", "a_k", "a_v", "a_pos", "s_k", "s_v", "w_k", "w_v"
 
 # every symbol include/hyq.h declares
 EXPORTS = ["hyq_status_string", "hyq_cache_buffer_bytes", "hyq_workspace_bytes", "hyq_quantize_kv",
-           "hyq_append_token", "hyq_select_vlines", "hyq_decode_attn", "hyq_prefill_attn"]
+           "hyq_append_token", "hyq_select_vlines", "hyq_decode_attn", "hyq_prefill_attn",
+           "hyq_prefill_attn_mx"]
 
 
 class HyqShape(C.Structure):
@@ -68,6 +69,8 @@ def load() -> C.CDLL:
     lib.hyq_decode_attn.argtypes = [C.POINTER(HyqCache), vp, vp, i32, vp, sz, vp]
     lib.hyq_prefill_attn.restype = C.c_int
     lib.hyq_prefill_attn.argtypes = [C.POINTER(HyqShape), vp, vp, vp, i32, vp, i32, vp, vp, sz, vp]
+    lib.hyq_prefill_attn_mx.restype = C.c_int
+    lib.hyq_prefill_attn_mx.argtypes = [C.POINTER(HyqShape), vp, vp, vp, i32, vp, i32, vp, vp, sz, vp]
     _lib = lib
     return lib
 

@@ -234,9 +234,12 @@ def prefill_workspace(shape: Shape, N: int, device=None) -> torch.Tensor:
 
 def prefill_attn(shape: Shape, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                  anchors: torch.Tensor | None = None, out: torch.Tensor | None = None,
-                 ws: torch.Tensor | None = None) -> torch.Tensor:
-    """Hybrid prefill attention for one sequence (hyq_prefill_attn); fp32 out [Hq][N][128].
+                 ws: torch.Tensor | None = None, bulk: str = "int8") -> torch.Tensor:
+    """Hybrid prefill attention for one sequence; fp32 out [Hq][N][128].  ``bulk`` picks the
+    bulk Q.K format: "int8" (hyq_prefill_attn) or "mxfp4" (hyq_prefill_attn_mx).
     ``ws`` (from ``prefill_workspace``) receives the quantized operands."""
+    if bulk not in ("int8", "mxfp4"):
+        raise ValueError(f"bulk: 'int8' or 'mxfp4', not {bulk!r}")
     lib = _lib.load()
     N = q.shape[1]
     _bf16(q, (shape.n_q_heads, N, D), "q")
@@ -255,7 +258,8 @@ def prefill_attn(shape: Shape, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor
     if ws is None:
         ws = prefill_workspace(shape, N, q.device)
     s = shape.c()
-    check("hyq_prefill_attn", lib.hyq_prefill_attn(C.byref(s), _ptr(q), _ptr(k), _ptr(v), N,
-                                                   _ptr(anchors if n_anchor else None), n_anchor, _ptr(out),
-                                                   _ptr(ws), ws.numel(), _stream()))
+    name = "hyq_prefill_attn" if bulk == "int8" else "hyq_prefill_attn_mx"
+    check(name, getattr(lib, name)(C.byref(s), _ptr(q), _ptr(k), _ptr(v), N,
+                                   _ptr(anchors if n_anchor else None), n_anchor, _ptr(out),
+                                   _ptr(ws), ws.numel(), _stream()))
     return out

@@ -387,9 +387,12 @@ int hyq_select_vlines(const hyq_shape_t* shape, hyq_cache_t* cache, const void* 
   return HYQ_OK;
 }
 
-int hyq_prefill_attn(const hyq_shape_t* shape, const void* q, const void* k, const void* v, int32_t len,
-                     const int32_t* anchors, int32_t n_anchor, float* o, void* ws, size_t ws_bytes,
-                     hipStream_t stream) {
+}  // extern "C"
+
+// Both prefill entry points: argument checks, workspace carving, the launch sequence.
+static int prefill_common(const hyq_shape_t* shape, const void* q, const void* k, const void* v, int32_t len,
+                          const int32_t* anchors, int32_t n_anchor, float* o, void* ws, size_t ws_bytes,
+                          hipStream_t stream, int bulk) {
   int st = check_shape(shape);
   if (st) return st;
   if (shape->batch != 1) return HYQ_ERR_UNSUPPORTED;
@@ -425,8 +428,23 @@ int hyq_prefill_attn(const hyq_shape_t* shape, const void* q, const void* k, con
   p.ka16 = (uint16_t*)(wb + w.ka16);
   p.va16 = (uint16_t*)(wb + w.va16);
   p.n_anchor_pad = (n_anchor + 63) / 64 * 64;
+  p.bulk = bulk;
   if (hyq::launch_prefill(p, stream) != hipSuccess) return HYQ_ERR_HIP;
   return HYQ_OK;
+}
+
+extern "C" {
+
+int hyq_prefill_attn(const hyq_shape_t* shape, const void* q, const void* k, const void* v, int32_t len,
+                     const int32_t* anchors, int32_t n_anchor, float* o, void* ws, size_t ws_bytes,
+                     hipStream_t stream) {
+  return prefill_common(shape, q, k, v, len, anchors, n_anchor, o, ws, ws_bytes, stream, 0);
+}
+
+int hyq_prefill_attn_mx(const hyq_shape_t* shape, const void* q, const void* k, const void* v, int32_t len,
+                        const int32_t* anchors, int32_t n_anchor, float* o, void* ws, size_t ws_bytes,
+                        hipStream_t stream) {
+  return prefill_common(shape, q, k, v, len, anchors, n_anchor, o, ws, ws_bytes, stream, 1);
 }
 
 }  // extern "C"

@@ -98,6 +98,7 @@ struct PrefillParams {
   uint16_t* ka16;           // anchor K rows (list order), bf16
   uint16_t* va16;           // anchor V^T (list order), bf16, operand order
   int n_anchor_pad;         // n_anchor rounded up to 64 (rows of ka16 / va16 written)
+  int bulk;                 // bulk Q.K^T format: 0 INT8 codes, 1 MXFP4 (codes in the q8 / k8 sections)
 };
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream);
 

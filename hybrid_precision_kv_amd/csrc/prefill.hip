@@ -115,8 +115,37 @@ __global__ void __launch_bounds__(256) pf_bitmap_kernel(PrefillParams p) {
   }
 }
 
-// K: per (KV head, 64-key block) symmetric INT8 with the anchors left out of the maximum;
+// MXFP4 block of 32 values held by one lane: shared exponent e = floor(log2 max|x|) - 2
+// (E8M0 range, -127 for a zero block) and E2M1 codes of x * 2^-e (exact scaling; the
+// hardware conversion rounds to nearest even and saturates at 6), element i in nibble i of
+// the 16 bytes (low nibble first).  Returns e.
+__device__ inline int mxfp4_block(const float (&x)[32], u32x4& codes) {
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(x[i]));
+  int ex = 0;
+  (void)frexpf(amax, &ex);  // amax = f 2^ex, f in [0.5, 1): floor(log2 amax) = ex - 1
+  const int e = amax == 0.0f ? -127 : min(127, max(-127, ex - 3));
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    uint32_t w = 0;
+#define HYQ_FP4_PAIR(SEL)                                                                       \
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, __builtin_amdgcn_ldexpf(x[8 * d + 2 * SEL], -e), \
+                                               __builtin_amdgcn_ldexpf(x[8 * d + 2 * SEL + 1], -e), 1.0f, SEL)
+    HYQ_FP4_PAIR(0);
+    HYQ_FP4_PAIR(1);
+    HYQ_FP4_PAIR(2);
+    HYQ_FP4_PAIR(3);
+#undef HYQ_FP4_PAIR
+    codes[d] = w;
+  }
+  return e;
+}
+
+// K: per (KV head, 64-key block) symmetric INT8 with the anchors left out of the maximum
+// (BULK 0), or MXFP4 per key and 32-channel block (BULK 1: every row, anchors included);
 // V: per-channel maximum of |V| over the block's non-anchor keys.
+template <int BULK>
 __global__ void __launch_bounds__(256) pf_kquant_kernel(PrefillParams p) {
   __shared__ float red[4];
   __shared__ float vt[64][129];
@@ -125,11 +154,12 @@ __global__ void __launch_bounds__(256) pf_kquant_kernel(PrefillParams p) {
   const int key = blk * KBLK + row;
   const int nw = p.Npad >> 5, nb = p.Npad >> 6;
   const uint32_t word = p.abits[(size_t)h * nw + (key >> 5)];
-  const bool live = key < p.N && !((word >> (key & 31)) & 1u);
+  const bool inside = key < p.N;
+  const bool live = inside && !((word >> (key & 31)) & 1u);
   float kx[32], vx[32];
 #pragma unroll
   for (int e = 0; e < 32; ++e) { kx[e] = 0.0f; vx[e] = 0.0f; }
-  if (live) {
+  if (inside) {
     const u32x4* ks = (const u32x4*)(p.k + ((size_t)h * p.N + key) * D + 32 * qd);
     const u32x4* vs = (const u32x4*)(p.v + ((size_t)h * p.N + key) * D + 32 * qd);
 #pragma unroll
@@ -138,35 +168,45 @@ __global__ void __launch_bounds__(256) pf_kquant_kernel(PrefillParams p) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         kx[8 * c + 2 * e] = bf_lo(a[e]); kx[8 * c + 2 * e + 1] = bf_hi(a[e]);
-        vx[8 * c + 2 * e] = bf_lo(b[e]); vx[8 * c + 2 * e + 1] = bf_hi(b[e]);
+        vx[8 * c + 2 * e] = live ? bf_lo(b[e]) : 0.0f; vx[8 * c + 2 * e + 1] = live ? bf_hi(b[e]) : 0.0f;
       }
     }
   }
-  float amax = 0.0f;
-#pragma unroll
-  for (int e = 0; e < 32; ++e) amax = fmaxf(amax, fabsf(kx[e]));
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) amax = fmaxf(amax, shfl_xor_f(amax, o));
-  if ((t & 63) == 0) red[t >> 6] = amax;
 #pragma unroll
   for (int e = 0; e < 32; ++e) vt[row][32 * qd + e] = fabsf(vx[e]);
-  __syncthreads();
-  amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  const float s = __fdiv_rn(amax, 127.0f);
-  // operand order: dim 32 qd + 8 jj + e  ->  byte 64 (qd >> 1) + 16 jj + 8 (qd & 1) + e, and
-  // 16-byte chunk k = 4 (qd >> 1) + jj of the row at [tile][chunk][key in tile][16]
-  int8_t* dst = p.k8 + ((size_t)h * nb + blk) * 8192 + (4 * (qd >> 1)) * 1024 + row * 16 + 8 * (qd & 1);
+  uint8_t* tile = (uint8_t*)p.k8 + ((size_t)h * nb + blk) * 8192;
+  if (BULK == 1) {
+    // codes of channel block qd of this key: [block][key][16 B]; scale bytes [block][key%16][key/16]
+    u32x4 codes;
+    const int e = mxfp4_block(kx, codes);
+    *(u32x4*)(tile + (qd * 64 + row) * 16) = codes;
+    tile[4096 + (qd * 16 + (row & 15)) * 4 + (row >> 4)] = (uint8_t)(e + 127);
+    __syncthreads();
+  } else {
+    float amax = 0.0f;
 #pragma unroll
-  for (int jj = 0; jj < 4; ++jj) {
-    uint32_t w0 = 0, w1 = 0;
+    for (int e = 0; e < 32; ++e) amax = fmaxf(amax, live ? fabsf(kx[e]) : 0.0f);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      w0 |= (uint32_t)(int8_code(kx[8 * jj + e], s) & 0xff) << (8 * e);
-      w1 |= (uint32_t)(int8_code(kx[8 * jj + 4 + e], s) & 0xff) << (8 * e);
+    for (int o = 32; o >= 1; o >>= 1) amax = fmaxf(amax, shfl_xor_f(amax, o));
+    if ((t & 63) == 0) red[t >> 6] = amax;
+    __syncthreads();
+    amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    const float s = __fdiv_rn(amax, 127.0f);
+    // operand order: dim 32 qd + 8 jj + e  ->  byte 64 (qd >> 1) + 16 jj + 8 (qd & 1) + e, and
+    // 16-byte chunk k = 4 (qd >> 1) + jj of the row at [tile][chunk][key in tile][16]
+    uint8_t* dst = tile + (4 * (qd >> 1)) * 1024 + row * 16 + 8 * (qd & 1);
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      uint32_t w0 = 0, w1 = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        w0 |= (uint32_t)(int8_code(live ? kx[8 * jj + e] : 0.0f, s) & 0xff) << (8 * e);
+        w1 |= (uint32_t)(int8_code(live ? kx[8 * jj + 4 + e] : 0.0f, s) & 0xff) << (8 * e);
+      }
+      *(uint2*)(dst + 1024 * jj) = make_uint2(w0, w1);
     }
-    *(uint2*)(dst + 1024 * jj) = make_uint2(w0, w1);
+    if (t == 0) p.sk[(size_t)h * nb + blk] = s;
   }
-  if (t == 0) p.sk[(size_t)h * nb + blk] = s;
   if (t < D) {
     float m = 0.0f;
     for (int r = 0; r < 64; ++r) m = fmaxf(m, vt[r][t]);
@@ -299,38 +339,41 @@ __device__ inline void row_update(const Ctx& c, RowState& st, const bool (&valid
   }
 }
 
-// Quantized tile t: INT8 K codes of keys [64 t, 64 t + 64) ([chunk][key][16] as stored), the
-// tile's E4M3 V codes (as stored) and its anchor words.  fetch: global -> registers (issued
-// ahead of use), store: registers -> LDS.
+// Quantized tile t: K codes of keys [64 t, 64 t + 64) as stored (INT8: [chunk][key][16],
+// 8 KB; MXFP4: [block][key][16] codes, 4 KB, then 256 scale bytes), the tile's E4M3 V codes
+// (as stored) and its anchor words.  fetch: global -> registers (issued ahead of use),
+// store: registers -> LDS.
 struct TileQRegs {
   u32x4 k[2], v[2];
   uint32_t w0, w1;  // anchor bitmap words of the tile
-  float sk;         // K scale of the tile
+  float sk;         // K scale of the tile (INT8)
 };
+template <int BULK>
 __device__ inline void fetch_tile_q(const PrefillParams& p, const Ctx& c, int t, TileQRegs& r) {
   const uint32_t* ab = p.abits + (size_t)c.hk * (c.Npad >> 5) + 2 * t;
   r.w0 = ab[0];
   r.w1 = ab[1];
-  r.sk = p.sk[(size_t)c.hk * c.nb64 + t];
+  if (BULK == 0) r.sk = p.sk[(size_t)c.hk * c.nb64 + t];
   const size_t tile = ((size_t)c.hk * c.nb64 + t) * 8192;
   const int8_t* kt = p.k8 + tile;
   const uint8_t* vt = p.v8 + tile;
+  r.k[0] = *(const u32x4*)(kt + 16 * c.tid);
+  if (BULK == 0) r.k[1] = *(const u32x4*)(kt + 16 * (c.tid + 256));
+  else if (c.tid < 16) r.k[1] = *(const u32x4*)(kt + 4096 + 16 * c.tid);
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    r.k[i] = *(const u32x4*)(kt + 16 * (c.tid + 256 * i));
-    r.v[i] = *(const u32x4*)(vt + 16 * (c.tid + 256 * i));
-  }
+  for (int i = 0; i < 2; ++i) r.v[i] = *(const u32x4*)(vt + 16 * (c.tid + 256 * i));
 }
+template <int BULK>
 __device__ inline void store_tile_q(const Ctx& c, uint8_t* lds, const TileQRegs& r) {
+  *(u32x4*)(lds + 16 * c.tid) = r.k[0];
+  if (BULK == 0) *(u32x4*)(lds + 16 * (c.tid + 256)) = r.k[1];
+  else if (c.tid < 16) *(u32x4*)(lds + 4096 + 16 * c.tid) = r.k[1];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int ch = c.tid + 256 * i;
-    *(u32x4*)(lds + 16 * ch) = r.k[i];
-    *(u32x4*)(lds + LDS_QV + 16 * ch) = r.v[i];
-  }
+  for (int i = 0; i < 2; ++i) *(u32x4*)(lds + LDS_QV + 16 * (c.tid + 256 * i)) = r.v[i];
   if (c.tid < 64) {  // anchor mask of key tid, built once per tile for every wave
     const uint32_t word = c.tid < 32 ? r.w0 : r.w1;
-    *(int*)(lds + LDS_QBIAS + 4 * c.tid) = ((word >> (c.tid & 31)) & 1u) ? NEG_DOT : 0;
+    const bool anchor = (word >> (c.tid & 31)) & 1u;
+    *(int*)(lds + LDS_QBIAS + 4 * c.tid) = BULK == 0 ? (anchor ? NEG_DOT : 0) : (anchor ? (int)0xff800000u : 0);
   }
 }
 
@@ -350,43 +393,79 @@ __device__ inline void load_tile_bf(const Ctx& c, uint8_t* lds, const uint16_t* 
   }
 }
 
+// Q operand of the bulk segment, held in registers for the whole segment: INT8 codes
+// (qi[qb][s] = bytes 64 s + 16 j of query row 16 qb + l16), or MXFP4 codes of channel block j
+// of that row (q4[qb]) with the E8M0 scale bytes of both rows in qs[qb] (byte 0).
+struct QOps {
+  i32x4 qi[2][2];
+  u32x4 q4[2];
+  uint32_t qs[2];
+};
+template <int BULK>
+struct BulkT;
+template <>
+struct BulkT<0> {
+  typedef i32x4 S;  // exact INT8 dot products
+};
+template <>
+struct BulkT<1> {
+  typedef f32x4 S;  // MX dot products (block scales applied by the MFMA)
+};
+
 // Scores of one quantized tile (or of its 16-key block kb) for the wave's 32 queries:
-// S^T = K . Q^T on INT8 codes (Q codes in registers: qi[qb][s] = bytes 64 s + 16 j of query
-// row 16 qb + l16), with the masked keys (anchors; on an EDGE tile also j > i - 128) pushed
-// to NEG_DOT through the MFMA's C input.
-template <bool EDGE>
-__device__ inline void qk_block_q(const Ctx& c, const uint8_t* buf, const i32x4 (*qi)[2], int t, int kb,
-                                  i32x4 (&S2)[2][4]) {
-  const i32x4 kf0 = *(const i32x4*)(buf + (c.j * 64 + 16 * kb + c.l16) * 16);
-  const i32x4 kf1 = *(const i32x4*)(buf + ((4 + c.j) * 64 + 16 * kb + c.l16) * 16);
-  const i32x4 bias = *(const i32x4*)(buf + LDS_QBIAS + 4 * (16 * kb + 4 * c.j));  // keys 16kb+4j+r
+// S^T = K . Q^T on INT8 codes, or on MXFP4 codes with their E8M0 scales, with the masked keys
+// (anchors; on an EDGE tile also j > i - 128) pushed to NEG_DOT / -inf through the MFMA's C
+// input.
+template <int BULK, bool EDGE>
+__device__ inline void qk_block_q(const Ctx& c, const uint8_t* buf, const QOps& q, int t, int kb,
+                                  typename BulkT<BULK>::S (&S2)[2][4]) {
+  typedef typename BulkT<BULK>::S S;
+  const S bias = *(const S*)(buf + LDS_QBIAS + 4 * (16 * kb + 4 * c.j));  // keys 16kb+4j+r
+  S acc[2];
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
-    i32x4 acc = bias;
+    acc[qb] = bias;
     if (EDGE) {
       const int row = c.r0w + 16 * qb + c.l16;
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        if (64 * t + 16 * kb + 4 * c.j + r > row - WIN) acc[r] = NEG_DOT;
+        if (64 * t + 16 * kb + 4 * c.j + r > row - WIN) acc[qb][r] = BULK == 0 ? NEG_DOT : -INFINITY;
     }
-    S2[qb][kb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(kf0, qi[qb][0], acc, 0, 0, 0);
   }
+  if constexpr (BULK == 0) {
+    const i32x4 kf0 = *(const i32x4*)(buf + (c.j * 64 + 16 * kb + c.l16) * 16);
+    const i32x4 kf1 = *(const i32x4*)(buf + ((4 + c.j) * 64 + 16 * kb + c.l16) * 16);
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb)
-    S2[qb][kb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(kf1, qi[qb][1], S2[qb][kb], 0, 0, 0);
-}
-template <bool EDGE>
-__device__ inline void qk_tile_q(const Ctx& c, const uint8_t* buf, const i32x4 (&qi)[2][2], int t,
-                                 i32x4 (&S2)[2][4]) {
+    for (int qb = 0; qb < 2; ++qb) S2[qb][kb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(kf0, q.qi[qb][0], acc[qb], 0, 0, 0);
 #pragma unroll
-  for (int kb = 0; kb < 4; ++kb) qk_block_q<EDGE>(c, buf, qi, t, kb, S2);
+    for (int qb = 0; qb < 2; ++qb)
+      S2[qb][kb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(kf1, q.qi[qb][1], S2[qb][kb], 0, 0, 0);
+  } else {
+    // A: codes of key 16 kb + l16, channel block j; its scale is byte kb of the lane's dword
+    const u32x4 kc = *(const u32x4*)(buf + (c.j * 64 + 16 * kb + c.l16) * 16);
+    const uint32_t ksc = *(const uint32_t*)(buf + 4096 + (c.j * 16 + c.l16) * 4) >> (8 * kb);
+    const i32x8 a = {(int)kc[0], (int)kc[1], (int)kc[2], (int)kc[3], 0, 0, 0, 0};
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const i32x8 bq = {(int)q.q4[qb][0], (int)q.q4[qb][1], (int)q.q4[qb][2], (int)q.q4[qb][3], 0, 0, 0, 0};
+      S2[qb][kb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, bq, acc[qb], 4, 4, 0, (int)ksc, 0,
+                                                                    (int)q.qs[qb]);
+    }
+  }
 }
-__device__ inline void qk_tile(const Ctx& c, const uint8_t* buf, const i32x4 (&qi)[2][2], int t,
-                               i32x4 (&S2)[2][4]) {
+template <int BULK, bool EDGE>
+__device__ inline void qk_tile_q(const Ctx& c, const uint8_t* buf, const QOps& q, int t,
+                                 typename BulkT<BULK>::S (&S2)[2][4]) {
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) qk_block_q<BULK, EDGE>(c, buf, q, t, kb, S2);
+}
+template <int BULK>
+__device__ inline void qk_tile(const Ctx& c, const uint8_t* buf, const QOps& q, int t,
+                               typename BulkT<BULK>::S (&S2)[2][4]) {
   if (64 * t + 63 <= c.r0w - WIN)  // every key of the tile is at least 128 before every row
-    qk_tile_q<false>(c, buf, qi, t, S2);
+    qk_tile_q<BULK, false>(c, buf, q, t, S2);
   else
-    qk_tile_q<true>(c, buf, qi, t, S2);
+    qk_tile_q<BULK, true>(c, buf, q, t, S2);
 }
 
 // Online softmax of one quantized tile's scores: the row-state max update (rescaling the
@@ -396,24 +475,42 @@ __device__ inline void qk_tile(const Ctx& c, const uint8_t* buf, const i32x4 (&q
 // as the exponentials free them, so its MFMAs run under this softmax's VALU work.
 // c2 = s_Q s_K alpha log2(e) (wave-uniform).  Below C2_FAST_MIN a masked score is not
 // guaranteed to underflow exp2, so the masked entries are zeroed explicitly.
-template <bool TINY, bool FUSE_QK = false>
-__device__ inline void softmax_tile_q(const Ctx& c, i32x4 (&S2)[2][4], float c2, RowState& st, i32x8& pk,
-                                      const uint8_t* qkbuf = nullptr, const i32x4 (*qi)[2] = nullptr, int tq = 0) {
+template <int BULK, bool TINY, bool FUSE_QK = false>
+__device__ inline void softmax_tile_q(const Ctx& c, typename BulkT<BULK>::S (&S2)[2][4], float c2, RowState& st,
+                                      i32x8& pk, const uint8_t* qkbuf = nullptr, const QOps* q = nullptr,
+                                      int tq = 0) {
   bool valid[2];
   float tmax[2], muse[2];
-  int mi[2];
+  if constexpr (BULK == 0) {
+    int mi[2];
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    mi[qb] = NEG_DOT;
+    for (int qb = 0; qb < 2; ++qb) {
+      mi[qb] = NEG_DOT;
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-      mi[qb] = max(mi[qb], max(max(S2[qb][kb][0], S2[qb][kb][1]), max(S2[qb][kb][2], S2[qb][kb][3])));
-  }
-  col4_max2_i(mi[0], mi[1]);
+      for (int kb = 0; kb < 4; ++kb)
+        mi[qb] = max(mi[qb], max(max(S2[qb][kb][0], S2[qb][kb][1]), max(S2[qb][kb][2], S2[qb][kb][3])));
+    }
+    col4_max2_i(mi[0], mi[1]);
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    valid[qb] = mi[qb] > NEG_DOT / 2;
-    tmax[qb] = (float)mi[qb] * c2;
+    for (int qb = 0; qb < 2; ++qb) {
+      valid[qb] = mi[qb] > NEG_DOT / 2;
+      tmax[qb] = (float)mi[qb] * c2;
+    }
+  } else {
+    float mf[2];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      mf[qb] = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+        mf[qb] = fmaxf(mf[qb], fmaxf(fmaxf(S2[qb][kb][0], S2[qb][kb][1]), fmaxf(S2[qb][kb][2], S2[qb][kb][3])));
+    }
+    col4_max2_f(mf[0], mf[1]);
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      valid[qb] = mf[qb] > -INFINITY;
+      tmax[qb] = mf[qb] * c2;
+    }
   }
   row_update(c, st, valid, tmax, LOG2_448, muse);
   // w[2 kb + qb]: codes of block qb, keys 16 kb + 4 j + r -- the row-sum B operand as is, and
@@ -427,14 +524,14 @@ __device__ inline void softmax_tile_q(const Ctx& c, i32x4 (&S2)[2][4], float c2,
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         pv[r] = __builtin_amdgcn_exp2f(__builtin_fmaf((float)S2[qb][kb][r], c2, -muse[qb]));
-        if (TINY && S2[qb][kb][r] <= NEG_DOT / 2) pv[r] = 0.0f;
+        if (BULK == 0 && TINY && S2[qb][kb][r] <= NEG_DOT / 2) pv[r] = 0.0f;
       }
       // the first conversion's high half is overwritten by the second: any old value will do
       const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(pv[0], pv[1], __float_as_int(pv[1]), false);
       w[2 * kb + qb] = __builtin_amdgcn_cvt_pk_fp8_f32(pv[2], pv[3], lo, true);
     }
     // block kb's score registers are free: the next tile's (interior) block kb goes there
-    if (FUSE_QK) qk_block_q<false>(c, qkbuf, qi, tq, kb, S2);
+    if (FUSE_QK) qk_block_q<BULK, false>(c, qkbuf, *q, tq, kb, S2);
   }
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb)
@@ -554,93 +651,98 @@ __device__ inline void compute_tile_bf(const PrefillParams& p, const Ctx& c, con
 // is due and QK^T(t+2) is an interior tile the loop runs unrolled by four, so the buffer
 // offsets are constants and no step is conditional; the rest runs one conditional step at a
 // time.
-template <bool TINY>
+// exp2 scale of a tile's scores: s_Q s_K alpha log2(e) for INT8 codes, alpha log2(e) for MX
+// dots (already scaled)
+template <int BULK, bool TINY>
 __device__ inline float tile_c2(float sq_u, float sk) {
+  if (BULK == 1) return AL2;
   float c2 = uniform_f(sq_u * sk * AL2);
   if (TINY) c2 = c2 > 0.0f ? c2 : 1.0f;  // a zero scale means every valid dot is 0
   return c2;
 }
 
+template <int BULK>
 struct PipeA {
   TileQRegs pre;      // tile in flight from global memory
   float sk1, sk2, sk3;  // K scales of tiles t+1, t+2, t+3
-  i32x4 S2[2][4];     // scores of tile t+1
+  typename BulkT<BULK>::S S2[2][4];  // scores of tile t+1
   i32x8 pk;           // P codes of tile t
 };
 
-template <bool TINY, int PH>
-__device__ inline void segment_a_main(const PrefillParams& p, const Ctx& c, uint8_t* lds, const i32x4 (&qi)[2][2],
-                                      int nA, float sq_u, int t, PipeA& a, RowState& st) {
-  store_tile_q(c, lds + ((PH + 3) % RING) * LDS_QBUF, a.pre);
+template <int BULK, bool TINY, int PH>
+__device__ inline void segment_a_main(const PrefillParams& p, const Ctx& c, uint8_t* lds, const QOps& q,
+                                      int nA, float sq_u, int t, PipeA<BULK>& a, RowState& st) {
+  store_tile_q<BULK>(c, lds + ((PH + 3) % RING) * LDS_QBUF, a.pre);
   a.sk3 = a.pre.sk;
-  fetch_tile_q(p, c, min(t + 4, nA - 1), a.pre);  // past the end: loaded, never stored
+  fetch_tile_q<BULK>(p, c, min(t + 4, nA - 1), a.pre);  // past the end: loaded, never stored
   pv_tile_q(c, lds + PH * LDS_QBUF, a.pk, st);
-  softmax_tile_q<TINY, true>(c, a.S2, tile_c2<TINY>(sq_u, a.sk1), st, a.pk, lds + ((PH + 2) % RING) * LDS_QBUF,
-                             qi, t + 2);
+  softmax_tile_q<BULK, TINY, true>(c, a.S2, tile_c2<BULK, TINY>(sq_u, a.sk1), st, a.pk,
+                                   lds + ((PH + 2) % RING) * LDS_QBUF, &q, t + 2);
   __syncthreads();
   a.sk1 = a.sk2;
   a.sk2 = a.sk3;
 }
 
-template <bool TINY>
-__device__ inline void segment_a_tail(const PrefillParams& p, const Ctx& c, uint8_t* lds, const i32x4 (&qi)[2][2],
-                                      int nA, int nAw, float sq_u, int t, PipeA& a, RowState& st) {
+template <int BULK, bool TINY>
+__device__ inline void segment_a_tail(const PrefillParams& p, const Ctx& c, uint8_t* lds, const QOps& q,
+                                      int nA, int nAw, float sq_u, int t, PipeA<BULK>& a, RowState& st) {
   if (t + 3 < nA) {
-    store_tile_q(c, lds + ((t + 3) % RING) * LDS_QBUF, a.pre);
+    store_tile_q<BULK>(c, lds + ((t + 3) % RING) * LDS_QBUF, a.pre);
     a.sk3 = a.pre.sk;
   }
-  if (t + 4 < nA) fetch_tile_q(p, c, t + 4, a.pre);
+  if (t + 4 < nA) fetch_tile_q<BULK>(p, c, t + 4, a.pre);
   if (t < nAw) pv_tile_q(c, lds + (t % RING) * LDS_QBUF, a.pk, st);
-  if (t + 1 < nAw) softmax_tile_q<TINY>(c, a.S2, tile_c2<TINY>(sq_u, a.sk1), st, a.pk);
-  if (t + 2 < nAw) qk_tile(c, lds + ((t + 2) % RING) * LDS_QBUF, qi, t + 2, a.S2);
+  if (t + 1 < nAw) softmax_tile_q<BULK, TINY>(c, a.S2, tile_c2<BULK, TINY>(sq_u, a.sk1), st, a.pk);
+  if (t + 2 < nAw) qk_tile<BULK>(c, lds + ((t + 2) % RING) * LDS_QBUF, q, t + 2, a.S2);
   __syncthreads();
   a.sk1 = a.sk2;
   a.sk2 = a.sk3;
 }
 
-template <bool TINY>
-__device__ inline void segment_a(const PrefillParams& p, const Ctx& c, uint8_t* lds, const i32x4 (&qi)[2][2],
+template <int BULK, bool TINY>
+__device__ inline void segment_a(const PrefillParams& p, const Ctx& c, uint8_t* lds, const QOps& q,
                                  int nA, float sq_u, RowState& st) {
   const int nAw = c.r0w + 31 - WIN >= 0 ? ((c.r0w + 31 - WIN) >> 6) + 1 : 0;
   // interior tiles (every key at least 128 before every row of the wave): 64 t + 63 <= r0w - 128
   const int nInt = c.r0w - WIN - 63 >= 0 ? ((c.r0w - WIN - 63) >> 6) + 1 : 0;
   if (nA <= 0) return;
-  PipeA a;
+  PipeA<BULK> a;
   float sk0 = 0.0f;
   a.sk1 = a.sk2 = a.sk3 = 0.0f;
   __syncthreads();  // nothing else uses the tile buffers now
-  fetch_tile_q(p, c, 0, a.pre);
-  store_tile_q(c, lds, a.pre);
+  fetch_tile_q<BULK>(p, c, 0, a.pre);
+  store_tile_q<BULK>(c, lds, a.pre);
   sk0 = a.pre.sk;
   if (nA > 1) {
-    fetch_tile_q(p, c, 1, a.pre);
-    store_tile_q(c, lds + LDS_QBUF, a.pre);
+    fetch_tile_q<BULK>(p, c, 1, a.pre);
+    store_tile_q<BULK>(c, lds + LDS_QBUF, a.pre);
     a.sk1 = a.pre.sk;
   }
   if (nA > 2) {
-    fetch_tile_q(p, c, 2, a.pre);
-    store_tile_q(c, lds + 2 * LDS_QBUF, a.pre);
+    fetch_tile_q<BULK>(p, c, 2, a.pre);
+    store_tile_q<BULK>(c, lds + 2 * LDS_QBUF, a.pre);
     a.sk2 = a.pre.sk;
   }
-  if (nA > 3) fetch_tile_q(p, c, 3, a.pre);
+  if (nA > 3) fetch_tile_q<BULK>(p, c, 3, a.pre);
   __syncthreads();
   // prologue: scores and P codes of tile 0, scores of tile 1
   if (nAw > 0) {
-    qk_tile(c, lds, qi, 0, a.S2);
-    softmax_tile_q<TINY>(c, a.S2, tile_c2<TINY>(sq_u, sk0), st, a.pk);
+    qk_tile<BULK>(c, lds, q, 0, a.S2);
+    softmax_tile_q<BULK, TINY>(c, a.S2, tile_c2<BULK, TINY>(sq_u, sk0), st, a.pk);
   }
-  if (1 < nAw) qk_tile(c, lds + LDS_QBUF, qi, 1, a.S2);
+  if (1 < nAw) qk_tile<BULK>(c, lds + LDS_QBUF, q, 1, a.S2);
   int t = 0;
   // group t .. t+3: stores up to tile t+6 < nA, QK^T up to tile t+5 interior (< nInt <= nAw)
   for (; t + 6 < nA && t + 5 < nInt; t += RING) {
-    segment_a_main<TINY, 0>(p, c, lds, qi, nA, sq_u, t, a, st);
-    segment_a_main<TINY, 1>(p, c, lds, qi, nA, sq_u, t + 1, a, st);
-    segment_a_main<TINY, 2>(p, c, lds, qi, nA, sq_u, t + 2, a, st);
-    segment_a_main<TINY, 3>(p, c, lds, qi, nA, sq_u, t + 3, a, st);
+    segment_a_main<BULK, TINY, 0>(p, c, lds, q, nA, sq_u, t, a, st);
+    segment_a_main<BULK, TINY, 1>(p, c, lds, q, nA, sq_u, t + 1, a, st);
+    segment_a_main<BULK, TINY, 2>(p, c, lds, q, nA, sq_u, t + 2, a, st);
+    segment_a_main<BULK, TINY, 3>(p, c, lds, q, nA, sq_u, t + 3, a, st);
   }
-  for (; t < nA; ++t) segment_a_tail<TINY>(p, c, lds, qi, nA, nAw, sq_u, t, a, st);
+  for (; t < nA; ++t) segment_a_tail<BULK, TINY>(p, c, lds, q, nA, nAw, sq_u, t, a, st);
 }
 
+template <int BULK>
 __global__ void __launch_bounds__(256, 2) pf_attn_kernel(PrefillParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[LDS_TOTAL];
   __shared__ int anc_s[64];
@@ -686,10 +788,46 @@ __global__ void __launch_bounds__(256, 2) pf_attn_kernel(PrefillParams p) {
   c.Npad = p.Npad;
   c.nb64 = p.Npad >> 6;
 
-  // ---- Q: bf16 operand fragments, block maximum, INT8 codes (also stored)
-  i32x4 qi[2][2];
-  float sq;
-  {
+  // ---- Q: INT8 codes (block maximum over the 64-row block, exchanged through LDS) or MXFP4
+  // codes of the lane's channel block; the codes are also stored in the workspace
+  QOps qo;
+  float sq = 0.0f;
+  if (c.tid == 0) {
+    // anchors some row of the workgroup may use: a <= r0 + 127 - 128
+    const int32_t* anc = p.anchors + (size_t)c.hk * p.n_anchor;
+    const int lim = r0 + WG_ROWS - 1 - WIN;
+    int lo = 0, hi = p.n_anchor;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (anc[mid] <= lim) lo = mid + 1; else hi = mid;
+    }
+    nb_anchor_s = lo;
+  }
+  if constexpr (BULK == 1) {
+    // lane (qb, l16, j): channels 32 j .. 32 j + 31 of row 16 qb + l16 -- one MX block
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const int row = c.r0w + 16 * qb + c.l16;
+      float x[32];
+#pragma unroll
+      for (int v4 = 0; v4 < 4; ++v4) {
+        const u32x4 w = row < c.N ? *(const u32x4*)(p.q + ((size_t)c.h * c.N + row) * D + 32 * c.j + 8 * v4)
+                                  : (u32x4){0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          x[8 * v4 + 2 * e] = bf_lo(w[e]);
+          x[8 * v4 + 2 * e + 1] = bf_hi(w[e]);
+        }
+      }
+      const int e = mxfp4_block(x, qo.q4[qb]);
+      qo.qs[qb] = (uint32_t)(e + 127);
+      // workspace row: codes of block j at bytes 16 j, scale byte at 64 + j
+      int8_t* qrow = p.q8 + ((size_t)c.h * c.Npad + row) * D;
+      *(u32x4*)(qrow + 16 * c.j) = qo.q4[qb];
+      qrow[64 + c.j] = (int8_t)(e + 127);
+    }
+    __syncthreads();
+  } else {
     u32x4 qf[2][4];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
@@ -710,17 +848,6 @@ __global__ void __launch_bounds__(256, 2) pf_attn_kernel(PrefillParams p) {
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) amax = fmaxf(amax, shfl_xor_f(amax, o));
     if (lane == 0) qmax[wave] = amax;
-    if (c.tid == 0) {
-      // anchors some row of the workgroup may use: a <= r0 + 127 - 128
-      const int32_t* anc = p.anchors + (size_t)c.hk * p.n_anchor;
-      const int lim = r0 + WG_ROWS - 1 - WIN;
-      int lo = 0, hi = p.n_anchor;
-      while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if (anc[mid] <= lim) lo = mid + 1; else hi = mid;
-      }
-      nb_anchor_s = lo;
-    }
     __syncthreads();
     sq = __fdiv_rn(fmaxf(qmax[wave], qmax[wave ^ 1]), 127.0f);
 #pragma unroll
@@ -738,11 +865,11 @@ __global__ void __launch_bounds__(256, 2) pf_attn_kernel(PrefillParams p) {
             w1 |= (uint32_t)(int8_code(bf_lo(x[2 + e]), sq) & 0xff) << (16 * e);
             w1 |= (uint32_t)(int8_code(bf_hi(x[2 + e]), sq) & 0xff) << (16 * e + 8);
           }
-          qi[qb][s8][2 * hh] = (int)w0;
-          qi[qb][s8][2 * hh + 1] = (int)w1;
+          qo.qi[qb][s8][2 * hh] = (int)w0;
+          qo.qi[qb][s8][2 * hh + 1] = (int)w1;
         }
         const int row = c.r0w + 16 * qb + c.l16;
-        *(i32x4*)(p.q8 + ((size_t)c.h * c.Npad + row) * D + 64 * s8 + 16 * c.j) = qi[qb][s8];
+        *(i32x4*)(p.q8 + ((size_t)c.h * c.Npad + row) * D + 64 * s8 + 16 * c.j) = qo.qi[qb][s8];
       }
     }
     if (lane == 0 && (wave & 1) == 0) p.sq[(size_t)c.h * c.nb64 + (c.r0w >> 6)] = sq;
@@ -759,8 +886,11 @@ __global__ void __launch_bounds__(256, 2) pf_attn_kernel(PrefillParams p) {
   const int lastA = r0 + WG_ROWS - 1 - WIN;
   const int nA = lastA >= 0 ? (lastA >> 6) + 1 : 0;
   // Masked INT8 scores underflow exp2 only when s_Q s_K is not tiny; the rare wave with a
-  // tiny product over its tiles runs the variant that zeroes them explicitly.
-  {
+  // tiny product over its tiles runs the variant that zeroes them explicitly.  MX scores are
+  // floats whose masked entries are -inf.
+  if constexpr (BULK == 1) {
+    segment_a<1, false>(p, c, lds, qo, nA, 0.0f, st);
+  } else {
     float m = INFINITY;
     for (int t = c.tid; t < nA; t += 256) m = fminf(m, p.sk[(size_t)c.hk * c.nb64 + t]);
 #pragma unroll
@@ -770,9 +900,9 @@ __global__ void __launch_bounds__(256, 2) pf_attn_kernel(PrefillParams p) {
     m = fminf(fminf(skmin[0], skmin[1]), fminf(skmin[2], skmin[3]));
     const float sq_u = uniform_f(sq);
     if (sq_u * m * AL2 >= C2_FAST_MIN)
-      segment_a<false>(p, c, lds, qi, nA, sq_u, st);
+      segment_a<0, false>(p, c, lds, qo, nA, sq_u, st);
     else
-      segment_a<true>(p, c, lds, qi, nA, sq_u, st);
+      segment_a<0, true>(p, c, lds, qo, nA, sq_u, st);
   }
   // acc holds sum E4M3(448 p) * code(V): scale to values
 #pragma unroll
@@ -836,12 +966,18 @@ __global__ void __launch_bounds__(256, 2) pf_attn_kernel(PrefillParams p) {
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream) {
   const int Hkv = p.Hkv;
   hipLaunchKernelGGL(pf_bitmap_kernel, dim3(Hkv), dim3(256), 0, stream, p);
-  hipLaunchKernelGGL(pf_kquant_kernel, dim3(p.Npad / KBLK, Hkv), dim3(256), 0, stream, p);
+  if (p.bulk == 1)
+    hipLaunchKernelGGL(pf_kquant_kernel<1>, dim3(p.Npad / KBLK, Hkv), dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL(pf_kquant_kernel<0>, dim3(p.Npad / KBLK, Hkv), dim3(256), 0, stream, p);
   hipLaunchKernelGGL(pf_vscale_kernel, dim3(Hkv), dim3(1024), 0, stream, p);
   hipLaunchKernelGGL(pf_vquant_kernel, dim3(p.Npad / 32, Hkv), dim3(128), 0, stream, p);
   if (p.n_anchor_pad > 0)
     hipLaunchKernelGGL(pf_agather_kernel, dim3(p.n_anchor_pad / 32, Hkv), dim3(128), 0, stream, p);
-  hipLaunchKernelGGL(pf_attn_kernel, dim3((p.Npad / WG_ROWS) * p.Hq), dim3(256), 0, stream, p);
+  if (p.bulk == 1)
+    hipLaunchKernelGGL(pf_attn_kernel<1>, dim3((p.Npad / WG_ROWS) * p.Hq), dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL(pf_attn_kernel<0>, dim3((p.Npad / WG_ROWS) * p.Hq), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 

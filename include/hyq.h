@@ -241,6 +241,24 @@ int hyq_prefill_attn(const hyq_shape_t* shape, const void* q, const void* k, con
                      int32_t len, const int32_t* anchors, int32_t n_anchor, float* o, void* ws,
                      size_t ws_bytes, hipStream_t stream);
 
+/* Hybrid prefill attention with a 4-bit bulk Q.K (HyQuant paper §4.2, the INT4/FP4 option for
+   the bulk operands): as hyq_prefill_attn in every argument, error and key partition, except
+   that the bulk Q.K uses MXFP4 (OCP Microscaling) operands instead of INT8:
+     Q and K (every row, anchors included), per row and 32-channel block: shared exponent
+        e = clamp(floor(log2 max|x|) - 2, -127, 127) (-127 for an all-zero block), codes
+        = E2M1(x * 2^-e) rounded to nearest even and saturated at +-6;
+     score = fp32(sum over blocks of 2^(eQ + eK) * dot(codes)) / sqrt(128).
+   P.V, V codes, s_V and the bf16 keys are as in hyq_prefill_attn.  Workspace sections as there,
+   with q8 and k8 reinterpreted and sq, sk left unwritten:
+     q8 row (128 bytes): byte 16 j + i/2 holds channel 32 j + i of block j (i even in the low
+        nibble), byte 64 + j the biased exponent e + 127 of block j, bytes 68.. unspecified;
+     k8 tile of 64 keys (8192 bytes): byte (j 64 + r) 16 + i/2 holds channel 32 j + i of key
+        64 T + r; byte 4096 + (j 16 + (r & 15)) 4 + (r >> 4) holds that key's block-j e + 127;
+        the rest unspecified. */
+int hyq_prefill_attn_mx(const hyq_shape_t* shape, const void* q, const void* k, const void* v,
+                        int32_t len, const int32_t* anchors, int32_t n_anchor, float* o, void* ws,
+                        size_t ws_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -152,3 +152,30 @@ def read_prefill_ws(ws: np.ndarray, Hq: int, Hkv: int, N: int, anchor_cap: int) 
                 sk=sec("sk", np.float32, Hkv * (Np // 64)).reshape(Hkv, Np // 64),
                 sv=sec("sv", np.float32, Hkv * D).reshape(Hkv, D),
                 abits=sec("abits", np.uint32, Hkv * (Np // 32)).reshape(Hkv, Np // 32))
+
+
+def _nibbles(b: np.ndarray) -> np.ndarray:
+    """[..., n] bytes -> [..., 2n] 4-bit codes, the low nibble first."""
+    out = np.empty(b.shape[:-1] + (2 * b.shape[-1],), np.uint8)
+    out[..., 0::2] = b & 0xF
+    out[..., 1::2] = b >> 4
+    return out
+
+
+def read_prefill_mx(ws: np.ndarray, Hq: int, Hkv: int, N: int, anchor_cap: int) -> dict:
+    """Decode the MXFP4 operands of hyq_prefill_attn_mx from its workspace (uint8 numpy):
+    q4 uint8 E2M1 codes [Hq][Np][128], qe int [Hq][Np][4] block exponents (stored e + 127),
+    k4 [Hkv][Np][128], ke [Hkv][Np][4]."""
+    o = prefill_ws_offsets(Hq, Hkv, N, anchor_cap)
+    Np = o["Np"]
+    qraw = ws[o["q8"]:o["q8"] + Hq * Np * D].reshape(Hq, Np, D)
+    q4 = _nibbles(qraw[:, :, :64])
+    qe = qraw[:, :, 64:68].astype(np.int64) - 127
+    # K tile of 64 keys: codes [block j][key r][16 B], then scale byte of (j, r) at
+    # 4096 + (16 j + (r & 15)) * 4 + (r >> 4)
+    kraw = ws[o["k8"]:o["k8"] + Hkv * Np * D].reshape(Hkv, Np // 64, 8192)
+    codes = kraw[:, :, :4096].reshape(Hkv, Np // 64, 4, 64, 16).transpose(0, 1, 3, 2, 4)
+    k4 = _nibbles(codes.reshape(Hkv, Np // 64, 64, 64)).reshape(Hkv, Np, D)
+    sc = kraw[:, :, 4096:4352].reshape(Hkv, Np // 64, 4, 16, 4)  # [j][r & 15][r >> 4]
+    ke = sc.transpose(0, 1, 4, 3, 2).reshape(Hkv, Np, 4).astype(np.int64) - 127
+    return dict(Np=Np, q4=q4, qe=qe, k4=k4, ke=ke)
