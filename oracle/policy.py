@@ -243,3 +243,47 @@ def select_dense(K_bits: np.ndarray, proxy_bits: np.ndarray, W: int = 128, pct_n
     k = k_rule(L, W, pct_num, pct_den)
     S = vertical_scores(nm.bf16_to_f32(np.asarray(proxy_bits).reshape(-1, D)), K, P)
     return topk_lower_index(S, k), S
+
+
+# ---------------------------------------------------------------- Alg. 1 taken literally
+def k_alg1(P: int, r_num: int = 5, r_den: int = 100) -> int:
+    """Anchor count as the HyQuant paper's Alg. 1 writes it: k = min(P, max(1, ceil(P r))) on
+    the P = L - W candidates (0 when P = 0), ratio r = r_num / r_den, integers only."""
+    if P <= 0:
+        return 0
+    return min(P, max(1, (P * r_num + r_den - 1) // r_den))
+
+
+def tail_query_mean(Q_bits: np.ndarray, W: int = 128) -> np.ndarray:
+    """The tail-query proxy of HyQuant paper Alg. 1: the mean of the last t = min(W, L_Q)
+    queries of each Q head.  Q_bits [H][L_Q][D] bf16 bits -> fp64 [H][D]."""
+    Q = nm.bf16_to_f32(Q_bits).astype(np.float64)
+    t = min(W, Q.shape[1])
+    return Q[:, Q.shape[1] - t:, :].mean(axis=1)
+
+
+def select_tail_mean(K_bits: np.ndarray, Q_bits: np.ndarray, W: int = 128, r_num: int = 5,
+                     r_den: int = 100, k: int | None = None):
+    """Vertical-token identification as HyQuant paper Alg. 1 writes it, for one sequence:
+    the candidates are the prefix [0, P), P = max(0, L_K - W) (empty when P = 0); each Q head
+    h scores them with raw logits S_h(j) = qbar_h . k_j (no softmax, no 1/sqrt(D)) of its
+    tail-query mean qbar_h against its KV head h // g (the GQA-native form); the set of each
+    Q head is its own top-k (ties to the lower position, ascending).
+    K_bits [Hkv][L_K][D], Q_bits [Hq][L_Q][D] (bf16 bits).  k: defaults to ``k_alg1(P)``.
+    Returns (idx int64 [Hq][k], S fp64 [Hq][P])."""
+    K = nm.bf16_to_f32(K_bits).astype(np.float64)
+    Hkv, L, D = K.shape
+    Hq = Q_bits.shape[0]
+    g = Hq // Hkv
+    P = max(0, L - W)
+    if k is None:
+        k = k_alg1(P, r_num, r_den)
+    qbar = tail_query_mean(Q_bits, W)
+    S = np.zeros((Hq, P))
+    for hk in range(Hkv):
+        # the g Q heads of KV head hk against its prefix keys: [g][D] x [D][P]
+        S[hk * g:(hk + 1) * g] = qbar[hk * g:(hk + 1) * g] @ K[hk, :P].T
+    idx = np.zeros((Hq, k), np.int64)
+    for h in range(Hq):
+        idx[h] = topk_lower_index(S[h], k)
+    return idx, S

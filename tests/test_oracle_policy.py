@@ -210,3 +210,80 @@ def test_promoted_positions_carry_bf16_of_dequant():
     c2 = pol.HybridCacheRef(g=2)
     c2.freeze(s.K, s.V, np.array([3]))
     assert np.array_equal(c2.stored_kv()[0][10], Kh1[10])
+
+
+# ----------------------------------------------------------------------------- Alg. 1 literal selector
+
+def test_k_alg1_closed_forms():
+    # Alg. 1: k = min(P, max(1, ceil(P r))), on the candidates, not on the context length
+    assert pol.k_alg1(0) == 0 and pol.k_alg1(-3) == 0
+    assert pol.k_alg1(896) == 45  # ceil(0.05 * 896) = ceil(44.8)
+    assert pol.k_alg1(900) == 45 and pol.k_alg1(901) == 46
+    assert pol.k_alg1(1) == 1 and pol.k_alg1(19) == 1 and pol.k_alg1(20) == 1 and pol.k_alg1(21) == 2
+    assert pol.k_alg1(7, 100, 100) == 7 and pol.k_alg1(7, 1, 1000) == 1
+    assert pol.k_alg1(32640, 5, 100) == 1632
+
+
+def _bits(rng, shape, scale=1.0):
+    return nm.f32_to_bf16((rng.standard_normal(shape) * scale).astype(np.float32))
+
+
+@pytest.mark.parametrize("LQ", [1, 50, 128, 129, 300])
+def test_tail_mean_scores_are_mean_of_tail_logits(LQ):
+    """Raw logits are linear in the proxy: qbar . k_j must equal the average over the tail
+    queries of q_i . k_j, computed here query by query with explicit loops; the tail is the
+    last min(128, L_Q) queries."""
+    rng = np.random.default_rng(LQ)
+    Hkv, g, L, D = 2, 2, 150, 8
+    K = _bits(rng, (Hkv, L, D))
+    Q = _bits(rng, (Hkv * g, LQ, D))
+    idx, S = pol.select_tail_mean(K, Q, W=128, k=5)
+    Kf, Qf = nm.bf16_to_f32(K), nm.bf16_to_f32(Q)
+    P = L - 128
+    t = min(128, LQ)
+    for h in range(Hkv * g):
+        for j in range(P):
+            tot = 0.0
+            for i in range(LQ - t, LQ):
+                tot += sum(float(Qf[h, i, d]) * float(Kf[h // g, j, d]) for d in range(D))
+            assert abs(S[h, j] - tot / t) <= 1e-12 * (1 + abs(tot))
+    # a query outside the tail changes nothing; one inside does
+    if LQ > 128:
+        Q2 = Q.copy()
+        Q2[:, LQ - 129] = _bits(rng, (Hkv * g, D), 10.0)
+        assert np.array_equal(pol.select_tail_mean(K, Q2, k=5)[1], S)
+    Q3 = Q.copy()
+    Q3[:, LQ - 1] = _bits(rng, (Hkv * g, D), 10.0)
+    assert not np.array_equal(pol.select_tail_mean(K, Q3, k=5)[1], S)
+
+
+def test_tail_mean_gqa_form_equals_repeated_kv():
+    """Alg. 1's GQA-native branch must give what the H = H_Q branch gives on keys repeated
+    per Q head (Q head h reads KV head h // g)."""
+    rng = np.random.default_rng(11)
+    Hkv, g, L, D = 3, 4, 400, 16
+    K = _bits(rng, (Hkv, L, D))
+    Q = _bits(rng, (Hkv * g, 200, D))
+    idx, S = pol.select_tail_mean(K, Q)
+    idx_r, S_r = pol.select_tail_mean(np.repeat(K, g, axis=0), Q)
+    assert np.array_equal(S, S_r) and np.array_equal(idx, idx_r)
+    assert idx.shape == (Hkv * g, pol.k_alg1(L - 128))
+
+
+def test_tail_mean_planted_and_degenerate():
+    rng = np.random.default_rng(12)
+    Hkv, g, L, D = 1, 2, 600, 32
+    K = nm.bf16_to_f32(_bits(rng, (Hkv, L, D), 0.1))
+    Q = nm.bf16_to_f32(_bits(rng, (Hkv * g, 128, D), 0.1))
+    u = np.zeros(D, np.float32)
+    u[3] = 1.0
+    Q[0] += 2.0 * u  # head 0's tail mean points along u
+    planted = [17, 250, 401]
+    for j in planted:
+        K[0, j] += 3.0 * u
+    idx, S = pol.select_tail_mean(nm.f32_to_bf16(K), nm.f32_to_bf16(Q), k=3)
+    assert list(idx[0]) == planted
+    # the window is never a candidate, and P = 0 selects nothing
+    assert S.shape == (2, L - 128)
+    idx0, S0 = pol.select_tail_mean(nm.f32_to_bf16(K[:, :128]), nm.f32_to_bf16(Q))
+    assert idx0.shape == (2, 0) and S0.shape == (2, 0)
