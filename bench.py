@@ -51,6 +51,8 @@ def parse():
     ap.add_argument("--no-rows", action="store_true",
                     help="skip the other hot-path rows (append, selector/refresh, prefill)")
     ap.add_argument("--prefill-lens", default="8192,32768")
+    ap.add_argument("--only-alg1", action="store_true",
+                    help="run only the Alg. 1-literal selector row (against the Eq. 4 selector)")
     ap.add_argument("--only-prefill", action="store_true",
                     help="run only the hybrid-prefill rows (for profiling the prefill kernels)")
     return ap.parse_args()
@@ -246,6 +248,76 @@ def bench_selector(torch, hq, gen, dev, B=4, Hq=64, Hkv=8, L=32768):
     return res
 
 
+def bench_selector_alg1(torch, hq, gen, dev, L=32768, Hq=32, Hkv=8, n_dec=16):
+    """Alg. 1-literal selector (tail-query mean, raw logits, one set per Q head) against the
+    Eq. 4 selector at the prefill-to-decode boundary (one sequence, 32 Q / 8 KV heads, 32K
+    keys, planted vertical keys): time of each call, overlap of the sets, and the relative
+    MSE of hybrid decode (anchors bf16, the rest INT4, 128-token window) against exact fp32
+    attention for n_dec new queries, with each set as the anchors.  The per-Q-head sets are
+    evaluated on a cache with one KV head copy per Q head."""
+    G = Hq // Hkv
+    P = L - W
+    u = torch.randn(Hkv, D, generator=gen, device=dev)
+    u = u / u.norm(dim=-1, keepdim=True)
+    K = torch.randn(Hkv, L, D, generator=gen, device=dev)
+    pos = torch.cat([torch.zeros(Hkv, 1, dtype=torch.long, device=dev),
+                     1 + torch.rand(Hkv, P - 1, generator=gen, device=dev).argsort(dim=1)[:, :15]], dim=1)
+    K[torch.arange(Hkv, device=dev)[:, None], pos] += 4.0 * u[:, None, :]
+    K = K.to(torch.bfloat16)[None].contiguous()
+    V = torch.randn(1, Hkv, L, D, generator=gen, device=dev).to(torch.bfloat16)
+    uq = u.repeat_interleave(G, dim=0)
+    tail = (2.0 * uq[:, None, :] + torch.randn(Hq, W, D, generator=gen, device=dev)).to(torch.bfloat16)[None].contiguous()
+    qd = (2.0 * uq[None] + torch.randn(n_dec, Hq, D, generator=gen, device=dev)).to(torch.bfloat16)
+    shape = hq.Shape.for_context(1, Hq, Hkv, L)
+    k1, k4 = hq.anchor_count_alg1(L), hq.anchor_count(L)
+    ws = hq.select_tail_workspace(shape, L, dev)
+    proxy = tail[:, :, W - 64:].contiguous()
+    us1, _ = timed(torch, lambda: hq.select_vlines_tail(shape, k1, K, tail, ws=ws), 10)
+    us4, _ = timed(torch, lambda: hq.select_vlines(shape, k4, dense_k=K, proxy=proxy), 10)
+    A1 = hq.select_vlines_tail(shape, k1, K, tail)[0]  # [Hq][k1]
+    A4 = hq.select_vlines(shape, k4, dense_k=K, proxy=proxy)  # [1][Hkv][k4]
+    ov = []
+    for h in range(Hq):
+        a, b = A1[h].long(), A4[0, h // G].long()
+        ov.append(torch.isin(a, b).sum().item() / min(len(a), len(b)))
+    # exact attention (fp32) for the decode queries
+    Kf, Vf = K[0].float(), V[0].float()
+    Ke, Ve = Kf.repeat_interleave(G, dim=0), Vf.repeat_interleave(G, dim=0)  # [Hq][L][D]
+    exact = [torch.softmax(torch.bmm(Ke, qd[i].float()[:, :, None])[:, :, 0] / math.sqrt(D), dim=-1)[:, None, :]
+             .bmm(Ve)[:, 0] for i in range(n_dec)]
+
+    def rel_mse(cache):
+        num = den = 0.0
+        for i in range(n_dec):
+            o = hq.decode_attn(cache, qd[i][None].contiguous())[0]
+            num += ((o - exact[i]) ** 2).sum().item()
+            den += (exact[i] ** 2).sum().item()
+        return num / den
+
+    res = {"workload": f"selector at the prefill boundary ctx{L} hq{Hq} hkv{Hkv} (planted vertical keys)",
+           "alg1_k": k1, "eq4_k": k4, "alg1_us": round(us1, 1), "eq4_us": round(us4, 1),
+           "overlap_mean": round(sum(ov) / len(ov), 4), "overlap_min": round(min(ov), 4)}
+    c4 = hq.HybridKVCache(shape, dev)
+    hq.quantize_kv(c4, K, V, A4.contiguous(), proxy)
+    res["eq4_rel_mse"] = float(f"{rel_mse(c4):.4g}")
+    c0 = hq.HybridKVCache(shape, dev)
+    hq.quantize_kv(c0, K, V, None, proxy)
+    res["no_anchor_rel_mse"] = float(f"{rel_mse(c0):.4g}")
+    del c4, c0
+    shape_e = hq.Shape.for_context(1, Hq, Hq, L)
+    ce = hq.HybridKVCache(shape_e, dev)
+    hq.quantize_kv(ce, Ke.to(torch.bfloat16)[None].contiguous(), Ve.to(torch.bfloat16)[None].contiguous(),
+                   A1[None].contiguous(), proxy)
+    res["alg1_rel_mse"] = float(f"{rel_mse(ce):.4g}")
+    del ce
+    # roofline of the Alg. 1 call: prefix keys once per KV head, the tail queries, the indices
+    alg_bytes = Hkv * P * D * 2 + Hq * W * D * 2 + Hq * k1 * 4
+    res["roofline"] = {"bound": "hbm", "achieved": round(alg_bytes / (us1 * 1e-6) / 1e9, 1), "peak": 8000.0,
+                       "unit": "GB/s", "frac": round(alg_bytes / (us1 * 1e-6) / 8e12, 4), "traffic": None,
+                       "bytes": alg_bytes}
+    return res
+
+
 def prefill_ops(anchors_row, N, Hq):
     """Algorithmic MFMA work of the hybrid prefill (per Q head: every (query, key) pair the
     method visits, QK^T and PV at 2 x 128 multiply-adds each): quantized pairs j <= i-128 not
@@ -349,6 +421,11 @@ def main():
         print(json.dumps({"error": "no GPU visible"}))
         sys.exit(3)
     dev = torch.device("cuda:0")
+    if args.only_alg1:
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(args.seed)
+        print(json.dumps({"rows": {"selector_alg1": bench_selector_alg1(torch, hq, gen, dev)}}), flush=True)
+        return
     if args.only_prefill:
         gen = torch.Generator(device=dev)
         gen.manual_seed(args.seed)
@@ -464,6 +541,8 @@ def main():
             print(f"[bench] prefill mxfp4 N={n}: {rows[f'prefill_mx_{n}']['us_per_call']} us", file=sys.stderr,
                   flush=True)
         rows["selector"] = bench_selector(torch, hq, gen, dev)
+        rows["selector_alg1"] = bench_selector_alg1(torch, hq, gen, dev)
+        print(f"[bench] alg1 selector: {rows['selector_alg1']}", file=sys.stderr, flush=True)
         line["rows"] = rows
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(args, G, cpu_bytes_per_head)

@@ -10,14 +10,14 @@ LIB_PATH = os.path.join(HERE, "libhyq.so")
 HYQ_OK = 0
 STATUS = {0: "HYQ_OK", 1: "HYQ_ERR_INVALID", 2: "HYQ_ERR_UNSUPPORTED", 3: "HYQ_ERR_CAPACITY",
           4: "HYQ_ERR_WORKSPACE", 5: "HYQ_ERR_HIP"}
-HYQ_OP_DECODE, HYQ_OP_SELECT, HYQ_OP_PREFILL = 1, 2, 3
+HYQ_OP_DECODE, HYQ_OP_SELECT, HYQ_OP_PREFILL, HYQ_OP_SELECT_TAIL = 1, 2, 3, 4
 HYQ_NBUF = 10
 BUFFERS = ["int4", "slot_pos", "a_k", "a_v", "a_pos", "s_k", "s_v", "w_k", "w_v", "proxy_q"]
 
 # every symbol include/hyq.h declares
 EXPORTS = ["hyq_status_string", "hyq_cache_buffer_bytes", "hyq_workspace_bytes", "hyq_quantize_kv",
            "hyq_append_token", "hyq_select_vlines", "hyq_decode_attn", "hyq_prefill_attn",
-           "hyq_prefill_attn_mx"]
+           "hyq_prefill_attn_mx", "hyq_select_vlines_tail"]
 
 
 class HyqShape(C.Structure):
@@ -69,6 +69,8 @@ def load() -> C.CDLL:
     lib.hyq_decode_attn.argtypes = [C.POINTER(HyqCache), vp, vp, i32, vp, sz, vp]
     lib.hyq_prefill_attn.restype = C.c_int
     lib.hyq_prefill_attn.argtypes = [C.POINTER(HyqShape), vp, vp, vp, i32, vp, i32, vp, vp, sz, vp]
+    lib.hyq_select_vlines_tail.restype = C.c_int
+    lib.hyq_select_vlines_tail.argtypes = [C.POINTER(HyqShape), vp, i32, vp, i32, i32, vp, vp, vp, sz, vp]
     lib.hyq_prefill_attn_mx.restype = C.c_int
     lib.hyq_prefill_attn_mx.argtypes = [C.POINTER(HyqShape), vp, vp, vp, i32, vp, i32, vp, vp, sz, vp]
     _lib = lib

@@ -44,6 +44,14 @@ def anchor_count(L: int, pct_num: int = 5, pct_den: int = 100, window: int = WIN
     return min(P, max(1, -(-L * pct_num // pct_den)))
 
 
+def anchor_count_alg1(L: int, r_num: int = 5, r_den: int = 100, window: int = WINDOW) -> int:
+    """Alg. 1's count on the candidates: k = min(P, max(1, ceil(P r))), P = max(0, L - window)."""
+    P = max(0, L - window)
+    if P == 0:
+        return 0
+    return min(P, max(1, -(-P * r_num // r_den)))
+
+
 @dataclass
 class Shape:
     batch: int
@@ -218,6 +226,38 @@ def select_vlines(shape: Shape, k: int, cache: HybridKVCache | None = None, dens
     check("hyq_select_vlines", lib.hyq_select_vlines(
         C.byref(s), C.byref(cache.c) if cache is not None else None, _ptr(dense_k), L,
         _ptr(proxy), n_proxy, k, int(apply), _ptr(idx), _ptr(sc), _ptr(ws), ws.numel(), _stream()))
+    idx = idx[..., :k]
+    return (idx, sc) if scores else idx
+
+
+def select_tail_workspace(shape: Shape, L: int, device=None) -> torch.Tensor:
+    """A workspace for hyq_select_vlines_tail at context length L (uint8, on ``device``)."""
+    lib = _lib.load()
+    s = shape.c()
+    need = int(lib.hyq_workspace_bytes(C.byref(s), _lib.HYQ_OP_SELECT_TAIL, L, 0))
+    if need == 0:
+        raise ValueError(f"select_vlines_tail: unsupported shape or length L={L}")
+    return torch.empty(need, dtype=torch.uint8, device=device or "cuda")
+
+
+def select_vlines_tail(shape: Shape, k: int, dense_k: torch.Tensor, q: torch.Tensor, scores: bool = False,
+                       ws: torch.Tensor | None = None):
+    """Alg. 1-literal selector (hyq_select_vlines_tail): tail-query mean, raw logits, one set
+    per Q head; returns idx [B][Hq][k] (and the logits [B][Hq][P])."""
+    lib = _lib.load()
+    L = dense_k.shape[2]
+    _bf16(dense_k, (shape.batch, shape.n_kv_heads, L, D), "dense_k")
+    n_q = q.shape[2]
+    _bf16(q, (shape.batch, shape.n_q_heads, n_q, D), "q")
+    P = max(0, L - WINDOW)
+    dev = dense_k.device
+    idx = torch.empty((shape.batch, shape.n_q_heads, max(k, 1)), dtype=torch.int32, device=dev)
+    sc = torch.empty((shape.batch, shape.n_q_heads, max(P, 1)), dtype=torch.float32, device=dev) if scores else None
+    s = shape.c()
+    if ws is None:
+        ws = select_tail_workspace(shape, L, dev)
+    check("hyq_select_vlines_tail", lib.hyq_select_vlines_tail(
+        C.byref(s), _ptr(dense_k), L, _ptr(q), n_q, k, _ptr(idx), _ptr(sc), _ptr(ws), ws.numel(), _stream()))
     idx = idx[..., :k]
     return (idx, sc) if scores else idx
 

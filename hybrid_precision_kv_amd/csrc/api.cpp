@@ -102,6 +102,20 @@ SelectWs select_ws(const hyq_shape_t* s, int32_t len) {
   return w;
 }
 
+// Alg. 1 selector workspace: tail means [B][Hq][128] f32, then order keys [B][Hq][P] u32
+struct TailWs {
+  size_t qbar, keys, total;
+};
+TailWs tail_ws(const hyq_shape_t* s, int32_t len) {
+  TailWs w;
+  const size_t BH = (size_t)s->batch * s->n_q_heads;
+  const size_t P = len > W ? (size_t)(len - W) : 1;
+  w.qbar = 0;
+  w.keys = r256(BH * D * 4);
+  w.total = w.keys + r256(BH * P * 4);
+  return w;
+}
+
 // prefill workspace layout (sections in this order, each rounded up to 256 bytes)
 struct PrefillWs {
   size_t q8, sq, k8, sk, v8, sv, vmax, abits, vt16, ka16, va16, total;
@@ -198,6 +212,7 @@ size_t hyq_workspace_bytes(const hyq_shape_t* s, int op, int32_t len, int32_t n_
     }
     case HYQ_OP_SELECT: return len > 0 ? select_ws(s, len).total : 0;
     case HYQ_OP_PREFILL: return len > 0 && len <= HYQ_PREFILL_MAX_LEN ? prefill_ws(s, len).total : 0;
+    case HYQ_OP_SELECT_TAIL: return len > 0 ? tail_ws(s, len).total : 0;
     default: return 0;
   }
 }
@@ -434,6 +449,35 @@ static int prefill_common(const hyq_shape_t* shape, const void* q, const void* k
 }
 
 extern "C" {
+
+int hyq_select_vlines_tail(const hyq_shape_t* shape, const void* k, int32_t len, const void* q, int32_t n_q,
+                           int32_t k_sel, int32_t* idx_out, float* scores_out, void* ws, size_t ws_bytes,
+                           hipStream_t stream) {
+  int st = check_shape(shape);
+  if (st) return st;
+  if (!k || !q || len <= 0 || n_q <= 0) return HYQ_ERR_INVALID;
+  const int P = len > W ? len - W : 0;
+  if (k_sel < 0 || k_sel > P || (k_sel > 0 && !idx_out)) return HYQ_ERR_INVALID;
+  if (P == 0) return HYQ_OK;
+  const TailWs w = tail_ws(shape, len);
+  if (!ws || ws_bytes < w.total) return HYQ_ERR_WORKSPACE;
+  hyq::TailSelectParams p;
+  p.k = (const uint16_t*)k;
+  p.q = (const uint16_t*)q;
+  p.B = shape->batch;
+  p.Hkv = shape->n_kv_heads;
+  p.G = shape->n_q_heads / shape->n_kv_heads;
+  p.len = len;
+  p.n_q = n_q;
+  p.t = n_q < W ? n_q : W;
+  p.k_sel = k_sel;
+  p.qbar = (float*)((char*)ws + w.qbar);
+  p.keys = (uint32_t*)((char*)ws + w.keys);
+  p.scores_out = scores_out;
+  p.idx_out = idx_out;
+  if (hyq::launch_select_tail(p, stream) != hipSuccess) return HYQ_ERR_HIP;
+  return HYQ_OK;
+}
 
 int hyq_prefill_attn(const hyq_shape_t* shape, const void* q, const void* k, const void* v, int32_t len,
                      const int32_t* anchors, int32_t n_anchor, float* o, void* ws, size_t ws_bytes,

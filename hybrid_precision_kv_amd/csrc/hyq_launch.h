@@ -52,6 +52,20 @@ struct SelectParams {
 };
 hipError_t launch_select(SelectParams p, hipStream_t stream);
 int select_task_count(int n_tiles);
+// radix top-k of `rows` rows of P order-preserving keys (largest first, ties to the lower
+// position), indices ascending into idx_out [rows][k]
+hipError_t launch_topk_keys(const uint32_t* keys, int P, int k, int rows, int32_t* idx_out, hipStream_t stream);
+
+struct TailSelectParams {
+  const uint16_t* k;  // [B][Hkv][len][128] dense keys
+  const uint16_t* q;  // [B][Hq][n_q][128] queries
+  int B, Hkv, G, len, n_q, t, k_sel;
+  float* qbar;        // [B][Hq][128] tail-query means
+  uint32_t* keys;     // [B][Hq][len - 128] order-preserving keys of the logits
+  float* scores_out;  // [B][Hq][len - 128] logits, nullable
+  int32_t* idx_out;   // [B][Hq][k_sel]
+};
+hipError_t launch_select_tail(const TailSelectParams& p, hipStream_t stream);
 
 struct RefreshParams {
   uint8_t* int4;

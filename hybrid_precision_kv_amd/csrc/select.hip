@@ -387,7 +387,8 @@ __global__ __launch_bounds__(256) void select_rowmerge_kernel(SelectParams p) {
 }
 
 // ---------------------------------------------------------------- top-k (radix select)
-// One workgroup per head.  Scores are >= 0, so their bit patterns order like the values.
+// One workgroup per head.  Scores are >= 0, so their bit patterns order like the values (other
+// callers pass keys already mapped to an order-preserving unsigned form).
 // Keeps every score above the k-th largest value T and the lowest-position scores equal to T,
 // written in ascending position order.
 constexpr int TK_THREADS = 1024;
@@ -540,5 +541,16 @@ hipError_t launch_select(SelectParams p, hipStream_t stream) {
 }
 
 int select_task_count(int n_tiles) { return (n_tiles + SW - 1) / SW; }
+
+hipError_t launch_topk_keys(const uint32_t* keys, int P, int k, int rows, int32_t* idx_out, hipStream_t stream) {
+  SelectParams p{};
+  p.scores = (float*)keys;  // read as 32-bit keys
+  p.len = P + WIN;
+  p.k = k;
+  p.idx_out = idx_out;
+  if (P <= TK_REG * TK_THREADS) hipLaunchKernelGGL(topk_kernel<true>, dim3(rows), dim3(TK_THREADS), 0, stream, p);
+  else hipLaunchKernelGGL(topk_kernel<false>, dim3(rows), dim3(TK_THREADS), 0, stream, p);
+  return hipGetLastError();
+}
 
 }  // namespace hyq

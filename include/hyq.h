@@ -80,6 +80,7 @@ extern "C" {
 #define HYQ_OP_DECODE 1
 #define HYQ_OP_SELECT 2
 #define HYQ_OP_PREFILL 3
+#define HYQ_OP_SELECT_TAIL 4
 
 typedef struct {
   int32_t batch;        /* sequences */
@@ -129,8 +130,8 @@ const char* hyq_status_string(int status);
 int hyq_cache_buffer_bytes(const hyq_shape_t* shape, size_t bytes[HYQ_NBUF]);
 
 /* Workspace bytes an operation needs: op = HYQ_OP_DECODE (len unused; n_splits = the value
-   that will be passed, 0 = automatic), HYQ_OP_SELECT (len = context length), HYQ_OP_PREFILL
-   (len = sequence length).  Returns 0 for an invalid shape. */
+   that will be passed, 0 = automatic), HYQ_OP_SELECT and HYQ_OP_SELECT_TAIL (len = context
+   length), HYQ_OP_PREFILL (len = sequence length).  Returns 0 for an invalid shape. */
 size_t hyq_workspace_bytes(const hyq_shape_t* shape, int op, int32_t len, int32_t n_splits);
 
 /* Freeze: prefill -> decode cache organisation (HyQuant paper Alg. 4).
@@ -181,6 +182,28 @@ int hyq_select_vlines(const hyq_shape_t* shape, hyq_cache_t* cache, const void* 
                       int32_t len, const void* proxy, int32_t n_proxy, int32_t k, int32_t apply,
                       int32_t* idx_out, float* scores_out, void* ws, size_t ws_bytes,
                       hipStream_t stream);
+
+/* Vertical-token identification as the HyQuant paper's Alg. 1 writes it (appendix A.1), the
+   literal alternative to hyq_select_vlines' Eq. 4 scores.  For each (b, Q head h):
+     qbar_h = mean of the last t = min(128, n_q) query rows (fp32: four partial sums of 32
+              consecutive rows each, in ascending row order, added in row order, then an
+              IEEE divide by t);
+     S_h(j) = qbar_h . k_j for every prefix key j in [0, P), P = len - 128, with the keys of KV
+              head h / (Hq / Hkv) (raw logits: no 1/sqrt(128), no softmax; fp32);
+     idx_h  = the k largest S_h (ties to the lower position; +0 and -0 tie), ascending.
+   One set per Q head: the sets of one KV group may differ, so they are not applied to a cache.
+   k: device bf16 [B][Hkv][len][128]; q: device bf16 [B][Hq][n_q][128]; idx_out: device int32
+   [B][Hq][k_sel] (nullable when k_sel = 0); scores_out: device f32 [B][Hq][P] (nullable).
+   k_sel: 0 <= k_sel <= P (Alg. 1 takes min(P, max(1, ceil(P r))); the caller passes it).
+   P = 0 (len <= 128) is accepted with k_sel = 0 and does nothing.
+   ws: device workspace of at least hyq_workspace_bytes(shape, HYQ_OP_SELECT_TAIL, len, 0)
+   bytes, no initialisation needed; calls sharing one workspace must not overlap in time.
+   Three kernel launches (tail means, logits, top-k).  Reads k and q only.
+   Errors: INVALID (null pointers, len or n_q <= 0, k_sel outside [0, P]), UNSUPPORTED,
+   WORKSPACE, HIP. */
+int hyq_select_vlines_tail(const hyq_shape_t* shape, const void* k, int32_t len, const void* q,
+                           int32_t n_q, int32_t k_sel, int32_t* idx_out, float* scores_out,
+                           void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* Decode attention over the hybrid cache (HyQuant paper §4.3 Eq. 8-9, Alg. 3): for every
    (b, Q head), o = sum_j softmax_j(q . k_j / sqrt(128)) v_j over all len cached positions,
