@@ -387,132 +387,248 @@ __global__ __launch_bounds__(256) void select_rowmerge_kernel(SelectParams p) {
 }
 
 // ---------------------------------------------------------------- top-k (radix select)
-// One workgroup per head.  Scores are >= 0, so their bit patterns order like the values (other
-// callers pass keys already mapped to an order-preserving unsigned form).
-// Keeps every score above the k-th largest value T and the lowest-position scores equal to T,
-// written in ascending position order.
+// One workgroup of 1024 threads per row of P unsigned keys (scores >= 0 as their bit patterns,
+// or keys already mapped to an order-preserving unsigned form).  Keeps every key above the
+// k-th largest value T and the lowest positions equal to T, written in ascending position order.
+//   * Rows of up to 32768 keys are staged once in LDS (one padding word after every 32 keys, so
+//     strided and per-thread-contiguous reads are both free of bank conflicts); longer rows are
+//     re-read from global memory.
+//   * Radix select on digits of 11, 8, 8 and 5 bits.  The first digit is counted over every
+//     key; the keys that share the chosen first digit (a few per cent) are copied to a
+//     candidate list, and the three later digits scan only that list.
+//   * Masked lanes add to per-lane dummy counters and write to per-lane dummy slots, and loads
+//     past the row are clamped, so no load or LDS atomic sits behind a branch.
+//   * Ordered output: each thread describes its contiguous positions by bit masks of the keys
+//     above and equal to T; two block prefix sums give every thread its output offset.
+// Every loop is rolled or unrolled by at most 8: the code runs once per workgroup, so its
+// size sets the instruction-fetch time.
 constexpr int TK_THREADS = 1024;
+constexpr int TK_WAVES = TK_THREADS / 64;
+constexpr int TK_BATCH = 8 * TK_THREADS;  // keys per batch of the strided passes
+constexpr int TK_LDS_KEYS = 32768;        // rows up to this length are staged in LDS
+constexpr int TK_BINS = 2048;             // first digit: bits 31..21
+constexpr int TK_CAND = 4096;             // keys kept after the first digit
+constexpr int TK_TRASH = 64;              // per-lane dummy counters / slots for masked lanes
 
-constexpr int TK_REG = 32;  // scores per thread kept in registers (P <= 32768)
-
-__device__ inline int wave_incl_scan(int x, int lane) {
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int y = __shfl_up(x, off);
-    if (lane >= off) x += y;
-  }
+__device__ inline int wave_scan_incl(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);  // row_bcast:15 -> rows 1, 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);  // row_bcast:31 -> rows 2, 3
   return x;
 }
-
-// exclusive prefix over the 1024 threads (wave scans + the 16 wave totals); *tot = sum
-__device__ inline int tk_block_scan(int v, int* wtot, int* tot) {
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int incl = wave_incl_scan(v, lane);
+__device__ inline int block_scan_excl(int v, int* wtot) {
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int incl = wave_scan_incl(v);
   if (lane == 63) wtot[wv] = incl;
   __syncthreads();
-  int before = 0, all = 0;
-#pragma unroll
-  for (int w = 0; w < TK_THREADS / 64; ++w) {
-    const int t = wtot[w];
-    before += w < wv ? t : 0;
-    all += t;
-  }
+  const int t = wave_scan_incl(lane < TK_WAVES ? wtot[lane] : 0);
+  const int before = wv ? __builtin_amdgcn_readlane(t, wv - 1) : 0;
   __syncthreads();
-  *tot = all;
   return before + incl - v;
 }
+__device__ inline int mbcnt64(uint64_t m) {
+  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+__device__ inline int pad32(int i) { return i + (i >> 5); }
+// hist[bin] += 1 for every lane (masked lanes pass their own dummy bin).  The lanes that share
+// the first lane's bin are added by one of them, so keys concentrated in a few bins do not
+// serialise on one LDS address; the atomic is issued by every lane, without a branch.
+__device__ inline void hist_add(int* hist, int bin, int lane) {
+  const int b0 = __builtin_amdgcn_readfirstlane(bin);
+  const uint64_t same = __builtin_amdgcn_ballot_w64(bin == b0);
+  const bool grouped = bin == b0, first = grouped && mbcnt64(same) == 0;
+  atomicAdd(&hist[grouped && !first ? TK_BINS + lane : bin], grouped ? (first ? (int)__builtin_popcountll(same) : 0) : 1);
+}
 
-// REG: every thread loads its contiguous range of scores once into registers (P <= TK_REG *
-// TK_THREADS); otherwise each pass re-reads them.
-template <bool REG>
-__global__ __launch_bounds__(TK_THREADS) void topk_kernel(SelectParams p) {
-  __shared__ int hist[256];
-  __shared__ int whist[TK_THREADS / 64][256];  // per-wave histograms (few distinct high digits)
-  __shared__ int wtot[TK_THREADS / 64];
+template <bool LDS>
+__device__ void topk_row(const uint32_t* g, int P, int k, int32_t* out) {
+  extern __shared__ uint32_t dyn[];  // LDS: keys of the batches covering P, padded
+  __shared__ int hist[TK_BINS + TK_TRASH];
+  __shared__ uint32_t cand[TK_CAND + TK_TRASH];
+  __shared__ int tsum[TK_WAVES];
   __shared__ uint32_t s_prefix, s_mask;
-  __shared__ int s_need;
-  const int hb = blockIdx.x, tid = threadIdx.x;
-  const int P = p.len - WIN > 0 ? p.len - WIN : 0;
-  const uint32_t* sc = (const uint32_t*)(p.scores + hb * (size_t)P);
-  int32_t* out = p.idx_out + hb * (size_t)p.k;
-  // each thread owns the contiguous positions [lo, hi)
-  const int per = (P + TK_THREADS - 1) / TK_THREADS;
-  const int lo = min(P, tid * per), hi = min(P, lo + per);
-  uint32_t v[REG ? TK_REG : 1];
-  if constexpr (REG) {
-#pragma unroll
-    for (int i = 0; i < TK_REG; ++i) v[i] = lo + i < hi ? sc[lo + i] : 0u;
-  }
-  auto val = [&](int i) -> uint32_t {  // score at position lo + i
-    if constexpr (REG) return v[i]; else return sc[lo + i];
+  __shared__ int s_need, s_ncand, s_bin;  // s_bin: keys in the chosen bin of the last digit
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int nb = (P + TK_BATCH - 1) / TK_BATCH;
+  // key at i for any i of the covered batches: staged zeros past P (LDS) or a clamped read
+  // (global; the caller ignores it), so no load sits behind a branch
+  auto key = [&](int i) -> uint32_t {
+    if constexpr (LDS) return dyn[pad32(i)]; else return g[min(i, P - 1)];
   };
-  const int cnt = REG ? TK_REG : per;
-  if (tid == 0) { s_prefix = 0u; s_mask = 0u; s_need = p.k; }
+  for (int i = tid; i < TK_BINS + TK_TRASH; i += TK_THREADS) hist[i] = 0;
+  if (tid == 0) s_ncand = 0;
   __syncthreads();
-  // four 8-bit digits, most significant first: find T and how many of it to keep
-  const int wv = tid >> 6;
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    for (int i = tid; i < (TK_THREADS / 64) * 256; i += TK_THREADS) (&whist[0][0])[i] = 0;
+  // ---- stage (LDS) and count the first digit, bits 31..21
+  for (int b = tid; b < nb * TK_BATCH; b += TK_BATCH) {
+    uint32_t x[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) x[u] = g[min(b + u * TK_THREADS, P - 1)];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = b + u * TK_THREADS;
+      if constexpr (LDS) dyn[pad32(i)] = i < P ? x[u] : 0u;
+      hist_add(hist, i < P ? (int)(x[u] >> 21) : TK_BINS + lane, lane);
+    }
+  }
+  __syncthreads();
+  {
+    const int d0 = TK_BINS - 1 - 2 * tid;  // thread t owns digits d0, d0 - 1
+    const int c0 = hist[d0], c1 = hist[d0 - 1];
+    const int run = block_scan_excl(c0 + c1, tsum);
+    if (tid < 256) hist[tid] = 0;
+    if (run < k && run + c0 >= k) {
+      s_prefix = (uint32_t)d0 << 21;
+      s_need = k - run;
+      s_bin = c0;
+    } else if (run + c0 < k && (run + c0 + c1 >= k || d0 == 1)) {
+      s_prefix = (uint32_t)(d0 - 1) << 21;
+      s_need = k - run - c0;
+      s_bin = c1;
+    }
+    if (tid == 0) s_mask = 0xFFE00000u;
     __syncthreads();
+  }
+  // ---- digits 20..13, 12..5, 4..0 over the keys with the prefix; wave 0 finds each.  As
+  // soon as the keys with the current prefix fit the candidate list they are copied there
+  // (one LDS atomic per wave and batch) and the remaining digits scan only them.
+  bool use_cand = false;
+  int ncand = 0;
+  for (int pass = 1; pass < 4; ++pass) {
+    const int shift = pass == 1 ? 13 : pass == 2 ? 5 : 0;
+    const int nbins = pass == 3 ? 32 : 256;
+    if (!use_cand && s_bin <= TK_CAND) {
+      const uint32_t prefix = s_prefix, mask = s_mask;
+      for (int b = tid; b < nb * TK_BATCH; b += TK_BATCH) {
+        uint32_t x[8];
+        uint64_t m[8];
+        int cnt[8], tot = 0;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int i = b + u * TK_THREADS;
+          x[u] = key(i);
+          m[u] = __builtin_amdgcn_ballot_w64(i < P && (x[u] & mask) == prefix);
+          cnt[u] = tot;
+          tot += (int)__builtin_popcountll(m[u]);
+        }
+        if (tot) {
+          int base = 0;
+          if (lane == 0) base = atomicAdd(&s_ncand, tot);
+          base = __builtin_amdgcn_readfirstlane(base);
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            const bool mine = (m[u] >> lane) & 1u;
+            const int slot = base + cnt[u] + mbcnt64(m[u]);
+            cand[mine && slot < TK_CAND ? slot : TK_CAND + lane] = x[u];
+          }
+        }
+      }
+      __syncthreads();
+      ncand = min(s_ncand, TK_CAND);
+      use_cand = true;
+    }
     const uint32_t prefix = s_prefix, mask = s_mask;
+    if (use_cand) {
+      for (int i = tid; i < ncand; i += TK_THREADS) {
+        const uint32_t x = cand[i];
+        hist_add(hist, (x & mask) == prefix ? (int)((x >> shift) & (nbins - 1)) : TK_BINS + lane, lane);
+      }
+    } else {
+      for (int b = tid; b < nb * TK_BATCH; b += TK_BATCH) {
+        uint32_t x[8];
 #pragma unroll
-    for (int i = 0; i < cnt; ++i) {
-      if (lo + i >= hi) continue;
-      const uint32_t x = val(i);
-      if ((x & mask) == prefix) atomicAdd(&whist[wv][(x >> shift) & 255], 1);
+        for (int u = 0; u < 8; ++u) x[u] = key(b + u * TK_THREADS);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const bool in = b + u * TK_THREADS < P && (x[u] & mask) == prefix;
+          hist_add(hist, in ? (int)((x[u] >> shift) & (nbins - 1)) : TK_BINS + lane, lane);
+        }
+      }
     }
     __syncthreads();
-    // digit d = 255 - tid: count with digit >= d (a suffix sum, as a prefix over tid); the
-    // chosen digit is the largest d whose count reaches `need`
-    const int need = s_need;
-    int h = 0, incl = 0;
-    if (tid < 256) {
+    if (wv == 0) {  // lane l owns digits nbins - 1 - 4 l - r (r < 4); clears them for the next
+      const int need = s_need;
+      int c4[4], h = 0;
 #pragma unroll
-      for (int w = 0; w < TK_THREADS / 64; ++w) h += whist[w][255 - tid];
-      incl = wave_incl_scan(h, tid & 63);
-      if ((tid & 63) == 63) hist[tid >> 6] = incl;
-    }
-    __syncthreads();
-    if (tid < 256) {
-      for (int w = 0; w < (tid >> 6); ++w) incl += hist[w];
-      const int excl = incl - h;
-      const int d = 255 - tid;
-      if (excl < need && (incl >= need || d == 0)) {
-        s_prefix = prefix | ((uint32_t)d << shift);
-        s_mask = mask | (255u << shift);
-        s_need = need - excl;  // how many elements equal to the final prefix must be kept
+      for (int r = 0; r < 4; ++r) {
+        const int d = nbins - 1 - 4 * lane - r;
+        c4[r] = d >= 0 ? hist[d] : 0;
+        h += c4[r];
+        if (d >= 0) hist[d] = 0;
+      }
+      int run = wave_scan_incl(h) - h;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int d = nbins - 1 - 4 * lane - r;
+        if (d >= 0 && run < need && (run + c4[r] >= need || d == 0)) {
+          s_prefix = prefix | ((uint32_t)d << shift);
+          s_mask = mask | ((uint32_t)(nbins - 1) << shift);
+          s_need = need - run;
+          s_bin = c4[r];
+        }
+        run += c4[r];
       }
     }
     __syncthreads();
   }
   const uint32_t T = s_prefix;
   const int need_eq = s_need;
-  // ordered compaction
-  int n_gt = 0, n_eq = 0;
+  // ---- ordered compaction: thread t owns the contiguous positions [lo, hi), in chunks of 32
+  // described by bit masks of the keys above T and equal to T
+  const int per = (P + TK_THREADS - 1) / TK_THREADS;
+  const int lo = min(P, tid * per), hi = min(P, lo + per);
+  auto masks = [&](int c, uint32_t& gtm, uint32_t& eqm) {
+    const int n = hi - c;
+    const uint32_t inm = n >= 32 ? ~0u : ((1u << n) - 1u);
+    gtm = 0u;
+    eqm = 0u;
 #pragma unroll
-  for (int i = 0; i < cnt; ++i) {
-    if (lo + i >= hi) continue;
-    const uint32_t x = val(i);
-    n_gt += x > T;
-    n_eq += x == T;
+    for (int e = 0; e < 32; ++e) {
+      const uint32_t x = key(c + e);
+      gtm |= x > T ? (1u << e) : 0u;
+      eqm |= x == T ? (1u << e) : 0u;
+    }
+    gtm &= inm;
+    eqm &= inm;
+  };
+  uint32_t gt0 = 0u, eq0 = 0u;  // the first chunk's masks, kept for the output
+  int n_gt = 0, n_eq = 0;
+  for (int c = lo; c < hi; c += 32) {
+    uint32_t gtm, eqm;
+    masks(c, gtm, eqm);
+    if (c == lo) { gt0 = gtm; eq0 = eqm; }
+    n_gt += __builtin_popcount(gtm);
+    n_eq += __builtin_popcount(eqm);
   }
-  int tot;
-  const int eq_before = tk_block_scan(n_eq, wtot, &tot);
+  const int eq_before = block_scan_excl(n_eq, tsum);
   int take_eq = need_eq - eq_before;
   take_eq = take_eq < 0 ? 0 : (take_eq > n_eq ? n_eq : take_eq);
-  const int mine = n_gt + take_eq;
-  int o = tk_block_scan(mine, wtot, &tot);
-  int eq_left = take_eq;
-#pragma unroll
-  for (int i = 0; i < cnt; ++i) {
-    if (lo + i >= hi) continue;
-    const uint32_t x = val(i);
-    if (x > T || (x == T && eq_left > 0)) {
-      if (x == T) --eq_left;
-      if (o < p.k) out[o] = lo + i;  // exactly k are kept for finite scores; never write past k
+  int o = block_scan_excl(n_gt + take_eq, tsum);
+  for (int c = lo; c < hi; c += 32) {
+    uint32_t gtm = gt0, eqm = eq0;
+    if (c != lo) masks(c, gtm, eqm);
+    uint32_t sel = gtm;
+    while (take_eq > 0 && eqm) {  // the lowest positions equal to T
+      sel |= eqm & (0u - eqm);
+      eqm &= eqm - 1u;
+      --take_eq;
+    }
+    while (sel) {
+      const int e = __builtin_ctz(sel);
+      sel &= sel - 1u;
+      if (o < k) out[o] = c + e;
       ++o;
     }
   }
+}
+
+
+template <bool LDS>
+__global__ __launch_bounds__(TK_THREADS) void topk_kernel(const uint32_t* keys, int P, int k, int32_t* idx) {
+  topk_row<LDS>(keys + blockIdx.x * (size_t)P, P, k, idx + blockIdx.x * (size_t)k);
 }
 
 }  // namespace
@@ -531,25 +647,20 @@ hipError_t launch_select(SelectParams p, hipStream_t stream) {
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(select_pass_kernel<2>, grid, dim3(SW * 64), 0, stream, p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  if (p.k > 0) {
-    const int P = p.len > WIN ? p.len - WIN : 0;
-    if (P <= TK_REG * TK_THREADS) hipLaunchKernelGGL(topk_kernel<true>, dim3(H), dim3(TK_THREADS), 0, stream, p);
-    else hipLaunchKernelGGL(topk_kernel<false>, dim3(H), dim3(TK_THREADS), 0, stream, p);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-  }
+  if (p.k > 0) return launch_topk_keys((const uint32_t*)p.scores, p.len - WIN, p.k, H, p.idx_out, stream);
   return hipSuccess;
 }
 
 int select_task_count(int n_tiles) { return (n_tiles + SW - 1) / SW; }
 
 hipError_t launch_topk_keys(const uint32_t* keys, int P, int k, int rows, int32_t* idx_out, hipStream_t stream) {
-  SelectParams p{};
-  p.scores = (float*)keys;  // read as 32-bit keys
-  p.len = P + WIN;
-  p.k = k;
-  p.idx_out = idx_out;
-  if (P <= TK_REG * TK_THREADS) hipLaunchKernelGGL(topk_kernel<true>, dim3(rows), dim3(TK_THREADS), 0, stream, p);
-  else hipLaunchKernelGGL(topk_kernel<false>, dim3(rows), dim3(TK_THREADS), 0, stream, p);
+  if (P <= TK_LDS_KEYS) {
+    // staged batches of TK_BATCH keys, one padding word per 32
+    const size_t lds = (size_t)((P + TK_BATCH - 1) / TK_BATCH) * TK_BATCH / 32 * 33 * sizeof(uint32_t);
+    hipLaunchKernelGGL(topk_kernel<true>, dim3(rows), dim3(TK_THREADS), lds, stream, keys, P, k, idx_out);
+  } else {
+    hipLaunchKernelGGL(topk_kernel<false>, dim3(rows), dim3(TK_THREADS), 0, stream, keys, P, k, idx_out);
+  }
   return hipGetLastError();
 }
 
