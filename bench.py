@@ -51,6 +51,8 @@ def parse():
     ap.add_argument("--no-rows", action="store_true",
                     help="skip the other hot-path rows (append, selector/refresh, prefill)")
     ap.add_argument("--prefill-lens", default="8192,32768")
+    ap.add_argument("--only-selector", action="store_true",
+                    help="run only the selector rows (Eq. 4 selector and cache maintenance, Alg. 1 variant)")
     ap.add_argument("--only-alg1", action="store_true",
                     help="run only the Alg. 1-literal selector row (against the Eq. 4 selector)")
     ap.add_argument("--only-prefill", action="store_true",
@@ -154,6 +156,33 @@ def timed(torch, fn, reps, warm=2):
     return sum(t) / len(t), min(t)
 
 
+def timed_graph(torch, fn, reps):
+    """Mean microseconds of fn() replayed from a captured graph (its launches only, no host
+    cost per call), and fn's result from the first replay."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for _ in range(2):
+            fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        out = fn()
+    g.replay()
+    torch.cuda.synchronize()
+    first = out.clone() if hasattr(out, "clone") else out
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) * 1e3 / reps
+    del g
+    return us, first
+
+
 def bench_maintenance(torch, hq, cache, B, Hkv, G, L, gen, dev, ws, out, splits):
     """Decode steps with cache maintenance on one layer: per token hyq_append_token +
     hyq_decode_attn, and every 64 tokens hyq_select_vlines(apply=1) at the 5% rule (the
@@ -231,7 +260,11 @@ def bench_selector(torch, hq, gen, dev, B=4, Hq=64, Hkv=8, L=32768):
     for pct in (1, 5, 10):
         k = hq.anchor_count(L, pct)
         us, _ = timed(torch, lambda: hq.select_vlines(shape, k, cache=cache), 5)
+        res[f"select_{pct}pct_us_eager"] = round(us, 1)
+        ref = hq.select_vlines(shape, k, cache=cache)
+        us, got = timed_graph(torch, lambda: hq.select_vlines(shape, k, cache=cache), 10)
         res[f"select_{pct}pct_us"] = round(us, 1)
+        res[f"select_{pct}pct_graph_equal"] = bool(torch.equal(got, ref))
     k_t = torch.randn(B, Hkv, D, generator=gen, device=dev).to(torch.bfloat16)
     q_t = torch.randn(B, Hq, D, generator=gen, device=dev).to(torch.bfloat16)
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
@@ -272,10 +305,14 @@ def bench_selector_alg1(torch, hq, gen, dev, L=32768, Hq=32, Hkv=8, n_dec=16):
     k1, k4 = hq.anchor_count_alg1(L), hq.anchor_count(L)
     ws = hq.select_tail_workspace(shape, L, dev)
     proxy = tail[:, :, W - 64:].contiguous()
-    us1, _ = timed(torch, lambda: hq.select_vlines_tail(shape, k1, K, tail, ws=ws), 10)
-    us4, _ = timed(torch, lambda: hq.select_vlines(shape, k4, dense_k=K, proxy=proxy), 10)
+    us1_eager, _ = timed(torch, lambda: hq.select_vlines_tail(shape, k1, K, tail, ws=ws), 10)
+    us4_eager, _ = timed(torch, lambda: hq.select_vlines(shape, k4, dense_k=K, proxy=proxy), 10)
     A1 = hq.select_vlines_tail(shape, k1, K, tail)[0]  # [Hq][k1]
     A4 = hq.select_vlines(shape, k4, dense_k=K, proxy=proxy)  # [1][Hkv][k4]
+    # device time: the calls replayed from captured graphs (the replay's sets must match)
+    us1, g1 = timed_graph(torch, lambda: hq.select_vlines_tail(shape, k1, K, tail, ws=ws), 20)
+    us4, g4 = timed_graph(torch, lambda: hq.select_vlines(shape, k4, dense_k=K, proxy=proxy), 20)
+    graph_same = bool(torch.equal(g1[0], A1) and torch.equal(g4, A4))
     ov = []
     for h in range(Hq):
         a, b = A1[h].long(), A4[0, h // G].long()
@@ -296,6 +333,7 @@ def bench_selector_alg1(torch, hq, gen, dev, L=32768, Hq=32, Hkv=8, n_dec=16):
 
     res = {"workload": f"selector at the prefill boundary ctx{L} hq{Hq} hkv{Hkv} (planted vertical keys)",
            "alg1_k": k1, "eq4_k": k4, "alg1_us": round(us1, 1), "eq4_us": round(us4, 1),
+           "alg1_us_eager": round(us1_eager, 1), "eq4_us_eager": round(us4_eager, 1), "graph_sets_equal": graph_same,
            "overlap_mean": round(sum(ov) / len(ov), 4), "overlap_min": round(min(ov), 4)}
     c4 = hq.HybridKVCache(shape, dev)
     hq.quantize_kv(c4, K, V, A4.contiguous(), proxy)
@@ -421,6 +459,13 @@ def main():
         print(json.dumps({"error": "no GPU visible"}))
         sys.exit(3)
     dev = torch.device("cuda:0")
+    if args.only_selector:
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(args.seed)
+        rows = {"selector": bench_selector(torch, hq, gen, dev),
+                "selector_alg1": bench_selector_alg1(torch, hq, gen, dev)}
+        print(json.dumps({"rows": rows}), flush=True)
+        return
     if args.only_alg1:
         gen = torch.Generator(device=dev)
         gen.manual_seed(args.seed)
