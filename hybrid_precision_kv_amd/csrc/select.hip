@@ -76,7 +76,8 @@ __device__ inline const uint16_t* proxy_row(const SelectParams& p, int b, int hk
 // per 16-row block rb and entry idx = 64 g + 16 q4 + n (row 16 rb + n, channels 32 g + 8 q4 ..
 // + 7): pq16 = f16 with the nibble-pair channel order and 1/16 on k-slots 2,3,6,7 (INT4 keys),
 // pqbf = bf16 in natural order (bf16 keys).  Rows >= R are zero.  Also the per-row group sums
-// qsum[r][g] = sum_{c in g} q[r][c] (fp32 of the f16-rounded q, as the MFMA uses it).
+// qsum[r][g] = 2^-24 sum_{c in g} q[r][c] (fp32 of the f16-rounded q, as the MFMA uses it, in
+// the units of the subnormal f16 codes).
 __global__ __launch_bounds__(256) void select_prep_kernel(SelectParams p) {
   const int hb = blockIdx.y, b = hb / p.Hkv, hkv = hb % p.Hkv;
   const int R = p.n_proxy * p.G, RB = (R + 15) >> 4;
@@ -105,7 +106,7 @@ __global__ __launch_bounds__(256) void select_prep_kernel(SelectParams p) {
     const uint16_t* row = proxy_row(p, b, hkv, r) + 32 * g;
     float s = 0.f;
     for (int c = 0; c < 32; ++c) s += (float)(_Float16)bf16_bits_to_f32(row[c]);
-    p.qsum[(size_t)hb * R * 4 + idx] = s;
+    p.qsum[(size_t)hb * R * 4 + idx] = s * (1.0f / 16777216.0f);  // in the codes' 2^-24 units
   }
 }
 
@@ -212,31 +213,29 @@ __device__ inline void scoresB(const KeyOpsB& o, const bf16x8 (&bq)[4], float (&
 // B operands (and per-row values) of row block rb, loaded one block ahead of their use.
 // INT4: entry [group g][lane]; bf16: the lane's rows at channels 32 q4 + 8 tt .. +7 =
 // prepared entry [group q4][16 tt + n].
+// Every load is unconditional and used as loaded (row indices past R are clamped: those rows
+// are masked by the caller), so a block's loads stay in flight while the previous block runs.
 template <int PASS, int KIND>
 struct RowBlock {
   f16x8 b4[KIND == 0 ? 4 : 1];
   bf16x8 bb[KIND == 0 ? 1 : 4];
-  float qsb, M, iz;
+  float qsb, M;  // M: the row's max plus log2 of its normaliser (pass 2)
 };
 template <int PASS, int KIND>
 __device__ inline void load_rows(const SelectParams& p, size_t hb, int R, int rb, int lane, RowBlock<PASS, KIND>& x) {
   const int n = lane & 15, q4 = lane >> 4;
+  const int r = min(rb * 16 + n, R - 1);
   if constexpr (KIND == 0) {
     const f16x8* pq16 = (const f16x8*)p.pq16 + (hb * p.rb_stride + rb) * 256;
 #pragma unroll
     for (int g = 0; g < 4; ++g) x.b4[g] = pq16[g * 64 + lane];
-    const int rq = rb * 16 + n;  // minima MFMA B operand: row lane%16, group lane/16
-    x.qsb = rq < R ? p.qsum[(hb * R + rq) * 4 + q4] * (1.0f / 16777216.0f) : 0.0f;
+    x.qsb = p.qsum[(hb * R + r) * 4 + q4];  // minima MFMA B operand: row lane%16, group lane/16
   } else {
     const bf16x8* pqbf = (const bf16x8*)p.pqbf + (hb * p.rb_stride + rb) * 256;
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) x.bb[tt] = pqbf[q4 * 64 + 16 * tt + n];
   }
-  if (PASS == 2) {
-    const int r = rb * 16 + n;
-    x.M = r < R ? p.rowstat[(hb * R + r) * 2] : 0.0f;
-    x.iz = r < R ? p.rowstat[(hb * R + r) * 2 + 1] : 0.0f;
-  }
+  if (PASS == 2) x.M = p.rowstat[(hb * R + r) * 2];
 }
 
 // Sweep of the proxy rows for one wave's keys (KIND 0: INT4 tile, 1: bf16 keys).  PASS 1
@@ -252,15 +251,12 @@ __device__ inline void sweep(const SelectParams& p, const KeySrc& ks, size_t hb,
   KeyOpsB kb;
   if (KIND == 0) load_keys4(p, ks, hb, lane, k4);
   else load_keysB(p, ks, hb, lane, kb);
-  RowBlock<PASS, KIND> cur, nxt;
-  load_rows(p, hb, R, 0, lane, cur);
-  for (int rb = 0; rb < RB; ++rb) {
-    if (rb + 1 < RB) load_rows(p, hb, R, rb + 1, lane, nxt);
+  auto block = [&](const RowBlock<PASS, KIND>& x, int rb) {
     const int r = rb * 16 + n;
     const bool rvalid = r < R;
     float sc[8];
-    if constexpr (KIND == 0) scores4(k4, cur.b4, cur.qsb, sc);
-    else scoresB(kb, cur.bb, sc);
+    if constexpr (KIND == 0) scores4(k4, x.b4, x.qsb, sc);
+    else scoresB(kb, x.bb, sc);
     if (PASS == 1) {
       float m = -INFINITY;
 #pragma unroll
@@ -278,9 +274,20 @@ __device__ inline void sweep(const SelectParams& p, const KeySrc& ks, size_t hb,
       }
     } else if (rvalid) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) colsum[j] += valid[j] ? __builtin_amdgcn_exp2f(sc[j] - cur.M) * cur.iz : 0.f;
+      for (int j = 0; j < 8; ++j) colsum[j] += valid[j] ? __builtin_amdgcn_exp2f(sc[j] - x.M) : 0.f;
     }
-    cur = nxt;
+  };
+  // two row blocks in flight: the loads of block rb + 1 are issued before block rb runs.  The
+  // loads are unconditional (past the last block they re-read it) so that the compiler can
+  // count them and wait only for the block about to run.
+  RowBlock<PASS, KIND> b0, b1;
+  load_rows(p, hb, R, 0, lane, b0);
+  for (int rb = 0; rb < RB; rb += 2) {
+    load_rows(p, hb, R, min(rb + 1, RB - 1), lane, b1);
+    block(b0, rb);
+    if (rb + 1 >= RB) break;
+    load_rows(p, hb, R, min(rb + 2, RB - 1), lane, b0);
+    block(b1, rb + 1);
   }
 }
 
@@ -360,7 +367,8 @@ __global__ __launch_bounds__(SW * 64) __attribute__((amdgpu_waves_per_eu(3))) vo
   }
 }
 
-// row partials -> (max, 1 / normaliser) per row: one wave per row, lanes over the tasks
+// row partials -> (max + log2 normaliser, 1 / normaliser) per row: one wave per row, lanes
+// over the tasks
 __global__ __launch_bounds__(256) void select_rowmerge_kernel(SelectParams p) {
   const int hb = blockIdx.y, lane = threadIdx.x & 63;
   const int R = p.n_proxy * p.G;
@@ -380,8 +388,8 @@ __global__ __launch_bounds__(256) void select_rowmerge_kernel(SelectParams p) {
   }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) S += shfl_xor_f(S, o);
-  if (lane == 0) {
-    p.rowstat[((size_t)hb * R + r) * 2] = M;
+  if (lane == 0) {  // exp2(s - M') = exp2(s - M) / S
+    p.rowstat[((size_t)hb * R + r) * 2] = S > 0.f ? M + __log2f(S) : INFINITY;
     p.rowstat[((size_t)hb * R + r) * 2 + 1] = 1.0f / S;
   }
 }
