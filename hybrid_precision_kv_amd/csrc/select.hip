@@ -169,12 +169,14 @@ __device__ inline void load_keysB(const SelectParams& p, const KeySrc& ks, size_
   }
 }
 
-// Scores (log2 domain, alpha included) of this lane's 8 (key, row) pairs for one row block:
-// keys 4q4 + j (block 0) and 16 + 4q4 + j (block 1), row r0 + n.
+// Raw scores of this lane's 8 (key, row) pairs for one row block -- keys 4q4 + j (block 0) and
+// 16 + 4q4 + j (block 1), row r0 + n -- in units where SCALE4 / SCALEB (log2 e / sqrt(128),
+// times 2^24 for the INT4 codes) turns them into log2-domain scores.
 // INT4: q.k = sum_g s_g (q_g . code_g) + sum_g m_g qsum_g; codes carry 2^-24 and qsb carries
 // the rows' group sums times 2^-24 (B operand: group lane/16, row lane%16).
+constexpr float SCALE4 = LOG2E * 0.08838834764831845f * 16777216.0f;
+constexpr float SCALEB = LOG2E * 0.08838834764831845f;
 __device__ inline void scores4(const KeyOps4& o, const f16x8 (&bq)[4], float qsb, float (&sc)[8]) {
-  const float c = LOG2E * 0.08838834764831845f * 16777216.0f;
   f32x4 v0 = __builtin_amdgcn_mfma_f32_16x16x4f32(o.ma[0], qsb, (f32x4){0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
   f32x4 v1 = __builtin_amdgcn_mfma_f32_16x16x4f32(o.ma[1], qsb, (f32x4){0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
   f32x4 acc0[4], acc1[4];
@@ -190,13 +192,12 @@ __device__ inline void scores4(const KeyOps4& o, const f16x8 (&bq)[4], float qsb
       v0[j] = fmaf(o.sc[0][g][j], acc0[g][j], v0[j]);
       v1[j] = fmaf(o.sc[1][g][j], acc1[g][j], v1[j]);
     }
-    sc[j] = v0[j] * c;
-    sc[4 + j] = v1[j] * c;
+    sc[j] = v0[j];
+    sc[4 + j] = v1[j];
   }
 }
 
 __device__ inline void scoresB(const KeyOpsB& o, const bf16x8 (&bq)[4], float (&sc)[8]) {
-  const float alpha_log2 = LOG2E * 0.08838834764831845f;
   f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int tt = 0; tt < 4; ++tt) {
@@ -205,8 +206,8 @@ __device__ inline void scoresB(const KeyOpsB& o, const bf16x8 (&bq)[4], float (&
   }
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    sc[j] = a0[j] * alpha_log2;
-    sc[4 + j] = a1[j] * alpha_log2;
+    sc[j] = a0[j];
+    sc[4 + j] = a1[j];
   }
 }
 
@@ -241,31 +242,34 @@ __device__ inline void load_rows(const SelectParams& p, size_t hb, int R, int rb
 // Sweep of the proxy rows for one wave's keys (KIND 0: INT4 tile, 1: bf16 keys).  PASS 1
 // writes the wave's per-row (max, sum exp2) partial to red[wave][r]; PASS 2 accumulates the
 // column sums of the lane's 8 keys into colsum.
-template <int PASS, int KIND>
+// FULL: all 32 keys of the tile are valid (every tile but a segment's last)
+template <int PASS, int KIND, bool FULL>
 __device__ inline void sweep(const SelectParams& p, const KeySrc& ks, size_t hb, int lane, int wave,
                              const bool (&valid)[8], float* red, float (&colsum)[8]) {
   const int n = lane & 15, q4 = lane >> 4;
   const int R = p.n_proxy * p.G;
   const int RB = (R + 15) >> 4;
+  const float c = KIND == 0 ? SCALE4 : SCALEB;
   KeyOps4 k4;
   KeyOpsB kb;
   if (KIND == 0) load_keys4(p, ks, hb, lane, k4);
   else load_keysB(p, ks, hb, lane, kb);
+  auto ok = [&](int j) { return FULL || valid[j]; };
   auto block = [&](const RowBlock<PASS, KIND>& x, int rb) {
     const int r = rb * 16 + n;
     const bool rvalid = r < R;
-    float sc[8];
-    if constexpr (KIND == 0) scores4(k4, x.b4, x.qsb, sc);
-    else scoresB(kb, x.bb, sc);
+    float v[8];
+    if constexpr (KIND == 0) scores4(k4, x.b4, x.qsb, v);
+    else scoresB(kb, x.bb, v);
     if (PASS == 1) {
-      float m = -INFINITY;
+      float m = -INFINITY;  // max of the raw scores; c > 0, so c * max = max of the scaled ones
 #pragma unroll
-      for (int j = 0; j < 8; ++j) m = valid[j] ? fmaxf(m, sc[j]) : m;
-      m = col4_max(m);
+      for (int j = 0; j < 8; ++j) m = ok(j) ? fmaxf(m, v[j]) : m;
+      m = col4_max(m) * c;
       float s = 0.f;
       if (m != -INFINITY) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) s += valid[j] ? __builtin_amdgcn_exp2f(sc[j] - m) : 0.f;
+        for (int j = 0; j < 8; ++j) s += ok(j) ? __builtin_amdgcn_exp2f(fmaf(v[j], c, -m)) : 0.f;
       }
       s = col4_sum(s);
       if (q4 == 0 && rvalid) {
@@ -274,7 +278,7 @@ __device__ inline void sweep(const SelectParams& p, const KeySrc& ks, size_t hb,
       }
     } else if (rvalid) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) colsum[j] += valid[j] ? __builtin_amdgcn_exp2f(sc[j] - x.M) : 0.f;
+      for (int j = 0; j < 8; ++j) colsum[j] += ok(j) ? __builtin_amdgcn_exp2f(fmaf(v[j], c, -x.M)) : 0.f;
     }
   };
   // two row blocks in flight: the loads of block rb + 1 are issued before block rb runs.  The
@@ -315,8 +319,14 @@ __global__ __launch_bounds__(SW * 64) __attribute__((amdgpu_waves_per_eu(3))) vo
   }
   float colsum[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   if (has) {
-    if (ks.kind == 0) sweep<PASS, 0>(p, ks, hb, lane, wave, valid, red, colsum);
-    else sweep<PASS, 1>(p, ks, hb, lane, wave, valid, red, colsum);
+    const bool full = (ks.tile + 1) * 32 <= ks.count;
+    if (ks.kind == 0) {
+      if (full) sweep<PASS, 0, true>(p, ks, hb, lane, wave, valid, red, colsum);
+      else sweep<PASS, 0, false>(p, ks, hb, lane, wave, valid, red, colsum);
+    } else {
+      if (full) sweep<PASS, 1, true>(p, ks, hb, lane, wave, valid, red, colsum);
+      else sweep<PASS, 1, false>(p, ks, hb, lane, wave, valid, red, colsum);
+    }
   } else if (PASS == 1 && q4 == 0) {
     for (int r = n; r < R; r += 16) {  // no keys: empty partials
       red[((size_t)wave * R + r) * 2] = -INFINITY;
