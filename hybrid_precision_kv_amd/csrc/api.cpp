@@ -154,16 +154,23 @@ int cu_count() {
   return n;
 }
 
-// Splits per (b, KV head): one full round of workgroups -- two decode workgroups fit on a CU
-// (register budget) -- and at least ~4 tiles per wave.
+// Splits per (b, KV head).  Long streams per worker: one full round of two workgroups per CU
+// (the register budget fits two) when every wave still gets >= 16 tiles.  Otherwise the call
+// is latency bound and one workgroup per CU does better, with about 4 tiles per wave but never
+// fewer than 16 splits (measured at batch 1: 16 splits best at 1K and 4K tokens, 32 at 16K
+// and 32K; at batch 16 x 32K, 4 splits = two workgroups per CU).
 int auto_splits(const hyq_cache_t* c) {
   const int G = c->shape.n_q_heads / c->shape.n_kv_heads;
   const long units = (long)nheads(&c->shape) * ((G + 3) / 4);
   const long tiles = (c->n_int4 + 31) / 32 + 3 * ((c->n_anchor + 31) / 32 + (c->n_staged + 31) / 32 + 4);
-  const long target = 2L * cu_count();
-  long s = (target + units - 1) / units;
-  const long by_work = (tiles + 15) / 16;
-  if (s > by_work) s = by_work;
+  const long cus = cu_count();
+  long s = (2 * cus + units - 1) / units;
+  if (tiles < 16 * 4 * s) {
+    s = (cus + units - 1) / units;
+    long by_work = (tiles + 15) / 16;
+    if (by_work < 16) by_work = 16;
+    if (s > by_work) s = by_work;
+  }
   if (s < 1) s = 1;
   if (s > 256) s = 256;
   return (int)s;
