@@ -289,7 +289,9 @@ __global__ __launch_bounds__(256) void refresh_gather_kernel(RefreshParams p) {
 // 32 g + 4 sub + e (e < 4) of K (kv = 0) or V (kv = 1); the group's min and max come from a
 // reduction over its 8 lanes, and every code follows the group quantizer's formula.  A V code
 // is one nibble of a dword shared by 8 slots: each slot is written by exactly one move, so the
-// nibble is replaced with one atomic XOR of (old ^ new), which commutes with the other slots'.
+// nibble is replaced with one atomic XOR of (old ^ new), which commutes with the other slots'
+// (and is skipped when the nibble already holds the code: the atomics, not the read, bound
+// this kernel).  The next move's list entry is loaded while the current move runs.
 constexpr int MOVE_BLOCKS = 16;
 
 __device__ inline void put_vcode(uint8_t* slab, int slot, int c, uint32_t code) {
@@ -320,8 +322,12 @@ __global__ __launch_bounds__(256) void refresh_move_kernel(RefreshParams p) {
   int32_t* slot_pos = p.slot_pos + hb * (size_t)p.int4_cap;
   const size_t aslab = (size_t)p.anchor_cap * D, sslab = (size_t)p.staging_cap * D;
   const int kv = lane >> 5, g = (lane >> 3) & 3, sub = lane & 7;
-  for (int t = blockIdx.x * 4 + (threadIdx.x >> 6); t < n; t += waves) {
-    const int dst = s.mv_dst[t], kind = s.mv_kind[t], src = s.mv_src[t];
+  int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  int ndst = 0, nkind = 0, nsrc = 0;
+  if (t < n) { ndst = s.mv_dst[t]; nkind = s.mv_kind[t]; nsrc = s.mv_src[t]; }
+  for (; t < n; t += waves) {
+    const int dst = ndst, kind = nkind, src = nsrc;
+    if (t + waves < n) { ndst = s.mv_dst[t + waves]; nkind = s.mv_kind[t + waves]; nsrc = s.mv_src[t + waves]; }
     const int src_cap = kind == 0 ? p.anchor_cap : kind == 1 ? p.staging_cap : p.int4_cap;
     if (dst < 0 || dst >= p.int4_cap || src < 0 || src >= src_cap) continue;
     if (kind <= 1) {
