@@ -258,6 +258,12 @@ def bench_decode_bs1(torch, hq, gen, dev, ctxs=(1024, 4096, 16384, 32768), Hq=32
                        "hbm_frac": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4), "bytes_per_step": nbytes,
                        "resident_MB": round(layers * nbytes / 1e6, 1), "us_per_step_eager": round(us_eager, 2),
                        "graph_equal": bool(torch.equal(got, ref))}
+        if not all_bf16 and B == 1:
+            # full step on one layer: append + decode per token, select-and-refresh every 64
+            # (host-driven, per-call events: the batch-1 append and decode times include launch gaps)
+            m = bench_maintenance(torch, hq, lay[0][0], B, Hkv, G, L, gen, dev, ws, o, 0)
+            out[str(L)]["full_step_us_eager"] = m["us_per_token_amortized"]
+            out[str(L)]["select_refresh_us"] = m["select_refresh_us"]
         del lay, ws
         torch.cuda.empty_cache()
     return out
@@ -445,20 +451,32 @@ def cpu_baseline(args, G, bytes_per_head):
         c = pol.HybridCacheRef(g=G)
         c.freeze(s.K, s.V, A)
         heads.append((c, nm.bf16_to_f32(s.queries(1)[:, 0])))
-    t0 = time.perf_counter()
-    passes = 0
-    while True:  # whole passes over the sample until >= 10 s of oracle work
-        for c, q in heads:
-            Kh, Vh = c.stored_kv()
-            att.decode_ref(q, Kh, Vh)
-        passes += 1
-        dt = time.perf_counter() - t0
-        if dt >= 10.0 or passes >= 200:
-            break
-    gbs = bytes_per_head * len(heads) * passes / dt / 1e9
-    return {"value": round(gbs, 3), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{passes} passes over {len(heads)} (sequence, KV head) caches of {args.ctx} positions, "
-                      f"GQA {G}, one decode step each ({dt:.1f} s; a full step is {args.batch * args.hkv} such heads)"}
+    def run(seconds):  # whole passes over the sample until >= `seconds` of oracle work
+        t0 = time.perf_counter()
+        passes = 0
+        while True:
+            for c, q in heads:
+                Kh, Vh = c.stored_kv()
+                att.decode_ref(q, Kh, Vh)
+            passes += 1
+            dt = time.perf_counter() - t0
+            if dt >= seconds or passes >= 200:
+                return bytes_per_head * len(heads) * passes / dt / 1e9, passes, dt
+
+    gbs, passes, dt = run(10.0)
+    res = {"value": round(gbs, 3), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+           "sample": f"{passes} passes over {len(heads)} (sequence, KV head) caches of {args.ctx} positions, "
+                     f"GQA {G}, one decode step each ({dt:.1f} s; a full step is {args.batch * args.hkv} such heads)"}
+    try:  # the same oracle on one thread
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1):
+            gbs1, passes1, dt1 = run(3.0)
+        res["value_1thread"] = round(gbs1, 3)
+        res["sample_1thread"] = f"{passes1} passes, {dt1:.1f} s"
+    except Exception as e:  # threadpoolctl missing: report the all-core figure only
+        res["value_1thread"] = None
+        res["sample_1thread"] = f"not measured ({type(e).__name__})"
+    return res
 
 
 def main():
