@@ -120,3 +120,41 @@ def test_prefill_workspace_layout_and_errors(lib):
     assert f(C.byref(one), 0x10, 0x20, 0x30, 1000, None, 0, 0x40, None, need, None) == 4
     assert f(C.byref(one), 0x10, 0x20, 0x30, (1 << 20) + 1, None, 0, 0x40, 0x50, need, None) == 2
     assert f(C.byref(one), 0x10, 0x20, 0x30, 1000, 0x60, one.anchor_cap + 1, 0x40, 0x50, need, None) == 3
+
+
+def test_prefill_mx_shares_the_prefill_checks(lib):
+    one = _shape(batch=1, n_q_heads=32, n_kv_heads=8)
+    from tests.gpu_layout import prefill_ws_offsets
+    need = prefill_ws_offsets(32, 8, 1000, one.anchor_cap)["total"]
+    f = lib.hyq_prefill_attn_mx
+    assert f(C.byref(_shape(batch=2)), 0x10, 0x20, 0x30, 1000, None, 0, 0x40, 0x50, need, None) == 2
+    assert f(C.byref(one), None, 0x20, 0x30, 1000, None, 0, 0x40, 0x50, need, None) == 1
+    assert f(C.byref(one), 0x10, 0x20, 0x30, 1000, 0x60, 873, 0x40, 0x50, need, None) == 1
+    assert f(C.byref(one), 0x10, 0x20, 0x30, 1000, None, 0, 0x40, 0x50, need - 1, None) == 4
+    assert f(C.byref(one), 0x10, 0x20, 0x30, 1000, 0x60, one.anchor_cap + 1, 0x40, 0x50, need, None) == 3
+
+
+def test_select_tail_workspace_and_errors(lib):
+    s = _shape(batch=2, n_q_heads=8, n_kv_heads=2)
+    r256 = lambda x: (x + 255) // 256 * 256
+    for L in (1, 128, 129, 1000, 32768):
+        P = max(1, L - 128)
+        assert lib.hyq_workspace_bytes(C.byref(s), _lib.HYQ_OP_SELECT_TAIL, L, 0) == \
+            r256(2 * 8 * 128 * 4) + r256(2 * 8 * P * 4)
+    assert lib.hyq_workspace_bytes(C.byref(s), _lib.HYQ_OP_SELECT_TAIL, 0, 0) == 0
+    f = lib.hyq_select_vlines_tail
+    need = lib.hyq_workspace_bytes(C.byref(s), _lib.HYQ_OP_SELECT_TAIL, 1000, 0)
+    # null tensors, bad lengths, k outside [0, P], missing output -> INVALID; small ws -> WORKSPACE
+    assert f(C.byref(s), None, 1000, 0x20, 64, 10, 0x30, None, 0x40, need, None) == 1
+    assert f(C.byref(s), 0x10, 1000, None, 64, 10, 0x30, None, 0x40, need, None) == 1
+    assert f(C.byref(s), 0x10, 0, 0x20, 64, 0, 0x30, None, 0x40, need, None) == 1
+    assert f(C.byref(s), 0x10, 1000, 0x20, 0, 10, 0x30, None, 0x40, need, None) == 1
+    assert f(C.byref(s), 0x10, 1000, 0x20, 64, 873, 0x30, None, 0x40, need, None) == 1
+    assert f(C.byref(s), 0x10, 1000, 0x20, 64, -1, 0x30, None, 0x40, need, None) == 1
+    assert f(C.byref(s), 0x10, 1000, 0x20, 64, 10, None, None, 0x40, need, None) == 1
+    assert f(C.byref(s), 0x10, 1000, 0x20, 64, 10, 0x30, None, 0x40, need - 1, None) == 4
+    assert f(C.byref(s), 0x10, 1000, 0x20, 64, 10, 0x30, None, None, need, None) == 4
+    assert f(C.byref(_shape(head_dim=64)), 0x10, 1000, 0x20, 64, 10, 0x30, None, 0x40, need, None) == 2
+    # no candidates: k = 0 is accepted and nothing is launched; k = 1 is rejected
+    assert f(C.byref(s), 0x10, 128, 0x20, 64, 0, None, None, None, 0, None) == 0
+    assert f(C.byref(s), 0x10, 128, 0x20, 64, 1, 0x30, None, 0x40, need, None) == 1
