@@ -564,6 +564,21 @@ def main():
         for _ in range(5):
             b2.copy_(a)
         torch.cuda.synchronize()
+    # context for the peak: the read rate a plain streaming reduction reaches on this device
+    # (torch's row sums over 4 GiB of fp32 resident in HBM, 4 KB rows; bytes read / time.  Of
+    # the torch reductions tried, row sums read fastest: a full sum reaches about 4 TB/s)
+    probe = torch.ones(1 << 30, dtype=torch.float32, device=dev).view(1 << 20, 1024)
+    for _ in range(3):
+        probe.sum(dim=1)
+    torch.cuda.synchronize()
+    pe0, pe1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    pe0.record()
+    for _ in range(10):
+        probe.sum(dim=1)
+    pe1.record()
+    torch.cuda.synchronize()
+    read_probe = probe.numel() * 4 * 10 / (pe0.elapsed_time(pe1) * 1e-3) / 1e9
+    del probe
     workload = f"qwen3-8b-shape decode bs{B} ctx{L} hq{Hq} hkv{Hkv} layers{nl}"
     traffic = stored_traffic(workload)
     line = {
@@ -587,7 +602,9 @@ def main():
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "kernel": "hyq_decode_attn (split-K kernel + merge kernel, timed together)",
                      "kernel_us_mean": round(mean_us, 2),
-                     "kernel_us_p50": round(per[len(per) // 2], 2), "kernel_us_p90": round(per[int(0.9 * len(per))], 2)},
+                     "kernel_us_p50": round(per[len(per) // 2], 2), "kernel_us_p90": round(per[int(0.9 * len(per))], 2),
+                     "read_probe_GBs": round(read_probe, 1),
+                     "read_probe": "torch row sums over 4 GiB resident fp32 (context for the peak, not the peak)"},
         "wall_s_timed": round(wall, 3),
     }
     c0 = layers[0][0]
