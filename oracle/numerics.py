@@ -83,13 +83,14 @@ def dequant_asym(codes, s16, m16) -> np.ndarray:
     return sf * np.asarray(codes).astype(F32) + mf
 
 
-def quant_int4_token(x_row, group: int = 32):
+def quant_int4_token(x_row, group: int = 32, bits: int = 4):
     """Quantize one or more token vectors ``[..., D]`` in contiguous groups of ``group``
-    channels (INT4, 15 levels).  Returns codes ``[..., D]`` and s16, m16 ``[..., D/group]``."""
+    channels with 2^bits - 1 levels (INT4: 15; the bit width is a parameter of the HyQuant
+    paper's Alg. 3 and Alg. 4).  Returns codes ``[..., D]`` and s16, m16 ``[..., D/group]``."""
     x = np.asarray(x_row, dtype=F32)
     D = x.shape[-1]
     xg = x.reshape(x.shape[:-1] + (D // group, group))
-    c, s, m = quant_asym(xg, 15)
+    c, s, m = quant_asym(xg, (1 << bits) - 1)
     return c.reshape(x.shape), s, m
 
 

@@ -97,13 +97,15 @@ class HybridCacheRef:
       STAGED -- left the window since the last refresh, bf16 (staging buffer)
       ANCHOR -- vertical-line positions, bf16
       INT4   -- everything else: per token, per 32-channel group asymmetric INT4 with
-                fp16 scale and minimum (numerics.quant_asym)
+                fp16 scale and minimum (numerics.quant_asym); ``bits`` = 8 stores this bulk
+                with 255 levels instead (the bit width is a parameter of Alg. 3 and Alg. 4)
     The value of a position is its bf16 value, or the dequantized INT4 value.
     """
 
     def __init__(self, D: int = 128, W: int = 128, group: int = 32, g: int = 4,
-                 proxy_cap: int = 64):
+                 proxy_cap: int = 64, bits: int = 4):
         self.D, self.W, self.group, self.g, self.proxy_cap = D, W, group, g, proxy_cap
+        self.bits = bits
         self.L = 0
         self.kind = np.zeros(0, np.int8)
         self.kb = np.zeros((0, D), np.uint16)  # bf16 K (valid for WIN/STAGED/ANCHOR)
@@ -135,9 +137,9 @@ class HybridCacheRef:
         """Quantize the bf16 values held at ``pos`` to INT4 (Alg. 4 Quant, G = 32)."""
         if len(pos) == 0:
             return
-        c, s, m = nm.quant_int4_token(nm.bf16_to_f32(self.kb[pos]), self.group)
+        c, s, m = nm.quant_int4_token(nm.bf16_to_f32(self.kb[pos]), self.group, self.bits)
         self.kc[pos], self.ks[pos], self.km[pos] = c, s, m
-        c, s, m = nm.quant_int4_token(nm.bf16_to_f32(self.vb[pos]), self.group)
+        c, s, m = nm.quant_int4_token(nm.bf16_to_f32(self.vb[pos]), self.group, self.bits)
         self.vc[pos], self.vs[pos], self.vm[pos] = c, s, m
         self.kind[pos] = INT4
 

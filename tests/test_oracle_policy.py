@@ -287,3 +287,21 @@ def test_tail_mean_planted_and_degenerate():
     assert S.shape == (2, L - 128)
     idx0, S0 = pol.select_tail_mean(nm.f32_to_bf16(K[:, :128]), nm.f32_to_bf16(Q))
     assert idx0.shape == (2, 0) and S0.shape == (2, 0)
+
+
+def test_cache_8bit_bulk_is_finer_and_keeps_the_rest():
+    """bits = 8 changes only the quantized bulk: windows, anchors and staging keep bf16, the
+    quantized positions are the same, and their error is smaller than with INT4."""
+    s = synth.HeadStream(91, 700, 4)
+    A, _ = pol.select_dense(s.K, s.queries(64))
+    c4, c8 = pol.HybridCacheRef(g=4), pol.HybridCacheRef(g=4, bits=8)
+    for c in (c4, c8):
+        c.freeze(s.K, s.V, A)
+    assert c4.counts() == c8.counts() and np.array_equal(c4.anchors(), c8.anchors())
+    K4, V4 = c4.stored_kv()
+    K8, V8 = c8.stored_kv()
+    K, V = nm.bf16_to_f32(s.K), nm.bf16_to_f32(s.V)
+    q = c4.kind[:700] == pol.INT4
+    assert np.array_equal(K8[~q], K[~q]) and np.array_equal(V8[~q], V[~q])
+    assert np.abs(K8[q] - K[q]).mean() < np.abs(K4[q] - K[q]).mean() / 8
+    assert c8.kc[:700][q].max() > 15
