@@ -23,8 +23,11 @@ int check_shape(const hyq_shape_t* s) {
   if (s->staging_cap <= 0 || s->staging_cap % 32 || s->int4_cap < 0 || s->int4_cap % 32 || s->anchor_cap < 0 ||
       s->anchor_cap % 32)
     return HYQ_ERR_INVALID;
+  if (s->bits != 0 && s->bits != 4 && s->bits != 8) return HYQ_ERR_UNSUPPORTED;
   return HYQ_OK;
 }
+
+int qbits(const hyq_shape_t* s) { return s->bits == 8 ? 8 : 4; }
 
 size_t nheads(const hyq_shape_t* s) { return (size_t)s->batch * s->n_kv_heads; }
 
@@ -54,6 +57,7 @@ hyq::CacheView view(const hyq_cache_t* c) {
   v.anchor_cap = c->shape.anchor_cap;
   v.staging_cap = c->shape.staging_cap;
   v.proxy_cap = c->shape.proxy_cap;
+  v.bits = qbits(&c->shape);
   return v;
 }
 
@@ -197,7 +201,7 @@ int hyq_cache_buffer_bytes(const hyq_shape_t* s, size_t bytes[HYQ_NBUF]) {
   if (st) return st;
   if (!bytes) return HYQ_ERR_INVALID;
   const size_t H = nheads(s);
-  bytes[HYQ_BUF_INT4] = H * s->int4_cap * 160;  // 5120-byte record per 32-slot tile
+  bytes[HYQ_BUF_INT4] = H * s->int4_cap * (qbits(s) == 8 ? 288 : 160);  // 5120 / 9216-byte record per 32-slot tile
   bytes[HYQ_BUF_SLOT_POS] = H * s->int4_cap * 4;
   bytes[HYQ_BUF_A_K] = H * s->anchor_cap * D * 2;
   bytes[HYQ_BUF_A_V] = H * s->anchor_cap * D * 2;
@@ -296,6 +300,7 @@ int hyq_decode_attn(const hyq_cache_t* c, const void* q, float* o, int32_t n_spl
   p.Hkv = c->shape.n_kv_heads;
   p.G = c->shape.n_q_heads / c->shape.n_kv_heads;
   p.int4_cap = c->shape.int4_cap;
+  p.bits = qbits(&c->shape);
   p.anchor_cap = c->shape.anchor_cap;
   p.staging_cap = c->shape.staging_cap;
   p.n_int4 = c->n_int4;
@@ -345,6 +350,7 @@ int hyq_select_vlines(const hyq_shape_t* shape, hyq_cache_t* cache, const void* 
     p.G = G;
     p.len = len;
     p.int4_cap = shape->int4_cap;
+    p.bits = qbits(shape);
     p.anchor_cap = shape->anchor_cap;
     p.staging_cap = shape->staging_cap;
     if (dense) {
@@ -390,6 +396,7 @@ int hyq_select_vlines(const hyq_shape_t* shape, hyq_cache_t* cache, const void* 
     r.len = len;
     r.k = k;
     r.int4_cap = shape->int4_cap;
+    r.bits = qbits(shape);
     r.anchor_cap = shape->anchor_cap;
     r.staging_cap = shape->staging_cap;
     r.n_int4_old = cache->n_int4;

@@ -29,11 +29,14 @@ __device__ inline int slot_to_pos(const int32_t* anc, int n_anchor, int s) {
 // nibble j of a V-code dword -> k-slot e (inverse of kslot_nibble)
 __device__ inline int nibble_kslot(int j) { return ((j & 3) << 1) | (j >> 2); }
 
-// ---------------------------------------------------------------- Freeze: INT4 slots
+// ---------------------------------------------------------------- Freeze: quantized slots
+// BITS = 4: the INT4 record; BITS = 8: byte codes, 255 levels (same record structure)
+template <int BITS>
 __global__ __launch_bounds__(256) void freeze_int4_kernel(CacheView c, const uint16_t* __restrict__ k,
                                                           const uint16_t* __restrict__ v, int len,
                                                           const int32_t* __restrict__ anchors, int n_anchor,
                                                           int n_int4) {
+  typedef QL<BITS> L;
   __shared__ uint8_t vlds[D][32];
   const int tile = blockIdx.x, b = blockIdx.z, hkv = blockIdx.y;
   const size_t hb = (size_t)b * c.Hkv + hkv;
@@ -42,7 +45,7 @@ __global__ __launch_bounds__(256) void freeze_int4_kernel(CacheView c, const uin
   const int slot = tile * 32 + sl;
   bool valid = slot < n_int4;
   const int32_t* anc = anchors ? anchors + hb * (size_t)n_anchor : nullptr;
-  uint8_t* slab = c.int4 + hb * (size_t)c.int4_cap * 160;
+  uint8_t* slab = c.int4 + hb * (size_t)c.int4_cap * L::SLOT;
   int pos = valid ? slot_to_pos(anc, n_anchor, slot) : 0;
   if (pos >= len) { valid = false; pos = 0; }  // anchors outside [0, len - W): contract violation
 
@@ -60,42 +63,64 @@ __global__ __launch_bounds__(256) void freeze_int4_kernel(CacheView c, const uin
         x[j + 2 * e + 1] = bf16_bits_to_f32((uint16_t)(w[e] >> 16));
       }
     }
-    quant_group32(x, code, s16, m16);
+    quant_group32<(1 << BITS) - 1>(x, code, s16, m16);
   } else {
 #pragma unroll
     for (int j = 0; j < 32; ++j) code[j] = 0;
   }
   const uint32_t smw = (uint32_t)__half_as_ushort(s16) | ((uint32_t)__half_as_ushort(m16) << 16);
   if (kv == 0) {
-    u32x4 packed;
+    // the slot's group chunk: channel j at nibble j (INT4) or byte j (INT8)
 #pragma unroll
-    for (int d4 = 0; d4 < 4; ++d4) {
-      uint32_t w = 0;
+    for (int h = 0; h < BITS / 4; ++h) {
+      u32x4 packed;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) w |= (uint32_t)code[8 * d4 + j] << (4 * j);
-      packed[d4] = w;
+      for (int d4 = 0; d4 < 4; ++d4) {
+        uint32_t w = 0;
+#pragma unroll
+        for (int j = 0; j < 32 / BITS; ++j) w |= (uint32_t)code[16 * h + (32 / BITS) * d4 + j] << (BITS * j);
+        packed[d4] = w;
+      }
+      *(u32x4*)(slab + kcode_chunk_b<BITS>(slot, g) + 16 * h) = packed;
     }
-    *(u32x4*)(slab + kcode_chunk(slot, g)) = packed;
-    *(uint32_t*)(slab + ksm_byte(slot, g)) = smw;
+    *(uint32_t*)(slab + ksm_byte_b<BITS>(slot, g)) = smw;
     if (g == 0) c.slot_pos[hb * (size_t)c.int4_cap + slot] = valid ? pos : -1;
   } else {
-    *(uint32_t*)(slab + vsm_byte(slot, g)) = smw;
+    *(uint32_t*)(slab + vsm_byte_b<BITS>(slot, g)) = smw;
 #pragma unroll
     for (int j = 0; j < 32; ++j) vlds[32 * g + j][sl] = code[j];
   }
   __syncthreads();
-  uint32_t* vtile = (uint32_t*)(slab + (size_t)tile * T4_BYTES + T4_VC);
-  for (int d = t; d < 512; d += 256) {  // d = vcode_dword_in_tile(p, ch) for the quad's slots
-    const int l = (d & 255) >> 2, q = l >> 4, i = l & 15, r = 4 * (d >> 8) + (d & 3);
-    const int ch = 16 * r + i;
-    uint32_t w = 0;
+  uint32_t* vtile = (uint32_t*)(slab + (size_t)tile * L::TB + L::VC);
+  if (BITS == 4) {
+    for (int d = t; d < 512; d += 256) {  // d = vcode_dword_in_tile(p, ch) for the quad's slots
+      const int l = (d & 255) >> 2, q = l >> 4, i = l & 15, r = 4 * (d >> 8) + (d & 3);
+      const int ch = 16 * r + i;
+      uint32_t w = 0;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int e = nibble_kslot(j);
-      const int p = 4 * q + (e & 3) + 16 * (e >> 2);
-      w |= (uint32_t)vlds[ch][p] << (4 * j);
+      for (int j = 0; j < 8; ++j) {
+        const int e = nibble_kslot(j);
+        const int p = 4 * q + (e & 3) + 16 * (e >> 2);
+        w |= (uint32_t)vlds[ch][p] << (4 * j);
+      }
+      vtile[d] = w;
     }
-    vtile[d] = w;
+  } else {
+    // dword d = 2 entry + half8 of entry ((hf * 4 + q) * 16 + i) * 4 + r4: bytes 4 half8 .. + 3
+    for (int d = t; d < 1024; d += 256) {
+      const int entry = d >> 1, half8 = d & 1;
+      const int r4 = entry & 3, i = (entry >> 2) & 15, q = (entry >> 6) & 3, hf = entry >> 8;
+      const int ch = 16 * (4 * hf + r4) + i;
+      uint32_t w = 0;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const int byte = 4 * half8 + b;  // byte = kslot_byte(e): invert it
+        const int e = (byte & 4) | ((byte & 1) << 1) | ((byte >> 1) & 1);
+        const int p = 4 * q + (e & 3) + 16 * (e >> 2);
+        w |= (uint32_t)vlds[ch][p] << (8 * b);
+      }
+      vtile[d] = w;
+    }
   }
 }
 
@@ -219,7 +244,10 @@ hipError_t launch_freeze(const CacheView& c, const uint16_t* k, const uint16_t* 
   const int n_int4 = P - n_anchor;
   if (n_int4 > 0) {
     dim3 grid((n_int4 + 31) / 32, c.Hkv, c.B);
-    hipLaunchKernelGGL(freeze_int4_kernel, grid, dim3(256), 0, stream, c, k, v, len, anchors, n_anchor, n_int4);
+    if (c.bits == 8)
+      hipLaunchKernelGGL(freeze_int4_kernel<8>, grid, dim3(256), 0, stream, c, k, v, len, anchors, n_anchor, n_int4);
+    else
+      hipLaunchKernelGGL(freeze_int4_kernel<4>, grid, dim3(256), 0, stream, c, k, v, len, anchors, n_anchor, n_int4);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (n_anchor > 0) {

@@ -56,22 +56,50 @@ struct WaveState {
   f32x4 acc[8];
 };
 
-struct Int4Tile {
-  u32x4 kc0, kc1, vc0, vc1, ks0, ks1, vs0, vs1;
-};
+// 8 INT8 codes (two dwords) -> 8 f16 MFMA operands (subnormal bit patterns, exact: codes <=
+// 255).  Element order: bytes 0,2 | 1,3 | 4,6 | 5,7 (kslot_byte).
+__device__ inline f16x8 codes8_to_f16(uint32_t x0, uint32_t x1) {
+  u32x4 a;
+  a[0] = x0 & 0x00FF00FFu;
+  a[1] = (x0 >> 8) & 0x00FF00FFu;
+  a[2] = x1 & 0x00FF00FFu;
+  a[3] = (x1 >> 8) & 0x00FF00FFu;
+  return __builtin_bit_cast(f16x8, a);
+}
 
-// all loads of one 32-slot INT4 tile record for this lane; every one is a coalesced read of the
-// same 5 KB record
-__device__ inline void load_int4_tile(Int4Tile& x, const uint8_t* slab, int t, uint32_t lane16, uint32_t smoff) {
-  const uint8_t* rec = slab + (size_t)t * T4_BYTES;
-  x.kc0 = *(const u32x4*)(rec + lane16);
-  x.kc1 = *(const u32x4*)(rec + 1024 + lane16);
-  x.vc0 = *(const u32x4*)(rec + T4_VC + lane16);
-  x.vc1 = *(const u32x4*)(rec + T4_VC + 1024 + lane16);
-  x.ks0 = *(const u32x4*)(rec + T4_KSM + smoff);
-  x.ks1 = *(const u32x4*)(rec + T4_KSM + 256 + smoff);
-  x.vs0 = *(const u32x4*)(rec + T4_VSM + smoff);
-  x.vs1 = *(const u32x4*)(rec + T4_VSM + 256 + smoff);
+// one 32-slot tile record of the quantized store for this lane (BITS = 4: the 5 KB INT4
+// record, 16 B of K and of V codes per lane and block; BITS = 8: the 9 KB INT8 record, 32 B)
+template <int BITS>
+struct QTile {
+  u32x4 kc0[BITS / 4], kc1[BITS / 4], vc0[BITS / 4], vc1[BITS / 4];
+  u32x4 ks0, ks1, vs0, vs1;
+};
+typedef QTile<4> Int4Tile;
+
+// all loads of one tile record for this lane; every one is a coalesced read of the record
+template <int BITS>
+__device__ inline void load_int4_tile(QTile<BITS>& x, const uint8_t* slab, int t, uint32_t lane16, uint32_t smoff) {
+  typedef QL<BITS> L;
+  const uint8_t* rec = slab + (size_t)t * L::TB;
+  const uint32_t lo = lane16 * (BITS / 4);  // this lane's bytes inside a 16-slot block
+#pragma unroll
+  for (int h = 0; h < BITS / 4; ++h) {
+    x.kc0[h] = *(const u32x4*)(rec + lo + 16 * h);
+    x.kc1[h] = *(const u32x4*)(rec + 64 * L::CB + lo + 16 * h);
+    x.vc0[h] = *(const u32x4*)(rec + L::VC + lo + 16 * h);
+    x.vc1[h] = *(const u32x4*)(rec + L::VC + 64 * L::CB + lo + 16 * h);
+  }
+  x.ks0 = *(const u32x4*)(rec + L::KSM + smoff);
+  x.ks1 = *(const u32x4*)(rec + L::KSM + 256 + smoff);
+  x.vs0 = *(const u32x4*)(rec + L::VSM + smoff);
+  x.vs1 = *(const u32x4*)(rec + L::VSM + 256 + smoff);
+}
+// MFMA operand of 8 codes: K chunk dword tt (INT4) / dwords 2tt, 2tt+1 (INT8) of a block, or
+// V entry r4 of a half
+template <int BITS>
+__device__ inline f16x8 qcodes(const u32x4 (&c)[BITS / 4], int i) {
+  if constexpr (BITS == 4) return codes_to_f16(c[0][i]);
+  else return codes8_to_f16(c[i >> 1][2 * (i & 1)], c[i >> 1][2 * (i & 1) + 1]);
 }
 
 // online-softmax update for one tile; sc[8] are log2-domain scores (-inf = masked)
@@ -93,14 +121,14 @@ __device__ inline void tile_softmax(WaveState& st, const float (&sc)[8], float (
   st.l += ((pv[0] + pv[1]) + (pv[2] + pv[3])) + ((pv[4] + pv[5]) + (pv[6] + pv[7]));
 }
 
-template <bool MASK>
-__device__ inline void int4_tile(WaveState& st, const Int4Tile& x, const f16x8 (&bq)[4], float qsum24, float c_int4,
+template <int BITS, bool MASK>
+__device__ inline void int4_tile(WaveState& st, const QTile<BITS>& x, const f16x8 (&bq)[4], float qsum24, float c_int4,
                                  int base, int n_int4, int q4) {
   f32x4 S0 = {0.f, 0.f, 0.f, 0.f}, S1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int tt = 0; tt < 4; ++tt) {
-    S0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(codes_to_f16(x.kc0[tt]), bq[tt], S0, 0, 0, 0);
-    S1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(codes_to_f16(x.kc1[tt]), bq[tt], S1, 0, 0, 0);
+    S0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(qcodes<BITS>(x.kc0, tt), bq[tt], S0, 0, 0, 0);
+    S1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(qcodes<BITS>(x.kc1, tt), bq[tt], S1, 0, 0, 0);
   }
   float sc[8];
   bool valid[8];
@@ -129,8 +157,8 @@ __device__ inline void int4_tile(WaveState& st, const Int4Tile& x, const f16x8 (
   for (int j = 0; j < 8; ++j) {
     const uint32_t smv = j < 4 ? x.vs0[j] : x.vs1[j - 4];
     const float pj = pv[j];
-    // k-slots 2,3,6,7 meet codes multiplied by 16 (see codes_to_f16)
-    float pp = pj * half_lo(smv) * ((j & 2) ? PSCALE * 0.0625f : PSCALE);
+    // INT4: k-slots 2,3,6,7 meet codes multiplied by 16 (see codes_to_f16)
+    float pp = pj * half_lo(smv) * ((BITS == 4 && (j & 2)) ? PSCALE * 0.0625f : PSCALE);
     float mm = pj * half_hi(smv);
     if (MASK) {  // unused slots may hold any scale/min bits: keep them out entirely
       pp = valid[j] ? pp : 0.f;
@@ -144,13 +172,14 @@ __device__ inline void int4_tile(WaveState& st, const Int4Tile& x, const f16x8 (
   st.mt += mt;
   f16x8 a[8];
 #pragma unroll
-  for (int rr = 0; rr < 8; ++rr) a[rr] = codes_to_f16(rr < 4 ? x.vc0[rr] : x.vc1[rr - 4]);
+  for (int rr = 0; rr < 8; ++rr) a[rr] = rr < 4 ? qcodes<BITS>(x.vc0, rr) : qcodes<BITS>(x.vc1, rr - 4);
 #pragma unroll
   for (int rr = 0; rr < 8; ++rr) st.acc[rr] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[rr], bhi, st.acc[rr], 0, 0, 0);
 #pragma unroll
   for (int rr = 0; rr < 8; ++rr) st.acc[rr] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[rr], blo, st.acc[rr], 0, 0, 0);
 }
 
+template <int BITS>
 __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n = lane & 15, q4 = lane >> 4;
@@ -173,9 +202,9 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
     q_lds[h2][cp] = v;
   }
   __syncthreads();
-  // B operand of the INT4 path: q[head] restricted to this lane's column group, channels in
-  // the order the nibble extraction produces them (k-slots 2,3,6,7 divided by 16); zero
-  // outside the group
+  // B operand of the quantized path: q[head] restricted to this lane's column group, channels
+  // in the order the code extraction produces them (INT4: k-slots 2,3,6,7 divided by 16);
+  // zero outside the group
   f16x8 bq4[4];
   float qsum = 0.f;
   const bool use = head_ok && (g == q4);
@@ -190,7 +219,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float v = f[kslot_nibble(e)] * ((e & 2) ? 0.0625f : 1.0f);
+      const float v = BITS == 4 ? f[kslot_nibble(e)] * ((e & 2) ? 0.0625f : 1.0f) : f[kslot_byte(e)];
       bq4[t][e] = use ? (_Float16)v : (_Float16)0.f;
     }
   }
@@ -222,23 +251,23 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
   const int TA = (p.n_anchor + 31) >> 5, TS = (p.n_staged + 31) >> 5, TWn = (p.n_win + 31) >> 5;
   const int TB = TA + TS + TWn;
   const int wr = NW - 1 - w;  // bf16 tiles u with u % NW == wr
-  const uint8_t* slab = p.int4 + hb * (size_t)p.int4_cap * 160;
+  const uint8_t* slab = p.int4 + hb * (size_t)p.int4_cap * QL<BITS>::SLOT;
   const uint32_t lane16 = (uint32_t)lane * 16;
   const uint32_t smoff = (uint32_t)(g * 64 + q4 * 16);
   const int full = p.n_int4 >> 5;  // tiles below this index hold 32 valid slots
   if (w < T4) {
-    Int4Tile ta, tb;
+    QTile<BITS> ta, tb;
     int t = w;
     load_int4_tile(ta, slab, t, lane16, smoff);
     for (;;) {
       load_int4_tile(tb, slab, t + NW < T4 ? t + NW : t, lane16, smoff);
-      if (t < full) int4_tile<false>(st, ta, bq4, qsum24, c_int4, t * 32, p.n_int4, q4);
-      else int4_tile<true>(st, ta, bq4, qsum24, c_int4, t * 32, p.n_int4, q4);
+      if (t < full) int4_tile<BITS, false>(st, ta, bq4, qsum24, c_int4, t * 32, p.n_int4, q4);
+      else int4_tile<BITS, true>(st, ta, bq4, qsum24, c_int4, t * 32, p.n_int4, q4);
       t += NW;
       if (t >= T4) break;
       load_int4_tile(ta, slab, t + NW < T4 ? t + NW : t, lane16, smoff);
-      if (t < full) int4_tile<false>(st, tb, bq4, qsum24, c_int4, t * 32, p.n_int4, q4);
-      else int4_tile<true>(st, tb, bq4, qsum24, c_int4, t * 32, p.n_int4, q4);
+      if (t < full) int4_tile<BITS, false>(st, tb, bq4, qsum24, c_int4, t * 32, p.n_int4, q4);
+      else int4_tile<BITS, true>(st, tb, bq4, qsum24, c_int4, t * 32, p.n_int4, q4);
       t += NW;
       if (t >= T4) break;
     }
@@ -399,7 +428,8 @@ __global__ __launch_bounds__(64) void decode_reduce_kernel(const float* __restri
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
   const int nsub = (p.G + 3) >> 2;
   dim3 grid(p.n_splits, p.Hkv * nsub, p.B);
-  hipLaunchKernelGGL(decode_split_kernel, grid, dim3(256), 0, stream, p);
+  if (p.bits == 8) hipLaunchKernelGGL(decode_split_kernel<8>, grid, dim3(256), 0, stream, p);
+  else hipLaunchKernelGGL(decode_split_kernel<4>, grid, dim3(256), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(decode_reduce_kernel, dim3(p.B * p.Hkv * p.G), dim3(64), 0, stream, p.part, p.o, p.n_splits);

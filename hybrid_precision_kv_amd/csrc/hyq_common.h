@@ -73,6 +73,54 @@ __device__ __host__ inline size_t vsm_byte(int slot, int g) {
   return (size_t)(slot >> 5) * T4_BYTES + T4_VSM + 4 * (size_t)(((slot >> 4) & 1) * 64 + g * 16 + (slot & 15));
 }
 
+// Quantized store of BITS-bit codes (4: the INT4 record above; 8: the same structure with
+// byte codes).  Per 32-slot tile: K codes, V codes, K (scale, min), V (scale, min).
+template <int BITS>
+struct QL {
+  static constexpr int CB = 4 * BITS;         // bytes of one (slot, 32-channel group) K chunk
+  static constexpr int CODES = 512 * BITS;    // bytes of the K (and of the V) codes of a tile
+  static constexpr int VC = CODES;            // offset of the V codes
+  static constexpr int KSM = 2 * CODES;       // offset of the K (scale, min)
+  static constexpr int VSM = KSM + 512;       // offset of the V (scale, min)
+  static constexpr int TB = KSM + 1024;       // bytes per tile: 5120 (INT4), 9216 (INT8)
+  static constexpr int SLOT = TB / 32;        // bytes per slot: 160, 288
+};
+// K codes of (slot, group q4): CB bytes, channel 32 q4 + j at nibble j (INT4, 8 per dword) or
+// byte j (INT8); region = [16-slot block][q4][slot in block][CB]
+template <int BITS>
+__device__ __host__ inline size_t kcode_chunk_b(int slot, int q4) {
+  return (size_t)(slot >> 5) * QL<BITS>::TB +
+         (size_t)(((slot >> 4) & 1) * 64 * QL<BITS>::CB + q4 * 16 * QL<BITS>::CB + (slot & 15) * QL<BITS>::CB);
+}
+template <int BITS>
+__device__ __host__ inline size_t ksm_byte_b(int slot, int g) {
+  return (size_t)(slot >> 5) * QL<BITS>::TB + QL<BITS>::KSM + 4 * (size_t)(((slot >> 4) & 1) * 64 + g * 16 + (slot & 15));
+}
+template <int BITS>
+__device__ __host__ inline size_t vsm_byte_b(int slot, int g) {
+  return (size_t)(slot >> 5) * QL<BITS>::TB + QL<BITS>::VSM + 4 * (size_t)(((slot >> 4) & 1) * 64 + g * 16 + (slot & 15));
+}
+// INT8 V codes: entry (half, quad, channel & 15, r4) of 8 bytes holds channel 16 (4 half + r4)
+// + i for the 8 slots of the quad; the slot with k-slot e sits in byte kslot_byte(e) (bytes
+// (0,2), (1,3), (4,6), (5,7) are extracted with one mask each and feed k-slots (0,1) .. (6,7))
+__device__ __host__ inline int kslot_byte(int e) { return (e & 4) | ((e & 1) << 1) | ((e >> 1) & 1); }
+// V code of (slot, channel): byte offset of the dword holding it and the code's bit shift
+template <int BITS>
+__device__ __host__ inline void vcode_loc(int slot, int c, size_t& dword_off, int& shift) {
+  const size_t tile = (size_t)(slot >> 5) * QL<BITS>::TB + QL<BITS>::VC;
+  const int p = slot & 31;
+  if (BITS == 4) {
+    dword_off = tile + 4 * (size_t)vcode_dword_in_tile(p, c);
+    shift = 4 * kslot_nibble(tile_kslot(p));
+  } else {
+    const int byte = ((((c >> 6) * 4 + tile_quad(p)) * 16 + (c & 15)) * 4 + ((c >> 4) & 3)) * 8 + kslot_byte(tile_kslot(p));
+    dword_off = tile + (size_t)(byte & ~3);
+    shift = 8 * (byte & 3);
+  }
+}
+// bytes per slot of the quantized store for a shape's bit width (0 means 4)
+__device__ __host__ inline int qslot_bytes(int bits) { return bits == 8 ? QL<8>::SLOT : QL<4>::SLOT; }
+
 // bf16 K (anchors / staging / window): element index for (pos, channel).  Tile = 4096
 // elements: [16-pos block][8-channel chunk tt][quad q4 = channel / 32][pos in block][8].
 __device__ __host__ inline size_t kbf_index(int pos, int c) {
@@ -86,16 +134,17 @@ __device__ __host__ inline size_t vbf_index(int pos, int c) {
   return (size_t)t * 4096 + (size_t)((((c >> 4) * 4 + tile_quad(p)) * 16 + (c & 15)) * 8 + tile_kslot(p));
 }
 
-// ---------------------------------------------------------------- INT4 group quantizer
-// One token, 32 contiguous channels.  Fixed IEEE fp32 operation order (this translation
-// unit is built with -ffp-contract=off):
-//   mn = min x, mx = max x; s = fp16((mx - mn) / 15); m = fp16(mn);
-//   code = s == 0 ? 0 : clamp(rint((x - m) / s), 0, 15)
+// ---------------------------------------------------------------- group quantizer
+// One token, 32 contiguous channels, LEVELS = 2^bits - 1 (15 for INT4).  Fixed IEEE fp32
+// operation order (the translation units using it are built with -ffp-contract=off):
+//   mn = min x, mx = max x; s = fp16((mx - mn) / LEVELS); m = fp16(mn);
+//   code = s == 0 ? 0 : clamp(rint((x - m) / s), 0, LEVELS)
+template <int LEVELS = 15>
 __device__ inline void quant_group32(const float* x, uint8_t* code, __half& s16, __half& m16) {
   float mn = x[0], mx = x[0];
 #pragma unroll
   for (int j = 1; j < 32; ++j) { mn = fminf(mn, x[j]); mx = fmaxf(mx, x[j]); }
-  float s32 = __fdiv_rn(__fsub_rn(mx, mn), 15.0f);
+  float s32 = __fdiv_rn(__fsub_rn(mx, mn), (float)LEVELS);
   s16 = __float2half_rn(s32);
   m16 = __float2half_rn(mn);
   float sf = __half2float(s16), mf = __half2float(m16);
@@ -104,7 +153,7 @@ __device__ inline void quant_group32(const float* x, uint8_t* code, __half& s16,
     float c = 0.0f;
     if (sf != 0.0f) {
       c = rintf(__fdiv_rn(__fsub_rn(x[j], mf), sf));
-      c = fminf(fmaxf(c, 0.0f), 15.0f);
+      c = fminf(fmaxf(c, 0.0f), (float)LEVELS);
     }
     code[j] = (uint8_t)c;
   }

@@ -15,6 +15,7 @@ struct DecodeParams {
   int int4_cap, anchor_cap, staging_cap;
   int n_int4, n_anchor, n_staged, n_win;
   int n_splits;
+  int bits;  // codes of the quantized store: 4 or 8
 };
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream);
 
@@ -27,6 +28,7 @@ struct CacheView {
   uint16_t* proxy_q;
   int B, Hkv, G;
   int int4_cap, anchor_cap, staging_cap, proxy_cap;
+  int bits;  // codes of the quantized store: 4 or 8
 };
 
 struct SelectParams {
@@ -49,6 +51,7 @@ struct SelectParams {
   float* rowstat;  // [H][R][2]
   float* scores;   // [H][len - 128] by position
   int32_t* idx_out;  // [H][k]
+  int bits;          // codes of the quantized store: 4 or 8
 };
 hipError_t launch_select(SelectParams p, hipStream_t stream);
 int select_task_count(int n_tiles);
@@ -81,6 +84,7 @@ struct RefreshParams {
   size_t ws_per_head;
   int inset_words, del_words, max_moves;
   int* status;  // [H] 0 = counts consistent
+  int bits;     // codes of the quantized store: 4 or 8
 };
 hipError_t launch_refresh(const RefreshParams& p, hipStream_t stream);
 // bytes of per-head refresh scratch

@@ -39,6 +39,14 @@ __device__ inline f16x8 codes_to_f16(uint32_t x) {
   a[3] = y & 0x00F000F0u;
   return __builtin_bit_cast(f16x8, a);
 }
+__device__ inline f16x8 codes8_to_f16(uint32_t x0, uint32_t x1) {  // bytes 0,2 | 1,3 | 4,6 | 5,7
+  u32x4 a;
+  a[0] = x0 & 0x00FF00FFu;
+  a[1] = (x0 >> 8) & 0x00FF00FFu;
+  a[2] = x1 & 0x00FF00FFu;
+  a[3] = (x1 >> 8) & 0x00FF00FFu;
+  return __builtin_bit_cast(f16x8, a);
+}
 __device__ inline float half_lo(uint32_t v) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(v & 0xffff)); }
 __device__ inline float half_hi(uint32_t v) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(v >> 16)); }
 
@@ -74,7 +82,8 @@ __device__ inline const uint16_t* proxy_row(const SelectParams& p, int b, int hk
 
 // Operand prep, once per call: proxy rows in the two B-operand orders of the score MFMAs,
 // per 16-row block rb and entry idx = 64 g + 16 q4 + n (row 16 rb + n, channels 32 g + 8 q4 ..
-// + 7): pq16 = f16 with the nibble-pair channel order and 1/16 on k-slots 2,3,6,7 (INT4 keys),
+// + 7): pq16 = f16 with the nibble-pair channel order and 1/16 on k-slots 2,3,6,7 (INT4 keys;
+// INT8 keys: the byte-pair order, no factor),
 // pqbf = bf16 in natural order (bf16 keys).  Rows >= R are zero.  Also the per-row group sums
 // qsum[r][g] = 2^-24 sum_{c in g} q[r][c] (fp32 of the f16-rounded q, as the MFMA uses it, in
 // the units of the subnormal f16 codes).
@@ -97,7 +106,8 @@ __global__ __launch_bounds__(256) void select_prep_kernel(SelectParams p) {
     }
     f16x8 h;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) h[e] = (_Float16)(f[kslot_nibble(e)] * ((e & 2) ? 0.0625f : 1.0f));
+    for (int e = 0; e < 8; ++e)
+      h[e] = p.bits == 8 ? (_Float16)f[kslot_byte(e)] : (_Float16)(f[kslot_nibble(e)] * ((e & 2) ? 0.0625f : 1.0f));
     pq16[t] = h;
     pqbf[t] = __builtin_bit_cast(bf16x8, w);
   }
@@ -123,23 +133,29 @@ struct KeyOpsB {
   bf16x8 a[2][4];    // [block][8-channel chunk]
 };
 
+template <int BITS>
 __device__ inline void load_keys4(const SelectParams& p, const KeySrc& ks, size_t hb, int lane, KeyOps4& o) {
+  typedef QL<BITS> L;
   const int n = lane & 15, q4 = lane >> 4;
-  const uint8_t* rec = p.int4 + hb * (size_t)p.int4_cap * 160 + (size_t)ks.tile * T4_BYTES;
+  const uint8_t* rec = p.int4 + hb * (size_t)p.int4_cap * L::SLOT + (size_t)ks.tile * L::TB;
 #pragma unroll
   for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-    for (int g = 0; g < 4; ++g)
-      o.a[blk][g] = codes_to_f16(*(const uint32_t*)(rec + blk * 1024 + g * 256 + n * 16 + q4 * 4));
+    for (int g = 0; g < 4; ++g) {
+      // channels 32 g + 8 q4 .. + 7 of key n: a dword of nibbles (INT4) or two of bytes (INT8)
+      const uint8_t* c = rec + blk * 64 * L::CB + g * 16 * L::CB + n * L::CB + q4 * BITS;
+      if constexpr (BITS == 4) o.a[blk][g] = codes_to_f16(*(const uint32_t*)c);
+      else o.a[blk][g] = codes8_to_f16(((const uint32_t*)c)[0], ((const uint32_t*)c)[1]);
+    }
 #pragma unroll
   for (int blk = 0; blk < 2; ++blk) {
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      const u32x4 w = *(const u32x4*)(rec + T4_KSM + blk * 256 + g * 64 + q4 * 16);
+      const u32x4 w = *(const u32x4*)(rec + L::KSM + blk * 256 + g * 64 + q4 * 16);
 #pragma unroll
       for (int j = 0; j < 4; ++j) o.sc[blk][g][j] = half_lo(w[j]);
     }
-    o.ma[blk] = half_hi(*(const uint32_t*)(rec + T4_KSM + blk * 256 + 4 * lane));
+    o.ma[blk] = half_hi(*(const uint32_t*)(rec + L::KSM + blk * 256 + 4 * lane));
   }
 }
 
@@ -243,7 +259,7 @@ __device__ inline void load_rows(const SelectParams& p, size_t hb, int R, int rb
 // writes the wave's per-row (max, sum exp2) partial to red[wave][r]; PASS 2 accumulates the
 // column sums of the lane's 8 keys into colsum.
 // FULL: all 32 keys of the tile are valid (every tile but a segment's last)
-template <int PASS, int KIND, bool FULL>
+template <int PASS, int KIND, bool FULL, int BITS>
 __device__ inline void sweep(const SelectParams& p, const KeySrc& ks, size_t hb, int lane, int wave,
                              const bool (&valid)[8], float* red, float (&colsum)[8]) {
   const int n = lane & 15, q4 = lane >> 4;
@@ -252,7 +268,7 @@ __device__ inline void sweep(const SelectParams& p, const KeySrc& ks, size_t hb,
   const float c = KIND == 0 ? SCALE4 : SCALEB;
   KeyOps4 k4;
   KeyOpsB kb;
-  if (KIND == 0) load_keys4(p, ks, hb, lane, k4);
+  if (KIND == 0) load_keys4<BITS>(p, ks, hb, lane, k4);
   else load_keysB(p, ks, hb, lane, kb);
   auto ok = [&](int j) { return FULL || valid[j]; };
   auto block = [&](const RowBlock<PASS, KIND>& x, int rb) {
@@ -299,7 +315,7 @@ __device__ inline void sweep(const SelectParams& p, const KeySrc& ks, size_t hb,
 // blocks, reading the prepared B operands straight from L2 (no LDS staging, no barrier inside
 // the sweep).  PASS 1: per-row (max, sum exp2) over the workgroup's keys -- each wave keeps its
 // partial of every row in LDS, merged once at the end; PASS 2: column sums by position.
-template <int PASS>
+template <int PASS, int BITS>
 __global__ __launch_bounds__(SW * 64) __attribute__((amdgpu_waves_per_eu(3))) void select_pass_kernel(SelectParams p) {
   extern __shared__ float red[];  // PASS 1: [SW][R][2]
   const int task = blockIdx.x, hb = blockIdx.y;
@@ -321,11 +337,11 @@ __global__ __launch_bounds__(SW * 64) __attribute__((amdgpu_waves_per_eu(3))) vo
   if (has) {
     const bool full = (ks.tile + 1) * 32 <= ks.count;
     if (ks.kind == 0) {
-      if (full) sweep<PASS, 0, true>(p, ks, hb, lane, wave, valid, red, colsum);
-      else sweep<PASS, 0, false>(p, ks, hb, lane, wave, valid, red, colsum);
+      if (full) sweep<PASS, 0, true, BITS>(p, ks, hb, lane, wave, valid, red, colsum);
+      else sweep<PASS, 0, false, BITS>(p, ks, hb, lane, wave, valid, red, colsum);
     } else {
-      if (full) sweep<PASS, 1, true>(p, ks, hb, lane, wave, valid, red, colsum);
-      else sweep<PASS, 1, false>(p, ks, hb, lane, wave, valid, red, colsum);
+      if (full) sweep<PASS, 1, true, BITS>(p, ks, hb, lane, wave, valid, red, colsum);
+      else sweep<PASS, 1, false, BITS>(p, ks, hb, lane, wave, valid, red, colsum);
     }
   } else if (PASS == 1 && q4 == 0) {
     for (int r = n; r < R; r += 16) {  // no keys: empty partials
@@ -659,11 +675,15 @@ hipError_t launch_select(SelectParams p, hipStream_t stream) {
   hipLaunchKernelGGL(select_prep_kernel, dim3((RB * 256 + 255) / 256, H), dim3(256), 0, stream, p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   dim3 grid(p.n_tasks, H);
-  hipLaunchKernelGGL(select_pass_kernel<1>, grid, dim3(SW * 64), (size_t)SW * R * 2 * sizeof(float), stream, p);
+  if (p.bits == 8)
+    hipLaunchKernelGGL((select_pass_kernel<1, 8>), grid, dim3(SW * 64), (size_t)SW * R * 2 * sizeof(float), stream, p);
+  else
+    hipLaunchKernelGGL((select_pass_kernel<1, 4>), grid, dim3(SW * 64), (size_t)SW * R * 2 * sizeof(float), stream, p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(select_rowmerge_kernel, dim3((R + 3) / 4, H), dim3(256), 0, stream, p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(select_pass_kernel<2>, grid, dim3(SW * 64), 0, stream, p);
+  if (p.bits == 8) hipLaunchKernelGGL((select_pass_kernel<2, 8>), grid, dim3(SW * 64), 0, stream, p);
+  else hipLaunchKernelGGL((select_pass_kernel<2, 4>), grid, dim3(SW * 64), 0, stream, p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (p.k > 0) return launch_topk_keys((const uint32_t*)p.scores, p.len - WIN, p.k, H, p.idx_out, stream);
   return hipSuccess;

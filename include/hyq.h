@@ -30,7 +30,7 @@
  *  Inside a tile, position/slot p = 4q + (e & 3) + 16*(e >> 2) with quad q = 0..3 and
  *  k-slot e = 0..7; "lane" below means 16*q + (row within a 16-position block).
  *
- *  int4     u8 [hb][int4_cap/32][5120]  one record per 32-slot INT4 tile:
+ *  int4     u8 [hb][int4_cap/32][5120]  one record per 32-slot INT4 tile (shape.bits 0 or 4):
  *     [0, 2048)    K codes  [16-slot block][q4][slot in block][16 B]: the 16 bytes hold
  *                  channels 32*q4 .. 32*q4+31 of the slot, channel 2j in the low nibble of
  *                  byte j, 2j+1 in its high nibble;
@@ -38,6 +38,13 @@
  *                  of quad q, k-slot e in nibble HYQ_V_NIBBLE[e] (4 bits each, low first);
  *     [4096, 4608) K (scale, min) fp16 pairs [16-slot block][group g][slot in block];
  *     [4608, 5120) V (scale, min), same order.  Dequantized x = scale * code + min.
+ *  With shape.bits = 8 the same store holds 8-bit codes (255 levels of the same group
+ *  quantizer), one 9216-byte record per 32-slot tile:
+ *     [0, 4096)    K codes  [16-slot block][q4][slot in block][32 B]: byte j holds channel
+ *                  32*q4 + j of the slot;
+ *     [4096, 8192) V codes  [half][q][i][r4][8 B]: channel 16*(4*half + r4) + i of the 8
+ *                  slots of quad q, k-slot e in byte HYQ_V_BYTE[e];
+ *     [8192, 8704) K (scale, min), [8704, 9216) V (scale, min), as above.
  *  slot_pos i32 [hb][int4_cap]          position held by each INT4 slot (-1 for unused).
  *  a_k, s_k, w_k  bf16 [hb][cap/32][4096]  anchor / staging / window K, per tile
  *                  [16-position block][tt][q4][position in block][8]: channels
@@ -67,11 +74,14 @@ extern "C" {
 #define HYQ_PROXY_CAP 64
 /* nibble index (0..7, 4 bits each, low first) of k-slot e inside a V-code dword */
 #define HYQ_V_NIBBLE_INIT {0, 4, 1, 5, 2, 6, 3, 7}
+/* byte index (0..7) of k-slot e inside an 8-byte INT8 V-code entry */
+#define HYQ_V_BYTE_INIT {0, 2, 1, 3, 4, 6, 5, 7}
 
 /* status codes */
 #define HYQ_OK 0
 #define HYQ_ERR_INVALID 1      /* null pointer, bad dimension, inconsistent counters */
-#define HYQ_ERR_UNSUPPORTED 2  /* head_dim != 128, group != 32, window != 128, GQA not in {1,2,4,8,16} */
+#define HYQ_ERR_UNSUPPORTED 2  /* head_dim != 128, group != 32, window != 128, GQA not in {1,2,4,8,16},
+                                  bits not in {0, 4, 8} */
 #define HYQ_ERR_CAPACITY 3     /* len > capacity, k > anchor_cap or > candidates, staging full */
 #define HYQ_ERR_WORKSPACE 4    /* workspace missing or smaller than hyq_workspace_bytes */
 #define HYQ_ERR_HIP 5          /* a kernel launch failed (hipGetLastError) */
@@ -93,6 +103,8 @@ typedef struct {
   int32_t staging_cap;  /* staging capacity per head, multiple of 32, >= the refresh interval */
   int32_t int4_cap;     /* INT4 slots per head, multiple of 32 */
   int32_t anchor_cap;   /* anchor slots per head, multiple of 32 */
+  int32_t bits;         /* codes of the quantized bulk (B_K = B_V of the HyQuant paper's Alg. 3
+                           and Alg. 4): 0 or 4 = INT4 (the paper's K4V4), 8 = INT8 */
 } hyq_shape_t;
 
 typedef struct {

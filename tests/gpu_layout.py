@@ -9,6 +9,7 @@ import numpy as np
 
 D, W = 128, 128
 KSLOT_NIBBLE = np.array([0, 4, 1, 5, 2, 6, 3, 7])
+KSLOT_BYTE = np.array([0, 2, 1, 3, 4, 6, 5, 7])  # INT8 V entries (HYQ_V_BYTE_INIT)
 
 
 def _tile_pos(p):
@@ -19,22 +20,30 @@ def _tile_pos(p):
 
 
 def read_cache(cache) -> list:
-    """Per (b, h_kv): dict with int4 {pos: (kcodes[128], ksm[4,2], vcodes[128], vsm[4,2])},
+    """Per (b, h_kv): dict with int4 {pos: (kcodes[128], ksm[4,2], vcodes[128], vsm[4,2])} (the
+    quantized store, INT4 or INT8 by the shape's bits),
     anchors {pos: (k bf16[128], v bf16[128])}, staged, window (same), in numpy."""
     s = cache.shape
     H = s.batch * s.n_kv_heads
     ctr = cache.counters()
     host = {n: t.cpu().numpy() for n, t in cache.buffers.items()}
     nt = s.int4_cap // 32
-    rec = host["int4"][: H * nt * 5120].reshape(H, nt, 5120)
-    # K codes: [16-slot block][q4][slot in block][16 bytes]
-    kc = rec[:, :, :2048].reshape(H, nt, 2, 4, 16, 16)
-    kc = kc.transpose(0, 1, 2, 4, 3, 5).reshape(H, s.int4_cap, 64)  # -> [slot][64 bytes]
-    # V codes: [half][quad][channel & 15][4 dwords r4], channel = 16*(4*half + r4) + i
-    vc = np.ascontiguousarray(rec[:, :, 2048:4096]).view(np.uint32).reshape(H, nt, 2, 4, 16, 4)
+    bits = 8 if getattr(s, "bits", 4) == 8 else 4
+    CB = 4 * bits                 # bytes of one (slot, group) K chunk
+    CODES = 512 * bits            # bytes of the K (and of the V) codes of a tile
+    TB = 2 * CODES + 1024
+    rec = host["int4"][: H * nt * TB].reshape(H, nt, TB)
+    # K codes: [16-slot block][q4][slot in block][CB bytes]
+    kc = rec[:, :, :CODES].reshape(H, nt, 2, 4, 16, CB)
+    kc = kc.transpose(0, 1, 2, 4, 3, 5).reshape(H, s.int4_cap, 4 * CB)  # -> [slot][4 CB bytes]
+    # V codes: [half][quad][channel & 15][r4][4 / 8 bytes], channel = 16*(4*half + r4) + i
+    if bits == 4:
+        vc = np.ascontiguousarray(rec[:, :, CODES:2 * CODES]).view(np.uint32).reshape(H, nt, 2, 4, 16, 4)
+    else:
+        vc = np.ascontiguousarray(rec[:, :, CODES:2 * CODES]).reshape(H, nt, 2, 4, 16, 4, 8)
     # (scale, min): [16-slot block][g][slot in block][2]
-    ksm = np.ascontiguousarray(rec[:, :, 4096:4608]).view(np.float16).reshape(H, nt * 2, 4, 16, 2)
-    vsm = np.ascontiguousarray(rec[:, :, 4608:5120]).view(np.float16).reshape(H, nt * 2, 4, 16, 2)
+    ksm = np.ascontiguousarray(rec[:, :, 2 * CODES:2 * CODES + 512]).view(np.float16).reshape(H, nt * 2, 4, 16, 2)
+    vsm = np.ascontiguousarray(rec[:, :, 2 * CODES + 512:TB]).view(np.float16).reshape(H, nt * 2, 4, 16, 2)
     slot_pos = host["slot_pos"][: H * s.int4_cap * 4].view(np.int32).reshape(H, s.int4_cap)
 
     p32 = np.arange(32)
@@ -61,15 +70,22 @@ def read_cache(cache) -> list:
     nsl = s.int4_cap
     sl = np.arange(nsl)
     q, e = _tile_pos(sl & 31)
-    shift = 4 * KSLOT_NIBBLE[e]
     vcodes = np.empty((H, nsl, D), np.uint8)
-    for c in range(D):
-        i, r = c & 15, c >> 4
-        words = vc[:, sl >> 5, r >> 2, q, i, r & 3]
-        vcodes[:, :, c] = (words >> shift) & 0xF
     kcodes = np.empty((H, nsl, D), np.uint8)
-    kcodes[:, :, 0::2] = kc & 0xF
-    kcodes[:, :, 1::2] = kc >> 4
+    if bits == 4:
+        shift = 4 * KSLOT_NIBBLE[e]
+        for c in range(D):
+            i, r = c & 15, c >> 4
+            words = vc[:, sl >> 5, r >> 2, q, i, r & 3]
+            vcodes[:, :, c] = (words >> shift) & 0xF
+        kcodes[:, :, 0::2] = kc & 0xF
+        kcodes[:, :, 1::2] = kc >> 4
+    else:
+        byte = KSLOT_BYTE[e]
+        for c in range(D):
+            i, r = c & 15, c >> 4
+            vcodes[:, :, c] = vc[:, sl >> 5, r >> 2, q, i, r & 3, byte]
+        kcodes[:] = kc
     ksm_s = ksm.transpose(0, 1, 3, 2, 4)[:, sl >> 4, sl & 15]  # [H][slot][g][2]
     vsm_s = vsm.transpose(0, 1, 3, 2, 4)[:, sl >> 4, sl & 15]
 

@@ -158,3 +158,17 @@ def test_select_tail_workspace_and_errors(lib):
     # no candidates: k = 0 is accepted and nothing is launched; k = 1 is rejected
     assert f(C.byref(s), 0x10, 128, 0x20, 64, 0, None, None, None, 0, None) == 0
     assert f(C.byref(s), 0x10, 128, 0x20, 64, 1, 0x30, None, 0x40, need, None) == 1
+
+
+def test_bit_width_field(lib):
+    out4 = (C.c_size_t * _lib.HYQ_NBUF)()
+    out8 = (C.c_size_t * _lib.HYQ_NBUF)()
+    assert lib.hyq_cache_buffer_bytes(C.byref(_shape()), C.byref(out4)) == 0
+    assert lib.hyq_cache_buffer_bytes(C.byref(_shape(bits=4)), C.byref(out8)) == 0
+    assert list(out4) == list(out8)  # 0 means 4
+    assert lib.hyq_cache_buffer_bytes(C.byref(_shape(bits=8)), C.byref(out8)) == 0
+    b4, b8 = dict(zip(_lib.BUFFERS, list(out4))), dict(zip(_lib.BUFFERS, list(out8)))
+    assert b8["int4"] == 4 * 1024 * 288  # 9216-byte record per 32-slot tile
+    assert {k: v for k, v in b8.items() if k != "int4"} == {k: v for k, v in b4.items() if k != "int4"}
+    for bad in (2, 3, 16, -4):
+        assert lib.hyq_cache_buffer_bytes(C.byref(_shape(bits=bad)), C.byref(out8)) == 2
