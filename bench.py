@@ -55,6 +55,8 @@ def parse():
                     help="run only the selector rows (Eq. 4 selector and cache maintenance, Alg. 1 variant)")
     ap.add_argument("--only-alg1", action="store_true",
                     help="run only the Alg. 1-literal selector row (against the Eq. 4 selector)")
+    ap.add_argument("--only-bits", action="store_true",
+                    help="run only the bulk bit-width row (K4V4 against K8V8 decode)")
     ap.add_argument("--only-prefill", action="store_true",
                     help="run only the hybrid-prefill rows (for profiling the prefill kernels)")
     return ap.parse_args()
@@ -81,9 +83,10 @@ def stored_traffic(workload: str):
     return t.get("bytes_per_launch")
 
 
-def make_layer(torch, hq, shape, B, Hkv, G, L, gen, device, all_bf16=False):
+def make_layer(torch, hq, shape, B, Hkv, G, L, gen, device, all_bf16=False, keep=False):
     """One layer: planted-anchor K/V/proxies on the GPU, anchors, Freeze into a hybrid cache.
-    all_bf16: every candidate position is an anchor (k = P), so nothing is quantized."""
+    all_bf16: every candidate position is an anchor (k = P), so nothing is quantized.
+    keep: also return the bf16 K and V the cache was frozen from."""
     Hq = Hkv * G
     H = B * Hkv
     u = torch.randn(H, D, generator=gen, device=device)
@@ -113,6 +116,8 @@ def make_layer(torch, hq, shape, B, Hkv, G, L, gen, device, all_bf16=False):
             anchors = torch_select(torch, K, proxy, G, k)
     cache = hq.HybridKVCache(shape, device)
     hq.quantize_kv(cache, K, V, anchors, proxy)
+    if keep:
+        return cache, q, K, V
     del K, V
     return cache, q
 
@@ -137,7 +142,8 @@ def torch_select(torch, K, proxy, G, k, chunk=16):
 def algorithmic_bytes(cache, B, Hkv, Hq):
     c = cache.counters()
     n_win = min(c["len"], W)
-    per_head = 160 * c["n_int4"] + 512 * (c["n_anchor"] + c["n_staged"] + n_win)
+    slot = 288 if cache.shape.bits == 8 else 160  # K and V codes + fp16 scale/min per token
+    per_head = slot * c["n_int4"] + 512 * (c["n_anchor"] + c["n_staged"] + n_win)
     return B * Hkv * per_head + B * Hq * D * (2 + 4)
 
 
@@ -266,6 +272,58 @@ def bench_decode_bs1(torch, hq, gen, dev, ctxs=(1024, 4096, 16384, 32768), Hq=32
             out[str(L)]["select_refresh_us"] = m["select_refresh_us"]
         del lay, ws
         torch.cuda.empty_cache()
+    return out
+
+
+def bench_decode_bits(torch, hq, gen, dev, B=16, L=32768, Hq=32, Hkv=8, layers=8, n_ref=2):
+    """Bit width of the quantized bulk (B_K = B_V of the HyQuant paper's Alg. 3/4): the batched
+    workload's decode with a K4V4 and a K8V8 bulk, both with the 5% bf16 anchors and the bf16
+    window.  Per width: time per step (launches rotating over ``layers`` caches), the
+    algorithmic bytes (160 or 288 B per quantized token) and the output's relative L2 error
+    against fp32 attention over the unquantized bf16 K/V of the first ``n_ref`` sequences."""
+    G = Hq // Hkv
+    out = {}
+    for bits in (4, 8):
+        shape = hq.Shape.for_context(B, Hq, Hkv, L + 64, bits=bits)
+        lay = []
+        for i in range(layers):
+            lay.append(make_layer(torch, hq, shape, B, Hkv, G, L, gen, dev, keep=(i == 0)))
+        c0, q0, K, V = lay[0]
+        lay[0] = (c0, q0)
+        nbytes = algorithmic_bytes(c0, B, Hkv, Hq)
+        ws = hq.decode_workspace(shape, 0, dev)
+        o = torch.empty(B, Hq, D, dtype=torch.float32, device=dev)
+        hq.decode_attn(c0, q0, 0, o, ws)
+        torch.cuda.synchronize()
+        err = []
+        for b in range(n_ref):  # fp32 dense attention, right operands made contiguous first
+            qf = q0[b].float().view(Hkv, G, D)
+            kt = K[b].float().transpose(1, 2).contiguous()
+            p = torch.softmax(torch.bmm(qf, kt) / math.sqrt(D), dim=-1)
+            ref = torch.bmm(p, V[b].float().contiguous()).view(Hq, D)
+            err.append(((o[b] - ref).norm() / ref.norm()).item())
+        del K, V
+
+        # back-to-back launches with events only at the ends, as in the headline loop (a batched
+        # step is long enough that queued launches hide the binding's host cost)
+        steps = 10 * layers
+        for i in range(layers):
+            hq.decode_attn(*lay[i], 0, o, ws)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for i in range(steps):
+            hq.decode_attn(*lay[i % layers], 0, o, ws)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / steps
+        out[f"k{bits}v{bits}"] = {"us_per_step": round(us, 2), "GB_per_s": round(nbytes / (us * 1e-6) / 1e9, 1),
+                                  "hbm_frac": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                                  "bytes_per_step": nbytes, "rel_l2_vs_fp32_unquantized": round(max(err), 6)}
+        del lay, ws
+        torch.cuda.empty_cache()
+    out["note"] = (f"bs{B} ctx{L} hq{Hq} hkv{Hkv}, {layers} resident layers, hybrid 5% anchors + bf16 window; "
+                   f"error over sequences 0..{n_ref - 1} of the first layer")
     return out
 
 
@@ -503,6 +561,11 @@ def main():
         gen.manual_seed(args.seed)
         print(json.dumps({"rows": {"selector_alg1": bench_selector_alg1(torch, hq, gen, dev)}}), flush=True)
         return
+    if args.only_bits:
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(args.seed)
+        print(json.dumps({"rows": {"decode_bit_width": bench_decode_bits(torch, hq, gen, dev)}}), flush=True)
+        return
     if args.only_prefill:
         gen = torch.Generator(device=dev)
         gen.manual_seed(args.seed)
@@ -628,6 +691,8 @@ def main():
                 r["hybrid_speedup"] = round(r["us_per_step"] / hyb, 2)
         rows["decode_all_bf16"] = allbf
         print(f"[bench] all-bf16 sweep done", file=sys.stderr, flush=True)
+        rows["decode_bit_width"] = bench_decode_bits(torch, hq, gen, dev, B=B, L=L, Hq=Hq, Hkv=Hkv)
+        print(f"[bench] bit widths: {rows['decode_bit_width']}", file=sys.stderr, flush=True)
         for n in [int(x) for x in args.prefill_lens.split(",") if x]:
             rows[f"prefill_{n}"] = bench_prefill(torch, hq, gen, dev, n)
             print(f"[bench] prefill N={n}: {rows[f'prefill_{n}']['us_per_call']} us", file=sys.stderr, flush=True)
