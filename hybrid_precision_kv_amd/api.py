@@ -206,6 +206,34 @@ def decode_attn(cache: HybridKVCache, q: torch.Tensor, n_splits: int = 0, out: t
     return out
 
 
+def decode_ragged_workspace_bytes(shape: Shape, n_seq: int, n_splits: int = 0) -> int:
+    lib = _lib.load()
+    s = shape.c()
+    return int(lib.hyq_decode_ragged_workspace_bytes(C.byref(s), n_seq, n_splits))
+
+
+def decode_attn_ragged(caches: list, q: torch.Tensor, n_splits: int = 0, out: torch.Tensor | None = None,
+                       ws: torch.Tensor | None = None) -> torch.Tensor:
+    """Decode over a variable-length batch (hyq_decode_attn_ragged): ``caches`` are
+    single-sequence caches of any lengths with the same heads and bit width; q [n][Hq][128]
+    bf16, one row block per cache; fp32 out [n][Hq][128]."""
+    n = len(caches)
+    s = caches[0].shape
+    _bf16(q, (n, s.n_q_heads, D), "q")
+    if out is None:
+        out = torch.empty((n, s.n_q_heads, D), dtype=torch.float32, device=q.device)
+    need = decode_ragged_workspace_bytes(s, n, n_splits)
+    if need == 0:
+        raise ValueError("unsupported ragged batch (sequence count or split count out of range)")
+    if ws is None:
+        ws = _ws.get(need, q.device)
+    ptrs = (C.POINTER(_lib.HyqCache) * n)(*[C.pointer(c.c) for c in caches])
+    lib = _lib.load()
+    check("hyq_decode_attn_ragged", lib.hyq_decode_attn_ragged(ptrs, n, _ptr(q), _ptr(out), n_splits, _ptr(ws),
+                                                               ws.numel(), _stream()))
+    return out
+
+
 def select_vlines(shape: Shape, k: int, cache: HybridKVCache | None = None, dense_k: torch.Tensor | None = None,
                   proxy: torch.Tensor | None = None, apply: bool = False, scores: bool = False):
     """Vertical-line selector (hyq_select_vlines); returns idx [B][Hkv][k] (and scores)."""

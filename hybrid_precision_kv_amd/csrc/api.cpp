@@ -2,6 +2,7 @@
 // counters, workspace sizing and kernel launches.  Declarations and contracts: include/hyq.h.
 #include <atomic>
 #include <hip/hip_runtime.h>
+#include <mutex>
 #include <string.h>
 
 #include "../../include/hyq.h"
@@ -180,6 +181,75 @@ int auto_splits(const hyq_cache_t* c) {
   return (int)s;
 }
 
+// ---- variable-length batches: one decode launch over many single-sequence caches
+
+// Split plan.  Each sequence's work is counted in tiles as in auto_splits.  The chip's budget
+// of split columns (two workgroups per CU; one per CU when every wave would get fewer than
+// 16 tiles) is shared in proportion to the work, at least one split per sequence and, on the
+// short-batch budget, at most max(16, tiles / 16) splits.  The total never exceeds
+// ragged_split_bound().
+int ragged_columns(int Hkv, int G, bool two_per_cu) {
+  const long u1 = (long)Hkv * ((G + 3) / 4);
+  const long cus = cu_count();
+  return (int)(((two_per_cu ? 2 : 1) * cus + u1 - 1) / u1);
+}
+long ragged_split_bound(int n_seq, int Hkv, int G, int n_splits) {
+  return n_splits > 0 ? (long)n_seq * n_splits : (long)ragged_columns(Hkv, G, true) + 2L * n_seq;
+}
+long seq_tiles(const hyq_cache_t* c) {
+  return (c->n_int4 + 31) / 32 + 3 * ((c->n_anchor + 31) / 32 + (c->n_staged + 31) / 32 + 4);
+}
+void ragged_plan(const hyq_cache_t* const* cs, int n, int Hkv, int G, int n_splits, int* out) {
+  if (n_splits > 0) {
+    for (int i = 0; i < n; ++i) out[i] = n_splits;
+    return;
+  }
+  long total = 0;
+  for (int i = 0; i < n; ++i) total += seq_tiles(cs[i]);
+  long C = ragged_columns(Hkv, G, true);
+  const bool low = total < 64 * C;
+  if (low) C = ragged_columns(Hkv, G, false);
+  for (int i = 0; i < n; ++i) {
+    const long t = seq_tiles(cs[i]);
+    long s = (long)((double)C * (double)t / (double)total + 0.5);
+    if (low) {
+      const long cap = (t + 15) / 16 > 16 ? (t + 15) / 16 : 16;
+      if (s > cap) s = cap;
+    }
+    out[i] = (int)(s < 1 ? 1 : s);
+  }
+}
+
+// workspace of a variable-length decode: descriptors, split map, then the partial records
+struct RaggedWs {
+  size_t seqs, map, part, total;
+};
+RaggedWs ragged_ws(int n_seq, int Hq, int Hkv, int n_splits) {
+  RaggedWs w;
+  const long bound = ragged_split_bound(n_seq, Hkv, Hq / Hkv, n_splits);
+  w.seqs = 0;
+  w.map = r256((size_t)n_seq * sizeof(hyq::RaggedSeq));
+  w.part = w.map + r256((size_t)bound * 4);
+  w.total = w.part + (size_t)bound * Hq * (D + 2) * sizeof(float);
+  return w;
+}
+
+// Host staging of the per-call tables: page-locked slots used round-robin, each guarded by an
+// event recorded after its copy, so a slot is rewritten only once the device has taken its
+// previous contents.  One ring per device, created on first use.
+constexpr int RAGGED_MAX_SEQ = 1024;
+struct TableRing {
+  static constexpr int SLOTS = 16;
+  static constexpr size_t SLOT_BYTES = 256 * 1024;
+  std::mutex mu;
+  uint8_t* host = nullptr;
+  hipEvent_t ev[SLOTS] = {};
+  bool pending[SLOTS] = {};
+  int next = 0;
+};
+static_assert(RAGGED_MAX_SEQ * sizeof(hyq::RaggedSeq) + 16384 * 4 <= TableRing::SLOT_BYTES, "ring slot size");
+TableRing g_rings[64];
+
 }  // namespace
 
 extern "C" {
@@ -309,6 +379,101 @@ int hyq_decode_attn(const hyq_cache_t* c, const void* q, float* o, int32_t n_spl
   p.n_win = c->len < W ? c->len : W;
   p.n_splits = S;
   hipError_t e = hyq::launch_decode(p, stream);
+  return e == hipSuccess ? HYQ_OK : HYQ_ERR_HIP;
+}
+
+size_t hyq_decode_ragged_workspace_bytes(const hyq_shape_t* s, int32_t n_seq, int32_t n_splits) {
+  if (check_shape(s) || n_seq <= 0 || n_seq > RAGGED_MAX_SEQ || n_splits < 0 || n_splits > 4096) return 0;
+  return ragged_ws(n_seq, s->n_q_heads, s->n_kv_heads, n_splits).total;
+}
+
+int hyq_decode_attn_ragged(const hyq_cache_t* const* caches, int32_t n_seq, const void* q, float* o,
+                           int32_t n_splits, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!caches || n_seq <= 0 || !q || !o || n_splits < 0 || n_splits > 4096) return HYQ_ERR_INVALID;
+  if (n_seq > RAGGED_MAX_SEQ) return HYQ_ERR_CAPACITY;
+  int st;
+  for (int i = 0; i < n_seq; ++i) {
+    const hyq_cache_t* c = caches[i];
+    if (!c) return HYQ_ERR_INVALID;
+    if ((st = check_shape(&c->shape))) return st;
+    if ((st = check_cache_ptrs(c))) return st;
+    if ((st = check_counters(c))) return st;
+    if (c->shape.batch != 1 || c->len <= 0) return HYQ_ERR_INVALID;
+    if (c->shape.n_q_heads != caches[0]->shape.n_q_heads || c->shape.n_kv_heads != caches[0]->shape.n_kv_heads ||
+        qbits(&c->shape) != qbits(&caches[0]->shape))
+      return HYQ_ERR_INVALID;
+  }
+  const hyq_shape_t& s0 = caches[0]->shape;
+  const int Hq = s0.n_q_heads, Hkv = s0.n_kv_heads, G = Hq / Hkv;
+  const RaggedWs w = ragged_ws(n_seq, Hq, Hkv, n_splits);
+  if (!ws || ws_bytes < w.total) return HYQ_ERR_WORKSPACE;
+  int plan[RAGGED_MAX_SEQ];
+  ragged_plan(caches, n_seq, Hkv, G, n_splits, plan);
+  long total = 0;
+  for (int i = 0; i < n_seq; ++i) total += plan[i];
+  if (total > ragged_split_bound(n_seq, Hkv, G, n_splits) || total > 16384) return HYQ_ERR_INVALID;
+
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return HYQ_ERR_HIP;
+  TableRing& ring = g_rings[dev];
+  std::lock_guard<std::mutex> lock(ring.mu);
+  if (!ring.host) {
+    void* h = nullptr;
+    if (hipHostMalloc(&h, TableRing::SLOTS * TableRing::SLOT_BYTES, hipHostMallocDefault) != hipSuccess)
+      return HYQ_ERR_HIP;
+    for (int i = 0; i < TableRing::SLOTS; ++i)
+      if (hipEventCreateWithFlags(&ring.ev[i], hipEventDisableTiming) != hipSuccess) return HYQ_ERR_HIP;
+    ring.host = (uint8_t*)h;
+  }
+  const int slot = ring.next;
+  ring.next = (slot + 1) % TableRing::SLOTS;
+  if (ring.pending[slot] && hipEventSynchronize(ring.ev[slot]) != hipSuccess) return HYQ_ERR_HIP;
+  ring.pending[slot] = false;
+  uint8_t* host = ring.host + (size_t)slot * TableRing::SLOT_BYTES;
+  hyq::RaggedSeq* seqs = (hyq::RaggedSeq*)(host + w.seqs);
+  uint32_t* map = (uint32_t*)(host + w.map);
+  long rec = 0, col = 0;
+  for (int i = 0; i < n_seq; ++i) {
+    const hyq_cache_t* c = caches[i];
+    hyq::RaggedSeq& d = seqs[i];
+    memset(&d, 0, sizeof d);
+    d.int4 = (const uint8_t*)c->int4;
+    d.a_k = (const uint16_t*)c->a_k;
+    d.a_v = (const uint16_t*)c->a_v;
+    d.s_k = (const uint16_t*)c->s_k;
+    d.s_v = (const uint16_t*)c->s_v;
+    d.w_k = (const uint16_t*)c->w_k;
+    d.w_v = (const uint16_t*)c->w_v;
+    d.int4_cap = c->shape.int4_cap;
+    d.anchor_cap = c->shape.anchor_cap;
+    d.staging_cap = c->shape.staging_cap;
+    d.n_int4 = c->n_int4;
+    d.n_anchor = c->n_anchor;
+    d.n_staged = c->n_staged;
+    d.n_win = c->len < W ? c->len : W;
+    d.n_splits = plan[i];
+    d.rec0 = (int)rec;
+    rec += (long)Hq * plan[i];
+    for (int j = 0; j < plan[i]; ++j) map[col++] = ((uint32_t)i << 16) | (uint32_t)j;
+  }
+  // descriptors and map are contiguous in the slot as in the workspace: one copy
+  const size_t bytes = w.map + (size_t)total * 4;
+  if (hipMemcpyAsync(ws, host, bytes, hipMemcpyHostToDevice, stream) != hipSuccess) return HYQ_ERR_HIP;
+  if (hipEventRecord(ring.ev[slot], stream) != hipSuccess) return HYQ_ERR_HIP;
+  ring.pending[slot] = true;
+
+  hyq::RaggedDecodeParams p;
+  p.seqs = (const hyq::RaggedSeq*)((uint8_t*)ws + w.seqs);
+  p.split_map = (const uint32_t*)((uint8_t*)ws + w.map);
+  p.q = (const uint16_t*)q;
+  p.part = (float*)((uint8_t*)ws + w.part);
+  p.o = o;
+  p.n_seq = n_seq;
+  p.Hkv = Hkv;
+  p.G = G;
+  p.total_splits = (int)total;
+  p.bits = qbits(&s0);
+  hipError_t e = hyq::launch_decode_ragged(p, stream);
   return e == hipSuccess ? HYQ_OK : HYQ_ERR_HIP;
 }
 

@@ -179,18 +179,77 @@ __device__ inline void int4_tile(WaveState& st, const QTile<BITS>& x, const f16x
   for (int rr = 0; rr < 8; ++rr) st.acc[rr] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[rr], blo, st.acc[rr], 0, 0, 0);
 }
 
+// What one workgroup reads and writes: the slabs of one (sequence, KV head), its counters,
+// its split, the q rows of the KV group's Q heads and the group's first partial record.
+struct HeadWork {
+  const uint8_t* int4;
+  const uint16_t *a_k, *a_v, *s_k, *s_v, *w_k, *w_v;
+  const uint16_t* q;
+  float* rec;
+  int n_int4, n_anchor, n_staged, n_win;
+  int n_splits, split;
+};
+
+// uniform batch: every sequence has the same counters; grid (split, KV head x head block, b)
 template <int BITS>
-__global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
+__device__ inline HeadWork head_work(const DecodeParams& p, int hkv) {
+  const size_t hb = (size_t)blockIdx.z * p.Hkv + hkv;
+  const size_t qh = (size_t)blockIdx.z * p.Hkv * p.G + (size_t)hkv * p.G;
+  HeadWork h;
+  h.int4 = p.int4 + hb * (size_t)p.int4_cap * QL<BITS>::SLOT;
+  h.a_k = p.a_k + hb * (size_t)p.anchor_cap * D;
+  h.a_v = p.a_v + hb * (size_t)p.anchor_cap * D;
+  h.s_k = p.s_k + hb * (size_t)p.staging_cap * D;
+  h.s_v = p.s_v + hb * (size_t)p.staging_cap * D;
+  h.w_k = p.w_k + hb * (size_t)WIN * D;
+  h.w_v = p.w_v + hb * (size_t)WIN * D;
+  h.q = p.q + qh * D;
+  h.rec = p.part + qh * p.n_splits * (D + 2);
+  h.n_int4 = p.n_int4;
+  h.n_anchor = p.n_anchor;
+  h.n_staged = p.n_staged;
+  h.n_win = p.n_win;
+  h.n_splits = p.n_splits;
+  h.split = blockIdx.x;
+  return h;
+}
+
+// variable-length batch: grid x enumerates the splits of all sequences (split_map), each
+// sequence in its own single-sequence cache
+template <int BITS>
+__device__ inline HeadWork head_work(const RaggedDecodeParams& p, int hkv) {
+  const uint32_t m = p.split_map[blockIdx.x];
+  const int seq = (int)(m >> 16);
+  const RaggedSeq& d = p.seqs[seq];
+  HeadWork h;
+  h.int4 = d.int4 + (size_t)hkv * d.int4_cap * QL<BITS>::SLOT;
+  h.a_k = d.a_k + (size_t)hkv * d.anchor_cap * D;
+  h.a_v = d.a_v + (size_t)hkv * d.anchor_cap * D;
+  h.s_k = d.s_k + (size_t)hkv * d.staging_cap * D;
+  h.s_v = d.s_v + (size_t)hkv * d.staging_cap * D;
+  h.w_k = d.w_k + (size_t)hkv * WIN * D;
+  h.w_v = d.w_v + (size_t)hkv * WIN * D;
+  h.q = p.q + ((size_t)seq * p.Hkv * p.G + (size_t)hkv * p.G) * D;
+  h.rec = p.part + ((size_t)d.rec0 + (size_t)hkv * p.G * d.n_splits) * (D + 2);
+  h.n_int4 = d.n_int4;
+  h.n_anchor = d.n_anchor;
+  h.n_staged = d.n_staged;
+  h.n_win = d.n_win;
+  h.n_splits = d.n_splits;
+  h.split = (int)(m & 0xffffu);
+  return h;
+}
+
+template <int BITS, class Params>
+__global__ __launch_bounds__(256) void decode_split_kernel(Params p) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n = lane & 15, q4 = lane >> 4;
   const int hh = n >> 2, g = n & 3;
-  const int split = blockIdx.x, b = blockIdx.z;
   const int nsub = (p.G + 3) >> 2;
   const int hkv = blockIdx.y / nsub, sub = blockIdx.y % nsub;
   const int head = sub * 4 + hh;  // Q head inside the KV group
   const bool head_ok = head < p.G;
-  const size_t hb = (size_t)b * p.Hkv + hkv;
-  const int Hq = p.Hkv * p.G;
+  const HeadWork hw = head_work<BITS>(p, hkv);
 
   // ---- q of the (up to 4) Q heads of this head block, staged once through LDS
   __shared__ uint32_t q_lds[4][D / 2];
@@ -198,7 +257,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
     const int h2 = threadIdx.x >> 6, cp = threadIdx.x & 63;  // 256 threads x 2 channels
     const int hd = sub * 4 + h2;
     uint32_t v = 0;
-    if (hd < p.G) v = *(const uint32_t*)(p.q + ((size_t)b * Hq + (size_t)hkv * p.G + hd) * D + 2 * cp);
+    if (hd < p.G) v = *(const uint32_t*)(hw.q + (size_t)hd * D + 2 * cp);
     q_lds[h2][cp] = v;
   }
   __syncthreads();
@@ -246,41 +305,40 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
 
   // ---- work of this worker: INT4 tiles w, w + NW, w + 2 NW, ... (the workers of a head sweep
   // the head's records side by side); bf16 tiles go to the workers with the fewest INT4 tiles
-  const int NW = p.n_splits * WAVES, w = split * WAVES + wave;
-  const int T4 = (p.n_int4 + 31) >> 5;
-  const int TA = (p.n_anchor + 31) >> 5, TS = (p.n_staged + 31) >> 5, TWn = (p.n_win + 31) >> 5;
+  const int NW = hw.n_splits * WAVES, w = hw.split * WAVES + wave;
+  const int T4 = (hw.n_int4 + 31) >> 5;
+  const int TA = (hw.n_anchor + 31) >> 5, TS = (hw.n_staged + 31) >> 5, TWn = (hw.n_win + 31) >> 5;
   const int TB = TA + TS + TWn;
   const int wr = NW - 1 - w;  // bf16 tiles u with u % NW == wr
-  const uint8_t* slab = p.int4 + hb * (size_t)p.int4_cap * QL<BITS>::SLOT;
+  const uint8_t* slab = hw.int4;
   const uint32_t lane16 = (uint32_t)lane * 16;
   const uint32_t smoff = (uint32_t)(g * 64 + q4 * 16);
-  const int full = p.n_int4 >> 5;  // tiles below this index hold 32 valid slots
+  const int full = hw.n_int4 >> 5;  // tiles below this index hold 32 valid slots
   if (w < T4) {
     QTile<BITS> ta, tb;
     int t = w;
     load_int4_tile(ta, slab, t, lane16, smoff);
     for (;;) {
       load_int4_tile(tb, slab, t + NW < T4 ? t + NW : t, lane16, smoff);
-      if (t < full) int4_tile<BITS, false>(st, ta, bq4, qsum24, c_int4, t * 32, p.n_int4, q4);
-      else int4_tile<BITS, true>(st, ta, bq4, qsum24, c_int4, t * 32, p.n_int4, q4);
+      if (t < full) int4_tile<BITS, false>(st, ta, bq4, qsum24, c_int4, t * 32, hw.n_int4, q4);
+      else int4_tile<BITS, true>(st, ta, bq4, qsum24, c_int4, t * 32, hw.n_int4, q4);
       t += NW;
       if (t >= T4) break;
       load_int4_tile(ta, slab, t + NW < T4 ? t + NW : t, lane16, smoff);
-      if (t < full) int4_tile<BITS, false>(st, tb, bq4, qsum24, c_int4, t * 32, p.n_int4, q4);
-      else int4_tile<BITS, true>(st, tb, bq4, qsum24, c_int4, t * 32, p.n_int4, q4);
+      if (t < full) int4_tile<BITS, false>(st, tb, bq4, qsum24, c_int4, t * 32, hw.n_int4, q4);
+      else int4_tile<BITS, true>(st, tb, bq4, qsum24, c_int4, t * 32, hw.n_int4, q4);
       t += NW;
       if (t >= T4) break;
     }
   }
 
   // ---- bf16 tiles (anchors, staging, window)
-  const size_t slab_a = (size_t)p.anchor_cap * D, slab_s = (size_t)p.staging_cap * D, slab_w = (size_t)WIN * D;
   for (int u = wr; u < TB; u += NW) {
     const uint16_t *kb, *vb;
     int cnt, tl;
-    if (u < TA) { kb = p.a_k + hb * slab_a; vb = p.a_v + hb * slab_a; cnt = p.n_anchor; tl = u; }
-    else if (u < TA + TS) { kb = p.s_k + hb * slab_s; vb = p.s_v + hb * slab_s; cnt = p.n_staged; tl = u - TA; }
-    else { kb = p.w_k + hb * slab_w; vb = p.w_v + hb * slab_w; cnt = p.n_win; tl = u - TA - TS; }
+    if (u < TA) { kb = hw.a_k; vb = hw.a_v; cnt = hw.n_anchor; tl = u; }
+    else if (u < TA + TS) { kb = hw.s_k; vb = hw.s_v; cnt = hw.n_staged; tl = u - TA; }
+    else { kb = hw.w_k; vb = hw.w_v; cnt = hw.n_win; tl = u - TA - TS; }
     const int base = tl * 32;
     const uint16_t* kt = kb + (size_t)tl * 4096 + lane * 8;
     const uint16_t* vt = vb + (size_t)tl * 4096 + lane * 8;
@@ -364,7 +422,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
         L += red_l[ww][h2] * f;
       }
     }
-    float* rec = p.part + (((size_t)b * Hq + (size_t)hkv * p.G + hd) * p.n_splits + split) * (D + 2);
+    float* rec = hw.rec + ((size_t)hd * hw.n_splits + hw.split) * (D + 2);
     if (c == 0) { rec[0] = M; rec[1] = L; }
     rec[2 + c] = O;
   }
@@ -374,12 +432,20 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
 // ReduceSoftmax over the split records (HyQuant paper Alg. 3): one workgroup per (b, Q head).
 // A separate launch: the kernel boundary makes the records of all XCDs visible without the
 // L2 write-back an in-kernel agent-scope release would cost every workgroup.
+template <bool RAGGED>
 __global__ __launch_bounds__(64) void decode_reduce_kernel(const float* __restrict__ part, float* __restrict__ o,
-                                                           int n_splits) {
+                                                           int n_splits, const RaggedSeq* __restrict__ seqs, int Hq) {
   // one wave per (b, Q head); lane j holds split j's (m, l) (64 splits per pass), every load of
   // a pass is independent so the whole merge costs about one memory latency per pass
   const int bh = blockIdx.x, lane = threadIdx.x;
-  const float* rec = part + (size_t)bh * n_splits * (D + 2);
+  const float* rec;
+  if constexpr (RAGGED) {  // a variable-length batch: the sequence's own split count and records
+    const RaggedSeq& d = seqs[bh / Hq];
+    n_splits = d.n_splits;
+    rec = part + ((size_t)d.rec0 + (size_t)(bh % Hq) * n_splits) * (D + 2);
+  } else {
+    rec = part + (size_t)bh * n_splits * (D + 2);
+  }
   float M = -INFINITY;
   for (int s0 = 0; s0 < n_splits; s0 += 64) {
     const int s = s0 + lane;
@@ -428,11 +494,24 @@ __global__ __launch_bounds__(64) void decode_reduce_kernel(const float* __restri
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
   const int nsub = (p.G + 3) >> 2;
   dim3 grid(p.n_splits, p.Hkv * nsub, p.B);
-  if (p.bits == 8) hipLaunchKernelGGL(decode_split_kernel<8>, grid, dim3(256), 0, stream, p);
-  else hipLaunchKernelGGL(decode_split_kernel<4>, grid, dim3(256), 0, stream, p);
+  if (p.bits == 8) hipLaunchKernelGGL((decode_split_kernel<8, DecodeParams>), grid, dim3(256), 0, stream, p);
+  else hipLaunchKernelGGL((decode_split_kernel<4, DecodeParams>), grid, dim3(256), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_reduce_kernel, dim3(p.B * p.Hkv * p.G), dim3(64), 0, stream, p.part, p.o, p.n_splits);
+  hipLaunchKernelGGL(decode_reduce_kernel<false>, dim3(p.B * p.Hkv * p.G), dim3(64), 0, stream, p.part, p.o,
+                     p.n_splits, (const RaggedSeq*)nullptr, p.Hkv * p.G);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_ragged(const RaggedDecodeParams& p, hipStream_t stream) {
+  const int nsub = (p.G + 3) >> 2;
+  dim3 grid(p.total_splits, p.Hkv * nsub, 1);
+  if (p.bits == 8) hipLaunchKernelGGL((decode_split_kernel<8, RaggedDecodeParams>), grid, dim3(256), 0, stream, p);
+  else hipLaunchKernelGGL((decode_split_kernel<4, RaggedDecodeParams>), grid, dim3(256), 0, stream, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(decode_reduce_kernel<true>, dim3(p.n_seq * p.Hkv * p.G), dim3(64), 0, stream, p.part, p.o, 0,
+                     p.seqs, p.Hkv * p.G);
   return hipGetLastError();
 }
 

@@ -19,6 +19,31 @@ struct DecodeParams {
 };
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream);
 
+// One sequence of a variable-length batch: its own single-sequence cache (buffers at that
+// cache's b = 0) with its own counters and split count.  Built on the host, copied into the
+// decode workspace before the launch.
+struct RaggedSeq {
+  const uint8_t* int4;
+  const uint16_t *a_k, *a_v, *s_k, *s_v, *w_k, *w_v;
+  int int4_cap, anchor_cap, staging_cap;
+  int n_int4, n_anchor, n_staged, n_win;
+  int n_splits;  // splits of every KV head of this sequence
+  int rec0;      // first partial record of this sequence: records [rec0 + h * n_splits + s]
+  int pad[5];
+};
+static_assert(sizeof(RaggedSeq) == 112, "RaggedSeq layout");
+
+struct RaggedDecodeParams {
+  const RaggedSeq* seqs;      // [n_seq] (device)
+  const uint32_t* split_map;  // [total_splits] (device): seq << 16 | split within the sequence
+  const uint16_t* q;          // [n_seq][Hq][128]
+  float* part;                // partial (m, l, acc) records, 130 floats each
+  float* o;                   // [n_seq][Hq][128]
+  int n_seq, Hkv, G, total_splits;
+  int bits;
+};
+hipError_t launch_decode_ragged(const RaggedDecodeParams& p, hipStream_t stream);
+
 struct CacheView {
   uint8_t* int4;
   int32_t* slot_pos;

@@ -229,6 +229,34 @@ int hyq_select_vlines_tail(const hyq_shape_t* shape, const void* k, int32_t len,
 int hyq_decode_attn(const hyq_cache_t* cache, const void* q, float* o, int32_t n_splits,
                     void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* Decode attention over a variable-length batch (the HyQuant paper's Alg. 3 for each
+   sequence; the paper's batched decode runs sequences of one length).  Each sequence is its
+   own single-sequence cache (shape.batch = 1), sized for its own length and maintained on its
+   own cadence by hyq_append_token and hyq_select_vlines; this call decodes them together in
+   one launch of the split kernel and one of the merge.  Every cache must share n_q_heads,
+   n_kv_heads and bits; capacities and counters may differ.
+   caches: host array of n_seq pointers (1 <= n_seq <= 1024), read only.
+   q: device bf16 [n_seq][Hq][128]; o: device f32 [n_seq][Hq][128].
+   n_splits: splits per (sequence, KV head); 0 = automatic (the device's split columns are
+   shared in proportion to each sequence's tile count, at least one each).
+   ws: >= hyq_decode_ragged_workspace_bytes(&caches[0]->shape, n_seq, n_splits) bytes of
+   device scratch, no initialisation needed.  It receives a table of the caches' pointers
+   and counters and the split plan (about 112 bytes per sequence plus 4 per split), copied
+   from page-locked host memory owned by the library (one 4 MiB ring per device, allocated
+   on the first call) by one asynchronous host-to-device copy on `stream` before the
+   kernels; the call therefore cannot be recorded into a graph.  Calls sharing one workspace
+   must not overlap in time (same stream is fine).  Reads the caches only.
+   Errors: INVALID (null or mismatched cache, batch != 1, len = 0, n_splits > 4096 or more
+   than 16384 splits in all), UNSUPPORTED, CAPACITY (n_seq > 1024), WORKSPACE, HIP. */
+int hyq_decode_attn_ragged(const hyq_cache_t* const* caches, int32_t n_seq, const void* q, float* o,
+                           int32_t n_splits, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Workspace bytes of hyq_decode_attn_ragged for n_seq sequences whose heads match `s`
+   (s->batch is ignored): an upper bound over any lengths for the automatic plan
+   (n_splits = 0), exact for a fixed n_splits.  0 for an invalid shape or n_seq outside
+   1..1024. */
+size_t hyq_decode_ragged_workspace_bytes(const hyq_shape_t* s, int32_t n_seq, int32_t n_splits);
+
 /* Hybrid prefill attention (HyQuant paper §4.2 Eq. 6-7, Alg. 2), causal, one sequence per
    call (shape->batch must be 1; Q head h reads KV head h / (Hq / Hkv)).
    For query i: keys [i-127, i] and anchors a <= i-128 use bf16 Q.K and bf16 P.V; every

@@ -172,3 +172,45 @@ def test_bit_width_field(lib):
     assert {k: v for k, v in b8.items() if k != "int4"} == {k: v for k, v in b4.items() if k != "int4"}
     for bad in (2, 3, 16, -4):
         assert lib.hyq_cache_buffer_bytes(C.byref(_shape(bits=bad)), C.byref(out8)) == 2
+
+
+def test_ragged_decode_host_checks(lib):
+    """hyq_decode_attn_ragged: workspace closed form and every rejection before any device work."""
+    one = _shape(batch=1)
+    r256 = lambda x: -(-x // 256) * 256
+    n, S, Hq = 3, 5, one.n_q_heads
+    assert lib.hyq_decode_ragged_workspace_bytes(C.byref(one), n, S) == r256(n * 112) + r256(n * S * 4) + \
+        n * S * Hq * 130 * 4
+    assert lib.hyq_decode_ragged_workspace_bytes(C.byref(one), 0, S) == 0
+    assert lib.hyq_decode_ragged_workspace_bytes(C.byref(one), 1025, S) == 0
+    assert lib.hyq_decode_ragged_workspace_bytes(C.byref(one), n, 0) > 0  # automatic plan: a bound
+    caches = [_fake_cache(), _fake_cache(len=300, n_int4=160, n_anchor=12), _fake_cache(len=128, n_int4=0,
+                                                                                          n_anchor=0)]
+    for c in caches:
+        c.shape = one
+    arr = lambda cs: (C.POINTER(HyqCache) * len(cs))(*[C.pointer(c) for c in cs])
+    big = 1 << 40
+    assert lib.hyq_decode_attn_ragged(None, 3, 0x10, 0x20, 0, 0x30, big, None) == 1
+    assert lib.hyq_decode_attn_ragged(arr(caches), 0, 0x10, 0x20, 0, 0x30, big, None) == 1
+    assert lib.hyq_decode_attn_ragged(arr(caches), 3, None, 0x20, 0, 0x30, big, None) == 1
+    assert lib.hyq_decode_attn_ragged(arr(caches), 3, 0x10, 0x20, -1, 0x30, big, None) == 1
+    assert lib.hyq_decode_attn_ragged(arr(caches * 342), 1026, 0x10, 0x20, 0, 0x30, big, None) == 3
+    nulls = (C.POINTER(HyqCache) * 2)(C.pointer(caches[0]))
+    assert lib.hyq_decode_attn_ragged(nulls, 2, 0x10, 0x20, 0, 0x30, big, None) == 1
+    two = _fake_cache()  # batch 2: not a single-sequence cache
+    assert lib.hyq_decode_attn_ragged(arr([caches[0], two]), 2, 0x10, 0x20, 0, 0x30, big, None) == 1
+    other = _fake_cache()
+    other.shape = _shape(batch=1, n_q_heads=16)
+    assert lib.hyq_decode_attn_ragged(arr([caches[0], other]), 2, 0x10, 0x20, 0, 0x30, big, None) == 1
+    wide = _fake_cache()
+    wide.shape = _shape(batch=1, bits=8)
+    assert lib.hyq_decode_attn_ragged(arr([caches[0], wide]), 2, 0x10, 0x20, 0, 0x30, big, None) == 1
+    bad = _fake_cache(n_int4=5)
+    bad.shape = one
+    assert lib.hyq_decode_attn_ragged(arr([caches[0], bad]), 2, 0x10, 0x20, 0, 0x30, big, None) == 1
+    need = lib.hyq_decode_ragged_workspace_bytes(C.byref(one), 3, S)
+    assert lib.hyq_decode_attn_ragged(arr(caches), 3, 0x10, 0x20, S, 0x30, need - 1, None) == 4
+    assert lib.hyq_decode_attn_ragged(arr(caches), 3, 0x10, 0x20, S, None, need, None) == 4
+    # more than 16384 splits in all
+    assert lib.hyq_decode_attn_ragged(arr(caches * 2), 6, 0x10, 0x20, 4096, 0x30, big, None) == 1
+    assert [c.len for c in caches] == [1000, 300, 128]  # caches are read only
