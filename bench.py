@@ -57,6 +57,8 @@ def parse():
                     help="run only the Alg. 1-literal selector row (against the Eq. 4 selector)")
     ap.add_argument("--only-bits", action="store_true",
                     help="run only the bulk bit-width row (K4V4 against K8V8 decode)")
+    ap.add_argument("--only-ragged", action="store_true",
+                    help="run only the variable-length batch row")
     ap.add_argument("--only-prefill", action="store_true",
                     help="run only the hybrid-prefill rows (for profiling the prefill kernels)")
     return ap.parse_args()
@@ -306,9 +308,9 @@ def bench_decode_bits(torch, hq, gen, dev, B=16, L=32768, Hq=32, Hkv=8, layers=8
 
         # back-to-back launches with events only at the ends, as in the headline loop (a batched
         # step is long enough that queued launches hide the binding's host cost)
-        steps = 10 * layers
-        for i in range(layers):
-            hq.decode_attn(*lay[i], 0, o, ws)
+        steps = 200
+        for i in range(40):  # warm-up long enough for the clocks to settle
+            hq.decode_attn(*lay[i % layers], 0, o, ws)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         e0.record()
@@ -324,6 +326,78 @@ def bench_decode_bits(torch, hq, gen, dev, B=16, L=32768, Hq=32, Hkv=8, layers=8
         torch.cuda.empty_cache()
     out["note"] = (f"bs{B} ctx{L} hq{Hq} hkv{Hkv}, {layers} resident layers, hybrid 5% anchors + bf16 window; "
                    f"error over sequences 0..{n_ref - 1} of the first layer")
+    return out
+
+
+def ragged_lengths(n_seq, seed, lo=2048, hi=32768):
+    """The variable-length batch's context lengths: seeded, uniform over [lo, hi]."""
+    import numpy as np
+    return [int(x) for x in np.random.default_rng(seed).integers(lo, hi + 1, size=n_seq)]
+
+
+def bench_decode_ragged(torch, hq, gen, dev, n_seq=16, Hq=32, Hkv=8, layers=4, seed=77):
+    """A variable-length batch: 16 sequences of seeded lengths in [2K, 32K], each its own
+    single-sequence cache (5% anchors), decoded by one hyq_decode_attn_ragged call per step,
+    rotating over ``layers`` resident batches.  Beside it: the same sequences decoded by one
+    hyq_decode_attn call each (device time from a captured graph of the 16 calls, and the
+    host-driven time)."""
+    G = Hq // Hkv
+    lens = ragged_lengths(n_seq, seed)
+    lay = []
+    for _ in range(layers):
+        cs, qs = [], []
+        for L in lens:
+            shape = hq.Shape.for_context(1, Hq, Hkv, L + 64)
+            c, q = make_layer(torch, hq, shape, 1, Hkv, G, L, gen, dev)
+            cs.append(c)
+            qs.append(q)
+        lay.append((cs, torch.cat(qs, dim=0)))
+    torch.cuda.synchronize()
+    nbytes = sum(algorithmic_bytes(c, 1, Hkv, Hq) for c in lay[0][0])
+    ws = torch.empty(hq.decode_ragged_workspace_bytes(lay[0][0][0].shape, n_seq), dtype=torch.uint8, device=dev)
+    o = torch.empty(n_seq, Hq, D, dtype=torch.float32, device=dev)
+    steps = 200
+    for i in range(40):  # warm-up long enough for the clocks to settle
+        hq.decode_attn_ragged(lay[i % layers][0], lay[i % layers][1], 0, o, ws)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        hq.decode_attn_ragged(lay[i % layers][0], lay[i % layers][1], 0, o, ws)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / steps
+    ragged_out = o.clone()  # the last step's output (layer (steps - 1) % layers)
+    # the same sequences one call each
+    wss = [hq.decode_workspace(c.shape, 0, dev) for c in lay[0][0]]
+    os1 = [torch.empty(1, Hq, D, dtype=torch.float32, device=dev) for _ in lens]
+
+    def one_by_one(cs, qq):
+        for j, c in enumerate(cs):
+            hq.decode_attn(c, qq[j:j + 1], 0, os1[j], wss[j])
+        return os1[0]
+    last = lay[(steps - 1) % layers]
+    one_by_one(*last)
+    torch.cuda.synchronize()
+    us_sep_eager, _ = timed(torch, lambda: one_by_one(*last), 20)
+    graph_us = []
+    for cs, qq in lay:
+        u, _ = timed_graph(torch, lambda: one_by_one(cs, qq), 10)
+        graph_us.append(u)
+    us_sep = sum(graph_us) / len(graph_us)
+    one_by_one(*last)
+    torch.cuda.synchronize()
+    # outputs agree up to the split plans (the automatic plans differ between the two forms)
+    diff = max(float((os1[j][0] - ragged_out[j]).abs().max()) for j in range(n_seq))
+    out = {"lengths": lens, "tokens": sum(lens), "us_per_step": round(us, 2),
+           "GB_per_s": round(nbytes / (us * 1e-6) / 1e9, 1),
+           "hbm_frac": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4), "bytes_per_step": nbytes,
+           "separate_calls_us_graph": round(us_sep, 2), "separate_calls_us_eager": round(us_sep_eager, 2),
+           "speedup_vs_separate_graph": round(us_sep / us, 2), "max_abs_diff_vs_separate": diff,
+           "note": f"{n_seq} single-sequence caches, hq{Hq} hkv{Hkv}, {layers} resident batches; ragged call "
+                   "timed back to back (events at the ends), includes its table copy"}
+    del lay, wss
+    torch.cuda.empty_cache()
     return out
 
 
@@ -566,6 +640,11 @@ def main():
         gen.manual_seed(args.seed)
         print(json.dumps({"rows": {"decode_bit_width": bench_decode_bits(torch, hq, gen, dev)}}), flush=True)
         return
+    if args.only_ragged:
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(args.seed)
+        print(json.dumps({"rows": {"decode_ragged": bench_decode_ragged(torch, hq, gen, dev)}}), flush=True)
+        return
     if args.only_prefill:
         gen = torch.Generator(device=dev)
         gen.manual_seed(args.seed)
@@ -693,6 +772,8 @@ def main():
         print(f"[bench] all-bf16 sweep done", file=sys.stderr, flush=True)
         rows["decode_bit_width"] = bench_decode_bits(torch, hq, gen, dev, B=B, L=L, Hq=Hq, Hkv=Hkv)
         print(f"[bench] bit widths: {rows['decode_bit_width']}", file=sys.stderr, flush=True)
+        rows["decode_ragged"] = bench_decode_ragged(torch, hq, gen, dev, Hq=Hq, Hkv=Hkv)
+        print(f"[bench] ragged batch: {rows['decode_ragged']}", file=sys.stderr, flush=True)
         for n in [int(x) for x in args.prefill_lens.split(",") if x]:
             rows[f"prefill_{n}"] = bench_prefill(torch, hq, gen, dev, n)
             print(f"[bench] prefill N={n}: {rows[f'prefill_{n}']['us_per_call']} us", file=sys.stderr, flush=True)

@@ -3,7 +3,9 @@
 #include <atomic>
 #include <hip/hip_runtime.h>
 #include <mutex>
+#include <queue>
 #include <string.h>
+#include <vector>
 
 #include "../../include/hyq.h"
 #include "hyq_launch.h"
@@ -185,8 +187,10 @@ int auto_splits(const hyq_cache_t* c) {
 
 // Split plan.  Each sequence's work is counted in tiles as in auto_splits.  The chip's budget
 // of split columns (two workgroups per CU; one per CU when every wave would get fewer than
-// 16 tiles) is shared in proportion to the work, at least one split per sequence and, on the
-// short-batch budget, at most max(16, tiles / 16) splits.  The total never exceeds
+// 16 tiles) is dealt out one column at a time to the sequence with the most tiles per split
+// (ties to the lower index), starting from one split each: the largest per-split load, which
+// sets the launch's time, is as small as whole columns allow.  On the short-batch budget a
+// sequence takes at most max(16, tiles / 16) splits.  The total never exceeds
 // ragged_split_bound().
 int ragged_columns(int Hkv, int G, bool two_per_cu) {
   const long u1 = (long)Hkv * ((G + 3) / 4);
@@ -200,23 +204,34 @@ long seq_tiles(const hyq_cache_t* c) {
   return (c->n_int4 + 31) / 32 + 3 * ((c->n_anchor + 31) / 32 + (c->n_staged + 31) / 32 + 4);
 }
 void ragged_plan(const hyq_cache_t* const* cs, int n, int Hkv, int G, int n_splits, int* out) {
-  if (n_splits > 0) {
-    for (int i = 0; i < n; ++i) out[i] = n_splits;
-    return;
-  }
+  for (int i = 0; i < n; ++i) out[i] = n_splits > 0 ? n_splits : 1;
+  if (n_splits > 0) return;
   long total = 0;
   for (int i = 0; i < n; ++i) total += seq_tiles(cs[i]);
   long C = ragged_columns(Hkv, G, true);
   const bool low = total < 64 * C;
   if (low) C = ragged_columns(Hkv, G, false);
-  for (int i = 0; i < n; ++i) {
-    const long t = seq_tiles(cs[i]);
-    long s = (long)((double)C * (double)t / (double)total + 0.5);
-    if (low) {
-      const long cap = (t + 15) / 16 > 16 ? (t + 15) / 16 : 16;
-      if (s > cap) s = cap;
+  // max-heap on tiles / splits, compared exactly as t_a * s_b vs t_b * s_a
+  struct Item {
+    long t;
+    int s, i;
+  };
+  auto less = [](const Item& a, const Item& b) {
+    const long l = a.t * b.s, r = b.t * a.s;
+    return l != r ? l < r : a.i > b.i;
+  };
+  std::priority_queue<Item, std::vector<Item>, decltype(less)> heap(less);
+  for (int i = 0; i < n; ++i) heap.push({seq_tiles(cs[i]), 1, i});
+  for (long left = C - n; left > 0 && !heap.empty(); --left) {
+    Item it = heap.top();
+    heap.pop();
+    const long cap = low ? ((it.t + 15) / 16 > 16 ? (it.t + 15) / 16 : 16) : 1L << 30;
+    if (it.s >= cap) {  // this sequence is done; the column goes to the next one
+      ++left;
+      continue;
     }
-    out[i] = (int)(s < 1 ? 1 : s);
+    out[it.i] = ++it.s;
+    heap.push(it);
   }
 }
 
