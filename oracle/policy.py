@@ -97,15 +97,17 @@ class HybridCacheRef:
       STAGED -- left the window since the last refresh, bf16 (staging buffer)
       ANCHOR -- vertical-line positions, bf16
       INT4   -- everything else: per token, per 32-channel group asymmetric INT4 with
-                fp16 scale and minimum (numerics.quant_asym); ``bits`` = 8 stores this bulk
-                with 255 levels instead (the bit width is a parameter of Alg. 3 and Alg. 4)
+                fp16 scale and minimum (numerics.quant_asym); ``bits`` sets B_K and
+                ``bits_v`` B_V (default: B_K), 2^bits - 1 levels each (the bit widths are
+                parameters of Alg. 3 and Alg. 4: 8 gives K8V8, bits=4 with bits_v=2 K4V2)
     The value of a position is its bf16 value, or the dequantized INT4 value.
     """
 
     def __init__(self, D: int = 128, W: int = 128, group: int = 32, g: int = 4,
-                 proxy_cap: int = 64, bits: int = 4):
+                 proxy_cap: int = 64, bits: int = 4, bits_v: int | None = None):
         self.D, self.W, self.group, self.g, self.proxy_cap = D, W, group, g, proxy_cap
         self.bits = bits
+        self.bits_v = bits if bits_v is None else bits_v
         self.L = 0
         self.kind = np.zeros(0, np.int8)
         self.kb = np.zeros((0, D), np.uint16)  # bf16 K (valid for WIN/STAGED/ANCHOR)
@@ -139,7 +141,7 @@ class HybridCacheRef:
             return
         c, s, m = nm.quant_int4_token(nm.bf16_to_f32(self.kb[pos]), self.group, self.bits)
         self.kc[pos], self.ks[pos], self.km[pos] = c, s, m
-        c, s, m = nm.quant_int4_token(nm.bf16_to_f32(self.vb[pos]), self.group, self.bits)
+        c, s, m = nm.quant_int4_token(nm.bf16_to_f32(self.vb[pos]), self.group, self.bits_v)
         self.vc[pos], self.vs[pos], self.vm[pos] = c, s, m
         self.kind[pos] = INT4
 

@@ -231,3 +231,31 @@ def test_int8_bulk_codes_are_nearest_level_by_exhaustive_search():
     # the error of the dequantized value is at most half a step, 17x finer than 15 levels
     xh = nm.dequant_asym(codes, s16[:, 0], m16[:, 0]).astype(np.float64)
     assert np.all(np.abs(xh - x) <= 0.5 * s * (1 + 1e-3) + 1e-12)
+
+
+def test_2bit_codes_are_nearest_level_by_exhaustive_search():
+    """The 2-bit bulk (3 levels, the B = 2 of Alg. 3/4's bit-width parameters): brute force
+    over the 4 levels, ties to the even code; every group uses both end levels (the minimum
+    maps to 0, the maximum to 3, up to the fp16 rounding of s and m)."""
+    x = _bf16_groups(2000, 12, scale=0.8, shift=0.2)
+    codes, s16, m16 = nm.quant_int4_token(x, 32, bits=2)
+    s = s16.astype(np.float64)[:, 0:1]
+    m = m16.astype(np.float64)[:, 0:1]
+    levels = s[..., None] * np.arange(4)[None, None, :] + m[..., None]
+    err = np.abs(x.astype(np.float64)[..., None] - levels)
+    ec = np.take_along_axis(err, codes[..., None].astype(np.int64), -1)[..., 0]
+    emin = err.min(-1)
+    assert np.all(ec <= emin + 1e-15)
+    ties = (np.sort(err, -1)[..., 1] - emin) <= 1e-15
+    assert np.all(codes[ties] % 2 == 0)
+    assert np.array_equal(codes[~ties], err.argmin(-1)[~ties])
+    assert codes.max() == 3 and (codes.min(axis=1) == 0).all() and (codes.max(axis=1) >= 2).all()
+    xh = nm.dequant_asym(codes, s16[:, 0], m16[:, 0]).astype(np.float64)
+    assert np.all(np.abs(xh - x) <= 0.5 * s * (1 + 1e-3) + 1e-12)
+    # a hand case: values on the three steps of [0, 3] and a midpoint between codes 1 and 2
+    y = np.zeros((1, 32), np.float32)
+    y[0, :4] = [0.0, 1.0, 2.0, 3.0]
+    y[0, 4] = 1.5
+    c, s1, m1 = nm.quant_int4_token(y, 32, bits=2)
+    assert float(s1[0, 0]) == 1.0 and float(m1[0, 0]) == 0.0
+    assert list(c[0, :5]) == [0, 1, 2, 3, 2]  # 1.5 is a tie: the even code

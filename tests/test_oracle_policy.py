@@ -305,3 +305,26 @@ def test_cache_8bit_bulk_is_finer_and_keeps_the_rest():
     assert np.array_equal(K8[~q], K[~q]) and np.array_equal(V8[~q], V[~q])
     assert np.abs(K8[q] - K[q]).mean() < np.abs(K4[q] - K[q]).mean() / 8
     assert c8.kc[:700][q].max() > 15
+
+
+@pytest.mark.parametrize("bk,bv", [(4, 2), (2, 2)])
+def test_cache_2bit_bulk_widths_are_per_operand(bk, bv):
+    """bits / bits_v set B_K and B_V separately: K codes follow bits, V codes bits_v; the
+    bf16 segments and the quantized positions do not depend on either, and the V error grows
+    as B_V drops (3 levels against 15)."""
+    s = synth.HeadStream(92, 600, 4)
+    A, _ = pol.select_dense(s.K, s.queries(64))
+    c44 = pol.HybridCacheRef(g=4)
+    cx = pol.HybridCacheRef(g=4, bits=bk, bits_v=bv)
+    for c in (c44, cx):
+        c.freeze(s.K, s.V, A)
+    assert c44.counts() == cx.counts() and np.array_equal(c44.anchors(), cx.anchors())
+    q = c44.kind[:600] == pol.INT4
+    assert cx.kc[:600][q].max() == (1 << bk) - 1 and cx.vc[:600][q].max() == (1 << bv) - 1
+    if bk == 4:
+        assert np.array_equal(cx.kc[:600][q], c44.kc[:600][q])  # K unchanged by bits_v
+    K, V = nm.bf16_to_f32(s.K), nm.bf16_to_f32(s.V)
+    K44, V44 = c44.stored_kv()
+    Kx, Vx = cx.stored_kv()
+    assert np.array_equal(Vx[~q], V[~q]) and np.array_equal(Kx[~q], K[~q])
+    assert np.abs(Vx[q] - V[q]).mean() > 3 * np.abs(V44[q] - V[q]).mean()
