@@ -25,7 +25,7 @@ class HyqShape(C.Structure):
     _fields_ = [("batch", C.c_int32), ("n_q_heads", C.c_int32), ("n_kv_heads", C.c_int32),
                 ("head_dim", C.c_int32), ("group", C.c_int32), ("window", C.c_int32),
                 ("proxy_cap", C.c_int32), ("staging_cap", C.c_int32), ("int4_cap", C.c_int32),
-                ("anchor_cap", C.c_int32), ("bits", C.c_int32)]
+                ("anchor_cap", C.c_int32), ("bits", C.c_int32), ("bits_v", C.c_int32)]
 
 
 class HyqCache(C.Structure):

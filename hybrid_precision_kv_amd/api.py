@@ -60,11 +60,12 @@ class Shape:
     int4_cap: int
     anchor_cap: int
     staging_cap: int = 64
-    bits: int = 4  # codes of the quantized bulk: 4 (INT4) or 8 (INT8)
+    bits: int = 4  # B_K: bits of the quantized bulk's K codes (4, 8 or 2)
+    bits_v: int = 0  # B_V: bits of its V codes (0 = B_K; K4V2 is bits=4, bits_v=2)
 
     def c(self) -> HyqShape:
         return HyqShape(self.batch, self.n_q_heads, self.n_kv_heads, D, 32, WINDOW, PROXY_CAP,
-                        self.staging_cap, self.int4_cap, self.anchor_cap, self.bits)
+                        self.staging_cap, self.int4_cap, self.anchor_cap, self.bits, self.bits_v)
 
     @property
     def g(self) -> int:
@@ -72,11 +73,12 @@ class Shape:
 
     @staticmethod
     def for_context(batch: int, n_q_heads: int, n_kv_heads: int, max_len: int, pct_num: int = 5,
-                    staging_cap: int = 64, bits: int = 4) -> "Shape":
+                    staging_cap: int = 64, bits: int = 4, bits_v: int = 0) -> "Shape":
         """Capacities for contexts up to ``max_len`` with anchors at ``pct_num``%."""
         r32 = lambda x: max(32, -(-x // 32) * 32)
         k = anchor_count(max_len, pct_num)
-        return Shape(batch, n_q_heads, n_kv_heads, r32(max(0, max_len - WINDOW)), r32(k), r32(staging_cap), bits)
+        return Shape(batch, n_q_heads, n_kv_heads, r32(max(0, max_len - WINDOW)), r32(k), r32(staging_cap), bits,
+                     bits_v)
 
 
 def buffer_bytes(shape: Shape) -> dict:

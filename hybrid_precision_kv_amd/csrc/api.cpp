@@ -26,11 +26,15 @@ int check_shape(const hyq_shape_t* s) {
   if (s->staging_cap <= 0 || s->staging_cap % 32 || s->int4_cap < 0 || s->int4_cap % 32 || s->anchor_cap < 0 ||
       s->anchor_cap % 32)
     return HYQ_ERR_INVALID;
-  if (s->bits != 0 && s->bits != 4 && s->bits != 8) return HYQ_ERR_UNSUPPORTED;
+  const int bk = s->bits ? s->bits : 4, bv = s->bits_v ? s->bits_v : bk;
+  if (!((bk == 4 && bv == 4) || (bk == 8 && bv == 8) || (bk == 4 && bv == 2) || (bk == 2 && bv == 2)))
+    return HYQ_ERR_UNSUPPORTED;
   return HYQ_OK;
 }
 
-int qbits(const hyq_shape_t* s) { return s->bits == 8 ? 8 : 4; }
+// B_K and B_V of a (validated) shape
+int qbits(const hyq_shape_t* s) { return s->bits ? s->bits : 4; }
+int qbits_v(const hyq_shape_t* s) { return s->bits_v ? s->bits_v : qbits(s); }
 
 size_t nheads(const hyq_shape_t* s) { return (size_t)s->batch * s->n_kv_heads; }
 
@@ -61,6 +65,7 @@ hyq::CacheView view(const hyq_cache_t* c) {
   v.staging_cap = c->shape.staging_cap;
   v.proxy_cap = c->shape.proxy_cap;
   v.bits = qbits(&c->shape);
+  v.bits_v = qbits_v(&c->shape);
   return v;
 }
 
@@ -286,7 +291,8 @@ int hyq_cache_buffer_bytes(const hyq_shape_t* s, size_t bytes[HYQ_NBUF]) {
   if (st) return st;
   if (!bytes) return HYQ_ERR_INVALID;
   const size_t H = nheads(s);
-  bytes[HYQ_BUF_INT4] = H * s->int4_cap * (qbits(s) == 8 ? 288 : 160);  // 5120 / 9216-byte record per 32-slot tile
+  // per 32-slot tile: 512 (B_K + B_V) code bytes and 1024 bytes of (scale, min)
+  bytes[HYQ_BUF_INT4] = H * s->int4_cap * (size_t)((512 * (qbits(s) + qbits_v(s)) + 1024) / 32);
   bytes[HYQ_BUF_SLOT_POS] = H * s->int4_cap * 4;
   bytes[HYQ_BUF_A_K] = H * s->anchor_cap * D * 2;
   bytes[HYQ_BUF_A_V] = H * s->anchor_cap * D * 2;
@@ -386,6 +392,7 @@ int hyq_decode_attn(const hyq_cache_t* c, const void* q, float* o, int32_t n_spl
   p.G = c->shape.n_q_heads / c->shape.n_kv_heads;
   p.int4_cap = c->shape.int4_cap;
   p.bits = qbits(&c->shape);
+  p.bits_v = qbits_v(&c->shape);
   p.anchor_cap = c->shape.anchor_cap;
   p.staging_cap = c->shape.staging_cap;
   p.n_int4 = c->n_int4;
@@ -415,7 +422,7 @@ int hyq_decode_attn_ragged(const hyq_cache_t* const* caches, int32_t n_seq, cons
     if ((st = check_counters(c))) return st;
     if (c->shape.batch != 1 || c->len <= 0) return HYQ_ERR_INVALID;
     if (c->shape.n_q_heads != caches[0]->shape.n_q_heads || c->shape.n_kv_heads != caches[0]->shape.n_kv_heads ||
-        qbits(&c->shape) != qbits(&caches[0]->shape))
+        qbits(&c->shape) != qbits(&caches[0]->shape) || qbits_v(&c->shape) != qbits_v(&caches[0]->shape))
       return HYQ_ERR_INVALID;
   }
   const hyq_shape_t& s0 = caches[0]->shape;
@@ -488,6 +495,7 @@ int hyq_decode_attn_ragged(const hyq_cache_t* const* caches, int32_t n_seq, cons
   p.G = G;
   p.total_splits = (int)total;
   p.bits = qbits(&s0);
+  p.bits_v = qbits_v(&s0);
   hipError_t e = hyq::launch_decode_ragged(p, stream);
   return e == hipSuccess ? HYQ_OK : HYQ_ERR_HIP;
 }
@@ -531,6 +539,7 @@ int hyq_select_vlines(const hyq_shape_t* shape, hyq_cache_t* cache, const void* 
     p.len = len;
     p.int4_cap = shape->int4_cap;
     p.bits = qbits(shape);
+    p.bits_v = qbits_v(shape);
     p.anchor_cap = shape->anchor_cap;
     p.staging_cap = shape->staging_cap;
     if (dense) {
@@ -577,6 +586,7 @@ int hyq_select_vlines(const hyq_shape_t* shape, hyq_cache_t* cache, const void* 
     r.k = k;
     r.int4_cap = shape->int4_cap;
     r.bits = qbits(shape);
+    r.bits_v = qbits_v(shape);
     r.anchor_cap = shape->anchor_cap;
     r.staging_cap = shape->staging_cap;
     r.n_int4_old = cache->n_int4;

@@ -30,13 +30,14 @@ __device__ inline int slot_to_pos(const int32_t* anc, int n_anchor, int s) {
 __device__ inline int nibble_kslot(int j) { return ((j & 3) << 1) | (j >> 2); }
 
 // ---------------------------------------------------------------- Freeze: quantized slots
-// BITS = 4: the INT4 record; BITS = 8: byte codes, 255 levels (same record structure)
-template <int BITS>
+// BK-bit K codes and BV-bit V codes, 2^B - 1 levels each (4/4: the INT4 record; 8/8, 4/2 and
+// 2/2: the same record structure)
+template <int BK, int BV>
 __global__ __launch_bounds__(256) void freeze_int4_kernel(CacheView c, const uint16_t* __restrict__ k,
                                                           const uint16_t* __restrict__ v, int len,
                                                           const int32_t* __restrict__ anchors, int n_anchor,
                                                           int n_int4) {
-  typedef QL<BITS> L;
+  typedef QL<BK, BV> L;
   __shared__ uint8_t vlds[D][32];
   const int tile = blockIdx.x, b = blockIdx.z, hkv = blockIdx.y;
   const size_t hb = (size_t)b * c.Hkv + hkv;
@@ -63,36 +64,57 @@ __global__ __launch_bounds__(256) void freeze_int4_kernel(CacheView c, const uin
         x[j + 2 * e + 1] = bf16_bits_to_f32((uint16_t)(w[e] >> 16));
       }
     }
-    quant_group32<(1 << BITS) - 1>(x, code, s16, m16);
+    if (kv) quant_group32<(1 << BV) - 1>(x, code, s16, m16);
+    else quant_group32<(1 << BK) - 1>(x, code, s16, m16);
   } else {
 #pragma unroll
     for (int j = 0; j < 32; ++j) code[j] = 0;
   }
   const uint32_t smw = (uint32_t)__half_as_ushort(s16) | ((uint32_t)__half_as_ushort(m16) << 16);
   if (kv == 0) {
-    // the slot's group chunk: channel j at nibble j (INT4) or byte j (INT8)
+    // the slot's group chunk (BK dwords): channel j at bits BK j
+    uint32_t kw[BK];
 #pragma unroll
-    for (int h = 0; h < BITS / 4; ++h) {
-      u32x4 packed;
+    for (int d = 0; d < BK; ++d) {
+      uint32_t w = 0;
 #pragma unroll
-      for (int d4 = 0; d4 < 4; ++d4) {
-        uint32_t w = 0;
-#pragma unroll
-        for (int j = 0; j < 32 / BITS; ++j) w |= (uint32_t)code[16 * h + (32 / BITS) * d4 + j] << (BITS * j);
-        packed[d4] = w;
-      }
-      *(u32x4*)(slab + kcode_chunk_b<BITS>(slot, g) + 16 * h) = packed;
+      for (int j = 0; j < 32 / BK; ++j) w |= (uint32_t)code[(32 / BK) * d + j] << (BK * j);
+      kw[d] = w;
     }
-    *(uint32_t*)(slab + ksm_byte_b<BITS>(slot, g)) = smw;
+    uint8_t* chunk = slab + kcode_chunk_b<BK, BV>(slot, g);
+    if constexpr (BK == 2) {
+      *(uint2*)chunk = make_uint2(kw[0], kw[1]);
+    } else {
+#pragma unroll
+      for (int h = 0; h < BK / 4; ++h)
+        *(u32x4*)(chunk + 16 * h) = (u32x4){kw[4 * h], kw[4 * h + 1], kw[4 * h + 2], kw[4 * h + 3]};
+    }
+    *(uint32_t*)(slab + ksm_byte_b<BK, BV>(slot, g)) = smw;
     if (g == 0) c.slot_pos[hb * (size_t)c.int4_cap + slot] = valid ? pos : -1;
   } else {
-    *(uint32_t*)(slab + vsm_byte_b<BITS>(slot, g)) = smw;
+    *(uint32_t*)(slab + vsm_byte_b<BK, BV>(slot, g)) = smw;
 #pragma unroll
     for (int j = 0; j < 32; ++j) vlds[32 * g + j][sl] = code[j];
   }
   __syncthreads();
   uint32_t* vtile = (uint32_t*)(slab + (size_t)tile * L::TB + L::VC);
-  if (BITS == 4) {
+  if constexpr (BV == 2) {
+    // dword d = (q * 16 + i) * 4 + d4: channel blocks 2 d4 + h at the quad's 8 slots
+    {
+      const int d = t, d4 = d & 3, i = (d >> 2) & 15, q = d >> 6;
+      uint32_t w = 0;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int ch = 16 * (2 * d4 + h) + i;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int p = 4 * q + (e & 3) + 16 * (e >> 2);
+          w |= (uint32_t)vlds[ch][p] << (2 * (e >> 1) + 16 * (e & 1) + 8 * h);
+        }
+      }
+      vtile[d] = w;
+    }
+  } else if constexpr (BV == 4) {
     for (int d = t; d < 512; d += 256) {  // d = vcode_dword_in_tile(p, ch) for the quad's slots
       const int l = (d & 255) >> 2, q = l >> 4, i = l & 15, r = 4 * (d >> 8) + (d & 3);
       const int ch = 16 * r + i;
@@ -244,11 +266,12 @@ hipError_t launch_freeze(const CacheView& c, const uint16_t* k, const uint16_t* 
   const int n_int4 = P - n_anchor;
   if (n_int4 > 0) {
     dim3 grid((n_int4 + 31) / 32, c.Hkv, c.B);
-    if (c.bits == 8)
-      hipLaunchKernelGGL(freeze_int4_kernel<8>, grid, dim3(256), 0, stream, c, k, v, len, anchors, n_anchor, n_int4);
-    else
-      hipLaunchKernelGGL(freeze_int4_kernel<4>, grid, dim3(256), 0, stream, c, k, v, len, anchors, n_anchor, n_int4);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    e = with_widths(c.bits, c.bits_v, [&](auto BK, auto BV) {
+      hipLaunchKernelGGL((freeze_int4_kernel<decltype(BK)::value, decltype(BV)::value>), grid, dim3(256), 0, stream,
+                         c, k, v, len, anchors, n_anchor, n_int4);
+      return hipGetLastError();
+    });
+    if (e != hipSuccess) return e;
   }
   if (n_anchor > 0) {
     dim3 grid((n_anchor + 31) / 32, c.Hkv, c.B);

@@ -67,39 +67,70 @@ __device__ inline f16x8 codes8_to_f16(uint32_t x0, uint32_t x1) {
   return __builtin_bit_cast(f16x8, a);
 }
 
-// one 32-slot tile record of the quantized store for this lane (BITS = 4: the 5 KB INT4
-// record, 16 B of K and of V codes per lane and block; BITS = 8: the 9 KB INT8 record, 32 B)
-template <int BITS>
+// one 32-slot tile record of the quantized store for this lane: BK dwords of K codes per
+// 16-slot block (the lane's slot and channel group), 2 BV dwords of V codes (the lane's channel
+// row at its quad's 8 slots, all 8 channel blocks), and the scale/min quads
+template <int BK, int BV>
 struct QTile {
-  u32x4 kc0[BITS / 4], kc1[BITS / 4], vc0[BITS / 4], vc1[BITS / 4];
+  uint32_t kc0[BK], kc1[BK], vc[2 * BV];
   u32x4 ks0, ks1, vs0, vs1;
 };
-typedef QTile<4> Int4Tile;
+
+// n dwords at p (16-byte aligned for n >= 4, 8-byte aligned for n = 2)
+template <int N>
+__device__ inline void load_dw(uint32_t (&d)[N], const uint8_t* p) {
+  if constexpr (N == 2) {
+    const uint2 v = *(const uint2*)p;
+    d[0] = v.x;
+    d[1] = v.y;
+  } else {
+#pragma unroll
+    for (int h = 0; h < N / 4; ++h) {
+      const u32x4 v = *(const u32x4*)(p + 16 * h);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) d[4 * h + e] = v[e];
+    }
+  }
+}
 
 // all loads of one tile record for this lane; every one is a coalesced read of the record
-template <int BITS>
-__device__ inline void load_int4_tile(QTile<BITS>& x, const uint8_t* slab, int t, uint32_t lane16, uint32_t smoff) {
-  typedef QL<BITS> L;
+template <int BK, int BV>
+__device__ inline void load_int4_tile(QTile<BK, BV>& x, const uint8_t* slab, int t, uint32_t lane, uint32_t smoff) {
+  typedef QL<BK, BV> L;
   const uint8_t* rec = slab + (size_t)t * L::TB;
-  const uint32_t lo = lane16 * (BITS / 4);  // this lane's bytes inside a 16-slot block
-#pragma unroll
-  for (int h = 0; h < BITS / 4; ++h) {
-    x.kc0[h] = *(const u32x4*)(rec + lo + 16 * h);
-    x.kc1[h] = *(const u32x4*)(rec + 64 * L::CB + lo + 16 * h);
-    x.vc0[h] = *(const u32x4*)(rec + L::VC + lo + 16 * h);
-    x.vc1[h] = *(const u32x4*)(rec + L::VC + 64 * L::CB + lo + 16 * h);
+  load_dw<BK>(x.kc0, rec + lane * L::CB);
+  load_dw<BK>(x.kc1, rec + 64 * L::CB + lane * L::CB);
+  if constexpr (BV == 2) {
+    load_dw<4>(*(uint32_t(*)[4])x.vc, rec + L::VC + lane * 16);
+  } else {  // two halves (channel blocks 0-3, 4-7) of 64 x 4 BV bytes
+    load_dw<BV>(*(uint32_t(*)[BV])x.vc, rec + L::VC + lane * 4 * BV);
+    load_dw<BV>(*(uint32_t(*)[BV])(x.vc + BV), rec + L::VC + 256 * BV + lane * 4 * BV);
   }
   x.ks0 = *(const u32x4*)(rec + L::KSM + smoff);
   x.ks1 = *(const u32x4*)(rec + L::KSM + 256 + smoff);
   x.vs0 = *(const u32x4*)(rec + L::VSM + smoff);
   x.vs1 = *(const u32x4*)(rec + L::VSM + 256 + smoff);
 }
-// MFMA operand of 8 codes: K chunk dword tt (INT4) / dwords 2tt, 2tt+1 (INT8) of a block, or
-// V entry r4 of a half
-template <int BITS>
-__device__ inline f16x8 qcodes(const u32x4 (&c)[BITS / 4], int i) {
-  if constexpr (BITS == 4) return codes_to_f16(c[0][i]);
-  else return codes8_to_f16(c[i >> 1][2 * (i & 1)], c[i >> 1][2 * (i & 1) + 1]);
+// MFMA operand of 8 codes: K step tt of a block's chunk (B = BK), or V channel block rr (B = BV)
+template <int B, int N>
+__device__ inline f16x8 qcodes(const uint32_t (&c)[N], int i) {
+  if constexpr (B == 4) return codes_to_f16(c[i]);
+  else if constexpr (B == 8) return codes8_to_f16(c[2 * i], c[2 * i + 1]);
+  else return codes2_to_f16(c[i >> 1], i & 1);
+}
+// factor the other operand carries for element e of a code operand
+template <int B>
+__device__ inline float code_factor(int e) {
+  if constexpr (B == 4) return (e & 2) ? 0.0625f : 1.0f;
+  else if constexpr (B == 8) return 1.0f;
+  else return (e & 6) == 0 ? 1.0f : (e & 6) == 2 ? 0.25f : (e & 6) == 4 ? 0.0625f : 0.015625f;
+}
+// channel (inside the 32-channel group) of element e of K step tt
+template <int B>
+__device__ inline int kstep_channel(int tt, int e) {
+  if constexpr (B == 4) return 8 * tt + kslot_nibble(e);
+  else if constexpr (B == 8) return 8 * tt + kslot_byte(e);
+  else return 16 * (tt >> 1) + code2_of(tt & 1, e);
 }
 
 // online-softmax update for one tile; sc[8] are log2-domain scores (-inf = masked)
@@ -121,14 +152,14 @@ __device__ inline void tile_softmax(WaveState& st, const float (&sc)[8], float (
   st.l += ((pv[0] + pv[1]) + (pv[2] + pv[3])) + ((pv[4] + pv[5]) + (pv[6] + pv[7]));
 }
 
-template <int BITS, bool MASK>
-__device__ inline void int4_tile(WaveState& st, const QTile<BITS>& x, const f16x8 (&bq)[4], float qsum24, float c_int4,
-                                 int base, int n_int4, int q4) {
+template <int BK, int BV, bool MASK>
+__device__ inline void int4_tile(WaveState& st, const QTile<BK, BV>& x, const f16x8 (&bq)[4], float qsum24,
+                                 float c_int4, int base, int n_int4, int q4) {
   f32x4 S0 = {0.f, 0.f, 0.f, 0.f}, S1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int tt = 0; tt < 4; ++tt) {
-    S0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(qcodes<BITS>(x.kc0, tt), bq[tt], S0, 0, 0, 0);
-    S1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(qcodes<BITS>(x.kc1, tt), bq[tt], S1, 0, 0, 0);
+    S0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(qcodes<BK>(x.kc0, tt), bq[tt], S0, 0, 0, 0);
+    S1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(qcodes<BK>(x.kc1, tt), bq[tt], S1, 0, 0, 0);
   }
   float sc[8];
   bool valid[8];
@@ -157,8 +188,8 @@ __device__ inline void int4_tile(WaveState& st, const QTile<BITS>& x, const f16x
   for (int j = 0; j < 8; ++j) {
     const uint32_t smv = j < 4 ? x.vs0[j] : x.vs1[j - 4];
     const float pj = pv[j];
-    // INT4: k-slots 2,3,6,7 meet codes multiplied by 16 (see codes_to_f16)
-    float pp = pj * half_lo(smv) * ((BITS == 4 && (j & 2)) ? PSCALE * 0.0625f : PSCALE);
+    // code operands scaled per k-slot (INT4: x16 on k-slots 2,3,6,7; 2-bit: 4^(j >> 1))
+    float pp = pj * half_lo(smv) * (PSCALE * code_factor<BV>(j));
     float mm = pj * half_hi(smv);
     if (MASK) {  // unused slots may hold any scale/min bits: keep them out entirely
       pp = valid[j] ? pp : 0.f;
@@ -172,7 +203,7 @@ __device__ inline void int4_tile(WaveState& st, const QTile<BITS>& x, const f16x
   st.mt += mt;
   f16x8 a[8];
 #pragma unroll
-  for (int rr = 0; rr < 8; ++rr) a[rr] = rr < 4 ? qcodes<BITS>(x.vc0, rr) : qcodes<BITS>(x.vc1, rr - 4);
+  for (int rr = 0; rr < 8; ++rr) a[rr] = qcodes<BV>(x.vc, rr);
 #pragma unroll
   for (int rr = 0; rr < 8; ++rr) st.acc[rr] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[rr], bhi, st.acc[rr], 0, 0, 0);
 #pragma unroll
@@ -191,12 +222,12 @@ struct HeadWork {
 };
 
 // uniform batch: every sequence has the same counters; grid (split, KV head x head block, b)
-template <int BITS>
+template <int BK, int BV>
 __device__ inline HeadWork head_work(const DecodeParams& p, int hkv) {
   const size_t hb = (size_t)blockIdx.z * p.Hkv + hkv;
   const size_t qh = (size_t)blockIdx.z * p.Hkv * p.G + (size_t)hkv * p.G;
   HeadWork h;
-  h.int4 = p.int4 + hb * (size_t)p.int4_cap * QL<BITS>::SLOT;
+  h.int4 = p.int4 + hb * (size_t)p.int4_cap * QL<BK, BV>::SLOT;
   h.a_k = p.a_k + hb * (size_t)p.anchor_cap * D;
   h.a_v = p.a_v + hb * (size_t)p.anchor_cap * D;
   h.s_k = p.s_k + hb * (size_t)p.staging_cap * D;
@@ -216,13 +247,13 @@ __device__ inline HeadWork head_work(const DecodeParams& p, int hkv) {
 
 // variable-length batch: grid x enumerates the splits of all sequences (split_map), each
 // sequence in its own single-sequence cache
-template <int BITS>
+template <int BK, int BV>
 __device__ inline HeadWork head_work(const RaggedDecodeParams& p, int hkv) {
   const uint32_t m = p.split_map[blockIdx.x];
   const int seq = (int)(m >> 16);
   const RaggedSeq& d = p.seqs[seq];
   HeadWork h;
-  h.int4 = d.int4 + (size_t)hkv * d.int4_cap * QL<BITS>::SLOT;
+  h.int4 = d.int4 + (size_t)hkv * d.int4_cap * QL<BK, BV>::SLOT;
   h.a_k = d.a_k + (size_t)hkv * d.anchor_cap * D;
   h.a_v = d.a_v + (size_t)hkv * d.anchor_cap * D;
   h.s_k = d.s_k + (size_t)hkv * d.staging_cap * D;
@@ -240,7 +271,7 @@ __device__ inline HeadWork head_work(const RaggedDecodeParams& p, int hkv) {
   return h;
 }
 
-template <int BITS, class Params>
+template <int BK, int BV, class Params>
 __global__ __launch_bounds__(256) void decode_split_kernel(Params p) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n = lane & 15, q4 = lane >> 4;
@@ -249,7 +280,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(Params p) {
   const int hkv = blockIdx.y / nsub, sub = blockIdx.y % nsub;
   const int head = sub * 4 + hh;  // Q head inside the KV group
   const bool head_ok = head < p.G;
-  const HeadWork hw = head_work<BITS>(p, hkv);
+  const HeadWork hw = head_work<BK, BV>(p, hkv);
 
   // ---- q of the (up to 4) Q heads of this head block, staged once through LDS
   __shared__ uint32_t q_lds[4][D / 2];
@@ -262,25 +293,29 @@ __global__ __launch_bounds__(256) void decode_split_kernel(Params p) {
   }
   __syncthreads();
   // B operand of the quantized path: q[head] restricted to this lane's column group, channels
-  // in the order the code extraction produces them (INT4: k-slots 2,3,6,7 divided by 16);
-  // zero outside the group
+  // in the order the code extraction produces them, times the inverse of the code operand's
+  // per-element factor (INT4: 1/16 on k-slots 2,3,6,7; 2-bit: 4^-(e >> 1)); zero outside the group
   f16x8 bq4[4];
   float qsum = 0.f;
   const bool use = head_ok && (g == q4);
+  {
+    float f[32];  // channels 32 q4 .. 32 q4 + 31
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    const u32x4 w = *(const u32x4*)&q_lds[hh][16 * q4 + 4 * t];  // channels 32q4+8t .. +7
-    float f[8];
+    for (int t = 0; t < 4; ++t) {
+      const u32x4 w = *(const u32x4*)&q_lds[hh][16 * q4 + 4 * t];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      f[2 * e] = bf16_bits_to_f32((uint16_t)(w[e] & 0xffff));
-      f[2 * e + 1] = bf16_bits_to_f32((uint16_t)(w[e] >> 16));
+      for (int e = 0; e < 4; ++e) {
+        f[8 * t + 2 * e] = bf16_bits_to_f32((uint16_t)(w[e] & 0xffff));
+        f[8 * t + 2 * e + 1] = bf16_bits_to_f32((uint16_t)(w[e] >> 16));
+      }
     }
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float v = BITS == 4 ? f[kslot_nibble(e)] * ((e & 2) ? 0.0625f : 1.0f) : f[kslot_byte(e)];
-      bq4[t][e] = use ? (_Float16)v : (_Float16)0.f;
-    }
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float v = f[kstep_channel<BK>(t, e)] * code_factor<BK>(e);
+        bq4[t][e] = use ? (_Float16)v : (_Float16)0.f;
+      }
   }
   if (head_ok) {
 #pragma unroll
@@ -311,22 +346,21 @@ __global__ __launch_bounds__(256) void decode_split_kernel(Params p) {
   const int TB = TA + TS + TWn;
   const int wr = NW - 1 - w;  // bf16 tiles u with u % NW == wr
   const uint8_t* slab = hw.int4;
-  const uint32_t lane16 = (uint32_t)lane * 16;
   const uint32_t smoff = (uint32_t)(g * 64 + q4 * 16);
   const int full = hw.n_int4 >> 5;  // tiles below this index hold 32 valid slots
   if (w < T4) {
-    QTile<BITS> ta, tb;
+    QTile<BK, BV> ta, tb;
     int t = w;
-    load_int4_tile(ta, slab, t, lane16, smoff);
+    load_int4_tile(ta, slab, t, (uint32_t)lane, smoff);
     for (;;) {
-      load_int4_tile(tb, slab, t + NW < T4 ? t + NW : t, lane16, smoff);
-      if (t < full) int4_tile<BITS, false>(st, ta, bq4, qsum24, c_int4, t * 32, hw.n_int4, q4);
-      else int4_tile<BITS, true>(st, ta, bq4, qsum24, c_int4, t * 32, hw.n_int4, q4);
+      load_int4_tile(tb, slab, t + NW < T4 ? t + NW : t, (uint32_t)lane, smoff);
+      if (t < full) int4_tile<BK, BV, false>(st, ta, bq4, qsum24, c_int4, t * 32, hw.n_int4, q4);
+      else int4_tile<BK, BV, true>(st, ta, bq4, qsum24, c_int4, t * 32, hw.n_int4, q4);
       t += NW;
       if (t >= T4) break;
-      load_int4_tile(ta, slab, t + NW < T4 ? t + NW : t, lane16, smoff);
-      if (t < full) int4_tile<BITS, false>(st, tb, bq4, qsum24, c_int4, t * 32, hw.n_int4, q4);
-      else int4_tile<BITS, true>(st, tb, bq4, qsum24, c_int4, t * 32, hw.n_int4, q4);
+      load_int4_tile(ta, slab, t + NW < T4 ? t + NW : t, (uint32_t)lane, smoff);
+      if (t < full) int4_tile<BK, BV, false>(st, tb, bq4, qsum24, c_int4, t * 32, hw.n_int4, q4);
+      else int4_tile<BK, BV, true>(st, tb, bq4, qsum24, c_int4, t * 32, hw.n_int4, q4);
       t += NW;
       if (t >= T4) break;
     }
@@ -494,9 +528,11 @@ __global__ __launch_bounds__(64) void decode_reduce_kernel(const float* __restri
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
   const int nsub = (p.G + 3) >> 2;
   dim3 grid(p.n_splits, p.Hkv * nsub, p.B);
-  if (p.bits == 8) hipLaunchKernelGGL((decode_split_kernel<8, DecodeParams>), grid, dim3(256), 0, stream, p);
-  else hipLaunchKernelGGL((decode_split_kernel<4, DecodeParams>), grid, dim3(256), 0, stream, p);
-  hipError_t e = hipGetLastError();
+  hipError_t e = with_widths(p.bits, p.bits_v, [&](auto BK, auto BV) {
+    hipLaunchKernelGGL((decode_split_kernel<decltype(BK)::value, decltype(BV)::value, DecodeParams>), grid, dim3(256),
+                       0, stream, p);
+    return hipGetLastError();
+  });
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(decode_reduce_kernel<false>, dim3(p.B * p.Hkv * p.G), dim3(64), 0, stream, p.part, p.o,
                      p.n_splits, (const RaggedSeq*)nullptr, p.Hkv * p.G);
@@ -506,9 +542,11 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
 hipError_t launch_decode_ragged(const RaggedDecodeParams& p, hipStream_t stream) {
   const int nsub = (p.G + 3) >> 2;
   dim3 grid(p.total_splits, p.Hkv * nsub, 1);
-  if (p.bits == 8) hipLaunchKernelGGL((decode_split_kernel<8, RaggedDecodeParams>), grid, dim3(256), 0, stream, p);
-  else hipLaunchKernelGGL((decode_split_kernel<4, RaggedDecodeParams>), grid, dim3(256), 0, stream, p);
-  hipError_t e = hipGetLastError();
+  hipError_t e = with_widths(p.bits, p.bits_v, [&](auto BK, auto BV) {
+    hipLaunchKernelGGL((decode_split_kernel<decltype(BK)::value, decltype(BV)::value, RaggedDecodeParams>), grid,
+                       dim3(256), 0, stream, p);
+    return hipGetLastError();
+  });
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(decode_reduce_kernel<true>, dim3(p.n_seq * p.Hkv * p.G), dim3(64), 0, stream, p.part, p.o, 0,
                      p.seqs, p.Hkv * p.G);

@@ -73,53 +73,76 @@ __device__ __host__ inline size_t vsm_byte(int slot, int g) {
   return (size_t)(slot >> 5) * T4_BYTES + T4_VSM + 4 * (size_t)(((slot >> 4) & 1) * 64 + g * 16 + (slot & 15));
 }
 
-// Quantized store of BITS-bit codes (4: the INT4 record above; 8: the same structure with
-// byte codes).  Per 32-slot tile: K codes, V codes, K (scale, min), V (scale, min).
-template <int BITS>
+// Quantized store with BK-bit K codes and BV-bit V codes (4/4: the INT4 record above; 8/8 and
+// 2-bit widths: the same structure).  Per 32-slot tile: K codes, V codes, K (scale, min),
+// V (scale, min).
+template <int BK, int BV = BK>
 struct QL {
-  static constexpr int CB = 4 * BITS;         // bytes of one (slot, 32-channel group) K chunk
-  static constexpr int CODES = 512 * BITS;    // bytes of the K (and of the V) codes of a tile
-  static constexpr int VC = CODES;            // offset of the V codes
-  static constexpr int KSM = 2 * CODES;       // offset of the K (scale, min)
+  static constexpr int CB = 4 * BK;           // bytes of one (slot, 32-channel group) K chunk
+  static constexpr int VC = 512 * BK;         // offset of the V codes (after the K codes)
+  static constexpr int VCODES = 512 * BV;     // bytes of the V codes of a tile
+  static constexpr int KSM = VC + VCODES;     // offset of the K (scale, min)
   static constexpr int VSM = KSM + 512;       // offset of the V (scale, min)
-  static constexpr int TB = KSM + 1024;       // bytes per tile: 5120 (INT4), 9216 (INT8)
-  static constexpr int SLOT = TB / 32;        // bytes per slot: 160, 288
+  static constexpr int TB = KSM + 1024;       // bytes per tile: 5120 (4/4), 9216 (8/8), 4096 (4/2), 3072 (2/2)
+  static constexpr int SLOT = TB / 32;        // bytes per slot: 160, 288, 128, 96
 };
-// K codes of (slot, group q4): CB bytes, channel 32 q4 + j at nibble j (INT4, 8 per dword) or
-// byte j (INT8); region = [16-slot block][q4][slot in block][CB]
-template <int BITS>
+// K codes of (slot, group q4): CB bytes, channel 32 q4 + j at bits BK j .. of the chunk read as
+// little-endian dwords (INT4: nibble j, 8 per dword; INT8: byte j; 2-bit: 16 per dword);
+// region = [16-slot block][q4][slot in block][CB]
+template <int BK, int BV = BK>
 __device__ __host__ inline size_t kcode_chunk_b(int slot, int q4) {
-  return (size_t)(slot >> 5) * QL<BITS>::TB +
-         (size_t)(((slot >> 4) & 1) * 64 * QL<BITS>::CB + q4 * 16 * QL<BITS>::CB + (slot & 15) * QL<BITS>::CB);
+  typedef QL<BK, BV> L;
+  return (size_t)(slot >> 5) * L::TB + (size_t)(((slot >> 4) & 1) * 64 * L::CB + q4 * 16 * L::CB + (slot & 15) * L::CB);
 }
-template <int BITS>
+template <int BK, int BV = BK>
 __device__ __host__ inline size_t ksm_byte_b(int slot, int g) {
-  return (size_t)(slot >> 5) * QL<BITS>::TB + QL<BITS>::KSM + 4 * (size_t)(((slot >> 4) & 1) * 64 + g * 16 + (slot & 15));
+  return (size_t)(slot >> 5) * QL<BK, BV>::TB + QL<BK, BV>::KSM + 4 * (size_t)(((slot >> 4) & 1) * 64 + g * 16 + (slot & 15));
 }
-template <int BITS>
+template <int BK, int BV = BK>
 __device__ __host__ inline size_t vsm_byte_b(int slot, int g) {
-  return (size_t)(slot >> 5) * QL<BITS>::TB + QL<BITS>::VSM + 4 * (size_t)(((slot >> 4) & 1) * 64 + g * 16 + (slot & 15));
+  return (size_t)(slot >> 5) * QL<BK, BV>::TB + QL<BK, BV>::VSM + 4 * (size_t)(((slot >> 4) & 1) * 64 + g * 16 + (slot & 15));
+}
+// 2-bit codes: a dword holds 16 codes, code j at bits 2j.  With h = 0 or 1 (the dword shifted
+// right by 8 h), the masks 0x00030003, 0x000C000C, 0x00300030, 0x00C000C0 give the f16 operand
+// elements e = 0 .. 7, element e being code code2_of(h, e) multiplied by 4^(e >> 1) (the other
+// operand carries 4^-(e >> 1)).
+__device__ __host__ inline int code2_of(int h, int e) { return 4 * h + (e >> 1) + 8 * (e & 1); }
+__device__ inline f16x8 codes2_to_f16(uint32_t x, int h) {
+  const uint32_t y = h ? x >> 8 : x;
+  u32x4 a;
+  a[0] = y & 0x00030003u;
+  a[1] = y & 0x000C000Cu;
+  a[2] = y & 0x00300030u;
+  a[3] = y & 0x00C000C0u;
+  return __builtin_bit_cast(f16x8, a);
 }
 // INT8 V codes: entry (half, quad, channel & 15, r4) of 8 bytes holds channel 16 (4 half + r4)
 // + i for the 8 slots of the quad; the slot with k-slot e sits in byte kslot_byte(e) (bytes
 // (0,2), (1,3), (4,6), (5,7) are extracted with one mask each and feed k-slots (0,1) .. (6,7))
 __device__ __host__ inline int kslot_byte(int e) { return (e & 4) | ((e & 1) << 1) | ((e >> 1) & 1); }
+// 2-bit V codes: dword (quad, channel & 15, d4) holds channels 16 (2 d4 + h) + (c & 15), h = 0, 1,
+// at the 8 slots of the quad: the slot with k-slot e at bits 2 (e >> 1) + 16 (e & 1) + 8 h, so
+// codes2_to_f16(dword, h) gives channel block 2 d4 + h in k-slot order
 // V code of (slot, channel): byte offset of the dword holding it and the code's bit shift
-template <int BITS>
+template <int BK, int BV = BK>
 __device__ __host__ inline void vcode_loc(int slot, int c, size_t& dword_off, int& shift) {
-  const size_t tile = (size_t)(slot >> 5) * QL<BITS>::TB + QL<BITS>::VC;
+  const size_t tile = (size_t)(slot >> 5) * QL<BK, BV>::TB + QL<BK, BV>::VC;
   const int p = slot & 31;
-  if (BITS == 4) {
+  if (BV == 4) {
     dword_off = tile + 4 * (size_t)vcode_dword_in_tile(p, c);
     shift = 4 * kslot_nibble(tile_kslot(p));
+  } else if (BV == 2) {
+    const int e = tile_kslot(p), rr = c >> 4;
+    dword_off = tile + 4 * (size_t)((tile_quad(p) * 16 + (c & 15)) * 4 + (rr >> 1));
+    shift = 2 * (e >> 1) + 16 * (e & 1) + 8 * (rr & 1);
   } else {
     const int byte = ((((c >> 6) * 4 + tile_quad(p)) * 16 + (c & 15)) * 4 + ((c >> 4) & 3)) * 8 + kslot_byte(tile_kslot(p));
     dword_off = tile + (size_t)(byte & ~3);
     shift = 8 * (byte & 3);
   }
 }
-// bytes per slot of the quantized store for a shape's bit width (0 means 4)
-__device__ __host__ inline int qslot_bytes(int bits) { return bits == 8 ? QL<8>::SLOT : QL<4>::SLOT; }
+// bytes per slot of the quantized store for (B_K, B_V)
+__device__ __host__ inline int qslot_bytes(int bk, int bv) { return (512 * (bk + bv) + 1024) / 32; }
 
 // bf16 K (anchors / staging / window): element index for (pos, channel).  Tile = 4096
 // elements: [16-pos block][8-channel chunk tt][quad q4 = channel / 32][pos in block][8].

@@ -2,8 +2,21 @@
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <type_traits>
 
 namespace hyq {
+
+// Runs f(integral_constant<B_K>, integral_constant<B_V>) for the supported code widths
+// (4/4, 8/8, 4/2, 2/2); any other pair is an invalid value.
+template <class F>
+hipError_t with_widths(int bk, int bv, F&& f) {
+  using std::integral_constant;
+  if (bk == 4 && bv == 4) return f(integral_constant<int, 4>{}, integral_constant<int, 4>{});
+  if (bk == 8 && bv == 8) return f(integral_constant<int, 8>{}, integral_constant<int, 8>{});
+  if (bk == 4 && bv == 2) return f(integral_constant<int, 4>{}, integral_constant<int, 2>{});
+  if (bk == 2 && bv == 2) return f(integral_constant<int, 2>{}, integral_constant<int, 2>{});
+  return hipErrorInvalidValue;
+}
 
 struct DecodeParams {
   const uint8_t* int4;  // [hb][int4_cap/32] 5120-byte tile records
@@ -15,7 +28,7 @@ struct DecodeParams {
   int int4_cap, anchor_cap, staging_cap;
   int n_int4, n_anchor, n_staged, n_win;
   int n_splits;
-  int bits;  // codes of the quantized store: 4 or 8
+  int bits, bits_v;  // B_K and B_V of the quantized store: (4, 4), (8, 8), (4, 2) or (2, 2)
 };
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream);
 
@@ -40,7 +53,7 @@ struct RaggedDecodeParams {
   float* part;                // partial (m, l, acc) records, 130 floats each
   float* o;                   // [n_seq][Hq][128]
   int n_seq, Hkv, G, total_splits;
-  int bits;
+  int bits, bits_v;  // B_K, B_V
 };
 hipError_t launch_decode_ragged(const RaggedDecodeParams& p, hipStream_t stream);
 
@@ -53,7 +66,7 @@ struct CacheView {
   uint16_t* proxy_q;
   int B, Hkv, G;
   int int4_cap, anchor_cap, staging_cap, proxy_cap;
-  int bits;  // codes of the quantized store: 4 or 8
+  int bits, bits_v;  // B_K and B_V of the quantized store: (4, 4), (8, 8), (4, 2) or (2, 2)
 };
 
 struct SelectParams {
@@ -76,7 +89,7 @@ struct SelectParams {
   float* rowstat;  // [H][R][2]
   float* scores;   // [H][len - 128] by position
   int32_t* idx_out;  // [H][k]
-  int bits;          // codes of the quantized store: 4 or 8
+  int bits, bits_v;  // B_K, B_V of the quantized store (the record layout depends on both)
 };
 hipError_t launch_select(SelectParams p, hipStream_t stream);
 int select_task_count(int n_tiles);
@@ -109,7 +122,7 @@ struct RefreshParams {
   size_t ws_per_head;
   int inset_words, del_words, max_moves;
   int* status;  // [H] 0 = counts consistent
-  int bits;     // codes of the quantized store: 4 or 8
+  int bits, bits_v;  // B_K, B_V of the quantized store
 };
 hipError_t launch_refresh(const RefreshParams& p, hipStream_t stream);
 // bytes of per-head refresh scratch

@@ -233,7 +233,7 @@ __global__ __launch_bounds__(PT) void refresh_plan_kernel(RefreshParams p) {
 }
 
 // ------------------------------------------------------------------ gather: one wave per new anchor
-template <int BITS>
+template <int BK, int BV>
 __global__ __launch_bounds__(256) void refresh_gather_kernel(RefreshParams p) {
   const int hb = blockIdx.y, lane = threadIdx.x & 63;
   const int i = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -263,23 +263,18 @@ __global__ __launch_bounds__(256) void refresh_gather_kernel(RefreshParams p) {
   // a quantized position: dequantize its slot
   const int t = s.slot_of[i];
   if (t < 0 || t >= p.int4_cap) return;
-  const uint8_t* slab = p.int4 + hb * (size_t)p.int4_cap * QL<BITS>::SLOT;
-  constexpr uint32_t CM = (1u << BITS) - 1u;
+  const uint8_t* slab = p.int4 + hb * (size_t)p.int4_cap * QL<BK, BV>::SLOT;
   for (int c = lane; c < D; c += 64) {
     const int g = c >> 5;
-    uint32_t kc;
-    if constexpr (BITS == 4) {
-      const uint8_t kb = slab[kcode_chunk_b<4>(t, g) + ((c & 31) >> 1)];
-      kc = (c & 1) ? (kb >> 4) : (kb & 15u);
-    } else {
-      kc = slab[kcode_chunk_b<8>(t, g) + (c & 31)];
-    }
+    // K code: channel c & 31 of the chunk at bits BK (c & 31), read from its byte
+    const int kbit = BK * (c & 31);
+    const uint32_t kc = ((uint32_t)slab[kcode_chunk_b<BK, BV>(t, g) + (kbit >> 3)] >> (kbit & 7)) & ((1u << BK) - 1u);
     size_t voff;
     int vsh;
-    vcode_loc<BITS>(t, c, voff, vsh);
-    const uint32_t vc = (*(const uint32_t*)(slab + voff) >> vsh) & CM;
-    const uint32_t ksm = *(const uint32_t*)(slab + ksm_byte_b<BITS>(t, g));
-    const uint32_t vsm = *(const uint32_t*)(slab + vsm_byte_b<BITS>(t, g));
+    vcode_loc<BK, BV>(t, c, voff, vsh);
+    const uint32_t vc = (*(const uint32_t*)(slab + voff) >> vsh) & ((1u << BV) - 1u);
+    const uint32_t ksm = *(const uint32_t*)(slab + ksm_byte_b<BK, BV>(t, g));
+    const uint32_t vsm = *(const uint32_t*)(slab + vsm_byte_b<BK, BV>(t, g));
     // dequantized value = scale * code + min in fp32 (exact product, one rounding), then bf16
     const float kx = __half2float(__ushort_as_half((unsigned short)(ksm & 0xffff))) * (float)kc +
                      __half2float(__ushort_as_half((unsigned short)(ksm >> 16)));
@@ -303,13 +298,13 @@ __global__ __launch_bounds__(256) void refresh_gather_kernel(RefreshParams p) {
 // this kernel).  The next move's list entry is loaded while the current move runs.
 constexpr int MOVE_BLOCKS = 16;
 
-template <int BITS>
+template <int BK, int BV>
 __device__ inline void put_vcode(uint8_t* slab, int slot, int c, uint32_t code) {
   size_t off;
   int sh;
-  vcode_loc<BITS>(slot, c, off, sh);
+  vcode_loc<BK, BV>(slot, c, off, sh);
   unsigned* dw = (unsigned*)(slab + off);
-  const uint32_t delta = (((*dw >> sh) & ((1u << BITS) - 1u)) ^ code) << sh;
+  const uint32_t delta = (((*dw >> sh) & ((1u << BV) - 1u)) ^ code) << sh;
   if (delta) atomicXor(dw, delta);
 }
 
@@ -324,9 +319,9 @@ __device__ inline float group8_max(float v) {
   return v;
 }
 
-template <int BITS>
+template <int BK, int BV>
 __global__ __launch_bounds__(256) void refresh_move_kernel(RefreshParams p) {
-  typedef QL<BITS> L;
+  typedef QL<BK, BV> L;
   const int hb = blockIdx.y, lane = threadIdx.x & 63;
   const Scratch s = scratch(p, hb);
   const int n = min(s.cnt[0], p.max_moves), waves = gridDim.x * 4;
@@ -363,7 +358,7 @@ __global__ __launch_bounds__(256) void refresh_move_kernel(RefreshParams p) {
       const float mn = group8_min(fminf(fminf(x[0], x[1]), fminf(x[2], x[3])));
       const float mx = group8_max(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
       // the group quantizer's scale, minimum and codes (same operations, same order)
-      constexpr float LEVELS = (float)((1 << BITS) - 1);
+      const float LEVELS = kv ? (float)((1 << BV) - 1) : (float)((1 << BK) - 1);
       const __half s16 = __float2half_rn(__fdiv_rn(__fsub_rn(mx, mn), LEVELS));
       const __half m16 = __float2half_rn(mn);
       const float sf = __half2float(s16), mf = __half2float(m16);
@@ -379,40 +374,46 @@ __global__ __launch_bounds__(256) void refresh_move_kernel(RefreshParams p) {
       }
       const uint32_t smw = (uint32_t)__half_as_ushort(s16) | ((uint32_t)__half_as_ushort(m16) << 16);
       if (kv == 0) {
-        if constexpr (BITS == 4) {
+        if constexpr (BK == 4) {
           // nibbles 4 sub + e of the group's 32; dword sub / 2 holds lanes sub & ~1 (low) and | 1
           const uint32_t half16 = code[0] | (code[1] << 4) | (code[2] << 8) | (code[3] << 12);
           const uint32_t other = (uint32_t)__float_as_int(shfl_xor_f(__int_as_float((int)half16), 1));
-          if ((sub & 1) == 0) *(uint32_t*)(slab + kcode_chunk_b<4>(dst, g) + 4 * (sub >> 1)) = half16 | (other << 16);
-        } else {
+          if ((sub & 1) == 0) *(uint32_t*)(slab + kcode_chunk_b<BK, BV>(dst, g) + 4 * (sub >> 1)) = half16 | (other << 16);
+        } else if constexpr (BK == 8) {
           // bytes 4 sub + e of the group's 32: one dword per lane
-          *(uint32_t*)(slab + kcode_chunk_b<8>(dst, g) + 4 * sub) =
+          *(uint32_t*)(slab + kcode_chunk_b<BK, BV>(dst, g) + 4 * sub) =
               code[0] | (code[1] << 8) | (code[2] << 16) | (code[3] << 24);
+        } else {
+          // 2-bit codes 4 sub + e: byte sub & 3 of dword sub / 4, OR-ed over the dword's 4 lanes
+          uint32_t w = (code[0] | (code[1] << 2) | (code[2] << 4) | (code[3] << 6)) << (8 * (sub & 3));
+          w |= (uint32_t)__float_as_int(shfl_xor_f(__int_as_float((int)w), 1));
+          w |= (uint32_t)__float_as_int(shfl_xor_f(__int_as_float((int)w), 2));
+          if ((sub & 3) == 0) *(uint32_t*)(slab + kcode_chunk_b<BK, BV>(dst, g) + 4 * (sub >> 2)) = w;
         }
-        if (sub == 0) *(uint32_t*)(slab + ksm_byte_b<BITS>(dst, g)) = smw;
+        if (sub == 0) *(uint32_t*)(slab + ksm_byte_b<BK, BV>(dst, g)) = smw;
       } else {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) put_vcode<BITS>(slab, dst, c0 + e, code[e]);
-        if (sub == 0) *(uint32_t*)(slab + vsm_byte_b<BITS>(dst, g)) = smw;
+        for (int e = 0; e < 4; ++e) put_vcode<BK, BV>(slab, dst, c0 + e, code[e]);
+        if (sub == 0) *(uint32_t*)(slab + vsm_byte_b<BK, BV>(dst, g)) = smw;
       }
       if (lane == 0) slot_pos[dst] = kind == 0 ? p.a_pos[hb * (size_t)p.anchor_cap + src] : ps0 + src;
     } else {
       // move a quantized slot: codes, (scale, min), position
-      constexpr int KDW = L::CB / 4;  // dwords per (slot, group) K chunk: 4 or 8
+      constexpr int KDW = L::CB / 4;  // dwords per (slot, group) K chunk: BK
       if (lane < 4 * KDW) {  // K code chunks as dwords
         const int q4 = lane / KDW, d = lane % KDW;
-        *(uint32_t*)(slab + kcode_chunk_b<BITS>(dst, q4) + 4 * d) =
-            *(const uint32_t*)(slab + kcode_chunk_b<BITS>(src, q4) + 4 * d);
+        *(uint32_t*)(slab + kcode_chunk_b<BK, BV>(dst, q4) + 4 * d) =
+            *(const uint32_t*)(slab + kcode_chunk_b<BK, BV>(src, q4) + 4 * d);
       } else if (lane < 4 * KDW + 4) {
         const int q4 = lane - 4 * KDW;
-        *(uint32_t*)(slab + ksm_byte_b<BITS>(dst, q4)) = *(const uint32_t*)(slab + ksm_byte_b<BITS>(src, q4));
-        *(uint32_t*)(slab + vsm_byte_b<BITS>(dst, q4)) = *(const uint32_t*)(slab + vsm_byte_b<BITS>(src, q4));
+        *(uint32_t*)(slab + ksm_byte_b<BK, BV>(dst, q4)) = *(const uint32_t*)(slab + ksm_byte_b<BK, BV>(src, q4));
+        *(uint32_t*)(slab + vsm_byte_b<BK, BV>(dst, q4)) = *(const uint32_t*)(slab + vsm_byte_b<BK, BV>(src, q4));
       }
       for (int c = lane; c < D; c += 64) {
         size_t off;
         int shs;
-        vcode_loc<BITS>(src, c, off, shs);
-        put_vcode<BITS>(slab, dst, c, (*(const uint32_t*)(slab + off) >> shs) & ((1u << BITS) - 1u));
+        vcode_loc<BK, BV>(src, c, off, shs);
+        put_vcode<BK, BV>(slab, dst, c, (*(const uint32_t*)(slab + off) >> shs) & ((1u << BV) - 1u));
       }
       if (lane == 0) slot_pos[dst] = slot_pos[src];
     }
@@ -449,13 +450,14 @@ hipError_t launch_refresh(const RefreshParams& p, hipStream_t stream) {
   const int H = p.B * p.Hkv;
   hipLaunchKernelGGL(refresh_plan_kernel, dim3(H), dim3(PT), 0, stream, p);
   const int ka = min(p.k, p.anchor_cap);
-  if (ka > 0) {
-    if (p.bits == 8) hipLaunchKernelGGL(refresh_gather_kernel<8>, dim3((ka + 3) / 4, H), dim3(256), 0, stream, p);
-    else hipLaunchKernelGGL(refresh_gather_kernel<4>, dim3((ka + 3) / 4, H), dim3(256), 0, stream, p);
-  }
   const dim3 mgrid(std::max(1, std::min((p.max_moves + 3) / 4, MOVE_BLOCKS)), H);
-  if (p.bits == 8) hipLaunchKernelGGL(refresh_move_kernel<8>, mgrid, dim3(256), 0, stream, p);
-  else hipLaunchKernelGGL(refresh_move_kernel<4>, mgrid, dim3(256), 0, stream, p);
+  hipError_t e = with_widths(p.bits, p.bits_v, [&](auto BK, auto BV) {
+    constexpr int K = decltype(BK)::value, V = decltype(BV)::value;
+    if (ka > 0) hipLaunchKernelGGL((refresh_gather_kernel<K, V>), dim3((ka + 3) / 4, H), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((refresh_move_kernel<K, V>), mgrid, dim3(256), 0, stream, p);
+    return hipGetLastError();
+  });
+  if (e != hipSuccess) return e;
   const int a_end = min((p.k + 31) & ~31, p.anchor_cap);
   if (a_end > 0) hipLaunchKernelGGL(refresh_store_kernel, dim3((a_end + 3) / 4, H), dim3(256), 0, stream, p);
   return hipGetLastError();

@@ -98,16 +98,38 @@ __global__ __launch_bounds__(256) void select_prep_kernel(SelectParams p) {
     const int r = 16 * rb + n;
     u32x4 w = {0u, 0u, 0u, 0u};
     if (r < R) w = *(const u32x4*)(proxy_row(p, b, hkv, r) + 32 * g + 8 * q4);
-    float f[8];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      f[2 * e] = bf16_bits_to_f32((uint16_t)(w[e] & 0xffff));
-      f[2 * e + 1] = bf16_bits_to_f32((uint16_t)(w[e] >> 16));
-    }
     f16x8 h;
+    if (p.bits == 2) {
+      // 2-bit keys: lane quad q4 takes the group's channels 16 (q4 >> 1) + code2_of(q4 & 1, e),
+      // times 4^-(e >> 1)
+      u32x4 w2[2] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};
+      if (r < R) {
+        w2[0] = *(const u32x4*)(proxy_row(p, b, hkv, r) + 32 * g + 16 * (q4 >> 1));
+        w2[1] = *(const u32x4*)(proxy_row(p, b, hkv, r) + 32 * g + 16 * (q4 >> 1) + 8);
+      }
+      float f[16];
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
-      h[e] = p.bits == 8 ? (_Float16)f[kslot_byte(e)] : (_Float16)(f[kslot_nibble(e)] * ((e & 2) ? 0.0625f : 1.0f));
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t x = w2[e >> 2][e & 3];
+        f[2 * e] = bf16_bits_to_f32((uint16_t)(x & 0xffff));
+        f[2 * e + 1] = bf16_bits_to_f32((uint16_t)(x >> 16));
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float fac = (e & 6) == 0 ? 1.0f : (e & 6) == 2 ? 0.25f : (e & 6) == 4 ? 0.0625f : 0.015625f;
+        h[e] = (_Float16)(f[code2_of(q4 & 1, e)] * fac);
+      }
+    } else {
+      float f[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        f[2 * e] = bf16_bits_to_f32((uint16_t)(w[e] & 0xffff));
+        f[2 * e + 1] = bf16_bits_to_f32((uint16_t)(w[e] >> 16));
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        h[e] = p.bits == 8 ? (_Float16)f[kslot_byte(e)] : (_Float16)(f[kslot_nibble(e)] * ((e & 2) ? 0.0625f : 1.0f));
+    }
     pq16[t] = h;
     pqbf[t] = __builtin_bit_cast(bf16x8, w);
   }
@@ -133,19 +155,21 @@ struct KeyOpsB {
   bf16x8 a[2][4];    // [block][8-channel chunk]
 };
 
-template <int BITS>
+template <int BK, int BV>
 __device__ inline void load_keys4(const SelectParams& p, const KeySrc& ks, size_t hb, int lane, KeyOps4& o) {
-  typedef QL<BITS> L;
+  typedef QL<BK, BV> L;
   const int n = lane & 15, q4 = lane >> 4;
   const uint8_t* rec = p.int4 + hb * (size_t)p.int4_cap * L::SLOT + (size_t)ks.tile * L::TB;
 #pragma unroll
   for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      // channels 32 g + 8 q4 .. + 7 of key n: a dword of nibbles (INT4) or two of bytes (INT8)
-      const uint8_t* c = rec + blk * 64 * L::CB + g * 16 * L::CB + n * L::CB + q4 * BITS;
-      if constexpr (BITS == 4) o.a[blk][g] = codes_to_f16(*(const uint32_t*)c);
-      else o.a[blk][g] = codes8_to_f16(((const uint32_t*)c)[0], ((const uint32_t*)c)[1]);
+      // key n, group g: channels 8 q4 .. + 7 (a dword of nibbles, INT4; two of bytes, INT8), or
+      // the 2-bit channel set of step q4 (half q4 & 1 of dword q4 >> 1)
+      const uint8_t* ch = rec + blk * 64 * L::CB + g * 16 * L::CB + n * L::CB;
+      if constexpr (BK == 4) o.a[blk][g] = codes_to_f16(*(const uint32_t*)(ch + 4 * q4));
+      else if constexpr (BK == 8) o.a[blk][g] = codes8_to_f16(((const uint32_t*)(ch + 8 * q4))[0], ((const uint32_t*)(ch + 8 * q4))[1]);
+      else o.a[blk][g] = codes2_to_f16(*(const uint32_t*)(ch + 4 * (q4 >> 1)), q4 & 1);
     }
 #pragma unroll
   for (int blk = 0; blk < 2; ++blk) {
@@ -259,7 +283,7 @@ __device__ inline void load_rows(const SelectParams& p, size_t hb, int R, int rb
 // writes the wave's per-row (max, sum exp2) partial to red[wave][r]; PASS 2 accumulates the
 // column sums of the lane's 8 keys into colsum.
 // FULL: all 32 keys of the tile are valid (every tile but a segment's last)
-template <int PASS, int KIND, bool FULL, int BITS>
+template <int PASS, int KIND, bool FULL, int BK, int BV>
 __device__ inline void sweep(const SelectParams& p, const KeySrc& ks, size_t hb, int lane, int wave,
                              const bool (&valid)[8], float* red, float (&colsum)[8]) {
   const int n = lane & 15, q4 = lane >> 4;
@@ -268,7 +292,7 @@ __device__ inline void sweep(const SelectParams& p, const KeySrc& ks, size_t hb,
   const float c = KIND == 0 ? SCALE4 : SCALEB;
   KeyOps4 k4;
   KeyOpsB kb;
-  if (KIND == 0) load_keys4<BITS>(p, ks, hb, lane, k4);
+  if (KIND == 0) load_keys4<BK, BV>(p, ks, hb, lane, k4);
   else load_keysB(p, ks, hb, lane, kb);
   auto ok = [&](int j) { return FULL || valid[j]; };
   auto block = [&](const RowBlock<PASS, KIND>& x, int rb) {
@@ -315,7 +339,7 @@ __device__ inline void sweep(const SelectParams& p, const KeySrc& ks, size_t hb,
 // blocks, reading the prepared B operands straight from L2 (no LDS staging, no barrier inside
 // the sweep).  PASS 1: per-row (max, sum exp2) over the workgroup's keys -- each wave keeps its
 // partial of every row in LDS, merged once at the end; PASS 2: column sums by position.
-template <int PASS, int BITS>
+template <int PASS, int BK, int BV>
 __global__ __launch_bounds__(SW * 64) __attribute__((amdgpu_waves_per_eu(3))) void select_pass_kernel(SelectParams p) {
   extern __shared__ float red[];  // PASS 1: [SW][R][2]
   const int task = blockIdx.x, hb = blockIdx.y;
@@ -337,11 +361,11 @@ __global__ __launch_bounds__(SW * 64) __attribute__((amdgpu_waves_per_eu(3))) vo
   if (has) {
     const bool full = (ks.tile + 1) * 32 <= ks.count;
     if (ks.kind == 0) {
-      if (full) sweep<PASS, 0, true, BITS>(p, ks, hb, lane, wave, valid, red, colsum);
-      else sweep<PASS, 0, false, BITS>(p, ks, hb, lane, wave, valid, red, colsum);
+      if (full) sweep<PASS, 0, true, BK, BV>(p, ks, hb, lane, wave, valid, red, colsum);
+      else sweep<PASS, 0, false, BK, BV>(p, ks, hb, lane, wave, valid, red, colsum);
     } else {
-      if (full) sweep<PASS, 1, true, BITS>(p, ks, hb, lane, wave, valid, red, colsum);
-      else sweep<PASS, 1, false, BITS>(p, ks, hb, lane, wave, valid, red, colsum);
+      if (full) sweep<PASS, 1, true, BK, BV>(p, ks, hb, lane, wave, valid, red, colsum);
+      else sweep<PASS, 1, false, BK, BV>(p, ks, hb, lane, wave, valid, red, colsum);
     }
   } else if (PASS == 1 && q4 == 0) {
     for (int r = n; r < R; r += 16) {  // no keys: empty partials
@@ -675,16 +699,20 @@ hipError_t launch_select(SelectParams p, hipStream_t stream) {
   hipLaunchKernelGGL(select_prep_kernel, dim3((RB * 256 + 255) / 256, H), dim3(256), 0, stream, p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   dim3 grid(p.n_tasks, H);
-  if (p.bits == 8)
-    hipLaunchKernelGGL((select_pass_kernel<1, 8>), grid, dim3(SW * 64), (size_t)SW * R * 2 * sizeof(float), stream, p);
-  else
-    hipLaunchKernelGGL((select_pass_kernel<1, 4>), grid, dim3(SW * 64), (size_t)SW * R * 2 * sizeof(float), stream, p);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  e = with_widths(p.bits, p.bits_v, [&](auto BK, auto BV) {
+    hipLaunchKernelGGL((select_pass_kernel<1, decltype(BK)::value, decltype(BV)::value>), grid, dim3(SW * 64),
+                       (size_t)SW * R * 2 * sizeof(float), stream, p);
+    return hipGetLastError();
+  });
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(select_rowmerge_kernel, dim3((R + 3) / 4, H), dim3(256), 0, stream, p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  if (p.bits == 8) hipLaunchKernelGGL((select_pass_kernel<2, 8>), grid, dim3(SW * 64), 0, stream, p);
-  else hipLaunchKernelGGL((select_pass_kernel<2, 4>), grid, dim3(SW * 64), 0, stream, p);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  e = with_widths(p.bits, p.bits_v, [&](auto BK, auto BV) {
+    hipLaunchKernelGGL((select_pass_kernel<2, decltype(BK)::value, decltype(BV)::value>), grid, dim3(SW * 64), 0,
+                       stream, p);
+    return hipGetLastError();
+  });
+  if (e != hipSuccess) return e;
   if (p.k > 0) return launch_topk_keys((const uint32_t*)p.scores, p.len - WIN, p.k, H, p.idx_out, stream);
   return hipSuccess;
 }

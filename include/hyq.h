@@ -45,6 +45,13 @@
  *     [4096, 8192) V codes  [half][q][i][r4][8 B]: channel 16*(4*half + r4) + i of the 8
  *                  slots of quad q, k-slot e in byte HYQ_V_BYTE[e];
  *     [8192, 8704) K (scale, min), [8704, 9216) V (scale, min), as above.
+ *  In general a tile record holds, in this order, 512*B_K bytes of K codes, 512*B_V bytes of
+ *  V codes and the two 512-byte (scale, min) regions: 5120 (4/4), 9216 (8/8), 4096 (4/2) or
+ *  3072 (2/2) bytes.  2-bit codes (3 levels):
+ *     K codes  [16-slot block][q4][slot in block][8 B]: channel 32*q4 + j at bits 2*(j & 15)
+ *              of little-endian dword j >> 4;
+ *     V codes  u32 [q][i][d4]: channels 16*(2*d4 + h) + i (h = 0, 1) of the 8 slots of
+ *              quad q, k-slot e at bits 2*(e >> 1) + 16*(e & 1) + 8*h.
  *  slot_pos i32 [hb][int4_cap]          position held by each INT4 slot (-1 for unused).
  *  a_k, s_k, w_k  bf16 [hb][cap/32][4096]  anchor / staging / window K, per tile
  *                  [16-position block][tt][q4][position in block][8]: channels
@@ -103,8 +110,11 @@ typedef struct {
   int32_t staging_cap;  /* staging capacity per head, multiple of 32, >= the refresh interval */
   int32_t int4_cap;     /* INT4 slots per head, multiple of 32 */
   int32_t anchor_cap;   /* anchor slots per head, multiple of 32 */
-  int32_t bits;         /* codes of the quantized bulk (B_K = B_V of the HyQuant paper's Alg. 3
-                           and Alg. 4): 0 or 4 = INT4 (the paper's K4V4), 8 = INT8 */
+  int32_t bits;         /* B_K, bits of the quantized bulk's K codes (the HyQuant paper's Alg. 3
+                           and Alg. 4 take B_K and B_V as parameters): 0 or 4 = INT4, 8, or 2 */
+  int32_t bits_v;       /* B_V, bits of its V codes: 0 = same as B_K, else 2, 4 or 8.  Supported
+                           (B_K, B_V): (4, 4) the paper's K4V4, (8, 8), (4, 2), (2, 2); any other
+                           pair is UNSUPPORTED */
 } hyq_shape_t;
 
 typedef struct {

@@ -21,29 +21,33 @@ def _tile_pos(p):
 
 def read_cache(cache) -> list:
     """Per (b, h_kv): dict with int4 {pos: (kcodes[128], ksm[4,2], vcodes[128], vsm[4,2])} (the
-    quantized store, INT4 or INT8 by the shape's bits),
+    quantized store, codes of the shape's B_K / B_V bits),
     anchors {pos: (k bf16[128], v bf16[128])}, staged, window (same), in numpy."""
     s = cache.shape
     H = s.batch * s.n_kv_heads
     ctr = cache.counters()
     host = {n: t.cpu().numpy() for n, t in cache.buffers.items()}
     nt = s.int4_cap // 32
-    bits = 8 if getattr(s, "bits", 4) == 8 else 4
-    CB = 4 * bits                 # bytes of one (slot, group) K chunk
-    CODES = 512 * bits            # bytes of the K (and of the V) codes of a tile
-    TB = 2 * CODES + 1024
+    bk = getattr(s, "bits", 4) or 4
+    bv = getattr(s, "bits_v", 0) or bk
+    CB = 4 * bk                   # bytes of one (slot, group) K chunk
+    VC = 512 * bk                 # offset of the V codes in a tile record
+    KSM = VC + 512 * bv           # offset of the K (scale, min)
+    TB = KSM + 1024
     rec = host["int4"][: H * nt * TB].reshape(H, nt, TB)
     # K codes: [16-slot block][q4][slot in block][CB bytes]
-    kc = rec[:, :, :CODES].reshape(H, nt, 2, 4, 16, CB)
-    kc = kc.transpose(0, 1, 2, 4, 3, 5).reshape(H, s.int4_cap, 4 * CB)  # -> [slot][4 CB bytes]
-    # V codes: [half][quad][channel & 15][r4][4 / 8 bytes], channel = 16*(4*half + r4) + i
-    if bits == 4:
-        vc = np.ascontiguousarray(rec[:, :, CODES:2 * CODES]).view(np.uint32).reshape(H, nt, 2, 4, 16, 4)
-    else:
-        vc = np.ascontiguousarray(rec[:, :, CODES:2 * CODES]).reshape(H, nt, 2, 4, 16, 4, 8)
+    kc = rec[:, :, :VC].reshape(H, nt, 2, 4, 16, CB)
+    kc = kc.transpose(0, 1, 2, 4, 3, 5).reshape(H, s.int4_cap, 4, CB)  # -> [slot][group][CB bytes]
+    vraw = np.ascontiguousarray(rec[:, :, VC:KSM])
+    if bv == 4:    # u32 [half][quad][channel & 15][r4], channel = 16*(4*half + r4) + i
+        vc = vraw.view(np.uint32).reshape(H, nt, 2, 4, 16, 4)
+    elif bv == 8:  # [half][quad][i][r4][8 bytes]
+        vc = vraw.reshape(H, nt, 2, 4, 16, 4, 8)
+    else:          # u32 [quad][i][d4]: channels 16*(2*d4 + h) + i
+        vc = vraw.view(np.uint32).reshape(H, nt, 4, 16, 4)
     # (scale, min): [16-slot block][g][slot in block][2]
-    ksm = np.ascontiguousarray(rec[:, :, 2 * CODES:2 * CODES + 512]).view(np.float16).reshape(H, nt * 2, 4, 16, 2)
-    vsm = np.ascontiguousarray(rec[:, :, 2 * CODES + 512:TB]).view(np.float16).reshape(H, nt * 2, 4, 16, 2)
+    ksm = np.ascontiguousarray(rec[:, :, KSM:KSM + 512]).view(np.float16).reshape(H, nt * 2, 4, 16, 2)
+    vsm = np.ascontiguousarray(rec[:, :, KSM + 512:TB]).view(np.float16).reshape(H, nt * 2, 4, 16, 2)
     slot_pos = host["slot_pos"][: H * s.int4_cap * 4].view(np.int32).reshape(H, s.int4_cap)
 
     p32 = np.arange(32)
@@ -72,20 +76,25 @@ def read_cache(cache) -> list:
     q, e = _tile_pos(sl & 31)
     vcodes = np.empty((H, nsl, D), np.uint8)
     kcodes = np.empty((H, nsl, D), np.uint8)
-    if bits == 4:
+    if bv == 4:
         shift = 4 * KSLOT_NIBBLE[e]
         for c in range(D):
             i, r = c & 15, c >> 4
             words = vc[:, sl >> 5, r >> 2, q, i, r & 3]
             vcodes[:, :, c] = (words >> shift) & 0xF
-        kcodes[:, :, 0::2] = kc & 0xF
-        kcodes[:, :, 1::2] = kc >> 4
-    else:
+    elif bv == 8:
         byte = KSLOT_BYTE[e]
         for c in range(D):
             i, r = c & 15, c >> 4
             vcodes[:, :, c] = vc[:, sl >> 5, r >> 2, q, i, r & 3, byte]
-        kcodes[:] = kc
+    else:
+        for c in range(D):
+            i, r = c & 15, c >> 4
+            words = vc[:, sl >> 5, q, i, r >> 1]
+            vcodes[:, :, c] = (words >> (2 * (e >> 1) + 16 * (e & 1) + 8 * (r & 1))) & 0x3
+    # K: channel 32 g + j at bits bk * j of the group's chunk (little-endian)
+    kbits = np.unpackbits(kc, axis=-1, bitorder="little").reshape(H, s.int4_cap, 4, 32, bk)
+    kcodes[:] = (kbits.astype(np.uint32) << np.arange(bk, dtype=np.uint32)).sum(-1).reshape(H, s.int4_cap, D)
     ksm_s = ksm.transpose(0, 1, 3, 2, 4)[:, sl >> 4, sl & 15]  # [H][slot][g][2]
     vsm_s = vsm.transpose(0, 1, 3, 2, 4)[:, sl >> 4, sl & 15]
 

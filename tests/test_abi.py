@@ -170,8 +170,12 @@ def test_bit_width_field(lib):
     b4, b8 = dict(zip(_lib.BUFFERS, list(out4))), dict(zip(_lib.BUFFERS, list(out8)))
     assert b8["int4"] == 4 * 1024 * 288  # 9216-byte record per 32-slot tile
     assert {k: v for k, v in b8.items() if k != "int4"} == {k: v for k, v in b4.items() if k != "int4"}
-    for bad in (2, 3, 16, -4):
-        assert lib.hyq_cache_buffer_bytes(C.byref(_shape(bits=bad)), C.byref(out8)) == 2
+    # B_K / B_V pairs: record of 512 (B_K + B_V) + 1024 bytes per 32-slot tile
+    for bk, bv, rec in ((4, 2, 4096), (2, 2, 3072), (2, 0, 3072), (8, 0, 9216), (4, 4, 5120), (0, 2, 4096)):
+        assert lib.hyq_cache_buffer_bytes(C.byref(_shape(bits=bk, bits_v=bv)), C.byref(out8)) == 0
+        assert dict(zip(_lib.BUFFERS, list(out8)))["int4"] == 2 * 2 * 1024 * rec // 32
+    for bk, bv in ((3, 0), (16, 0), (-4, 0), (2, 4), (8, 4), (4, 8), (8, 2), (2, 8), (4, 3), (4, -2)):
+        assert lib.hyq_cache_buffer_bytes(C.byref(_shape(bits=bk, bits_v=bv)), C.byref(out8)) == 2
 
 
 def test_ragged_decode_host_checks(lib):

@@ -25,9 +25,10 @@ def dev(a: np.ndarray) -> torch.Tensor:
 class Pair:
     """The same seeded workload on the GPU cache and in per-head oracle caches."""
 
-    def __init__(self, seed, B, Hkv, G, L, n_steps=0, pct=5, staging_cap=64, max_len=None, bits=4):
+    def __init__(self, seed, B, Hkv, G, L, n_steps=0, pct=5, staging_cap=64, max_len=None, bits=4, bits_v=None):
         self.B, self.Hkv, self.G, self.L = B, Hkv, G, L
-        print(f"[case] seed={seed} B={B} Hkv={Hkv} G={G} L={L} steps={n_steps} bits={bits}", flush=True)
+        bv = bits if bits_v is None else bits_v
+        print(f"[case] seed={seed} B={B} Hkv={Hkv} G={G} L={L} steps={n_steps} bits={bits}/{bv}", flush=True)
         self.d = synth.gen_batch(seed, B, Hkv, G, L, n_proxy=64, n_steps=n_steps)
         k = pol.k_rule(L, pct_num=pct)
         self.refs = []
@@ -37,10 +38,10 @@ class Pair:
                 prox = self.d["proxy"][b, h * G:(h + 1) * G]
                 A, _ = pol.select_dense(self.d["K"][b, h], prox, pct_num=pct)
                 anchors[b, h, :k] = A
-                r = pol.HybridCacheRef(g=G, bits=bits)
+                r = pol.HybridCacheRef(g=G, bits=bits, bits_v=bv)
                 r.freeze(self.d["K"][b, h], self.d["V"][b, h], A, prox)
                 self.refs.append(r)
-        shape = hq.Shape.for_context(B, Hkv * G, Hkv, max_len or (L + n_steps), pct, staging_cap, bits)
+        shape = hq.Shape.for_context(B, Hkv * G, Hkv, max_len or (L + n_steps), pct, staging_cap, bits, bv)
         self.cache = hq.HybridKVCache(shape)
         hq.quantize_kv(self.cache, dev(self.d["K"]), dev(self.d["V"]),
                        torch.from_numpy(anchors[..., :k].copy()).cuda() if k else None, dev(self.d["proxy"]))
