@@ -144,7 +144,8 @@ def torch_select(torch, K, proxy, G, k, chunk=16):
 def algorithmic_bytes(cache, B, Hkv, Hq):
     c = cache.counters()
     n_win = min(c["len"], W)
-    slot = 288 if cache.shape.bits == 8 else 160  # K and V codes + fp16 scale/min per token
+    sh = cache.shape
+    slot = (512 * ((sh.bits or 4) + (sh.bits_v or sh.bits or 4)) + 1024) // 32  # codes + fp16 scale/min per token
     per_head = slot * c["n_int4"] + 512 * (c["n_anchor"] + c["n_staged"] + n_win)
     return B * Hkv * per_head + B * Hq * D * (2 + 4)
 
@@ -278,15 +279,15 @@ def bench_decode_bs1(torch, hq, gen, dev, ctxs=(1024, 4096, 16384, 32768), Hq=32
 
 
 def bench_decode_bits(torch, hq, gen, dev, B=16, L=32768, Hq=32, Hkv=8, layers=8, n_ref=2):
-    """Bit width of the quantized bulk (B_K = B_V of the HyQuant paper's Alg. 3/4): the batched
-    workload's decode with a K4V4 and a K8V8 bulk, both with the 5% bf16 anchors and the bf16
-    window.  Per width: time per step (launches rotating over ``layers`` caches), the
-    algorithmic bytes (160 or 288 B per quantized token) and the output's relative L2 error
-    against fp32 attention over the unquantized bf16 K/V of the first ``n_ref`` sequences."""
+    """Bit widths of the quantized bulk (B_K, B_V of the HyQuant paper's Alg. 3/4): the batched
+    workload's decode with K4V4, K8V8, K4V2 and K2V2 bulks, all with the 5% bf16 anchors and the
+    bf16 window.  Per width: time per step (launches rotating over ``layers`` caches), the
+    algorithmic bytes (160, 288, 128 or 96 B per quantized token) and the output's relative L2
+    error against fp32 attention over the unquantized bf16 K/V of the first ``n_ref`` sequences."""
     G = Hq // Hkv
     out = {}
-    for bits in (4, 8):
-        shape = hq.Shape.for_context(B, Hq, Hkv, L + 64, bits=bits)
+    for bits, bits_v in ((4, 4), (8, 8), (4, 2), (2, 2)):
+        shape = hq.Shape.for_context(B, Hq, Hkv, L + 64, bits=bits, bits_v=bits_v)
         lay = []
         for i in range(layers):
             lay.append(make_layer(torch, hq, shape, B, Hkv, G, L, gen, dev, keep=(i == 0)))
@@ -319,7 +320,7 @@ def bench_decode_bits(torch, hq, gen, dev, B=16, L=32768, Hq=32, Hkv=8, layers=8
         e1.record()
         torch.cuda.synchronize()
         us = e0.elapsed_time(e1) * 1e3 / steps
-        out[f"k{bits}v{bits}"] = {"us_per_step": round(us, 2), "GB_per_s": round(nbytes / (us * 1e-6) / 1e9, 1),
+        out[f"k{bits}v{bits_v}"] = {"us_per_step": round(us, 2), "GB_per_s": round(nbytes / (us * 1e-6) / 1e9, 1),
                                   "hbm_frac": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
                                   "bytes_per_step": nbytes, "rel_l2_vs_fp32_unquantized": round(max(err), 6)}
         del lay, ws
