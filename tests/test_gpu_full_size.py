@@ -1,0 +1,67 @@
+"""Decode parity at the batched workload's full size and launch configuration: batch 16 x
+32768-token contexts, 32 Q / 8 KV heads, 5% anchors, automatic splits (the configuration the
+benchmark times), for every built bulk width (K4V4, K8V8, K4V2, K2V2), against the oracle on
+sampled (sequence, KV head) pairs.
+
+The whole batch is drawn from the shared seeded generator.  Sampled heads take the oracle's
+anchor sets (so both sides freeze the same positions); the other heads take the GPU dense
+selector's, which only serve as inputs.  After Freeze and one appended token, each sampled
+head's output must meet the decode bar (2e-3 max-abs, 1e-3 relative L2 against the oracle's
+fp64 decode over the head's stored cache)."""
+import numpy as np
+import pytest
+import torch
+
+from hybrid_precision_kv_amd import api as hq
+from hybrid_precision_kv_amd import synth
+from oracle import attention as att
+from oracle import numerics as nm
+from oracle import policy as pol
+from tests.test_gpu_decode import MAX_ABS, REL_L2, dev
+
+pytestmark = pytest.mark.gpu
+
+B, HKV, G, L = 16, 8, 4, 32768
+SAMPLE = [(0, 0), (7, 3), (15, 7)]
+
+
+@pytest.fixture(scope="module")
+def batch():
+    print(f"[case] full size: generating B={B} Hkv={HKV} G={G} L={L}", flush=True)
+    d = synth.gen_batch(12000, B, HKV, G, L, n_proxy=64, n_steps=1)
+    print("[case] full size: generated", flush=True)
+    k = pol.k_rule(L)
+    shape = hq.Shape.for_context(B, HKV * G, HKV, L + 1)
+    Kd, Pd = dev(d["K"]), dev(d["proxy"])
+    anchors = hq.select_vlines(shape, k, dense_k=Kd, proxy=Pd).cpu().numpy()
+    for b, h in SAMPLE:
+        A, _ = pol.select_dense(d["K"][b, h], d["proxy"][b, h * G:(h + 1) * G])
+        anchors[b, h] = A
+    d["anchors"] = anchors
+    d["Kd"], d["Vd"], d["Pd"] = Kd, dev(d["V"]), Pd
+    return d
+
+
+@pytest.mark.parametrize("bk,bv", [(4, 4), (8, 8), (4, 2), (2, 2)])
+def test_full_size_decode_sampled(batch, bk, bv):
+    d = batch
+    print(f"[case] full size K{bk}V{bv}", flush=True)
+    shape = hq.Shape.for_context(B, HKV * G, HKV, L + 1, bits=bk, bits_v=bv)
+    cache = hq.HybridKVCache(shape)
+    hq.quantize_kv(cache, d["Kd"], d["Vd"], torch.from_numpy(d["anchors"]).cuda(), d["Pd"])
+    hq.append_token(cache, dev(d["new_k"][:, :, 0]), dev(d["new_v"][:, :, 0]), dev(d["new_q"][:, :, 0]))
+    q = d["new_q"][:, :, 0]
+    o = hq.decode_attn(cache, dev(q), 0).cpu().numpy()
+    assert np.all(np.isfinite(o))
+    for b, h in SAMPLE:
+        r = pol.HybridCacheRef(g=G, bits=bk, bits_v=bv)
+        r.freeze(d["K"][b, h], d["V"][b, h], d["anchors"][b, h], d["proxy"][b, h * G:(h + 1) * G])
+        r.append(d["new_k"][b, h, 0], d["new_v"][b, h, 0], q[b, h * G:(h + 1) * G])
+        Kh, Vh = r.stored_kv()
+        ref = att.decode_ref(nm.bf16_to_f32(q[b, h * G:(h + 1) * G]), Kh, Vh)
+        got = o[b, h * G:(h + 1) * G]
+        err = np.abs(got - ref).max()
+        rel = np.linalg.norm(got - ref) / np.linalg.norm(ref)
+        assert err <= MAX_ABS and rel <= REL_L2, f"K{bk}V{bv} b{b} h{h}: max-abs {err:.3g} rel-L2 {rel:.3g}"
+    del cache
+    torch.cuda.empty_cache()
