@@ -168,9 +168,10 @@ int cu_count() {
 
 // Splits per (b, KV head).  Long streams per worker: one full round of two workgroups per CU
 // (the register budget fits two) when every wave still gets >= 16 tiles.  Otherwise the call
-// is latency bound and one workgroup per CU does better, with about 4 tiles per wave but never
-// fewer than 16 splits (measured at batch 1: 16 splits best at 1K and 4K tokens, 32 at 16K
-// and 32K; at batch 16 x 32K, 4 splits = two workgroups per CU).
+// is latency bound and one workgroup per CU does better, down to about one tile per wave but
+// never fewer than 16 splits (measured at batch 1 with the one-latency merge: 16 and 32 splits
+// tie at 1K tokens, 32 is best at 4K, 16K and 32K, 48 and 64 are slower everywhere; at batch
+// 16 x 32K, 4 splits = two workgroups per CU).
 int auto_splits(const hyq_cache_t* c) {
   const int G = c->shape.n_q_heads / c->shape.n_kv_heads;
   const long units = (long)nheads(&c->shape) * ((G + 3) / 4);
@@ -179,7 +180,7 @@ int auto_splits(const hyq_cache_t* c) {
   long s = (2 * cus + units - 1) / units;
   if (tiles < 16 * 4 * s) {
     s = (cus + units - 1) / units;
-    long by_work = (tiles + 15) / 16;
+    long by_work = (tiles + 3) / 4;
     if (by_work < 16) by_work = 16;
     if (s > by_work) s = by_work;
   }
@@ -195,7 +196,7 @@ int auto_splits(const hyq_cache_t* c) {
 // 16 tiles) is dealt out one column at a time to the sequence with the most tiles per split
 // (ties to the lower index), starting from one split each: the largest per-split load, which
 // sets the launch's time, is as small as whole columns allow.  On the short-batch budget a
-// sequence takes at most max(16, tiles / 16) splits.  The total never exceeds
+// sequence takes at most max(16, tiles / 4) splits (as auto_splits).  The total never exceeds
 // ragged_split_bound().
 int ragged_columns(int Hkv, int G, bool two_per_cu) {
   const long u1 = (long)Hkv * ((G + 3) / 4);
@@ -230,7 +231,7 @@ void ragged_plan(const hyq_cache_t* const* cs, int n, int Hkv, int G, int n_spli
   for (long left = C - n; left > 0 && !heap.empty(); --left) {
     Item it = heap.top();
     heap.pop();
-    const long cap = low ? ((it.t + 15) / 16 > 16 ? (it.t + 15) / 16 : 16) : 1L << 30;
+    const long cap = low ? ((it.t + 3) / 4 > 16 ? (it.t + 3) / 4 : 16) : 1L << 30;
     if (it.s >= cap) {  // this sequence is done; the column goes to the next one
       ++left;
       continue;

@@ -466,7 +466,42 @@ __global__ __launch_bounds__(256) void decode_split_kernel(Params p) {
 // ReduceSoftmax over the split records (HyQuant paper Alg. 3): one workgroup per (b, Q head).
 // A separate launch: the kernel boundary makes the records of all XCDs visible without the
 // L2 write-back an in-kernel agent-scope release would cost every workgroup.
-constexpr int FAST_SPLITS = 32;  // merges of up to this many splits take the one-latency path
+// Merge of n_splits <= NS records with every load issued before the first is used: lane
+// j < n_splits reads split j's (m, l), and every lane its two channels of all records (indices
+// clamped, the surplus weighted 0), so the merge costs one memory latency.  Same arithmetic
+// and order as the multi-pass merge below.
+template <int NS>
+__device__ inline void merge_one_latency(const float* rec, int n_splits, float* o, int lane) {
+  const int last = n_splits - 1;
+  const float* rl = rec + (size_t)min(lane, last) * (D + 2);
+  const float m = rl[0], l = rl[1];
+  float a[NS], c[NS];
+#pragma unroll
+  for (int j = 0; j < NS; ++j) {
+    const float* r = rec + (size_t)min(j, last) * (D + 2) + 2;
+    a[j] = r[lane];
+    c[j] = r[lane + 64];
+  }
+  float M = lane < n_splits ? m : -INFINITY;
+#pragma unroll
+  for (int k = 32; k >= 1; k >>= 1) M = fmaxf(M, shfl_xor_f(M, k));
+  float w = 0.f, lw = 0.f;
+  if (M != -INFINITY && lane < n_splits) {
+    w = __builtin_amdgcn_exp2f(m - M);
+    lw = l * w;
+  }
+#pragma unroll
+  for (int k = 32; k >= 1; k >>= 1) lw += shfl_xor_f(lw, k);
+  float O0 = 0.f, O1 = 0.f;
+#pragma unroll
+  for (int j = 0; j < NS; ++j) {
+    const float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), j));  // 0 past the last split
+    O0 = fmaf(a[j], wj, O0);
+    O1 = fmaf(c[j], wj, O1);
+  }
+  o[lane] = O0 / lw;
+  o[lane + 64] = O1 / lw;
+}
 
 template <bool RAGGED>
 __global__ __launch_bounds__(64) void decode_reduce_kernel(const float* __restrict__ part, float* __restrict__ o,
@@ -482,42 +517,9 @@ __global__ __launch_bounds__(64) void decode_reduce_kernel(const float* __restri
   } else {
     rec = part + (size_t)bh * n_splits * (D + 2);
   }
-  if (n_splits <= FAST_SPLITS) {
-    // every load of the merge is issued before the first is used: lane j < n_splits reads split
-    // j's (m, l), and every lane its two channels of all records (indices clamped, the surplus
-    // weighted 0), so the merge costs one memory latency
-    const int last = n_splits - 1;
-    const float* rl = rec + (size_t)min(lane, last) * (D + 2);
-    const float m = rl[0], l = rl[1];
-    float a[FAST_SPLITS], c[FAST_SPLITS];
-#pragma unroll
-    for (int j = 0; j < FAST_SPLITS; ++j) {
-      const float* r = rec + (size_t)min(j, last) * (D + 2) + 2;
-      a[j] = r[lane];
-      c[j] = r[lane + 64];
-    }
-    const float mine = lane < n_splits ? m : -INFINITY;
-    float Mf = mine;
-#pragma unroll
-    for (int k = 32; k >= 1; k >>= 1) Mf = fmaxf(Mf, shfl_xor_f(Mf, k));
-    float w = 0.f, lw = 0.f;
-    if (Mf != -INFINITY && lane < n_splits) {
-      w = __builtin_amdgcn_exp2f(m - Mf);
-      lw = l * w;
-    }
-#pragma unroll
-    for (int k = 32; k >= 1; k >>= 1) lw += shfl_xor_f(lw, k);
-    float O0 = 0.f, O1 = 0.f;
-#pragma unroll
-    for (int j = 0; j < FAST_SPLITS; ++j) {
-      const float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), j));  // 0 past the last split
-      O0 = fmaf(a[j], wj, O0);
-      O1 = fmaf(c[j], wj, O1);
-    }
-    o[(size_t)bh * D + lane] = O0 / lw;
-    o[(size_t)bh * D + lane + 64] = O1 / lw;
-    return;
-  }
+  if (n_splits <= 8) return merge_one_latency<8>(rec, n_splits, o + (size_t)bh * D, lane);
+  if (n_splits <= 32) return merge_one_latency<32>(rec, n_splits, o + (size_t)bh * D, lane);
+  if (n_splits <= 64) return merge_one_latency<64>(rec, n_splits, o + (size_t)bh * D, lane);
   float M = -INFINITY;
   for (int s0 = 0; s0 < n_splits; s0 += 64) {
     const int s = s0 + lane;
