@@ -615,8 +615,8 @@ def cpu_baseline(args, G, bytes_per_head):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1 (sharding is described in "
-                                   "the design notes, not launched)"}))
+        print(json.dumps({"error": "the benchmark runs on one GPU: --gpus must be 1 (the path shards by "
+                                   "sequence or KV head, which no run here launches)"}))
         sys.exit(2)
     import torch
     from hybrid_precision_kv_amd import api as hq

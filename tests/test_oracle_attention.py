@@ -169,7 +169,7 @@ def test_table14_accounting_reproduced():
         assert round(overhead(t["staging_capacity"], L), 1) == t["staging_pct"][i]
         tot = overhead(0.05 * L, L) + 2 * overhead(128, L)
         assert abs(tot - t["total_pct_approx"][i]) < 0.15
-    # this build's format carries fp16 scale+min per 32 channels: 5 bits per element,
+    # the library's INT4 format carries fp16 scale+min per 32 channels: 5 bits per element,
     # i.e. 160 bytes per quantized position (K+V, D = 128) versus 512 in bf16
     assert 2 * 128 * 5 // 8 == 160 and 2 * 128 * 2 == 512
 
