@@ -29,6 +29,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "hybrid decode-attn µs/step + achieved HBM GB/s, 32K ctx, bs1/bs16"
 HBM_PEAK_GBS = 8000.0
+EXP_PEAK_T = 256 * 4 * 16 / 4 * 2.4e9 / 1e12  # exp2 per second (T): quarter-rate transcendental
 D, W = 128, 128
 
 
@@ -418,6 +419,15 @@ def bench_selector(torch, hq, gen, dev, B=4, Hq=64, Hkv=8, L=32768):
         us, got = timed_graph(torch, lambda: hq.select_vlines(shape, k, cache=cache), 10)
         res[f"select_{pct}pct_us"] = round(us, 1)
         res[f"select_{pct}pct_graph_equal"] = bool(torch.equal(got, ref))
+    # ALU roofline: the irreducible work is one exp2 per (proxy row, key) pair in each of the
+    # two passes (row normalisers, then Eq. 4 column sums); the peak is the transcendental
+    # rate with packed fp32 off: 256 CUs x 4 SIMDs x 16 lanes / 4 cycles x 2.4 GHz
+    pairs = B * Hkv * (64 * G) * (L - W)
+    exps = 2 * pairs
+    us5 = res["select_5pct_us"]
+    res["roofline"] = {"bound": "alu", "achieved": round(exps / (us5 * 1e-6) / 1e12, 3), "peak": EXP_PEAK_T,
+                       "unit": "Texp/s", "frac": round(exps / (us5 * 1e-6) / 1e12 / EXP_PEAK_T, 4), "traffic": None,
+                       "exps_per_call": exps, "basis": "5% call; two exp2 per (proxy row, key) pair"}
     k_t = torch.randn(B, Hkv, D, generator=gen, device=dev).to(torch.bfloat16)
     q_t = torch.randn(B, Hq, D, generator=gen, device=dev).to(torch.bfloat16)
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
