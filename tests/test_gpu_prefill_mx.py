@@ -116,9 +116,11 @@ def test_prefill_mx_deterministic():
     assert np.array_equal(a, b)
 
 
-@pytest.mark.parametrize("N,blocks,heads", [(8192, [0, 2, 64, 127], [0, 5, 31])])
+@pytest.mark.parametrize("N,blocks,heads", [(8192, [0, 2, 64, 127], [0, 5, 31]),
+                                           (32768, [0, 255, 511], [0, 31])])
 def test_prefill_mx_full_size_sampled(N, blocks, heads):
-    """Hybrid-prefill workload shape (32 Q / 8 KV heads, 5% anchors): operands compared in
-    full, outputs on sampled (64-query block, head) pairs."""
+    """Hybrid-prefill workload shapes (32 Q / 8 KV heads, 5% anchors, 8K and 32K tokens, the
+    lengths the benchmark times): operands compared in full, outputs on sampled (64-query
+    block, head) pairs."""
     d = synth.gen_prefill(6600 + N, 32, 8, N)
     parity_mx(d, anchors_dense(d, 32, 8, N), 32, 8, N, f"full N={N}", blocks=blocks, heads=heads)
