@@ -7,7 +7,9 @@ The whole batch is drawn from the shared seeded generator.  Sampled heads take t
 anchor sets (so both sides freeze the same positions); the other heads take the GPU dense
 selector's, which only serve as inputs.  After Freeze and one appended token, each sampled
 head's output must meet the decode bar (2e-3 max-abs, 1e-3 relative L2 against the oracle's
-fp64 decode over the head's stored cache)."""
+fp64 decode over the head's stored cache).  The maintenance step at the same size (64
+appends, cache-mode selection, refresh) is checked on the same sampled heads: scores within
+1e-5 of the largest, sets equal except near-ties, then decode after the refresh."""
 import numpy as np
 import pytest
 import torch
@@ -18,6 +20,7 @@ from oracle import attention as att
 from oracle import numerics as nm
 from oracle import policy as pol
 from tests.test_gpu_decode import MAX_ABS, REL_L2, dev
+from tests.test_gpu_select import check_set
 
 pytestmark = pytest.mark.gpu
 
@@ -28,7 +31,7 @@ SAMPLE = [(0, 0), (7, 3), (15, 7)]
 @pytest.fixture(scope="module")
 def batch():
     print(f"[case] full size: generating B={B} Hkv={HKV} G={G} L={L}", flush=True)
-    d = synth.gen_batch(12000, B, HKV, G, L, n_proxy=64, n_steps=1)
+    d = synth.gen_batch(12000, B, HKV, G, L, n_proxy=64, n_steps=64)
     print("[case] full size: generated", flush=True)
     k = pol.k_rule(L)
     shape = hq.Shape.for_context(B, HKV * G, HKV, L + 1)
@@ -63,5 +66,53 @@ def test_full_size_decode_sampled(batch, bk, bv):
         err = np.abs(got - ref).max()
         rel = np.linalg.norm(got - ref) / np.linalg.norm(ref)
         assert err <= MAX_ABS and rel <= REL_L2, f"K{bk}V{bv} b{b} h{h}: max-abs {err:.3g} rel-L2 {rel:.3g}"
+    del cache
+    torch.cuda.empty_cache()
+
+
+def _check_decode(o, q, refs):
+    for (b, h), r in refs.items():
+        Kh, Vh = r.stored_kv()
+        ref = att.decode_ref(nm.bf16_to_f32(q[b, h * G:(h + 1) * G]), Kh, Vh)
+        got = o[b, h * G:(h + 1) * G]
+        err = np.abs(got - ref).max()
+        rel = np.linalg.norm(got - ref) / np.linalg.norm(ref)
+        assert err <= MAX_ABS and rel <= REL_L2, f"b{b} h{h}: max-abs {err:.3g} rel-L2 {rel:.3g}"
+
+
+def test_full_size_select_and_refresh_sampled(batch):
+    """bs16 x 32K, 32/8 heads, K4V4: 64 appends fill the staging buffers, then hyq_select_vlines
+    over the cache at the 5% rule and apply (the maintenance step the benchmark times)."""
+    d = batch
+    print("[case] full size maintenance K4V4", flush=True)
+    shape = hq.Shape.for_context(B, HKV * G, HKV, L + 64)
+    cache = hq.HybridKVCache(shape)
+    hq.quantize_kv(cache, d["Kd"], d["Vd"], torch.from_numpy(d["anchors"]).cuda(), d["Pd"])
+    refs = {}
+    for b, h in SAMPLE:
+        r = pol.HybridCacheRef(g=G)
+        r.freeze(d["K"][b, h], d["V"][b, h], d["anchors"][b, h], d["proxy"][b, h * G:(h + 1) * G])
+        refs[(b, h)] = r
+    for t in range(64):
+        hq.append_token(cache, dev(d["new_k"][:, :, t]), dev(d["new_v"][:, :, t]), dev(d["new_q"][:, :, t]))
+        for (b, h), r in refs.items():
+            r.append(d["new_k"][b, h, t], d["new_v"][b, h, t], d["new_q"][b, h * G:(h + 1) * G, t])
+    k = pol.k_rule(cache.len)
+    idx, sc = hq.select_vlines(shape, k, cache=cache, scores=True)
+    idx, sc = idx.cpu().numpy(), sc.cpu().numpy()
+    P = cache.len - 128
+    flips = 0
+    for (b, h), r in refs.items():
+        A, S = r.select()
+        assert np.max(np.abs(sc[b, h, :P] - S)) <= 1e-5 * S.max(), f"scores b{b} h{h}"
+        flips += check_set(idx[b, h], S, k, f"full size b{b} h{h}")
+    idx2 = hq.select_vlines(shape, k, cache=cache, apply=True).cpu().numpy()
+    assert np.array_equal(idx2, idx)
+    for (b, h), r in refs.items():
+        r.refresh(idx[b, h])
+    assert cache.n_anchor == k and cache.n_staged == 0 and cache.n_int4 == P - k
+    q = d["new_q"][:, :, 63]
+    _check_decode(hq.decode_attn(cache, dev(q), 0).cpu().numpy(), q, refs)
+    print(f"[full size] maintenance: k={k}, near-tie flips {flips}", flush=True)
     del cache
     torch.cuda.empty_cache()
