@@ -116,3 +116,59 @@ def test_full_size_select_and_refresh_sampled(batch):
     print(f"[full size] maintenance: k={k}, near-tie flips {flips}", flush=True)
     del cache
     torch.cuda.empty_cache()
+
+
+def test_full_size_batch1_decode_all_heads():
+    """Batch 1 x 32768 at 32/8 heads with automatic splits (32 per KV head: the latency-bound
+    plan the batch-1 benchmark rows time), every head against the oracle."""
+    print("[case] full size batch 1", flush=True)
+    d = synth.gen_batch(12100, 1, HKV, G, L, n_proxy=64, n_steps=1)
+    shape = hq.Shape.for_context(1, HKV * G, HKV, L + 1)
+    k = pol.k_rule(L)
+    anchors = np.zeros((1, HKV, k), np.int32)
+    refs = {}
+    for h in range(HKV):
+        A, _ = pol.select_dense(d["K"][0, h], d["proxy"][0, h * G:(h + 1) * G])
+        anchors[0, h] = A
+        r = pol.HybridCacheRef(g=G)
+        r.freeze(d["K"][0, h], d["V"][0, h], A, d["proxy"][0, h * G:(h + 1) * G])
+        r.append(d["new_k"][0, h, 0], d["new_v"][0, h, 0], d["new_q"][0, h * G:(h + 1) * G, 0])
+        refs[(0, h)] = r
+    cache = hq.HybridKVCache(shape)
+    hq.quantize_kv(cache, dev(d["K"]), dev(d["V"]), torch.from_numpy(anchors).cuda(), dev(d["proxy"]))
+    hq.append_token(cache, dev(d["new_k"][:, :, 0]), dev(d["new_v"][:, :, 0]), dev(d["new_q"][:, :, 0]))
+    q = d["new_q"][:, :, 0]
+    _check_decode(hq.decode_attn(cache, dev(q), 0).cpu().numpy(), q, refs)
+
+
+def test_full_size_selector_qwen32b_shape():
+    """The selector row's workload: 64 Q / 8 KV heads (GQA 8), batch 4 x 32768, cache-mode
+    selection at 1%, 5% and 10% of the context; sampled heads against the oracle (scores
+    within 1e-5 of the largest, sets equal except near-ties)."""
+    Bs, Gs = 4, 8
+    print(f"[case] full size selector B={Bs} G={Gs}", flush=True)
+    d = synth.gen_batch(12200, Bs, HKV, Gs, L, n_proxy=64)
+    shape = hq.Shape.for_context(Bs, HKV * Gs, HKV, L, 10)
+    k5 = pol.k_rule(L)
+    anchors = hq.select_vlines(shape, k5, dense_k=dev(d["K"]), proxy=dev(d["proxy"])).cpu().numpy()
+    sample = [(0, 0), (3, 7)]
+    refs = {}
+    for b, h in sample:
+        A, _ = pol.select_dense(d["K"][b, h], d["proxy"][b, h * Gs:(h + 1) * Gs])
+        anchors[b, h] = A
+        r = pol.HybridCacheRef(g=Gs)
+        r.freeze(d["K"][b, h], d["V"][b, h], A, d["proxy"][b, h * Gs:(h + 1) * Gs])
+        refs[(b, h)] = r
+    cache = hq.HybridKVCache(shape)
+    hq.quantize_kv(cache, dev(d["K"]), dev(d["V"]), torch.from_numpy(anchors).cuda(), dev(d["proxy"]))
+    P = L - 128
+    flips = 0
+    for pct in (1, 5, 10):
+        k = pol.k_rule(L, pct_num=pct)
+        idx, sc = hq.select_vlines(shape, k, cache=cache, scores=True)
+        idx, sc = idx.cpu().numpy(), sc.cpu().numpy()
+        for (b, h), r in refs.items():
+            _, S = r.select(pct_num=pct)
+            assert np.max(np.abs(sc[b, h, :P] - S)) <= 1e-5 * S.max(), f"scores {pct}% b{b} h{h}"
+            flips += check_set(idx[b, h], S, k, f"selector {pct}% b{b} h{h}")
+    print(f"[full size] selector: near-tie flips {flips}", flush=True)
