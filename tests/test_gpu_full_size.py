@@ -19,7 +19,7 @@ from hybrid_precision_kv_amd import synth
 from oracle import attention as att
 from oracle import numerics as nm
 from oracle import policy as pol
-from tests.test_gpu_decode import MAX_ABS, REL_L2, dev
+from tests.test_gpu_decode import MAX_ABS, REL_L2, Pair, dev
 from tests.test_gpu_select import check_set
 
 pytestmark = pytest.mark.gpu
@@ -172,3 +172,11 @@ def test_full_size_selector_qwen32b_shape():
             assert np.max(np.abs(sc[b, h, :P] - S)) <= 1e-5 * S.max(), f"scores {pct}% b{b} h{h}"
             flips += check_set(idx[b, h], S, k, f"selector {pct}% b{b} h{h}")
     print(f"[full size] selector: near-tie flips {flips}", flush=True)
+
+
+def test_full_size_all_bf16_batch1():
+    """The all-bf16 comparison row at 32768 tokens (k = P: every candidate an anchor, nothing
+    quantized), 32/8 heads, automatic splits, every head against the oracle."""
+    p = Pair(12300, 1, HKV, G, L, n_steps=1, pct=100)
+    assert p.cache.n_int4 == 0 and p.cache.n_anchor == L - 128
+    p.decode_check(p.append())
