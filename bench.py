@@ -66,10 +66,13 @@ def parse():
 
 
 def kernel_source_hash() -> str:
+    """Hash of the decode kernel's sources and of its compile flags."""
+    from hybrid_precision_kv_amd import build
     h = hashlib.sha256()
     for f in ("decode.hip", "hyq_common.h"):
         with open(os.path.join(ROOT, "hybrid_precision_kv_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
+    h.update(" ".join(build.COMMON + build.EXTRA["decode.hip"]).encode())
     return h.hexdigest()[:16]
 
 
