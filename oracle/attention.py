@@ -201,8 +201,42 @@ def mx_dot(q4, qe, k4, ke) -> np.ndarray:
     return qv @ kv.T
 
 
+MIDPOINT_BAND = 2.0 ** -16
+
+
+def _count_near_midpoints(stats, p32, valid, seg):
+    """Diagnostic of the rounded prefill: how many stored p values another fp32
+    implementation could round the other way.  An fp32 value x = 448 p (segment A, E4M3) or
+    x = p (segments B and C, bf16) is counted when it lies within MIDPOINT_BAND * x of a
+    rounding midpoint of its format; a different but correct fp32 evaluation of the same
+    score and exponential (another association, an exp2 with a rescaled argument) moves x
+    by far less than that band for scores of the sizes met here, so the count bounds the
+    codes that can differ.  stats gets n_A / near_A / n_BC / near_BC and p_near_max_A /
+    p_near_max_BC (the largest p among the counted values of each kind)."""
+    x = np.asarray(p32, np.float64)
+    if seg == "A":
+        x = (np.float32(448) * np.asarray(p32, np.float32)).astype(np.float64)
+        tab = nm.e4m3_decode_table()[:127]
+        hi = np.clip(np.searchsorted(tab, x, side="left"), 1, 126)
+        up = np.where(hi < 126, (tab[hi] + tab[np.minimum(hi + 1, 126)]) / 2, np.inf)  # none above 448
+        mids = np.stack([(tab[hi - 1] + tab[hi]) / 2, up])
+        dist = np.abs(mids - x[None]).min(axis=0)
+    else:
+        u = np.asarray(p32, np.float32).view(np.uint32).astype(np.int64)
+        ulp = np.ldexp(1.0, ((u >> 23) & 0xFF).astype(np.int64) - 127 - 7)  # bf16 spacing at x
+        dist = np.abs((u & 0xFFFF) - 0x8000) / 65536.0 * ulp
+    near = valid & (x > 0) & (dist <= MIDPOINT_BAND * x)
+    key = "A" if seg == "A" else "BC"
+    stats["n_" + key] = stats.get("n_" + key, 0) + int(np.count_nonzero(valid))
+    stats["near_" + key] = stats.get("near_" + key, 0) + int(np.count_nonzero(near))
+    if near.any():
+        pm = float(np.asarray(p32, np.float64)[near].max())
+        stats["p_near_max_" + key] = max(stats.get("p_near_max_" + key, 0.0), pm)
+
+
 def prefill_ref(Q_bits, K_bits, V_bits, anchors, W: int = 128, BM: int = 64, BN: int = 64,
-                blocks=None, round_p: bool = True, heads=None, qz=None, bulk: str = "int8"):
+                blocks=None, round_p: bool = True, heads=None, qz=None, bulk: str = "int8",
+                stats=None):
     """Emulation of the hybrid prefill operator (HyQuant paper §4.2 Eq. 6-7, Alg. 2).
 
     For query i (causal), keys split three ways (Eq. 1 applied per query):
@@ -217,16 +251,20 @@ def prefill_ref(Q_bits, K_bits, V_bits, anchors, W: int = 128, BM: int = 64, BN:
     segment A: e4m3(448 p) / 448, segments B and C: bf16(p); l sums the rounded values.
 
     Precision.  With ``round_p`` the values that decide a rounded code -- the score s,
-    the running max m and p -- are taken in IEEE fp32 (the pages fix no precision for
-    them; fp32 is the operator's): s = ((dot * s_Q) * s_K) * alpha for quantized keys
-    (dot an exact integer), s = fp32(fp32(q.k) * alpha) for bf16 keys, p = fp32(exp(s - m)),
-    then 448 p in fp32 before the E4M3 rounding.  The rescale factors, l and the
-    accumulator stay fp64.  Without ``round_p`` everything is fp64 (the exact mixed
+    the running max m and p -- are IEEE fp32 values (the pages fix no precision for them;
+    the online softmax of a FlashAttention-style operator keeps fp32 state).  The score
+    follows Alg. 2's Segment A line, which multiplies the integer dot by the product of the
+    two scales and then by alpha: s = fp32(fp32(dot * fp32(s_Q * s_K)) * alpha) (dot an
+    exact integer); bf16 keys: s = fp32(fp32(q.k) * alpha) with q.k exact.  p is the
+    correctly rounded fp32 value of exp(fp32(s - m)) (an fp64 exponential rounded once to
+    fp32), then 448 p is rounded to fp32 before the E4M3 rounding.  The rescale factors, l
+    and the accumulator stay fp64.  Without ``round_p`` everything is fp64 (the exact mixed
     softmax of Eq. 7).  ``blocks`` / ``heads``: optional lists of 64-query blocks and Q heads
     to compute (others are NaN); ``qz``: the ``prefill_quantize`` result, if already at hand.
     ``bulk="mxfp4"``: the quantized segment's Q.K^T uses ``prefill_quantize_mx`` operands,
     s = fp32(exact MX dot) * alpha (the products and their block sums are exact in fp64; the
-    operator accumulates them in fp32), everything else unchanged.
+    operator accumulates them in fp32), everything else unchanged.  ``stats``: an optional
+    dict that receives the near-midpoint counts of ``_count_near_midpoints``.
     Returns fp64 [Hq][N][D].
     """
     Qf = nm.bf16_to_f32(Q_bits).astype(np.float64)
@@ -280,8 +318,11 @@ def prefill_ref(Q_bits, K_bits, V_bits, anchors, W: int = 128, BM: int = 64, BN:
                 c = np.where(live & had, np.exp(np.where(had, m, 0.0).astype(np.float64)
                                                  - np.where(live, m_new, 0.0)), 0.0)
                 with np.errstate(invalid="ignore"):
-                    p = np.where(valid, np.exp(s - np.where(live, m_new, ft(0))[:, None]), ft(0))
+                    z = s - np.where(live, m_new, ft(0))[:, None]  # fp32 difference when rounding
+                    p = np.where(valid, np.exp(z.astype(np.float64)).astype(ft), ft(0))
                 if round_p:
+                    if stats is not None:
+                        _count_near_midpoints(stats, p, valid, seg)
                     if seg == "A":
                         p = nm.e4m3_round_fast(np.float32(448) * p) / 448.0
                     else:
@@ -301,7 +342,8 @@ def prefill_ref(Q_bits, K_bits, V_bits, anchors, W: int = 128, BM: int = 64, BN:
                     else:
                         dot = q8 @ k8[j].T
                         if round_p:
-                            s = ((dot.astype(np.float32) * np.float32(sq)) * qz["sk"][hk, t]) * np.float32(alpha)
+                            ssc = np.float32(sq) * np.float32(qz["sk"][hk, t])  # s_Q s_K (fp32)
+                            s = (dot.astype(np.float32) * ssc) * np.float32(alpha)
                         else:
                             s = dot.astype(np.float64) * (sq * float(qz["sk"][hk, t])) * alpha
                     valid = (j[None, :] <= rows[:, None] - W) & ~isanc[j][None, :]

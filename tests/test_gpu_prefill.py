@@ -4,10 +4,13 @@ against the oracle's step-by-step emulation.
 Bar:
   * operand quantization -- INT8 Q and K codes, E4M3 V codes, their fp32 scales and the anchor
     bitmap -- bit-exact (read back from the documented workspace layout);
-  * outputs within 2e-3 max-abs and 1e-3 relative L2 of ``oracle.attention.prefill_ref``,
-    which takes the P rounding decisions in fp32 like the kernel.  The P codes themselves are
-    not compared: the kernel's exp2 and the oracle's exp may land on opposite sides of an
-    E4M3 rounding boundary for a rare element, and that effect lies inside the output bound.
+  * outputs within 2e-3 max-abs and 1e-3 relative L2 of ``oracle.attention.prefill_ref``, for
+    every case alike.  The bar is stated for unit-scale activations, so every case draws its
+    inputs at that scale (|V| below about 8, the tie case included).  The P codes are not
+    compared one by one: the pages fix no precision for the exponential, so the kernel's
+    exp2 and the oracle's correctly rounded exp may round a p that sits on an E4M3 (or bf16)
+    midpoint differently.  Each case prints how many stored p values lie that close to a
+    midpoint (an upper bound on such flips) and its margin to the bar.
 """
 import numpy as np
 import pytest
@@ -62,24 +65,32 @@ def check_operands(w, qz, A, N):
     assert np.array_equal(w["abits"], bits), "anchor bitmap"
 
 
-def check_out(o, ref, label, vscale=1.0):
-    """vscale: how much larger than the unit-variance inputs' (|V| up to about 4.5) the values
-    are; an output error (a rare P rounding flip times a value) scales with them."""
+def check_out(o, ref, label):
     m = ~np.isnan(ref)
     assert m.any()
     diff = np.abs(o[m] - ref[m])
     rel = np.linalg.norm(o[m] - ref[m]) / np.linalg.norm(ref[m])
-    print(f"[{label}] max-abs {diff.max():.3g} rel-L2 {rel:.3g}")
-    assert diff.max() <= MAX_ABS * vscale and rel <= REL_L2, label
+    print(f"[{label}] max-abs {diff.max():.3g} (bar/err {MAX_ABS / max(diff.max(), 1e-30):.1f}x) "
+          f"rel-L2 {rel:.3g} (bar/err {REL_L2 / max(rel, 1e-30):.1f}x)")
+    assert diff.max() <= MAX_ABS and rel <= REL_L2, label
 
 
-def parity(d, A, Hq, Hkv, N, label, blocks=None, heads=None, vscale=1.0):
+def report_midpoints(stats, label):
+    """Stored p values near a rounding midpoint (possible P-code flips), from the oracle."""
+    print(f"[{label}] p near an E4M3 midpoint: {stats.get('near_A', 0)} of {stats.get('n_A', 0)} "
+          f"(largest p {stats.get('p_near_max_A', 0):.3g}); near a bf16 midpoint: "
+          f"{stats.get('near_BC', 0)} of {stats.get('n_BC', 0)}")
+
+
+def parity(d, A, Hq, Hkv, N, label, blocks=None, heads=None):
     print(f"[case] {label} Hq={Hq} Hkv={Hkv} N={N} k={A.shape[1]}", flush=True)
     o, w = run_gpu(d, A, Hq, Hkv, N)
     qz = att.prefill_quantize(d["Q"], d["K"], d["V"], A)
     check_operands(w, qz, A, N)
-    ref = att.prefill_ref(d["Q"], d["K"], d["V"], A, blocks=blocks, heads=heads, qz=qz)
-    check_out(o, ref, label, vscale)
+    stats = {}
+    ref = att.prefill_ref(d["Q"], d["K"], d["V"], A, blocks=blocks, heads=heads, qz=qz, stats=stats)
+    report_midpoints(stats, label)
+    check_out(o, ref, label)
     return o
 
 
@@ -125,7 +136,9 @@ def test_prefill_degenerate_scales():
 
 
 def test_prefill_e4m3_ties():
-    """V values on E4M3 rounding midpoints (s_V = 1 exactly): ties must go to the even code."""
+    """V values on E4M3 rounding midpoints: ties must go to the even code.  The values are
+    midpoints times 2^-6 with channel maxima 7, so s_V = 7 / 448 = 2^-6 exactly and every
+    V / s_V is the midpoint itself, at the unit scale of the other cases."""
     N = 300
     d = synth.gen_prefill(5400, 2, 1, N)
     V = nm.bf16_to_f32(d["V"])[0]
@@ -133,10 +146,10 @@ def test_prefill_e4m3_ties():
     vals = nm.e4m3_decode_table()[:126]
     mids = ((vals[:-1] + vals[1:]) / 2).astype(np.float32)
     mids = mids[nm.bf16_to_f32(nm.f32_to_bf16(mids)) == mids]  # midpoints bf16 can hold
-    V[:, :] = rng.choice(mids, size=V.shape) * rng.choice([-1, 1], size=V.shape)
-    V[0, :] = 448.0  # channel maxima 448 -> s_V = 1
+    V[:, :] = rng.choice(mids, size=V.shape) * rng.choice([-1, 1], size=V.shape) * np.float32(2.0 ** -6)
+    V[0, :] = 7.0  # channel maxima 7 -> s_V = 2^-6
     d["V"][0] = nm.f32_to_bf16(V.astype(np.float32))
-    parity(d, np.zeros((1, 0), np.int32), 2, 1, N, "e4m3 ties", vscale=448 / 4.5)
+    parity(d, np.zeros((1, 0), np.int32), 2, 1, N, "e4m3 ties")
 
 
 def test_prefill_deterministic():

@@ -18,7 +18,7 @@ from oracle import attention as att
 from oracle import numerics as nm
 from tests.gpu_layout import read_prefill_mx, read_prefill_ws
 from tests.test_gpu_decode import dev
-from tests.test_gpu_prefill import anchors_dense, check_out
+from tests.test_gpu_prefill import anchors_dense, check_out, report_midpoints
 
 pytestmark = pytest.mark.gpu
 
@@ -50,13 +50,15 @@ def check_operands_mx(w, qz, A, N):
     assert np.array_equal(w["abits"], bits), "anchor bitmap"
 
 
-def parity_mx(d, A, Hq, Hkv, N, label, blocks=None, heads=None, vscale=1.0):
+def parity_mx(d, A, Hq, Hkv, N, label, blocks=None, heads=None):
     print(f"[case] mx {label} Hq={Hq} Hkv={Hkv} N={N} k={A.shape[1]}", flush=True)
     o, w = run_gpu_mx(d, A, Hq, Hkv, N)
     qz = att.prefill_quantize_mx(d["Q"], d["K"], d["V"], A)
     check_operands_mx(w, qz, A, N)
-    ref = att.prefill_ref(d["Q"], d["K"], d["V"], A, blocks=blocks, heads=heads, qz=qz, bulk="mxfp4")
-    check_out(o, ref, "mx " + label, vscale)
+    stats = {}
+    ref = att.prefill_ref(d["Q"], d["K"], d["V"], A, blocks=blocks, heads=heads, qz=qz, bulk="mxfp4", stats=stats)
+    report_midpoints(stats, "mx " + label)
+    check_out(o, ref, "mx " + label)
     return o
 
 
