@@ -16,8 +16,14 @@
 //    q.k = sum_g s_g * (q_g . code_g) + m_g * sum(q_g).
 //  * Sum over the 4 groups with two DPP quad permutes; max across the tile with two lane swaps.
 //  * P.V on the same MFMA: A = V codes of 16 channels x 8 positions per lane, B = P' = p * s_V
-//    (the MFMA output layout of the K product is exactly the B layout needed here), split into
-//    f16 hi + lo parts so the weights keep ~22 bits.  The V min enters as sum p * m_V.
+//    times a power of two 2^e (the MFMA output layout of the K product is exactly the B layout
+//    needed here), split into f16 hi + lo parts so the weights keep ~22 bits.  Each MFMA column
+//    keeps its own e, chosen so that the largest s_V seen times 2^e stays inside [4, 2^15): P'
+//    never overflows f16 and never sinks into its subnormals for any fp16 scale.  When a tile's
+//    s_V leave that band, e moves and the accumulator is rescaled by the exact power of two
+//    (as the softmax rescales it when the max grows).  The V min enters as sum p * m_V in fp32.
+//  * q enters the f16 operands times a power of two per head that puts its largest |q| in
+//    [2^13, 2^14), undone in fp32 after the MFMA: no f16 overflow and no subnormal q.
 //  * bf16 tiles (anchors, staging, window) use the bf16 MFMA with the same softmax state.
 //  * Every load is a coalesced 1 KB read of one 5 KB tile record (layouts in hyq_common.h); the
 //    next INT4 tile is loaded while the current one is computed (two register sets).  Worker w
@@ -33,9 +39,15 @@ namespace {
 
 constexpr int WAVES = 4;
 constexpr float LOG2E = 1.4426950408889634f;
-constexpr float PSCALE = 256.0f;              // P' = p * s_V * PSCALE keeps f16 weights normal
-constexpr float ACC_SCALE = 65536.0f;         // 2^24 / PSCALE: INT4 accumulators -> true scale
-constexpr float BF_PSCALE = 1.0f / 65536.0f;  // bf16 tiles feed p * PSCALE * 2^-24
+// V weight scale 2^e of an MFMA column: the column's largest s_V times 2^e is kept inside
+// [PS_LO, PS_HI); a move puts it in [2^PS_TARGET - 1, 2^PS_TARGET).  The start value 2^8 keeps
+// every unit-scale input (s_V below 2^7) inside the band.
+constexpr float PS_INIT = 256.0f;
+constexpr float PS_HI = 32768.0f;
+constexpr float PS_LO = 4.0f;
+constexpr int PS_TARGET = 8;
+// q scale: the head's largest |q| times 2^sigma lands in [2^(Q_TARGET-1), 2^Q_TARGET)
+constexpr int Q_TARGET = 14;
 
 // 8 INT4 codes (one dword) -> 8 f16 MFMA operands (subnormal bit patterns).  Element order:
 // nibbles 0,4 | 1,5 (x16) | 2,6 | 3,7 (x16).
@@ -53,8 +65,42 @@ __device__ inline float half_hi(uint32_t v) { return (float)__builtin_bit_cast(_
 
 struct WaveState {
   float m, l, mt;
+  float ps, ps_hi, ps_lo;  // V weight scale 2^e of this lane's column, and the band on max s_V
   f32x4 acc[8];
 };
+
+// Largest fp16 scale s_V of this lane's 8 positions (low halves of the (scale, min) pairs;
+// the scales are >= 0, so the packed f16 max of the low halves is their max).
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+__device__ inline float max_vscale(const uint32_t (&smv)[8]) {
+  f16x2 a[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    a[j] = __builtin_elementwise_max(__builtin_bit_cast(f16x2, smv[2 * j]), __builtin_bit_cast(f16x2, smv[2 * j + 1]));
+  const f16x2 b = __builtin_elementwise_max(__builtin_elementwise_max(a[0], a[1]), __builtin_elementwise_max(a[2], a[3]));
+  return (float)b[0];
+}
+
+// Keeps the column's V weight scale inside its band for a tile whose largest s_V on this lane
+// is smax: the four lanes of a column (l, l^16, l^32, l^48) agree on the column maximum, and a
+// column that leaves the band moves its scale and rescales its accumulator exactly.  The
+// common case is one compare per lane and one wave vote.
+__device__ inline void track_vscale(WaveState& st, float smax) {
+  const bool out = smax >= st.ps_hi || (smax > 0.f && smax < st.ps_lo);
+  if (__builtin_amdgcn_ballot_w64(out) == 0) return;
+  const float cm = col4_max(smax);
+  if (cm >= st.ps_hi || (cm > 0.f && cm < st.ps_lo)) {
+    int ex;
+    (void)frexpf(cm, &ex);  // cm = f 2^ex, f in [0.5, 1)
+    const float ps = ldexpf(1.0f, PS_TARGET - ex);
+    const float f = ps / st.ps;  // a power of two: exact
+#pragma unroll
+    for (int r = 0; r < 8; ++r) st.acc[r] *= f;
+    st.ps = ps;
+    st.ps_hi = PS_HI / ps;
+    st.ps_lo = PS_LO / ps;
+  }
+}
 
 // 8 INT8 codes (two dwords) -> 8 f16 MFMA operands (subnormal bit patterns, exact: codes <=
 // 255).  Element order: bytes 0,2 | 1,3 | 4,6 | 5,7 (kslot_byte).
@@ -180,6 +226,15 @@ __device__ inline void int4_tile(WaveState& st, const QTile<BK, BV>& x, const f1
       sc[4 + r] = valid[4 + r] ? sc[4 + r] : -INFINITY;
     }
   }
+  {
+    uint32_t smv[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      smv[j] = j < 4 ? x.vs0[j] : x.vs1[j - 4];
+      if (MASK) smv[j] = valid[j] ? smv[j] : 0u;  // unused slots may hold any bits
+    }
+    track_vscale(st, max_vscale(smv));
+  }
   float pv[8];
   tile_softmax(st, sc, pv);
   f16x8 bhi, blo;
@@ -189,7 +244,7 @@ __device__ inline void int4_tile(WaveState& st, const QTile<BK, BV>& x, const f1
     const uint32_t smv = j < 4 ? x.vs0[j] : x.vs1[j - 4];
     const float pj = pv[j];
     // code operands scaled per k-slot (INT4: x16 on k-slots 2,3,6,7; 2-bit: 4^(j >> 1))
-    float pp = pj * half_lo(smv) * (PSCALE * code_factor<BV>(j));
+    float pp = pj * half_lo(smv) * (st.ps * code_factor<BV>(j));
     float mm = pj * half_hi(smv);
     if (MASK) {  // unused slots may hold any scale/min bits: keep them out entirely
       pp = valid[j] ? pp : 0.f;
@@ -298,8 +353,10 @@ __global__ __launch_bounds__(256) void decode_split_kernel(Params p) {
   f16x8 bq4[4];
   float qsum = 0.f;
   const bool use = head_ok && (g == q4);
+  float qs;  // 2^sigma: the head's largest |q| times qs lies in [2^13, 2^14)
   {
     float f[32];  // channels 32 q4 .. 32 q4 + 31
+    float amax = 0.f;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const u32x4 w = *(const u32x4*)&q_lds[hh][16 * q4 + 4 * t];
@@ -310,10 +367,16 @@ __global__ __launch_bounds__(256) void decode_split_kernel(Params p) {
       }
     }
 #pragma unroll
+    for (int c = 0; c < 32; ++c) amax = fmaxf(amax, fabsf(f[c]));
+    amax = col4_max(amax);  // lanes l, l^16, l^32, l^48: the four channel blocks of head hh
+    int ex = 0;
+    if (amax > 0.f) (void)frexpf(amax, &ex);
+    qs = ldexpf(1.0f, min(100, max(-100, Q_TARGET - ex)));
+#pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float v = f[kstep_channel<BK>(t, e)] * code_factor<BK>(e);
+        const float v = f[kstep_channel<BK>(t, e)] * qs * code_factor<BK>(e);
         bq4[t][e] = use ? (_Float16)v : (_Float16)0.f;
       }
   }
@@ -323,18 +386,21 @@ __global__ __launch_bounds__(256) void decode_split_kernel(Params p) {
       const u32x4 w = *(const u32x4*)&q_lds[hh][16 * g + 4 * t];
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        qsum += (float)(_Float16)bf16_bits_to_f32((uint16_t)(w[e] & 0xffff)) +
-                (float)(_Float16)bf16_bits_to_f32((uint16_t)(w[e] >> 16));
+        qsum += (float)(_Float16)(bf16_bits_to_f32((uint16_t)(w[e] & 0xffff)) * qs) +
+                (float)(_Float16)(bf16_bits_to_f32((uint16_t)(w[e] >> 16)) * qs);
     }
   }
   const float qsum24 = qsum * (1.0f / 16777216.0f);
   const float alpha_log2 = LOG2E * 0.08838834764831845f;  // log2(e) / sqrt(128)
-  const float c_int4 = alpha_log2 * 16777216.0f;
+  const float c_int4 = alpha_log2 * 16777216.0f / qs;
 
   WaveState st;
   st.m = -INFINITY;
   st.l = 0.f;
   st.mt = 0.f;
+  st.ps = PS_INIT;
+  st.ps_hi = PS_HI / PS_INIT;
+  st.ps_lo = PS_LO / PS_INIT;
 #pragma unroll
   for (int r = 0; r < 8; ++r) st.acc[r] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
@@ -408,9 +474,10 @@ __global__ __launch_bounds__(256) void decode_split_kernel(Params p) {
     float pv[8];
     tile_softmax(st, sc, pv);
     bf16x8 bhi, blo;
+    const float bfs = st.ps * (1.0f / 16777216.0f);  // bf16 tiles feed p 2^e 2^-24
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const float pp = valid[j] ? pv[j] * BF_PSCALE : 0.f;
+      const float pp = valid[j] ? pv[j] * bfs : 0.f;
       const __bf16 h = (__bf16)pp;
       bhi[j] = h;
       blo[j] = (__bf16)(pp - (float)h);
@@ -436,7 +503,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(Params p) {
   for (int rr = 0; rr < 8; ++rr) {
     if ((rr >> 1) == g) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) red_o[wave][hh][16 * rr + 4 * q4 + r] = st.acc[rr][r] * ACC_SCALE + st.mt;
+      for (int r = 0; r < 4; ++r) red_o[wave][hh][16 * rr + 4 * q4 + r] = st.acc[rr][r] * (16777216.0f / st.ps) + st.mt;
     }
   }
   __syncthreads();
