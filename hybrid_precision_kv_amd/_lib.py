@@ -18,7 +18,7 @@ BUFFERS = ["int4", "slot_pos", "a_k", "a_v", "a_pos", "s_k", "s_v", "w_k", "w_v"
 EXPORTS = ["hyq_status_string", "hyq_cache_buffer_bytes", "hyq_workspace_bytes", "hyq_quantize_kv",
            "hyq_append_token", "hyq_select_vlines", "hyq_decode_attn", "hyq_prefill_attn",
            "hyq_prefill_attn_mx", "hyq_select_vlines_tail", "hyq_decode_attn_ragged",
-           "hyq_decode_ragged_workspace_bytes"]
+           "hyq_decode_ragged_workspace_bytes", "hyq_decode_ragged_table_bytes", "hyq_decode_ragged_plan"]
 
 
 class HyqShape(C.Structure):
@@ -73,9 +73,13 @@ def load() -> C.CDLL:
     lib.hyq_select_vlines_tail.restype = C.c_int
     lib.hyq_select_vlines_tail.argtypes = [C.POINTER(HyqShape), vp, i32, vp, i32, i32, vp, vp, vp, sz, vp]
     lib.hyq_decode_attn_ragged.restype = C.c_int
-    lib.hyq_decode_attn_ragged.argtypes = [C.POINTER(C.POINTER(HyqCache)), i32, vp, vp, i32, vp, sz, vp]
+    lib.hyq_decode_attn_ragged.argtypes = [C.POINTER(C.POINTER(HyqCache)), i32, vp, vp, i32, vp, sz, vp, sz, vp]
     lib.hyq_decode_ragged_workspace_bytes.restype = sz
     lib.hyq_decode_ragged_workspace_bytes.argtypes = [C.POINTER(HyqShape), i32, i32]
+    lib.hyq_decode_ragged_table_bytes.restype = sz
+    lib.hyq_decode_ragged_table_bytes.argtypes = [C.POINTER(HyqShape), i32, i32]
+    lib.hyq_decode_ragged_plan.restype = C.c_int
+    lib.hyq_decode_ragged_plan.argtypes = [C.POINTER(C.POINTER(HyqCache)), i32, i32, vp, sz, C.POINTER(i32)]
     lib.hyq_prefill_attn_mx.restype = C.c_int
     lib.hyq_prefill_attn_mx.argtypes = [C.POINTER(HyqShape), vp, vp, vp, i32, vp, i32, vp, vp, sz, vp]
     _lib = lib

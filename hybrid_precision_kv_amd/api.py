@@ -214,11 +214,72 @@ def decode_ragged_workspace_bytes(shape: Shape, n_seq: int, n_splits: int = 0) -
     return int(lib.hyq_decode_ragged_workspace_bytes(C.byref(s), n_seq, n_splits))
 
 
+def decode_ragged_table_bytes(shape: Shape, n_seq: int, n_splits: int = 0) -> int:
+    lib = _lib.load()
+    s = shape.c()
+    return int(lib.hyq_decode_ragged_table_bytes(C.byref(s), n_seq, n_splits))
+
+
+def decode_ragged_table(shape: Shape, n_seq: int, n_splits: int = 0) -> torch.Tensor:
+    """A page-locked host table for hyq_decode_attn_ragged (uint8)."""
+    need = decode_ragged_table_bytes(shape, n_seq, n_splits)
+    if need == 0:
+        raise ValueError("unsupported ragged batch (sequence count or split count out of range)")
+    return torch.empty(need, dtype=torch.uint8, pin_memory=True)
+
+
+class _TableRing:
+    """Page-locked tables used in turn by calls that pass none: a table is written again only
+    after the stream has passed the call that last used it (an event per table)."""
+
+    SLOTS = 8
+
+    def __init__(self):
+        self.tabs = [None] * self.SLOTS
+        self.events = [None] * self.SLOTS
+        self.i = 0
+
+    def get(self, nbytes: int):
+        i = self.i
+        self.i = (i + 1) % self.SLOTS
+        if self.events[i] is not None:
+            self.events[i].synchronize()
+            self.events[i] = None
+        if self.tabs[i] is None or self.tabs[i].numel() < nbytes:
+            self.tabs[i] = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+        return i, self.tabs[i]
+
+    def used(self, i: int) -> None:
+        ev = torch.cuda.Event()
+        ev.record()
+        self.events[i] = ev
+
+
+_tables = _TableRing()
+
+
+def _cache_ptrs(caches: list):
+    return (C.POINTER(_lib.HyqCache) * len(caches))(*[C.pointer(c.c) for c in caches])
+
+
+def decode_ragged_plan(caches: list, table: torch.Tensor, n_splits: int = 0) -> int:
+    """Rewrite ``table`` for the caches' current counters (hyq_decode_ragged_plan, host only);
+    returns the total split count, which must equal the one a captured call recorded."""
+    total = C.c_int32(0)
+    lib = _lib.load()
+    check("hyq_decode_ragged_plan", lib.hyq_decode_ragged_plan(_cache_ptrs(caches), len(caches), n_splits,
+                                                               _ptr(table), table.numel(), C.byref(total)))
+    return int(total.value)
+
+
 def decode_attn_ragged(caches: list, q: torch.Tensor, n_splits: int = 0, out: torch.Tensor | None = None,
-                       ws: torch.Tensor | None = None) -> torch.Tensor:
+                       ws: torch.Tensor | None = None, table: torch.Tensor | None = None) -> torch.Tensor:
     """Decode over a variable-length batch (hyq_decode_attn_ragged): ``caches`` are
     single-sequence caches of any lengths with the same heads and bit width; q [n][Hq][128]
-    bf16, one row block per cache; fp32 out [n][Hq][128]."""
+    bf16, one row block per cache; fp32 out [n][Hq][128].  ``table``: a page-locked host table
+    from ``decode_ragged_table`` that the caller keeps alive and unchanged until the stream has
+    passed the call (needed when the call is captured into a graph); without one, the
+    binding's own ring of tables is used."""
     n = len(caches)
     s = caches[0].shape
     _bf16(q, (n, s.n_q_heads, D), "q")
@@ -229,10 +290,17 @@ def decode_attn_ragged(caches: list, q: torch.Tensor, n_splits: int = 0, out: to
         raise ValueError("unsupported ragged batch (sequence count or split count out of range)")
     if ws is None:
         ws = _ws.get(need, q.device)
-    ptrs = (C.POINTER(_lib.HyqCache) * n)(*[C.pointer(c.c) for c in caches])
+    slot = None
+    if table is None:
+        slot, table = _tables.get(decode_ragged_table_bytes(s, n, n_splits))
+    if table.device.type != "cpu":
+        raise ValueError("table: host memory expected")
     lib = _lib.load()
-    check("hyq_decode_attn_ragged", lib.hyq_decode_attn_ragged(ptrs, n, _ptr(q), _ptr(out), n_splits, _ptr(ws),
-                                                               ws.numel(), _stream()))
+    check("hyq_decode_attn_ragged", lib.hyq_decode_attn_ragged(_cache_ptrs(caches), n, _ptr(q), _ptr(out), n_splits,
+                                                               _ptr(table), table.numel(), _ptr(ws), ws.numel(),
+                                                               _stream()))
+    if slot is not None:
+        _tables.used(slot)
     return out
 
 

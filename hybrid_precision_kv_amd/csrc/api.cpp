@@ -2,7 +2,6 @@
 // counters, workspace sizing and kernel launches.  Declarations and contracts: include/hyq.h.
 #include <atomic>
 #include <hip/hip_runtime.h>
-#include <mutex>
 #include <queue>
 #include <string.h>
 #include <vector>
@@ -258,21 +257,69 @@ RaggedWs ragged_ws(int n_seq, int Hq, int Hkv, int n_splits) {
   return w;
 }
 
-// Host staging of the per-call tables: page-locked slots used round-robin, each guarded by an
-// event recorded after its copy, so a slot is rewritten only once the device has taken its
-// previous contents.  One ring per device, created on first use.
 constexpr int RAGGED_MAX_SEQ = 1024;
-struct TableRing {
-  static constexpr int SLOTS = 16;
-  static constexpr size_t SLOT_BYTES = 256 * 1024;
-  std::mutex mu;
-  uint8_t* host = nullptr;
-  hipEvent_t ev[SLOTS] = {};
-  bool pending[SLOTS] = {};
-  int next = 0;
-};
-static_assert(RAGGED_MAX_SEQ * sizeof(hyq::RaggedSeq) + 16384 * 4 <= TableRing::SLOT_BYTES, "ring slot size");
-TableRing g_rings[64];
+constexpr long RAGGED_MAX_SPLITS = 16384;
+
+// Checks a variable-length batch and writes its descriptors and split plan into `table` (host
+// memory of at least w.part bytes, laid out as the head of the workspace).  Host only.
+int ragged_prepare(const hyq_cache_t* const* caches, int32_t n_seq, int32_t n_splits, void* table,
+                   size_t table_bytes, RaggedWs& w, long& total) {
+  if (!caches || n_seq <= 0 || n_splits < 0 || n_splits > 4096) return HYQ_ERR_INVALID;
+  if (n_seq > RAGGED_MAX_SEQ) return HYQ_ERR_CAPACITY;
+  int st;
+  for (int i = 0; i < n_seq; ++i) {
+    const hyq_cache_t* c = caches[i];
+    if (!c) return HYQ_ERR_INVALID;
+    if ((st = check_shape(&c->shape))) return st;
+    if ((st = check_cache_ptrs(c))) return st;
+    if ((st = check_counters(c))) return st;
+    if (c->shape.batch != 1 || c->len <= 0) return HYQ_ERR_INVALID;
+    if (c->shape.n_q_heads != caches[0]->shape.n_q_heads || c->shape.n_kv_heads != caches[0]->shape.n_kv_heads ||
+        qbits(&c->shape) != qbits(&caches[0]->shape) || qbits_v(&c->shape) != qbits_v(&caches[0]->shape))
+      return HYQ_ERR_INVALID;
+  }
+  const hyq_shape_t& s0 = caches[0]->shape;
+  const int Hq = s0.n_q_heads, Hkv = s0.n_kv_heads, G = Hq / Hkv;
+  w = ragged_ws(n_seq, Hq, Hkv, n_splits);
+  if (!table || table_bytes < w.part) return HYQ_ERR_WORKSPACE;
+  int plan[RAGGED_MAX_SEQ];
+  ragged_plan(caches, n_seq, Hkv, G, n_splits, plan);
+  total = 0;
+  for (int i = 0; i < n_seq; ++i) total += plan[i];
+  if (total > ragged_split_bound(n_seq, Hkv, G, n_splits) || total > RAGGED_MAX_SPLITS) return HYQ_ERR_INVALID;
+  uint8_t* host = (uint8_t*)table;
+  hyq::RaggedSeq* seqs = (hyq::RaggedSeq*)(host + w.seqs);
+  uint32_t* map = (uint32_t*)(host + w.map);
+  long rec = 0, col = 0;
+  for (int i = 0; i < n_seq; ++i) {
+    const hyq_cache_t* c = caches[i];
+    hyq::RaggedSeq d;
+    memset(&d, 0, sizeof d);
+    d.int4 = (const uint8_t*)c->int4;
+    d.a_k = (const uint16_t*)c->a_k;
+    d.a_v = (const uint16_t*)c->a_v;
+    d.s_k = (const uint16_t*)c->s_k;
+    d.s_v = (const uint16_t*)c->s_v;
+    d.w_k = (const uint16_t*)c->w_k;
+    d.w_v = (const uint16_t*)c->w_v;
+    d.int4_cap = c->shape.int4_cap;
+    d.anchor_cap = c->shape.anchor_cap;
+    d.staging_cap = c->shape.staging_cap;
+    d.n_int4 = c->n_int4;
+    d.n_anchor = c->n_anchor;
+    d.n_staged = c->n_staged;
+    d.n_win = c->len < W ? c->len : W;
+    d.n_splits = plan[i];
+    d.rec0 = (int)rec;
+    memcpy(&seqs[i], &d, sizeof d);
+    rec += (long)Hq * plan[i];
+    for (int j = 0; j < plan[i]; ++j) map[col++] = ((uint32_t)i << 16) | (uint32_t)j;
+  }
+  // the gap between the descriptors and the map is padding: keep it defined
+  memset(host + w.seqs + (size_t)n_seq * sizeof(hyq::RaggedSeq), 0, w.map - w.seqs - (size_t)n_seq * sizeof(hyq::RaggedSeq));
+  memset(host + w.map + (size_t)total * 4, 0, w.part - w.map - (size_t)total * 4);
+  return HYQ_OK;
+}
 
 }  // namespace
 
@@ -413,81 +460,33 @@ size_t hyq_decode_ragged_workspace_bytes(const hyq_shape_t* s, int32_t n_seq, in
   return ragged_ws(n_seq, s->n_q_heads, s->n_kv_heads, n_splits).total;
 }
 
-int hyq_decode_attn_ragged(const hyq_cache_t* const* caches, int32_t n_seq, const void* q, float* o,
-                           int32_t n_splits, void* ws, size_t ws_bytes, hipStream_t stream) {
-  if (!caches || n_seq <= 0 || !q || !o || n_splits < 0 || n_splits > 4096) return HYQ_ERR_INVALID;
-  if (n_seq > RAGGED_MAX_SEQ) return HYQ_ERR_CAPACITY;
-  int st;
-  for (int i = 0; i < n_seq; ++i) {
-    const hyq_cache_t* c = caches[i];
-    if (!c) return HYQ_ERR_INVALID;
-    if ((st = check_shape(&c->shape))) return st;
-    if ((st = check_cache_ptrs(c))) return st;
-    if ((st = check_counters(c))) return st;
-    if (c->shape.batch != 1 || c->len <= 0) return HYQ_ERR_INVALID;
-    if (c->shape.n_q_heads != caches[0]->shape.n_q_heads || c->shape.n_kv_heads != caches[0]->shape.n_kv_heads ||
-        qbits(&c->shape) != qbits(&caches[0]->shape) || qbits_v(&c->shape) != qbits_v(&caches[0]->shape))
-      return HYQ_ERR_INVALID;
-  }
-  const hyq_shape_t& s0 = caches[0]->shape;
-  const int Hq = s0.n_q_heads, Hkv = s0.n_kv_heads, G = Hq / Hkv;
-  const RaggedWs w = ragged_ws(n_seq, Hq, Hkv, n_splits);
-  if (!ws || ws_bytes < w.total) return HYQ_ERR_WORKSPACE;
-  int plan[RAGGED_MAX_SEQ];
-  ragged_plan(caches, n_seq, Hkv, G, n_splits, plan);
+size_t hyq_decode_ragged_table_bytes(const hyq_shape_t* s, int32_t n_seq, int32_t n_splits) {
+  if (check_shape(s) || n_seq <= 0 || n_seq > RAGGED_MAX_SEQ || n_splits < 0 || n_splits > 4096) return 0;
+  return ragged_ws(n_seq, s->n_q_heads, s->n_kv_heads, n_splits).part;
+}
+
+int hyq_decode_ragged_plan(const hyq_cache_t* const* caches, int32_t n_seq, int32_t n_splits, void* table,
+                           size_t table_bytes, int32_t* total_splits) {
+  RaggedWs w;
   long total = 0;
-  for (int i = 0; i < n_seq; ++i) total += plan[i];
-  if (total > ragged_split_bound(n_seq, Hkv, G, n_splits) || total > 16384) return HYQ_ERR_INVALID;
+  const int st = ragged_prepare(caches, n_seq, n_splits, table, table_bytes, w, total);
+  if (st) return st;
+  if (total_splits) *total_splits = (int32_t)total;
+  return HYQ_OK;
+}
 
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return HYQ_ERR_HIP;
-  TableRing& ring = g_rings[dev];
-  std::lock_guard<std::mutex> lock(ring.mu);
-  if (!ring.host) {
-    void* h = nullptr;
-    if (hipHostMalloc(&h, TableRing::SLOTS * TableRing::SLOT_BYTES, hipHostMallocDefault) != hipSuccess)
-      return HYQ_ERR_HIP;
-    for (int i = 0; i < TableRing::SLOTS; ++i)
-      if (hipEventCreateWithFlags(&ring.ev[i], hipEventDisableTiming) != hipSuccess) return HYQ_ERR_HIP;
-    ring.host = (uint8_t*)h;
-  }
-  const int slot = ring.next;
-  ring.next = (slot + 1) % TableRing::SLOTS;
-  if (ring.pending[slot] && hipEventSynchronize(ring.ev[slot]) != hipSuccess) return HYQ_ERR_HIP;
-  ring.pending[slot] = false;
-  uint8_t* host = ring.host + (size_t)slot * TableRing::SLOT_BYTES;
-  hyq::RaggedSeq* seqs = (hyq::RaggedSeq*)(host + w.seqs);
-  uint32_t* map = (uint32_t*)(host + w.map);
-  long rec = 0, col = 0;
-  for (int i = 0; i < n_seq; ++i) {
-    const hyq_cache_t* c = caches[i];
-    hyq::RaggedSeq& d = seqs[i];
-    memset(&d, 0, sizeof d);
-    d.int4 = (const uint8_t*)c->int4;
-    d.a_k = (const uint16_t*)c->a_k;
-    d.a_v = (const uint16_t*)c->a_v;
-    d.s_k = (const uint16_t*)c->s_k;
-    d.s_v = (const uint16_t*)c->s_v;
-    d.w_k = (const uint16_t*)c->w_k;
-    d.w_v = (const uint16_t*)c->w_v;
-    d.int4_cap = c->shape.int4_cap;
-    d.anchor_cap = c->shape.anchor_cap;
-    d.staging_cap = c->shape.staging_cap;
-    d.n_int4 = c->n_int4;
-    d.n_anchor = c->n_anchor;
-    d.n_staged = c->n_staged;
-    d.n_win = c->len < W ? c->len : W;
-    d.n_splits = plan[i];
-    d.rec0 = (int)rec;
-    rec += (long)Hq * plan[i];
-    for (int j = 0; j < plan[i]; ++j) map[col++] = ((uint32_t)i << 16) | (uint32_t)j;
-  }
-  // descriptors and map are contiguous in the slot as in the workspace: one copy
-  const size_t bytes = w.map + (size_t)total * 4;
-  if (hipMemcpyAsync(ws, host, bytes, hipMemcpyHostToDevice, stream) != hipSuccess) return HYQ_ERR_HIP;
-  if (hipEventRecord(ring.ev[slot], stream) != hipSuccess) return HYQ_ERR_HIP;
-  ring.pending[slot] = true;
-
+int hyq_decode_attn_ragged(const hyq_cache_t* const* caches, int32_t n_seq, const void* q, float* o,
+                           int32_t n_splits, void* table, size_t table_bytes, void* ws, size_t ws_bytes,
+                           hipStream_t stream) {
+  if (!q || !o) return HYQ_ERR_INVALID;
+  RaggedWs w;
+  long total = 0;
+  int st = ragged_prepare(caches, n_seq, n_splits, table, table_bytes, w, total);
+  if (st) return st;
+  if (!ws || ws_bytes < w.total) return HYQ_ERR_WORKSPACE;
+  // descriptors and map are contiguous in the table as in the workspace: one copy
+  if (hipMemcpyAsync(ws, table, w.part, hipMemcpyHostToDevice, stream) != hipSuccess) return HYQ_ERR_HIP;
+  const hyq_shape_t& s0 = caches[0]->shape;
   hyq::RaggedDecodeParams p;
   p.seqs = (const hyq::RaggedSeq*)((uint8_t*)ws + w.seqs);
   p.split_map = (const uint32_t*)((uint8_t*)ws + w.map);
@@ -495,8 +494,8 @@ int hyq_decode_attn_ragged(const hyq_cache_t* const* caches, int32_t n_seq, cons
   p.part = (float*)((uint8_t*)ws + w.part);
   p.o = o;
   p.n_seq = n_seq;
-  p.Hkv = Hkv;
-  p.G = G;
+  p.Hkv = s0.n_kv_heads;
+  p.G = s0.n_q_heads / s0.n_kv_heads;
   p.total_splits = (int)total;
   p.bits = qbits(&s0);
   p.bits_v = qbits_v(&s0);

@@ -13,7 +13,8 @@
  * General rules for every entry point
  * -----------------------------------
  *  - Pointers marked "device" are HIP device pointers owned by the caller; the library
- *    never allocates, frees or synchronises, and keeps no mutable global state.
+ *    never allocates, frees or synchronises.  Its only global state is a per-device cache of
+ *    the compute-unit count (a device constant).
  *  - Work is enqueued asynchronously on the caller's stream; inputs must stay alive until
  *    the stream has passed the call.  Host structs are read/updated before returning.
  *  - All checks run on the host before anything is enqueued.  On any error nothing is
@@ -249,23 +250,40 @@ int hyq_decode_attn(const hyq_cache_t* cache, const void* q, float* o, int32_t n
    q: device bf16 [n_seq][Hq][128]; o: device f32 [n_seq][Hq][128].
    n_splits: splits per (sequence, KV head); 0 = automatic (the device's split columns are
    shared in proportion to each sequence's tile count, at least one each).
+   table: caller-owned HOST memory of at least hyq_decode_ragged_table_bytes(&caches[0]->shape,
+   n_seq, n_splits) bytes.  The call writes into it the caches' pointers and counters and the
+   split plan (about 112 bytes per sequence plus 4 per split, the layout of the head of the
+   workspace) and enqueues one host-to-device copy of it into `ws` on `stream`, then the two
+   kernels.  The caller keeps `table` unchanged until the stream has passed the call (a ring of
+   tables, or an event, is the caller's).  Page-locked memory (hipHostMalloc, a pinned torch
+   tensor) keeps the copy asynchronous and lets the call be recorded into a graph: a replay
+   copies whatever `table` holds at that moment, so after appends or refreshes change the
+   counters, rewrite it with hyq_decode_ragged_plan (same caches, same n_splits; the replay is
+   valid while the total split count it returns is the one recorded).
    ws: >= hyq_decode_ragged_workspace_bytes(&caches[0]->shape, n_seq, n_splits) bytes of
-   device scratch, no initialisation needed.  It receives a table of the caches' pointers
-   and counters and the split plan (about 112 bytes per sequence plus 4 per split), copied
-   from page-locked host memory owned by the library (one 4 MiB ring per device, allocated
-   on the first call) by one asynchronous host-to-device copy on `stream` before the
-   kernels; the call therefore cannot be recorded into a graph.  Calls sharing one workspace
-   must not overlap in time (same stream is fine).  Reads the caches only.
+   device scratch, no initialisation needed.  Calls sharing one workspace must not overlap in
+   time (same stream is fine).  Reads the caches only; allocates, frees and waits for nothing.
    Errors: INVALID (null or mismatched cache, batch != 1, len = 0, n_splits > 4096 or more
-   than 16384 splits in all), UNSUPPORTED, CAPACITY (n_seq > 1024), WORKSPACE, HIP. */
+   than 16384 splits in all), UNSUPPORTED, CAPACITY (n_seq > 1024), WORKSPACE (table or ws
+   missing or too small), HIP. */
 int hyq_decode_attn_ragged(const hyq_cache_t* const* caches, int32_t n_seq, const void* q, float* o,
-                           int32_t n_splits, void* ws, size_t ws_bytes, hipStream_t stream);
+                           int32_t n_splits, void* table, size_t table_bytes, void* ws, size_t ws_bytes,
+                           hipStream_t stream);
+
+/* Host only: writes the table hyq_decode_attn_ragged would write for these caches (same checks
+   and errors, no GPU work) and, if total_splits is not NULL, the number of split workgroup
+   columns the launch uses. */
+int hyq_decode_ragged_plan(const hyq_cache_t* const* caches, int32_t n_seq, int32_t n_splits, void* table,
+                           size_t table_bytes, int32_t* total_splits);
 
 /* Workspace bytes of hyq_decode_attn_ragged for n_seq sequences whose heads match `s`
    (s->batch is ignored): an upper bound over any lengths for the automatic plan
    (n_splits = 0), exact for a fixed n_splits.  0 for an invalid shape or n_seq outside
    1..1024. */
 size_t hyq_decode_ragged_workspace_bytes(const hyq_shape_t* s, int32_t n_seq, int32_t n_splits);
+
+/* Host table bytes of hyq_decode_attn_ragged (same bound rules as the workspace). */
+size_t hyq_decode_ragged_table_bytes(const hyq_shape_t* s, int32_t n_seq, int32_t n_splits);
 
 /* Hybrid prefill attention (HyQuant paper §4.2 Eq. 6-7, Alg. 2), causal, one sequence per
    call (shape->batch must be 1; Q head h reads KV head h / (Hq / Hkv)).

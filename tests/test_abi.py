@@ -179,14 +179,17 @@ def test_bit_width_field(lib):
 
 
 def test_ragged_decode_host_checks(lib):
-    """hyq_decode_attn_ragged: workspace closed form and every rejection before any device work."""
+    """hyq_decode_attn_ragged: workspace and table closed forms and every rejection before any
+    device work."""
     one = _shape(batch=1)
     r256 = lambda x: -(-x // 256) * 256
     n, S, Hq = 3, 5, one.n_q_heads
     assert lib.hyq_decode_ragged_workspace_bytes(C.byref(one), n, S) == r256(n * 112) + r256(n * S * 4) + \
         n * S * Hq * 130 * 4
+    assert lib.hyq_decode_ragged_table_bytes(C.byref(one), n, S) == r256(n * 112) + r256(n * S * 4)
     assert lib.hyq_decode_ragged_workspace_bytes(C.byref(one), 0, S) == 0
     assert lib.hyq_decode_ragged_workspace_bytes(C.byref(one), 1025, S) == 0
+    assert lib.hyq_decode_ragged_table_bytes(C.byref(one), 1025, S) == 0
     assert lib.hyq_decode_ragged_workspace_bytes(C.byref(one), n, 0) > 0  # automatic plan: a bound
     caches = [_fake_cache(), _fake_cache(len=300, n_int4=160, n_anchor=12), _fake_cache(len=128, n_int4=0,
                                                                                           n_anchor=0)]
@@ -194,27 +197,70 @@ def test_ragged_decode_host_checks(lib):
         c.shape = one
     arr = lambda cs: (C.POINTER(HyqCache) * len(cs))(*[C.pointer(c) for c in cs])
     big = 1 << 40
-    assert lib.hyq_decode_attn_ragged(None, 3, 0x10, 0x20, 0, 0x30, big, None) == 1
-    assert lib.hyq_decode_attn_ragged(arr(caches), 0, 0x10, 0x20, 0, 0x30, big, None) == 1
-    assert lib.hyq_decode_attn_ragged(arr(caches), 3, None, 0x20, 0, 0x30, big, None) == 1
-    assert lib.hyq_decode_attn_ragged(arr(caches), 3, 0x10, 0x20, -1, 0x30, big, None) == 1
-    assert lib.hyq_decode_attn_ragged(arr(caches * 342), 1026, 0x10, 0x20, 0, 0x30, big, None) == 3
+    tab = (C.c_uint8 * (1 << 20))()
+    tb = C.cast(tab, C.c_void_p)
+    T = len(tab)
+    assert lib.hyq_decode_attn_ragged(None, 3, 0x10, 0x20, 0, tb, T, 0x30, big, None) == 1
+    assert lib.hyq_decode_attn_ragged(arr(caches), 0, 0x10, 0x20, 0, tb, T, 0x30, big, None) == 1
+    assert lib.hyq_decode_attn_ragged(arr(caches), 3, None, 0x20, 0, tb, T, 0x30, big, None) == 1
+    assert lib.hyq_decode_attn_ragged(arr(caches), 3, 0x10, 0x20, -1, tb, T, 0x30, big, None) == 1
+    assert lib.hyq_decode_attn_ragged(arr(caches * 342), 1026, 0x10, 0x20, 0, tb, T, 0x30, big, None) == 3
     nulls = (C.POINTER(HyqCache) * 2)(C.pointer(caches[0]))
-    assert lib.hyq_decode_attn_ragged(nulls, 2, 0x10, 0x20, 0, 0x30, big, None) == 1
+    assert lib.hyq_decode_attn_ragged(nulls, 2, 0x10, 0x20, 0, tb, T, 0x30, big, None) == 1
     two = _fake_cache()  # batch 2: not a single-sequence cache
-    assert lib.hyq_decode_attn_ragged(arr([caches[0], two]), 2, 0x10, 0x20, 0, 0x30, big, None) == 1
+    assert lib.hyq_decode_attn_ragged(arr([caches[0], two]), 2, 0x10, 0x20, 0, tb, T, 0x30, big, None) == 1
     other = _fake_cache()
     other.shape = _shape(batch=1, n_q_heads=16)
-    assert lib.hyq_decode_attn_ragged(arr([caches[0], other]), 2, 0x10, 0x20, 0, 0x30, big, None) == 1
+    assert lib.hyq_decode_attn_ragged(arr([caches[0], other]), 2, 0x10, 0x20, 0, tb, T, 0x30, big, None) == 1
     wide = _fake_cache()
     wide.shape = _shape(batch=1, bits=8)
-    assert lib.hyq_decode_attn_ragged(arr([caches[0], wide]), 2, 0x10, 0x20, 0, 0x30, big, None) == 1
+    assert lib.hyq_decode_attn_ragged(arr([caches[0], wide]), 2, 0x10, 0x20, 0, tb, T, 0x30, big, None) == 1
     bad = _fake_cache(n_int4=5)
     bad.shape = one
-    assert lib.hyq_decode_attn_ragged(arr([caches[0], bad]), 2, 0x10, 0x20, 0, 0x30, big, None) == 1
+    assert lib.hyq_decode_attn_ragged(arr([caches[0], bad]), 2, 0x10, 0x20, 0, tb, T, 0x30, big, None) == 1
     need = lib.hyq_decode_ragged_workspace_bytes(C.byref(one), 3, S)
-    assert lib.hyq_decode_attn_ragged(arr(caches), 3, 0x10, 0x20, S, 0x30, need - 1, None) == 4
-    assert lib.hyq_decode_attn_ragged(arr(caches), 3, 0x10, 0x20, S, None, need, None) == 4
+    tneed = lib.hyq_decode_ragged_table_bytes(C.byref(one), 3, S)
+    assert lib.hyq_decode_attn_ragged(arr(caches), 3, 0x10, 0x20, S, tb, T, 0x30, need - 1, None) == 4
+    assert lib.hyq_decode_attn_ragged(arr(caches), 3, 0x10, 0x20, S, tb, T, None, need, None) == 4
+    assert lib.hyq_decode_attn_ragged(arr(caches), 3, 0x10, 0x20, S, tb, tneed - 1, 0x30, need, None) == 4
+    assert lib.hyq_decode_attn_ragged(arr(caches), 3, 0x10, 0x20, S, None, tneed, 0x30, need, None) == 4
     # more than 16384 splits in all
-    assert lib.hyq_decode_attn_ragged(arr(caches * 2), 6, 0x10, 0x20, 4096, 0x30, big, None) == 1
+    assert lib.hyq_decode_attn_ragged(arr(caches * 2), 6, 0x10, 0x20, 4096, tb, T, 0x30, big, None) == 1
+    assert [c.len for c in caches] == [1000, 300, 128]  # caches are read only
+
+
+def test_ragged_plan_writes_the_documented_table(lib):
+    """hyq_decode_ragged_plan (host only): one 112-byte descriptor per sequence (slab pointers,
+    capacities, counters, split count, first record), then the split map (sequence << 16 |
+    split), at a fixed split count and for the automatic plan (every sequence gets at least one
+    split, the total is the one reported)."""
+    import struct
+    one = _shape(batch=1)
+    caches = [_fake_cache(), _fake_cache(len=300, n_int4=160, n_anchor=12), _fake_cache(len=128, n_int4=0,
+                                                                                          n_anchor=0)]
+    for c in caches:
+        c.shape = one
+    arr = (C.POINTER(HyqCache) * 3)(*[C.pointer(c) for c in caches])
+    r256 = lambda x: -(-x // 256) * 256
+    for S in (5, 0):
+        nb = lib.hyq_decode_ragged_table_bytes(C.byref(one), 3, S)
+        tab = (C.c_uint8 * nb)()
+        total = C.c_int32(-1)
+        assert lib.hyq_decode_ragged_plan(arr, 3, S, C.cast(tab, C.c_void_p), nb, C.byref(total)) == 0
+        raw = bytes(tab)
+        splits, rec0 = [], 0
+        for i, c in enumerate(caches):
+            d = struct.unpack_from("<7Q13i", raw, 112 * i)
+            assert list(d[:7]) == [c.int4, c.a_k, c.a_v, c.s_k, c.s_v, c.w_k, c.w_v]
+            assert list(d[7:14]) == [one.int4_cap, one.anchor_cap, one.staging_cap, c.n_int4, c.n_anchor,
+                                     c.n_staged, min(c.len, 128)]
+            assert d[15] == rec0 and d[14] >= 1 and (S == 0 or d[14] == S)
+            splits.append(d[14])
+            rec0 += one.n_q_heads * d[14]
+        assert total.value == sum(splits)
+        m = struct.unpack_from(f"<{total.value}I", raw, r256(3 * 112))
+        assert list(m) == [(i << 16) | j for i in range(3) for j in range(splits[i])]
+        if S == 0:  # the longest sequence (most tiles) gets the most splits
+            assert splits[0] >= splits[1] >= splits[2]
+    assert lib.hyq_decode_ragged_plan(arr, 3, 5, None, 1 << 20, None) == 4
     assert [c.len for c in caches] == [1000, 300, 128]  # caches are read only

@@ -118,3 +118,42 @@ def test_ragged_deterministic_and_workspace_reuse():
     b = hq.decode_attn_ragged([p.cache for p in pairs], q, ws=ws)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+
+
+def test_ragged_graph_capture_and_replan():
+    """The call recorded into a HIP graph with a caller-owned page-locked table: every replay
+    (eager work and synchronisations in between) equals the eager call; after appends change
+    the counters, hyq_decode_ragged_plan rewrites the table and the replays follow them."""
+    pairs = [Pair(9500 + i, 1, 2, 4, L, n_steps=2) for i, L in enumerate([2000, 700, 129])]
+    qs = [p.append() for p in pairs]
+    q = torch.cat([dev(x) for x in qs], dim=0)
+    caches = [p.cache for p in pairs]
+    S = 3  # a fixed split count keeps the recorded grid valid when the counters change
+    shape = caches[0].shape
+    ws = torch.empty(hq.decode_ragged_workspace_bytes(shape, 3, S), dtype=torch.uint8, device="cuda")
+    table = hq.decode_ragged_table(shape, 3, S)
+    out = torch.empty((3, shape.n_q_heads, 128), dtype=torch.float32, device="cuda")
+    eager = hq.decode_attn_ragged(caches, q, S, ws=torch.empty_like(ws)).clone()
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        hq.decode_attn_ragged(caches, q, S, out=out, ws=ws, table=table)
+    torch.cuda.synchronize()
+    for r in range(3):
+        out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay {r}"
+        hq.decode_attn(caches[0], dev(qs[0]))  # eager work between replays
+        torch.cuda.synchronize()
+    qs2 = [p.append() for p in pairs]  # the counters move on
+    q.copy_(torch.cat([dev(x) for x in qs2], dim=0))
+    assert hq.decode_ragged_plan(caches, table, S) == 3 * S
+    g.replay()
+    torch.cuda.synchronize()
+    eager2 = hq.decode_attn_ragged(caches, q, S, ws=torch.empty_like(ws))
+    torch.cuda.synchronize()
+    assert torch.equal(out, eager2)
+    ragged_check(pairs, qs2, n_splits=S)
