@@ -11,6 +11,7 @@ HYQ_OK = 0
 STATUS = {0: "HYQ_OK", 1: "HYQ_ERR_INVALID", 2: "HYQ_ERR_UNSUPPORTED", 3: "HYQ_ERR_CAPACITY",
           4: "HYQ_ERR_WORKSPACE", 5: "HYQ_ERR_HIP"}
 HYQ_OP_DECODE, HYQ_OP_SELECT, HYQ_OP_PREFILL, HYQ_OP_SELECT_TAIL = 1, 2, 3, 4
+HYQ_NOALLOC_SCRATCH_BYTES = 8 << 20
 HYQ_NBUF = 10
 BUFFERS = ["int4", "slot_pos", "a_k", "a_v", "a_pos", "s_k", "s_v", "w_k", "w_v", "proxy_q"]
 
@@ -18,7 +19,7 @@ BUFFERS = ["int4", "slot_pos", "a_k", "a_v", "a_pos", "s_k", "s_v", "w_k", "w_v"
 EXPORTS = ["hyq_status_string", "hyq_cache_buffer_bytes", "hyq_workspace_bytes", "hyq_quantize_kv",
            "hyq_append_token", "hyq_select_vlines", "hyq_decode_attn", "hyq_prefill_attn",
            "hyq_prefill_attn_mx", "hyq_select_vlines_tail", "hyq_decode_attn_ragged",
-           "hyq_decode_ragged_workspace_bytes", "hyq_decode_ragged_table_bytes", "hyq_decode_ragged_plan"]
+           "hyq_decode_ragged_workspace_bytes", "hyq_decode_ragged_table_bytes", "hyq_decode_ragged_plan", "hyq_decode_attn_noalloc"]
 
 
 class HyqShape(C.Structure):
@@ -68,6 +69,8 @@ def load() -> C.CDLL:
                                       vp, vp, vp, sz, vp]
     lib.hyq_decode_attn.restype = C.c_int
     lib.hyq_decode_attn.argtypes = [C.POINTER(HyqCache), vp, vp, i32, vp, sz, vp]
+    lib.hyq_decode_attn_noalloc.restype = C.c_int
+    lib.hyq_decode_attn_noalloc.argtypes = [C.POINTER(HyqCache), vp, vp, i32, vp]
     lib.hyq_prefill_attn.restype = C.c_int
     lib.hyq_prefill_attn.argtypes = [C.POINTER(HyqShape), vp, vp, vp, i32, vp, i32, vp, vp, sz, vp]
     lib.hyq_select_vlines_tail.restype = C.c_int

@@ -208,6 +208,19 @@ def decode_attn(cache: HybridKVCache, q: torch.Tensor, n_splits: int = 0, out: t
     return out
 
 
+def decode_attn_noalloc(cache: HybridKVCache, q: torch.Tensor, out: torch.Tensor, n_splits: int = 0) -> torch.Tensor:
+    """hyq_decode_attn_noalloc: the decode with its split records in the library's static
+    per-GPU scratch (no allocation anywhere; ``out`` is the caller's fp32 [B][Hq][128])."""
+    s = cache.shape
+    _bf16(q, (s.batch, s.n_q_heads, D), "q")
+    if out.dtype != torch.float32 or tuple(out.shape) != (s.batch, s.n_q_heads, D) or not out.is_contiguous():
+        raise ValueError("out: contiguous float32 [B][Hq][128]")
+    lib = _lib.load()
+    check("hyq_decode_attn_noalloc", lib.hyq_decode_attn_noalloc(C.byref(cache.c), _ptr(q), _ptr(out), n_splits,
+                                                                 _stream()))
+    return out
+
+
 def decode_ragged_workspace_bytes(shape: Shape, n_seq: int, n_splits: int = 0) -> int:
     lib = _lib.load()
     s = shape.c()

@@ -416,8 +416,12 @@ int hyq_append_token(hyq_cache_t* c, const void* k_t, const void* v_t, const voi
   return HYQ_OK;
 }
 
-int hyq_decode_attn(const hyq_cache_t* c, const void* q, float* o, int32_t n_splits, void* ws, size_t ws_bytes,
-                    hipStream_t stream) {
+}  // extern "C"
+
+// hyq_decode_attn and hyq_decode_attn_noalloc: checks, split count, launch with `ws` (device
+// memory of ws_bytes, or the static scratch when `noalloc`) as the split records
+static int decode_common(const hyq_cache_t* c, const void* q, float* o, int32_t n_splits, void* ws, size_t ws_bytes,
+                         bool noalloc, hipStream_t stream) {
   if (!c) return HYQ_ERR_INVALID;
   int st = check_shape(&c->shape);
   if (st) return st;
@@ -426,6 +430,13 @@ int hyq_decode_attn(const hyq_cache_t* c, const void* q, float* o, int32_t n_spl
   if (!q || !o || c->len <= 0 || n_splits < 0 || n_splits > 4096) return HYQ_ERR_INVALID;
   const int S = n_splits > 0 ? n_splits : auto_splits(c);
   const size_t need = (size_t)c->shape.batch * c->shape.n_q_heads * S * (D + 2) * sizeof(float);
+  if (noalloc) {
+    if (need > HYQ_NOALLOC_SCRATCH_BYTES) return HYQ_ERR_WORKSPACE;
+    float* p = nullptr;
+    if (hyq::noalloc_scratch(&p) != hipSuccess) return HYQ_ERR_HIP;
+    ws = p;
+    ws_bytes = HYQ_NOALLOC_SCRATCH_BYTES;
+  }
   if (!ws || ws_bytes < need) return HYQ_ERR_WORKSPACE;
   hyq::DecodeParams p;
   p.int4 = (const uint8_t*)c->int4;
@@ -453,6 +464,17 @@ int hyq_decode_attn(const hyq_cache_t* c, const void* q, float* o, int32_t n_spl
   p.n_splits = S;
   hipError_t e = hyq::launch_decode(p, stream);
   return e == hipSuccess ? HYQ_OK : HYQ_ERR_HIP;
+}
+
+extern "C" {
+
+int hyq_decode_attn(const hyq_cache_t* c, const void* q, float* o, int32_t n_splits, void* ws, size_t ws_bytes,
+                    hipStream_t stream) {
+  return decode_common(c, q, o, n_splits, ws, ws_bytes, false, stream);
+}
+
+int hyq_decode_attn_noalloc(const hyq_cache_t* c, const void* q, float* o, int32_t n_splits, hipStream_t stream) {
+  return decode_common(c, q, o, n_splits, nullptr, 0, true, stream);
 }
 
 size_t hyq_decode_ragged_workspace_bytes(const hyq_shape_t* s, int32_t n_seq, int32_t n_splits) {

@@ -30,6 +30,8 @@
 //    of a head takes tiles w, w + NW, ... so the head's workers sweep its records together.
 //  * 4 waves per workgroup merge their states in LDS and write one record per split; a second
 //    small launch merges the records.
+#include <mutex>
+
 #include "hyq_common.h"
 #include "hyq_launch.h"
 
@@ -631,6 +633,35 @@ __global__ __launch_bounds__(64) void decode_reduce_kernel(const float* __restri
 }
 
 }  // namespace
+
+// Split records of the decode entry point that allocates nothing (for callers that cannot
+// allocate: code under graph capture, serving loops that forbid allocation): one array per
+// device, held until the process ends.  Host code never uses this name as an address: the
+// device address is looked up once per device with hipGetSymbolAddress and kept below.
+static __device__ __align__(256) float scratch[HYQ_NOALLOC_SCRATCH_BYTES / sizeof(float)];
+
+namespace {
+constexpr int SCRATCH_MAX_DEVICES = 64;
+std::once_flag g_scratch_once[SCRATCH_MAX_DEVICES];
+float* g_scratch_ptr[SCRATCH_MAX_DEVICES];
+hipError_t g_scratch_err[SCRATCH_MAX_DEVICES];
+}  // namespace
+
+hipError_t noalloc_scratch(float** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= SCRATCH_MAX_DEVICES) return hipErrorInvalidDevice;
+  std::call_once(g_scratch_once[dev], [dev]() {  // runs with `dev` current
+    void* p = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = g_scratch_err[dev] == hipSuccess ? (float*)p : nullptr;
+  });
+  if (g_scratch_err[dev] != hipSuccess) return g_scratch_err[dev];
+  if (!g_scratch_ptr[dev]) return hipErrorInvalidSymbol;
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
   const int nsub = (p.G + 3) >> 2;

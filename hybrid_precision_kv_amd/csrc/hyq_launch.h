@@ -31,6 +31,9 @@ struct DecodeParams {
   int bits, bits_v;  // B_K and B_V of the quantized store: (4, 4), (8, 8), (4, 2) or (2, 2)
 };
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream);
+// Device address of the current device's static decode scratch (HYQ_NOALLOC_SCRATCH_BYTES),
+// looked up once per device.
+hipError_t noalloc_scratch(float** ptr);
 
 // One sequence of a variable-length batch: its own single-sequence cache (buffers at that
 // cache's b = 0) with its own counters and split count.  Built on the host, copied into the

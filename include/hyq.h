@@ -13,8 +13,9 @@
  * General rules for every entry point
  * -----------------------------------
  *  - Pointers marked "device" are HIP device pointers owned by the caller; the library
- *    never allocates, frees or synchronises.  Its only global state is a per-device cache of
- *    the compute-unit count (a device constant).
+ *    never allocates, frees or synchronises.  Its only global state is per device: a cache
+ *    of the compute-unit count (a device constant) and, for hyq_decode_attn_noalloc alone,
+ *    the static scratch array and its looked-up address.
  *  - Work is enqueued asynchronously on the caller's stream; inputs must stay alive until
  *    the stream has passed the call.  Host structs are read/updated before returning.
  *  - All checks run on the host before anything is enqueued.  On any error nothing is
@@ -239,6 +240,19 @@ int hyq_select_vlines_tail(const hyq_shape_t* shape, const void* k, int32_t len,
    then their merge).  Reads the cache only.  Errors: INVALID, UNSUPPORTED, WORKSPACE, HIP. */
 int hyq_decode_attn(const hyq_cache_t* cache, const void* q, float* o, int32_t n_splits,
                     void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* For callers that cannot allocate (code under graph capture, serving loops or harnesses
+   that forbid allocation): hyq_decode_attn with its split records in a static device array of
+   HYQ_NOALLOC_SCRATCH_BYTES per GPU (allocated with the library's code object, held until the
+   process ends) instead of a caller workspace.  Same arguments, kernels, results and errors as
+   hyq_decode_attn, plus WORKSPACE when batch * n_q_heads * splits * 130 * 4 bytes exceed the
+   scratch (splits = n_splits, or the automatic count).  Calls no allocating routine.  Every
+   call on one GPU uses that GPU's one array: calls that overlap in time on one GPU (two
+   streams, two threads) race; calls on one stream are ordered and safe.  No initialisation
+   is needed (every record is written before it is read). */
+#define HYQ_NOALLOC_SCRATCH_BYTES (8u << 20)
+int hyq_decode_attn_noalloc(const hyq_cache_t* cache, const void* q, float* o, int32_t n_splits,
+                            hipStream_t stream);
 
 /* Decode attention over a variable-length batch (the HyQuant paper's Alg. 3 for each
    sequence; the paper's batched decode runs sequences of one length).  Each sequence is its

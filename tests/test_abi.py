@@ -264,3 +264,22 @@ def test_ragged_plan_writes_the_documented_table(lib):
             assert splits[0] >= splits[1] >= splits[2]
     assert lib.hyq_decode_ragged_plan(arr, 3, 5, None, 1 << 20, None) == 4
     assert [c.len for c in caches] == [1000, 300, 128]  # caches are read only
+
+
+def test_noalloc_decode_host_checks(lib):
+    """hyq_decode_attn_noalloc rejects a call whose split records exceed the static scratch
+    (batch * Hq * splits * 130 * 4 > HYQ_NOALLOC_SCRATCH_BYTES) before any device work, and
+    validates like hyq_decode_attn."""
+    c = _fake_cache()
+    before = bytes(c)
+    per_split = c.shape.batch * c.shape.n_q_heads * 130 * 4
+    too_many = _lib.HYQ_NOALLOC_SCRATCH_BYTES // per_split + 1
+    assert too_many <= 4096
+    assert lib.hyq_decode_attn_noalloc(C.byref(c), 0x10, 0x20, too_many, None) == 4
+    assert lib.hyq_decode_attn_noalloc(None, 0x10, 0x20, 0, None) == 1
+    assert lib.hyq_decode_attn_noalloc(C.byref(c), None, 0x20, 0, None) == 1
+    assert lib.hyq_decode_attn_noalloc(C.byref(c), 0x10, 0x20, -1, None) == 1
+    assert lib.hyq_decode_attn_noalloc(C.byref(c), 0x10, 0x20, 4097, None) == 1
+    bad = _fake_cache(n_int4=5)
+    assert lib.hyq_decode_attn_noalloc(C.byref(bad), 0x10, 0x20, 0, None) == 1
+    assert bytes(c) == before
