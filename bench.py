@@ -29,7 +29,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "hybrid decode-attn µs/step + achieved HBM GB/s, 32K ctx, bs1/bs16"
 HBM_PEAK_GBS = 8000.0
-EXP_PEAK_T = 256 * 4 * 16 / 4 * 2.4e9 / 1e12  # exp2 per second (T): quarter-rate transcendental
+MFMA_BF16_PEAK_T = 2500.0  # dense f16/bf16 MFMA, TFLOP/s
 D, W = 128, 128
 
 
@@ -46,6 +46,8 @@ def parse():
     ap.add_argument("--splits", type=int, default=0, help="splits per (b, KV head); 0 = library default")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-heads", type=int, default=32)
+    ap.add_argument("--no-cpu-rows", action="store_true",
+                    help="time the oracle on the decode sample only (not the selector, refresh and prefill rows)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 1 GiB device copy (PMC byte-counter calibration)")
     ap.add_argument("--seed", type=int, default=3000)
@@ -223,10 +225,27 @@ def bench_maintenance(torch, hq, cache, B, Hkv, G, L, gen, dev, ws, out, splits)
     ev[1].record()
     torch.cuda.synchronize()
     t_ref = ev[0].elapsed_time(ev[1]) * 1e3
-    return {"append_us": round(t_app / 64, 2), "decode_us_with_staging": round(t_dec / 64, 2),
+    # device time of the per-token work from captured graphs (the staging emptied by the
+    # refresh above takes the 51 appends the warm-ups and captures make; a replay repeats the
+    # recorded appends into the same slots)
+    k_t, v_t, q_t = toks[0]
+
+    def app16():  # 16 appends per graph: one replay of a single tiny kernel measures the host
+        for _ in range(16):
+            hq.append_token(cache, k_t, v_t, q_t)
+    us_app_g = timed_graph(torch, app16, 10)[0] / 16
+
+    def step():
+        hq.append_token(cache, k_t, v_t, q_t)
+        return hq.decode_attn(cache, q_t, splits, out, ws)
+    us_step_g, _ = timed_graph(torch, step, 20)
+    return {"append_us": round(us_app_g, 2), "append_us_eager": round(t_app / 64, 2),
+            "append_decode_us_graph": round(us_step_g, 2), "decode_us_with_staging": round(t_dec / 64, 2),
             "select_refresh_us": round(t_ref, 1), "anchors_after_refresh": k,
-            "us_per_token_amortized": round((t_app + t_dec + t_ref) / 64, 2),
-            "note": f"one layer, bs{B} ctx {L}+64, refresh every 64 tokens"}
+            "us_per_token_amortized": round(us_step_g + t_ref / 64, 2),
+            "note": f"one layer, bs{B} ctx {L}+64, refresh every 64 tokens; append_us (a graph of 16 appends, per "
+                    "append) and append_decode_us_graph are device time from captured graphs, select_refresh_us one "
+                    "eager call; us_per_token_amortized = append_decode_us_graph + select_refresh_us / 64"}
 
 
 def bench_decode_bs1(torch, hq, gen, dev, ctxs=(1024, 4096, 16384, 32768), Hq=32, Hkv=8, layers=36, steps=100,
@@ -433,15 +452,17 @@ def bench_selector(torch, hq, gen, dev, B=4, Hq=64, Hkv=8, L=32768):
         us, got = timed_graph(torch, lambda: hq.select_vlines(shape, k, cache=cache), 10)
         res[f"select_{pct}pct_us"] = round(us, 1)
         res[f"select_{pct}pct_graph_equal"] = bool(torch.equal(got, ref))
-    # ALU roofline: the irreducible work is one exp2 per (proxy row, key) pair in each of the
-    # two passes (row normalisers, then Eq. 4 column sums); the peak is the transcendental
-    # rate with packed fp32 off: 256 CUs x 4 SIMDs x 16 lanes / 4 cycles x 2.4 GHz
-    pairs = B * Hkv * (64 * G) * (L - W)
-    exps = 2 * pairs
+    # MFMA roofline: the algorithmic work of one selection is one alpha Q K^T over every proxy
+    # row and key (2 R L D flops per (b, KV head), R = 64 G rows) at the dense f16/bf16 MFMA
+    # peak; the two-pass softmax computes that product twice and takes two exponentials per
+    # (row, key) pair, which the achieved figure does not credit
+    R = 64 * G
+    flops = 2.0 * B * Hkv * R * L * D
     us5 = res["select_5pct_us"]
-    res["roofline"] = {"bound": "alu", "achieved": round(exps / (us5 * 1e-6) / 1e12, 3), "peak": EXP_PEAK_T,
-                       "unit": "Texp/s", "frac": round(exps / (us5 * 1e-6) / 1e12 / EXP_PEAK_T, 4), "traffic": None,
-                       "exps_per_call": exps, "basis": "5% call; two exp2 per (proxy row, key) pair"}
+    res["roofline"] = {"bound": "mfma", "achieved": round(flops / (us5 * 1e-6) / 1e12, 1), "peak": MFMA_BF16_PEAK_T,
+                       "unit": "TFLOP/s", "frac": round(flops / (us5 * 1e-6) / 1e12 / MFMA_BF16_PEAK_T, 4),
+                       "traffic": None, "flops_per_call": flops, "exps_per_call": 2 * B * Hkv * R * (L - W),
+                       "basis": "5% call; one Q.K^T of every proxy row against every key, f16/bf16 dense peak"}
     k_t = torch.randn(B, Hkv, D, generator=gen, device=dev).to(torch.bfloat16)
     q_t = torch.randn(B, Hq, D, generator=gen, device=dev).to(torch.bfloat16)
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
@@ -623,7 +644,15 @@ def cpu_baseline(args, G, bytes_per_head):
     gbs, passes, dt = run(10.0)
     res = {"value": round(gbs, 3), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
            "sample": f"{passes} passes over {len(heads)} (sequence, KV head) caches of {args.ctx} positions, "
-                     f"GQA {G}, one decode step each ({dt:.1f} s; a full step is {args.batch * args.hkv} such heads)"}
+                     f"GQA {G}, one decode step each ({dt:.1f} s; a full step is {args.batch * args.hkv} such heads)",
+           "cpu_model": cpu_model(), "host_cpus": len(os.sched_getaffinity(0))}
+    per_head_s = dt / (passes * len(heads))
+    res["decode_us_per_step"] = {
+        f"bs{args.batch}_{args.ctx}": round(per_head_s * args.batch * args.hkv * 1e6, 1),
+        f"bs1_{args.ctx}": round(per_head_s * args.hkv * 1e6, 1),
+        "note": "oracle decode time per (sequence, KV head) from the sample above, times the heads of one step"}
+    if not args.no_cpu_rows:
+        res["rows"] = cpu_rows(args)
     try:  # the same oracle on one thread
         from threadpoolctl import threadpool_limits
         with threadpool_limits(limits=1):
@@ -634,6 +663,69 @@ def cpu_baseline(args, G, bytes_per_head):
         res["value_1thread"] = None
         res["sample_1thread"] = f"not measured ({type(e).__name__})"
     return res
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_rows(args):
+    """The oracle on bounded samples of the other hot-path rows, extrapolated to one call:
+    cache-mode selection and refresh at 64 Q / 8 KV heads, 32K (two (sequence, KV head) caches,
+    64 appends each), and the hybrid prefill at 8192 tokens, 32 Q / 8 KV heads (operand
+    quantization in full, then six seeded random (64-query block, Q head) pairs)."""
+    import numpy as np
+    from hybrid_precision_kv_amd import synth
+    from oracle import attention as att
+    from oracle import policy as pol
+    out = {}
+    L, G, n_heads_call = 32768, 8, 4 * 8
+    t_sel, t_ref, n = 0.0, 0.0, 2
+    for i in range(n):
+        s = synth.HeadStream(synth.seed_for(args.seed + 7, i, 0), L, G)
+        prox = s.queries(64)
+        A, _ = pol.select_dense(s.K, prox)
+        c = pol.HybridCacheRef(g=G)
+        c.freeze(s.K, s.V, A, prox)
+        k, v, q = s.new_tokens(64)
+        for j in range(64):
+            c.append(k[j], v[j], q[:, j])
+        t0 = time.perf_counter()
+        A2, _ = c.select()
+        t1 = time.perf_counter()
+        c.refresh(A2)
+        t2 = time.perf_counter()
+        t_sel += t1 - t0
+        t_ref += t2 - t1
+    out["selector_5pct"] = {"us_per_call": round(t_sel / n * n_heads_call * 1e6, 1),
+                            "sample": f"{n} of the {n_heads_call} (sequence, KV head) caches of bs4 x {L}, "
+                                      f"64 Q / 8 KV heads, cache mode after 64 appends ({t_sel:.1f} s)"}
+    out["refresh"] = {"us_per_call": round(t_ref / n * n_heads_call * 1e6, 1),
+                      "sample": f"the same {n} caches, the new set applied ({t_ref:.2f} s)"}
+    N, Hq, Hkv = 8192, 32, 8
+    d = synth.gen_prefill(args.seed + 8, Hq, Hkv, N)
+    anchors = [pol.select_dense(d["K"][h], d["Q"][h * 4:(h + 1) * 4, N - 64:])[0] for h in range(Hkv)]
+    t0 = time.perf_counter()
+    qz = att.prefill_quantize(d["Q"], d["K"], d["V"], anchors)
+    t_q = time.perf_counter() - t0
+    rng = np.random.default_rng(args.seed)
+    nb, ns = N // 64, 6
+    picks = [(int(rng.integers(nb)), int(rng.integers(Hq))) for _ in range(ns)]
+    t0 = time.perf_counter()
+    for b, h in picks:
+        att.prefill_ref(d["Q"], d["K"], d["V"], anchors, blocks=[b], heads=[h], qz=qz)
+    t_b = (time.perf_counter() - t0) / ns
+    out[f"prefill_{N}"] = {"us_per_call": round((t_q + t_b * nb * Hq) * 1e6, 1),
+                           "sample": f"operand quantization in full ({t_q:.1f} s), then {ns} random (64-query block, "
+                                     f"Q head) pairs of {nb * Hq} ({t_b:.2f} s each), extrapolated"}
+    return out
 
 
 def main():
@@ -757,6 +849,7 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5),
         "us_per_step": round(ms_per_step * 1e3, 2),
+        "tokens_per_s_attention_only": round(B / (nl * ms_per_step * 1e-3), 1),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -773,6 +866,8 @@ def main():
                      "read_probe_GBs": round(read_probe, 1),
                      "read_probe": "torch row sums over 4 GiB resident fp32 (context for the peak, not the peak)"},
         "wall_s_timed": round(wall, 3),
+        "tokens_note": f"tokens_per_s_attention_only = batch / ({nl} layers x one layer's decode-attention step): "
+                       "the attention share of a decode step, not an end-to-end model rate",
     }
     c0 = layers[0][0]
     cpu_bytes_per_head = 160 * c0.n_int4 + 512 * (c0.n_anchor + min(L, W)) + G * D * 6
