@@ -183,6 +183,7 @@ class _Workspace:
 
 
 _ws = _Workspace()
+_ws_ragged = _Workspace()
 
 
 def decode_workspace(shape: Shape, n_splits: int = 0, device="cuda") -> torch.Tensor:
@@ -302,7 +303,7 @@ def decode_attn_ragged(caches: list, q: torch.Tensor, n_splits: int = 0, out: to
     if need == 0:
         raise ValueError("unsupported ragged batch (sequence count or split count out of range)")
     if ws is None:
-        ws = _ws.get(need, q.device)
+        ws = _ws_ragged.get(need, q.device)
     slot = None
     if table is None:
         slot, table = _tables.get(decode_ragged_table_bytes(s, n, n_splits))

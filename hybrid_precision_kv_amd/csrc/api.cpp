@@ -171,7 +171,7 @@ int cu_count() {
 // never fewer than 16 splits (measured at batch 1 with the one-latency merge: 16 and 32 splits
 // tie at 1K tokens, 32 is best at 4K, 16K and 32K, 48 and 64 are slower everywhere; at batch
 // 16 x 32K, 4 splits = two workgroups per CU).
-int auto_splits(const hyq_cache_t* c) {
+int auto_splits(const hyq_cache_t* c, int* waves) {
   const int G = c->shape.n_q_heads / c->shape.n_kv_heads;
   const long units = (long)nheads(&c->shape) * ((G + 3) / 4);
   const long tiles = (c->n_int4 + 31) / 32 + 3 * ((c->n_anchor + 31) / 32 + (c->n_staged + 31) / 32 + 4);
@@ -180,11 +180,15 @@ int auto_splits(const hyq_cache_t* c) {
   // 100.7 us); K4V2, K4V4 and K8V8 measure best at two
   const long per_cu = qbits(&c->shape) + qbits_v(&c->shape) == 4 ? 3 : 2;
   long s = (per_cu * cus + units - 1) / units;
+  *waves = 4;
   if (tiles < 16 * 4 * s) {
     s = (cus + units - 1) / units;
     long by_work = (tiles + 3) / 4;
     if (by_work < 16) by_work = 16;
     if (s > by_work) s = by_work;
+    // eight waves per workgroup when every wave still gets a tile (more loads in flight, a
+    // shorter chain per wave); with fewer tiles the extra waves idle
+    if (tiles >= 8 * s) *waves = 8;
   }
   if (s < 1) s = 1;
   if (s > 256) s = 256;
@@ -428,7 +432,8 @@ static int decode_common(const hyq_cache_t* c, const void* q, float* o, int32_t 
   if ((st = check_cache_ptrs(c))) return st;
   if ((st = check_counters(c))) return st;
   if (!q || !o || c->len <= 0 || n_splits < 0 || n_splits > 4096) return HYQ_ERR_INVALID;
-  const int S = n_splits > 0 ? n_splits : auto_splits(c);
+  int waves = 4;
+  const int S = n_splits > 0 ? n_splits : auto_splits(c, &waves);
   const size_t need = (size_t)c->shape.batch * c->shape.n_q_heads * S * (D + 2) * sizeof(float);
   if (noalloc) {
     if (need > HYQ_NOALLOC_SCRATCH_BYTES) return HYQ_ERR_WORKSPACE;
@@ -462,6 +467,7 @@ static int decode_common(const hyq_cache_t* c, const void* q, float* o, int32_t 
   p.n_staged = c->n_staged;
   p.n_win = c->len < W ? c->len : W;
   p.n_splits = S;
+  p.waves = waves;
   hipError_t e = hyq::launch_decode(p, stream);
   return e == hipSuccess ? HYQ_OK : HYQ_ERR_HIP;
 }

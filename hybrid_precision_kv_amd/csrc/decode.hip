@@ -39,7 +39,6 @@ namespace hyq {
 
 namespace {
 
-constexpr int WAVES = 4;
 constexpr float LOG2E = 1.4426950408889634f;
 // V weight scale 2^e of an MFMA column: the column's largest s_V times 2^e is kept inside
 // [PS_LO, PS_HI); a move puts it in [2^PS_TARGET - 1, 2^PS_TARGET).  The start value 2^8 keeps
@@ -328,8 +327,12 @@ __device__ inline HeadWork head_work(const RaggedDecodeParams& p, int hkv) {
   return h;
 }
 
-template <int BK, int BV, class Params>
-__global__ __launch_bounds__(256) void decode_split_kernel(Params p) {
+// NWAVES waves per workgroup: 4 when the launch is bandwidth bound (two workgroups per CU), 8
+// when it is latency bound (one workgroup per CU: twice the tile loads in flight per CU and
+// half the dependent chain per wave)
+template <int BK, int BV, class Params, int NWAVES>
+__global__ __launch_bounds__(64 * NWAVES) void decode_split_kernel(Params p) {
+  constexpr int WAVES = NWAVES;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n = lane & 15, q4 = lane >> 4;
   const int hh = n >> 2, g = n & 3;
@@ -341,7 +344,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(Params p) {
 
   // ---- q of the (up to 4) Q heads of this head block, staged once through LDS
   __shared__ uint32_t q_lds[4][D / 2];
-  {
+  if (threadIdx.x < 256) {
     const int h2 = threadIdx.x >> 6, cp = threadIdx.x & 63;  // 256 threads x 2 channels
     const int hd = sub * 4 + h2;
     uint32_t v = 0;
@@ -416,19 +419,23 @@ __global__ __launch_bounds__(256) void decode_split_kernel(Params p) {
   const uint8_t* slab = hw.int4;
   const uint32_t smoff = (uint32_t)(g * 64 + q4 * 16);
   const int full = hw.n_int4 >> 5;  // tiles below this index hold 32 valid slots
+  auto tile = [&](const QTile<BK, BV>& x, int t) {
+    if (t < full) int4_tile<BK, BV, false>(st, x, bq4, qsum24, c_int4, t * 32, hw.n_int4, q4);
+    else int4_tile<BK, BV, true>(st, x, bq4, qsum24, c_int4, t * 32, hw.n_int4, q4);
+  };
+  // two tiles in flight: the next tile's loads are issued before the current one is computed;
+  // a prefetch past the wave's last tile re-reads the current one (in bounds, never used)
   if (w < T4) {
     QTile<BK, BV> ta, tb;
     int t = w;
     load_int4_tile(ta, slab, t, (uint32_t)lane, smoff);
     for (;;) {
       load_int4_tile(tb, slab, t + NW < T4 ? t + NW : t, (uint32_t)lane, smoff);
-      if (t < full) int4_tile<BK, BV, false>(st, ta, bq4, qsum24, c_int4, t * 32, hw.n_int4, q4);
-      else int4_tile<BK, BV, true>(st, ta, bq4, qsum24, c_int4, t * 32, hw.n_int4, q4);
+      tile(ta, t);
       t += NW;
       if (t >= T4) break;
       load_int4_tile(ta, slab, t + NW < T4 ? t + NW : t, (uint32_t)lane, smoff);
-      if (t < full) int4_tile<BK, BV, false>(st, tb, bq4, qsum24, c_int4, t * 32, hw.n_int4, q4);
-      else int4_tile<BK, BV, true>(st, tb, bq4, qsum24, c_int4, t * 32, hw.n_int4, q4);
+      tile(tb, t);
       t += NW;
       if (t >= T4) break;
     }
@@ -509,7 +516,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(Params p) {
     }
   }
   __syncthreads();
-  for (int idx = threadIdx.x; idx < 4 * D; idx += 256) {
+  for (int idx = threadIdx.x; idx < 4 * D; idx += 64 * WAVES) {
     const int h2 = idx / D, c = idx % D;
     const int hd = sub * 4 + h2;
     if (hd >= p.G) continue;
@@ -667,8 +674,11 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
   const int nsub = (p.G + 3) >> 2;
   dim3 grid(p.n_splits, p.Hkv * nsub, p.B);
   hipError_t e = with_widths(p.bits, p.bits_v, [&](auto BK, auto BV) {
-    hipLaunchKernelGGL((decode_split_kernel<decltype(BK)::value, decltype(BV)::value, DecodeParams>), grid, dim3(256),
-                       0, stream, p);
+    constexpr int bk = decltype(BK)::value, bv = decltype(BV)::value;
+    if (p.waves == 8)
+      hipLaunchKernelGGL((decode_split_kernel<bk, bv, DecodeParams, 8>), grid, dim3(512), 0, stream, p);
+    else
+      hipLaunchKernelGGL((decode_split_kernel<bk, bv, DecodeParams, 4>), grid, dim3(256), 0, stream, p);
     return hipGetLastError();
   });
   if (e != hipSuccess) return e;
@@ -681,7 +691,7 @@ hipError_t launch_decode_ragged(const RaggedDecodeParams& p, hipStream_t stream)
   const int nsub = (p.G + 3) >> 2;
   dim3 grid(p.total_splits, p.Hkv * nsub, 1);
   hipError_t e = with_widths(p.bits, p.bits_v, [&](auto BK, auto BV) {
-    hipLaunchKernelGGL((decode_split_kernel<decltype(BK)::value, decltype(BV)::value, RaggedDecodeParams>), grid,
+    hipLaunchKernelGGL((decode_split_kernel<decltype(BK)::value, decltype(BV)::value, RaggedDecodeParams, 4>), grid,
                        dim3(256), 0, stream, p);
     return hipGetLastError();
   });

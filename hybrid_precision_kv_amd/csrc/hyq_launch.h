@@ -29,6 +29,7 @@ struct DecodeParams {
   int n_int4, n_anchor, n_staged, n_win;
   int n_splits;
   int bits, bits_v;  // B_K and B_V of the quantized store: (4, 4), (8, 8), (4, 2) or (2, 2)
+  int waves;         // waves per split workgroup: 4, or 8 for latency-bound launches
 };
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream);
 // Device address of the current device's static decode scratch (HYQ_NOALLOC_SCRATCH_BYTES),

@@ -90,7 +90,7 @@ extern "C" {
 #define HYQ_OK 0
 #define HYQ_ERR_INVALID 1      /* null pointer, bad dimension, inconsistent counters */
 #define HYQ_ERR_UNSUPPORTED 2  /* head_dim != 128, group != 32, window != 128, GQA not in {1,2,4,8,16},
-                                  bits not in {0, 4, 8} */
+                                  an unsupported (bits, bits_v) pair */
 #define HYQ_ERR_CAPACITY 3     /* len > capacity, k > anchor_cap or > candidates, staging full */
 #define HYQ_ERR_WORKSPACE 4    /* workspace missing or smaller than hyq_workspace_bytes */
 #define HYQ_ERR_HIP 5          /* a kernel launch failed (hipGetLastError) */
