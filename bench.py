@@ -62,6 +62,8 @@ def parse():
                     help="run only the bulk bit-width row (K4V4 against K8V8 decode)")
     ap.add_argument("--only-ragged", action="store_true",
                     help="run only the variable-length batch row")
+    ap.add_argument("--only-gqa8", action="store_true",
+                    help="run only the GQA-8 decode row (64 Q / 8 KV heads, bs4 x 32K)")
     ap.add_argument("--only-prefill", action="store_true",
                     help="run only the hybrid-prefill rows (for profiling the prefill kernels)")
     return ap.parse_args()
@@ -351,6 +353,43 @@ def bench_decode_bits(torch, hq, gen, dev, B=16, L=32768, Hq=32, Hkv=8, layers=8
     out["note"] = (f"bs{B} ctx{L} hq{Hq} hkv{Hkv}, {layers} resident layers, hybrid 5% anchors + bf16 window; "
                    f"error over sequences 0..{n_ref - 1} of the first layer")
     return out
+
+
+def bench_decode_gqa8(torch, hq, gen, dev, B=4, L=32768, Hq=64, Hkv=8, layers=16, steps=100, copy_cal=False):
+    """Decode at GQA 8 (the Qwen3-32B shape of the selector workload: 64 Q / 8 KV heads, batch 4,
+    32K, 5% anchors): hyq_decode_attn per step rotating over ``layers`` resident caches.  Each
+    KV head's Q heads are served by two 4-head blocks that read its slab together; the
+    algorithmic bytes count the slab once."""
+    G = Hq // Hkv
+    shape = hq.Shape.for_context(B, Hq, Hkv, L + 64)
+    lay = [make_layer(torch, hq, shape, B, Hkv, G, L, gen, dev) for _ in range(layers)]
+    torch.cuda.synchronize()
+    nbytes = algorithmic_bytes(lay[0][0], B, Hkv, Hq)
+    ws = hq.decode_workspace(shape, 0, dev)
+    o = torch.empty(B, Hq, D, dtype=torch.float32, device=dev)
+    for i in range(20):
+        hq.decode_attn(lay[i % layers][0], lay[i % layers][1], 0, o, ws)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        hq.decode_attn(lay[i % layers][0], lay[i % layers][1], 0, o, ws)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / steps
+    if copy_cal:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        b2 = torch.empty_like(a)
+        for _ in range(5):
+            b2.copy_(a)
+        torch.cuda.synchronize()
+        del a, b2
+    del lay
+    torch.cuda.empty_cache()
+    return {"workload": f"qwen3-32b-shape decode bs{B} ctx{L} hq{Hq} hkv{Hkv} layers{layers}",
+            "us_per_step": round(us, 2), "GB_per_s": round(nbytes / (us * 1e-6) / 1e9, 1),
+            "hbm_frac": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4), "bytes_per_step": nbytes,
+            "note": "two 4-head blocks per KV head, dispatched back to back on one XCD; bytes count the slab once"}
 
 
 def ragged_lengths(n_seq, seed, lo=2048, hi=32768):
@@ -762,6 +801,12 @@ def main():
         gen.manual_seed(args.seed)
         print(json.dumps({"rows": {"decode_ragged": bench_decode_ragged(torch, hq, gen, dev)}}), flush=True)
         return
+    if args.only_gqa8:
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(args.seed)
+        print(json.dumps({"rows": {"decode_gqa8": bench_decode_gqa8(torch, hq, gen, dev,
+                                                                     copy_cal=args.copy_calibration)}}), flush=True)
+        return
     if args.only_prefill:
         gen = torch.Generator(device=dev)
         gen.manual_seed(args.seed)
@@ -892,6 +937,8 @@ def main():
         print(f"[bench] all-bf16 sweep done", file=sys.stderr, flush=True)
         rows["decode_bit_width"] = bench_decode_bits(torch, hq, gen, dev, B=B, L=L, Hq=Hq, Hkv=Hkv)
         print(f"[bench] bit widths: {rows['decode_bit_width']}", file=sys.stderr, flush=True)
+        rows["decode_gqa8"] = bench_decode_gqa8(torch, hq, gen, dev)
+        print(f"[bench] gqa8: {rows['decode_gqa8']}", file=sys.stderr, flush=True)
         rows["decode_ragged"] = bench_decode_ragged(torch, hq, gen, dev, Hq=Hq, Hkv=Hkv)
         print(f"[bench] ragged batch: {rows['decode_ragged']}", file=sys.stderr, flush=True)
         for n in [int(x) for x in args.prefill_lens.split(",") if x]:

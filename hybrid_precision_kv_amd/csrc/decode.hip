@@ -277,11 +277,57 @@ struct HeadWork {
   int n_splits, split;
 };
 
-// uniform batch: every sequence has the same counters; grid (split, KV head x head block, b)
+// The work of one workgroup: split `split` of KV head `hkv` of sequence `b`, for Q-head block
+// `sub` (Q heads 4 sub .. 4 sub + 3 of the KV group).
+struct Unit {
+  int split, hkv, sub, b;
+};
+
+// Uniform batch: a 1-D grid.  With one head block per KV head (GQA up to 4) the workgroup id
+// enumerates (split, KV head, sequence), split fastest.  With several head blocks, the blocks
+// of one (split, KV head, sequence) get ids 8 apart: workgroups are dealt to the 8 XCDs in
+// turn, so they run on one XCD one after the other and read the same tiles together -- the
+// slab is streamed from HBM once and the other blocks' reads hit that XCD's L2.  The id
+// space is padded to whole groups of 8; padding workgroups return at once.
+__host__ __device__ inline int decode_grid_size(int n_splits, int Hkv, int B, int G) {
+  const int nsub = (G + 3) >> 2, units = n_splits * Hkv * B;
+  return nsub == 1 ? units : (units + 7) / 8 * 8 * nsub;
+}
+__device__ inline bool unit_of(const DecodeParams& p, Unit& u) {
+  const int nsub = (p.G + 3) >> 2;
+  const int L = blockIdx.x;
+  int r;  // index over (split, KV head, sequence), split fastest
+  if (nsub == 1) {
+    r = L;
+    u.sub = 0;
+  } else {
+    const int k = L >> 3;
+    u.sub = k % nsub;
+    r = (k / nsub) * 8 + (L & 7);
+  }
+  const int per_b = p.n_splits * p.Hkv;
+  if (r >= per_b * p.B) return false;
+  u.split = r % p.n_splits;
+  u.hkv = (r / p.n_splits) % p.Hkv;
+  u.b = r / per_b;
+  return true;
+}
+// variable-length batch: grid (split of the batch, KV head x head block)
+__device__ inline bool unit_of(const RaggedDecodeParams& p, Unit& u) {
+  const int nsub = (p.G + 3) >> 2;
+  u.hkv = blockIdx.y / nsub;
+  u.sub = blockIdx.y % nsub;
+  u.split = 0;  // from the split map
+  u.b = 0;
+  return true;
+}
+
+// uniform batch: every sequence has the same counters
 template <int BK, int BV>
-__device__ inline HeadWork head_work(const DecodeParams& p, int hkv) {
-  const size_t hb = (size_t)blockIdx.z * p.Hkv + hkv;
-  const size_t qh = (size_t)blockIdx.z * p.Hkv * p.G + (size_t)hkv * p.G;
+__device__ inline HeadWork head_work(const DecodeParams& p, const Unit& u) {
+  const int hkv = u.hkv;
+  const size_t hb = (size_t)u.b * p.Hkv + hkv;
+  const size_t qh = (size_t)u.b * p.Hkv * p.G + (size_t)hkv * p.G;
   HeadWork h;
   h.int4 = p.int4 + hb * (size_t)p.int4_cap * QL<BK, BV>::SLOT;
   h.a_k = p.a_k + hb * (size_t)p.anchor_cap * D;
@@ -297,14 +343,15 @@ __device__ inline HeadWork head_work(const DecodeParams& p, int hkv) {
   h.n_staged = p.n_staged;
   h.n_win = p.n_win;
   h.n_splits = p.n_splits;
-  h.split = blockIdx.x;
+  h.split = u.split;
   return h;
 }
 
 // variable-length batch: grid x enumerates the splits of all sequences (split_map), each
 // sequence in its own single-sequence cache
 template <int BK, int BV>
-__device__ inline HeadWork head_work(const RaggedDecodeParams& p, int hkv) {
+__device__ inline HeadWork head_work(const RaggedDecodeParams& p, const Unit& u) {
+  const int hkv = u.hkv;
   const uint32_t m = p.split_map[blockIdx.x];
   const int seq = (int)(m >> 16);
   const RaggedSeq& d = p.seqs[seq];
@@ -336,11 +383,12 @@ __global__ __launch_bounds__(64 * NWAVES) void decode_split_kernel(Params p) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n = lane & 15, q4 = lane >> 4;
   const int hh = n >> 2, g = n & 3;
-  const int nsub = (p.G + 3) >> 2;
-  const int hkv = blockIdx.y / nsub, sub = blockIdx.y % nsub;
+  Unit u;
+  if (!unit_of(p, u)) return;  // padding of the grid (the whole workgroup)
+  const int sub = u.sub;
   const int head = sub * 4 + hh;  // Q head inside the KV group
   const bool head_ok = head < p.G;
-  const HeadWork hw = head_work<BK, BV>(p, hkv);
+  const HeadWork hw = head_work<BK, BV>(p, u);
 
   // ---- q of the (up to 4) Q heads of this head block, staged once through LDS
   __shared__ uint32_t q_lds[4][D / 2];
@@ -671,8 +719,7 @@ hipError_t noalloc_scratch(float** ptr) {
 }
 
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
-  const int nsub = (p.G + 3) >> 2;
-  dim3 grid(p.n_splits, p.Hkv * nsub, p.B);
+  dim3 grid(decode_grid_size(p.n_splits, p.Hkv, p.B, p.G));
   hipError_t e = with_widths(p.bits, p.bits_v, [&](auto BK, auto BV) {
     constexpr int bk = decltype(BK)::value, bv = decltype(BV)::value;
     if (p.waves == 8)
