@@ -17,11 +17,12 @@
 // Four launches:
 //   plan   (one workgroup per head): bitmaps of the new set and of the old anchors with
 //          per-word prefix counts (so "which old anchor / which new index is position p" is
-//          an O(1) rank), the promoted slots, and the move list (targets, kinds, sources);
+//          an O(1) rank), the promoted slots, each new anchor's source, and the move list
+//          (targets, kinds, sources);
 //   gather (grid over heads x new anchors): the new anchor rows, bf16, into a temp store;
-//   move   (grid over heads x moves): quantize demoted rows into slots / move tail slots;
-//   store  (grid over heads x anchor rows): anchor store <- temp, positions.
-// Writes of single V codes go through dword atomics (8 slots share each V-code dword).
+//   move   (grid over heads x chunks of the move list): quantize demoted rows into slots / move
+//          tail slots, each destination tile written by one wave;
+//   store  (grid over heads x anchor tiles): anchor store <- temp, positions.
 //
 // Built with -ffp-contract=off (the quantizer's operation order is part of its contract).
 #include <algorithm>
@@ -59,7 +60,7 @@ struct Scratch {
   int32_t* pre_new;  // [inset_words] set bits before word w (new set)
   int32_t* pre_old;  // [inset_words] set bits before word w (old anchors)
   uint32_t* del;     // [del_words] promoted (deleted) INT4 slots
-  int32_t* slot_of;  // [anchor_cap] INT4 slot of new anchor i (when it is promoted), else -1
+  int32_t* src_of;   // [anchor_cap] source of new anchor i: kind << 29 | index (SRC_* kinds)
   int32_t* mv_dst;   // [max_moves]
   int32_t* mv_kind;  // [max_moves] 0 old anchor, 1 staged, 2 INT4 slot
   int32_t* mv_src;   // [max_moves]
@@ -77,8 +78,8 @@ __device__ inline Scratch scratch(const RefreshParams& p, int hb) {
   s.pre_new = (int32_t*)(s.oldanc + iw);
   s.pre_old = s.pre_new + iw;
   s.del = (uint32_t*)(s.pre_old + iw);
-  s.slot_of = (int32_t*)(s.del + p.del_words);
-  s.mv_dst = s.slot_of + p.anchor_cap;
+  s.src_of = (int32_t*)(s.del + p.del_words);
+  s.mv_dst = s.src_of + p.anchor_cap;
   s.mv_kind = s.mv_dst + p.max_moves;
   s.mv_src = s.mv_kind + p.max_moves;
   s.cnt = s.mv_src + p.max_moves;
@@ -86,6 +87,12 @@ __device__ inline Scratch scratch(const RefreshParams& p, int hb) {
   s.tv = s.tk + (size_t)p.anchor_cap * D;
   return s;
 }
+
+// where new anchor i's bf16 row comes from: an old anchor (its rank), a staged token (its
+// staging index), a promoted quantized slot (dequantized), or nowhere (a malformed set)
+constexpr int SRC_ANCHOR = 0, SRC_STAGED = 1, SRC_SLOT = 2, SRC_NONE = 3;
+constexpr int SRC_SHIFT = 29;
+__device__ inline int32_t src_code(int kind, int index) { return (kind << SRC_SHIFT) | index; }
 
 __device__ inline bool bit_at(const uint32_t* bm, int pos) { return (bm[pos >> 5] >> (pos & 31)) & 1u; }
 __device__ inline int rank_at(const uint32_t* bm, const int32_t* pre, int pos) {
@@ -108,7 +115,7 @@ __global__ __launch_bounds__(PT) void refresh_plan_kernel(RefreshParams p) {
   // ---- bitmaps of the new set and of the old anchors, cleared deletion bitmap
   for (int i = tid; i < iw; i += PT) { s.inset[i] = 0u; s.oldanc[i] = 0u; }
   for (int i = tid; i < p.del_words; i += PT) s.del[i] = 0u;
-  for (int i = tid; i < k_new && i < p.anchor_cap; i += PT) s.slot_of[i] = -1;
+  for (int i = tid; i < k_new && i < p.anchor_cap; i += PT) s.src_of[i] = src_code(SRC_NONE, 0);
   __syncthreads();
   for (int i = tid; i < k_new; i += PT) {
     const int pos = idx[i];
@@ -137,18 +144,39 @@ __global__ __launch_bounds__(PT) void refresh_plan_kernel(RefreshParams p) {
   __syncthreads();
   auto in_set = [&](int pos) -> bool { return pos >= 0 && pos < P && bit_at(s.inset, pos); };
 
-  // ---- INT4 slots whose position is in the set are promoted: delete, record the slot
+  // ---- INT4 slots whose position is in the set are promoted: delete, record the slot.  Eight
+  // slots per thread per pass (their loads in flight together); the 64 slots of a wave at one
+  // step are consecutive, so each deletion word comes whole from one ballot.
   int npro = 0;
-  for (int t = tid; t < n_old; t += PT) {
-    const int pos = slot_pos[t];
-    if (in_set(pos)) {
-      atomicOr(&s.del[t >> 5], 1u << (t & 31));
-      const int i = rank_at(s.inset, s.pre_new, pos);
-      if (i < k_new && i < p.anchor_cap) s.slot_of[i] = t;
-      ++npro;
+  constexpr int UB = 8;
+  const int lane = tid & 63;
+  for (int t0 = tid; t0 < n_old; t0 += PT * UB) {
+    int pos[UB];
+    uint32_t w[UB];
+#pragma unroll
+    for (int u = 0; u < UB; ++u) pos[u] = t0 + u * PT < n_old ? slot_pos[t0 + u * PT] : -1;
+#pragma unroll
+    for (int u = 0; u < UB; ++u) w[u] = pos[u] >= 0 && pos[u] < P ? s.inset[pos[u] >> 5] : 0u;
+#pragma unroll
+    for (int u = 0; u < UB; ++u) {
+      const int t = t0 + u * PT;
+      const bool hit = (w[u] >> (pos[u] & 31)) & 1u;
+      const uint64_t m = __ballot(hit);
+      if (t < n_old && (lane & 31) == 0) s.del[t >> 5] = (uint32_t)(m >> (lane & 32));
+      if (hit) {
+        const int i = s.pre_new[pos[u] >> 5] + __popc(w[u] & ((1u << (pos[u] & 31)) - 1u));
+        if (i < k_new && i < p.anchor_cap) s.src_of[i] = src_code(SRC_SLOT, t);
+        ++npro;
+      }
     }
   }
   __syncthreads();
+  // ---- the other new anchors' sources: staged tokens and old anchors (these win over a slot)
+  for (int i = tid; i < k_new && i < p.anchor_cap; i += PT) {
+    const int pos = idx[i];
+    if (pos >= ps0 && pos < P) s.src_of[i] = src_code(SRC_STAGED, pos - ps0);
+    else if (pos >= 0 && pos < P && bit_at(s.oldanc, pos)) s.src_of[i] = src_code(SRC_ANCHOR, rank_at(s.oldanc, s.pre_old, pos));
+  }
 
   // ---- new INT4 entries E (old anchors, then staged tokens, not in the set, ascending),
   // holes (deleted slots), and the move list targets <- sources
@@ -180,42 +208,50 @@ __global__ __launch_bounds__(PT) void refresh_plan_kernel(RefreshParams p) {
   const int w_lo = tail_lo >> 5, w_hi = (n_old + 31) >> 5;
   const int per_w = (w_hi - w_lo + PT - 1) / PT;
   int ct = 0;
-  for (int w = w_lo + tid * per_w; w < min(w_hi, w_lo + (tid + 1) * per_w); ++w)
+  for (int w = w_lo + tid * per_w; w < min(w_hi, w_lo + (tid + 1) * per_w); ++w) {
+    const uint32_t dw = s.del[w];
     for (int bit = 0; bit < 32; ++bit) {
       const int t = w * 32 + bit;
-      if (t >= tail_lo && t < n_old && !((s.del[w] >> bit) & 1u)) ++ct;
+      if (t >= tail_lo && t < n_old && !((dw >> bit) & 1u)) ++ct;
     }
+  }
   const int off_t = block_scan(ct, sh, &tot);
   {
     int o = e + off_t;
-    for (int w = w_lo + tid * per_w; w < min(w_hi, w_lo + (tid + 1) * per_w); ++w)
+    for (int w = w_lo + tid * per_w; w < min(w_hi, w_lo + (tid + 1) * per_w); ++w) {
+      const uint32_t dw = s.del[w];
       for (int bit = 0; bit < 32; ++bit) {
         const int t = w * 32 + bit;
-        if (t >= tail_lo && t < n_old && !((s.del[w] >> bit) & 1u)) {
+        if (t >= tail_lo && t < n_old && !((dw >> bit) & 1u)) {
           if (o < p.max_moves) { s.mv_kind[o] = 2; s.mv_src[o] = t; }
           ++o;
         }
       }
+    }
   }
   const int n_moves = e + tot;
   // targets: deleted slots below min(n_new, n_old), ascending, then fresh slots [n_old, n_new)
   const int hw = (tail_lo + 31) >> 5;
   const int per_h = (hw + PT - 1) / PT;
   int ch = 0;
-  for (int w = tid * per_h; w < min(hw, (tid + 1) * per_h); ++w)
+  for (int w = tid * per_h; w < min(hw, (tid + 1) * per_h); ++w) {
+    const uint32_t dw = s.del[w];
     for (int bit = 0; bit < 32; ++bit) {
       const int t = w * 32 + bit;
-      if (t < tail_lo && ((s.del[w] >> bit) & 1u)) ++ch;
+      if (t < tail_lo && ((dw >> bit) & 1u)) ++ch;
     }
+  }
   const int off_h = block_scan(ch, sh, &tot);
   const int n_holes = tot;
   {
     int o = off_h;
-    for (int w = tid * per_h; w < min(hw, (tid + 1) * per_h); ++w)
+    for (int w = tid * per_h; w < min(hw, (tid + 1) * per_h); ++w) {
+      const uint32_t dw = s.del[w];
       for (int bit = 0; bit < 32; ++bit) {
         const int t = w * 32 + bit;
-        if (t < tail_lo && ((s.del[w] >> bit) & 1u)) { if (o < p.max_moves) s.mv_dst[o] = t; ++o; }
+        if (t < tail_lo && ((dw >> bit) & 1u)) { if (o < p.max_moves) s.mv_dst[o] = t; ++o; }
       }
+    }
   }
   for (int t = n_old + tid; t < n_new; t += PT)
     if (n_holes + (t - n_old) < p.max_moves) s.mv_dst[n_holes + (t - n_old)] = t;
@@ -232,81 +268,102 @@ __global__ __launch_bounds__(PT) void refresh_plan_kernel(RefreshParams p) {
   }
 }
 
-// ------------------------------------------------------------------ gather: one wave per new anchor
+// ------------------------------------------------------------------ gather: 16 lanes per new anchor
+// Lane l = lane & 15 of a row holds channels 8 l .. 8 l + 7 (group l / 4): a 16-byte load of a
+// bf16 K row, eight 2-byte loads of a bf16 V row, or the codes and (scale, min) of a quantized
+// slot; the row goes to the temp store with two 16-byte stores.
+constexpr int GATHER_ROWS = 16;  // rows per workgroup: 4 waves x 4 rows
+
 template <int BK, int BV>
 __global__ __launch_bounds__(256) void refresh_gather_kernel(RefreshParams p) {
-  const int hb = blockIdx.y, lane = threadIdx.x & 63;
-  const int i = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int k_new = p.k;
-  if (i >= k_new || i >= p.anchor_cap) return;
-  const int P = p.len - WIN;
-  const int ps0 = P - p.n_staged;
+  const int hb = blockIdx.y, l = threadIdx.x & 15;
+  const int i = blockIdx.x * GATHER_ROWS + (threadIdx.x >> 4);
+  if (i >= p.k || i >= p.anchor_cap) return;
   const Scratch s = scratch(p, hb);
   const size_t aslab = (size_t)p.anchor_cap * D, sslab = (size_t)p.staging_cap * D;
-  const int pos = p.idx[hb * (size_t)k_new + i];
-  uint16_t* tk = s.tk + (size_t)i * D;
-  uint16_t* tv = s.tv + (size_t)i * D;
-  if (pos < 0 || pos >= P) return;  // malformed set: nothing to gather (status reports it)
-  if (pos >= ps0 || bit_at(s.oldanc, pos)) {
-    // bf16 already: a staged token or an old anchor
-    const uint16_t *sk, *sv;
-    int si, cap;
-    if (pos >= ps0) { sk = p.s_k + hb * sslab; sv = p.s_v + hb * sslab; si = pos - ps0; cap = p.staging_cap; }
-    else { sk = p.a_k + hb * aslab; sv = p.a_v + hb * aslab; si = rank_at(s.oldanc, s.pre_old, pos); cap = p.anchor_cap; }
-    if (si >= cap) return;
-    for (int c = lane; c < D; c += 64) {
-      tk[c] = sk[kbf_index(si, c)];
-      tv[c] = sv[vbf_index(si, c)];
+  const int32_t code = s.src_of[i];
+  const int kind = code >> SRC_SHIFT, si = code & ((1 << SRC_SHIFT) - 1);
+  const int c0 = 8 * l, g = l >> 2;
+  uint32_t ko[4], vo[4];
+  if (kind == SRC_ANCHOR || kind == SRC_STAGED) {
+    // bf16 already: an old anchor or a staged token
+    const bool anc = kind == SRC_ANCHOR;
+    if (si >= (anc ? p.anchor_cap : p.staging_cap)) return;
+    const uint16_t* sk = anc ? p.a_k + hb * aslab : p.s_k + hb * sslab;
+    const uint16_t* sv = anc ? p.a_v + hb * aslab : p.s_v + hb * sslab;
+    const u32x4 kr = *(const u32x4*)(sk + kbf_index(si, c0));  // channels c0 .. c0+7
+    ko[0] = kr[0]; ko[1] = kr[1]; ko[2] = kr[2]; ko[3] = kr[3];
+    uint16_t vr[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) vr[e] = sv[vbf_index(si, c0 + e)];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) vo[e] = (uint32_t)vr[2 * e] | ((uint32_t)vr[2 * e + 1] << 16);
+  } else if (kind == SRC_SLOT) {
+    // a quantized position: dequantize its slot
+    if (si >= p.int4_cap) return;
+    const uint8_t* slab = p.int4 + hb * (size_t)p.int4_cap * QL<BK, BV>::SLOT;
+    // K codes of channels c0 .. c0+7: 8 BK bits from bit 8 BK (l & 3) of the group's chunk
+    const int kbit = 8 * BK * (l & 3);
+    uint64_t kbits;
+    if constexpr (BK == 8) kbits = *(const uint64_t*)(slab + kcode_chunk_b<BK, BV>(si, g) + (kbit >> 3));
+    else kbits = *(const uint32_t*)(slab + kcode_chunk_b<BK, BV>(si, g) + 4 * (kbit >> 5)) >> (kbit & 31);
+    uint32_t vw[8];
+    int vsh[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      size_t off;
+      vcode_loc<BK, BV>(si, c0 + e, off, vsh[e]);
+      vw[e] = *(const uint32_t*)(slab + off);
     }
-    return;
+    const uint32_t ksm = *(const uint32_t*)(slab + ksm_byte_b<BK, BV>(si, g));
+    const uint32_t vsm = *(const uint32_t*)(slab + vsm_byte_b<BK, BV>(si, g));
+    const float ks = __half2float(__ushort_as_half((unsigned short)(ksm & 0xffff)));
+    const float km = __half2float(__ushort_as_half((unsigned short)(ksm >> 16)));
+    const float vs = __half2float(__ushort_as_half((unsigned short)(vsm & 0xffff)));
+    const float vm = __half2float(__ushort_as_half((unsigned short)(vsm >> 16)));
+    uint16_t kx[8], vx[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t kc = (uint32_t)(kbits >> (BK * e)) & ((1u << BK) - 1u);
+      const uint32_t vc = (vw[e] >> vsh[e]) & ((1u << BV) - 1u);
+      // dequantized value = scale * code + min in fp32 (exact product, one rounding), then bf16
+      kx[e] = f32_to_bf16_bits(ks * (float)kc + km);
+      vx[e] = f32_to_bf16_bits(vs * (float)vc + vm);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      ko[e] = (uint32_t)kx[2 * e] | ((uint32_t)kx[2 * e + 1] << 16);
+      vo[e] = (uint32_t)vx[2 * e] | ((uint32_t)vx[2 * e + 1] << 16);
+    }
+  } else {
+    return;  // malformed set: nothing to gather (the status reports it)
   }
-  // a quantized position: dequantize its slot
-  const int t = s.slot_of[i];
-  if (t < 0 || t >= p.int4_cap) return;
-  const uint8_t* slab = p.int4 + hb * (size_t)p.int4_cap * QL<BK, BV>::SLOT;
-  for (int c = lane; c < D; c += 64) {
-    const int g = c >> 5;
-    // K code: channel c & 31 of the chunk at bits BK (c & 31), read from its byte
-    const int kbit = BK * (c & 31);
-    const uint32_t kc = ((uint32_t)slab[kcode_chunk_b<BK, BV>(t, g) + (kbit >> 3)] >> (kbit & 7)) & ((1u << BK) - 1u);
-    size_t voff;
-    int vsh;
-    vcode_loc<BK, BV>(t, c, voff, vsh);
-    const uint32_t vc = (*(const uint32_t*)(slab + voff) >> vsh) & ((1u << BV) - 1u);
-    const uint32_t ksm = *(const uint32_t*)(slab + ksm_byte_b<BK, BV>(t, g));
-    const uint32_t vsm = *(const uint32_t*)(slab + vsm_byte_b<BK, BV>(t, g));
-    // dequantized value = scale * code + min in fp32 (exact product, one rounding), then bf16
-    const float kx = __half2float(__ushort_as_half((unsigned short)(ksm & 0xffff))) * (float)kc +
-                     __half2float(__ushort_as_half((unsigned short)(ksm >> 16)));
-    const float vx = __half2float(__ushort_as_half((unsigned short)(vsm & 0xffff))) * (float)vc +
-                     __half2float(__ushort_as_half((unsigned short)(vsm >> 16)));
-    tk[c] = f32_to_bf16_bits(kx);
-    tv[c] = f32_to_bf16_bits(vx);
-  }
+  *(u32x4*)(s.tk + (size_t)i * D + c0) = (u32x4){ko[0], ko[1], ko[2], ko[3]};
+  *(u32x4*)(s.tv + (size_t)i * D + c0) = (u32x4){vo[0], vo[1], vo[2], vo[3]};
 }
 
-// ------------------------------------------------------------------ move: one wave per move
-// The plan's move count is known only on the device, so a fixed grid of MOVE_BLOCKS workgroups
-// per head walks the list (wave w takes moves w, w + waves, ...).
+// ------------------------------------------------------------------ move: tile-owner waves
+// The move list is sorted by destination slot (holes ascending, then fresh slots ascending), so
+// the moves into one 32-slot tile form a contiguous run of at most 32 entries.  Wave w takes the
+// entries [MV_CHUNK w, MV_CHUNK (w + 1)) and owns every tile whose first move lies there; it
+// runs past its chunk to finish its last tile.  One 64-lane load of the list from MV_CHUNK w - 1
+// covers a chunk plus the longest run, so a wave reads its part of the list once.
+//
+// A V code shares its dword with the other slots of its quad only (every width), so the owner
+// of a tile is the only writer of that tile's V-code dwords: it loads the dwords of the quads
+// its moves touch into registers (lane = 32 + 8 g + sub keeps channels 32 g + 4 sub + e,
+// e < 4, the same lanes that quantize those channels), replaces the codes there, and stores the
+// dwords back -- plain loads and stores, no atomics.  Kept codes of slots nobody moves are
+// written back unchanged (a tail slot read as a source by another wave keeps its value).  A
+// 2-bit dword also spans channels c and c + 16 (lanes sub and sub + 4): those two lanes'
+// copies are merged before the store.
 //
 // Demoting a bf16 row uses the whole wave: lane = 32 kv + 8 g + sub holds channels
-// 32 g + 4 sub + e (e < 4) of K (kv = 0) or V (kv = 1); the group's min and max come from a
-// reduction over its 8 lanes, and every code follows the group quantizer's formula.  A V code
-// is one nibble of a dword shared by 8 slots: each slot is written by exactly one move, so the
-// nibble is replaced with one atomic XOR of (old ^ new), which commutes with the other slots'
-// (and is skipped when the nibble already holds the code: the atomics, not the read, bound
-// this kernel).  The next move's list entry is loaded while the current move runs.
-constexpr int MOVE_BLOCKS = 16;
-
-template <int BK, int BV>
-__device__ inline void put_vcode(uint8_t* slab, int slot, int c, uint32_t code) {
-  size_t off;
-  int sh;
-  vcode_loc<BK, BV>(slot, c, off, sh);
-  unsigned* dw = (unsigned*)(slab + off);
-  const uint32_t delta = (((*dw >> sh) & ((1u << BV) - 1u)) ^ code) << sh;
-  if (delta) atomicXor(dw, delta);
-}
+// 32 g + 4 sub + e of K (kv = 0) or V (kv = 1); the group's min and max come from a reduction
+// over its 8 lanes, and every code follows the group quantizer's formula.  The next move's
+// source words are loaded while the current move is processed.
+constexpr int MV_CHUNK = 16;
+constexpr int MOVE_WAVES = 4;  // waves per workgroup
 
 __device__ inline float group8_min(float v) {
 #pragma unroll
@@ -319,124 +376,274 @@ __device__ inline float group8_max(float v) {
   return v;
 }
 
+// source words of one move, per lane (see load_move)
+struct MoveSrc {
+  uint32_t r[4];
+  uint32_t sm;
+  int32_t pos;
+};
+
 template <int BK, int BV>
-__global__ __launch_bounds__(256) void refresh_move_kernel(RefreshParams p) {
-  typedef QL<BK, BV> L;
-  const int hb = blockIdx.y, lane = threadIdx.x & 63;
-  const Scratch s = scratch(p, hb);
-  const int n = min(s.cnt[0], p.max_moves), waves = gridDim.x * 4;
-  const int P = p.len - WIN;
-  const int ps0 = P - p.n_staged;
-  uint8_t* slab = p.int4 + hb * (size_t)p.int4_cap * L::SLOT;
-  int32_t* slot_pos = p.slot_pos + hb * (size_t)p.int4_cap;
+__device__ inline MoveSrc load_move(const RefreshParams& p, int hb, int kind, int src, int lane, const uint8_t* slab,
+                                    const int32_t* slot_pos, int ps0) {
+  const int kv = lane >> 5, g = (lane >> 3) & 3, sub = lane & 7, c0 = 32 * g + 4 * sub;
   const size_t aslab = (size_t)p.anchor_cap * D, sslab = (size_t)p.staging_cap * D;
-  const int kv = lane >> 5, g = (lane >> 3) & 3, sub = lane & 7;
-  int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  int ndst = 0, nkind = 0, nsrc = 0;
-  if (t < n) { ndst = s.mv_dst[t]; nkind = s.mv_kind[t]; nsrc = s.mv_src[t]; }
-  for (; t < n; t += waves) {
-    const int dst = ndst, kind = nkind, src = nsrc;
-    if (t + waves < n) { ndst = s.mv_dst[t + waves]; nkind = s.mv_kind[t + waves]; nsrc = s.mv_src[t + waves]; }
-    const int src_cap = kind == 0 ? p.anchor_cap : kind == 1 ? p.staging_cap : p.int4_cap;
-    if (dst < 0 || dst >= p.int4_cap || src < 0 || src >= src_cap) continue;
-    if (kind <= 1) {
-      // quantize a bf16 row (old anchor or staged token) into slot dst
-      const uint16_t* sk = kind == 0 ? p.a_k + hb * aslab : p.s_k + hb * sslab;
-      const uint16_t* sv = kind == 0 ? p.a_v + hb * aslab : p.s_v + hb * sslab;
-      const int c0 = 32 * g + 4 * sub;
-      float x[4];
-      if (kv == 0) {
-        const uint2 raw = *(const uint2*)(sk + kbf_index(src, c0));  // channels c0 .. c0+3
-        x[0] = bf16_bits_to_f32((uint16_t)raw.x);
-        x[1] = bf16_bits_to_f32((uint16_t)(raw.x >> 16));
-        x[2] = bf16_bits_to_f32((uint16_t)raw.y);
-        x[3] = bf16_bits_to_f32((uint16_t)(raw.y >> 16));
-      } else {
+  MoveSrc m = {{0u, 0u, 0u, 0u}, 0u, -1};
+  const int src_cap = kind == 0 ? p.anchor_cap : kind == 1 ? p.staging_cap : p.int4_cap;
+  if (src < 0 || src >= src_cap) return m;  // not executed (the move loop checks the same bound)
+  if (kind <= 1) {
+    // bf16 row: K lanes read channels c0 .. c0+3 (8 bytes), V lanes the same channels (4 x 2 bytes)
+    const uint16_t* sk = kind == 0 ? p.a_k + hb * aslab : p.s_k + hb * sslab;
+    const uint16_t* sv = kind == 0 ? p.a_v + hb * aslab : p.s_v + hb * sslab;
+    if (kv == 0) {
+      const uint2 raw = *(const uint2*)(sk + kbf_index(src, c0));
+      m.r[0] = raw.x;
+      m.r[1] = raw.y;
+    } else {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) x[e] = bf16_bits_to_f32(sv[vbf_index(src, c0 + e)]);
-      }
-      const float mn = group8_min(fminf(fminf(x[0], x[1]), fminf(x[2], x[3])));
-      const float mx = group8_max(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
-      // the group quantizer's scale, minimum and codes (same operations, same order)
-      const float LEVELS = kv ? (float)((1 << BV) - 1) : (float)((1 << BK) - 1);
-      const __half s16 = __float2half_rn(__fdiv_rn(__fsub_rn(mx, mn), LEVELS));
-      const __half m16 = __float2half_rn(mn);
-      const float sf = __half2float(s16), mf = __half2float(m16);
-      uint32_t code[4];
+      for (int e = 0; e < 4; ++e) m.r[e] = sv[vbf_index(src, c0 + e)];
+    }
+    if (lane == 0) m.pos = kind == 0 ? p.a_pos[hb * (size_t)p.anchor_cap + src] : ps0 + src;
+  } else {
+    // quantized slot: K lanes sub < BK read dword sub of the group's K chunk, lane sub 0 the
+    // group's (scale, min); V lanes read the dwords holding their 4 channels' codes
+    if (kv == 0) {
+      if (sub < BK) m.r[0] = *(const uint32_t*)(slab + kcode_chunk_b<BK, BV>(src, g) + 4 * sub);
+      if (sub == 0) m.sm = *(const uint32_t*)(slab + ksm_byte_b<BK, BV>(src, g));
+    } else {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        float cq = 0.0f;
-        if (sf != 0.0f) {
-          cq = rintf(__fdiv_rn(__fsub_rn(x[e], mf), sf));
-          cq = fminf(fmaxf(cq, 0.0f), LEVELS);
-        }
-        code[e] = (uint32_t)cq;
-      }
-      const uint32_t smw = (uint32_t)__half_as_ushort(s16) | ((uint32_t)__half_as_ushort(m16) << 16);
-      if (kv == 0) {
-        if constexpr (BK == 4) {
-          // nibbles 4 sub + e of the group's 32; dword sub / 2 holds lanes sub & ~1 (low) and | 1
-          const uint32_t half16 = code[0] | (code[1] << 4) | (code[2] << 8) | (code[3] << 12);
-          const uint32_t other = (uint32_t)__float_as_int(shfl_xor_f(__int_as_float((int)half16), 1));
-          if ((sub & 1) == 0) *(uint32_t*)(slab + kcode_chunk_b<BK, BV>(dst, g) + 4 * (sub >> 1)) = half16 | (other << 16);
-        } else if constexpr (BK == 8) {
-          // bytes 4 sub + e of the group's 32: one dword per lane
-          *(uint32_t*)(slab + kcode_chunk_b<BK, BV>(dst, g) + 4 * sub) =
-              code[0] | (code[1] << 8) | (code[2] << 16) | (code[3] << 24);
-        } else {
-          // 2-bit codes 4 sub + e: byte sub & 3 of dword sub / 4, OR-ed over the dword's 4 lanes
-          uint32_t w = (code[0] | (code[1] << 2) | (code[2] << 4) | (code[3] << 6)) << (8 * (sub & 3));
-          w |= (uint32_t)__float_as_int(shfl_xor_f(__int_as_float((int)w), 1));
-          w |= (uint32_t)__float_as_int(shfl_xor_f(__int_as_float((int)w), 2));
-          if ((sub & 3) == 0) *(uint32_t*)(slab + kcode_chunk_b<BK, BV>(dst, g) + 4 * (sub >> 2)) = w;
-        }
-        if (sub == 0) *(uint32_t*)(slab + ksm_byte_b<BK, BV>(dst, g)) = smw;
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) put_vcode<BK, BV>(slab, dst, c0 + e, code[e]);
-        if (sub == 0) *(uint32_t*)(slab + vsm_byte_b<BK, BV>(dst, g)) = smw;
-      }
-      if (lane == 0) slot_pos[dst] = kind == 0 ? p.a_pos[hb * (size_t)p.anchor_cap + src] : ps0 + src;
-    } else {
-      // move a quantized slot: codes, (scale, min), position
-      constexpr int KDW = L::CB / 4;  // dwords per (slot, group) K chunk: BK
-      if (lane < 4 * KDW) {  // K code chunks as dwords
-        const int q4 = lane / KDW, d = lane % KDW;
-        *(uint32_t*)(slab + kcode_chunk_b<BK, BV>(dst, q4) + 4 * d) =
-            *(const uint32_t*)(slab + kcode_chunk_b<BK, BV>(src, q4) + 4 * d);
-      } else if (lane < 4 * KDW + 4) {
-        const int q4 = lane - 4 * KDW;
-        *(uint32_t*)(slab + ksm_byte_b<BK, BV>(dst, q4)) = *(const uint32_t*)(slab + ksm_byte_b<BK, BV>(src, q4));
-        *(uint32_t*)(slab + vsm_byte_b<BK, BV>(dst, q4)) = *(const uint32_t*)(slab + vsm_byte_b<BK, BV>(src, q4));
-      }
-      for (int c = lane; c < D; c += 64) {
         size_t off;
-        int shs;
-        vcode_loc<BK, BV>(src, c, off, shs);
-        put_vcode<BK, BV>(slab, dst, c, (*(const uint32_t*)(slab + off) >> shs) & ((1u << BV) - 1u));
+        int sh;
+        vcode_loc<BK, BV>(src, c0 + e, off, sh);
+        m.r[e] = *(const uint32_t*)(slab + off);
       }
-      if (lane == 0) slot_pos[dst] = slot_pos[src];
+      if (sub == 0) m.sm = *(const uint32_t*)(slab + vsm_byte_b<BK, BV>(src, g));
+    }
+    if (lane == 0) m.pos = slot_pos[src];
+  }
+  return m;
+}
+
+template <int BK, int BV>
+__global__ __launch_bounds__(64 * MOVE_WAVES) void refresh_move_kernel(RefreshParams p) {
+  constexpr int NH = BV == 8 ? 2 : 1;  // V-code dwords per (quad, channel): INT8 codes take two
+  constexpr uint32_t VMASK = (1u << BV) - 1u;
+  const int hb = blockIdx.y, lane = threadIdx.x & 63;
+  const Scratch s = scratch(p, hb);
+  const int n = min(s.cnt[0], p.max_moves);
+  const int lo = (blockIdx.x * MOVE_WAVES + (threadIdx.x >> 6)) * MV_CHUNK;
+  if (lo >= n) return;
+  const int P = p.len - WIN;
+  const int ps0 = P - p.n_staged;
+  uint8_t* slab = p.int4 + hb * (size_t)p.int4_cap * QL<BK, BV>::SLOT;
+  int32_t* slot_pos = p.slot_pos + hb * (size_t)p.int4_cap;
+  const int kv = lane >> 5, g = (lane >> 3) & 3, sub = lane & 7, c0 = 32 * g + 4 * sub;
+  const int n_tiles = p.int4_cap >> 5;
+
+  // the list window: lane i holds entry lo - 1 + i
+  const int me = lo - 1 + lane;
+  const bool in_list = me >= 0 && me < n;
+  const int wdst = in_list ? s.mv_dst[me] : -1, wkind = in_list ? s.mv_kind[me] : 0, wsrc = in_list ? s.mv_src[me] : -1;
+  const int wtile = wdst >> 5;
+  const int prev_tile = __shfl_up(wtile, 1);
+  const bool starts = in_list && lane >= 1 && (me == 0 || wtile != prev_tile);
+  const uint64_t start_mask = __ballot(starts);
+  // first owned entry: the first tile start at lanes 1 .. MV_CHUNK; the end: the first tile start
+  // at lanes > MV_CHUNK, else the end of the list
+  const uint64_t own = start_mask & (((1ull << MV_CHUNK) - 1ull) << 1);
+  if (own == 0) return;  // the whole chunk continues a tile owned by an earlier wave
+  const int j0 = __builtin_ctzll(own);
+  const uint64_t later = start_mask & ~((2ull << MV_CHUNK) - 1ull);
+  const int j_end = later ? __builtin_ctzll(later) : min(64, n - (lo - 1));
+
+  MoveSrc nxt = load_move<BK, BV>(p, hb, __shfl(wkind, j0), __shfl(wsrc, j0), lane, slab, slot_pos, ps0);
+  uint32_t vq[4][4][NH];
+  int tile = -1;
+  uint32_t qmask = 0;
+  for (int j = j0; j < j_end; ++j) {
+    const int dst = __builtin_amdgcn_readfirstlane(__shfl(wdst, j));
+    const int kind = __builtin_amdgcn_readfirstlane(__shfl(wkind, j));
+    const int src = __builtin_amdgcn_readfirstlane(__shfl(wsrc, j));
+    const MoveSrc cur = nxt;
+    if (j + 1 < j_end) nxt = load_move<BK, BV>(p, hb, __shfl(wkind, j + 1), __shfl(wsrc, j + 1), lane, slab, slot_pos, ps0);
+    if ((dst >> 5) != tile) {
+      // a new tile: the quads its moves touch, their V-code dwords into registers
+      tile = dst >> 5;
+      const bool mine = lane >= j && lane < j_end && wtile == tile && wdst >= 0;
+      qmask = 0;
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq)
+        if (__ballot(mine && tile_quad(wdst & 31) == qq)) qmask |= 1u << qq;
+      if (tile < 0 || tile >= n_tiles) qmask = 0;
+      if (kv == 1) {
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq)
+          if (qmask >> qq & 1u) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+#pragma unroll
+              for (int hh = 0; hh < NH; ++hh) {
+                size_t off;
+                int sh;
+                vcode_loc<BK, BV>(32 * tile + 4 * qq + 16 * hh, c0 + e, off, sh);
+                vq[qq][e][hh] = *(const uint32_t*)(slab + off);
+              }
+          }
+      }
+    }
+    const int src_cap = kind == 0 ? p.anchor_cap : kind == 1 ? p.staging_cap : p.int4_cap;
+    const bool valid = dst >= 0 && dst < p.int4_cap && src >= 0 && src < src_cap;
+    if (valid) {
+      uint32_t code[4];
+      if (kind <= 1) {
+        // quantize a bf16 row (old anchor or staged token) into slot dst
+        float x[4];
+        if (kv == 0) {
+          x[0] = bf16_bits_to_f32((uint16_t)cur.r[0]);
+          x[1] = bf16_bits_to_f32((uint16_t)(cur.r[0] >> 16));
+          x[2] = bf16_bits_to_f32((uint16_t)cur.r[1]);
+          x[3] = bf16_bits_to_f32((uint16_t)(cur.r[1] >> 16));
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) x[e] = bf16_bits_to_f32((uint16_t)cur.r[e]);
+        }
+        const float mn = group8_min(fminf(fminf(x[0], x[1]), fminf(x[2], x[3])));
+        const float mx = group8_max(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
+        // the group quantizer's scale, minimum and codes (same operations, same order)
+        const float LEVELS = kv ? (float)((1 << BV) - 1) : (float)((1 << BK) - 1);
+        const __half s16 = __float2half_rn(__fdiv_rn(__fsub_rn(mx, mn), LEVELS));
+        const __half m16 = __float2half_rn(mn);
+        const float sf = __half2float(s16), mf = __half2float(m16);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float cq = 0.0f;
+          if (sf != 0.0f) {
+            cq = rintf(__fdiv_rn(__fsub_rn(x[e], mf), sf));
+            cq = fminf(fmaxf(cq, 0.0f), LEVELS);
+          }
+          code[e] = (uint32_t)cq;
+        }
+        const uint32_t smw = (uint32_t)__half_as_ushort(s16) | ((uint32_t)__half_as_ushort(m16) << 16);
+        if (kv == 0) {
+          if constexpr (BK == 4) {
+            // nibbles 4 sub + e of the group's 32; dword sub / 2 holds lanes sub & ~1 (low) and | 1
+            const uint32_t half16 = code[0] | (code[1] << 4) | (code[2] << 8) | (code[3] << 12);
+            const uint32_t other = (uint32_t)__float_as_int(shfl_xor_f(__int_as_float((int)half16), 1));
+            if ((sub & 1) == 0) *(uint32_t*)(slab + kcode_chunk_b<BK, BV>(dst, g) + 4 * (sub >> 1)) = half16 | (other << 16);
+          } else if constexpr (BK == 8) {
+            // bytes 4 sub + e of the group's 32: one dword per lane
+            *(uint32_t*)(slab + kcode_chunk_b<BK, BV>(dst, g) + 4 * sub) =
+                code[0] | (code[1] << 8) | (code[2] << 16) | (code[3] << 24);
+          } else {
+            // 2-bit codes 4 sub + e: byte sub & 3 of dword sub / 4, OR-ed over the dword's 4 lanes
+            uint32_t w = (code[0] | (code[1] << 2) | (code[2] << 4) | (code[3] << 6)) << (8 * (sub & 3));
+            w |= (uint32_t)__float_as_int(shfl_xor_f(__int_as_float((int)w), 1));
+            w |= (uint32_t)__float_as_int(shfl_xor_f(__int_as_float((int)w), 2));
+            if ((sub & 3) == 0) *(uint32_t*)(slab + kcode_chunk_b<BK, BV>(dst, g) + 4 * (sub >> 2)) = w;
+          }
+          if (sub == 0) *(uint32_t*)(slab + ksm_byte_b<BK, BV>(dst, g)) = smw;
+        } else if (sub == 0) {
+          *(uint32_t*)(slab + vsm_byte_b<BK, BV>(dst, g)) = smw;
+        }
+      } else {
+        // move a quantized slot: K chunk dwords and (scale, min) as read, V codes re-placed
+        if (kv == 0) {
+          if (sub < BK) *(uint32_t*)(slab + kcode_chunk_b<BK, BV>(dst, g) + 4 * sub) = cur.r[0];
+          if (sub == 0) *(uint32_t*)(slab + ksm_byte_b<BK, BV>(dst, g)) = cur.sm;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            size_t off;
+            int sh;
+            vcode_loc<BK, BV>(src, c0 + e, off, sh);
+            code[e] = (cur.r[e] >> sh) & VMASK;
+          }
+          if (sub == 0) *(uint32_t*)(slab + vsm_byte_b<BK, BV>(dst, g)) = cur.sm;
+        }
+      }
+      if (kv == 1) {
+        // replace slot dst's codes in the owned dwords (quad and half are wave-uniform)
+        const int q = tile_quad(dst & 31), h = NH == 2 ? (dst & 31) >> 4 : 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          size_t off;
+          int sh;
+          vcode_loc<BK, BV>(dst, c0 + e, off, sh);
+#pragma unroll
+          for (int qq = 0; qq < 4; ++qq)
+#pragma unroll
+            for (int hh = 0; hh < NH; ++hh)
+              if (qq == q && hh == h) vq[qq][e][hh] = (vq[qq][e][hh] & ~(VMASK << sh)) | (code[e] << sh);
+        }
+      }
+      if (lane == 0) slot_pos[dst] = cur.pos;
+    }
+    // the tile's last move: the owned dwords go back
+    if (j + 1 == j_end || (__builtin_amdgcn_readfirstlane(__shfl(wdst, j + 1)) >> 5) != tile) {
+      if (kv == 1) {
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq)
+          if (qmask >> qq & 1u) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+#pragma unroll
+              for (int hh = 0; hh < NH; ++hh) {
+                size_t off;
+                int sh;
+                vcode_loc<BK, BV>(32 * tile + 4 * qq + 16 * hh, c0 + e, off, sh);
+                if constexpr (BV == 2) {
+                  // a 2-bit dword holds channels c (bytes 0 and 2) and c + 16 (bytes 1 and 3):
+                  // lanes sub and sub + 4 edit one each; the merged dword goes out once
+                  const uint32_t other = (uint32_t)__shfl_xor((int)vq[qq][e][hh], 4);
+                  if (sub < 4) *(uint32_t*)(slab + off) = (vq[qq][e][hh] & 0x00FF00FFu) | (other & 0xFF00FF00u);
+                } else {
+                  *(uint32_t*)(slab + off) = vq[qq][e][hh];
+                }
+              }
+          }
+      }
     }
   }
 }
 
-// ------------------------------------------------------------------ store: one wave per anchor row
-// anchor store <- temp (tile layouts), positions, zeroed tail of the last tile
+// ------------------------------------------------------------------ store: one workgroup per anchor tile
+// anchor store <- temp (tile layouts), positions, zeroed tail of the last tile.  The tile's 32
+// temp rows of K and V (row-major, 16 KB) are staged in LDS with 16-byte loads, then written in
+// the tile layouts with 16-byte stores: a K chunk is 8 consecutive channels of one position
+// (a permutation of the temp's 16-byte pieces), a V piece one channel at the 8 positions of a
+// quad (a transpose, gathered from LDS).
 __global__ __launch_bounds__(256) void refresh_store_kernel(RefreshParams p) {
-  const int hb = blockIdx.y, lane = threadIdx.x & 63;
-  const int i = blockIdx.x * 4 + (threadIdx.x >> 6);
+  __shared__ uint16_t sk[32][D], sv[32][D];
+  const int hb = blockIdx.y, tile = blockIdx.x, tid = threadIdx.x;
   const int k_new = p.k;
-  const int a_end = min((k_new + 31) & ~31, p.anchor_cap);
-  if (i >= a_end) return;
+  const int i0 = tile * 32;
   const Scratch s = scratch(p, hb);
-  const size_t aslab = (size_t)p.anchor_cap * D;
-  uint16_t* a_k = p.a_k + hb * aslab;
-  uint16_t* a_v = p.a_v + hb * aslab;
-  for (int c = lane; c < D; c += 64) {
-    a_k[kbf_index(i, c)] = i < k_new ? s.tk[(size_t)i * D + c] : (uint16_t)0;
-    a_v[vbf_index(i, c)] = i < k_new ? s.tv[(size_t)i * D + c] : (uint16_t)0;
+  for (int ch = tid; ch < 1024; ch += 256) {  // 32 rows x 16 pieces, K then V
+    const int kv = ch >> 9, row = (ch >> 4) & 31, part = ch & 15;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (i0 + row < k_new) v = *(const u32x4*)((kv ? s.tv : s.tk) + (size_t)(i0 + row) * D + 8 * part);
+    *(u32x4*)(kv ? &sv[row][8 * part] : &sk[row][8 * part]) = v;
   }
-  if (lane == 0) p.a_pos[hb * (size_t)p.anchor_cap + i] = i < k_new ? p.idx[hb * (size_t)k_new + i] : -1;
+  __syncthreads();
+  const size_t aslab = (size_t)p.anchor_cap * D;
+  uint16_t* ak = p.a_k + hb * aslab + (size_t)tile * 4096;
+  uint16_t* av = p.a_v + hb * aslab + (size_t)tile * 4096;
+  for (int ch = tid; ch < 512; ch += 256) {
+    // K chunk ch = ((p16 * 4 + tt) * 4 + q4) * 16 + p15: channels 32 q4 + 8 tt .. + 7 of position 16 p16 + p15
+    const int p15 = ch & 15, q4 = (ch >> 4) & 3, tt = (ch >> 6) & 3, p16 = ch >> 8;
+    *(u32x4*)(ak + 8 * ch) = *(const u32x4*)&sk[16 * p16 + p15][32 * q4 + 8 * tt];
+    // V piece ch = ((c >> 4) * 4 + q) * 16 + (c & 15): channel c at the positions of quad q, k-slot order
+    const int ci = ch & 15, q = (ch >> 4) & 3, cb = ch >> 6, c = 16 * cb + ci;
+    uint32_t w[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int pa = 4 * q + ((2 * e) & 3) + 16 * ((2 * e) >> 2), pb = 4 * q + ((2 * e + 1) & 3) + 16 * ((2 * e + 1) >> 2);
+      w[e] = (uint32_t)sv[pa][c] | ((uint32_t)sv[pb][c] << 16);
+    }
+    *(u32x4*)(av + 8 * ch) = (u32x4){w[0], w[1], w[2], w[3]};
+  }
+  if (tid < 32) p.a_pos[hb * (size_t)p.anchor_cap + i0 + tid] = i0 + tid < k_new ? p.idx[hb * (size_t)k_new + i0 + tid] : -1;
 }
 
 }  // namespace
@@ -450,16 +657,17 @@ hipError_t launch_refresh(const RefreshParams& p, hipStream_t stream) {
   const int H = p.B * p.Hkv;
   hipLaunchKernelGGL(refresh_plan_kernel, dim3(H), dim3(PT), 0, stream, p);
   const int ka = min(p.k, p.anchor_cap);
-  const dim3 mgrid(std::max(1, std::min((p.max_moves + 3) / 4, MOVE_BLOCKS)), H);
+  const int move_waves = (p.max_moves + MV_CHUNK - 1) / MV_CHUNK;
+  const dim3 mgrid(std::max(1, (move_waves + MOVE_WAVES - 1) / MOVE_WAVES), H);
   hipError_t e = with_widths(p.bits, p.bits_v, [&](auto BK, auto BV) {
     constexpr int K = decltype(BK)::value, V = decltype(BV)::value;
-    if (ka > 0) hipLaunchKernelGGL((refresh_gather_kernel<K, V>), dim3((ka + 3) / 4, H), dim3(256), 0, stream, p);
-    hipLaunchKernelGGL((refresh_move_kernel<K, V>), mgrid, dim3(256), 0, stream, p);
+    if (ka > 0) hipLaunchKernelGGL((refresh_gather_kernel<K, V>), dim3((ka + GATHER_ROWS - 1) / GATHER_ROWS, H), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((refresh_move_kernel<K, V>), mgrid, dim3(64 * MOVE_WAVES), 0, stream, p);
     return hipGetLastError();
   });
   if (e != hipSuccess) return e;
   const int a_end = min((p.k + 31) & ~31, p.anchor_cap);
-  if (a_end > 0) hipLaunchKernelGGL(refresh_store_kernel, dim3((a_end + 3) / 4, H), dim3(256), 0, stream, p);
+  if (a_end > 0) hipLaunchKernelGGL(refresh_store_kernel, dim3(a_end / 32, H), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
