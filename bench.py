@@ -222,11 +222,20 @@ def bench_maintenance(torch, hq, cache, B, Hkv, G, L, gen, dev, ws, out, splits)
         t_app += ev[0].elapsed_time(ev[1]) * 1e3
         t_dec += ev[1].elapsed_time(ev[2]) * 1e3
     k = hq.anchor_count(cache.len)
+    # the selection alone (no state change), then the same selection applied: the difference
+    # is the refresh
+    ev[0].record()
+    idx = hq.select_vlines(cache.shape, k, cache=cache)
+    ev[1].record()
+    torch.cuda.synchronize()
+    t_sel = ev[0].elapsed_time(ev[1]) * 1e3
+    model = refresh_bytes(torch, cache, idx)
     ev[0].record()
     hq.select_vlines(cache.shape, k, cache=cache, apply=True)
     ev[1].record()
     torch.cuda.synchronize()
     t_ref = ev[0].elapsed_time(ev[1]) * 1e3
+    t_apply = max(t_ref - t_sel, 1e-3)
     # device time of the per-token work from captured graphs (the staging emptied by the
     # refresh above takes the 51 appends the warm-ups and captures make; a replay repeats the
     # recorded appends into the same slots)
@@ -243,11 +252,73 @@ def bench_maintenance(torch, hq, cache, B, Hkv, G, L, gen, dev, ws, out, splits)
     us_step_g, _ = timed_graph(torch, step, 20)
     return {"append_us": round(us_app_g, 2), "append_us_eager": round(t_app / 64, 2),
             "append_decode_us_graph": round(us_step_g, 2), "decode_us_with_staging": round(t_dec / 64, 2),
-            "select_refresh_us": round(t_ref, 1), "anchors_after_refresh": k,
+            "select_refresh_us": round(t_ref, 1), "select_us": round(t_sel, 1), "refresh_us": round(t_apply, 1),
+            "refresh_bytes": model,
+            "refresh_roofline": {"bound": "hbm", "achieved_min_bytes": round(model["min_bytes"] / (t_apply * 1e-6) / 1e9, 1),
+                                 "achieved_moved_bytes": round(model["moved_bytes"] / (t_apply * 1e-6) / 1e9, 1),
+                                 "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                 "frac_min_bytes": round(model["min_bytes"] / (t_apply * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)},
+            "anchors_after_refresh": k,
             "us_per_token_amortized": round(us_step_g + t_ref / 64, 2),
             "note": f"one layer, bs{B} ctx {L}+64, refresh every 64 tokens; append_us (a graph of 16 appends, per "
                     "append) and append_decode_us_graph are device time from captured graphs, select_refresh_us one "
                     "eager call; us_per_token_amortized = append_decode_us_graph + select_refresh_us / 64"}
+
+
+def refresh_bytes(torch, cache, idx):
+    """Byte model of one refresh (select with apply=1) that installs the set ``idx`` [B][Hkv][k]
+    into ``cache`` as it stands, counted per head from the positions before the refresh.
+    min_bytes: what any refresh must move -- the new anchors' sources (bf16 rows of kept anchors
+    and staged tokens, quantized slots of promoted positions) and their bf16 rows written, the
+    demoted rows read (bf16) and written as slots, the tail slots moved down (read + write), and
+    the position arrays.  moved_bytes adds this design's extra traffic: the new anchor rows pass
+    through a temporary store (written once, read once more), the V-code dwords of every quad a
+    move touches are read and written whole, the plan reads the slot positions and writes its
+    bitmaps and move list."""
+    s = cache.shape
+    c = cache.counters()
+    B, Hkv = idx.shape[0], idx.shape[1]
+    L = c["len"]
+    P = max(0, L - W)
+    n_old, n_anc, n_st = c["n_int4"], c["n_anchor"], c["n_staged"]
+    bk = s.bits or 4
+    bv = s.bits_v or bk
+    slot = (512 * (bk + bv) + 1024) // 32
+    a_pos = cache.view("a_pos", torch.int32).view(B * Hkv, s.anchor_cap)[:, :n_anc].cpu().numpy()
+    s_pos = cache.view("slot_pos", torch.int32).view(B * Hkv, s.int4_cap)[:, :n_old].cpu().numpy()
+    new = idx.reshape(B * Hkv, -1).cpu().numpy()
+    import numpy as np
+    k = new.shape[1]
+    tot = {"demoted": 0, "promoted": 0, "kept": 0, "tail_moves": 0, "tiles_touched": 0}
+    mn, mv = 0, 0
+    for h in range(B * Hkv):
+        nset = np.zeros(max(P, 1), dtype=bool)
+        nset[new[h]] = True
+        kept_a = int(nset[a_pos[h]].sum())
+        staged = np.arange(P - n_st, P)
+        kept_s = int(nset[staged].sum())
+        dele = nset[s_pos[h]]
+        p = int(dele.sum())
+        e = (n_anc - kept_a) + (n_st - kept_s)
+        n_new = n_old - p + e
+        tail = int((~dele[n_new:n_old]).sum()) if n_new < n_old else 0
+        holes = np.nonzero(dele[:min(n_new, n_old)])[0]
+        dst = np.concatenate([holes, np.arange(n_old, max(n_new, n_old))])
+        tiles = len(np.unique(dst >> 5))
+        quads = len(np.unique((dst >> 5) * 4 + ((dst & 15) >> 2)))
+        tot["demoted"] += e
+        tot["promoted"] += p
+        tot["kept"] += kept_a + kept_s
+        tot["tail_moves"] += tail
+        tot["tiles_touched"] += tiles
+        row = 2 * D * 2  # a bf16 K row and V row
+        a_end = (k + 31) // 32 * 32
+        m = (kept_a + kept_s) * row + p * slot + k * row  # new anchors: sources read, rows written
+        m += e * (row + slot) + tail * 2 * slot + 4 * (k + n_anc + a_end + e + tail)
+        mn += m
+        vq = 512 * bv // 4  # bytes of one quad's V codes (all channels)
+        mv += m + 2 * k * row + 2 * quads * vq + 4 * n_old + 12 * len(dst)
+    return {"min_bytes": mn, "moved_bytes": mv, **tot, "heads": B * Hkv, "k": k}
 
 
 def bench_decode_bs1(torch, hq, gen, dev, ctxs=(1024, 4096, 16384, 32768), Hq=32, Hkv=8, layers=36, steps=100,

@@ -273,6 +273,7 @@ struct HeadWork {
   const uint16_t *a_k, *a_v, *s_k, *s_v, *w_k, *w_v;
   const uint16_t* q;
   float* rec;
+  float* out;  // with a single split: the group's output rows, written directly (no merge launch)
   int n_int4, n_anchor, n_staged, n_win;
   int n_splits, split;
 };
@@ -328,7 +329,7 @@ __device__ inline HeadWork head_work(const DecodeParams& p, const Unit& u) {
   const int hkv = u.hkv;
   const size_t hb = (size_t)u.b * p.Hkv + hkv;
   const size_t qh = (size_t)u.b * p.Hkv * p.G + (size_t)hkv * p.G;
-  HeadWork h;
+  HeadWork h = {};
   h.int4 = p.int4 + hb * (size_t)p.int4_cap * QL<BK, BV>::SLOT;
   h.a_k = p.a_k + hb * (size_t)p.anchor_cap * D;
   h.a_v = p.a_v + hb * (size_t)p.anchor_cap * D;
@@ -338,6 +339,7 @@ __device__ inline HeadWork head_work(const DecodeParams& p, const Unit& u) {
   h.w_v = p.w_v + hb * (size_t)WIN * D;
   h.q = p.q + qh * D;
   h.rec = p.part + qh * p.n_splits * (D + 2);
+  h.out = p.n_splits == 1 ? p.o + qh * D : nullptr;
   h.n_int4 = p.n_int4;
   h.n_anchor = p.n_anchor;
   h.n_staged = p.n_staged;
@@ -355,7 +357,7 @@ __device__ inline HeadWork head_work(const RaggedDecodeParams& p, const Unit& u)
   const uint32_t m = p.split_map[blockIdx.x];
   const int seq = (int)(m >> 16);
   const RaggedSeq& d = p.seqs[seq];
-  HeadWork h;
+  HeadWork h = {};
   h.int4 = d.int4 + (size_t)hkv * d.int4_cap * QL<BK, BV>::SLOT;
   h.a_k = d.a_k + (size_t)hkv * d.anchor_cap * D;
   h.a_v = d.a_v + (size_t)hkv * d.anchor_cap * D;
@@ -365,6 +367,7 @@ __device__ inline HeadWork head_work(const RaggedDecodeParams& p, const Unit& u)
   h.w_v = d.w_v + (size_t)hkv * WIN * D;
   h.q = p.q + ((size_t)seq * p.Hkv * p.G + (size_t)hkv * p.G) * D;
   h.rec = p.part + ((size_t)d.rec0 + (size_t)hkv * p.G * d.n_splits) * (D + 2);
+  h.out = nullptr;  // a variable-length batch always merges its records
   h.n_int4 = d.n_int4;
   h.n_anchor = d.n_anchor;
   h.n_staged = d.n_staged;
@@ -580,6 +583,11 @@ __global__ __launch_bounds__(64 * NWAVES) void decode_split_kernel(Params p) {
         L += red_l[ww][h2] * f;
       }
     }
+    if (hw.out) {
+      // the merge of one record, as the merge computes it (weight exp2(0) = 1)
+      hw.out[(size_t)hd * D + c] = __builtin_fmaf(O, 1.0f, 0.0f) / L;
+      continue;
+    }
     float* rec = hw.rec + ((size_t)hd * hw.n_splits + hw.split) * (D + 2);
     if (c == 0) { rec[0] = M; rec[1] = L; }
     rec[2 + c] = O;
@@ -729,6 +737,7 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
     return hipGetLastError();
   });
   if (e != hipSuccess) return e;
+  if (p.n_splits == 1) return hipSuccess;  // the split kernel wrote the outputs
   hipLaunchKernelGGL(decode_reduce_kernel<false>, dim3(p.B * p.Hkv * p.G), dim3(64), 0, stream, p.part, p.o,
                      p.n_splits, (const RaggedSeq*)nullptr, p.Hkv * p.G);
   return hipGetLastError();

@@ -350,10 +350,11 @@ __global__ __launch_bounds__(256) void refresh_gather_kernel(RefreshParams p) {
 // covers a chunk plus the longest run, so a wave reads its part of the list once.
 //
 // A V code shares its dword with the other slots of its quad only (every width), so the owner
-// of a tile is the only writer of that tile's V-code dwords: it loads the dwords of the quads
-// its moves touch into registers (lane = 32 + 8 g + sub keeps channels 32 g + 4 sub + e,
-// e < 4, the same lanes that quantize those channels), replaces the codes there, and stores the
-// dwords back -- plain loads and stores, no atomics.  Kept codes of slots nobody moves are
+// of a tile is the only writer of that tile's V-code dwords: it copies the dwords of the quads
+// its moves touch into LDS (lane = 32 + 8 g + sub keeps those of channels 32 g + 4 sub + e,
+// e < 4 -- the channels it quantizes -- in a column only it reads and writes, indexed by quad,
+// e and half), replaces the codes there, and stores the dwords back -- plain loads and
+// stores, no atomics.  Kept codes of slots nobody moves are
 // written back unchanged (a tail slot read as a source by another wave keeps its value).  A
 // 2-bit dword also spans channels c and c + 16 (lanes sub and sub + 4): those two lanes'
 // copies are merged before the store.
@@ -383,6 +384,13 @@ struct MoveSrc {
   int32_t pos;
 };
 
+// Offsets inside one head's slab fit 32 bits; computing them as such keeps the address math
+// off the 64-bit path.
+template <typename T>
+__device__ inline const T* at32(const void* base, size_t off) {
+  return (const T*)((const uint8_t*)base + (uint32_t)off);
+}
+
 template <int BK, int BV>
 __device__ inline MoveSrc load_move(const RefreshParams& p, int hb, int kind, int src, int lane, const uint8_t* slab,
                                     const int32_t* slot_pos, int ps0) {
@@ -396,29 +404,29 @@ __device__ inline MoveSrc load_move(const RefreshParams& p, int hb, int kind, in
     const uint16_t* sk = kind == 0 ? p.a_k + hb * aslab : p.s_k + hb * sslab;
     const uint16_t* sv = kind == 0 ? p.a_v + hb * aslab : p.s_v + hb * sslab;
     if (kv == 0) {
-      const uint2 raw = *(const uint2*)(sk + kbf_index(src, c0));
+      const uint2 raw = *at32<uint2>(sk, 2 * kbf_index(src, c0));
       m.r[0] = raw.x;
       m.r[1] = raw.y;
     } else {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) m.r[e] = sv[vbf_index(src, c0 + e)];
+      for (int e = 0; e < 4; ++e) m.r[e] = *at32<uint16_t>(sv, 2 * vbf_index(src, c0 + e));
     }
     if (lane == 0) m.pos = kind == 0 ? p.a_pos[hb * (size_t)p.anchor_cap + src] : ps0 + src;
   } else {
     // quantized slot: K lanes sub < BK read dword sub of the group's K chunk, lane sub 0 the
     // group's (scale, min); V lanes read the dwords holding their 4 channels' codes
     if (kv == 0) {
-      if (sub < BK) m.r[0] = *(const uint32_t*)(slab + kcode_chunk_b<BK, BV>(src, g) + 4 * sub);
-      if (sub == 0) m.sm = *(const uint32_t*)(slab + ksm_byte_b<BK, BV>(src, g));
+      if (sub < BK) m.r[0] = *at32<uint32_t>(slab, kcode_chunk_b<BK, BV>(src, g) + 4 * sub);
+      if (sub == 0) m.sm = *at32<uint32_t>(slab, ksm_byte_b<BK, BV>(src, g));
     } else {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         size_t off;
         int sh;
         vcode_loc<BK, BV>(src, c0 + e, off, sh);
-        m.r[e] = *(const uint32_t*)(slab + off);
+        m.r[e] = *at32<uint32_t>(slab, off);
       }
-      if (sub == 0) m.sm = *(const uint32_t*)(slab + vsm_byte_b<BK, BV>(src, g));
+      if (sub == 0) m.sm = *at32<uint32_t>(slab, vsm_byte_b<BK, BV>(src, g));
     }
     if (lane == 0) m.pos = slot_pos[src];
   }
@@ -428,7 +436,10 @@ __device__ inline MoveSrc load_move(const RefreshParams& p, int hb, int kind, in
 template <int BK, int BV>
 __global__ __launch_bounds__(64 * MOVE_WAVES) void refresh_move_kernel(RefreshParams p) {
   constexpr int NH = BV == 8 ? 2 : 1;  // V-code dwords per (quad, channel): INT8 codes take two
+  constexpr int NSLOT = 16 * NH;       // owned dwords per V lane: (quad, channel e, half)
   constexpr uint32_t VMASK = (1u << BV) - 1u;
+  // the owned V-code dwords, one column per V lane: [slot (quad, e, half)][lane - 32]
+  __shared__ uint32_t vbuf[MOVE_WAVES][NSLOT][32];
   const int hb = blockIdx.y, lane = threadIdx.x & 63;
   const Scratch s = scratch(p, hb);
   const int n = min(s.cnt[0], p.max_moves);
@@ -440,6 +451,8 @@ __global__ __launch_bounds__(64 * MOVE_WAVES) void refresh_move_kernel(RefreshPa
   int32_t* slot_pos = p.slot_pos + hb * (size_t)p.int4_cap;
   const int kv = lane >> 5, g = (lane >> 3) & 3, sub = lane & 7, c0 = 32 * g + 4 * sub;
   const int n_tiles = p.int4_cap >> 5;
+  uint32_t* vb = &vbuf[threadIdx.x >> 6][0][lane & 31];
+  auto vslot = [](int q, int e, int h) { return ((q * 4 + e) * NH + h) * 32; };
 
   // the list window: lane i holds entry lo - 1 + i
   const int me = lo - 1 + lane;
@@ -458,7 +471,6 @@ __global__ __launch_bounds__(64 * MOVE_WAVES) void refresh_move_kernel(RefreshPa
   const int j_end = later ? __builtin_ctzll(later) : min(64, n - (lo - 1));
 
   MoveSrc nxt = load_move<BK, BV>(p, hb, __shfl(wkind, j0), __shfl(wsrc, j0), lane, slab, slot_pos, ps0);
-  uint32_t vq[4][4][NH];
   int tile = -1;
   uint32_t qmask = 0;
   for (int j = j0; j < j_end; ++j) {
@@ -468,7 +480,7 @@ __global__ __launch_bounds__(64 * MOVE_WAVES) void refresh_move_kernel(RefreshPa
     const MoveSrc cur = nxt;
     if (j + 1 < j_end) nxt = load_move<BK, BV>(p, hb, __shfl(wkind, j + 1), __shfl(wsrc, j + 1), lane, slab, slot_pos, ps0);
     if ((dst >> 5) != tile) {
-      // a new tile: the quads its moves touch, their V-code dwords into registers
+      // a new tile: the quads its moves touch, their V-code dwords into this lane's column
       tile = dst >> 5;
       const bool mine = lane >= j && lane < j_end && wtile == tile && wdst >= 0;
       qmask = 0;
@@ -480,6 +492,7 @@ __global__ __launch_bounds__(64 * MOVE_WAVES) void refresh_move_kernel(RefreshPa
 #pragma unroll
         for (int qq = 0; qq < 4; ++qq)
           if (qmask >> qq & 1u) {
+            uint32_t w[4][NH];
 #pragma unroll
             for (int e = 0; e < 4; ++e)
 #pragma unroll
@@ -487,8 +500,12 @@ __global__ __launch_bounds__(64 * MOVE_WAVES) void refresh_move_kernel(RefreshPa
                 size_t off;
                 int sh;
                 vcode_loc<BK, BV>(32 * tile + 4 * qq + 16 * hh, c0 + e, off, sh);
-                vq[qq][e][hh] = *(const uint32_t*)(slab + off);
+                w[e][hh] = *at32<uint32_t>(slab, off);
               }
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+#pragma unroll
+              for (int hh = 0; hh < NH; ++hh) vb[vslot(qq, e, hh)] = w[e][hh];
           }
       }
     }
@@ -526,31 +543,31 @@ __global__ __launch_bounds__(64 * MOVE_WAVES) void refresh_move_kernel(RefreshPa
         }
         const uint32_t smw = (uint32_t)__half_as_ushort(s16) | ((uint32_t)__half_as_ushort(m16) << 16);
         if (kv == 0) {
+          uint32_t* kc = (uint32_t*)(slab + (uint32_t)kcode_chunk_b<BK, BV>(dst, g));
           if constexpr (BK == 4) {
             // nibbles 4 sub + e of the group's 32; dword sub / 2 holds lanes sub & ~1 (low) and | 1
             const uint32_t half16 = code[0] | (code[1] << 4) | (code[2] << 8) | (code[3] << 12);
             const uint32_t other = (uint32_t)__float_as_int(shfl_xor_f(__int_as_float((int)half16), 1));
-            if ((sub & 1) == 0) *(uint32_t*)(slab + kcode_chunk_b<BK, BV>(dst, g) + 4 * (sub >> 1)) = half16 | (other << 16);
+            if ((sub & 1) == 0) kc[sub >> 1] = half16 | (other << 16);
           } else if constexpr (BK == 8) {
             // bytes 4 sub + e of the group's 32: one dword per lane
-            *(uint32_t*)(slab + kcode_chunk_b<BK, BV>(dst, g) + 4 * sub) =
-                code[0] | (code[1] << 8) | (code[2] << 16) | (code[3] << 24);
+            kc[sub] = code[0] | (code[1] << 8) | (code[2] << 16) | (code[3] << 24);
           } else {
             // 2-bit codes 4 sub + e: byte sub & 3 of dword sub / 4, OR-ed over the dword's 4 lanes
             uint32_t w = (code[0] | (code[1] << 2) | (code[2] << 4) | (code[3] << 6)) << (8 * (sub & 3));
             w |= (uint32_t)__float_as_int(shfl_xor_f(__int_as_float((int)w), 1));
             w |= (uint32_t)__float_as_int(shfl_xor_f(__int_as_float((int)w), 2));
-            if ((sub & 3) == 0) *(uint32_t*)(slab + kcode_chunk_b<BK, BV>(dst, g) + 4 * (sub >> 2)) = w;
+            if ((sub & 3) == 0) kc[sub >> 2] = w;
           }
-          if (sub == 0) *(uint32_t*)(slab + ksm_byte_b<BK, BV>(dst, g)) = smw;
+          if (sub == 0) *(uint32_t*)(slab + (uint32_t)ksm_byte_b<BK, BV>(dst, g)) = smw;
         } else if (sub == 0) {
-          *(uint32_t*)(slab + vsm_byte_b<BK, BV>(dst, g)) = smw;
+          *(uint32_t*)(slab + (uint32_t)vsm_byte_b<BK, BV>(dst, g)) = smw;
         }
       } else {
         // move a quantized slot: K chunk dwords and (scale, min) as read, V codes re-placed
         if (kv == 0) {
-          if (sub < BK) *(uint32_t*)(slab + kcode_chunk_b<BK, BV>(dst, g) + 4 * sub) = cur.r[0];
-          if (sub == 0) *(uint32_t*)(slab + ksm_byte_b<BK, BV>(dst, g)) = cur.sm;
+          if (sub < BK) *(uint32_t*)(slab + (uint32_t)(kcode_chunk_b<BK, BV>(dst, g) + 4 * sub)) = cur.r[0];
+          if (sub == 0) *(uint32_t*)(slab + (uint32_t)ksm_byte_b<BK, BV>(dst, g)) = cur.sm;
         } else {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
@@ -559,7 +576,7 @@ __global__ __launch_bounds__(64 * MOVE_WAVES) void refresh_move_kernel(RefreshPa
             vcode_loc<BK, BV>(src, c0 + e, off, sh);
             code[e] = (cur.r[e] >> sh) & VMASK;
           }
-          if (sub == 0) *(uint32_t*)(slab + vsm_byte_b<BK, BV>(dst, g)) = cur.sm;
+          if (sub == 0) *(uint32_t*)(slab + (uint32_t)vsm_byte_b<BK, BV>(dst, g)) = cur.sm;
         }
       }
       if (kv == 1) {
@@ -570,11 +587,8 @@ __global__ __launch_bounds__(64 * MOVE_WAVES) void refresh_move_kernel(RefreshPa
           size_t off;
           int sh;
           vcode_loc<BK, BV>(dst, c0 + e, off, sh);
-#pragma unroll
-          for (int qq = 0; qq < 4; ++qq)
-#pragma unroll
-            for (int hh = 0; hh < NH; ++hh)
-              if (qq == q && hh == h) vq[qq][e][hh] = (vq[qq][e][hh] & ~(VMASK << sh)) | (code[e] << sh);
+          uint32_t* w = &vb[vslot(q, e, h)];
+          *w = (*w & ~(VMASK << sh)) | (code[e] << sh);
         }
       }
       if (lane == 0) slot_pos[dst] = cur.pos;
@@ -592,13 +606,14 @@ __global__ __launch_bounds__(64 * MOVE_WAVES) void refresh_move_kernel(RefreshPa
                 size_t off;
                 int sh;
                 vcode_loc<BK, BV>(32 * tile + 4 * qq + 16 * hh, c0 + e, off, sh);
+                const uint32_t w = vb[vslot(qq, e, hh)];
                 if constexpr (BV == 2) {
                   // a 2-bit dword holds channels c (bytes 0 and 2) and c + 16 (bytes 1 and 3):
                   // lanes sub and sub + 4 edit one each; the merged dword goes out once
-                  const uint32_t other = (uint32_t)__shfl_xor((int)vq[qq][e][hh], 4);
-                  if (sub < 4) *(uint32_t*)(slab + off) = (vq[qq][e][hh] & 0x00FF00FFu) | (other & 0xFF00FF00u);
+                  const uint32_t other = (uint32_t)__shfl_xor((int)w, 4);
+                  if (sub < 4) *(uint32_t*)(slab + (uint32_t)off) = (w & 0x00FF00FFu) | (other & 0xFF00FF00u);
                 } else {
-                  *(uint32_t*)(slab + off) = vq[qq][e][hh];
+                  *(uint32_t*)(slab + (uint32_t)off) = w;
                 }
               }
           }
