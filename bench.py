@@ -66,6 +66,9 @@ def parse():
                     help="run only the GQA-8 decode row (64 Q / 8 KV heads, bs4 x 32K)")
     ap.add_argument("--only-prefill", action="store_true",
                     help="run only the hybrid-prefill rows (for profiling the prefill kernels)")
+    ap.add_argument("--only-bs1", action="store_true",
+                    help="run only the batch-1 decode sweep (for a kernel trace of its launches)")
+    ap.add_argument("--bs1-ctxs", default="1024,4096,16384,32768")
     return ap.parse_args()
 
 
@@ -877,6 +880,12 @@ def main():
         gen.manual_seed(args.seed)
         print(json.dumps({"rows": {"decode_gqa8": bench_decode_gqa8(torch, hq, gen, dev,
                                                                      copy_cal=args.copy_calibration)}}), flush=True)
+        return
+    if args.only_bs1:
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(args.seed)
+        ctxs = tuple(int(x) for x in args.bs1_ctxs.split(",") if x)
+        print(json.dumps({"rows": {"decode_bs1": bench_decode_bs1(torch, hq, gen, dev, ctxs=ctxs)}}), flush=True)
         return
     if args.only_prefill:
         gen = torch.Generator(device=dev)
