@@ -37,7 +37,9 @@ def parse():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[1])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=300,
+                    help="untimed steps before the timed loop; from idle the device needs about 30 ms of "
+                         "sustained load (about 300 steps) to reach its steady rate")
     ap.add_argument("--batch", type=int, default=16)
     ap.add_argument("--ctx", type=int, default=32768)
     ap.add_argument("--layers", type=int, default=36)
@@ -159,6 +161,21 @@ def algorithmic_bytes(cache, B, Hkv, Hq):
     slot = (512 * ((sh.bits or 4) + (sh.bits_v or sh.bits or 4)) + 1024) // 32  # codes + fp16 scale/min per token
     per_head = slot * c["n_int4"] + 512 * (c["n_anchor"] + c["n_staged"] + n_win)
     return B * Hkv * per_head + B * Hq * D * (2 + 4)
+
+
+def settle(torch, fn, ms=40.0):
+    """Run fn back to back for about ``ms`` of device time before a timed region: from idle the
+    device needs tens of milliseconds of sustained load to reach its steady rate (the first
+    100 batched decode steps after an idle second run about 1.6x slower than steady state)."""
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    fn()
+    b.record()
+    torch.cuda.synchronize()
+    us = max(a.elapsed_time(b) * 1e3, 1.0)
+    for _ in range(int(min(4000, max(4, ms * 1e3 / us)))):
+        fn()
+    torch.cuda.synchronize()
 
 
 def timed(torch, fn, reps, warm=2):
@@ -340,9 +357,8 @@ def bench_decode_bs1(torch, hq, gen, dev, ctxs=(1024, 4096, 16384, 32768), Hq=32
         nbytes = algorithmic_bytes(lay[0][0], B, Hkv, Hq)
         ws = hq.decode_workspace(shape, 0, dev)
         o = torch.empty(B, Hq, D, dtype=torch.float32, device=dev)
-        for i in range(10):
-            hq.decode_attn(lay[i % layers][0], lay[i % layers][1], 0, o, ws)
-        torch.cuda.synchronize()
+        rot = iter(range(1 << 30))
+        settle(torch, lambda: hq.decode_attn(*lay[next(rot) % layers], 0, o, ws))
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for i in range(steps):
@@ -409,8 +425,8 @@ def bench_decode_bits(torch, hq, gen, dev, B=16, L=32768, Hq=32, Hkv=8, layers=8
         # back-to-back launches with events only at the ends, as in the headline loop (a batched
         # step is long enough that queued launches hide the binding's host cost)
         steps = 200
-        for i in range(40):  # warm-up long enough for the clocks to settle
-            hq.decode_attn(*lay[i % layers], 0, o, ws)
+        rot = iter(range(1 << 30))
+        settle(torch, lambda: hq.decode_attn(*lay[next(rot) % layers], 0, o, ws))
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         e0.record()
@@ -441,9 +457,8 @@ def bench_decode_gqa8(torch, hq, gen, dev, B=4, L=32768, Hq=64, Hkv=8, layers=16
     nbytes = algorithmic_bytes(lay[0][0], B, Hkv, Hq)
     ws = hq.decode_workspace(shape, 0, dev)
     o = torch.empty(B, Hq, D, dtype=torch.float32, device=dev)
-    for i in range(20):
-        hq.decode_attn(lay[i % layers][0], lay[i % layers][1], 0, o, ws)
-    torch.cuda.synchronize()
+    rot = iter(range(1 << 30))
+    settle(torch, lambda: hq.decode_attn(*lay[next(rot) % layers], 0, o, ws))
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for i in range(steps):
@@ -494,9 +509,12 @@ def bench_decode_ragged(torch, hq, gen, dev, n_seq=16, Hq=32, Hkv=8, layers=4, s
     ws = torch.empty(hq.decode_ragged_workspace_bytes(lay[0][0][0].shape, n_seq), dtype=torch.uint8, device=dev)
     o = torch.empty(n_seq, Hq, D, dtype=torch.float32, device=dev)
     steps = 200
-    for i in range(40):  # warm-up long enough for the clocks to settle
-        hq.decode_attn_ragged(lay[i % layers][0], lay[i % layers][1], 0, o, ws)
-    torch.cuda.synchronize()
+    rot = iter(range(1 << 30))
+
+    def one():
+        i = next(rot) % layers
+        hq.decode_attn_ragged(lay[i][0], lay[i][1], 0, o, ws)
+    settle(torch, one)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for i in range(steps):
@@ -557,6 +575,7 @@ def bench_selector(torch, hq, gen, dev, B=4, Hq=64, Hkv=8, L=32768):
     shape = hq.Shape.for_context(B, Hq, Hkv, L + 64, 10)
     cache, _ = make_layer(torch, hq, shape, B, Hkv, G, L, gen, dev)
     res = {"workload": f"qwen3-32b-shape select bs{B} ctx{L} hq{Hq} hkv{Hkv}"}
+    settle(torch, lambda: hq.select_vlines(shape, hq.anchor_count(L, 5), cache=cache))
     for pct in (1, 5, 10):
         k = hq.anchor_count(L, pct)
         us, _ = timed(torch, lambda: hq.select_vlines(shape, k, cache=cache), 5)
@@ -703,8 +722,9 @@ def bench_prefill(torch, hq, gen, dev, N, Hq=32, Hkv=8, bulk="int8"):
     ws = hq.prefill_workspace(shape, N, dev)
     o = torch.empty(Hq, N, D, dtype=torch.float32, device=dev)
     reps = 10 if N <= 8192 else 3
-    us, us_min = timed(torch, lambda: hq.prefill_attn(shape, Q, K, V, anchors=anchors, out=o, ws=ws, bulk=bulk),
-                       reps)
+    call = lambda: hq.prefill_attn(shape, Q, K, V, anchors=anchors, out=o, ws=ws, bulk=bulk)  # noqa: E731
+    settle(torch, call)
+    us, us_min = timed(torch, call, reps)
     ops8, opsb = prefill_ops(anchors[0].cpu().numpy(), N, Hq)
     if bulk == "mxfp4":  # Q.K^T half of the bulk work at the fp4 peak, P.V half at fp8
         t_roof = 0.5 * ops8 / 10.1e15 + 0.5 * ops8 / 5.0e15 + opsb / 2.5e15
