@@ -2,8 +2,9 @@
 //
 // Query i attends, causally, to three key sets: the window [i-127, i] and the anchors
 // a <= i-128 in bf16, and every other key j <= i-128 through INT8 Q.K and FP8 P.V.  The pass
-// is split into operand quantization (Alg. 2 Stage 2: four small kernels writing codes and
-// scales into the caller's workspace) and one attention kernel (Alg. 2 Stage 3) that runs a
+// is split into operand quantization (Alg. 2 Stage 2: three small kernels writing codes,
+// scales, the anchor bitmap and the gathered anchor rows into the caller's workspace) and one
+// attention kernel (Alg. 2 Stage 3) that runs a
 // single online softmax per query row over 64-key tiles in the order: quantized tiles,
 // anchor tiles, window tiles.
 //
@@ -93,28 +94,6 @@ __device__ inline void col4_max2_f(float& a, float& b) {
 
 // ------------------------------------------------------------------ operand quantization
 
-// Anchor bitmap: bit (j & 31) of word j >> 5 is set for every listed anchor j.
-__global__ void __launch_bounds__(256) pf_bitmap_kernel(PrefillParams p) {
-  const int h = blockIdx.x;
-  const int nw = p.Npad >> 5;
-  const int32_t* anc = p.anchors + (size_t)h * p.n_anchor;
-  for (int w = threadIdx.x; w < nw; w += blockDim.x) {
-    const int lo_key = 32 * w;
-    int lo = 0, hi = p.n_anchor;
-    while (lo < hi) {
-      const int mid = (lo + hi) >> 1;
-      if (anc[mid] < lo_key) lo = mid + 1; else hi = mid;
-    }
-    uint32_t bits = 0;
-    for (int i = lo; i < p.n_anchor; ++i) {
-      const int a = anc[i];
-      if (a < lo_key || a >= lo_key + 32) break;
-      bits |= 1u << (a - lo_key);
-    }
-    p.abits[(size_t)h * nw + w] = bits;
-  }
-}
-
 // MXFP4 block of 32 values held by one lane: shared exponent e = floor(log2 max|x|) - 2
 // (E8M0 range, -127 for a zero block) and E2M1 codes of x * 2^-e (exact scaling; the
 // hardware conversion rounds to nearest even and saturates at 6), element i in nibble i of
@@ -142,18 +121,67 @@ __device__ inline int mxfp4_block(const float (&x)[32], u32x4& codes) {
   return e;
 }
 
-// K: per (KV head, 64-key block) symmetric INT8 with the anchors left out of the maximum
-// (BULK 0), or MXFP4 per key and 32-channel block (BULK 1: every row, anchors included);
-// V: per-channel maximum of |V| over the block's non-anchor keys.
+// Anchor gather: K rows (list order) and V^T in the bf16 operand order for the 32 list
+// entries of tile b (channel c per thread); entries past n_anchor (or outside [0, N)) are zero.
+__device__ inline void anchor_gather(const PrefillParams& p, int b, int h, int c) {
+  const int32_t* anc = p.anchors + (size_t)h * p.n_anchor;
+  const int Ac = p.n_anchor_pad;
+  uint32_t raw[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) raw[i] = 0;
+#pragma unroll
+  for (int kk = 0; kk < 32; ++kk) {
+    const int idx = 32 * b + kk;
+    const int a = idx < p.n_anchor ? anc[idx] : -1;
+    uint16_t kb = 0, vb = 0;
+    if (a >= 0 && a < p.N) {
+      kb = p.k[((size_t)h * p.N + a) * D + c];
+      vb = p.v[((size_t)h * p.N + a) * D + c];
+    }
+    p.ka16[((size_t)h * Ac + idx) * D + c] = kb;
+    raw[kk >> 1] |= (uint32_t)vb << (16 * (kk & 1));
+  }
+  uint16_t* tblk = p.va16 + ((size_t)h * (Ac >> 5) + b) * D * 32;
+#pragma unroll
+  for (int g = 0; g < 4; ++g)
+    *(u32x4*)(tblk + (g * D + c) * 8) = (u32x4){raw[4 * g], raw[4 * g + 1], raw[4 * g + 2], raw[4 * g + 3]};
+}
+
+// One launch for the operands that need no global reduction.  Workgroups x < Npad / 64, per
+// (KV head, 64-key block):
+//   * the block's two words of the anchor bitmap (bit (j & 31) of word j >> 5 set for every
+//     listed anchor j; the threads scan the sorted list side by side);
+//   * K: symmetric INT8 with the anchors left out of the maximum (BULK 0), or MXFP4 per key
+//     and 32-channel block (BULK 1: every row, anchors included);
+//   * V: per-channel maximum of |V| over the block's non-anchor keys.
+// The workgroups after those gather two 32-entry tiles of the anchor list each.
 template <int BULK>
 __global__ void __launch_bounds__(256) pf_kquant_kernel(PrefillParams p) {
   __shared__ float red[4];
   __shared__ float vt[64][129];
+  __shared__ uint32_t bw[2];
   const int blk = blockIdx.x, h = blockIdx.y;
   const int t = threadIdx.x, row = t >> 2, qd = t & 3;
-  const int key = blk * KBLK + row;
   const int nw = p.Npad >> 5, nb = p.Npad >> 6;
-  const uint32_t word = p.abits[(size_t)h * nw + (key >> 5)];
+  if (blk >= nb) {  // anchor gather: tiles 2 (blk - nb) and 2 (blk - nb) + 1
+    const int b = 2 * (blk - nb) + (t >> 7);
+    if (32 * b < p.n_anchor_pad) anchor_gather(p, b, h, t & (D - 1));
+    return;
+  }
+  const int key = blk * KBLK + row;
+  if (t < 2) bw[t] = 0u;
+  __syncthreads();
+  {
+    const int32_t* anc = p.anchors + (size_t)h * p.n_anchor;
+    const int lo_key = blk * KBLK;
+    for (int i = t; i < p.n_anchor; i += 256) {
+      const int a = anc[i];
+      if (a >= lo_key && a < lo_key + KBLK) atomicOr(&bw[(a - lo_key) >> 5], 1u << (a & 31));
+    }
+  }
+  __syncthreads();
+  if (t < 2) p.abits[(size_t)h * nw + 2 * blk + t] = bw[t];
+  const uint32_t word = bw[row >> 5];
   const bool inside = key < p.N;
   const bool live = inside && !((word >> (key & 31)) & 1u);
   float kx[32], vx[32];
@@ -220,7 +248,13 @@ __global__ void __launch_bounds__(1024) pf_vscale_kernel(PrefillParams p) {
   const int h = blockIdx.x, c = threadIdx.x & (D - 1), g = threadIdx.x >> 7;
   const int nb = p.Npad >> 6;
   float m = 0.0f;
-  for (int b = g; b < nb; b += 8) m = fmaxf(m, p.vmax[((size_t)h * nb + b) * D + c]);
+  for (int b0 = g; b0 < nb; b0 += 64) {  // eight loads in flight per thread
+    float x[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) x[u] = b0 + 8 * u < nb ? p.vmax[((size_t)h * nb + b0 + 8 * u) * D + c] : 0.0f;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) m = fmaxf(m, x[u]);
+  }
   part[g][c] = m;
   __syncthreads();
   if (g == 0) {
@@ -261,33 +295,6 @@ __global__ void __launch_bounds__(128) pf_vquant_kernel(PrefillParams p) {
 #pragma unroll
   for (int hh = 0; hh < 2; ++hh)
     *(u32x4*)(blk + (hh * D + c) * 16) = (u32x4){w[4 * hh], w[4 * hh + 1], w[4 * hh + 2], w[4 * hh + 3]};
-#pragma unroll
-  for (int g = 0; g < 4; ++g)
-    *(u32x4*)(tblk + (g * D + c) * 8) = (u32x4){raw[4 * g], raw[4 * g + 1], raw[4 * g + 2], raw[4 * g + 3]};
-}
-
-// Anchor gather: K rows (list order) and V^T in the bf16 operand order, for list entries
-// [0, n_anchor_pad); entries past n_anchor (or outside [0, N)) are zero.
-__global__ void __launch_bounds__(128) pf_agather_kernel(PrefillParams p) {
-  const int b = blockIdx.x, h = blockIdx.y, c = threadIdx.x;
-  const int32_t* anc = p.anchors + (size_t)h * p.n_anchor;
-  const int Ac = p.n_anchor_pad;
-  uint32_t raw[16];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) raw[i] = 0;
-#pragma unroll
-  for (int kk = 0; kk < 32; ++kk) {
-    const int idx = 32 * b + kk;
-    const int a = idx < p.n_anchor ? anc[idx] : -1;
-    uint16_t kb = 0, vb = 0;
-    if (a >= 0 && a < p.N) {
-      kb = p.k[((size_t)h * p.N + a) * D + c];
-      vb = p.v[((size_t)h * p.N + a) * D + c];
-    }
-    p.ka16[((size_t)h * Ac + idx) * D + c] = kb;
-    raw[kk >> 1] |= (uint32_t)vb << (16 * (kk & 1));
-  }
-  uint16_t* tblk = p.va16 + ((size_t)h * (Ac >> 5) + b) * D * 32;
 #pragma unroll
   for (int g = 0; g < 4; ++g)
     *(u32x4*)(tblk + (g * D + c) * 8) = (u32x4){raw[4 * g], raw[4 * g + 1], raw[4 * g + 2], raw[4 * g + 3]};
@@ -965,15 +972,14 @@ __global__ void __launch_bounds__(256, 2) pf_attn_kernel(PrefillParams p) {
 
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream) {
   const int Hkv = p.Hkv;
-  hipLaunchKernelGGL(pf_bitmap_kernel, dim3(Hkv), dim3(256), 0, stream, p);
+  // K quantization and bitmap per 64-key block, then the anchor gather (two tiles per workgroup)
+  const dim3 g1(p.Npad / KBLK + (p.n_anchor_pad / 32 + 1) / 2, Hkv);
   if (p.bulk == 1)
-    hipLaunchKernelGGL(pf_kquant_kernel<1>, dim3(p.Npad / KBLK, Hkv), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL(pf_kquant_kernel<1>, g1, dim3(256), 0, stream, p);
   else
-    hipLaunchKernelGGL(pf_kquant_kernel<0>, dim3(p.Npad / KBLK, Hkv), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL(pf_kquant_kernel<0>, g1, dim3(256), 0, stream, p);
   hipLaunchKernelGGL(pf_vscale_kernel, dim3(Hkv), dim3(1024), 0, stream, p);
   hipLaunchKernelGGL(pf_vquant_kernel, dim3(p.Npad / 32, Hkv), dim3(128), 0, stream, p);
-  if (p.n_anchor_pad > 0)
-    hipLaunchKernelGGL(pf_agather_kernel, dim3(p.n_anchor_pad / 32, Hkv), dim3(128), 0, stream, p);
   if (p.bulk == 1)
     hipLaunchKernelGGL(pf_attn_kernel<1>, dim3((p.Npad / WG_ROWS) * p.Hq), dim3(256), 0, stream, p);
   else
