@@ -154,54 +154,64 @@ __device__ inline void anchor_gather(const PrefillParams& p, int b, int h, int c
 //   * K: symmetric INT8 with the anchors left out of the maximum (BULK 0), or MXFP4 per key
 //     and 32-channel block (BULK 1: every row, anchors included);
 //   * V: per-channel maximum of |V| over the block's non-anchor keys.
-// The workgroups after those gather two 32-entry tiles of the anchor list each.
+// The first ceil(n_anchor_pad / 64) workgroups of each head gather two 32-entry tiles of the
+// anchor list each (first, so that they start in the first round of workgroups).
 template <int BULK>
 __global__ void __launch_bounds__(256) pf_kquant_kernel(PrefillParams p) {
   __shared__ float red[4];
-  __shared__ float vt[64][129];
+  __shared__ uint16_t vt[64][130];  // |V| as bf16 bit patterns (ordered as the values: >= 0)
   __shared__ uint32_t bw[2];
-  const int blk = blockIdx.x, h = blockIdx.y;
+  const int h = blockIdx.y;
   const int t = threadIdx.x, row = t >> 2, qd = t & 3;
   const int nw = p.Npad >> 5, nb = p.Npad >> 6;
-  if (blk >= nb) {  // anchor gather: tiles 2 (blk - nb) and 2 (blk - nb) + 1
-    const int b = 2 * (blk - nb) + (t >> 7);
+  const int n_gather = (p.n_anchor_pad / 32 + 1) / 2;
+  if ((int)blockIdx.x < n_gather) {  // anchor gather: tiles 2 x and 2 x + 1
+    const int b = 2 * blockIdx.x + (t >> 7);
     if (32 * b < p.n_anchor_pad) anchor_gather(p, b, h, t & (D - 1));
     return;
   }
+  const int blk = blockIdx.x - n_gather;
   const int key = blk * KBLK + row;
+  const bool inside = key < p.N;
+  // the block's K and V rows are loaded first (they do not depend on the bitmap)
+  u32x4 kr[4], vr[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) { kr[c] = (u32x4){0u, 0u, 0u, 0u}; vr[c] = kr[c]; }
+  if (inside) {
+    const u32x4* ks = (const u32x4*)(p.k + ((size_t)h * p.N + key) * D + 32 * qd);
+    const u32x4* vs = (const u32x4*)(p.v + ((size_t)h * p.N + key) * D + 32 * qd);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) { kr[c] = ks[c]; vr[c] = vs[c]; }
+  }
   if (t < 2) bw[t] = 0u;
   __syncthreads();
   {
     const int32_t* anc = p.anchors + (size_t)h * p.n_anchor;
     const int lo_key = blk * KBLK;
-    for (int i = t; i < p.n_anchor; i += 256) {
-      const int a = anc[i];
-      if (a >= lo_key && a < lo_key + KBLK) atomicOr(&bw[(a - lo_key) >> 5], 1u << (a & 31));
+    for (int i0 = t; i0 < p.n_anchor; i0 += 8 * 256) {  // eight entries per thread in flight
+      int a[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) a[u] = i0 + 256 * u < p.n_anchor ? anc[i0 + 256 * u] : -1;
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (a[u] >= lo_key && a[u] < lo_key + KBLK) atomicOr(&bw[(a[u] - lo_key) >> 5], 1u << (a[u] & 31));
     }
   }
   __syncthreads();
   if (t < 2) p.abits[(size_t)h * nw + 2 * blk + t] = bw[t];
   const uint32_t word = bw[row >> 5];
-  const bool inside = key < p.N;
   const bool live = inside && !((word >> (key & 31)) & 1u);
   float kx[32], vx[32];
 #pragma unroll
-  for (int e = 0; e < 32; ++e) { kx[e] = 0.0f; vx[e] = 0.0f; }
-  if (inside) {
-    const u32x4* ks = (const u32x4*)(p.k + ((size_t)h * p.N + key) * D + 32 * qd);
-    const u32x4* vs = (const u32x4*)(p.v + ((size_t)h * p.N + key) * D + 32 * qd);
+  for (int c = 0; c < 4; ++c) {
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const u32x4 a = ks[c], b = vs[c];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        kx[8 * c + 2 * e] = bf_lo(a[e]); kx[8 * c + 2 * e + 1] = bf_hi(a[e]);
-        vx[8 * c + 2 * e] = live ? bf_lo(b[e]) : 0.0f; vx[8 * c + 2 * e + 1] = live ? bf_hi(b[e]) : 0.0f;
-      }
+    for (int e = 0; e < 4; ++e) {
+      kx[8 * c + 2 * e] = bf_lo(kr[c][e]); kx[8 * c + 2 * e + 1] = bf_hi(kr[c][e]);
+      vx[8 * c + 2 * e] = live ? bf_lo(vr[c][e]) : 0.0f; vx[8 * c + 2 * e + 1] = live ? bf_hi(vr[c][e]) : 0.0f;
     }
   }
 #pragma unroll
-  for (int e = 0; e < 32; ++e) vt[row][32 * qd + e] = fabsf(vx[e]);
+  for (int e = 0; e < 32; ++e) vt[row][32 * qd + e] = (uint16_t)(__float_as_uint(fabsf(vx[e])) >> 16);  // exact: bf16
   uint8_t* tile = (uint8_t*)p.k8 + ((size_t)h * nb + blk) * 8192;
   if (BULK == 1) {
     // codes of channel block qd of this key: [block][key][16 B]; scale bytes [block][key%16][key/16]
@@ -236,9 +246,9 @@ __global__ void __launch_bounds__(256) pf_kquant_kernel(PrefillParams p) {
     if (t == 0) p.sk[(size_t)h * nb + blk] = s;
   }
   if (t < D) {
-    float m = 0.0f;
-    for (int r = 0; r < 64; ++r) m = fmaxf(m, vt[r][t]);
-    p.vmax[((size_t)h * nb + blk) * D + t] = m;
+    uint32_t m = 0u;
+    for (int r = 0; r < 64; ++r) m = max(m, (uint32_t)vt[r][t]);
+    p.vmax[((size_t)h * nb + blk) * D + t] = __uint_as_float(m << 16);
   }
 }
 
@@ -972,8 +982,8 @@ __global__ void __launch_bounds__(256, 2) pf_attn_kernel(PrefillParams p) {
 
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream) {
   const int Hkv = p.Hkv;
-  // K quantization and bitmap per 64-key block, then the anchor gather (two tiles per workgroup)
-  const dim3 g1(p.Npad / KBLK + (p.n_anchor_pad / 32 + 1) / 2, Hkv);
+  // the anchor gather (two tiles per workgroup), then K quantization and bitmap per 64-key block
+  const dim3 g1((p.n_anchor_pad / 32 + 1) / 2 + p.Npad / KBLK, Hkv);
   if (p.bulk == 1)
     hipLaunchKernelGGL(pf_kquant_kernel<1>, g1, dim3(256), 0, stream, p);
   else
