@@ -933,6 +933,23 @@ def main():
     ws = hq.decode_workspace(shape, args.splits, dev)
     out = torch.empty(B, Hq, D, dtype=torch.float32, device=dev)
     nl = len(layers)
+    # context for the peak, taken before the timed region on a loaded device: the read rate a
+    # plain streaming reduction reaches (torch's row sums over 4 GiB of fp32 resident in HBM,
+    # 4 KB rows; bytes read / time; 50 untimed passes first.  Of the torch reductions tried,
+    # row sums read fastest: a full sum reaches about 4 TB/s).  It does not replace the decode
+    # warm-up: the decode's own first few hundred steps run slower however busy the device was
+    probe = torch.ones(1 << 30, dtype=torch.float32, device=dev).view(1 << 20, 1024)
+    for _ in range(50):
+        probe.sum(dim=1)
+    torch.cuda.synchronize()
+    pe0, pe1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    pe0.record()
+    for _ in range(10):
+        probe.sum(dim=1)
+    pe1.record()
+    torch.cuda.synchronize()
+    read_probe = probe.numel() * 4 * 10 / (pe0.elapsed_time(pe1) * 1e-3) / 1e9
+    del probe
     for i in range(args.warmup):
         c, q = layers[i % nl]
         hq.decode_attn(c, q, args.splits, out, ws)
@@ -968,21 +985,6 @@ def main():
         for _ in range(5):
             b2.copy_(a)
         torch.cuda.synchronize()
-    # context for the peak: the read rate a plain streaming reduction reaches on this device
-    # (torch's row sums over 4 GiB of fp32 resident in HBM, 4 KB rows; bytes read / time.  Of
-    # the torch reductions tried, row sums read fastest: a full sum reaches about 4 TB/s)
-    probe = torch.ones(1 << 30, dtype=torch.float32, device=dev).view(1 << 20, 1024)
-    for _ in range(3):
-        probe.sum(dim=1)
-    torch.cuda.synchronize()
-    pe0, pe1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    pe0.record()
-    for _ in range(10):
-        probe.sum(dim=1)
-    pe1.record()
-    torch.cuda.synchronize()
-    read_probe = probe.numel() * 4 * 10 / (pe0.elapsed_time(pe1) * 1e-3) / 1e9
-    del probe
     workload = f"qwen3-8b-shape decode bs{B} ctx{L} hq{Hq} hkv{Hkv} layers{nl}"
     traffic = stored_traffic(workload)
     line = {
