@@ -608,21 +608,19 @@ __global__ __launch_bounds__(64 * NWAVES) void decode_split_kernel(Params p) {
 // A separate launch: the kernel boundary makes the records of all XCDs visible without the
 // L2 write-back an in-kernel agent-scope release would cost every workgroup.
 // Merge of n_splits <= NS records with every load issued before the first is used: lane
-// j < n_splits reads split j's (m, l), and every lane its two channels of all records (indices
-// clamped, the surplus weighted 0), so the merge costs one memory latency.  Same arithmetic
-// and order as the multi-pass merge below.
+// j < n_splits reads split j's (m, l), and every lane its two adjacent channels 2 lane,
+// 2 lane + 1 of all records with one 8-byte load each (indices clamped, the surplus weighted
+// 0), so the merge costs one memory latency.  Same arithmetic and order per channel as the
+// multi-pass merge below.
 template <int NS>
 __device__ inline void merge_one_latency(const float* rec, int n_splits, float* o, int lane) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
   const int last = n_splits - 1;
-  const float* rl = rec + (size_t)min(lane, last) * (D + 2);
-  const float m = rl[0], l = rl[1];
-  float a[NS], c[NS];
+  const f32x2 ml = *(const f32x2*)(rec + (size_t)min(lane, last) * (D + 2));
+  const float m = ml[0], l = ml[1];
+  f32x2 a[NS];
 #pragma unroll
-  for (int j = 0; j < NS; ++j) {
-    const float* r = rec + (size_t)min(j, last) * (D + 2) + 2;
-    a[j] = r[lane];
-    c[j] = r[lane + 64];
-  }
+  for (int j = 0; j < NS; ++j) a[j] = *(const f32x2*)(rec + (size_t)min(j, last) * (D + 2) + 2 + 2 * lane);
   float M = lane < n_splits ? m : -INFINITY;
 #pragma unroll
   for (int k = 32; k >= 1; k >>= 1) M = fmaxf(M, shfl_xor_f(M, k));
@@ -637,11 +635,10 @@ __device__ inline void merge_one_latency(const float* rec, int n_splits, float* 
 #pragma unroll
   for (int j = 0; j < NS; ++j) {
     const float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), j));  // 0 past the last split
-    O0 = fmaf(a[j], wj, O0);
-    O1 = fmaf(c[j], wj, O1);
+    O0 = fmaf(a[j][0], wj, O0);
+    O1 = fmaf(a[j][1], wj, O1);
   }
-  o[lane] = O0 / lw;
-  o[lane + 64] = O1 / lw;
+  *(f32x2*)(o + 2 * lane) = (f32x2){O0 / lw, O1 / lw};
 }
 
 template <bool RAGGED>
@@ -659,6 +656,7 @@ __global__ __launch_bounds__(64) void decode_reduce_kernel(const float* __restri
     rec = part + (size_t)bh * n_splits * (D + 2);
   }
   if (n_splits <= 8) return merge_one_latency<8>(rec, n_splits, o + (size_t)bh * D, lane);
+  if (n_splits <= 16) return merge_one_latency<16>(rec, n_splits, o + (size_t)bh * D, lane);
   if (n_splits <= 32) return merge_one_latency<32>(rec, n_splits, o + (size_t)bh * D, lane);
   if (n_splits <= 64) return merge_one_latency<64>(rec, n_splits, o + (size_t)bh * D, lane);
   float M = -INFINITY;
