@@ -655,6 +655,7 @@ __global__ __launch_bounds__(64) void decode_reduce_kernel(const float* __restri
   } else {
     rec = part + (size_t)bh * n_splits * (D + 2);
   }
+  if (n_splits <= 4) return merge_one_latency<4>(rec, n_splits, o + (size_t)bh * D, lane);
   if (n_splits <= 8) return merge_one_latency<8>(rec, n_splits, o + (size_t)bh * D, lane);
   if (n_splits <= 16) return merge_one_latency<16>(rec, n_splits, o + (size_t)bh * D, lane);
   if (n_splits <= 32) return merge_one_latency<32>(rec, n_splits, o + (size_t)bh * D, lane);
