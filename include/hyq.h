@@ -237,7 +237,8 @@ int hyq_select_vlines_tail(const hyq_shape_t* shape, const void* k, int32_t len,
    head), 0 = automatic.  ws: >= hyq_workspace_bytes(shape, HYQ_OP_DECODE, 0, n_splits) bytes
    of scratch for the split partial states (no initialisation needed); calls sharing one
    workspace must not overlap in time (same stream is fine).  Two kernel launches (splits,
-   then their merge).  Reads the cache only.  Errors: INVALID, UNSUPPORTED, WORKSPACE, HIP. */
+   then their merge); with one split, one launch that writes o itself.  Reads the cache
+   only.  Errors: INVALID, UNSUPPORTED, WORKSPACE, HIP. */
 int hyq_decode_attn(const hyq_cache_t* cache, const void* q, float* o, int32_t n_splits,
                     void* ws, size_t ws_bytes, hipStream_t stream);
 
@@ -338,7 +339,8 @@ size_t hyq_decode_ragged_table_bytes(const hyq_shape_t* s, int32_t n_seq, int32_
    Operand order of an INT8 row: byte 64 s + 16 j + 8 t + e holds channel
    32 (2 s + t) + 8 j + e (s, t in {0,1}, j < 4, e < 8).
    Calls sharing one workspace must not overlap in time (same stream is fine).
-   Six kernel launches.  Errors: INVALID (null pointers, len <= 0, n_anchor outside
+   Four kernel launches (K quantization with the anchor bitmap and gather, V scale, V
+   quantization, attention).  Errors: INVALID (null pointers, len <= 0, n_anchor outside
    [0, max(0, len-128)]), CAPACITY (n_anchor > shape->anchor_cap), UNSUPPORTED (batch != 1,
    len > HYQ_PREFILL_MAX_LEN), WORKSPACE, HIP. */
 #define HYQ_PREFILL_MAX_LEN (1 << 20)
