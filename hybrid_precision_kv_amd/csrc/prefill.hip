@@ -55,10 +55,14 @@ typedef long i64;
 __device__ inline float bf_lo(uint32_t x) { return __uint_as_float(x << 16); }
 __device__ inline float bf_hi(uint32_t x) { return __uint_as_float(x & 0xffff0000u); }
 
-// symmetric INT8 code of x with scale s (s == 0 -> 0); IEEE divide, half-even rounding
-__device__ inline int int8_code(float x, float s) {
+// reciprocal for int8_code: 0 when s is zero or below the normal range (those take the IEEE
+// division)
+__device__ inline float int8_rcp(float s) { return s >= 0x1p-120f ? __builtin_amdgcn_rcpf(s) : 0.0f; }
+// symmetric INT8 code of x with scale s (s == 0 -> 0) and r = int8_rcp(s): the IEEE quotient
+// rounded half-even, clamped to [-127, 127]
+__device__ inline int int8_code(float x, float s, float r) {
   if (s == 0.0f) return 0;
-  float c = rintf(__fdiv_rn(x, s));
+  float c = r != 0.0f ? rint_div(x, s, r) : rintf(__fdiv_rn(x, s));
   c = fminf(fmaxf(c, -127.0f), 127.0f);
   return (int)c;
 }
@@ -230,6 +234,7 @@ __global__ void __launch_bounds__(256) pf_kquant_kernel(PrefillParams p) {
     __syncthreads();
     amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
     const float s = __fdiv_rn(amax, 127.0f);
+    const float rs = int8_rcp(s);
     // operand order: dim 32 qd + 8 jj + e  ->  byte 64 (qd >> 1) + 16 jj + 8 (qd & 1) + e, and
     // 16-byte chunk k = 4 (qd >> 1) + jj of the row at [tile][chunk][key in tile][16]
     uint8_t* dst = tile + (4 * (qd >> 1)) * 1024 + row * 16 + 8 * (qd & 1);
@@ -238,8 +243,8 @@ __global__ void __launch_bounds__(256) pf_kquant_kernel(PrefillParams p) {
       uint32_t w0 = 0, w1 = 0;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        w0 |= (uint32_t)(int8_code(live ? kx[8 * jj + e] : 0.0f, s) & 0xff) << (8 * e);
-        w1 |= (uint32_t)(int8_code(live ? kx[8 * jj + 4 + e] : 0.0f, s) & 0xff) << (8 * e);
+        w0 |= (uint32_t)(int8_code(live ? kx[8 * jj + e] : 0.0f, s, rs) & 0xff) << (8 * e);
+        w1 |= (uint32_t)(int8_code(live ? kx[8 * jj + 4 + e] : 0.0f, s, rs) & 0xff) << (8 * e);
       }
       *(uint2*)(dst + 1024 * jj) = make_uint2(w0, w1);
     }
@@ -867,6 +872,7 @@ __global__ void __launch_bounds__(256, 2) pf_attn_kernel(PrefillParams p) {
     if (lane == 0) qmax[wave] = amax;
     __syncthreads();
     sq = __fdiv_rn(fmaxf(qmax[wave], qmax[wave ^ 1]), 127.0f);
+    const float rq = int8_rcp(sq);
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
 #pragma unroll
@@ -877,10 +883,10 @@ __global__ void __launch_bounds__(256, 2) pf_attn_kernel(PrefillParams p) {
           uint32_t w0 = 0, w1 = 0;
 #pragma unroll
           for (int e = 0; e < 2; ++e) {
-            w0 |= (uint32_t)(int8_code(bf_lo(x[e]), sq) & 0xff) << (16 * e);
-            w0 |= (uint32_t)(int8_code(bf_hi(x[e]), sq) & 0xff) << (16 * e + 8);
-            w1 |= (uint32_t)(int8_code(bf_lo(x[2 + e]), sq) & 0xff) << (16 * e);
-            w1 |= (uint32_t)(int8_code(bf_hi(x[2 + e]), sq) & 0xff) << (16 * e + 8);
+            w0 |= (uint32_t)(int8_code(bf_lo(x[e]), sq, rq) & 0xff) << (16 * e);
+            w0 |= (uint32_t)(int8_code(bf_hi(x[e]), sq, rq) & 0xff) << (16 * e + 8);
+            w1 |= (uint32_t)(int8_code(bf_lo(x[2 + e]), sq, rq) & 0xff) << (16 * e);
+            w1 |= (uint32_t)(int8_code(bf_hi(x[2 + e]), sq, rq) & 0xff) << (16 * e + 8);
           }
           qo.qi[qb][s8][2 * hh] = (int)w0;
           qo.qi[qb][s8][2 * hh + 1] = (int)w1;

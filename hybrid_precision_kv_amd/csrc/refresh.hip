@@ -532,11 +532,12 @@ __global__ __launch_bounds__(64 * MOVE_WAVES) void refresh_move_kernel(RefreshPa
         const __half s16 = __float2half_rn(__fdiv_rn(__fsub_rn(mx, mn), LEVELS));
         const __half m16 = __float2half_rn(mn);
         const float sf = __half2float(s16), mf = __half2float(m16);
+        const float rf = sf != 0.0f ? __builtin_amdgcn_rcpf(sf) : 0.0f;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           float cq = 0.0f;
           if (sf != 0.0f) {
-            cq = rintf(__fdiv_rn(__fsub_rn(x[e], mf), sf));
+            cq = rint_div(__fsub_rn(x[e], mf), sf, rf);  // = rint(IEEE (x - m) / s)
             cq = fminf(fmaxf(cq, 0.0f), LEVELS);
           }
           code[e] = (uint32_t)cq;
