@@ -39,6 +39,8 @@ __global__ __launch_bounds__(256) void freeze_int4_kernel(CacheView c, const uin
                                                           int n_int4) {
   typedef QL<BK, BV> L;
   __shared__ uint8_t vlds[D][32];
+  __shared__ int win[64];  // a_i - i for the 64 anchors from c0 on (INT_MAX past the list)
+  __shared__ int s_c0, s_ok;
   const int tile = blockIdx.x, b = blockIdx.z, hkv = blockIdx.y;
   const size_t hb = (size_t)b * c.Hkv + hkv;
   const int t = threadIdx.x;
@@ -47,7 +49,49 @@ __global__ __launch_bounds__(256) void freeze_int4_kernel(CacheView c, const uin
   bool valid = slot < n_int4;
   const int32_t* anc = anchors ? anchors + hb * (size_t)n_anchor : nullptr;
   uint8_t* slab = c.int4 + hb * (size_t)c.int4_cap * L::SLOT;
-  int pos = valid ? slot_to_pos(anc, n_anchor, slot) : 0;
+  // Positions of the tile's 32 slots: slot s holds position s + c(s), c(s) = the number of
+  // anchors with a_i - i <= s (a_i - i does not decrease with i).  Wave 0 finds c0 = c(s0) for
+  // the tile's first slot with a 64-way search (each round probes 64 indices at once), then
+  // stages a_i - i of the next 64 anchors; every slot counts inside that window.  A tile whose
+  // range holds more than the window's anchors takes the per-slot binary search.
+  const int s0 = tile * 32;
+  if (t < 64) {
+    int lo = 0, hi = n_anchor;  // c0 in [lo, hi]
+    while (lo < hi) {
+      const int idx = lo + (int)(((long)(hi - lo) * t) >> 6);
+      const bool gt = anc[idx] - idx > s0;
+      const uint64_t m = __ballot(gt);
+      if (m & 1ull) { hi = lo; break; }  // the first probe (index lo) already exceeds s0
+      const int first = m ? __builtin_ctzll(m) : 64;
+      const int nlo = lo + (int)(((long)(hi - lo) * (first - 1)) >> 6) + 1;
+      const int nhi = first < 64 ? lo + (int)(((long)(hi - lo) * first) >> 6) : hi;
+      lo = nlo;
+      hi = nhi;
+    }
+    const int c0 = hi;
+    const int i = c0 + t;
+    const int w = i < n_anchor ? anc[i] - i : 0x7fffffff;
+    win[t] = w;
+    const bool covered = __ballot(t == 63 && (w > s0 + 31)) != 0;  // the window reaches past the tile
+    if (t == 0) { s_c0 = c0; s_ok = covered; }
+  }
+  __syncthreads();
+  int pos = 0;
+  if (valid) {
+    if (s_ok) {
+      int lo2 = 0, hi2 = 64;  // first window entry above slot
+#pragma unroll
+      for (int step = 0; step < 7; ++step) {
+        if (lo2 < hi2) {
+          const int mid = (lo2 + hi2) >> 1;
+          if (win[mid] <= slot) lo2 = mid + 1; else hi2 = mid;
+        }
+      }
+      pos = slot + s_c0 + lo2;
+    } else {
+      pos = slot_to_pos(anc, n_anchor, slot);
+    }
+  }
   if (pos >= len) { valid = false; pos = 0; }  // anchors outside [0, len - W): contract violation
 
   uint8_t code[32];
