@@ -71,6 +71,8 @@ def parse():
     ap.add_argument("--only-bs1", action="store_true",
                     help="run only the batch-1 decode sweep (for a kernel trace of its launches)")
     ap.add_argument("--bs1-ctxs", default="1024,4096,16384,32768")
+    ap.add_argument("--only-freeze", action="store_true",
+                    help="run only the Freeze row (bs16 x 32K quantization into the hybrid layout)")
     return ap.parse_args()
 
 
@@ -686,6 +688,48 @@ def bench_selector_alg1(torch, hq, gen, dev, L=32768, Hq=32, Hkv=8, n_dec=16):
     return res
 
 
+def freeze_bytes(B, Hq, Hkv, L, k, n_proxy, slot_bytes):
+    """Algorithmic bytes of one Freeze (HyQuant paper Alg. 4): every K and V row read once as
+    bf16, the anchor list and the proxy queries read; written: one quantized slot record
+    (codes plus fp16 scale and min) and its position for each of the L - W - k bulk
+    positions, a bf16 K and V row and its position for each anchor, the bf16 window, the
+    proxy ring.  Clearing the staging store is not counted (the empty set needs no bytes)."""
+    n_int4 = L - W - k
+    read = B * Hkv * (2 * L * D * 2 + 4 * k) + B * Hq * n_proxy * D * 2
+    write = B * Hkv * ((slot_bytes + 4) * n_int4 + (512 + 4) * k + 512 * W) + B * Hq * n_proxy * D * 2
+    return read + write
+
+
+def bench_freeze(torch, hq, gen, dev, B=16, L=32768, Hq=32, Hkv=8, bits=4, reps=20):
+    """Freeze at the batched decode workload: bs16 x 32K, 32 Q / 8 KV heads, K4V4 bulk, the 5%
+    anchor count at random ascending positions of the candidate prefix, 64 proxy queries.
+    Timed per call with events after the device has settled; HBM roofline on the
+    algorithmic bytes of freeze_bytes."""
+    shape = hq.Shape.for_context(B, Hq, Hkv, L + 64, bits=bits)
+    K = torch.randn(B, Hkv, L, D, generator=gen, device=dev, dtype=torch.bfloat16)
+    V = torch.randn(B, Hkv, L, D, generator=gen, device=dev, dtype=torch.bfloat16)
+    proxy = torch.randn(B, Hq, 64, D, generator=gen, device=dev).to(torch.bfloat16)
+    k = hq.anchor_count(L, 5)
+    P = L - W
+    anchors = torch.rand(B * Hkv, P, generator=gen, device=dev).argsort(dim=1)[:, :k]
+    anchors = anchors.sort(dim=1).values.to(torch.int32).view(B, Hkv, k).contiguous()
+    cache = hq.HybridKVCache(shape, dev)
+    f = lambda: hq.quantize_kv(cache, K, V, anchors, proxy)  # noqa: E731
+    settle(torch, f)
+    us, us_min = timed(torch, f, reps)
+    slot = (512 * 2 * bits + 1024) // 32
+    nbytes = freeze_bytes(B, Hq, Hkv, L, k, 64, slot)
+    achieved = nbytes / (us * 1e-6) / 1e9
+    del K, V, cache
+    torch.cuda.empty_cache()
+    return {"workload": f"freeze bs{B} ctx{L} hq{Hq} hkv{Hkv} anchors{k} K{bits}V{bits}",
+            "us_per_call": round(us, 1), "us_min": round(us_min, 1), "bytes_per_call": nbytes,
+            "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                         "kernel": "hyq_quantize_kv (quantized slots, anchor and window stores, staging "
+                                   "clear, proxy ring; all launches of the call)"}}
+
+
 def prefill_ops(anchors_row, N, Hq):
     """Algorithmic MFMA work of the hybrid prefill (per Q head: every (query, key) pair the
     method visits, QK^T and PV at 2 x 128 multiply-adds each): quantized pairs j <= i-128 not
@@ -811,8 +855,8 @@ def cpu_model() -> str:
 
 def cpu_rows(args):
     """The oracle on bounded samples of the other hot-path rows, extrapolated to one call:
-    cache-mode selection and refresh at 64 Q / 8 KV heads, 32K (two (sequence, KV head) caches,
-    64 appends each), and the hybrid prefill at 8192 tokens, 32 Q / 8 KV heads (operand
+    Freeze, cache-mode selection and refresh at 64 Q / 8 KV heads, 32K (two (sequence, KV head)
+    caches, 64 appends each; Freeze scaled to the 128 heads of bs16 x 32K), and the hybrid prefill at 8192 tokens, 32 Q / 8 KV heads (operand
     quantization in full, then six seeded random (64-query block, Q head) pairs)."""
     import numpy as np
     from hybrid_precision_kv_amd import synth
@@ -820,13 +864,15 @@ def cpu_rows(args):
     from oracle import policy as pol
     out = {}
     L, G, n_heads_call = 32768, 8, 4 * 8
-    t_sel, t_ref, n = 0.0, 0.0, 2
+    t_sel, t_ref, t_frz, n = 0.0, 0.0, 0.0, 2
     for i in range(n):
         s = synth.HeadStream(synth.seed_for(args.seed + 7, i, 0), L, G)
         prox = s.queries(64)
         A, _ = pol.select_dense(s.K, prox)
         c = pol.HybridCacheRef(g=G)
+        t0 = time.perf_counter()
         c.freeze(s.K, s.V, A, prox)
+        t_frz += time.perf_counter() - t0
         k, v, q = s.new_tokens(64)
         for j in range(64):
             c.append(k[j], v[j], q[:, j])
@@ -840,6 +886,9 @@ def cpu_rows(args):
     out["selector_5pct"] = {"us_per_call": round(t_sel / n * n_heads_call * 1e6, 1),
                             "sample": f"{n} of the {n_heads_call} (sequence, KV head) caches of bs4 x {L}, "
                                       f"64 Q / 8 KV heads, cache mode after 64 appends ({t_sel:.1f} s)"}
+    out["freeze"] = {"us_per_call": round(t_frz / n * 16 * 8 * 1e6, 1),
+                     "sample": f"Freeze of {n} (sequence, KV head) caches of {L} positions ({t_frz:.2f} s), "
+                               f"times the 128 heads of bs16 x {L} at 8 KV heads"}
     out["refresh"] = {"us_per_call": round(t_ref / n * n_heads_call * 1e6, 1),
                       "sample": f"the same {n} caches, the new set applied ({t_ref:.2f} s)"}
     N, Hq, Hkv = 8192, 32, 8
@@ -906,6 +955,11 @@ def main():
         gen.manual_seed(args.seed)
         ctxs = tuple(int(x) for x in args.bs1_ctxs.split(",") if x)
         print(json.dumps({"rows": {"decode_bs1": bench_decode_bs1(torch, hq, gen, dev, ctxs=ctxs)}}), flush=True)
+        return
+    if args.only_freeze:
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(args.seed)
+        print(json.dumps({"rows": {"freeze": bench_freeze(torch, hq, gen, dev)}}), flush=True)
         return
     if args.only_prefill:
         gen = torch.Generator(device=dev)
@@ -1024,6 +1078,8 @@ def main():
                                                             out, args.splits)
         del layers, c0
         torch.cuda.empty_cache()
+        rows["freeze"] = bench_freeze(torch, hq, gen, dev, B=B, L=L, Hq=Hq, Hkv=Hkv)
+        print(f"[bench] freeze: {rows['freeze']}", file=sys.stderr, flush=True)
         rows["decode_bs1"] = bench_decode_bs1(torch, hq, gen, dev)
         print(f"[bench] bs1 sweep done", file=sys.stderr, flush=True)
         # the same kernel with every position in bf16 (k = P): what the hybrid layout saves

@@ -30,6 +30,7 @@ __device__ inline int slot_to_pos(const int32_t* anc, int n_anchor, int s) {
 __device__ inline int nibble_kslot(int j) { return ((j & 3) << 1) | (j >> 2); }
 
 // ---------------------------------------------------------------- Freeze: quantized slots
+constexpr int VROW = 36;  // dwords per slot row of the V-code staging (128 code bytes + 16 pad)
 // BK-bit K codes and BV-bit V codes, 2^B - 1 levels each (4/4: the INT4 record; 8/8, 4/2 and
 // 2/2: the same record structure)
 template <int BK, int BV>
@@ -38,13 +39,16 @@ __global__ __launch_bounds__(256) void freeze_int4_kernel(CacheView c, const uin
                                                           const int32_t* __restrict__ anchors, int n_anchor,
                                                           int n_int4) {
   typedef QL<BK, BV> L;
-  __shared__ uint8_t vlds[D][32];
+  // V codes of the tile, one byte each: row = slot, byte = channel (a row of 144 bytes: the
+  // 16-byte writes of the four groups of two slots fall on distinct banks)
+  __shared__ __align__(16) uint32_t vlds[32][VROW];
   __shared__ int win[64];  // a_i - i for the 64 anchors from c0 on (INT_MAX past the list)
   __shared__ int s_c0, s_ok;
   const int tile = blockIdx.x, b = blockIdx.z, hkv = blockIdx.y;
   const size_t hb = (size_t)b * c.Hkv + hkv;
   const int t = threadIdx.x;
-  const int sl = t >> 3, kv = (t >> 2) & 1, g = t & 3;
+  // waves 0-1 quantize K rows and waves 2-3 V rows (kv is uniform in a wave); slot sl, group g
+  const int kv = __builtin_amdgcn_readfirstlane(t >> 7), sl = (t >> 2) & 31, g = t & 3;
   const int slot = tile * 32 + sl;
   bool valid = slot < n_int4;
   const int32_t* anc = anchors ? anchors + hb * (size_t)n_anchor : nullptr;
@@ -94,7 +98,7 @@ __global__ __launch_bounds__(256) void freeze_int4_kernel(CacheView c, const uin
   }
   if (pos >= len) { valid = false; pos = 0; }  // anchors outside [0, len - W): contract violation
 
-  uint8_t code[32];
+  uint32_t code[32];
   __half s16 = __float2half(0.f), m16 = __float2half(0.f);
   if (valid) {
     const uint16_t* src = (kv ? v : k) + (hb * (size_t)len + pos) * D + 32 * g;
@@ -108,8 +112,12 @@ __global__ __launch_bounds__(256) void freeze_int4_kernel(CacheView c, const uin
         x[j + 2 * e + 1] = bf16_bits_to_f32((uint16_t)(w[e] >> 16));
       }
     }
-    if (kv) quant_group32<(1 << BV) - 1>(x, code, s16, m16);
-    else quant_group32<(1 << BK) - 1>(x, code, s16, m16);
+    if constexpr (BK == BV) {
+      quant_group32<(1 << BK) - 1>(x, code, s16, m16);
+    } else {
+      if (kv) quant_group32<(1 << BV) - 1>(x, code, s16, m16);
+      else quant_group32<(1 << BK) - 1>(x, code, s16, m16);
+    }
   } else {
 #pragma unroll
     for (int j = 0; j < 32; ++j) code[j] = 0;
@@ -122,7 +130,7 @@ __global__ __launch_bounds__(256) void freeze_int4_kernel(CacheView c, const uin
     for (int d = 0; d < BK; ++d) {
       uint32_t w = 0;
 #pragma unroll
-      for (int j = 0; j < 32 / BK; ++j) w |= (uint32_t)code[(32 / BK) * d + j] << (BK * j);
+      for (int j = 0; j < 32 / BK; ++j) w |= code[(32 / BK) * d + j] << (BK * j);
       kw[d] = w;
     }
     uint8_t* chunk = slab + kcode_chunk_b<BK, BV>(slot, g);
@@ -137,10 +145,15 @@ __global__ __launch_bounds__(256) void freeze_int4_kernel(CacheView c, const uin
     if (g == 0) c.slot_pos[hb * (size_t)c.int4_cap + slot] = valid ? pos : -1;
   } else {
     *(uint32_t*)(slab + vsm_byte_b<BK, BV>(slot, g)) = smw;
+    uint32_t b[8];
 #pragma unroll
-    for (int j = 0; j < 32; ++j) vlds[32 * g + j][sl] = code[j];
+    for (int i = 0; i < 8; ++i) b[i] = code[4 * i] | (code[4 * i + 1] << 8) | (code[4 * i + 2] << 16) | (code[4 * i + 3] << 24);
+    *(u32x4*)&vlds[sl][8 * g] = (u32x4){b[0], b[1], b[2], b[3]};
+    *(u32x4*)&vlds[sl][8 * g + 4] = (u32x4){b[4], b[5], b[6], b[7]};
   }
   __syncthreads();
+  const uint8_t* vb = (const uint8_t*)&vlds[0][0];
+  auto vcode = [&](int p, int ch) { return (uint32_t)vb[p * (4 * VROW) + ch]; };
   uint32_t* vtile = (uint32_t*)(slab + (size_t)tile * L::TB + L::VC);
   if constexpr (BV == 2) {
     // dword d = (q * 16 + i) * 4 + d4: channel blocks 2 d4 + h at the quad's 8 slots
@@ -153,7 +166,7 @@ __global__ __launch_bounds__(256) void freeze_int4_kernel(CacheView c, const uin
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int p = 4 * q + (e & 3) + 16 * (e >> 2);
-          w |= (uint32_t)vlds[ch][p] << (2 * (e >> 1) + 16 * (e & 1) + 8 * h);
+          w |= vcode(p, ch) << (2 * (e >> 1) + 16 * (e & 1) + 8 * h);
         }
       }
       vtile[d] = w;
@@ -167,7 +180,7 @@ __global__ __launch_bounds__(256) void freeze_int4_kernel(CacheView c, const uin
       for (int j = 0; j < 8; ++j) {
         const int e = nibble_kslot(j);
         const int p = 4 * q + (e & 3) + 16 * (e >> 2);
-        w |= (uint32_t)vlds[ch][p] << (4 * j);
+        w |= vcode(p, ch) << (4 * j);
       }
       vtile[d] = w;
     }
@@ -183,7 +196,7 @@ __global__ __launch_bounds__(256) void freeze_int4_kernel(CacheView c, const uin
         const int byte = 4 * half8 + b;  // byte = kslot_byte(e): invert it
         const int e = (byte & 4) | ((byte & 1) << 1) | ((byte >> 1) & 1);
         const int p = 4 * q + (e & 3) + 16 * (e >> 2);
-        w |= (uint32_t)vlds[ch][p] << (8 * b);
+        w |= vcode(p, ch) << (8 * b);
       }
       vtile[d] = w;
     }

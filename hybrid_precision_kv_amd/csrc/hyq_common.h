@@ -177,25 +177,43 @@ __device__ inline float rint_div(float a, float s, float r) {
 // operation order (the translation units using it are built with -ffp-contract=off):
 //   mn = min x, mx = max x; s = fp16((mx - mn) / LEVELS); m = fp16(mn);
 //   code = s == 0 ? 0 : clamp(rint((x - m) / s), 0, LEVELS)
+// The quotients come from the reciprocal as in rint_div, with the threshold set by the width:
+// a quotient that can change a clamped code is at most LEVELS + 1 in magnitude (beyond that
+// both roundings clamp to the same end), where q0 is within 2^-22 (LEVELS + 1) of the IEEE
+// quotient: 2^-18 for up to 4 bits, 2^-14 for 8 bits.  A q0 further than 2^-16 (2^-13) from a
+// half-integer rounds as the IEEE quotient does.  The codes are formed first; only a group
+// holding a quotient inside that band (about 1 in 1,000 groups at 4 bits) runs the IEEE
+// division, for those quotients alone.  With s = 0 the reciprocal is taken as 0: every
+// quotient is 0 and every code 0.
 template <int LEVELS = 15>
-__device__ inline void quant_group32(const float* x, uint8_t* code, __half& s16, __half& m16) {
+__device__ inline void quant_group32(const float* x, uint32_t* code, __half& s16, __half& m16) {
+  constexpr float THR = LEVELS <= 15 ? 0.5f - 0x1p-16f : 0.5f - 0x1p-13f;
   float mn = x[0], mx = x[0];
 #pragma unroll
   for (int j = 1; j < 32; ++j) { mn = fminf(mn, x[j]); mx = fmaxf(mx, x[j]); }
   float s32 = __fdiv_rn(__fsub_rn(mx, mn), (float)LEVELS);
   s16 = __float2half_rn(s32);
   m16 = __float2half_rn(mn);
-  float sf = __half2float(s16), mf = __half2float(m16);
+  const float sf = __half2float(s16), mf = __half2float(m16);
   const float rf = sf != 0.0f ? __builtin_amdgcn_rcpf(sf) : 0.0f;
+  float c[32];
+  float off = 0.0f;  // largest distance of a fast quotient from its integer
 #pragma unroll
   for (int j = 0; j < 32; ++j) {
-    float c = 0.0f;
-    if (sf != 0.0f) {
-      c = rint_div(__fsub_rn(x[j], mf), sf, rf);  // = rint(IEEE (x - m) / s)
-      c = fminf(fmaxf(c, 0.0f), (float)LEVELS);
-    }
-    code[j] = (uint8_t)c;
+    const float q0 = __fmul_rn(__fsub_rn(x[j], mf), rf);
+    c[j] = rintf(q0);
+    off = fmaxf(off, fabsf(__fsub_rn(q0, c[j])));
   }
+  if (off > THR) {
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+      const float a = __fsub_rn(x[j], mf);
+      const float q0 = __fmul_rn(a, rf);
+      if (fabsf(__fsub_rn(q0, rintf(q0))) > THR) c[j] = rintf(__fdiv_rn(a, sf));
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 32; ++j) code[j] = (uint32_t)fminf(fmaxf(c[j], 0.0f), (float)LEVELS);
 }
 
 // ---------------------------------------------------------------- cross-lane helpers
