@@ -98,40 +98,59 @@ __global__ __launch_bounds__(256) void freeze_int4_kernel(CacheView c, const uin
   }
   if (pos >= len) { valid = false; pos = 0; }  // anchors outside [0, len - W): contract violation
 
-  uint32_t code[32];
   __half s16 = __float2half(0.f), m16 = __float2half(0.f);
+  uint32_t cb[8];  // the group's 32 codes, one byte each (code j in byte j % 4 of dword j / 4)
+#pragma unroll
+  for (int d = 0; d < 8; ++d) cb[d] = 0;
   if (valid) {
     const uint16_t* src = (kv ? v : k) + (hb * (size_t)len + pos) * D + 32 * g;
-    float x[32];
+    u32x4 w[4];
 #pragma unroll
-    for (int j = 0; j < 32; j += 8) {
-      const u32x4 w = *(const u32x4*)(src + j);
+    for (int j = 0; j < 4; ++j) w[j] = *(const u32x4*)(src + 8 * j);
+    // channel j: the bf16 bits of dword j / 2 (low half for even j) as fp32
+    auto x = [&](int j) {
+      const uint32_t d = w[j >> 3][(j >> 1) & 3];
+      return __uint_as_float((j & 1) ? (d & 0xffff0000u) : (d << 16));
+    };
+    auto fresh = [&]() {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        x[j + 2 * e] = bf16_bits_to_f32((uint16_t)(w[e] & 0xffff));
-        x[j + 2 * e + 1] = bf16_bits_to_f32((uint16_t)(w[e] >> 16));
-      }
-    }
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) asm volatile("" : "+v"(w[j][e]));
+    };
     if constexpr (BK == BV) {
-      quant_group32<(1 << BK) - 1>(x, code, s16, m16);
+      quant_group32<(1 << BK) - 1, 8>(x, fresh, cb, s16, m16);
     } else {
-      if (kv) quant_group32<(1 << BV) - 1>(x, code, s16, m16);
-      else quant_group32<(1 << BK) - 1>(x, code, s16, m16);
+      if (kv == 0) quant_group32<(1 << BK) - 1, 8>(x, fresh, cb, s16, m16);
+      else quant_group32<(1 << BV) - 1, 8>(x, fresh, cb, s16, m16);
     }
-  } else {
-#pragma unroll
-    for (int j = 0; j < 32; ++j) code[j] = 0;
   }
   const uint32_t smw = (uint32_t)__half_as_ushort(s16) | ((uint32_t)__half_as_ushort(m16) << 16);
   if (kv == 0) {
     // the slot's group chunk (BK dwords): channel j at bits BK j
     uint32_t kw[BK];
+    if constexpr (BK == 8) {
 #pragma unroll
-    for (int d = 0; d < BK; ++d) {
-      uint32_t w = 0;
+      for (int d = 0; d < 8; ++d) kw[d] = cb[d];
+    } else if constexpr (BK == 4) {
 #pragma unroll
-      for (int j = 0; j < 32 / BK; ++j) w |= code[(32 / BK) * d + j] << (BK * j);
-      kw[d] = w;
+      for (int d = 0; d < 4; ++d) {  // bytes 0 and 2 of b | b >> 4 hold code pairs (4j, 4j + 1), (4j + 2, 4j + 3)
+        const uint32_t lo = cb[2 * d] | (cb[2 * d] >> 4), hi = cb[2 * d + 1] | (cb[2 * d + 1] >> 4);
+        kw[d] = __builtin_amdgcn_perm(hi, lo, 0x06040200u);
+      }
+    } else {
+#pragma unroll
+      for (int d = 0; d < 2; ++d) {  // four dwords of byte codes -> one dword of 2-bit codes
+        uint32_t w = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          uint32_t b = cb[4 * d + i];
+          b |= b >> 6;   // bits 0-3: codes (0, 1); bits 16-19: codes (2, 3)
+          b |= b >> 12;  // bits 0-7: codes 0..3
+          w |= (b & 0xffu) << (8 * i);
+        }
+        kw[d] = w;
+      }
     }
     uint8_t* chunk = slab + kcode_chunk_b<BK, BV>(slot, g);
     if constexpr (BK == 2) {
@@ -145,11 +164,8 @@ __global__ __launch_bounds__(256) void freeze_int4_kernel(CacheView c, const uin
     if (g == 0) c.slot_pos[hb * (size_t)c.int4_cap + slot] = valid ? pos : -1;
   } else {
     *(uint32_t*)(slab + vsm_byte_b<BK, BV>(slot, g)) = smw;
-    uint32_t b[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) b[i] = code[4 * i] | (code[4 * i + 1] << 8) | (code[4 * i + 2] << 16) | (code[4 * i + 3] << 24);
-    *(u32x4*)&vlds[sl][8 * g] = (u32x4){b[0], b[1], b[2], b[3]};
-    *(u32x4*)&vlds[sl][8 * g + 4] = (u32x4){b[4], b[5], b[6], b[7]};
+    *(u32x4*)&vlds[sl][8 * g] = (u32x4){cb[0], cb[1], cb[2], cb[3]};
+    *(u32x4*)&vlds[sl][8 * g + 4] = (u32x4){cb[4], cb[5], cb[6], cb[7]};
   }
   __syncthreads();
   const uint8_t* vb = (const uint8_t*)&vlds[0][0];

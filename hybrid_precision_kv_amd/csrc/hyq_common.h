@@ -185,35 +185,49 @@ __device__ inline float rint_div(float a, float s, float r) {
 // holding a quotient inside that band (about 1 in 1,000 groups at 4 bits) runs the IEEE
 // division, for those quotients alone.  With s = 0 the reciprocal is taken as 0: every
 // quotient is 0 and every code 0.
-template <int LEVELS = 15>
-__device__ inline void quant_group32(const float* x, uint32_t* code, __half& s16, __half& m16) {
+// x(j) gives channel j's value.  The codes come out packed: P bits each, code j at bit P j of
+// the P dwords of out (P = 2, 4 or 8).
+// fresh() runs before the rare exact pass: a caller whose x(j) decodes packed registers can
+// mark them rewritten there, so that the compiler decodes them again in that pass instead of
+// keeping all 32 differences (x - m) live across the fast pass.
+template <int LEVELS, int P, class X, class F>
+__device__ inline void quant_group32(X x, F fresh, uint32_t (&out)[P], __half& s16, __half& m16) {
   constexpr float THR = LEVELS <= 15 ? 0.5f - 0x1p-16f : 0.5f - 0x1p-13f;
-  float mn = x[0], mx = x[0];
+  constexpr int PER = 32 / P;  // codes per dword
+  float mn = x(0), mx = x(0);
 #pragma unroll
-  for (int j = 1; j < 32; ++j) { mn = fminf(mn, x[j]); mx = fmaxf(mx, x[j]); }
+  for (int j = 1; j < 32; ++j) { mn = fminf(mn, x(j)); mx = fmaxf(mx, x(j)); }
   float s32 = __fdiv_rn(__fsub_rn(mx, mn), (float)LEVELS);
   s16 = __float2half_rn(s32);
   m16 = __float2half_rn(mn);
   const float sf = __half2float(s16), mf = __half2float(m16);
   const float rf = sf != 0.0f ? __builtin_amdgcn_rcpf(sf) : 0.0f;
-  float c[32];
   float off = 0.0f;  // largest distance of a fast quotient from its integer
 #pragma unroll
-  for (int j = 0; j < 32; ++j) {
-    const float q0 = __fmul_rn(__fsub_rn(x[j], mf), rf);
-    c[j] = rintf(q0);
-    off = fmaxf(off, fabsf(__fsub_rn(q0, c[j])));
+  for (int d = 0; d < P; ++d) {
+    uint32_t w = 0;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const float q0 = __fmul_rn(__fsub_rn(x(PER * d + i), mf), rf);
+      const float c = rintf(q0);
+      off = fmaxf(off, fabsf(__fsub_rn(q0, c)));
+      w |= (uint32_t)fminf(fmaxf(c, 0.0f), (float)LEVELS) << (P * i);
+    }
+    out[d] = w;
   }
   if (off > THR) {
+    fresh();
 #pragma unroll
     for (int j = 0; j < 32; ++j) {
-      const float a = __fsub_rn(x[j], mf);
+      const float a = __fsub_rn(x(j), mf);
       const float q0 = __fmul_rn(a, rf);
-      if (fabsf(__fsub_rn(q0, rintf(q0))) > THR) c[j] = rintf(__fdiv_rn(a, sf));
+      if (fabsf(__fsub_rn(q0, rintf(q0))) > THR) {
+        const uint32_t c = (uint32_t)fminf(fmaxf(rintf(__fdiv_rn(a, sf)), 0.0f), (float)LEVELS);
+        const int sh = P * (j % PER);
+        out[j / PER] = (out[j / PER] & ~(((1u << P) - 1u) << sh)) | (c << sh);
+      }
     }
   }
-#pragma unroll
-  for (int j = 0; j < 32; ++j) code[j] = (uint32_t)fminf(fmaxf(c[j], 0.0f), (float)LEVELS);
 }
 
 // ---------------------------------------------------------------- cross-lane helpers
