@@ -211,7 +211,9 @@ __device__ inline void quant_group32(X x, F fresh, uint32_t (&out)[P], __half& s
       const float q0 = __fmul_rn(__fsub_rn(x(PER * d + i), mf), rf);
       const float c = rintf(q0);
       off = fmaxf(off, fabsf(__fsub_rn(q0, c)));
-      w |= (uint32_t)fminf(fmaxf(c, 0.0f), (float)LEVELS) << (P * i);
+      const float cc = fminf(fmaxf(c, 0.0f), (float)LEVELS);
+      if constexpr (P == 8) w = __builtin_amdgcn_cvt_pk_u8_f32(cc, i, w);  // byte i of w
+      else w |= (uint32_t)cc << (P * i);
     }
     out[d] = w;
   }
