@@ -181,10 +181,11 @@ __device__ inline float rint_div(float a, float s, float r) {
 // a quotient that can change a clamped code is at most LEVELS + 1 in magnitude (beyond that
 // both roundings clamp to the same end), where q0 is within 2^-22 (LEVELS + 1) of the IEEE
 // quotient: 2^-18 for up to 4 bits, 2^-14 for 8 bits.  A q0 further than 2^-16 (2^-13) from a
-// half-integer rounds as the IEEE quotient does.  The codes are formed first; only a group
-// holding a quotient inside that band (about 1 in 1,000 groups at 4 bits) runs the IEEE
-// division, for those quotients alone.  With s = 0 the reciprocal is taken as 0: every
-// quotient is 0 and every code 0.
+// half-integer rounds as the IEEE quotient does.  The codes are formed first; a group holding
+// a quotient inside that band runs the IEEE division for those quotients alone.  (With bf16
+// inputs and an fp16 scale and minimum, exact half-integer quotients are common: most waves
+// hold such a group.)  With s = 0 the reciprocal is taken as 0: every quotient is 0 and
+// every code 0.
 // x(j) gives channel j's value.  The codes come out packed: P bits each, code j at bit P j of
 // the P dwords of out (P = 2, 4 or 8).
 // fresh() runs before the rare exact pass: a caller whose x(j) decodes packed registers can
