@@ -37,9 +37,11 @@ def parse():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[1])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=300,
-                    help="untimed steps before the timed loop; from idle the device needs about 30 ms of "
-                         "sustained load (about 300 steps) to reach its steady rate")
+    ap.add_argument("--warmup", type=int, default=50,
+                    help="untimed decode steps right before the timed loop (after the --ramp-steps pre-pass)")
+    ap.add_argument("--ramp-steps", type=int, default=400,
+                    help="decode steps run before the warm-up steps, as part of setup: after setup the "
+                         "device needs a few hundred steps to reach its steady rate (reported as ramp_steps)")
     ap.add_argument("--batch", type=int, default=16)
     ap.add_argument("--ctx", type=int, default=32768)
     ap.add_argument("--layers", type=int, default=36)
@@ -1004,6 +1006,12 @@ def main():
     torch.cuda.synchronize()
     read_probe = probe.numel() * 4 * 10 / (pe0.elapsed_time(pe1) * 1e-3) / 1e9
     del probe
+    # device ramp (setup, untimed): from idle, and after setup, the decode reaches its steady
+    # rate only after a few hundred steps (the clocks' ramp, then a slower convergence of the
+    # nontemporal-load build over about 300 more steps); the W warm-up steps follow
+    for i in range(args.ramp_steps):
+        c, q = layers[i % nl]
+        hq.decode_attn(c, q, args.splits, out, ws)
     for i in range(args.warmup):
         c, q = layers[i % nl]
         hq.decode_attn(c, q, args.splits, out, ws)
@@ -1048,6 +1056,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "ramp_steps": args.ramp_steps,
         "ms_per_step": round(ms_per_step, 5),
         "us_per_step": round(ms_per_step * 1e3, 2),
         "tokens_per_s_attention_only": round(B / (nl * ms_per_step * 1e-3), 1),

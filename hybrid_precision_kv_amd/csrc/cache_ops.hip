@@ -280,17 +280,29 @@ __global__ __launch_bounds__(256) void freeze_bf16_kernel(CacheView c, const uin
   }
 }
 
-__global__ void fill_zero_kernel(uint32_t* __restrict__ p, size_t n) {
-  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) p[i] = 0u;
-}
-
-// proxy ring <- the last n queries of q_tail (slots 0..n-1)
-__global__ void proxy_init_kernel(CacheView c, const uint16_t* __restrict__ q_tail, int n_tail, int n) {
-  const int hq = blockIdx.y, b = blockIdx.z, j = blockIdx.x, ch = threadIdx.x;
-  const int Hq = c.Hkv * c.G;
-  const size_t src = (((size_t)b * Hq + hq) * n_tail + (n_tail - n + j)) * D + ch;
-  const size_t dst = (((size_t)b * Hq + hq) * c.proxy_cap + j) * D + ch;
-  c.proxy_q[dst] = q_tail[src];
+// The rest of Freeze in one launch: workgroups [0, n_clear) clear the K and V staging stores
+// (16-byte zero stores), the others fill the proxy ring with the last n queries of q_tail
+// (16 threads per 128-channel row, 16 bytes each).
+__global__ __launch_bounds__(256) void freeze_aux_kernel(CacheView c, size_t clear_vec, int n_clear,
+                                                         const uint16_t* __restrict__ q_tail, int n_tail, int n) {
+  const int t = threadIdx.x;
+  if ((int)blockIdx.x < n_clear) {
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    for (size_t i = (size_t)blockIdx.x * 256 + t; i < clear_vec; i += (size_t)n_clear * 256) {
+      ((u32x4*)c.s_k)[i] = z;
+      ((u32x4*)c.s_v)[i] = z;
+    }
+    return;
+  }
+  const size_t idx = (size_t)(blockIdx.x - n_clear) * 256 + t;
+  const size_t rows = (size_t)c.B * c.Hkv * c.G * n;
+  const size_t r = idx >> 4;
+  const int part = (int)(idx & 15);
+  if (r >= rows) return;
+  const size_t bh = r / n;  // b * Hq + hq
+  const int j = (int)(r % n);
+  const u32x4 w = *(const u32x4*)(q_tail + (bh * n_tail + (n_tail - n + j)) * D + 8 * part);
+  *(u32x4*)(c.proxy_q + (bh * c.proxy_cap + j) * D + 8 * part) = w;
 }
 
 // ---------------------------------------------------------------- append
@@ -320,14 +332,6 @@ __global__ __launch_bounds__(128) void append_kernel(CacheView c, const uint16_t
   }
 }
 
-hipError_t zero_fill(void* p, size_t bytes, hipStream_t stream) {
-  const size_t n = bytes / 4;
-  if (n == 0) return hipSuccess;
-  int blocks = (int)((n + 255) / 256);
-  if (blocks > 4096) blocks = 4096;
-  hipLaunchKernelGGL(fill_zero_kernel, dim3(blocks), dim3(256), 0, stream, (uint32_t*)p, n);
-  return hipGetLastError();
-}
 
 }  // namespace
 
@@ -356,13 +360,15 @@ hipError_t launch_freeze(const CacheView& c, const uint16_t* k, const uint16_t* 
     hipLaunchKernelGGL(freeze_bf16_kernel, grid, dim3(256), 0, stream, c, k, v, len, anchors, n_anchor, 1);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  const size_t stage_bytes = (size_t)c.B * c.Hkv * c.staging_cap * D * 2;
-  if ((e = zero_fill(c.s_k, stage_bytes, stream)) != hipSuccess) return e;
-  if ((e = zero_fill(c.s_v, stage_bytes, stream)) != hipSuccess) return e;
-  if (q_tail && n_tail > 0) {
-    const int n = n_tail < c.proxy_cap ? n_tail : c.proxy_cap;
-    dim3 grid(n, c.Hkv * c.G, c.B);
-    hipLaunchKernelGGL(proxy_init_kernel, grid, dim3(D), 0, stream, c, q_tail, n_tail, n);
+  // staging bytes per store: a multiple of 16 (staging_cap is a multiple of 32)
+  const size_t clear_vec = (size_t)c.B * c.Hkv * c.staging_cap * D * 2 / 16;
+  const int n_clear = clear_vec ? (int)((clear_vec + 255) / 256 < 1024 ? (clear_vec + 255) / 256 : 1024) : 0;
+  const int n = q_tail && n_tail > 0 ? (n_tail < c.proxy_cap ? n_tail : c.proxy_cap) : 0;
+  const size_t proxy_threads = (size_t)c.B * c.Hkv * c.G * n * 16;
+  const int n_proxy = (int)((proxy_threads + 255) / 256);
+  if (n_clear + n_proxy > 0) {
+    hipLaunchKernelGGL(freeze_aux_kernel, dim3(n_clear + n_proxy), dim3(256), 0, stream, c, clear_vec, n_clear,
+                       q_tail, n_tail, n);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   return hipSuccess;
