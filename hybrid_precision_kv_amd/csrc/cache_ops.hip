@@ -34,17 +34,15 @@ constexpr int VROW = 36;  // dwords per slot row of the V-code staging (128 code
 // BK-bit K codes and BV-bit V codes, 2^B - 1 levels each (4/4: the INT4 record; 8/8, 4/2 and
 // 2/2: the same record structure)
 template <int BK, int BV>
-__global__ __launch_bounds__(256) void freeze_int4_kernel(CacheView c, const uint16_t* __restrict__ k,
-                                                          const uint16_t* __restrict__ v, int len,
-                                                          const int32_t* __restrict__ anchors, int n_anchor,
-                                                          int n_int4) {
+__device__ inline void freeze_q_tile(const CacheView& c, const uint16_t* __restrict__ k,
+                                     const uint16_t* __restrict__ v, int len, const int32_t* __restrict__ anchors,
+                                     int n_anchor, int n_int4, int tile, int hkv, int b) {
   typedef QL<BK, BV> L;
   // V codes of the tile, one byte each: row = slot, byte = channel (a row of 144 bytes: the
   // 16-byte writes of the four groups of two slots fall on distinct banks)
   __shared__ __align__(16) uint32_t vlds[32][VROW];
   __shared__ int win[64];  // a_i - i for the 64 anchors from c0 on (INT_MAX past the list)
   __shared__ int s_c0, s_ok;
-  const int tile = blockIdx.x, b = blockIdx.z, hkv = blockIdx.y;
   const size_t hb = (size_t)b * c.Hkv + hkv;
   const int t = threadIdx.x;
   // waves 0-1 quantize K rows and waves 2-3 V rows (kv is uniform in a wave); slot sl, group g
@@ -222,12 +220,11 @@ __global__ __launch_bounds__(256) void freeze_int4_kernel(CacheView c, const uin
 // ---------------------------------------------------------------- Freeze: bf16 stores
 // mode 0: anchor store (tile u holds anchors 32u..32u+31); mode 1: window ring (tile u holds
 // ring slots 32u..32u+31).  Positions past the count are written as zeros.
-__global__ __launch_bounds__(256) void freeze_bf16_kernel(CacheView c, const uint16_t* __restrict__ k,
-                                                          const uint16_t* __restrict__ v, int len,
-                                                          const int32_t* __restrict__ anchors, int n_anchor,
-                                                          int mode) {
+__device__ inline void freeze_bf16_tile(const CacheView& c, const uint16_t* __restrict__ k,
+                                        const uint16_t* __restrict__ v, int len,
+                                        const int32_t* __restrict__ anchors, int n_anchor, int mode, int tile,
+                                        int hkv, int b) {
   __shared__ uint16_t vl[32][D + 8];
-  const int tile = blockIdx.x, b = blockIdx.z, hkv = blockIdx.y;
   const size_t hb = (size_t)b * c.Hkv + hkv;
   const int t = threadIdx.x;
   uint16_t *dk, *dv;
@@ -278,6 +275,20 @@ __global__ __launch_bounds__(256) void freeze_bf16_kernel(CacheView c, const uin
     }
     *(u32x4*)(vt + (size_t)ch * 8) = w;
   }
+}
+
+// Freeze's stores in one launch: workgroups x < n_at copy anchor tiles, the next WIN / 32 copy
+// window tiles, the rest quantize 32-slot tiles.  The copies come first, so their memory
+// traffic runs beside the quantizer's arithmetic instead of after it.
+template <int BK, int BV>
+__global__ __launch_bounds__(256) void freeze_kernel(CacheView c, const uint16_t* __restrict__ k,
+                                                     const uint16_t* __restrict__ v, int len,
+                                                     const int32_t* __restrict__ anchors, int n_anchor, int n_int4,
+                                                     int n_at) {
+  const int x = blockIdx.x, hkv = blockIdx.y, b = blockIdx.z;
+  if (x < n_at) freeze_bf16_tile(c, k, v, len, anchors, n_anchor, 0, x, hkv, b);
+  else if (x < n_at + WIN / 32) freeze_bf16_tile(c, k, v, len, anchors, n_anchor, 1, x - n_at, hkv, b);
+  else freeze_q_tile<BK, BV>(c, k, v, len, anchors, n_anchor, n_int4, x - n_at - WIN / 32, hkv, b);
 }
 
 // The rest of Freeze in one launch: workgroups [0, n_clear) clear the K and V staging stores
@@ -341,24 +352,15 @@ hipError_t launch_freeze(const CacheView& c, const uint16_t* k, const uint16_t* 
   hipError_t e;
   const int P = len > WIN ? len - WIN : 0;
   const int n_int4 = P - n_anchor;
-  if (n_int4 > 0) {
-    dim3 grid((n_int4 + 31) / 32, c.Hkv, c.B);
+  const int n_at = (n_anchor + 31) / 32;
+  {
+    dim3 grid(n_at + WIN / 32 + (n_int4 > 0 ? (n_int4 + 31) / 32 : 0), c.Hkv, c.B);
     e = with_widths(c.bits, c.bits_v, [&](auto BK, auto BV) {
-      hipLaunchKernelGGL((freeze_int4_kernel<decltype(BK)::value, decltype(BV)::value>), grid, dim3(256), 0, stream,
-                         c, k, v, len, anchors, n_anchor, n_int4);
+      hipLaunchKernelGGL((freeze_kernel<decltype(BK)::value, decltype(BV)::value>), grid, dim3(256), 0, stream, c, k,
+                         v, len, anchors, n_anchor, n_int4 > 0 ? n_int4 : 0, n_at);
       return hipGetLastError();
     });
     if (e != hipSuccess) return e;
-  }
-  if (n_anchor > 0) {
-    dim3 grid((n_anchor + 31) / 32, c.Hkv, c.B);
-    hipLaunchKernelGGL(freeze_bf16_kernel, grid, dim3(256), 0, stream, c, k, v, len, anchors, n_anchor, 0);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-  }
-  {
-    dim3 grid(WIN / 32, c.Hkv, c.B);
-    hipLaunchKernelGGL(freeze_bf16_kernel, grid, dim3(256), 0, stream, c, k, v, len, anchors, n_anchor, 1);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   // staging bytes per store: a multiple of 16 (staging_cap is a multiple of 32)
   const size_t clear_vec = (size_t)c.B * c.Hkv * c.staging_cap * D * 2 / 16;
