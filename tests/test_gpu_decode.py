@@ -26,9 +26,11 @@ class Pair:
     """The same seeded workload on the GPU cache and in per-head oracle caches."""
 
     def __init__(self, seed, B, Hkv, G, L, n_steps=0, pct=5, staging_cap=64, max_len=None, bits=4, bits_v=None,
-                 transform=None):
+                 transform=None, anchor_layout=None):
         """transform: optional callable that edits the drawn inputs (the dict of bf16 arrays)
-        in place before anything is stored, for inputs outside the unit-scale distribution."""
+        in place before anything is stored, for inputs outside the unit-scale distribution.
+        anchor_layout: optional callable (b, h, k, P) -> k ascending positions in [0, P) that
+        replaces the selector's anchors (both sides freeze with the same list)."""
         self.B, self.Hkv, self.G, self.L = B, Hkv, G, L
         bv = bits if bits_v is None else bits_v
         print(f"[case] seed={seed} B={B} Hkv={Hkv} G={G} L={L} steps={n_steps} bits={bits}/{bv}", flush=True)
@@ -41,7 +43,11 @@ class Pair:
         for b in range(B):
             for h in range(Hkv):
                 prox = self.d["proxy"][b, h * G:(h + 1) * G]
-                A, _ = pol.select_dense(self.d["K"][b, h], prox, pct_num=pct)
+                if anchor_layout is None:
+                    A, _ = pol.select_dense(self.d["K"][b, h], prox, pct_num=pct)
+                else:
+                    A = np.asarray(anchor_layout(b, h, k, max(0, L - 128)), np.int64)
+                    assert len(A) == k and np.all(np.diff(A) > 0) and (k == 0 or (A[0] >= 0 and A[-1] < L - 128))
                 anchors[b, h, :k] = A
                 r = pol.HybridCacheRef(g=G, bits=bits, bits_v=bv)
                 r.freeze(self.d["K"][b, h], self.d["V"][b, h], A, prox)
