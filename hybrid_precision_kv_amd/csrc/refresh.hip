@@ -363,7 +363,7 @@ __global__ __launch_bounds__(256) void refresh_gather_kernel(RefreshParams p) {
 // 32 g + 4 sub + e of K (kv = 0) or V (kv = 1); the group's min and max come from a reduction
 // over its 8 lanes, and every code follows the group quantizer's formula.  The next move's
 // source words are loaded while the current move is processed.
-constexpr int MV_CHUNK = 16;
+constexpr int MV_CHUNK = 4;
 constexpr int MOVE_WAVES = 4;  // waves per workgroup
 
 __device__ inline float group8_min(float v) {
