@@ -39,9 +39,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=50,
                     help="untimed decode steps right before the timed loop (after the --ramp-steps pre-pass)")
-    ap.add_argument("--ramp-steps", type=int, default=400,
+    ap.add_argument("--ramp-steps", type=int, default=1500,
                     help="decode steps run before the warm-up steps, as part of setup: after setup the "
-                         "device needs a few hundred steps to reach its steady rate (reported as ramp_steps)")
+                         "device needs several hundred steps to reach its steady rate (reported as ramp_steps)")
     ap.add_argument("--batch", type=int, default=16)
     ap.add_argument("--ctx", type=int, default=32768)
     ap.add_argument("--layers", type=int, default=36)
@@ -1007,8 +1007,9 @@ def main():
     read_probe = probe.numel() * 4 * 10 / (pe0.elapsed_time(pe1) * 1e-3) / 1e9
     del probe
     # device ramp (setup, untimed): from idle, and after setup, the decode reaches its steady
-    # rate only after a few hundred steps (the clocks' ramp, then a slower convergence of the
-    # nontemporal-load build over about 300 more steps); the W warm-up steps follow
+    # rate only after several hundred steps (the clocks' ramp, then a slower convergence of
+    # the nontemporal-load build that settles after about 700 steps); the W warm-up steps
+    # follow
     for i in range(args.ramp_steps):
         c, q = layers[i % nl]
         hq.decode_attn(c, q, args.splits, out, ws)
