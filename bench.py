@@ -12,7 +12,10 @@ generated on the GPU for the 36 layers; anchors come from hyq_select_vlines when
 available, else from a torch-side top-k of the same vertical-line score (input preparation
 only; the timed step is the library's decode kernel alone).
 
-Prints one JSON line (see the design notes for the field definitions).
+Prints one JSON line: the headline (metric, value in GB/s of algorithmic bytes per step,
+ms_per_step, roofline against the 8 TB/s HBM peak with the stored traffic counters, config),
+the other hot-path rows under `rows` (each with its own roofline where one applies), and the
+oracle timed on the host under `cpu_baseline`.
 """
 from __future__ import annotations
 

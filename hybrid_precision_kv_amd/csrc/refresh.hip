@@ -3,7 +3,7 @@
 // The selector runs every 64 decode tokens (techwalker.com article on HyQuant, design section);
 // the HyQuant paper ("HyQuant: Hybrid-Precision Quantization for LLM Attention") gives the set
 // (§4.1 Eq. 5) and the four storage segments (Alg. 3, Alg. 4) but not how a new set is applied.
-// Reading taken (stated in the design notes):
+// Reading taken:
 //   * anchors in the new set keep their bf16 values;
 //   * staged positions in the new set become anchors with their original bf16 values;
 //   * INT4 positions in the new set become anchors holding bf16(dequantized value) -- their

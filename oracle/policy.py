@@ -4,7 +4,7 @@ hybrid KV-cache state machine (test infrastructure only).
 "HyQuant paper" = the arXiv page "HyQuant: Hybrid-Precision Quantization for LLM
 Attention"; "techwalker article" = the techwalker.com article summarising it.
 
-Readings of the pages taken here (each is also listed in the design notes):
+Readings of the pages taken here:
   * The window is sliding: the last W positions [L-W, L) of the current length L
     (§4.1 Eq. 2 read with t0 = current length), W = 128 (§5.1, Table 15).
   * Anchors ("vertical lines") are chosen from the non-window prefix [0, L-W)
