@@ -169,6 +169,8 @@ size_t hyq_workspace_bytes(const hyq_shape_t* shape, int op, int32_t len, int32_
    token and 32-channel group (min/max asymmetric, fp16 scale = fp16((max-min)/15), fp16
    min, codes rint((x-min)/scale) clamped to [0,15]); staging emptied; unused tails zeroed.
    Counters: len, n_int4 = max(0,len-128) - n_anchor, n_anchor, n_staged = 0, proxy.
+   Two kernel launches (anchor and window copies with the quantized tiles; staging clear and
+   proxy ring).
    Errors: INVALID, UNSUPPORTED, CAPACITY (len-128-n_anchor > int4_cap, n_anchor >
    anchor_cap), HIP. */
 int hyq_quantize_kv(hyq_cache_t* cache, const void* k, const void* v, int32_t len,
