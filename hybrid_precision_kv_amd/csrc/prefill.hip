@@ -814,16 +814,23 @@ __global__ void __launch_bounds__(256, 2) pf_attn_kernel(PrefillParams p) {
   // codes of the lane's channel block; the codes are also stored in the workspace
   QOps qo;
   float sq = 0.0f;
-  if (c.tid == 0) {
-    // anchors some row of the workgroup may use: a <= r0 + 127 - 128
+  if (wave == 0) {
+    // the number of anchors some row of the workgroup may use (a <= r0 + 127 - 128), by a
+    // 64-way search of the sorted list: each round probes 64 entries at once, so up to 4096
+    // anchors take two rounds of loads (a binary search by one thread took about ten, and the
+    // workgroup's first barrier waited for them)
     const int32_t* anc = p.anchors + (size_t)c.hk * p.n_anchor;
     const int lim = r0 + WG_ROWS - 1 - WIN;
-    int lo = 0, hi = p.n_anchor;
+    int lo = 0, hi = p.n_anchor;  // the count lies in [lo, hi]
     while (lo < hi) {
-      const int mid = (lo + hi) >> 1;
-      if (anc[mid] <= lim) lo = mid + 1; else hi = mid;
+      const int step = (hi - lo + 63) >> 6;
+      const int idx = lo + (lane + 1) * step - 1;  // probe l: is the count above idx?
+      const bool le = idx < hi && anc[idx] <= lim;
+      const int nlo = lo + step * __builtin_popcountll(__ballot(le));
+      hi = min(hi, nlo + step - 1);
+      lo = nlo;
     }
-    nb_anchor_s = lo;
+    if (lane == 0) nb_anchor_s = lo;
   }
   if constexpr (BULK == 1) {
     // lane (qb, l16, j): channels 32 j .. 32 j + 31 of row 16 qb + l16 -- one MX block
