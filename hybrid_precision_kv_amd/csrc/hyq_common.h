@@ -181,11 +181,13 @@ __device__ inline float rint_div(float a, float s, float r) {
 // a quotient that can change a clamped code is at most LEVELS + 1 in magnitude (beyond that
 // both roundings clamp to the same end), where q0 is within 2^-22 (LEVELS + 1) of the IEEE
 // quotient: 2^-18 for up to 4 bits, 2^-14 for 8 bits.  A q0 further than 2^-16 (2^-13) from a
-// half-integer rounds as the IEEE quotient does.  The codes are formed first; a group holding
-// a quotient inside that band runs the IEEE division for those quotients alone.  (With bf16
-// inputs and an fp16 scale and minimum, exact half-integer quotients are common: most waves
-// hold such a group.)  With s = 0 the reciprocal is taken as 0: every quotient is 0 and
-// every code 0.
+// half-integer rounds as the IEEE quotient does.  The codes are formed first; a quotient
+// inside that band is settled with the IEEE division afterwards.  With bf16 inputs and an fp16
+// scale and minimum, exact half-integer quotients are common (about 7 in 10^4 of N(0,1)
+// values: most waves of 64 groups hold one), but in a wave they fall on one or two of the 32
+// channel positions, so the fast pass records, per position, whether any lane of the wave has
+// one (a wave vote), and the exact pass visits only those positions.  With s = 0 the
+// reciprocal is taken as 0: every quotient is 0 and every code 0.
 // x(j) gives channel j's value.  The codes come out packed: P bits each, code j at bit P j of
 // the P dwords of out (P = 2, 4 or 8).
 // fresh() runs before the rare exact pass: a caller whose x(j) decodes packed registers can
@@ -203,7 +205,7 @@ __device__ inline void quant_group32(X x, F fresh, uint32_t (&out)[P], __half& s
   m16 = __float2half_rn(mn);
   const float sf = __half2float(s16), mf = __half2float(m16);
   const float rf = sf != 0.0f ? __builtin_amdgcn_rcpf(sf) : 0.0f;
-  float off = 0.0f;  // largest distance of a fast quotient from its integer
+  uint32_t near = 0;  // bit j: some lane of the wave has its channel-j quotient near a tie
 #pragma unroll
   for (int d = 0; d < P; ++d) {
     uint32_t w = 0;
@@ -211,17 +213,18 @@ __device__ inline void quant_group32(X x, F fresh, uint32_t (&out)[P], __half& s
     for (int i = 0; i < PER; ++i) {
       const float q0 = __fmul_rn(__fsub_rn(x(PER * d + i), mf), rf);
       const float c = rintf(q0);
-      off = fmaxf(off, fabsf(__fsub_rn(q0, c)));
+      if (__ballot(fabsf(__fsub_rn(q0, c)) > THR)) near |= 1u << (PER * d + i);
       const float cc = fminf(fmaxf(c, 0.0f), (float)LEVELS);
       if constexpr (P == 8) w = __builtin_amdgcn_cvt_pk_u8_f32(cc, i, w);  // byte i of w
       else w |= (uint32_t)cc << (P * i);
     }
     out[d] = w;
   }
-  if (off > THR) {
+  if (near) {
     fresh();
 #pragma unroll
     for (int j = 0; j < 32; ++j) {
+      if (!(near & (1u << j))) continue;  // the same on every lane
       const float a = __fsub_rn(x(j), mf);
       const float q0 = __fmul_rn(a, rf);
       if (fabsf(__fsub_rn(q0, rintf(q0))) > THR) {
