@@ -173,7 +173,7 @@ int cu_count() {
 // 16 x 32K, 4 splits = two workgroups per CU).
 int auto_splits(const hyq_cache_t* c, int* waves) {
   const int G = c->shape.n_q_heads / c->shape.n_kv_heads;
-  const long units = (long)nheads(&c->shape) * ((G + 3) / 4);
+  const long units = (long)nheads(&c->shape) * hyq::decode_head_blocks(G);
   const long tiles = (c->n_int4 + 31) / 32 + 3 * ((c->n_anchor + 31) / 32 + (c->n_staged + 31) / 32 + 4);
   const long cus = cu_count();
   // K2V2 workgroups fit three per CU and gain from it (6 splits at bs16 x 32K: 96.9 against

@@ -208,34 +208,35 @@ __device__ inline void tile_softmax(WaveState& st, const float (&sc)[8], float (
   st.l += ((pv[0] + pv[1]) + (pv[2] + pv[3])) + ((pv[4] + pv[5]) + (pv[6] + pv[7]));
 }
 
-template <int BK, int BV, bool MASK>
-__device__ inline void int4_tile(WaveState& st, const QTile<BK, BV>& x, const f16x8 (&bq)[4], float qsum24,
-                                 float c_int4, int base, int n_int4, int q4) {
-  f32x4 S0 = {0.f, 0.f, 0.f, 0.f}, S1 = {0.f, 0.f, 0.f, 0.f};
+// One INT4 tile for HB column blocks of 4 Q heads each (HB = 2 serves 8 Q heads of one KV head
+// from one load of the tile): the code operands are extracted once and feed every block's
+// MFMAs; each block keeps its own softmax state.
+template <int BK, int BV, bool MASK, int HB>
+__device__ inline void int4_tile(WaveState (&st)[HB], const QTile<BK, BV>& x, const f16x8 (&bq)[HB][4],
+                                 const float (&qsum24)[HB], const float (&c_int4)[HB], int base, int n_int4,
+                                 int q4) {
+  f32x4 S0[HB], S1[HB];
+#pragma unroll
+  for (int hb = 0; hb < HB; ++hb) {
+    S0[hb] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    S1[hb] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  }
 #pragma unroll
   for (int tt = 0; tt < 4; ++tt) {
-    S0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(qcodes<BK>(x.kc0, tt), bq[tt], S0, 0, 0, 0);
-    S1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(qcodes<BK>(x.kc1, tt), bq[tt], S1, 0, 0, 0);
+    const f16x8 k0 = qcodes<BK>(x.kc0, tt), k1 = qcodes<BK>(x.kc1, tt);
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb) {
+      S0[hb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(k0, bq[hb][tt], S0[hb], 0, 0, 0);
+      S1[hb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(k1, bq[hb][tt], S1[hb], 0, 0, 0);
+    }
   }
-  float sc[8];
   bool valid[8];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    float v0 = fmaf(half_lo(x.ks0[r]), S0[r], half_hi(x.ks0[r]) * qsum24);
-    float v1 = fmaf(half_lo(x.ks1[r]), S1[r], half_hi(x.ks1[r]) * qsum24);
-    v0 += dpp_quad_xor1(v0);
-    v1 += dpp_quad_xor1(v1);
-    v0 += dpp_quad_xor2(v0);
-    v1 += dpp_quad_xor2(v1);
-    sc[r] = v0 * c_int4;
-    sc[4 + r] = v1 * c_int4;
-    if (MASK) {
-      valid[r] = base + 4 * q4 + r < n_int4;
-      valid[4 + r] = base + 16 + 4 * q4 + r < n_int4;
-      sc[r] = valid[r] ? sc[r] : -INFINITY;
-      sc[4 + r] = valid[4 + r] ? sc[4 + r] : -INFINITY;
-    }
+    valid[r] = !MASK || base + 4 * q4 + r < n_int4;
+    valid[4 + r] = !MASK || base + 16 + 4 * q4 + r < n_int4;
   }
+  float vmax;
   {
     uint32_t smv[8];
 #pragma unroll
@@ -243,36 +244,61 @@ __device__ inline void int4_tile(WaveState& st, const QTile<BK, BV>& x, const f1
       smv[j] = j < 4 ? x.vs0[j] : x.vs1[j - 4];
       if (MASK) smv[j] = valid[j] ? smv[j] : 0u;  // unused slots may hold any bits
     }
-    track_vscale(st, max_vscale(smv));
+    vmax = max_vscale(smv);
   }
-  float pv[8];
-  tile_softmax(st, sc, pv);
-  f16x8 bhi, blo;
-  float mt = 0.f;
+  f16x8 bhi[HB], blo[HB];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const uint32_t smv = j < 4 ? x.vs0[j] : x.vs1[j - 4];
-    const float pj = pv[j];
-    // code operands scaled per k-slot (INT4: x16 on k-slots 2,3,6,7; 2-bit: 4^(j >> 1))
-    float pp = pj * half_lo(smv) * (st.ps * code_factor<BV>(j));
-    float mm = pj * half_hi(smv);
-    if (MASK) {  // unused slots may hold any scale/min bits: keep them out entirely
-      pp = valid[j] ? pp : 0.f;
-      mm = valid[j] ? mm : 0.f;
+  for (int hb = 0; hb < HB; ++hb) {
+    float sc[8];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float v0 = fmaf(half_lo(x.ks0[r]), S0[hb][r], half_hi(x.ks0[r]) * qsum24[hb]);
+      float v1 = fmaf(half_lo(x.ks1[r]), S1[hb][r], half_hi(x.ks1[r]) * qsum24[hb]);
+      v0 += dpp_quad_xor1(v0);
+      v1 += dpp_quad_xor1(v1);
+      v0 += dpp_quad_xor2(v0);
+      v1 += dpp_quad_xor2(v1);
+      sc[r] = v0 * c_int4[hb];
+      sc[4 + r] = v1 * c_int4[hb];
+      if (MASK) {
+        sc[r] = valid[r] ? sc[r] : -INFINITY;
+        sc[4 + r] = valid[4 + r] ? sc[4 + r] : -INFINITY;
+      }
     }
-    mt += mm;
-    const _Float16 h = (_Float16)pp;
-    bhi[j] = h;
-    blo[j] = (_Float16)(pp - (float)h);
+    track_vscale(st[hb], vmax);
+    float pv[8];
+    tile_softmax(st[hb], sc, pv);
+    float mt = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t smv = j < 4 ? x.vs0[j] : x.vs1[j - 4];
+      const float pj = pv[j];
+      // code operands scaled per k-slot (INT4: x16 on k-slots 2,3,6,7; 2-bit: 4^(j >> 1))
+      float pp = pj * half_lo(smv) * (st[hb].ps * code_factor<BV>(j));
+      float mm = pj * half_hi(smv);
+      if (MASK) {  // unused slots may hold any scale/min bits: keep them out entirely
+        pp = valid[j] ? pp : 0.f;
+        mm = valid[j] ? mm : 0.f;
+      }
+      mt += mm;
+      const _Float16 h = (_Float16)pp;
+      bhi[hb][j] = h;
+      blo[hb][j] = (_Float16)(pp - (float)h);
+    }
+    st[hb].mt += mt;
   }
-  st.mt += mt;
   f16x8 a[8];
 #pragma unroll
   for (int rr = 0; rr < 8; ++rr) a[rr] = qcodes<BV>(x.vc, rr);
 #pragma unroll
-  for (int rr = 0; rr < 8; ++rr) st.acc[rr] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[rr], bhi, st.acc[rr], 0, 0, 0);
+  for (int hb = 0; hb < HB; ++hb) {
 #pragma unroll
-  for (int rr = 0; rr < 8; ++rr) st.acc[rr] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[rr], blo, st.acc[rr], 0, 0, 0);
+    for (int rr = 0; rr < 8; ++rr)
+      st[hb].acc[rr] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[rr], bhi[hb], st[hb].acc[rr], 0, 0, 0);
+#pragma unroll
+    for (int rr = 0; rr < 8; ++rr)
+      st[hb].acc[rr] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[rr], blo[hb], st[hb].acc[rr], 0, 0, 0);
+  }
 }
 
 // What one workgroup reads and writes: the slabs of one (sequence, KV head), its counters,
@@ -288,7 +314,7 @@ struct HeadWork {
 };
 
 // The work of one workgroup: split `split` of KV head `hkv` of sequence `b`, for Q-head block
-// `sub` (Q heads 4 sub .. 4 sub + 3 of the KV group).
+// `sub` (Q heads H sub .. H sub + H - 1 of the KV group, H = 4 per column block it serves).
 struct Unit {
   int split, hkv, sub, b;
 };
@@ -300,11 +326,11 @@ struct Unit {
 // slab is streamed from HBM once and the other blocks' reads hit that XCD's L2.  The id
 // space is padded to whole groups of 8; padding workgroups return at once.
 __host__ __device__ inline int decode_grid_size(int n_splits, int Hkv, int B, int G) {
-  const int nsub = (G + 3) >> 2, units = n_splits * Hkv * B;
+  const int nsub = decode_head_blocks(G), units = n_splits * Hkv * B;
   return nsub == 1 ? units : (units + 7) / 8 * 8 * nsub;
 }
 __device__ inline bool unit_of(const DecodeParams& p, Unit& u) {
-  const int nsub = (p.G + 3) >> 2;
+  const int nsub = decode_head_blocks(p.G);
   const int L = blockIdx.x;
   int r;  // index over (split, KV head, sequence), split fastest
   if (nsub == 1) {
@@ -388,86 +414,97 @@ __device__ inline HeadWork head_work(const RaggedDecodeParams& p, const Unit& u)
 
 // NWAVES waves per workgroup: 4 when the launch is bandwidth bound (two workgroups per CU), 8
 // when it is latency bound (one workgroup per CU: twice the tile loads in flight per CU and
-// half the dependent chain per wave)
-template <int BK, int BV, class Params, int NWAVES, bool NT>
+// half the dependent chain per wave).  HB column blocks of 4 Q heads per wave: 1 up to GQA 4,
+// 2 for GQA 8 and 16, so that one load of a tile serves 8 Q heads.
+template <int BK, int BV, class Params, int NWAVES, bool NT, int HB>
 __global__ __launch_bounds__(64 * NWAVES) void decode_split_kernel(Params p) {
   constexpr int WAVES = NWAVES;
+  constexpr int HW = 4 * HB;  // Q heads of the workgroup's head block
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n = lane & 15, q4 = lane >> 4;
   const int hh = n >> 2, g = n & 3;
   Unit u;
   if (!unit_of(p, u)) return;  // padding of the grid (the whole workgroup)
   const int sub = u.sub;
-  const int head = sub * 4 + hh;  // Q head inside the KV group
-  const bool head_ok = head < p.G;
   const HeadWork hw = head_work<BK, BV>(p, u);
 
-  // ---- q of the (up to 4) Q heads of this head block, staged once through LDS
-  __shared__ uint32_t q_lds[4][D / 2];
-  if (threadIdx.x < 256) {
-    const int h2 = threadIdx.x >> 6, cp = threadIdx.x & 63;  // 256 threads x 2 channels
-    const int hd = sub * 4 + h2;
+  // ---- q of the head block's Q heads, staged once through LDS
+  __shared__ uint32_t q_lds[HW][D / 2];
+  for (int idx = threadIdx.x; idx < HW * (D / 2); idx += 64 * WAVES) {
+    const int h2 = idx >> 6, cp = idx & 63;  // 2 channels per thread and pass
+    const int hd = sub * HW + h2;
     uint32_t v = 0;
     if (hd < p.G) v = *(const uint32_t*)(hw.q + (size_t)hd * D + 2 * cp);
     q_lds[h2][cp] = v;
   }
   __syncthreads();
-  // B operand of the quantized path: q[head] restricted to this lane's column group, channels
-  // in the order the code extraction produces them, times the inverse of the code operand's
-  // per-element factor (INT4: 1/16 on k-slots 2,3,6,7; 2-bit: 4^-(e >> 1)); zero outside the group
-  f16x8 bq4[4];
-  float qsum = 0.f;
-  const bool use = head_ok && (g == q4);
-  float qs;  // 2^sigma: the head's largest |q| times qs lies in [2^13, 2^14)
-  {
-    float f[32];  // channels 32 q4 .. 32 q4 + 31
-    float amax = 0.f;
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const u32x4 w = *(const u32x4*)&q_lds[hh][16 * q4 + 4 * t];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        f[8 * t + 2 * e] = bf16_bits_to_f32((uint16_t)(w[e] & 0xffff));
-        f[8 * t + 2 * e + 1] = bf16_bits_to_f32((uint16_t)(w[e] >> 16));
-      }
-    }
-#pragma unroll
-    for (int c = 0; c < 32; ++c) amax = fmaxf(amax, fabsf(f[c]));
-    amax = col4_max(amax);  // lanes l, l^16, l^32, l^48: the four channel blocks of head hh
-    int ex = 0;
-    if (amax > 0.f) (void)frexpf(amax, &ex);
-    qs = ldexpf(1.0f, min(100, max(-100, Q_TARGET - ex)));
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float v = f[kstep_channel<BK>(t, e)] * qs * code_factor<BK>(e);
-        bq4[t][e] = use ? (_Float16)v : (_Float16)0.f;
-      }
-  }
-  if (head_ok) {
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const u32x4 w = *(const u32x4*)&q_lds[hh][16 * g + 4 * t];
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        qsum += (float)(_Float16)(bf16_bits_to_f32((uint16_t)(w[e] & 0xffff)) * qs) +
-                (float)(_Float16)(bf16_bits_to_f32((uint16_t)(w[e] >> 16)) * qs);
-    }
-  }
-  const float qsum24 = qsum * (1.0f / 16777216.0f);
+  // B operand of the quantized path, per column block hb: q[head] restricted to this lane's
+  // column group, channels in the order the code extraction produces them, times the inverse
+  // of the code operand's per-element factor (INT4: 1/16 on k-slots 2,3,6,7; 2-bit:
+  // 4^-(e >> 1)); zero outside the group
+  f16x8 bq4[HB][4];
+  float qsum24[HB], c_int4[HB];
+  bool use[HB];
   const float alpha_log2 = LOG2E * 0.08838834764831845f;  // log2(e) / sqrt(128)
-  const float c_int4 = alpha_log2 * 16777216.0f / qs;
-
-  WaveState st;
-  st.m = -INFINITY;
-  st.l = 0.f;
-  st.mt = 0.f;
-  st.ps = PS_INIT;
-  st.ps_hi = PS_HI / PS_INIT;
-  st.ps_lo = PS_LO / PS_INIT;
 #pragma unroll
-  for (int r = 0; r < 8; ++r) st.acc[r] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  for (int hb = 0; hb < HB; ++hb) {
+    const int hl = 4 * hb + hh;  // this lane's head in the block
+    const bool head_ok = sub * HW + hl < p.G;
+    use[hb] = head_ok && (g == q4);
+    float qs;  // 2^sigma: the head's largest |q| times qs lies in [2^13, 2^14)
+    {
+      float f[32];  // channels 32 q4 .. 32 q4 + 31
+      float amax = 0.f;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const u32x4 w = *(const u32x4*)&q_lds[hl][16 * q4 + 4 * t];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          f[8 * t + 2 * e] = bf16_bits_to_f32((uint16_t)(w[e] & 0xffff));
+          f[8 * t + 2 * e + 1] = bf16_bits_to_f32((uint16_t)(w[e] >> 16));
+        }
+      }
+#pragma unroll
+      for (int c = 0; c < 32; ++c) amax = fmaxf(amax, fabsf(f[c]));
+      amax = col4_max(amax);  // lanes l, l^16, l^32, l^48: the four channel blocks of the head
+      int ex = 0;
+      if (amax > 0.f) (void)frexpf(amax, &ex);
+      qs = ldexpf(1.0f, min(100, max(-100, Q_TARGET - ex)));
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float v = f[kstep_channel<BK>(t, e)] * qs * code_factor<BK>(e);
+          bq4[hb][t][e] = use[hb] ? (_Float16)v : (_Float16)0.f;
+        }
+    }
+    float qsum = 0.f;
+    if (head_ok) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const u32x4 w = *(const u32x4*)&q_lds[hl][16 * g + 4 * t];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          qsum += (float)(_Float16)(bf16_bits_to_f32((uint16_t)(w[e] & 0xffff)) * qs) +
+                  (float)(_Float16)(bf16_bits_to_f32((uint16_t)(w[e] >> 16)) * qs);
+      }
+    }
+    qsum24[hb] = qsum * (1.0f / 16777216.0f);
+    c_int4[hb] = alpha_log2 * 16777216.0f / qs;
+  }
+
+  WaveState st[HB];
+#pragma unroll
+  for (int hb = 0; hb < HB; ++hb) {
+    st[hb].m = -INFINITY;
+    st[hb].l = 0.f;
+    st[hb].mt = 0.f;
+    st[hb].ps = PS_INIT;
+    st[hb].ps_hi = PS_HI / PS_INIT;
+    st[hb].ps_lo = PS_LO / PS_INIT;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) st[hb].acc[r] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  }
 
   // ---- work of this worker: INT4 tiles w, w + NW, w + 2 NW, ... (the workers of a head sweep
   // the head's records side by side); bf16 tiles go to the workers with the fewest INT4 tiles
@@ -480,21 +517,27 @@ __global__ __launch_bounds__(64 * NWAVES) void decode_split_kernel(Params p) {
   const uint32_t smoff = (uint32_t)(g * 64 + q4 * 16);
   const int full = hw.n_int4 >> 5;  // tiles below this index hold 32 valid slots
   auto tile = [&](const QTile<BK, BV>& x, int t) {
-    if (t < full) int4_tile<BK, BV, false>(st, x, bq4, qsum24, c_int4, t * 32, hw.n_int4, q4);
-    else int4_tile<BK, BV, true>(st, x, bq4, qsum24, c_int4, t * 32, hw.n_int4, q4);
+    if (t < full) int4_tile<BK, BV, false, HB>(st, x, bq4, qsum24, c_int4, t * 32, hw.n_int4, q4);
+    else int4_tile<BK, BV, true, HB>(st, x, bq4, qsum24, c_int4, t * 32, hw.n_int4, q4);
   };
-  // two tiles in flight: the next tile's loads are issued before the current one is computed;
-  // a prefetch past the wave's last tile re-reads the current one (in bounds, never used)
+  // two tiles in flight: the next tile's loads are issued before the current one is computed.
+  // The prefetch past the wave's last tile keeps the same loads (so the loop's waits stay
+  // exact) but every lane reads the current record's first bytes: one 16-byte chunk per load
+  // instead of the 5 KB record (never used).
+  auto prefetch = [&](QTile<BK, BV>& x, int t) {
+    const bool past = t + NW >= T4;
+    load_int4_tile<NT>(x, slab, past ? t : t + NW, past ? 0u : (uint32_t)lane, past ? 0u : smoff);
+  };
   if (w < T4) {
     QTile<BK, BV> ta, tb;
     int t = w;
     load_int4_tile<NT>(ta, slab, t, (uint32_t)lane, smoff);
     for (;;) {
-      load_int4_tile<NT>(tb, slab, t + NW < T4 ? t + NW : t, (uint32_t)lane, smoff);
+      prefetch(tb, t);
       tile(ta, t);
       t += NW;
       if (t >= T4) break;
-      load_int4_tile<NT>(ta, slab, t + NW < T4 ? t + NW : t, (uint32_t)lane, smoff);
+      prefetch(ta, t);
       tile(tb, t);
       t += NW;
       if (t >= T4) break;
@@ -516,69 +559,82 @@ __global__ __launch_bounds__(64 * NWAVES) void decode_split_kernel(Params p) {
     for (int j = 0; j < 8; ++j) ka[j] = __builtin_bit_cast(bf16x8, ld_stream<NT>((const u32x4*)(kt + j * 512)));
 #pragma unroll
     for (int j = 0; j < 8; ++j) va[j] = __builtin_bit_cast(bf16x8, ld_stream<NT>((const u32x4*)(vt + j * 512)));
-    f32x4 S0 = {0.f, 0.f, 0.f, 0.f}, S1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
-      // B operand: q[head] channels 32q4+8tt .. +7 in natural order, zero outside the group
-      u32x4 qw = *(const u32x4*)&q_lds[hh][16 * q4 + 4 * tt];
-      if (!use) qw = (u32x4){0u, 0u, 0u, 0u};
-      const bf16x8 bqb = __builtin_bit_cast(bf16x8, qw);
-      S0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[tt], bqb, S0, 0, 0, 0);
-      S1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[4 + tt], bqb, S1, 0, 0, 0);
-    }
-    float sc[8];
     bool valid[8];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      float v0 = S0[r], v1 = S1[r];
-      v0 += dpp_quad_xor1(v0);
-      v1 += dpp_quad_xor1(v1);
-      v0 += dpp_quad_xor2(v0);
-      v1 += dpp_quad_xor2(v1);
       valid[r] = base + 4 * q4 + r < cnt;
       valid[4 + r] = base + 16 + 4 * q4 + r < cnt;
-      sc[r] = valid[r] ? v0 * alpha_log2 : -INFINITY;
-      sc[4 + r] = valid[4 + r] ? v1 * alpha_log2 : -INFINITY;
-    }
-    float pv[8];
-    tile_softmax(st, sc, pv);
-    bf16x8 bhi, blo;
-    const float bfs = st.ps * (1.0f / 16777216.0f);  // bf16 tiles feed p 2^e 2^-24
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const float pp = valid[j] ? pv[j] * bfs : 0.f;
-      const __bf16 h = (__bf16)pp;
-      bhi[j] = h;
-      blo[j] = (__bf16)(pp - (float)h);
     }
 #pragma unroll
-    for (int rr = 0; rr < 8; ++rr) st.acc[rr] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[rr], bhi, st.acc[rr], 0, 0, 0);
+    for (int hb = 0; hb < HB; ++hb) {
+      f32x4 S0 = {0.f, 0.f, 0.f, 0.f}, S1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int rr = 0; rr < 8; ++rr) st.acc[rr] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[rr], blo, st.acc[rr], 0, 0, 0);
+      for (int tt = 0; tt < 4; ++tt) {
+        // B operand: q[head] channels 32q4+8tt .. +7 in natural order, zero outside the group
+        u32x4 qw = *(const u32x4*)&q_lds[4 * hb + hh][16 * q4 + 4 * tt];
+        if (!use[hb]) qw = (u32x4){0u, 0u, 0u, 0u};
+        const bf16x8 bqb = __builtin_bit_cast(bf16x8, qw);
+        S0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[tt], bqb, S0, 0, 0, 0);
+        S1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[4 + tt], bqb, S1, 0, 0, 0);
+      }
+      float sc[8];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float v0 = S0[r], v1 = S1[r];
+        v0 += dpp_quad_xor1(v0);
+        v1 += dpp_quad_xor1(v1);
+        v0 += dpp_quad_xor2(v0);
+        v1 += dpp_quad_xor2(v1);
+        sc[r] = valid[r] ? v0 * alpha_log2 : -INFINITY;
+        sc[4 + r] = valid[4 + r] ? v1 * alpha_log2 : -INFINITY;
+      }
+      float pv[8];
+      tile_softmax(st[hb], sc, pv);
+      bf16x8 bhi, blo;
+      const float bfs = st[hb].ps * (1.0f / 16777216.0f);  // bf16 tiles feed p 2^e 2^-24
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float pp = valid[j] ? pv[j] * bfs : 0.f;
+        const __bf16 h = (__bf16)pp;
+        bhi[j] = h;
+        blo[j] = (__bf16)(pp - (float)h);
+      }
+#pragma unroll
+      for (int rr = 0; rr < 8; ++rr)
+        st[hb].acc[rr] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[rr], bhi, st[hb].acc[rr], 0, 0, 0);
+#pragma unroll
+      for (int rr = 0; rr < 8; ++rr)
+        st[hb].acc[rr] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[rr], blo, st[hb].acc[rr], 0, 0, 0);
+    }
   }
 
-  // ---- per-wave totals, then merge the 4 waves through LDS
-  st.l += shfl_xor_f(st.l, 16);
-  st.l += shfl_xor_f(st.l, 32);
-  st.mt += shfl_xor_f(st.mt, 16);
-  st.mt += shfl_xor_f(st.mt, 32);
-  __shared__ float red_m[WAVES][4], red_l[WAVES][4];
-  __shared__ float red_o[WAVES][4][D];
-  if (n == 4 * hh && q4 == 0) {  // one lane per head (g == 0, quad 0)
-    red_m[wave][hh] = st.m;
-    red_l[wave][hh] = st.l;
-  }
+  // ---- per-wave totals, then merge the waves through LDS
+  __shared__ float red_m[WAVES][HW], red_l[WAVES][HW];
+  __shared__ float red_o[WAVES][HW][D];
 #pragma unroll
-  for (int rr = 0; rr < 8; ++rr) {
-    if ((rr >> 1) == g) {
+  for (int hb = 0; hb < HB; ++hb) {
+    st[hb].l += shfl_xor_f(st[hb].l, 16);
+    st[hb].l += shfl_xor_f(st[hb].l, 32);
+    st[hb].mt += shfl_xor_f(st[hb].mt, 16);
+    st[hb].mt += shfl_xor_f(st[hb].mt, 32);
+    const int hl = 4 * hb + hh;
+    if (n == 4 * hh && q4 == 0) {  // one lane per head (g == 0, quad 0)
+      red_m[wave][hl] = st[hb].m;
+      red_l[wave][hl] = st[hb].l;
+    }
 #pragma unroll
-      for (int r = 0; r < 4; ++r) red_o[wave][hh][16 * rr + 4 * q4 + r] = st.acc[rr][r] * (16777216.0f / st.ps) + st.mt;
+    for (int rr = 0; rr < 8; ++rr) {
+      if ((rr >> 1) == g) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          red_o[wave][hl][16 * rr + 4 * q4 + r] = st[hb].acc[rr][r] * (16777216.0f / st[hb].ps) + st[hb].mt;
+      }
     }
   }
   __syncthreads();
-  for (int idx = threadIdx.x; idx < 4 * D; idx += 64 * WAVES) {
+  for (int idx = threadIdx.x; idx < HW * D; idx += 64 * WAVES) {
     const int h2 = idx / D, c = idx % D;
-    const int hd = sub * 4 + h2;
+    const int hd = sub * HW + h2;
     if (hd >= p.G) continue;
     float M = red_m[0][h2];
 #pragma unroll
@@ -601,7 +657,6 @@ __global__ __launch_bounds__(64 * NWAVES) void decode_split_kernel(Params p) {
     if (c == 0) { rec[0] = M; rec[1] = L; }
     rec[2 + c] = O;
   }
-
 }
 
 // ReduceSoftmax over the split records (HyQuant paper Alg. 3): one workgroup per (b, Q head).
@@ -738,14 +793,23 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
   dim3 grid(decode_grid_size(p.n_splits, p.Hkv, p.B, p.G));
   hipError_t e = with_widths(p.bits, p.bits_v, [&](auto BK, auto BV) {
     constexpr int bk = decltype(BK)::value, bv = decltype(BV)::value;
-    // nontemporal loads unless the head blocks of a KV head share its slab through L2 (G > 4)
-    const bool nt = p.G <= 4;
+    // nontemporal loads unless the head blocks of a KV head share its slab through L2 (GQA 16)
+    const bool nt = decode_head_blocks(p.G) == 1;
+    const bool two = decode_heads_per_wave(p.G) == 8;  // two column blocks per wave
     if (p.waves == 8) {
-      if (nt) hipLaunchKernelGGL((decode_split_kernel<bk, bv, DecodeParams, 8, true>), grid, dim3(512), 0, stream, p);
-      else hipLaunchKernelGGL((decode_split_kernel<bk, bv, DecodeParams, 8, false>), grid, dim3(512), 0, stream, p);
+      if (two) {
+        if (nt) hipLaunchKernelGGL((decode_split_kernel<bk, bv, DecodeParams, 8, true, 2>), grid, dim3(512), 0, stream, p);
+        else hipLaunchKernelGGL((decode_split_kernel<bk, bv, DecodeParams, 8, false, 2>), grid, dim3(512), 0, stream, p);
+      } else {
+        hipLaunchKernelGGL((decode_split_kernel<bk, bv, DecodeParams, 8, true, 1>), grid, dim3(512), 0, stream, p);
+      }
     } else {
-      if (nt) hipLaunchKernelGGL((decode_split_kernel<bk, bv, DecodeParams, 4, true>), grid, dim3(256), 0, stream, p);
-      else hipLaunchKernelGGL((decode_split_kernel<bk, bv, DecodeParams, 4, false>), grid, dim3(256), 0, stream, p);
+      if (two) {
+        if (nt) hipLaunchKernelGGL((decode_split_kernel<bk, bv, DecodeParams, 4, true, 2>), grid, dim3(256), 0, stream, p);
+        else hipLaunchKernelGGL((decode_split_kernel<bk, bv, DecodeParams, 4, false, 2>), grid, dim3(256), 0, stream, p);
+      } else {
+        hipLaunchKernelGGL((decode_split_kernel<bk, bv, DecodeParams, 4, true, 1>), grid, dim3(256), 0, stream, p);
+      }
     }
     return hipGetLastError();
   });
@@ -762,9 +826,9 @@ hipError_t launch_decode_ragged(const RaggedDecodeParams& p, hipStream_t stream)
   hipError_t e = with_widths(p.bits, p.bits_v, [&](auto BK, auto BV) {
     constexpr int bk = decltype(BK)::value, bv = decltype(BV)::value;
     if (nsub == 1)
-      hipLaunchKernelGGL((decode_split_kernel<bk, bv, RaggedDecodeParams, 4, true>), grid, dim3(256), 0, stream, p);
+      hipLaunchKernelGGL((decode_split_kernel<bk, bv, RaggedDecodeParams, 4, true, 1>), grid, dim3(256), 0, stream, p);
     else
-      hipLaunchKernelGGL((decode_split_kernel<bk, bv, RaggedDecodeParams, 4, false>), grid, dim3(256), 0, stream, p);
+      hipLaunchKernelGGL((decode_split_kernel<bk, bv, RaggedDecodeParams, 4, false, 1>), grid, dim3(256), 0, stream, p);
     return hipGetLastError();
   });
   if (e != hipSuccess) return e;

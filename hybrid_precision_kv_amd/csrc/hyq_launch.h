@@ -32,6 +32,14 @@ struct DecodeParams {
   int waves;         // waves per split workgroup: 4, or 8 for latency-bound launches
 };
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream);
+// Q heads one decode wave serves in a uniform batch: its 16 MFMA columns are (head, channel
+// group) pairs of 4 heads; GQA 8 and 16 take two such column blocks, so that one load of a
+// tile serves 8 Q heads.  Head blocks per KV head: ceil(G / that).
+__host__ __device__ inline int decode_heads_per_wave(int G) { return G >= 8 ? 8 : 4; }
+__host__ __device__ inline int decode_head_blocks(int G) {
+  const int h = decode_heads_per_wave(G);
+  return (G + h - 1) / h;
+}
 // Device address of the current device's static decode scratch (HYQ_NOALLOC_SCRATCH_BYTES),
 // looked up once per device.
 hipError_t noalloc_scratch(float** ptr);
