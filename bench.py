@@ -455,8 +455,8 @@ def bench_decode_bits(torch, hq, gen, dev, B=16, L=32768, Hq=32, Hkv=8, layers=8
 def bench_decode_gqa8(torch, hq, gen, dev, B=4, L=32768, Hq=64, Hkv=8, layers=16, steps=100, copy_cal=False):
     """Decode at GQA 8 (the Qwen3-32B shape of the selector workload: 64 Q / 8 KV heads, batch 4,
     32K, 5% anchors): hyq_decode_attn per step rotating over ``layers`` resident caches.  Each
-    KV head's Q heads are served by two 4-head blocks that read its slab together; the
-    algorithmic bytes count the slab once."""
+    wave serves the 8 Q heads of its KV head with two 4-head MFMA column blocks, so the slab is
+    streamed once; the algorithmic bytes count it once."""
     G = Hq // Hkv
     shape = hq.Shape.for_context(B, Hq, Hkv, L + 64)
     lay = [make_layer(torch, hq, shape, B, Hkv, G, L, gen, dev) for _ in range(layers)]
@@ -485,7 +485,7 @@ def bench_decode_gqa8(torch, hq, gen, dev, B=4, L=32768, Hq=64, Hkv=8, layers=16
     return {"workload": f"qwen3-32b-shape decode bs{B} ctx{L} hq{Hq} hkv{Hkv} layers{layers}",
             "us_per_step": round(us, 2), "GB_per_s": round(nbytes / (us * 1e-6) / 1e9, 1),
             "hbm_frac": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4), "bytes_per_step": nbytes,
-            "note": "two 4-head blocks per KV head, dispatched back to back on one XCD; bytes count the slab once"}
+            "note": "one wave serves the 8 Q heads of a KV head (two 4-head column blocks); bytes count the slab once"}
 
 
 def ragged_lengths(n_seq, seed, lo=2048, hi=32768):

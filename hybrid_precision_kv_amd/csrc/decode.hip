@@ -9,7 +9,9 @@
 //  * Q.K^T on MFMA f32_16x16x32_f16.  A = 16 cached positions x 32 channels, B = the Q heads of
 //    the KV group spread over the 16 MFMA columns as (head, channel group) pairs: column
 //    4*h + g carries q[h] restricted to group g, so the MFMA returns per-group partial dots and
-//    every lane owns a distinct (head, group).  INT4 codes enter as f16 *subnormals*
+//    every lane owns a distinct (head, group).  At GQA 8 and 16 a wave holds two such column
+//    blocks (8 Q heads) and feeds both from one extraction of the tile's codes.  INT4 codes
+//    enter as f16 *subnormals*
 //    (bits 0x000c == c * 2^-24, exact): 8 codes become 8 MFMA operands with one shift and four
 //    masks (two of the four pairs come out multiplied by 16; the other operand carries 1/16 on
 //    those k-slots).  The per-group scale and min are applied in fp32 afterwards:
