@@ -366,15 +366,20 @@ __global__ __launch_bounds__(256) void refresh_gather_kernel(RefreshParams p) {
 constexpr int MV_CHUNK = 4;
 constexpr int MOVE_WAVES = 4;  // waves per workgroup
 
+// min / max over the 8 lanes of a group (lanes 8 k .. 8 k + 7) with DPP, no LDS trip: lane
+// swaps within each quad, then the half-row mirror pairs lane i with 7 - i (the other quad)
+__device__ inline float dpp_half_mirror(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false));
+}
 __device__ inline float group8_min(float v) {
-#pragma unroll
-  for (int o = 1; o < 8; o <<= 1) v = fminf(v, shfl_xor_f(v, o));
-  return v;
+  v = fminf(v, dpp_quad_xor1(v));
+  v = fminf(v, dpp_quad_xor2(v));
+  return fminf(v, dpp_half_mirror(v));
 }
 __device__ inline float group8_max(float v) {
-#pragma unroll
-  for (int o = 1; o < 8; o <<= 1) v = fmaxf(v, shfl_xor_f(v, o));
-  return v;
+  v = fmaxf(v, dpp_quad_xor1(v));
+  v = fmaxf(v, dpp_quad_xor2(v));
+  return fmaxf(v, dpp_half_mirror(v));
 }
 
 // source words of one move, per lane (see load_move)
@@ -470,15 +475,19 @@ __global__ __launch_bounds__(64 * MOVE_WAVES) void refresh_move_kernel(RefreshPa
   const uint64_t later = start_mask & ~((2ull << MV_CHUNK) - 1ull);
   const int j_end = later ? __builtin_ctzll(later) : min(64, n - (lo - 1));
 
-  MoveSrc nxt = load_move<BK, BV>(p, hb, __shfl(wkind, j0), __shfl(wsrc, j0), lane, slab, slot_pos, ps0);
+  // list entries are read across lanes with readlane (a uniform lane index, no LDS trip)
+  MoveSrc nxt = load_move<BK, BV>(p, hb, __builtin_amdgcn_readlane(wkind, j0), __builtin_amdgcn_readlane(wsrc, j0), lane,
+                                  slab, slot_pos, ps0);
   int tile = -1;
   uint32_t qmask = 0;
   for (int j = j0; j < j_end; ++j) {
-    const int dst = __builtin_amdgcn_readfirstlane(__shfl(wdst, j));
-    const int kind = __builtin_amdgcn_readfirstlane(__shfl(wkind, j));
-    const int src = __builtin_amdgcn_readfirstlane(__shfl(wsrc, j));
+    const int dst = __builtin_amdgcn_readlane(wdst, j);
+    const int kind = __builtin_amdgcn_readlane(wkind, j);
+    const int src = __builtin_amdgcn_readlane(wsrc, j);
     const MoveSrc cur = nxt;
-    if (j + 1 < j_end) nxt = load_move<BK, BV>(p, hb, __shfl(wkind, j + 1), __shfl(wsrc, j + 1), lane, slab, slot_pos, ps0);
+    if (j + 1 < j_end)
+      nxt = load_move<BK, BV>(p, hb, __builtin_amdgcn_readlane(wkind, j + 1), __builtin_amdgcn_readlane(wsrc, j + 1), lane,
+                              slab, slot_pos, ps0);
     if ((dst >> 5) != tile) {
       // a new tile: the quads its moves touch, their V-code dwords into this lane's column
       tile = dst >> 5;
@@ -548,7 +557,7 @@ __global__ __launch_bounds__(64 * MOVE_WAVES) void refresh_move_kernel(RefreshPa
           if constexpr (BK == 4) {
             // nibbles 4 sub + e of the group's 32; dword sub / 2 holds lanes sub & ~1 (low) and | 1
             const uint32_t half16 = code[0] | (code[1] << 4) | (code[2] << 8) | (code[3] << 12);
-            const uint32_t other = (uint32_t)__float_as_int(shfl_xor_f(__int_as_float((int)half16), 1));
+            const uint32_t other = (uint32_t)__float_as_int(dpp_quad_xor1(__int_as_float((int)half16)));
             if ((sub & 1) == 0) kc[sub >> 1] = half16 | (other << 16);
           } else if constexpr (BK == 8) {
             // bytes 4 sub + e of the group's 32: one dword per lane
@@ -556,8 +565,8 @@ __global__ __launch_bounds__(64 * MOVE_WAVES) void refresh_move_kernel(RefreshPa
           } else {
             // 2-bit codes 4 sub + e: byte sub & 3 of dword sub / 4, OR-ed over the dword's 4 lanes
             uint32_t w = (code[0] | (code[1] << 2) | (code[2] << 4) | (code[3] << 6)) << (8 * (sub & 3));
-            w |= (uint32_t)__float_as_int(shfl_xor_f(__int_as_float((int)w), 1));
-            w |= (uint32_t)__float_as_int(shfl_xor_f(__int_as_float((int)w), 2));
+            w |= (uint32_t)__float_as_int(dpp_quad_xor1(__int_as_float((int)w)));
+            w |= (uint32_t)__float_as_int(dpp_quad_xor2(__int_as_float((int)w)));
             if ((sub & 3) == 0) kc[sub >> 2] = w;
           }
           if (sub == 0) *(uint32_t*)(slab + (uint32_t)ksm_byte_b<BK, BV>(dst, g)) = smw;
@@ -595,7 +604,7 @@ __global__ __launch_bounds__(64 * MOVE_WAVES) void refresh_move_kernel(RefreshPa
       if (lane == 0) slot_pos[dst] = cur.pos;
     }
     // the tile's last move: the owned dwords go back
-    if (j + 1 == j_end || (__builtin_amdgcn_readfirstlane(__shfl(wdst, j + 1)) >> 5) != tile) {
+    if (j + 1 == j_end || (__builtin_amdgcn_readlane(wdst, j + 1) >> 5) != tile) {
       if (kv == 1) {
 #pragma unroll
         for (int qq = 0; qq < 4; ++qq)
