@@ -140,6 +140,18 @@ def test_gqa_factors(G):
     p.decode_check(q)
 
 
+@pytest.mark.parametrize("G", [8, 16])
+def test_gqa_wide_ragged_split_counts(G):
+    """GQA 8 and 16 (one wave serves two 4-head column blocks) over a ragged 3001-token cache
+    at split counts that leave each wave an odd, an even and a single INT4 tile, so the
+    prefetch past a wave's last tile falls on both halves of the double-buffered loop."""
+    p = Pair(320 + G, 1, 2, G, 3001, n_steps=2)
+    p.append()
+    q = p.append()
+    for s in (1, 3, 7, 40, 0):
+        p.decode_check(q, n_splits=s)
+
+
 @pytest.mark.parametrize("L", [1, 50, 127, 128, 129, 160, 161])
 def test_edge_lengths(L):
     p = Pair(500 + L, 1, 2, 4, L, n_steps=2)

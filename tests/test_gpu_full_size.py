@@ -141,6 +141,41 @@ def test_full_size_batch1_decode_all_heads():
     _check_decode(hq.decode_attn(cache, dev(q), 0).cpu().numpy(), q, refs)
 
 
+def test_full_size_gqa8_decode_sampled():
+    """The GQA-8 decode row's workload: 64 Q / 8 KV heads, batch 4 x 32768, 5% anchors,
+    automatic splits (one wave per 8 Q heads of a KV head); sampled heads against the oracle."""
+    Bs, Gs = 4, 8
+    print(f"[case] full size decode B={Bs} G={Gs}", flush=True)
+    d = synth.gen_batch(12300, Bs, HKV, Gs, L, n_proxy=64, n_steps=1)
+    shape = hq.Shape.for_context(Bs, HKV * Gs, HKV, L + 1)
+    k = pol.k_rule(L)
+    Kd, Pd = dev(d["K"]), dev(d["proxy"])
+    anchors = hq.select_vlines(shape, k, dense_k=Kd, proxy=Pd).cpu().numpy()
+    refs = {}
+    for b, h in [(0, 0), (2, 5), (3, 7)]:
+        A, _ = pol.select_dense(d["K"][b, h], d["proxy"][b, h * Gs:(h + 1) * Gs])
+        anchors[b, h] = A
+        r = pol.HybridCacheRef(g=Gs)
+        r.freeze(d["K"][b, h], d["V"][b, h], A, d["proxy"][b, h * Gs:(h + 1) * Gs])
+        r.append(d["new_k"][b, h, 0], d["new_v"][b, h, 0], d["new_q"][b, h * Gs:(h + 1) * Gs, 0])
+        refs[(b, h)] = r
+    cache = hq.HybridKVCache(shape)
+    hq.quantize_kv(cache, Kd, dev(d["V"]), torch.from_numpy(anchors).cuda(), Pd)
+    hq.append_token(cache, dev(d["new_k"][:, :, 0]), dev(d["new_v"][:, :, 0]), dev(d["new_q"][:, :, 0]))
+    q = d["new_q"][:, :, 0]
+    o = hq.decode_attn(cache, dev(q), 0).cpu().numpy()
+    assert np.all(np.isfinite(o))
+    for (b, h), r in refs.items():
+        Kh, Vh = r.stored_kv()
+        ref = att.decode_ref(nm.bf16_to_f32(q[b, h * Gs:(h + 1) * Gs]), Kh, Vh)
+        got = o[b, h * Gs:(h + 1) * Gs]
+        err = np.abs(got - ref).max()
+        rel = np.linalg.norm(got - ref) / np.linalg.norm(ref)
+        assert err <= MAX_ABS and rel <= REL_L2, f"G8 b{b} h{h}: max-abs {err:.3g} rel-L2 {rel:.3g}"
+    del cache
+    torch.cuda.empty_cache()
+
+
 def test_full_size_selector_qwen32b_shape():
     """The selector row's workload: 64 Q / 8 KV heads (GQA 8), batch 4 x 32768, cache-mode
     selection at 1%, 5% and 10% of the context; sampled heads against the oracle (scores
