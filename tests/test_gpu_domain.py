@@ -8,8 +8,11 @@ Domain: K and V below 65504 in magnitude (fp16 scale and min stay finite), q in 
     (the decode's per-column V weight scale moves in both directions inside a wave), tiny
     and large q;
   * constant groups (scale 0, every code 0) in K and V;
+  * the large, mixed and tiny V, large K and constant-group cases at GQA 8 and 16 (two
+    column blocks per wave);
   * split counts above 32 (33 to 256) and the automatic plan at 1 KV head x 32K, which takes
-    the multi-pass merge;
+    the multi-pass merge; batch 1 x 32K at GQA 8 and 16 (eight waves per workgroup, two
+    column blocks per wave);
   * the selector over 65,536 keys (rows longer than the top-k's LDS stage), dense and cache
     mode, with the refresh applied.
 
@@ -112,6 +115,19 @@ def test_constant_groups(bk, bv):
     p.decode_check(q)
 
 
+@pytest.mark.parametrize("G", [8, 16])
+@pytest.mark.parametrize("transform,bk,bv", [(large_v, 4, 4), (large_v, 2, 2), (mixed_v, 4, 4), (tiny_v, 4, 4),
+                                             (large_k, 4, 4), (constant_groups, 4, 2)])
+def test_wide_gqa_domain_edges(G, transform, bk, bv):
+    """GQA 8 and 16: one wave serves two 4-head column blocks, each with its own softmax state
+    and V weight scale; the same domain edges as above over a ragged cache and two split counts."""
+    p = Pair(9600 + G, 1, 2, G, 2500, n_steps=1, bits=bk, bits_v=bv, transform=transform)
+    p.codes_check()
+    q = p.append()
+    for s in (0, 5):
+        p.decode_check(q, n_splits=s, vnorm=True)
+
+
 def test_split_counts_above_32():
     """33 to 64 splits (the 64-record one-latency merge), 65 to 256 (the multi-pass merge), and
     more workers than tiles (idle splits carry an empty state)."""
@@ -125,6 +141,15 @@ def test_auto_splits_one_kv_head_32k():
     """1 KV head x 32K: the automatic plan spreads one head over the chip (the merge then takes
     more than 64 records)."""
     p = Pair(9401, 1, 1, 4, 32768, n_steps=1)
+    q = p.append()
+    p.decode_check(q)
+
+
+@pytest.mark.parametrize("G", [8, 16])
+def test_auto_splits_batch1_wide_gqa_32k(G):
+    """Batch 1 x 32K at GQA 8 and 16 over 2 KV heads: the automatic plan takes 128 and 64
+    splits per KV head with eight waves per workgroup, each wave serving two column blocks."""
+    p = Pair(9402 + G, 1, 2, G, 32768, n_steps=1)
     q = p.append()
     p.decode_check(q)
 
