@@ -205,7 +205,7 @@ int auto_splits(const hyq_cache_t* c, int* waves) {
 // sequence takes at most max(16, tiles / 4) splits (as auto_splits).  The total never exceeds
 // ragged_split_bound().
 int ragged_columns(int Hkv, int G, bool two_per_cu) {
-  const long u1 = (long)Hkv * ((G + 3) / 4);
+  const long u1 = (long)Hkv * hyq::decode_head_blocks(G);
   const long cus = cu_count();
   return (int)(((two_per_cu ? 2 : 1) * cus + u1 - 1) / u1);
 }

@@ -352,7 +352,7 @@ __device__ inline bool unit_of(const DecodeParams& p, Unit& u) {
 }
 // variable-length batch: grid (split of the batch, KV head x head block)
 __device__ inline bool unit_of(const RaggedDecodeParams& p, Unit& u) {
-  const int nsub = (p.G + 3) >> 2;
+  const int nsub = decode_head_blocks(p.G);
   u.hkv = blockIdx.y / nsub;
   u.sub = blockIdx.y % nsub;
   u.split = 0;  // from the split map
@@ -823,14 +823,20 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
 }
 
 hipError_t launch_decode_ragged(const RaggedDecodeParams& p, hipStream_t stream) {
-  const int nsub = (p.G + 3) >> 2;
+  const int nsub = decode_head_blocks(p.G);
   dim3 grid(p.total_splits, p.Hkv * nsub, 1);
   hipError_t e = with_widths(p.bits, p.bits_v, [&](auto BK, auto BV) {
     constexpr int bk = decltype(BK)::value, bv = decltype(BV)::value;
-    if (nsub == 1)
+    if (decode_heads_per_wave(p.G) == 8) {  // two column blocks per wave, as in the uniform batch
+      if (nsub == 1)
+        hipLaunchKernelGGL((decode_split_kernel<bk, bv, RaggedDecodeParams, 4, true, 2>), grid, dim3(256), 0, stream, p);
+      else
+        hipLaunchKernelGGL((decode_split_kernel<bk, bv, RaggedDecodeParams, 4, false, 2>), grid, dim3(256), 0, stream, p);
+    } else if (nsub == 1) {
       hipLaunchKernelGGL((decode_split_kernel<bk, bv, RaggedDecodeParams, 4, true, 1>), grid, dim3(256), 0, stream, p);
-    else
+    } else {
       hipLaunchKernelGGL((decode_split_kernel<bk, bv, RaggedDecodeParams, 4, false, 1>), grid, dim3(256), 0, stream, p);
+    }
     return hipGetLastError();
   });
   if (e != hipSuccess) return e;

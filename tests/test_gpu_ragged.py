@@ -65,6 +65,18 @@ def test_ragged_single_sequence_and_gqa():
     ragged_check(pairs, [p.append() for p in pairs], n_splits=2)
 
 
+@pytest.mark.parametrize("G", [8, 16])
+def test_ragged_wide_gqa_matches_single_cache(G):
+    """GQA 8 and 16: the variable-length launch takes the uniform batch's two column blocks per
+    wave; at a fixed split count every sequence is bit-identical to its single-cache decode."""
+    pairs = [Pair(9140 + G + i, 1, 2, G, L, n_steps=1) for i, L in enumerate([3001, 700, 129])]
+    qs = [p.append() for p in pairs]
+    for s in (0, 3):
+        o = ragged_check(pairs, qs, n_splits=s)
+        if s:
+            same_as_alone(pairs, qs, s, o)
+
+
 def test_ragged_staggered_refresh():
     """Four sequences of different lengths, 96 steps; sequence i runs select-and-refresh when its
     own staging holds 64 tokens minus 16 i (every sequence on its own cadence), and the batch is
