@@ -216,6 +216,11 @@ def timed_graph(torch, fn, reps):
     g.replay()
     torch.cuda.synchronize()
     first = out.clone() if hasattr(out, "clone") else out
+    # untimed replays: the first replays of a freshly captured graph run slower than later ones
+    # (the first few graphs of a process by up to 20% at bs16 x 32K)
+    for _ in range(max(3, reps // 2)):
+        g.replay()
+    torch.cuda.synchronize()
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a.record()
     for _ in range(reps):
@@ -265,7 +270,7 @@ def bench_maintenance(torch, hq, cache, B, Hkv, G, L, gen, dev, ws, out, splits)
     t_apply = max(t_ref - t_sel, 1e-3)
     # device time of the per-token work from captured graphs (the staging emptied by the
     # refresh above takes the 60 appends the warm-ups and captures make, of its 64 slots; a
-    # replay repeats the recorded appends into the same slots)
+    # replay, warm or timed, repeats the recorded appends into the same slots)
     k_t, v_t, q_t = toks[0]
     # the eager select-and-refresh above leaves the device below its steady rate, and at this
     # size the decode keeps speeding up for well over 100 ms of sustained load (152 -> 124 us
